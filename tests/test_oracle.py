@@ -1,0 +1,414 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with an
+independent statement of the result (hand-derived golden values, closed-form
+bounds, brute force on tiny inputs, a library attention routine).  The test
+functions call them; ``test_pins_catch_planted_mistakes`` plants plausible
+mistakes in the oracle (on the CPU, via monkeypatch) and checks that some pin
+fails for each one.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle.kv_oracle as O
+from selective_kv_cache_amd import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rows(seed, n, d, outliers=3, scale=8.0):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, d)).astype(np.float32)
+    ch = rng.choice(d, size=outliers, replace=False)
+    x[:, ch] *= np.float32(scale)
+    return x
+
+
+# --------------------------------------------------------------------- pins
+
+def pin_toy_example():
+    g = _golden("nested_toy.json")
+    qr = O.quantize_rows(np.asarray([g["x"]], np.float32), g["b"], g["r"])
+    assert float(qr.lo[0]) == g["lo"] and float(qr.delta[0]) == g["delta"]
+    assert qr.fine[0].tolist() == g["fine"]
+    assert qr.base[0].tolist() == g["base"]
+    assert qr.refine[0].tolist() == g["refine"]
+    np.testing.assert_allclose(O.dequant_base(qr)[0], g["base_values"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(O.dequant_refined(qr)[0], g["refined_values"], rtol=0, atol=1e-12)
+    assert O.pack_bits(qr.base, g["b"])[0].tolist() == g["packed_base"]
+    assert O.pack_bits(qr.refine, g["r"])[0].tolist() == g["packed_refine"]
+
+
+def pin_packing():
+    for case in _golden("packing.json")["cases"]:
+        codes = np.asarray([case["codes"]])
+        got = O.pack_bits(codes, case["w"])[0].tolist()
+        assert got == case["bytes"], (case, got)
+        back = O.unpack_bits(np.asarray([case["bytes"]], np.uint8), case["w"], len(case["codes"]))
+        assert back[0].tolist() == case["codes"]
+
+
+def pin_quant_bounds():
+    x = _rows(1, 400, 128)
+    for b, r in [(2, 0), (2, 2), (2, 4), (2, 8), (3, 2), (4, 4)]:
+        qr = O.quantize_rows(x, b, r)
+        xd = x.astype(np.float64)
+        lo = qr.lo.astype(np.float64)[:, None]
+        d = qr.delta.astype(np.float64)[:, None]
+        df = d / 2 ** r
+        base = O.dequant_base(qr)
+        ref = O.dequant_refined(qr)
+        slack = 1e-6 * d
+        assert np.all(np.abs(base - xd) <= d / 2 + slack), (b, r)
+        assert np.all(np.abs(ref - xd) <= df / 2 + slack), (b, r)
+        # the refined value lies inside the bin the base code names
+        c = qr.base.astype(np.float64)
+        assert np.all(ref >= lo + c * d - slack) and np.all(ref <= lo + (c + 1) * d + slack)
+        # codes in range, min element in bin 0, max element in the top bin
+        assert qr.base.max() <= 2 ** b - 1 and qr.refine.max() <= max(2 ** r - 1, 0)
+        amin, amax = x.argmin(1), x.argmax(1)
+        rows = np.arange(x.shape[0])
+        assert np.all(qr.fine[rows, amin] == 0)
+        assert np.all(qr.fine[rows, amax] == 2 ** (b + r) - 1)
+
+
+def pin_nested_equals_direct():
+    """2-bit code + 2 refinement bits reproduce the 4-bit quantizer's value in
+    the named bin; the base code equals the direct b-bit code."""
+    x = _rows(2, 300, 128)
+    for b, r in [(2, 2), (2, 4), (3, 2), (2, 8)]:
+        nested = O.quantize_rows(x, b, r)
+        direct = O.quantize_rows(x, b + r, 0)
+        coarse = O.quantize_rows(x, b, 0)
+        np.testing.assert_allclose(O.dequant_refined(nested), O.dequant_base(direct),
+                                   rtol=0, atol=1e-9)
+        assert np.array_equal(nested.base, coarse.base)
+        assert np.array_equal(nested.fine, direct.base)
+    # brute-force bin search in fp64: the fine code counts the sub-bin edges
+    # lo + j*delta_f (j = 1 .. 2^F - 1) at or below x; only elements within a
+    # hair of an edge may differ (fp32 rounding of (x - lo) / delta_f)
+    b, r = 2, 2
+    qr = O.quantize_rows(x[:40], b, r)
+    for i in range(40):
+        lo = float(qr.lo[i])
+        df = float(qr.delta[i]) / 2 ** r
+        for dd in range(128):
+            xv = float(x[i, dd])
+            j = sum(1 for e in range(1, 2 ** (b + r)) if lo + e * df <= xv)
+            if j != int(qr.fine[i, dd]):
+                near = min(abs(xv - (lo + e * df)) for e in range(1, 2 ** (b + r)))
+                assert near <= 1e-6 * max(1.0, abs(xv)), (i, dd, j, int(qr.fine[i, dd]))
+
+
+def pin_flat_row():
+    x = np.full((2, 8), 1.25, np.float32)
+    qr = O.quantize_rows(x, 2, 2)
+    assert np.all(qr.fine == 0) and np.all(qr.delta == 0)
+    assert np.all(O.dequant_base(qr) == 1.25) and np.all(O.dequant_refined(qr) == 1.25)
+
+
+def pin_scores_bruteforce():
+    rng = np.random.default_rng(3)
+    g_, n, d = 3, 7, 8
+    q = rng.standard_normal((g_, d))
+    k = rng.standard_normal((n, d))
+    got = O.token_scores(q, k)
+    for i in range(n):
+        best = -math.inf
+        for h in range(g_):
+            acc = 0.0
+            for j in range(d):
+                acc += float(q[h, j]) * float(k[i, j])
+            best = max(best, acc / math.sqrt(d))
+        assert abs(got[i] - best) <= 1e-12 * max(1.0, abs(best))
+
+
+def pin_select_bruteforce():
+    rng = np.random.default_rng(4)
+    for n, t in [(12, 4), (12, 12), (5, 9), (9, 0), (16, 7)]:
+        s = rng.integers(-3, 4, size=n).astype(np.float64)     # many exact ties
+        s[rng.integers(0, n)] = -0.0
+        ranked = sorted(range(n), key=lambda i: (-s[i], i))
+        want = sorted(ranked[: min(t, n)])
+        assert O.select_top_t(s, t).tolist() == want, (n, t, s)
+
+
+def _sdpa(q, k, v):
+    import torch
+    qt = torch.as_tensor(np.asarray(q, np.float64))[None, :, None, :]     # [1][G][1][D]
+    kt = torch.as_tensor(np.asarray(k, np.float64))[None, None].expand(1, q.shape[0], -1, -1)
+    vt = torch.as_tensor(np.asarray(v, np.float64))[None, None].expand(1, q.shape[0], -1, -1)
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt.contiguous(), vt.contiguous())
+    return out[0, :, 0, :].numpy()
+
+
+def pin_attend_textbook():
+    """T=0: no refinement, so the step is textbook softmax attention on the
+    base-precision keys and values (library routine, fp64)."""
+    x_k, x_v = _rows(5, 300, 64), _rows(6, 300, 64, outliers=0)
+    q = np.random.default_rng(7).standard_normal((4, 64))
+    kc, vc = O.quantize_rows(x_k, 2, 2), O.quantize_rows(x_v, 2, 2)
+    res = O.decode_head(q, kc, vc, 0)
+    want = _sdpa(q, O.dequant_base(kc), O.dequant_base(vc))
+    np.testing.assert_allclose(res.out, want, rtol=0, atol=1e-10)
+    assert res.sel.size == 0
+
+
+def pin_attend_converges():
+    """T=N: every token refined, so as r grows the output tends to fp64
+    attention on the unquantized K and V, within the perturbation bound
+    |dout| <= max|dV| + 2 max|V| (exp(2 eps) - 1), eps = ||q||_1 dF / (2 sqrt(D))."""
+    d = 64
+    x_k, x_v = _rows(8, 200, d), _rows(9, 200, d, outliers=0)
+    q = np.random.default_rng(10).standard_normal((2, d)) * 0.5
+    exact = _sdpa(q, x_k, x_v)
+    errs = []
+    for r in [0, 2, 4, 8, 10]:
+        kc, vc = O.quantize_rows(x_k, 2, r), O.quantize_rows(x_v, 2, r)
+        res = O.decode_head(q, kc, vc, x_k.shape[0])
+        err = np.abs(res.out - exact).max()
+        dfk = kc.delta.max() / 2 ** r
+        dfv = vc.delta.max() / 2 ** r
+        eps = np.abs(q).sum(1).max() * dfk / (2 * math.sqrt(d))
+        bound = dfv / 2 + 2 * np.abs(x_v).max() * (math.exp(2 * eps) - 1)
+        assert err <= bound * (1 + 1e-9), (r, err, bound)
+        errs.append(err)
+    assert all(errs[i + 1] < errs[i] for i in range(len(errs) - 1)), errs
+    assert errs[-1] < 2e-3
+
+
+def pin_decode_bruteforce():
+    """Whole (sequence, KV head) step on a tiny case in pure-Python loops:
+    dequantize, score = max over the group, top-T with the lower-index tie
+    rule, refined rows for the selection, softmax attention."""
+    n, d, g_, t, b, r = 9, 8, 2, 3, 2, 2
+    x_k, x_v = _rows(11, n, d, outliers=1), _rows(12, n, d, outliers=0)
+    x_k[7] = x_k[2]                     # an exact score tie
+    q = np.random.default_rng(13).standard_normal((g_, d))
+    kc, vc = O.quantize_rows(x_k, b, r), O.quantize_rows(x_v, b, r)
+    res = O.decode_head(q, kc, vc, t)
+
+    def val(qr, i, j, refined):
+        lo, dl = float(qr.lo[i]), float(qr.delta[i])
+        c = int(qr.base[i, j])
+        if not refined:
+            return lo + (c + 0.5) * dl
+        s = int(qr.refine[i, j])
+        return lo + c * dl + (s + 0.5) * dl / 2 ** r
+
+    score = []
+    for i in range(n):
+        best = -math.inf
+        for h in range(g_):
+            acc = sum(float(q[h, j]) * val(kc, i, j, False) for j in range(d))
+            best = max(best, acc / math.sqrt(d))
+        score.append(best)
+    sel = sorted(sorted(range(n), key=lambda i: (-score[i], i))[:t])
+    assert res.sel.tolist() == sel
+    for h in range(g_):
+        logits = [sum(float(q[h, j]) * val(kc, i, j, i in sel) for j in range(d)) / math.sqrt(d)
+                  for i in range(n)]
+        m = max(logits)
+        w = [math.exp(x - m) for x in logits]
+        for j in range(d):
+            o = sum(w[i] * val(vc, i, j, i in sel) for i in range(n)) / sum(w)
+            assert abs(res.out[h, j] - o) <= 1e-12 * max(1.0, abs(o))
+
+
+def pin_gqa_mapping():
+    """Query head h reads KV head floor(h / G) (contiguous groups)."""
+    w = W.small(n_q_heads=4, n_kv_heads=2, ctx=40, top_t=5)
+    k, v = W.layer_kv(w, 0)
+    q = W.query(w, 0)
+    cache = O.quantize_cache(k, v, 2, 2)
+    res = O.decode_step(q, cache, [0, 40], 5)
+    for kv in range(2):
+        kc = O._rows(cache.k, kv, 0, 40)
+        vc = O._rows(cache.v, kv, 0, 40)
+        for j, h in enumerate((2 * kv, 2 * kv + 1)):
+            alone = O.decode_head(q[0, h:h + 1], kc, vc, 10 ** 9)   # all refined: no selection coupling
+            full = O.decode_head(q[0, 2 * kv:2 * kv + 2], kc, vc, 10 ** 9)
+            np.testing.assert_allclose(full.out[j], alone.out[0], atol=1e-12)
+        # scores are the max over exactly this KV head's two query heads
+        s_pair = O.token_scores(q[0, 2 * kv:2 * kv + 2], O.dequant_base(kc))
+        np.testing.assert_allclose(res[(0, kv)].scores, s_pair, atol=1e-12)
+
+
+def pin_cache_trace():
+    g = _golden("cache_lru.json")
+    sim = O.CacheSim(g["slots"])
+    for t, st in enumerate(g["steps"]):
+        hits, misses = sim.step(np.asarray(st["sel"]), t)
+        assert (hits, misses) == (st["hits"], st["misses"]), (t, hits, misses)
+        assert sorted(sim.residents()) == st["residents"], (t, sorted(sim.residents()))
+
+
+def pin_cache_invariants():
+    rng = np.random.default_rng(14)
+    n, t, slots = 200, 20, 40
+    sim = O.CacheSim(slots)
+    for step in range(30):
+        sel = np.sort(rng.choice(n, size=t, replace=False))
+        hits, misses = sim.step(sel, step)
+        assert hits + misses == t
+        toks = [x for x in sim.slot_tok if x >= 0]
+        assert len(toks) == len(set(toks)) <= slots          # slot <-> token bijection
+        assert set(sel.tolist()) <= set(toks)                  # the selection is resident
+    sim = O.CacheSim(slots)                                    # a repeated selection always hits
+    sel = np.arange(0, 2 * t, 2)
+    assert sim.step(sel, 0) == (0, t)
+    for step in range(1, 5):
+        assert sim.step(sel, step) == (t, 0)
+
+
+PINS = [pin_toy_example, pin_packing, pin_quant_bounds, pin_nested_equals_direct, pin_flat_row,
+        pin_scores_bruteforce, pin_select_bruteforce, pin_attend_textbook, pin_attend_converges,
+        pin_decode_bruteforce, pin_gqa_mapping, pin_cache_trace, pin_cache_invariants]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(pin):
+    pin()
+
+
+def test_fetched_bytes():
+    # c3-shaped layer: T=2048 tokens, D=128, r=4 -> 2 rows of 64 B per token
+    assert O.fetched_bytes(2048, 128, 4) == 2048 * 2 * 64
+
+
+# ------------------------------------------------- planted mistakes (CPU only)
+
+def _fails_some_pin():
+    for pin in PINS:
+        try:
+            pin()
+        except AssertionError:
+            return True
+    return False
+
+
+def _mut_base_no_half(qr):
+    return qr.lo.astype(np.float64)[..., None] + qr.base * qr.delta.astype(np.float64)[..., None]
+
+
+def _mut_refined_no_half(qr):
+    d = qr.delta.astype(np.float64)[..., None]
+    return qr.lo.astype(np.float64)[..., None] + qr.base * d + qr.refine * d / 2 ** qr.r
+
+
+def _mut_scores_sum(q, k):
+    qg = np.asarray(q, np.float64)
+    return ((qg @ np.asarray(k, np.float64).T) / np.sqrt(qg.shape[-1])).sum(0)
+
+
+def _mut_scores_noscale(q, k):
+    return (np.asarray(q, np.float64) @ np.asarray(k, np.float64).T).max(0)
+
+
+def _mut_select_high_index(s, t):
+    s = np.asarray(s, np.float64)
+    idx = np.arange(s.shape[0])
+    order = np.lexsort((-idx, -s))
+    return np.sort(order[: min(t, s.shape[0])])
+
+
+def _mut_attend_keys_as_values(q, k, v):
+    qg = np.asarray(q, np.float64)
+    lg = (qg @ np.asarray(k, np.float64).T) / np.sqrt(qg.shape[-1])
+    p = np.exp(lg - lg.max(1, keepdims=True))
+    return (p @ np.asarray(k, np.float64)) / p.sum(1, keepdims=True)
+
+
+def _mut_pack_msb(codes, w):
+    codes = np.asarray(codes)
+    bits = (codes[..., :, None].astype(np.uint32) >> np.arange(w, dtype=np.uint32)[::-1]) & 1
+    bits = bits.reshape(codes.shape[:-1] + (-1,)).astype(np.uint8)
+    return np.packbits(bits, axis=-1, bitorder="big")
+
+
+_orig_quant = O.quantize_rows
+
+
+def _mut_quant_round(x, b, r):
+    qr = _orig_quant(x, b, r)
+    x = np.asarray(x, np.float32)
+    df = (qr.delta * np.float32(2.0 ** -r)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        u = (x - qr.lo[..., None]) / df[..., None]
+    u = np.where((df == 0)[..., None], 0, u)
+    fine = np.minimum(np.round(u), 2 ** (b + r) - 1).astype(np.uint16)
+    qr.fine, qr.base, qr.refine = fine, (fine >> r).astype(np.uint8), (fine & ((1 << r) - 1)).astype(np.uint8)
+    return qr
+
+
+def _mut_quant_swapped_fields(x, b, r):
+    qr = _orig_quant(x, b, r)
+    qr.base = (qr.fine & ((1 << b) - 1)).astype(np.uint8)
+    qr.refine = (qr.fine >> b).astype(np.uint8)
+    return qr
+
+
+_orig_decode_head = O.decode_head
+
+
+def _mut_decode_refines_unselected(q, kc, vc, t):
+    res = _orig_decode_head(q, kc, vc, t)
+    # refine the complement of the selection instead
+    n = kc.base.shape[0]
+    comp = np.setdiff1d(np.arange(n), res.sel)
+    kh, vh = O.dequant_base(kc), O.dequant_base(vc)
+    if comp.size:
+        kh[comp] = O.dequant_refined(O._take(kc, comp))
+        vh[comp] = O.dequant_refined(O._take(vc, comp))
+    res.out = O.attend(q, kh, vh)
+    return res
+
+
+def _mut_cache_evict_newest(self, sel, t):
+    sel = [int(x) for x in np.sort(np.asarray(sel))]
+    where = {int(tok): i for i, tok in enumerate(self.slot_tok) if tok >= 0}
+    hits = [x for x in sel if x in where]
+    misses = [x for x in sel if x not in where]
+    for x in hits:
+        self.stamp[where[x]] = t
+    free = [i for i in range(self.n_slots) if self.slot_tok[i] < 0]
+    ev = [i for i in range(self.n_slots) if self.slot_tok[i] >= 0 and int(self.slot_tok[i]) not in set(sel)]
+    ev.sort(key=lambda i: (-self.stamp[i], self.slot_tok[i]))
+    for x, slot in zip(misses, free + ev):
+        self.slot_tok[slot] = x
+        self.stamp[slot] = t
+    return len(hits), len(misses)
+
+
+MUTATIONS = [
+    ("dequant_base", _mut_base_no_half),
+    ("dequant_refined", _mut_refined_no_half),
+    ("token_scores", _mut_scores_sum),
+    ("token_scores", _mut_scores_noscale),
+    ("select_top_t", _mut_select_high_index),
+    ("attend", _mut_attend_keys_as_values),
+    ("pack_bits", _mut_pack_msb),
+    ("quantize_rows", _mut_quant_round),
+    ("quantize_rows", _mut_quant_swapped_fields),
+    ("decode_head", _mut_decode_refines_unselected),
+]
+
+
+@pytest.mark.parametrize("name,fn", MUTATIONS, ids=[f.__name__ for _, f in MUTATIONS])
+def test_pins_catch_planted_mistakes(monkeypatch, name, fn):
+    monkeypatch.setattr(O, name, fn)
+    assert _fails_some_pin(), f"no pin caught the planted mistake {fn.__name__}"
+
+
+def test_pins_catch_planted_cache_mistake(monkeypatch):
+    monkeypatch.setattr(O.CacheSim, "step", _mut_cache_evict_newest)
+    assert _fails_some_pin()
