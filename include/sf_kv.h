@@ -1,0 +1,210 @@
+/*
+ * sf_kv.h -- C ABI of the MI355X (gfx950) KV-cache refinement decode step.
+ *
+ * The method (StrataFlux selective precision streaming, as described on the
+ * page "StrataFlux -- Selective precision streaming -- What does it mean?"):
+ *   - the GPU keeps a resident low-bit KV cache: b-bit codes per element plus
+ *     a per-row scale (paragraph "Think about how a map app ...");
+ *   - each decode step scores every cached token against the current query
+ *     from the resident low-bit keys and picks the highest-scoring tokens per
+ *     KV head, a set shared by that head's GQA group of query heads
+ *     (paragraph "Which tiles count ...");
+ *   - the selected tokens' keys and values are refined with r extra bits that
+ *     subdivide the bin the base code already names (nested quantization,
+ *     paragraph "What travels over the link ...");
+ *   - attention runs over all tokens; unselected ones keep their low-bit value
+ *     (same paragraph; comparison table, row "StrataFlux");
+ *   - fetched refinement bits are kept and reused across steps (paragraph
+ *     "The map app also loads tiles ...").
+ *
+ * Conventions for every call:
+ *   - Pointers marked "device" are HIP device memory (hipMalloc or torch CUDA
+ *     tensors); "host" pointers are ordinary host memory.  The caller owns
+ *     every buffer it passes; the library never frees caller memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued asynchronously on it unless stated otherwise.
+ *   - Every call returns an sf_status and never throws.  Arguments are checked
+ *     before anything is enqueued: SF_ERR_INVALID_ARG / SF_ERR_UNSUPPORTED
+ *     mean nothing was written.  SF_ERR_HIP reports a HIP launch or copy
+ *     failure (sf_last_error_string() gives HIP's message).
+ *   - Inputs must be finite, with a finite max - min per row.
+ *
+ * Layouts (D = head_dim, Hkv = n_kv_heads, b = base_bits, r = refine_bits):
+ *   - a "row" is one token of one KV head: D values of K or of V;
+ *   - packed codes: each row is one little-endian bitstream, element d at bits
+ *     [w*d, w*d + w) (w = b for base codes, w = r for refinement codes), so a
+ *     row takes D*w/8 bytes;
+ *   - caches are head-major: codes [Hkv][cap][D*b/8] uint8, scales
+ *     [Hkv][cap][2] float = {lo, delta} with lo the row minimum and delta the
+ *     base bin width (max - min) / 2^b;
+ *   - a batch of sequences is packed along the token axis: sequence s owns
+ *     tokens [seq_off[s], seq_off[s+1]) of every head.
+ */
+#ifndef SF_KV_H
+#define SF_KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sf_status {
+  SF_OK = 0,
+  SF_ERR_INVALID_ARG = -1, /* bad pointer, size or combination; nothing written */
+  SF_ERR_UNSUPPORTED = -2, /* valid but not built for (e.g. head_dim != 128)  */
+  SF_ERR_HIP = -3,         /* a HIP call failed                                */
+  SF_ERR_OOM = -4,         /* device or pinned host allocation failed          */
+  SF_ERR_TIMEOUT = -5      /* a bounded wait on the refinement link expired    */
+} sf_status;
+
+/* Attention geometry and code widths.  Supported: head_dim == 128;
+ * n_q_heads % n_kv_heads == 0 with group G = n_q_heads / n_kv_heads <= 8;
+ * base_bits in {2, 3, 4}; refine_bits in [0, 8]. */
+typedef struct sf_geom {
+  int32_t head_dim;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t base_bits;
+  int32_t refine_bits;
+} sf_geom;
+
+/* Human-readable name of a status. */
+const char* sf_status_string(sf_status s);
+/* HIP's message for the last SF_ERR_HIP on this thread ("" if none). */
+const char* sf_last_error_string(void);
+
+/*
+ * sf_kv_quantize -- quantize and place rows of K or V (nested quantization,
+ * paragraph "What travels over the link ...").  Call once for K, once for V.
+ *
+ * Per row x[0..D): lo = min x, hi = max x, R = hi - lo (fp32),
+ * delta = R * 2^-b, delta_f = R * 2^-(b+r); fine code
+ * q_d = min(floor((x_d - lo) / delta_f), 2^(b+r) - 1) with one fp32
+ * subtraction and one correctly rounded fp32 division (q_d = 0 when
+ * delta_f == 0); base code c_d = q_d >> r, refinement code s_d = q_d & (2^r-1).
+ *
+ *   x            device, [n_tok][Hkv][D] fp32, token-major
+ *   n_tok        rows per head to quantize (>= 0; 0 is a no-op)
+ *   tok_begin    first token slot written in the cache, tok_begin + n_tok <= cap
+ *   cap          token capacity (row pitch) of codes/scales
+ *   codes        device, [Hkv][cap][D*b/8]; rows tok_begin.. are written
+ *   scales       device, [Hkv][cap][2]; {lo, delta} written for the same rows
+ *   refine_rows  device, [Hkv][n_tok][D*r/8] refinement codes; NULL iff r == 0
+ */
+sf_status sf_kv_quantize(const sf_geom* geom, const float* x, int64_t n_tok,
+                         int64_t tok_begin, int64_t cap, uint8_t* codes,
+                         float* scales, uint8_t* refine_rows, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Refinement store and device refinement cache.
+ *
+ * The store holds the refinement codes of every cached row (paragraph "Think
+ * about how a map app ...": the refinement bits live off the GPU, in host RAM
+ * on a machine with a dedicated GPU).  SF_TIER_DEVICE keeps them in HBM (no
+ * link, no cache); SF_TIER_HOST_PINNED keeps them in pinned host memory and
+ * gives each (sequence slot, KV head) a device cache of `cache_slots` rows
+ * that reuses fetched bits across steps (paragraph "The map app also loads
+ * tiles ..."): a selected resident is a hit; each miss is copied over the
+ * link with hipMemcpyAsync on a side stream and installed in a free slot,
+ * else in place of the resident not selected now that was selected longest
+ * ago (lower token index first).  Misses are waited for (policy "wait").
+ * All memory is allocated by sf_store_create and freed by sf_store_destroy.
+ * A store must not be used from two streams at once.
+ * ------------------------------------------------------------------------- */
+typedef struct sf_store_s* sf_store;
+
+enum { SF_TIER_DEVICE = 0, SF_TIER_HOST_PINNED = 1 };
+enum { SF_K = 0, SF_V = 1 };
+
+/* cap_tokens: token capacity (same pitch as the caches); max_seqs: batch
+ * slots with a cache of their own; cache_slots: rows per (seq, KV head) cache,
+ * must be >= every top_t used with the store (ignored for SF_TIER_DEVICE). */
+sf_status sf_store_create(const sf_geom* geom, int64_t cap_tokens, int32_t max_seqs,
+                          int32_t tier, int32_t cache_slots, sf_store* out);
+sf_status sf_store_destroy(sf_store store);
+
+/*
+ * sf_refine_store -- put refinement rows produced by sf_kv_quantize into the
+ * store at tokens [tok_begin, tok_begin + n_tok) of every head.
+ *   which        SF_K or SF_V
+ *   refine_rows  device, [Hkv][n_tok][D*r/8]
+ * Rows already cached on the device for those tokens are invalidated.
+ * For SF_TIER_HOST_PINNED the call copies device -> host and returns after
+ * the copy has completed (the stream is synchronized).
+ */
+sf_status sf_refine_store(sf_store store, int32_t which, const uint8_t* refine_rows,
+                          int64_t tok_begin, int64_t n_tok, void* stream);
+
+/* Drop every cached refinement row (next step misses on every selection). */
+sf_status sf_store_clear_cache(sf_store store, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Decode step.
+ * ------------------------------------------------------------------------- */
+typedef struct sf_step_stats {
+  int64_t selected;   /* selected (token, KV head) pairs in the step        */
+  int64_t hits;       /* of those, found in the device refinement cache    */
+  int64_t misses;     /* fetched over the link                             */
+  int64_t h2d_bytes;  /* refinement bytes copied host -> device            */
+} sf_step_stats;
+
+typedef struct sf_decode_args {
+  int32_t batch;                 /* B >= 1 sequences                                    */
+  const int64_t* seq_off_host;   /* host [B+1], nondecreasing, every sequence non-empty,
+                                    seq_off[B] <= cap                                   */
+  const int64_t* seq_off_dev;    /* device copy of the same [B+1] offsets               */
+  const float* q;                /* device [B][Hq][D] fp32 current queries              */
+  const uint8_t* k_codes;        /* device [Hkv][cap][D*b/8] base key codes             */
+  const float* k_scales;         /* device [Hkv][cap][2]                                */
+  const uint8_t* v_codes;        /* device [Hkv][cap][D*b/8] base value codes           */
+  const float* v_scales;         /* device [Hkv][cap][2]                                */
+  int64_t cap;                   /* token capacity of the caches                        */
+  sf_store store;                /* refinement store; may be NULL iff top_t == 0 or r == 0 */
+  int32_t top_t;                 /* T >= 0 tokens refined per (sequence, KV head);
+                                    all tokens when the sequence has <= T               */
+  float* out;                    /* device [B][Hq][D] fp32 attention output             */
+  int32_t* sel_out;              /* optional device [B][Hkv][T]: selected token indices
+                                    (relative to the sequence start), ascending, -1 pad */
+  float* scores_out;             /* optional device [Hkv][seq_off[B]-seq_off[0]] fp32:
+                                    the token scores the selection used                 */
+  sf_step_stats* stats;          /* optional host; filled when the call returns         */
+  void* workspace;               /* device scratch of sf_decode_workspace_size() bytes  */
+  size_t workspace_bytes;
+  int32_t flags;                 /* 0 (reserved)                                        */
+  void* score_events[2];         /* optional hipEvent_t pair recorded on `stream` just
+                                    before and after the score/attention kernel (both
+                                    NULL = none): lets a caller time that kernel       */
+} sf_decode_args;
+
+/* Scratch needed by sf_decode_step for this batch shape.
+ *   total_tokens   seq_off[B] - seq_off[0]
+ *   max_seq_tokens the longest sequence */
+sf_status sf_decode_workspace_size(const sf_geom* geom, int32_t batch, int64_t total_tokens,
+                                   int64_t max_seq_tokens, int32_t top_t, size_t* bytes);
+
+/*
+ * sf_decode_step -- one decode step of one layer for a packed batch.
+ *
+ * For each sequence s and KV head k (query head h belongs to KV head
+ * floor(h / G)):
+ *   1. score every token i of s from the resident base keys:
+ *      s_i = max over h in k's group of q_h . Khat_i / sqrt(D), where
+ *      Khat = lo + (c + 1/2) * delta (centre of the bin the code names);
+ *   2. select the T highest scores (ties to the lower token index);
+ *   3. refine the selected K and V rows with the stored r-bit codes:
+ *      Ktilde = lo + c * delta + (s + 1/2) * delta / 2^r;
+ *   4. out_h = softmax over all tokens of q_h . K* / sqrt(D), applied to V*,
+ *      with K*, V* refined for selected tokens and base-precision otherwise.
+ * Device-tier stores and T == 0 need no host round trip; a host-pinned store
+ * synchronizes the stream once per call to learn which rows to fetch.
+ * The workspace need not be initialised; its contents are undefined after.
+ */
+sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* args, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SF_KV_H */

@@ -214,14 +214,17 @@ class HeadResult:
     out: np.ndarray       # [G][D] fp64
 
 
-def decode_head(q_group: np.ndarray, kc: QuantRows, vc: QuantRows, t: int) -> HeadResult:
+def decode_head(q_group: np.ndarray, kc: QuantRows, vc: QuantRows, t: int,
+                sel: Optional[np.ndarray] = None) -> HeadResult:
     """One (sequence, KV head): score, select, refine the selection, attend.
 
-    ``kc``/``vc`` hold the head's rows [N][D]."""
+    ``kc``/``vc`` hold the head's rows [N][D].  ``sel`` overrides the
+    selection (used to check the attention step for another valid selection
+    when two selections differ only at a tie within the allowed tolerance)."""
     k_hat = dequant_base(kc)
     v_hat = dequant_base(vc)
     s = token_scores(q_group, k_hat)
-    sel = select_top_t(s, t)
+    sel = select_top_t(s, t) if sel is None else np.sort(np.asarray(sel, dtype=np.int64))
     k_star = k_hat.copy()
     v_star = v_hat.copy()
     if sel.size:

@@ -1,0 +1,176 @@
+"""Thin ctypes binding of the C ABI in include/sf_kv.h.
+
+Same names as the C entry points; argument marshalling only (torch tensors ->
+device pointers, the current HIP stream -> void*).  Every step of the decode
+path runs in the HIP library; there is no fallback: if libsf_kv.so is not
+built, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsf_kv.so")
+
+SF_OK, SF_ERR_INVALID_ARG, SF_ERR_UNSUPPORTED, SF_ERR_HIP, SF_ERR_OOM, SF_ERR_TIMEOUT = 0, -1, -2, -3, -4, -5
+SF_TIER_DEVICE, SF_TIER_HOST_PINNED = 0, 1
+SF_K, SF_V = 0, 1
+
+c_i32, c_i64, c_vp, c_size = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+
+EXPORTS = ("sf_status_string", "sf_last_error_string", "sf_kv_quantize", "sf_store_create",
+           "sf_store_destroy", "sf_refine_store", "sf_store_clear_cache", "sf_decode_workspace_size",
+           "sf_decode_step")
+
+
+class sf_geom(ctypes.Structure):
+    _fields_ = [("head_dim", c_i32), ("n_q_heads", c_i32), ("n_kv_heads", c_i32),
+                ("base_bits", c_i32), ("refine_bits", c_i32)]
+
+
+class sf_step_stats(ctypes.Structure):
+    _fields_ = [("selected", c_i64), ("hits", c_i64), ("misses", c_i64), ("h2d_bytes", c_i64)]
+
+    def as_dict(self):
+        return {k: int(getattr(self, k)) for k, _ in self._fields_}
+
+
+class sf_decode_args(ctypes.Structure):
+    _fields_ = [("batch", c_i32), ("seq_off_host", ctypes.POINTER(c_i64)), ("seq_off_dev", c_vp),
+                ("q", c_vp), ("k_codes", c_vp), ("k_scales", c_vp), ("v_codes", c_vp),
+                ("v_scales", c_vp), ("cap", c_i64), ("store", c_vp), ("top_t", c_i32), ("out", c_vp),
+                ("sel_out", c_vp), ("scores_out", c_vp), ("stats", ctypes.POINTER(sf_step_stats)),
+                ("workspace", c_vp), ("workspace_bytes", c_size), ("flags", c_i32),
+                ("score_events", c_vp * 2)]
+
+
+class SfError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        lib = _LIB
+        text = lib.sf_status_string(status).decode() if lib else str(status)
+        detail = lib.sf_last_error_string().decode() if lib else ""
+        super().__init__(f"{what}: {text}" + (f" ({detail})" if detail else ""))
+        self.status = status
+
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libsf_kv.so (after torch, so both share one HIP runtime)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    import torch  # noqa: F401  -- binds the library to torch's HIP runtime
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                           "(run `python -m selective_kv_cache_amd.build`)")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.sf_status_string.restype = ctypes.c_char_p
+    lib.sf_status_string.argtypes = [c_i32]
+    lib.sf_last_error_string.restype = ctypes.c_char_p
+    lib.sf_last_error_string.argtypes = []
+    G = ctypes.POINTER(sf_geom)
+    lib.sf_kv_quantize.argtypes = [G, c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp]
+    lib.sf_store_create.argtypes = [G, c_i64, c_i32, c_i32, c_i32, ctypes.POINTER(c_vp)]
+    lib.sf_store_destroy.argtypes = [c_vp]
+    lib.sf_refine_store.argtypes = [c_vp, c_i32, c_vp, c_i64, c_i64, c_vp]
+    lib.sf_store_clear_cache.argtypes = [c_vp, c_vp]
+    lib.sf_decode_workspace_size.argtypes = [G, c_i32, c_i64, c_i64, c_i32, ctypes.POINTER(c_size)]
+    lib.sf_decode_step.argtypes = [G, ctypes.POINTER(sf_decode_args), c_vp]
+    for name in EXPORTS:
+        if name not in ("sf_status_string", "sf_last_error_string"):
+            getattr(lib, name).restype = c_i32
+    _LIB = lib
+    return lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != SF_OK:
+        raise SfError(status, what)
+
+
+def _ptr(t) -> int:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def geom(head_dim: int, n_q_heads: int, n_kv_heads: int, base_bits: int, refine_bits: int) -> sf_geom:
+    return sf_geom(head_dim, n_q_heads, n_kv_heads, base_bits, refine_bits)
+
+
+def sf_kv_quantize(g: sf_geom, x, n_tok: int, tok_begin: int, cap: int, codes, scales, refine_rows=None,
+                   stream=None) -> None:
+    lib = load()
+    _check(lib.sf_kv_quantize(ctypes.byref(g), _ptr(x), n_tok, tok_begin, cap, _ptr(codes), _ptr(scales),
+                              _ptr(refine_rows), _stream(stream)), "sf_kv_quantize")
+
+
+def sf_store_create(g: sf_geom, cap_tokens: int, max_seqs: int, tier: int, cache_slots: int) -> int:
+    lib = load()
+    h = c_vp()
+    _check(lib.sf_store_create(ctypes.byref(g), cap_tokens, max_seqs, tier, cache_slots, ctypes.byref(h)),
+           "sf_store_create")
+    return h.value
+
+
+def sf_store_destroy(store: int) -> None:
+    _check(load().sf_store_destroy(store), "sf_store_destroy")
+
+
+def sf_refine_store(store: int, which: int, refine_rows, tok_begin: int, n_tok: int, stream=None) -> None:
+    _check(load().sf_refine_store(store, which, _ptr(refine_rows), tok_begin, n_tok, _stream(stream)),
+           "sf_refine_store")
+
+
+def sf_store_clear_cache(store: int, stream=None) -> None:
+    _check(load().sf_store_clear_cache(store, _stream(stream)), "sf_store_clear_cache")
+
+
+def sf_decode_workspace_size(g: sf_geom, batch: int, total_tokens: int, max_seq_tokens: int,
+                             top_t: int) -> int:
+    n = c_size()
+    _check(load().sf_decode_workspace_size(ctypes.byref(g), batch, total_tokens, max_seq_tokens, top_t,
+                                           ctypes.byref(n)), "sf_decode_workspace_size")
+    return int(n.value)
+
+
+def sf_decode_step(g: sf_geom, *, seq_off_host: Sequence[int], seq_off_dev, q, k_codes, k_scales, v_codes,
+                   v_scales, cap: int, store: Optional[int], top_t: int, out, workspace, sel_out=None,
+                   scores_out=None, want_stats: bool = False, score_events=None, stream=None):
+    """One decode step; returns the step statistics as a dict when asked."""
+    off = np.ascontiguousarray(np.asarray(seq_off_host, dtype=np.int64))
+    a = sf_decode_args()
+    a.batch = len(off) - 1
+    a.seq_off_host = off.ctypes.data_as(ctypes.POINTER(c_i64))
+    a.seq_off_dev = _ptr(seq_off_dev)
+    a.q, a.k_codes, a.k_scales = _ptr(q), _ptr(k_codes), _ptr(k_scales)
+    a.v_codes, a.v_scales = _ptr(v_codes), _ptr(v_scales)
+    a.cap, a.store, a.top_t = cap, store, top_t
+    a.out, a.sel_out, a.scores_out = _ptr(out), _ptr(sel_out), _ptr(scores_out)
+    st = sf_step_stats()
+    a.stats = ctypes.pointer(st) if want_stats else None
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    a.flags = 0
+    if score_events is not None:
+        a.score_events[0], a.score_events[1] = (e.cuda_event if hasattr(e, "cuda_event") else e
+                                                for e in score_events)
+    _check(load().sf_decode_step(ctypes.byref(g), ctypes.byref(a), _stream(stream)), "sf_decode_step")
+    return st.as_dict() if want_stats else None

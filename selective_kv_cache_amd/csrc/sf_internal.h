@@ -1,0 +1,99 @@
+// Internal declarations of the HIP library behind include/sf_kv.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sf_kv.h"
+
+namespace sfk {
+
+constexpr int kHeadDim = 128;            // the kernels are specialised for D = 128
+constexpr int kHistBits = 12;            // first-level score histogram: top 12 key bits
+constexpr int kHistBins = 1 << kHistBits;
+constexpr int kPartStride = kHeadDim + 2;  // one partial: acc[D], m, l
+
+void set_hip_error(hipError_t e, const char* where);
+void clear_error();
+
+// Order-preserving map of an fp32 score to uint32 (larger score -> larger
+// key); -0 and +0 map to the same key.
+__host__ __device__ inline uint32_t score_key(float s) {
+  uint32_t u = __builtin_bit_cast(uint32_t, s);
+  if ((u << 1) == 0) return 0x80000000u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Split plan of one decode step: the token axis of every sequence is cut into
+// splits of `split` tokens (score/attention partials) and the selection of
+// every sequence into chunks of `corr_chunk` tokens (refinement corrections).
+struct Plan {
+  int32_t batch;
+  int64_t total_tokens;
+  int64_t max_seq_tokens;
+  int32_t split;          // tokens per score/attention work-group
+  int32_t n_split;        // total splits over the batch
+  int32_t sel_chunk;      // tokens per selection work-group
+  int32_t n_sel_chunk;    // total selection chunks over the batch
+  int32_t corr_chunk;     // selected tokens per correction work-group
+  int32_t n_corr_chunk;   // total correction chunks (upper bound for sizing)
+  int32_t top_t;
+};
+
+// Workspace carve-out (byte offsets from the workspace base).
+struct Carve {
+  size_t scores, hist, counters, cand, bitmap, sel, part, corr, miss, total;
+};
+
+int32_t choose_split(int64_t total_tokens, int32_t n_kv_heads);
+Carve carve(const sf_geom& g, int32_t batch, int64_t total_tokens, int64_t max_seq_tokens,
+            int32_t top_t, int32_t n_split_bound, int32_t n_corr_bound);
+
+}  // namespace sfk
+
+// Geometry check shared by every entry point.
+sf_status sf_check_geom(const sf_geom* g);
+
+// Store internals, shared by the decode path.
+struct sf_store_s {
+  sf_geom g;
+  int64_t cap;
+  int32_t max_seqs;
+  int32_t tier;
+  int32_t slots;
+  int32_t row_bytes;       // refinement row: D * r / 8
+  int device;
+  // refinement rows [2][Hkv][cap][row_bytes]: device tier in HBM, host tier pinned
+  uint8_t* dev_rows;
+  uint8_t* host_rows;
+  // host tier: device refinement cache per (sequence slot, KV head)
+  uint8_t* cache_data;     // [max_seqs][Hkv][slots][2][row_bytes]
+  int32_t* tok_slot;       // [Hkv][cap] slot caching the token, -1 if none
+  int32_t* slot_tok;       // [max_seqs][Hkv][slots] token in the slot, -1 if free
+  int32_t* stamp;          // [max_seqs][Hkv][slots] last step the token was selected
+  int32_t step;
+  // staging for fetched rows and the miss lists
+  uint8_t* h_stage;        // pinned [max_seqs*Hkv*slots][2][row_bytes]
+  uint8_t* d_stage;        // device, same
+  int32_t* h_miss;         // pinned: [max_seqs*Hkv] counts, then [max_seqs*Hkv][slots] tokens
+  hipStream_t side;
+  hipEvent_t ev_side;
+};
+
+#define SF_HIP_CHECK(call)                                   \
+  do {                                                       \
+    hipError_t e_ = (call);                                  \
+    if (e_ != hipSuccess) {                                  \
+      sfk::set_hip_error(e_, #call);                         \
+      return SF_ERR_HIP;                                     \
+    }                                                        \
+  } while (0)
+
+#define SF_LAUNCH_CHECK(what)                                \
+  do {                                                       \
+    hipError_t e_ = hipGetLastError();                       \
+    if (e_ != hipSuccess) {                                  \
+      sfk::set_hip_error(e_, what);                          \
+      return SF_ERR_HIP;                                     \
+    }                                                        \
+  } while (0)

@@ -1,0 +1,363 @@
+// Refinement store, device refinement cache and the host-tier fetch.
+//
+// Method: page "StrataFlux -- Selective precision streaming -- What does it
+// mean?": refinement bits sit off the GPU, in host RAM on a machine with a
+// dedicated GPU (paragraph "Think about how a map app ..."); only the bits of
+// the selected tokens cross the link (comparison table, row "StrataFlux");
+// fetched bits are kept and reused across steps because selections repeat
+// (paragraph "The map app also loads tiles ...").
+//
+// Host tier, per decode step (after the selection is known):
+//   cache_lookup  (device, one work-group per (sequence, KV head)): a
+//                 selected token already cached is a hit and is stamped with
+//                 the step; misses, in ascending token order, take free slots
+//                 first, then the slots of residents not selected now, oldest
+//                 stamp first (lower token index first); the miss list
+//                 (token, slot) goes to the workspace
+//   host          copies the miss lists device -> pinned host, gathers the K
+//                 and V refinement rows of every miss from the pinned store
+//                 into a pinned staging buffer, and copies it host -> device
+//                 with hipMemcpyAsync on the store's side stream
+//   cache_install (device, after the side stream's event): rows -> slots
+// Policy on a miss: wait (the step uses every selected refinement).
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "sf_decode_kernels.h"
+
+namespace sfk {
+
+__global__ void fill_i32(int32_t* p, int64_t n, int32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+// Forget cached rows of tokens [t0, t1) (their refinement was rewritten).
+__global__ void cache_invalidate(int32_t* slot_tok, int32_t* tok_slot, int64_t n_slots_total, int32_t slots,
+                                 int32_t hkv, int64_t cap, int64_t t0, int64_t t1) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_slots_total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int32_t tok = slot_tok[i];
+    if (tok >= t0 && tok < t1) {
+      const int64_t kvh = (i / slots) % hkv;
+      tok_slot[kvh * cap + tok] = -1;
+      slot_tok[i] = -1;
+    }
+  }
+}
+
+constexpr int kLookupThreads = 1024;
+constexpr int kMaxSlots = 4096;   // keeps the lookup's sort in LDS (<= 64 KiB)
+
+// One work-group per (sequence, KV head).  Dynamic LDS: sort keys (pow2 >=
+// slots) as uint64 plus one miss flag per selected token.
+__global__ void __launch_bounds__(kLookupThreads)
+cache_lookup(DecodeParams p, int32_t* slot_tok, int32_t* stamp, int32_t* tok_slot, int32_t step, int32_t sort_n,
+             int32_t* miss) {
+  extern __shared__ uint64_t keys[];
+  uint32_t* flag = reinterpret_cast<uint32_t*>(keys + sort_n);   // [slots]: 1 = selected resident
+  int32_t* mrank = reinterpret_cast<int32_t*>(flag + p.slots);    // [top_t]: rank among misses, -1 = hit
+  __shared__ uint32_t cnt[kLookupThreads];
+
+  const int tid = threadIdx.x;
+  const int64_t sk = blockIdx.x;
+  const int seq = (int)(sk / p.hkv), kvh = (int)(sk % p.hkv);
+  const int64_t a = p.seq_off[seq];
+  const int64_t n = p.seq_off[seq + 1] - a;
+  const int32_t tn = (int32_t)(n < p.top_t ? n : p.top_t);
+  const int32_t* sel = p.sel + sk * p.top_t;
+  int32_t* st_tok = slot_tok + sk * p.slots;
+  int32_t* st_stamp = stamp + sk * p.slots;
+  int32_t* ts = tok_slot + (int64_t)kvh * p.cap;
+
+  for (int i = tid; i < p.slots; i += kLookupThreads) flag[i] = 0u;
+  __syncthreads();
+  // hits are stamped; misses flagged
+  for (int j = tid; j < tn; j += kLookupThreads) {
+    const int64_t g = a + sel[j];
+    const int32_t slot = ts[g];
+    if (slot >= 0) {
+      st_stamp[slot] = step;
+      flag[slot] = 1u;
+      mrank[j] = -1;
+    } else {
+      mrank[j] = 0;
+    }
+  }
+  __syncthreads();
+  // rank the misses in ascending token order (the selection is ascending)
+  const int per = (tn + kLookupThreads - 1) / kLookupThreads;
+  const int j0 = tid * per, j1 = std::min(j0 + per, (int)tn);
+  uint32_t c = 0;
+  for (int j = j0; j < j1; ++j) c += (mrank[j] == 0);
+  cnt[tid] = c;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t run = 0;
+    for (int t = 0; t < kLookupThreads; ++t) {
+      const uint32_t v = cnt[t];
+      cnt[t] = run;
+      run += v;
+    }
+    miss[sk * 2 * (int64_t)(p.top_t + 1)] = (int32_t)run;
+  }
+  __syncthreads();
+  uint32_t rk = cnt[tid];
+  for (int j = j0; j < j1; ++j)
+    if (mrank[j] == 0) mrank[j] = (int32_t)(rk++);
+  // victim order: free slots (by slot), then non-selected residents by (stamp, token)
+  for (int i = tid; i < sort_n; i += kLookupThreads) {
+    uint64_t k = ~0ull;
+    if (i < p.slots) {
+      const int32_t tok = st_tok[i];
+      if (tok < 0)
+        k = (uint64_t)i;
+      else if (!flag[i])
+        k = (1ull << 62) | ((uint64_t)(uint32_t)(st_stamp[i] + 1) << 31) | (uint64_t)(uint32_t)tok;
+    }
+    keys[i] = k;
+  }
+  __syncthreads();
+  for (int size = 2; size <= sort_n; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < sort_n; i += kLookupThreads) {
+        const int partner = i ^ stride;
+        if (partner > i) {
+          const bool up = (i & size) == 0;
+          const uint64_t x = keys[i], y = keys[partner];
+          if ((x > y) == up) {
+            keys[i] = y;
+            keys[partner] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // install the mapping of each miss into its victim slot
+  int32_t* ml = miss + sk * 2 * (int64_t)(p.top_t + 1) + 2;
+  for (int j = tid; j < tn; j += kLookupThreads) {
+    const int32_t k = mrank[j];
+    if (k < 0) continue;
+    const uint64_t key = keys[k];
+    if (key == ~0ull) continue;   // fewer victims than misses: cannot happen with slots >= T
+    int32_t slot;
+    if (key < (1ull << 62)) {
+      slot = (int32_t)key;
+    } else {
+      const int32_t old = (int32_t)(key & 0x7FFFFFFFull);
+      slot = ts[old];
+      ts[old] = -1;
+    }
+    const int32_t g = (int32_t)(a + sel[j]);
+    st_tok[slot] = g;
+    st_stamp[slot] = step;
+    ts[g] = slot;
+    ml[2 * k] = g;
+    ml[2 * k + 1] = slot;
+  }
+}
+
+// Copy staged rows into their cache slots: one work-group per (sequence, KV
+// head); `first` gives the staging offset of each group's misses.
+__global__ void __launch_bounds__(256)
+cache_install(const int32_t* miss, const int32_t* first, int32_t top_t, int32_t slots, int32_t rb,
+              const uint8_t* stage, uint8_t* cache_data) {
+  const int64_t sk = blockIdx.x;
+  const int32_t* m = miss + sk * 2 * (int64_t)(top_t + 1);
+  const int32_t nm = m[0];
+  const int64_t f = first[sk];
+  const int words = rb / 4;   // per row
+  for (int64_t i = threadIdx.x; i < (int64_t)nm * 2 * words; i += blockDim.x) {
+    const int64_t k = i / (2 * words);
+    const int64_t rest = i - k * 2 * words;
+    const int32_t slot = m[2 + 2 * k + 1];
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(stage + (f + k) * 2 * (int64_t)rb);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(cache_data + ((sk * slots + slot) * 2) * (int64_t)rb);
+    dst[rest] = src[rest];
+  }
+}
+
+}  // namespace sfk
+
+using namespace sfk;
+
+static void free_store(sf_store_s* s) {
+  if (!s) return;
+  if (s->dev_rows) (void)hipFree(s->dev_rows);
+  if (s->host_rows) (void)hipHostFree(s->host_rows);
+  if (s->cache_data) (void)hipFree(s->cache_data);
+  if (s->tok_slot) (void)hipFree(s->tok_slot);
+  if (s->slot_tok) (void)hipFree(s->slot_tok);
+  if (s->stamp) (void)hipFree(s->stamp);
+  if (s->h_stage) (void)hipHostFree(s->h_stage);
+  if (s->d_stage) (void)hipFree(s->d_stage);
+  if (s->h_miss) (void)hipHostFree(s->h_miss);
+  if (s->ev_side) (void)hipEventDestroy(s->ev_side);
+  if (s->side) (void)hipStreamDestroy(s->side);
+  delete s;
+}
+
+extern "C" sf_status sf_store_create(const sf_geom* geom, int64_t cap_tokens, int32_t max_seqs, int32_t tier,
+                                     int32_t cache_slots, sf_store* out) {
+  clear_error();
+  sf_status st = sf_check_geom(geom);
+  if (st != SF_OK) return st;
+  if (!out || cap_tokens <= 0 || max_seqs <= 0 || cap_tokens > 0x7fffffffLL) return SF_ERR_INVALID_ARG;
+  if (tier != SF_TIER_DEVICE && tier != SF_TIER_HOST_PINNED) return SF_ERR_INVALID_ARG;
+  if (geom->refine_bits == 0) return SF_ERR_INVALID_ARG;
+  if (tier == SF_TIER_HOST_PINNED && (cache_slots <= 0 || cache_slots > kMaxSlots)) return SF_ERR_INVALID_ARG;
+  *out = nullptr;
+  sf_store_s* s = new sf_store_s();
+  memset(s, 0, sizeof(*s));
+  s->g = *geom;
+  s->cap = cap_tokens;
+  s->max_seqs = max_seqs;
+  s->tier = tier;
+  s->slots = tier == SF_TIER_HOST_PINNED ? cache_slots : 0;
+  s->row_bytes = geom->head_dim * geom->refine_bits / 8;
+  const int64_t hkv = geom->n_kv_heads;
+  const size_t rows_bytes = (size_t)2 * hkv * cap_tokens * s->row_bytes;
+  if (hipGetDevice(&s->device) != hipSuccess) {
+    delete s;
+    return SF_ERR_HIP;
+  }
+#define SF_ALLOC(call)          \
+  if ((call) != hipSuccess) {   \
+    (void)hipGetLastError();    \
+    free_store(s);              \
+    return SF_ERR_OOM;          \
+  }
+  if (tier == SF_TIER_DEVICE) {
+    SF_ALLOC(hipMalloc((void**)&s->dev_rows, rows_bytes));
+    SF_ALLOC(hipMemset(s->dev_rows, 0, rows_bytes));
+  } else {
+    const int64_t nslots = (int64_t)max_seqs * hkv * s->slots;
+    SF_ALLOC(hipHostMalloc((void**)&s->host_rows, rows_bytes, hipHostMallocDefault));
+    memset(s->host_rows, 0, rows_bytes);
+    SF_ALLOC(hipMalloc((void**)&s->cache_data, (size_t)nslots * 2 * s->row_bytes));
+    SF_ALLOC(hipMalloc((void**)&s->tok_slot, (size_t)hkv * cap_tokens * 4));
+    SF_ALLOC(hipMalloc((void**)&s->slot_tok, (size_t)nslots * 4));
+    SF_ALLOC(hipMalloc((void**)&s->stamp, (size_t)nslots * 4));
+    SF_ALLOC(hipMemset(s->tok_slot, 0xFF, (size_t)hkv * cap_tokens * 4));
+    SF_ALLOC(hipMemset(s->slot_tok, 0xFF, (size_t)nslots * 4));
+    SF_ALLOC(hipMemset(s->stamp, 0xFF, (size_t)nslots * 4));
+    SF_ALLOC(hipHostMalloc((void**)&s->h_stage, (size_t)nslots * 2 * s->row_bytes, hipHostMallocDefault));
+    SF_ALLOC(hipMalloc((void**)&s->d_stage, (size_t)nslots * 2 * s->row_bytes));
+    SF_ALLOC(hipHostMalloc((void**)&s->h_miss, (size_t)max_seqs * hkv * (2 * (s->slots + 1) + 1) * 4,
+                           hipHostMallocDefault));
+    SF_ALLOC(hipStreamCreateWithFlags(&s->side, hipStreamNonBlocking));
+    SF_ALLOC(hipEventCreateWithFlags(&s->ev_side, hipEventDisableTiming));
+  }
+#undef SF_ALLOC
+  *out = s;
+  return SF_OK;
+}
+
+extern "C" sf_status sf_store_destroy(sf_store store) {
+  clear_error();
+  if (!store) return SF_ERR_INVALID_ARG;
+  (void)hipDeviceSynchronize();
+  free_store(store);
+  return SF_OK;
+}
+
+extern "C" sf_status sf_refine_store(sf_store s, int32_t which, const uint8_t* refine_rows, int64_t tok_begin,
+                                     int64_t n_tok, void* stream) {
+  clear_error();
+  if (!s || (which != SF_K && which != SF_V) || tok_begin < 0 || n_tok < 0 || tok_begin + n_tok > s->cap)
+    return SF_ERR_INVALID_ARG;
+  if (n_tok == 0) return SF_OK;
+  if (!refine_rows) return SF_ERR_INVALID_ARG;
+  hipStream_t hs = (hipStream_t)stream;
+  const int64_t hkv = s->g.n_kv_heads;
+  const size_t rb = s->row_bytes;
+  const size_t width = (size_t)n_tok * rb;
+  if (s->tier == SF_TIER_DEVICE) {
+    uint8_t* dst = s->dev_rows + ((size_t)which * hkv * s->cap + tok_begin) * rb;
+    SF_HIP_CHECK(hipMemcpy2DAsync(dst, (size_t)s->cap * rb, refine_rows, width, width, hkv,
+                                  hipMemcpyDeviceToDevice, hs));
+    return SF_OK;
+  }
+  uint8_t* dst = s->host_rows + ((size_t)which * hkv * s->cap + tok_begin) * rb;
+  SF_HIP_CHECK(hipMemcpy2DAsync(dst, (size_t)s->cap * rb, refine_rows, width, width, hkv,
+                                hipMemcpyDeviceToHost, hs));
+  const int64_t nslots = (int64_t)s->max_seqs * hkv * s->slots;
+  hipLaunchKernelGGL(cache_invalidate, dim3((unsigned)std::min<int64_t>((nslots + 255) / 256, 1024)), dim3(256), 0,
+                     hs, s->slot_tok, s->tok_slot, nslots, s->slots, (int32_t)hkv, s->cap, tok_begin,
+                     tok_begin + n_tok);
+  SF_LAUNCH_CHECK("cache_invalidate");
+  SF_HIP_CHECK(hipStreamSynchronize(hs));
+  return SF_OK;
+}
+
+extern "C" sf_status sf_store_clear_cache(sf_store s, void* stream) {
+  clear_error();
+  if (!s) return SF_ERR_INVALID_ARG;
+  if (s->tier != SF_TIER_HOST_PINNED) return SF_OK;
+  hipStream_t hs = (hipStream_t)stream;
+  const int64_t hkv = s->g.n_kv_heads;
+  const int64_t nslots = (int64_t)s->max_seqs * hkv * s->slots;
+  hipLaunchKernelGGL(fill_i32, dim3(1024), dim3(256), 0, hs, s->tok_slot, hkv * s->cap, -1);
+  hipLaunchKernelGGL(fill_i32, dim3(256), dim3(256), 0, hs, s->slot_tok, nslots, -1);
+  hipLaunchKernelGGL(fill_i32, dim3(256), dim3(256), 0, hs, s->stamp, nslots, -1);
+  SF_LAUNCH_CHECK("fill_i32");
+  return SF_OK;
+}
+
+// Host tier: look up the selection in the device cache, fetch the misses over
+// the link and install them.  Synchronizes `st` once to read the miss lists.
+sf_status sf_store_fetch(sf_store s, const DecodeParams& p, int32_t* miss_dev, hipStream_t st,
+                         sf_step_stats* stats) {
+  const int32_t B = p.batch, hkv = p.hkv;
+  const int64_t groups = (int64_t)B * hkv;
+  int sort_n = 1;
+  while (sort_n < s->slots) sort_n <<= 1;
+  const size_t lds = (size_t)sort_n * 8 + (size_t)s->slots * 4 + (size_t)p.top_t * 4;
+  const int32_t step = s->step++;
+  hipLaunchKernelGGL(cache_lookup, dim3((unsigned)groups), dim3(kLookupThreads), lds, st, p, s->slot_tok,
+                     s->stamp, s->tok_slot, step, sort_n, miss_dev);
+  SF_LAUNCH_CHECK("cache_lookup");
+  const size_t stride = 2 * (size_t)(p.top_t + 1);
+  SF_HIP_CHECK(hipMemcpyAsync(s->h_miss, miss_dev, groups * stride * 4, hipMemcpyDeviceToHost, st));
+  SF_HIP_CHECK(hipStreamSynchronize(st));
+
+  const int64_t rb = s->row_bytes;
+  const int64_t cap = s->cap;
+  std::vector<int32_t> first(groups);
+  int64_t total = 0;
+  for (int64_t g = 0; g < groups; ++g) {
+    const int32_t* m = s->h_miss + g * stride;
+    const int kvh = (int)(g % hkv);
+    first[g] = (int32_t)total;
+    for (int32_t k = 0; k < m[0]; ++k) {
+      const int64_t tok = m[2 + 2 * k];
+      uint8_t* dst = s->h_stage + (total + k) * 2 * rb;
+      memcpy(dst, s->host_rows + ((int64_t)(0 * hkv + kvh) * cap + tok) * rb, rb);
+      memcpy(dst + rb, s->host_rows + ((int64_t)(1 * hkv + kvh) * cap + tok) * rb, rb);
+    }
+    total += m[0];
+  }
+  if (total > 0) {
+    SF_HIP_CHECK(hipMemcpyAsync(s->d_stage, s->h_stage, (size_t)total * 2 * rb, hipMemcpyHostToDevice, s->side));
+    SF_HIP_CHECK(hipEventRecord(s->ev_side, s->side));
+    SF_HIP_CHECK(hipStreamWaitEvent(st, s->ev_side, 0));
+  }
+  if (stats) {
+    stats->misses = total;
+    stats->h2d_bytes = total * 2 * rb;
+  }
+  if (total > 0) {
+    // staging offsets per group, written behind the miss lists in the workspace
+    int32_t* h_first = s->h_miss + groups * stride;
+    memcpy(h_first, first.data(), groups * 4);
+    int32_t* d_first = miss_dev + groups * stride;
+    SF_HIP_CHECK(hipMemcpyAsync(d_first, h_first, groups * 4, hipMemcpyHostToDevice, st));
+    hipLaunchKernelGGL(cache_install, dim3((unsigned)groups), dim3(256), 0, st, miss_dev, d_first, p.top_t,
+                       s->slots, (int32_t)rb, s->d_stage, s->cache_data);
+    SF_LAUNCH_CHECK("cache_install");
+  }
+  return SF_OK;
+}

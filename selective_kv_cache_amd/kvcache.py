@@ -1,0 +1,92 @@
+"""Device buffers of one layer's resident KV cache and its refinement store.
+
+Marshalling only: allocates torch tensors in the layouts include/sf_kv.h
+documents and forwards to the C entry points (quantization, store, decode).
+"""
+from __future__ import annotations
+
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import binding as B
+
+
+class LayerCache:
+    """Codes and scales of K and V for one layer ([Hkv][cap][...]) plus the
+    refinement store.  ``tier`` is binding.SF_TIER_DEVICE or SF_TIER_HOST_PINNED."""
+
+    def __init__(self, g: B.sf_geom, cap: int, device="cuda", tier: int = B.SF_TIER_DEVICE,
+                 max_seqs: int = 1, cache_slots: int = 0):
+        self.g, self.cap, self.device, self.tier = g, cap, torch.device(device), tier
+        hkv, d, b, r = g.n_kv_heads, g.head_dim, g.base_bits, g.refine_bits
+        mk = lambda shape, dt: torch.empty(shape, dtype=dt, device=self.device)
+        self.k_codes = mk((hkv, cap, d * b // 8), torch.uint8)
+        self.v_codes = mk((hkv, cap, d * b // 8), torch.uint8)
+        self.k_scales = mk((hkv, cap, 2), torch.float32)
+        self.v_scales = mk((hkv, cap, 2), torch.float32)
+        self.store = B.sf_store_create(g, cap, max_seqs, tier, cache_slots) if r > 0 else None
+
+    def append(self, k: torch.Tensor, v: torch.Tensor, tok_begin: int, keep_refine: bool = False):
+        """Quantize token-major [n][Hkv][D] fp32 K and V into tokens
+        [tok_begin, tok_begin + n) and put their refinement rows in the store.
+        Returns the refinement rows (K, V) when ``keep_refine``."""
+        n = k.shape[0]
+        r = self.g.refine_bits
+        hkv, d = self.g.n_kv_heads, self.g.head_dim
+        out = []
+        for x, codes, scales, which in ((k, self.k_codes, self.k_scales, B.SF_K),
+                                        (v, self.v_codes, self.v_scales, B.SF_V)):
+            x = x.contiguous()
+            rr = torch.empty((hkv, n, d * r // 8), dtype=torch.uint8, device=self.device) if r else None
+            B.sf_kv_quantize(self.g, x, n, tok_begin, self.cap, codes, scales, rr)
+            if r:
+                B.sf_refine_store(self.store, which, rr, tok_begin, n)
+            out.append(rr)
+        return tuple(out) if keep_refine else None
+
+    def clear_cache(self):
+        if self.store is not None:
+            B.sf_store_clear_cache(self.store)
+
+    def close(self):
+        if self.store is not None:
+            B.sf_store_destroy(self.store)
+            self.store = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Decoder:
+    """Workspace and offsets for decode steps of one batch shape."""
+
+    def __init__(self, g: B.sf_geom, seq_off: Sequence[int], top_t: int, device="cuda"):
+        self.g, self.top_t = g, top_t
+        self.device = torch.device(device)
+        self.seq_off = np.asarray(seq_off, dtype=np.int64)
+        lens = np.diff(self.seq_off)
+        self.batch = len(lens)
+        self.total = int(self.seq_off[-1] - self.seq_off[0])
+        self.max_seq = int(lens.max())
+        self.seq_off_dev = torch.as_tensor(self.seq_off, device=self.device)
+        nbytes = B.sf_decode_workspace_size(g, self.batch, self.total, self.max_seq, top_t)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+
+    def step(self, cache: LayerCache, q: torch.Tensor, out: Optional[torch.Tensor] = None,
+             sel_out: Optional[torch.Tensor] = None, scores_out: Optional[torch.Tensor] = None,
+             want_stats: bool = False, score_events=None, stream=None):
+        if out is None:
+            out = torch.empty((self.batch, self.g.n_q_heads, self.g.head_dim), dtype=torch.float32,
+                              device=self.device)
+        st = B.sf_decode_step(self.g, seq_off_host=self.seq_off, seq_off_dev=self.seq_off_dev, q=q,
+                              k_codes=cache.k_codes, k_scales=cache.k_scales, v_codes=cache.v_codes,
+                              v_scales=cache.v_scales, cap=cache.cap, store=cache.store,
+                              top_t=self.top_t, out=out, workspace=self.workspace, sel_out=sel_out,
+                              scores_out=scores_out, want_stats=want_stats, score_events=score_events,
+                              stream=stream)
+        return (out, st) if want_stats else out

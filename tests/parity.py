@@ -1,0 +1,132 @@
+"""Shared helpers of the GPU parity tests: run one layer through the HIP path
+and through the oracle on the same seeded inputs, and compare."""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Optional, Sequence, Tuple
+
+import numpy as np
+
+import oracle.kv_oracle as O
+from selective_kv_cache_amd import workloads as W
+
+OUT_ATOL = 2e-3          # max abs error of fp32 outputs
+BOUNDARY_REL = 1e-4      # selections may differ only within this of the T-th score
+SCORE_REL = 1e-5         # fp32 score error relative to the sum of |terms|
+
+
+@dataclasses.dataclass
+class GpuRun:
+    out: np.ndarray
+    sel: np.ndarray          # [B][Hkv][T]
+    scores: np.ndarray       # [Hkv][ntot]
+    k_codes: np.ndarray
+    v_codes: np.ndarray
+    k_scales: np.ndarray
+    v_scales: np.ndarray
+    k_ref: Optional[np.ndarray]
+    v_ref: Optional[np.ndarray]
+
+
+def geom_of(w: W.Workload):
+    from selective_kv_cache_amd import binding as B
+    return B.geom(w.head_dim, w.n_q_heads, w.n_kv_heads, w.base_bits, w.refine_bits)
+
+
+def run_gpu(w: W.Workload, k: np.ndarray, v: np.ndarray, q: np.ndarray, seq_off: Sequence[int],
+            top_t: int, tier: int = 0, cap_extra: int = 0) -> GpuRun:
+    import torch
+    from selective_kv_cache_amd.kvcache import Decoder, LayerCache
+    g = geom_of(w)
+    ntot = int(seq_off[-1])
+    cache = LayerCache(g, ntot + cap_extra, tier=tier, max_seqs=len(seq_off) - 1,
+                       cache_slots=max(2 * top_t, 1))
+    try:
+        kd = torch.as_tensor(k, device="cuda")
+        vd = torch.as_tensor(v, device="cuda")
+        refs = cache.append(kd, vd, 0, keep_refine=True)
+        dec = Decoder(g, seq_off, top_t)
+        sel = torch.full((dec.batch, w.n_kv_heads, top_t), -7, dtype=torch.int32, device="cuda")
+        scores = torch.empty((w.n_kv_heads, dec.total), dtype=torch.float32, device="cuda")
+        out = dec.step(cache, torch.as_tensor(q, device="cuda"), sel_out=sel, scores_out=scores)
+        torch.cuda.synchronize()
+        cpu = lambda t: None if t is None else t.cpu().numpy()
+        return GpuRun(out=cpu(out), sel=cpu(sel), scores=cpu(scores), k_codes=cpu(cache.k_codes),
+                      v_codes=cpu(cache.v_codes), k_scales=cpu(cache.k_scales), v_scales=cpu(cache.v_scales),
+                      k_ref=cpu(refs[0]) if refs else None, v_ref=cpu(refs[1]) if refs else None)
+    finally:
+        cache.close()
+
+
+def check_codec(w: W.Workload, run: GpuRun, oc: O.QuantCache, ntot: int) -> None:
+    b, r = w.base_bits, w.refine_bits
+    for gpu_codes, gpu_scales, gpu_ref, qr in ((run.k_codes, run.k_scales, run.k_ref, oc.k),
+                                               (run.v_codes, run.v_scales, run.v_ref, oc.v)):
+        want = O.pack_bits(qr.base, b)
+        assert np.array_equal(gpu_codes[:, :ntot], want), "packed base codes differ"
+        assert np.array_equal(gpu_scales[:, :ntot, 0].view(np.uint32), qr.lo.view(np.uint32)), "lo differs"
+        assert np.array_equal(gpu_scales[:, :ntot, 1].view(np.uint32), qr.delta.view(np.uint32)), "delta differs"
+        if r:
+            assert np.array_equal(gpu_ref, O.pack_bits(qr.refine, r)), "refinement codes differ"
+
+
+def score_tolerance(q_group: np.ndarray, qr: O.QuantRows) -> np.ndarray:
+    """Per-token bound on fp32 evaluation error of the folded logit
+    (lo*sum q + delta*(sum q c + sum q / 2)) / sqrt(D), max over the group."""
+    aq = np.abs(q_group.astype(np.float64))                       # [G][D]
+    c = qr.base.astype(np.float64) + 0.5                           # [N][D]
+    mag = (np.abs(qr.lo.astype(np.float64))[:, None] * aq.sum(1)[None, :]
+           + qr.delta.astype(np.float64)[:, None] * (c @ aq.T))    # [N][G]
+    return SCORE_REL * mag.max(1) / np.sqrt(q_group.shape[-1]) + 1e-7
+
+
+def check_selection(gpu_sel: np.ndarray, gpu_scores: np.ndarray, ora_scores: np.ndarray, t: int) -> bool:
+    """True when the GPU selection equals the oracle's; otherwise asserts it
+    is valid: exactly the top-T of the GPU's own fp32 scores (ties to the
+    lower index) and differing from the oracle's only near the T-th score."""
+    n = ora_scores.shape[0]
+    tn = min(t, n)
+    got = gpu_sel[:tn]
+    assert np.all(gpu_sel[tn:] == -1), "padding"
+    assert np.all(np.diff(got) > 0) and (tn == 0 or (got[0] >= 0 and got[-1] < n)), "ascending, in range"
+    own = O.select_top_t(gpu_scores.astype(np.float64), t)
+    assert np.array_equal(got, own), "not the top-T of the GPU's own scores"
+    want = O.select_top_t(ora_scores, t)
+    if np.array_equal(got, want):
+        return True
+    s_t = np.sort(ora_scores)[::-1][tn - 1]
+    diff = np.setxor1d(got, want)
+    assert np.all(np.abs(ora_scores[diff] - s_t) <= BOUNDARY_REL * abs(s_t)), \
+        f"selection differs beyond the boundary allowance: {diff[:8]}"
+    return False
+
+
+def compare_layer(w: W.Workload, k, v, q, seq_off, top_t: int, run: GpuRun,
+                  heads: Optional[Sequence[Tuple[int, int]]] = None, codec: bool = True) -> Dict[str, float]:
+    ntot = int(seq_off[-1])
+    oc = O.quantize_cache(k, v, w.base_bits, w.refine_bits)
+    if codec:
+        check_codec(w, run, oc, ntot)
+    res = O.decode_step(q, oc, seq_off, top_t, heads=heads)
+    g = w.group
+    worst_out = worst_score = 0.0
+    differ = 0
+    for (s, h), hr in res.items():
+        a, e = int(seq_off[s]), int(seq_off[s + 1])
+        qg = q[s, h * g:(h + 1) * g]
+        gs = run.scores[h, a - int(seq_off[0]):e - int(seq_off[0])]
+        tol = score_tolerance(qg, O._rows(oc.k, h, a, e))
+        err = np.abs(gs.astype(np.float64) - hr.scores)
+        assert np.all(err <= tol), f"score error {err.max()} > tolerance at head {(s, h)}"
+        worst_score = max(worst_score, float((err / tol).max()))
+        same = check_selection(run.sel[s, h], gs, hr.scores, top_t)
+        ref = hr
+        if not same:
+            differ += 1
+            tn = min(top_t, e - a)
+            ref = O.decode_head(qg, O._rows(oc.k, h, a, e), O._rows(oc.v, h, a, e), top_t,
+                                sel=run.sel[s, h, :tn])
+        o_err = np.abs(run.out[s, h * g:(h + 1) * g].astype(np.float64) - ref.out).max()
+        assert o_err <= OUT_ATOL, f"output error {o_err} at {(s, h)}"
+        worst_out = max(worst_out, float(o_err))
+    return {"max_out_err": worst_out, "max_score_err_over_tol": worst_score, "selections_differing": differ}

@@ -1,0 +1,172 @@
+"""GPU parity: the HIP decode path against the oracle on the same seeded inputs.
+
+Bit-exact: packed base codes, refinement codes, (lo, delta) scales, and the
+selection whenever the oracle's boundary is not within 1e-4 of a tie.
+Scores within an fp32 evaluation bound; outputs within 2e-3 max abs.
+"""
+import numpy as np
+import pytest
+
+import oracle.kv_oracle as O
+import parity as P
+from selective_kv_cache_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(w, top_t=None, layer=0, heads=None, dup=None, flat_rows=(), tier=0):
+    lens = w.seq_lengths()
+    off = W.seq_offsets(lens)
+    k, v = W.layer_kv(w, layer)
+    if dup is not None:
+        dup(k, v)
+    for t in flat_rows:
+        k[t] = 0.75
+        v[t] = -1.5
+    q = W.query(w, layer)
+    t = w.top_t if top_t is None else top_t
+    print(f"case {w.name}: lens={lens[:4]}.. b={w.base_bits} r={w.refine_bits} T={t} G={w.group}", flush=True)
+    run = P.run_gpu(w, k, v, q, off, t, tier=tier)
+    stats = P.compare_layer(w, k, v, q, off, t, run, heads=heads)
+    print(stats, flush=True)
+    return run, stats
+
+
+def test_tiny_reference_layer():
+    _case(W.WORKLOADS["tiny_1k"])
+
+
+SMALL = [
+    dict(ctx=1000, n_q_heads=8, n_kv_heads=2, top_t=37),                       # ragged tail
+    dict(ctx=3000, n_q_heads=8, n_kv_heads=2, base_bits=3, refine_bits=2, top_t=100),
+    dict(ctx=2049, n_q_heads=4, n_kv_heads=1, base_bits=4, refine_bits=4, top_t=300),
+    dict(ctx=777, n_q_heads=2, n_kv_heads=2, top_t=50),                        # G = 1
+    dict(ctx=1500, n_q_heads=4, n_kv_heads=2, top_t=64),                       # G = 2
+    dict(ctx=1300, n_q_heads=8, n_kv_heads=1, top_t=64),                       # G = 8
+    dict(ctx=900, base_bits=2, refine_bits=0, top_t=64),                       # no refinement bits
+    dict(ctx=900, top_t=0),                                                    # nothing selected
+    dict(ctx=300, top_t=512),                                                  # N < T: all selected
+    dict(ctx=256, top_t=256),                                                  # N == T
+    dict(ctx=1, top_t=4),                                                      # one token
+    dict(ctx=5000, refine_bits=8, top_t=256, n_q_heads=8, n_kv_heads=2),
+]
+
+
+@pytest.mark.parametrize("i", range(len(SMALL)), ids=[",".join(f"{k}={v}" for k, v in o.items()) for o in SMALL])
+def test_small_shapes(i):
+    _case(W.small(cfg_id=220 + i, **SMALL[i]))
+
+
+def test_varlen_batch():
+    w = W.small("varlen", cfg_id=210, batch=3, n_q_heads=8, n_kv_heads=2, refine_bits=8, top_t=200)
+    lens = [700, 1500, 129]
+    off = W.seq_offsets(lens)
+    k, v = W.layer_kv(w, 0, n_tok=int(off[-1]))
+    q = W.query(w, 0)
+    run = P.run_gpu(w, k, v, q, off, w.top_t)
+    P.compare_layer(w, k, v, q, off, w.top_t, run)
+
+
+def test_ties_at_the_cut_go_to_the_lower_index():
+    w = W.small(cfg_id=300, ctx=600, top_t=50)
+    k, v = W.layer_kv(w, 0)
+    q = W.query(w, 0)
+    oc = O.quantize_cache(k, v, w.base_bits, w.refine_bits)
+    s = O.token_scores(q[0], O.dequant_base(O._rows(oc.k, 0, 0, 600)))
+    pivot = int(np.argsort(-s, kind="stable")[w.top_t - 1])         # the T-th ranked token
+    rng = np.random.default_rng(1)
+    dst = rng.choice(np.setdiff1d(np.arange(600), [pivot]), size=25, replace=False)
+    W.duplicate_rows(k, v, [pivot] * 25, dst)                       # 26 exact ties straddle the cut
+    off = W.seq_offsets([600])
+    run = P.run_gpu(w, k, v, q, off, w.top_t)
+    stats = P.compare_layer(w, k, v, q, off, w.top_t, run)
+    assert stats["selections_differing"] == 0
+    tied = np.sort(np.concatenate([[pivot], dst]))
+    chosen = np.intersect1d(run.sel[0, 0], tied)
+    assert 0 < chosen.size < tied.size
+    assert np.array_equal(chosen, tied[:chosen.size])              # the lowest indices of the tie win
+
+
+def test_flat_rows_and_all_equal_scores():
+    w = W.small(cfg_id=301, ctx=700, top_t=40)
+    _case(w, flat_rows=(3, 100, 699))
+    # every key identical: all scores tie, the selection is tokens 0..T-1
+    k, v = W.layer_kv(w, 0)
+    k[:] = k[5]
+    q = W.query(w, 0)
+    off = W.seq_offsets([700])
+    run = P.run_gpu(w, k, v, q, off, w.top_t)
+    P.compare_layer(w, k, v, q, off, w.top_t, run)
+    assert np.array_equal(run.sel[0, 0], np.arange(w.top_t))
+
+
+def test_deterministic_repeat():
+    w = W.small(cfg_id=302, ctx=5000, n_q_heads=8, n_kv_heads=2, top_t=128)
+    lens = w.seq_lengths()
+    off = W.seq_offsets(lens)
+    k, v = W.layer_kv(w, 0)
+    q = W.query(w, 0)
+    a = P.run_gpu(w, k, v, q, off, w.top_t)
+    b = P.run_gpu(w, k, v, q, off, w.top_t)
+    assert np.array_equal(a.out.view(np.uint32), b.out.view(np.uint32))
+    assert np.array_equal(a.sel, b.sel)
+
+
+def test_host_tier_matches_device_tier_and_cache_simulation():
+    """Host-pinned store + device refinement cache over several steps of an
+    AR(1) query process: outputs bit-identical to the device-resident store,
+    and hits/misses equal to the oracle's cache simulation."""
+    import torch
+    from selective_kv_cache_amd import binding as B
+    from selective_kv_cache_amd.kvcache import Decoder, LayerCache
+    w = W.small("reuse", cfg_id=303, ctx=3000, n_q_heads=8, n_kv_heads=2, base_bits=3, refine_bits=2,
+                top_t=128, rho=0.9)
+    g = P.geom_of(w)
+    off = W.seq_offsets([3000])
+    k, v = W.layer_kv(w, 0)
+    qs = W.queries(w, 0, 6)
+    dev = LayerCache(g, 3000, tier=B.SF_TIER_DEVICE)
+    host = LayerCache(g, 3000, tier=B.SF_TIER_HOST_PINNED, max_seqs=1, cache_slots=2 * w.top_t)
+    try:
+        kd, vd = torch.as_tensor(k, device="cuda"), torch.as_tensor(v, device="cuda")
+        dev.append(kd, vd, 0)
+        host.append(kd, vd, 0)
+        dec = Decoder(g, off, w.top_t)
+        sims = [O.CacheSim(2 * w.top_t) for _ in range(w.n_kv_heads)]
+        sel = torch.empty((1, w.n_kv_heads, w.top_t), dtype=torch.int32, device="cuda")
+        for t in range(qs.shape[0]):
+            qd = torch.as_tensor(qs[t], device="cuda")
+            o_dev = dec.step(dev, qd).cpu().numpy()
+            o_host, st = dec.step(host, qd, sel_out=sel, want_stats=True)
+            o_host = o_host.cpu().numpy()
+            assert np.array_equal(o_dev.view(np.uint32), o_host.view(np.uint32)), t
+            hits = misses = 0
+            for h in range(w.n_kv_heads):
+                hh, mm = sims[h].step(sel[0, h].cpu().numpy(), t)
+                hits, misses = hits + hh, misses + mm
+            assert (st["hits"], st["misses"]) == (hits, misses), (t, st, hits, misses)
+            assert st["h2d_bytes"] == O.fetched_bytes(misses, w.head_dim, w.refine_bits)
+            print(t, st, flush=True)
+        # a cold cache misses on the whole selection and still gives the same output
+        host.clear_cache()
+        o_host, st = dec.step(host, qd, want_stats=True)
+        assert st["misses"] == st["selected"] and st["hits"] == 0
+        assert np.array_equal(o_dev.view(np.uint32), o_host.cpu().numpy().view(np.uint32))
+    finally:
+        dev.close()
+        host.close()
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,heads", [("llama8b_32k", [(0, 0), (0, 7)]), ("llama8b_128k", [(0, 3)]),
+                                        ("qwen8b_b16", [(0, 0), (15, 5)])])
+def test_full_size_layer_sampled_heads(name, heads):
+    """Full-size layer in the benchmark's launch configuration; the oracle
+    checks some (sequence, KV head) pairs (all of them for codes and scores)."""
+    w = W.WORKLOADS[name]
+    off = W.seq_offsets(w.seq_lengths())
+    k, v = W.layer_kv(w, 0)
+    q = W.query(w, 0)
+    print(f"full size {name}: tokens={int(off[-1])}", flush=True)
+    run = P.run_gpu(w, k, v, q, off, w.top_t)
+    print(P.compare_layer(w, k, v, q, off, w.top_t, run, heads=heads), flush=True)
