@@ -9,7 +9,7 @@ Inputs are seeded synthetic K/V/q of the named head geometry, resident in HBM
 before timing starts.
 
 Prints ONE JSON line: steps/s (whole job), the step's algorithmic HBM GB/s,
-a roofline record of the dominant kernel (score/attention pass) timed live
+a roofline record of the dominant kernel (score or attention pass) timed live
 with HIP events, the CPU oracle timed on a bounded sample on the host, and
 secondary measurements (32K context; host-pinned refinement store with an
 AR(1) query process: hit rate and bytes fetched per step).
@@ -43,11 +43,16 @@ def algorithmic_bytes(w, lens):
     return tot
 
 
-def score_kernel_bytes(w, lens):
-    """Algorithmic bytes of one score/attention launch: base K and V codes and
-    scales of every token, plus the query."""
-    d, b, hkv = w.head_dim, w.base_bits, w.n_kv_heads
-    return sum(2 * n * hkv * (d * b // 8 + 8) + w.n_q_heads * d * 4 for n in lens)
+def kernel_bytes(w, lens):
+    """Algorithmic bytes of one launch of each pass.  score: base K codes and
+    scales of every token, plus the query.  attend: base K and V codes and
+    scales, the refinement rows of the selected K and V, the query; the split
+    partials it writes are not counted."""
+    d, b, r, hkv = w.head_dim, w.base_bits, w.refine_bits, w.n_kv_heads
+    score = sum(n * hkv * (d * b // 8 + 8) + w.n_q_heads * d * 4 for n in lens)
+    attend = sum(2 * n * hkv * (d * b // 8 + 8) + 2 * min(w.top_t, n) * hkv * d * r // 8 + w.n_q_heads * d * 4
+                 for n in lens)
+    return {"score": score, "attend": attend}
 
 
 class Model:
@@ -81,7 +86,7 @@ class Model:
         acc = {"selected": 0, "hits": 0, "misses": 0, "h2d_bytes": 0}
         for l in range(self.L):
             ev = events[l] if events is not None else None
-            res = self.dec.step(self.caches[l], (qs or self.qs)[l], out=self.outs[l], score_events=ev,
+            res = self.dec.step(self.caches[l], (qs or self.qs)[l], out=self.outs[l], events=ev,
                                 want_stats=stats)
             if stats:
                 for k2 in acc:
@@ -107,22 +112,24 @@ def time_steps(model, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def time_score_kernel(model, steps):
-    """Average duration of the score/attention kernel, from HIP events recorded
-    around each of its launches on the decode stream."""
+def time_kernels(model, steps):
+    """Average duration of the score and attention kernels, from HIP events
+    recorded around each of their launches on the decode stream."""
     import torch
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(model.L)] for _ in range(steps)]
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    evs = [[tuple(mk() for _ in range(4)) for _ in range(model.L)] for _ in range(steps)]
     for row in evs:
-        for a, b in row:
-            a.record()
-            b.record()
+        for quad in row:
+            for e in quad:
+                e.record()          # materialise the events before handing them over
     torch.cuda.synchronize()
     for s in range(steps):
         model.step(events=evs[s])
     torch.cuda.synchronize()
-    durs = [a.elapsed_time(b) for row in evs for a, b in row]
-    return float(np.mean(durs)), float(np.median(durs))
+    score = [q[0].elapsed_time(q[1]) for row in evs for q in row]
+    attend = [q[2].elapsed_time(q[3]) for row in evs for q in row]
+    return {"score": float(np.mean(score)), "attend": float(np.mean(attend)),
+            "score_median": float(np.median(score)), "attend_median": float(np.median(attend))}
 
 
 def cpu_baseline(w, layer_budget_s=30.0):
@@ -214,14 +221,15 @@ def main():
     model = Model(w, tier)
     log("timing steps")
     ms = time_steps(model, args.steps, args.warmup)
-    log(f"{ms:.3f} ms/step; timing the score/attention kernel")
-    k_mean, k_med = time_score_kernel(model, max(2, args.steps // 4))
+    log(f"{ms:.3f} ms/step; timing the score and attention kernels")
+    kt = time_kernels(model, max(2, args.steps // 4))
     model.close()
     del model
 
     step_bytes = algorithmic_bytes(w, w.seq_lengths()) * w.layers
-    kbytes = score_kernel_bytes(w, w.seq_lengths())
-    achieved = kbytes / (k_mean * 1e-3) / 1e9
+    kb = kernel_bytes(w, w.seq_lengths())
+    dom = max(("score", "attend"), key=lambda k: kt[k])
+    gbps = {k: kb[k] / (kt[k] * 1e-3) / 1e9 for k in kb}
     rec = {
         "metric": METRIC, "value": 1e3 / ms, "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
@@ -233,9 +241,12 @@ def main():
         "step_algorithmic_bytes": step_bytes,
         "step_hbm_gbps": step_bytes / (ms * 1e-3) / 1e9,
         "step_frac_of_peak": step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None, "kernel": "score_attn",
-                     "bytes_per_launch": kbytes, "avg_launch_ms": k_mean, "median_launch_ms": k_med},
+        "roofline": {"bound": "hbm", "achieved": gbps[dom], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": gbps[dom] / PEAK_HBM_GBPS, "traffic": None, "kernel": dom,
+                     "bytes_per_launch": kb[dom], "avg_launch_ms": kt[dom],
+                     "kernels": {k: {"bytes_per_launch": kb[k], "avg_launch_ms": kt[k],
+                                     "median_launch_ms": kt[k + "_median"], "achieved_gbps": gbps[k]}
+                                 for k in kb}},
     }
     if not args.no_secondary:
         sec = {}

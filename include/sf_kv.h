@@ -173,9 +173,10 @@ typedef struct sf_decode_args {
   void* workspace;               /* device scratch of sf_decode_workspace_size() bytes  */
   size_t workspace_bytes;
   int32_t flags;                 /* 0 (reserved)                                        */
-  void* score_events[2];         /* optional hipEvent_t pair recorded on `stream` just
-                                    before and after the score/attention kernel (both
-                                    NULL = none): lets a caller time that kernel       */
+  void* events[4];               /* optional hipEvent_t recorded on `stream` before and
+                                    after the score kernel ([0], [1]) and before and
+                                    after the attention kernel ([2], [3]); NULL = none.
+                                    Lets a caller time those kernels.                  */
 } sf_decode_args;
 
 /* Scratch needed by sf_decode_step for this batch shape.
@@ -197,8 +198,10 @@ sf_status sf_decode_workspace_size(const sf_geom* geom, int32_t batch, int64_t t
  *      Ktilde = lo + c * delta + (s + 1/2) * delta / 2^r;
  *   4. out_h = softmax over all tokens of q_h . K* / sqrt(D), applied to V*,
  *      with K*, V* refined for selected tokens and base-precision otherwise.
- * Device-tier stores and T == 0 need no host round trip; a host-pinned store
- * synchronizes the stream once per call to learn which rows to fetch.
+ * Kernels: score (reads the K codes), select, attention (reads K and V codes
+ * again and the refinement rows of the selection), combine.  Device-tier
+ * stores and T == 0 need no host round trip; a host-pinned store synchronizes
+ * the stream once per call to learn which rows to fetch.
  * The workspace need not be initialised; its contents are undefined after.
  */
 sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* args, void* stream);

@@ -45,7 +45,7 @@ class sf_decode_args(ctypes.Structure):
                 ("v_scales", c_vp), ("cap", c_i64), ("store", c_vp), ("top_t", c_i32), ("out", c_vp),
                 ("sel_out", c_vp), ("scores_out", c_vp), ("stats", ctypes.POINTER(sf_step_stats)),
                 ("workspace", c_vp), ("workspace_bytes", c_size), ("flags", c_i32),
-                ("score_events", c_vp * 2)]
+                ("events", c_vp * 4)]
 
 
 class SfError(RuntimeError):
@@ -153,7 +153,7 @@ def sf_decode_workspace_size(g: sf_geom, batch: int, total_tokens: int, max_seq_
 
 def sf_decode_step(g: sf_geom, *, seq_off_host: Sequence[int], seq_off_dev, q, k_codes, k_scales, v_codes,
                    v_scales, cap: int, store: Optional[int], top_t: int, out, workspace, sel_out=None,
-                   scores_out=None, want_stats: bool = False, score_events=None, stream=None):
+                   scores_out=None, want_stats: bool = False, events=None, stream=None):
     """One decode step; returns the step statistics as a dict when asked."""
     off = np.ascontiguousarray(np.asarray(seq_off_host, dtype=np.int64))
     a = sf_decode_args()
@@ -169,8 +169,8 @@ def sf_decode_step(g: sf_geom, *, seq_off_host: Sequence[int], seq_off_dev, q, k
     a.workspace = _ptr(workspace)
     a.workspace_bytes = workspace.numel() * workspace.element_size()
     a.flags = 0
-    if score_events is not None:
-        a.score_events[0], a.score_events[1] = (e.cuda_event if hasattr(e, "cuda_event") else e
-                                                for e in score_events)
+    if events is not None:       # (score begin, score end, attend begin, attend end), None allowed
+        for i, e in enumerate(events):
+            a.events[i] = None if e is None else (e.cuda_event if hasattr(e, "cuda_event") else e)
     _check(load().sf_decode_step(ctypes.byref(g), ctypes.byref(a), _stream(stream)), "sf_decode_step")
     return st.as_dict() if want_stats else None

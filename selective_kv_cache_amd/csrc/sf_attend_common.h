@@ -1,0 +1,224 @@
+// Pieces shared by the attention kernels: the selected-token work-group and
+// the per-wavefront partial merge.
+//
+// Page "StrataFlux -- Selective precision streaming -- What does it mean?",
+// paragraph "What travels over the link ...": a selected element is
+//   lo + c * delta + (s + 1/2) * delta / 2^r
+// (the r fetched bits name a sub-bin of the base code's bin).  Attention runs
+// over all tokens; the selected tokens' terms are computed here with their
+// refined keys and values, the other tokens' terms by the base pass, each
+// into partials (m, l, acc[D]) that only ever add positive weights.
+#pragma once
+
+#include "sf_decode_kernels.h"
+
+namespace sfk {
+
+constexpr float kRsqrtD = 0.08838834764831845f;   // 1 / sqrt(128)
+
+constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
+
+// Refinement row (rb bytes) of token `tok`: K when which == 0, V when 1.
+__device__ inline const uint32_t* refine_row(const DecodeParams& p, int64_t sk, int kvh, int64_t tok, int which) {
+  if (p.ref_rows)
+    return reinterpret_cast<const uint32_t*>(p.ref_rows + (((int64_t)which * p.hkv + kvh) * p.cap + tok) * p.rb);
+  int32_t slot = p.tok_slot[(int64_t)kvh * p.cap + tok];
+  slot = slot < 0 ? 0 : slot;   // installed by the lookup; never negative when consistent
+  return reinterpret_cast<const uint32_t*>(p.cache_data + ((sk * p.slots + slot) * 2 + which) * (int64_t)p.rb);
+}
+
+// Dot products of one quarter of head_dim (32 elements) with the G query
+// heads: base codes (BB bits) and refinement codes (R bits).
+template <int BB, int R, int G>
+__device__ inline void quarter_dots(const uint32_t* kb, const uint32_t* kr, const float* qs, int qd, float* dc,
+                                    float* ds) {
+#pragma unroll
+  for (int h = 0; h < G; ++h) dc[h] = ds[h] = 0.f;
+#pragma unroll
+  for (int d = 0; d < 32; ++d) {
+    const float c = (float)code_at<BB>(kb, d);
+    const float s = (float)code_at<R>(kr, d);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float qv = qs[h * kHeadDim + qd * 32 + d];
+      dc[h] = fmaf(qv, c, dc[h]);
+      ds[h] = fmaf(qv, s, ds[h]);
+    }
+  }
+}
+
+// Merge the four wavefronts' (m, l, acc) of a 256-thread work-group into one
+// partial.  mw/lw [4][G], accw [4][G][D] in LDS; called by all 256 threads
+// after a barrier.
+template <int G>
+__device__ inline void write_partial(float* part, const float (*mw)[G], const float (*lw)[G],
+                                     const float (*accw)[G][kHeadDim]) {
+  for (int i = threadIdx.x; i < G * kHeadDim; i += 256) {
+    const int h = i / kHeadDim, d = i % kHeadDim;
+    float M = -INFINITY;
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, mw[w][h]);
+    float A = 0.f, L = 0.f;
+    if (M != -INFINITY) {
+      for (int w = 0; w < 4; ++w) {
+        if (mw[w][h] == -INFINITY) continue;
+        const float e = expf(mw[w][h] - M);
+        A += e * accw[w][h][d];
+        L += e * lw[w][h];
+      }
+    }
+    part[h * kPartStride + d] = A;
+    if (d == 0) {
+      part[h * kPartStride + kHeadDim] = M;
+      part[h * kPartStride + kHeadDim + 1] = L;
+    }
+  }
+}
+
+// Selected tokens of one (sequence, KV head): kSelBlkTok of them per
+// work-group, 4 wavefronts x 16 tokens, 4 lanes (a quarter of head_dim each)
+// per token.  Writes the partial of the refined terms.
+template <int BB, int G>
+struct SelLds {
+  float qs[G][kHeadDim];
+  float qsum[G];
+  uint32_t vt[4][16][4 * BB + 1];
+  uint32_t vr[4][16][33];
+  float2 vsc[4][16];
+  float wt[4][G][16];
+  float mred[4][G], mall[4][G], lw[4][G];
+  float accw[4][G][kHeadDim];
+};
+
+template <int BB, int G>
+__device__ inline void selected_block(const DecodeParams& p, int blk, int kvh, uint8_t* smem) {
+  constexpr int W = 4 * BB;
+  using Lds = SelLds<BB, G>;
+  Lds& s = *reinterpret_cast<Lds*>(smem);
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tk = lane >> 2, qd = lane & 3;
+  int64_t lo, hi;
+  int first;
+  const int seq = locate_unit(p.seq_off, p.batch, kSelBlkTok, blk, true, p.top_t, lo, hi, first);
+  const int64_t a = p.seq_off[seq];
+  const int64_t sk = (int64_t)seq * p.hkv + kvh;
+  const int r = p.r;
+  const float sub = __builtin_ldexpf(1.0f, -r);
+  const uint32_t rmask = (1u << r) - 1u;
+
+  for (int i = tid; i < G * kHeadDim; i += 256)
+    s.qs[i / kHeadDim][i % kHeadDim] = p.q[((int64_t)seq * p.hq + kvh * G) * kHeadDim + i];
+  __syncthreads();
+  if (tid < G) {
+    float acc = 0.f;
+    for (int d = 0; d < kHeadDim; ++d) acc += s.qs[tid][d];
+    s.qsum[tid] = acc;
+  }
+  const int64_t j = lo + wid * 16 + tk;
+  const bool valid = j < hi;
+  const int64_t tok = valid ? a + p.sel[sk * p.top_t + j] : 0;
+  uint32_t kb[BB], kr[9];
+  float2 ksc = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int i = 0; i < BB; ++i) kb[i] = 0u;
+#pragma unroll
+  for (int i = 0; i < 9; ++i) kr[i] = 0u;
+  if (valid) {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(p.kc + ((int64_t)kvh * p.cap + tok) * (16 * BB)) + qd * BB;
+#pragma unroll
+    for (int i = 0; i < BB; ++i) kb[i] = src[i];
+    const uint32_t* rs = refine_row(p, sk, kvh, tok, 0) + qd * r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kr[i] = i < r ? rs[i] : 0u;
+    ksc = reinterpret_cast<const float2*>(p.ks)[(int64_t)kvh * p.cap + tok];
+  }
+  __syncthreads();
+  float dc[G], ds[G];
+  switch (r) {
+    case 1: quarter_dots<BB, 1, G>(kb, kr, &s.qs[0][0], qd, dc, ds); break;
+    case 2: quarter_dots<BB, 2, G>(kb, kr, &s.qs[0][0], qd, dc, ds); break;
+    case 3: quarter_dots<BB, 3, G>(kb, kr, &s.qs[0][0], qd, dc, ds); break;
+    case 4: quarter_dots<BB, 4, G>(kb, kr, &s.qs[0][0], qd, dc, ds); break;
+    case 5: quarter_dots<BB, 5, G>(kb, kr, &s.qs[0][0], qd, dc, ds); break;
+    case 6: quarter_dots<BB, 6, G>(kb, kr, &s.qs[0][0], qd, dc, ds); break;
+    case 7: quarter_dots<BB, 7, G>(kb, kr, &s.qs[0][0], qd, dc, ds); break;
+    default: quarter_dots<BB, 8, G>(kb, kr, &s.qs[0][0], qd, dc, ds); break;
+  }
+  float lr[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    dc[h] += __shfl_xor(dc[h], 1);
+    dc[h] += __shfl_xor(dc[h], 2);
+    ds[h] += __shfl_xor(ds[h], 1);
+    ds[h] += __shfl_xor(ds[h], 2);
+    lr[h] = (ksc.x * s.qsum[h] + ksc.y * (dc[h] + (ds[h] + 0.5f * s.qsum[h]) * sub)) * kRsqrtD;
+    const float mv = wave_max(valid ? lr[h] : -INFINITY);
+    if (lane == 0) s.mred[wid][h] = mv;
+  }
+  {
+    uint32_t* dstb = &s.vt[wid][tk][qd * BB];
+    uint32_t* dstr = &s.vr[wid][tk][qd * r];
+    if (valid) {
+      const uint32_t* src =
+          reinterpret_cast<const uint32_t*>(p.vc + ((int64_t)kvh * p.cap + tok) * (16 * BB)) + qd * BB;
+#pragma unroll
+      for (int i = 0; i < BB; ++i) dstb[i] = src[i];
+      const uint32_t* rs = refine_row(p, sk, kvh, tok, 1) + qd * r;
+      for (int i = 0; i < r; ++i) dstr[i] = rs[i];
+      if (qd == 0) s.vsc[wid][tk] = reinterpret_cast<const float2*>(p.vs)[(int64_t)kvh * p.cap + tok];
+    } else {
+#pragma unroll
+      for (int i = 0; i < BB; ++i) dstb[i] = 0u;
+      for (int i = 0; i < r; ++i) dstr[i] = 0u;
+      if (qd == 0) s.vsc[wid][tk] = make_float2(0.f, 0.f);
+    }
+    if (qd == 0) {
+      s.vt[wid][tk][W] = 0u;
+      s.vr[wid][tk][4 * r] = 0u;
+    }
+  }
+  __syncthreads();
+  float acc[G][2];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float M = fmaxf(fmaxf(s.mred[0][h], s.mred[1][h]), fmaxf(s.mred[2][h], s.mred[3][h]));
+    const float e = valid ? expf(lr[h] - M) : 0.f;
+    if (qd == 0) s.wt[wid][h][tk] = e;
+    const float ls = wave_sum(qd == 0 ? e : 0.f);
+    if (lane == 0) {
+      s.lw[wid][h] = ls;
+      s.mall[wid][h] = M;       // all waves share the work-group maximum
+    }
+    acc[h][0] = acc[h][1] = 0.f;
+  }
+  wave_barrier();
+  const int cpos = 2 * lane * BB, cwi = cpos >> 5, csh = cpos & 31;
+  const int rpos = 2 * lane * r, rwi = rpos >> 5, rsh = rpos & 31;
+  for (int jj = 0; jj < 16; ++jj) {
+    const uint64_t cwin = (uint64_t)s.vt[wid][jj][cwi] | ((uint64_t)s.vt[wid][jj][cwi + 1] << 32);
+    const uint32_t cc = (uint32_t)(cwin >> csh);
+    const uint64_t rwin = (uint64_t)s.vr[wid][jj][rwi] | ((uint64_t)s.vr[wid][jj][rwi + 1] << 32);
+    const uint32_t rr = (uint32_t)(rwin >> rsh);
+    const float c0 = (float)(cc & ((1u << BB) - 1u)), c1 = (float)((cc >> BB) & ((1u << BB) - 1u));
+    const float s0 = (float)(rr & rmask), s1 = (float)((rr >> r) & rmask);
+    const float2 sc = s.vsc[wid][jj];
+    const float v0 = fmaf((s0 + 0.5f) * sub, sc.y, fmaf(c0, sc.y, sc.x));
+    const float v1 = fmaf((s1 + 0.5f) * sub, sc.y, fmaf(c1, sc.y, sc.x));
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float w = s.wt[wid][h][jj];
+      acc[h][0] = fmaf(w, v0, acc[h][0]);
+      acc[h][1] = fmaf(w, v1, acc[h][1]);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    s.accw[wid][h][2 * lane] = acc[h][0];
+    s.accw[wid][h][2 * lane + 1] = acc[h][1];
+  }
+  __syncthreads();
+  float* part = p.part + ((int64_t)kvh * (p.n_sel_blk + p.n_split) + blk) * G * kPartStride;
+  write_partial<G>(part, s.mall, s.lw, s.accw);
+}
+
+}  // namespace sfk

@@ -7,8 +7,11 @@ namespace sfk {
 
 struct DecodeParams {
   int32_t batch, hq, hkv, grp, b, r, top_t;
-  int32_t split, sel_chunk, corr_chunk;
-  int32_t n_split, n_corr, bm_words;
+  int32_t score_split, split, sel_chunk;   // tokens per score / attention / selection work-group
+  int32_t n_score_split, n_split, bm_words;
+  int32_t use_refine;                      // selected rows take their refinement codes
+  int32_t n_sel_blk;                       // work-groups of selected tokens (kSelBlkTok each)
+  int32_t cnt_stride;                      // selection chunks per sequence (max)
   int64_t cap, ntot, off0, max_seq;
   const int64_t* seq_off;
   const float* q;
@@ -17,14 +20,14 @@ struct DecodeParams {
   const uint8_t* vc;
   const float* vs;
   float* scores;       // [hkv][ntot]
-  uint32_t* hist;      // [batch][hkv][kHistBins]
-  uint32_t* counters;  // [batch][hkv][4]: 0 candidates, 1 selection ticket
-  uint2* cand;         // [batch][hkv][max_seq] (score key, token)
+  uint32_t* hist;      // [batch][hkv][kHistBins]: histogram of the scores' top key bits
+  uint32_t* counters;  // [batch][hkv][cnt_stride]: candidates of each selection chunk
+  uint2* cand;         // [batch][hkv][max_seq] (score key, token); chunk c's at c*sel_chunk
   uint32_t* bitmap;    // [batch][hkv][bm_words]
   int32_t* sel;        // [batch][hkv][top_t]
   int32_t* sel_out;    // optional copy of sel
-  float* part;         // [hkv][n_split][grp][kPartStride]
-  float* corr;         // [hkv][n_corr][grp][kPartStride]
+  float* part;         // [hkv][n_sel_blk + n_split][grp][kPartStride]: selected-token
+                       // partials first, then the base partials of the splits
   // refinement rows: device tier store, or host-tier device cache
   const uint8_t* ref_rows;    // [2][hkv][cap][rb] or NULL
   const uint8_t* cache_data;  // [max_seqs][hkv][slots][2][rb] or NULL
@@ -83,5 +86,71 @@ __device__ inline uint32_t code_at(const uint32_t* words, int d) {
   if (sh + W > 32) v |= words[wi + 1] << (32 - sh);
   return v & ((1u << W) - 1u);
 }
+
+// Block-wide exclusive prefix sum of one value per thread (NT threads);
+// `lds` holds NT/64 words.  Every thread receives the block total too.
+template <int NT>
+__device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* lds, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) lds[wid] = x;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const uint32_t t = lds[w];
+    base += (w < wid) ? t : 0u;
+    tot += t;
+  }
+  __syncthreads();
+  total = tot;
+  return base + x - v;
+}
+
+// Find, in a histogram of NB bins counted from the top bin down, the bin b
+// with count(bins > b) < need <= count(bins >= b); writes b and the number
+// still needed inside b (need - count(bins > b)).  NT threads, NB % NT == 0;
+// needs 1 <= need <= total count.
+template <int NT, int NB>
+__device__ inline void find_threshold(const uint32_t* hist, uint32_t need, uint32_t* scan_lds, int* out_bin,
+                                      uint32_t* out_need) {
+  constexpr int PER = NB / NT;
+  const int top = NB - PER * (int)threadIdx.x;   // this thread: bins [top - PER, top)
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) s += hist[top - 1 - i];
+  uint32_t tot;
+  const uint32_t above = block_exclusive_scan<NT>(s, scan_lds, tot);
+  if (above < need && need <= above + s) {
+    uint32_t cum = above;
+    for (int i = 0; i < PER; ++i) {
+      const int b = top - 1 - i;
+      if (cum + hist[b] >= need) {
+        *out_bin = b;
+        *out_need = need - cum;
+        break;
+      }
+      cum += hist[b];
+    }
+  }
+  __syncthreads();
+}
+
+// Launchers (one per stage source file).
+bool launch_score(const DecodeParams& p, dim3 grid, hipStream_t st);
+void launch_select(const DecodeParams& p, dim3 grid, hipStream_t st);
+bool launch_attend(const DecodeParams& p, dim3 grid, hipStream_t st);
+void launch_combine(const DecodeParams& p, hipStream_t st);
+
+constexpr int kSelThreads = 512;
+constexpr int32_t kSelChunk = 4096;
+constexpr int32_t kMaxSelChunks = 512;   // longest sequence: kMaxSelChunks * kSelChunk tokens
+constexpr int32_t kSelBlkTok = 64;     // selected tokens per attention work-group
+constexpr int kCombineMax = 2048;      // partials per (sequence, query head)
 
 }  // namespace sfk

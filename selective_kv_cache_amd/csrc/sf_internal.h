@@ -24,30 +24,15 @@ __host__ __device__ inline uint32_t score_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Split plan of one decode step: the token axis of every sequence is cut into
-// splits of `split` tokens (score/attention partials) and the selection of
-// every sequence into chunks of `corr_chunk` tokens (refinement corrections).
-struct Plan {
-  int32_t batch;
-  int64_t total_tokens;
-  int64_t max_seq_tokens;
-  int32_t split;          // tokens per score/attention work-group
-  int32_t n_split;        // total splits over the batch
-  int32_t sel_chunk;      // tokens per selection work-group
-  int32_t n_sel_chunk;    // total selection chunks over the batch
-  int32_t corr_chunk;     // selected tokens per correction work-group
-  int32_t n_corr_chunk;   // total correction chunks (upper bound for sizing)
-  int32_t top_t;
-};
-
 // Workspace carve-out (byte offsets from the workspace base).
 struct Carve {
-  size_t scores, hist, counters, cand, bitmap, sel, part, corr, miss, total;
+  size_t scores, hist, counters, cand, bitmap, sel, part, miss, total;
 };
 
 int32_t choose_split(int64_t total_tokens, int32_t n_kv_heads);
+int32_t choose_score_split(int64_t total_tokens, int32_t n_kv_heads);
 Carve carve(const sf_geom& g, int32_t batch, int64_t total_tokens, int64_t max_seq_tokens,
-            int32_t top_t, int32_t n_split_bound, int32_t n_corr_bound);
+            int32_t top_t, int32_t n_split_bound);
 
 }  // namespace sfk
 

@@ -1,0 +1,385 @@
+// Matrix-core (CDNA4 MFMA) forms of the score pass and of the base attention
+// pass, for 2-bit base codes and GQA groups of up to 4 query heads.
+//
+// Logits (page "StrataFlux -- Selective precision streaming -- What does it
+// mean?", paragraph "Which tiles count ...": scores from the resident low-bit
+// keys).  With Khat = lo + (c + 1/2) * delta,
+//   q . Khat = (lo + delta/2) * sum(q) + delta * (q . c),
+// and q . c is an integer-code dot product.  Each query head is written as
+// s * (d0 + d1/254 + d2/254^2 + d3/254^3) with int8 digits dk, so q . c is
+// four exact int32 dot products: one v_mfma_i32_16x16x64_i8 tile holds
+// 4 heads x 4 digits (rows) against 16 tokens (columns), two tiles per 128
+// elements.  Lane l of the result then holds the four digit sums of head
+// l/16 for token l%16.
+//
+// Values (paragraph "Which tiles count": unselected tokens take part at base
+// precision).  sum_i p_i * vhat_i = sum_i p_i (lo_i + delta_i/2)
+//                                   + sum_i (p_i delta_i) c_i,
+// the first term a per-head scalar, the second a [heads x tokens] x
+// [tokens x 128] product on v_mfma_f32_16x16x32_f16: the weights p*delta go in
+// as fp16 hi + lo pieces (22 significant bits), the 2-bit codes as fp16
+// subnormals taken straight from the packed bits (a code c at mantissa bit
+// 2t reads as c * 2^(2t-24), exactly; the power of two is undone per tile).
+// The codes of 8 tokens at one element are gathered with one v_perm_b32 per
+// token pair, so the packed rows are read as they are stored.
+#include <math.h>
+
+#include "sf_attend_common.h"
+
+namespace sfk {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+constexpr float kInv254 = 1.0f / 254.0f;
+
+// Element (within a lane group's 32) carried by byte j of the B operand of
+// logit MFMA i, for 2-bit codes: byte j = (dword >> 2*(j/4)) byte (j%4).
+__device__ inline int kdim2(int i, int j) { return 16 * i + (j >> 2) + 4 * (j & 3); }
+
+__device__ inline void decode_b2(uint32_t w0, uint32_t w1, v4i& b0, v4i& b1) {
+  b0 = v4i{(int)(w0 & 0x03030303u), (int)((w0 >> 2) & 0x03030303u), (int)((w0 >> 4) & 0x03030303u),
+           (int)((w0 >> 6) & 0x03030303u)};
+  b1 = v4i{(int)(w1 & 0x03030303u), (int)((w1 >> 2) & 0x03030303u), (int)((w1 >> 4) & 0x03030303u),
+           (int)((w1 >> 6) & 0x03030303u)};
+}
+
+// Query digits and per-head constants, shared by both kernels.
+template <int G>
+struct QPrep {
+  int8_t dig[4][4][kHeadDim];   // [head][digit][element]
+  float scale[4];               // s_h
+  float sumq[4];                // sum(q_h)
+};
+
+// Work-group prologue: wave h < G turns query head h into digits.  Then each
+// lane builds its two A operands (row = 4*head + digit, 16 bytes = elements of
+// lane group l/16).
+template <int G>
+__device__ inline void prep_query(const float* q, QPrep<G>& qp, v4i& a0, v4i& a1) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  if (wid < G) {
+    const float x0 = q[wid * kHeadDim + 2 * lane], x1 = q[wid * kHeadDim + 2 * lane + 1];
+    const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+    const float sum = wave_sum(x0 + x1);
+    const float sc = amax > 0.f ? amax / 127.0f : 1.0f;
+    const float xs[2] = {x0 / sc, x1 / sc};
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      float r = xs[e];
+      int8_t dg[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float d = fminf(fmaxf(rintf(r), -127.f), 127.f);
+        dg[k] = (int8_t)d;
+        r = (r - d) * 254.0f;
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) qp.dig[wid][k][2 * lane + e] = dg[k];
+    }
+    if (lane == 0) {
+      qp.scale[wid] = sc;
+      qp.sumq[wid] = sum;
+    }
+  }
+  __syncthreads();
+  const int m = lane & 15, h = m >> 2, k = m & 3, g = lane >> 4;
+  uint32_t w[8];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int j = 4 * v + b;
+        const int dim = 32 * g + kdim2(i, j);
+        const uint32_t byte = h < G ? (uint32_t)(uint8_t)qp.dig[h][k][dim] : 0u;
+        word |= byte << (8 * b);
+      }
+      w[4 * i + v] = word;
+    }
+  }
+  a0 = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+  a1 = v4i{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+}
+
+// Logit of (head l/16, token l%16) from the digit sums; -inf for heads >= G.
+template <int G>
+__device__ inline float logit_from(const v4i& D, float2 ksc, float scale, float sumq, int hl) {
+  const float S = (float)D[0] + ((float)D[1] + ((float)D[2] + (float)D[3] * kInv254) * kInv254) * kInv254;
+  const float lg = (fmaf(0.5f, ksc.y, ksc.x) * sumq + ksc.y * (S * scale)) * kRsqrtD;
+  return hl < G ? lg : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// Score pass: grid (n_score_split, hkv), 4 wavefronts; tiles of 16 tokens.
+// ---------------------------------------------------------------------------
+template <int G>
+__global__ void __launch_bounds__(256) score_mfma(DecodeParams p) {
+  __shared__ QPrep<G> qp;
+  __shared__ uint32_t lhist[kHistBins];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int kvh = blockIdx.y;
+  int64_t lo, hi;
+  int first;
+  const int seq = locate_unit(p.seq_off, p.batch, p.score_split, blockIdx.x, false, 0, lo, hi, first);
+  const int64_t a = p.seq_off[seq];
+  for (int i = tid; i < kHistBins; i += 256) lhist[i] = 0u;
+  v4i a0, a1;
+  prep_query<G>(p.q + ((int64_t)seq * p.hq + kvh * G) * kHeadDim, qp, a0, a1);
+  const int t = lane & 15, hl = lane >> 4;
+  const float scale = qp.scale[hl < G ? hl : 0], sumq = qp.sumq[hl < G ? hl : 0];
+  const uint8_t* kbase = p.kc + (int64_t)kvh * p.cap * 32;
+  const float2* ksc = reinterpret_cast<const float2*>(p.ks) + (int64_t)kvh * p.cap;
+  float* scores = p.scores + (int64_t)kvh * p.ntot + (a - p.off0);
+  const int ntiles = (int)((hi - lo + 15) / 16);
+  constexpr int U = 8;
+  for (int k0 = wid; k0 < ntiles; k0 += 4 * U) {
+    uint2 w[U];
+    float2 sc[U];
+    int64_t li[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      li[u] = lo + 16 * (int64_t)(k0 + 4 * u) + t;
+      const int64_t tok = a + (li[u] < hi ? li[u] : lo);
+      w[u] = *reinterpret_cast<const uint2*>(kbase + tok * 32 + 8 * hl);
+      sc[u] = ksc[tok];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (k0 + 4 * u >= ntiles) break;
+      v4i b0, b1;
+      decode_b2(w[u].x, w[u].y, b0, b1);
+      v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, v4i{0, 0, 0, 0}, 0, 0, 0);
+      D = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, D, 0, 0, 0);
+      float lg = logit_from<G>(D, sc[u], scale, sumq, hl);
+      lg = fmaxf(lg, __shfl_xor(lg, 16));
+      lg = fmaxf(lg, __shfl_xor(lg, 32));
+      if (hl == 0 && li[u] < hi) {
+        scores[li[u]] = lg;
+        atomicAdd(&lhist[score_key(lg) >> (32 - kHistBits)], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t* gh = p.hist + ((int64_t)seq * p.hkv + kvh) * kHistBins;   // level-1 histogram
+  for (int i = tid; i < kHistBins; i += 256) {
+    const uint32_t c = lhist[i];
+    if (c) atomicAdd(&gh[i], c);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Base attention pass over one split (selected tokens left out): 4
+// wavefronts, chunks of 32 tokens (two logit tiles, one P.V step).
+// ---------------------------------------------------------------------------
+template <int G>
+struct MfmaLds {
+  QPrep<G> qp;
+  alignas(16) _Float16 wt[4][16][32];   // per wave: P.V weights [column][token]
+  float mw[4][G], lw[4][G];
+  float accw[4][G][kHeadDim];
+};
+
+template <int G>
+__device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh, uint8_t* smem) {
+  using Lds = MfmaLds<G>;
+  Lds& s = *reinterpret_cast<Lds*>(smem);
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  int64_t lo, hi;
+  int first;
+  const int seq = locate_unit(p.seq_off, p.batch, p.split, split, false, 0, lo, hi, first);
+  const int64_t a = p.seq_off[seq];
+  const int64_t sk = (int64_t)seq * p.hkv + kvh;
+  const uint32_t* bm = p.bitmap + sk * p.bm_words;
+  const bool masked = p.use_refine != 0;
+  for (int i = lane; i < 16 * 32; i += 64) (&s.wt[wid][0][0])[i] = (_Float16)0.f;
+  v4i a0, a1;
+  prep_query<G>(p.q + ((int64_t)seq * p.hq + kvh * G) * kHeadDim, s.qp, a0, a1);
+  const int t = lane & 15, hl = lane >> 4;        // logit layout: token t, head hl
+  const int n = lane & 15, rg = lane >> 4;        // P.V layout: column n, element rows 4rg..4rg+3
+  const float scale = s.qp.scale[hl < G ? hl : 0], sumq = s.qp.sumq[hl < G ? hl : 0];
+  const uint8_t* kbase = p.kc + (int64_t)kvh * p.cap * 32;
+  const uint8_t* vbase = p.vc + (int64_t)kvh * p.cap * 32;
+  const float2* kscg = reinterpret_cast<const float2*>(p.ks) + (int64_t)kvh * p.cap;
+  const float2* vscg = reinterpret_cast<const float2*>(p.vs) + (int64_t)kvh * p.cap;
+  // v_perm_b32 selector: half (n & 1) of each of two dwords
+  const uint32_t hsel = 2u * (uint32_t)(n & 1);
+  const uint32_t psel = hsel | ((hsel + 1u) << 8) | ((hsel + 4u) << 16) | ((hsel + 5u) << 24);
+  const int vdw = n >> 1;                         // dword of the V row holding elements 8n..8n+7
+
+  float m = -INFINITY, lsum = 0.f, t1 = 0.f;
+  int sexp = 127;                                 // weight scale 2^sexp; 127 = not set yet
+  v4f acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  const int nchunks = (int)((hi - lo + 31) / 32);
+  // loads of one chunk: K codes and scales of the two logit tiles (token t),
+  // V scales (token t), V dwords (8 tokens of lane group rg), selection bits
+  struct ChunkLoad {
+    uint2 kw[2];
+    float2 ksc[2], vsc[2];
+    uint32_t vw[8];
+    uint32_t selw;
+  };
+  auto load_chunk = [&](int c, ChunkLoad& L) {
+    const int64_t base = lo + 32 * (int64_t)c;
+    L.selw = masked ? bm[base >> 5] : 0u;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int64_t li = base + 16 * k + t;
+      const int64_t tok = a + (li < hi ? li : lo);
+      L.kw[k] = *reinterpret_cast<const uint2*>(kbase + tok * 32 + 8 * hl);
+      L.ksc[k] = kscg[tok];
+      L.vsc[k] = vscg[tok];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int64_t li = base + 8 * rg + e;
+      const int64_t tok = a + (li < hi ? li : lo);
+      L.vw[e] = *reinterpret_cast<const uint32_t*>(vbase + tok * 32 + 4 * vdw);
+    }
+  };
+  ChunkLoad cur, nxt;
+  if (wid < nchunks) load_chunk(wid, cur);
+  for (int c = wid; c < nchunks; c += 4) {
+    if (c + 4 < nchunks) load_chunk(c + 4, nxt);     // next chunk's loads in flight meanwhile
+    const int64_t base = lo + 32 * (int64_t)c;
+    const uint32_t selw = cur.selw;
+    const uint2* kw = cur.kw;
+    const float2* ksc = cur.ksc;
+    const float2* vsc = cur.vsc;
+    const uint32_t* vw = cur.vw;
+    bool ok[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) ok[k] = base + 16 * k + t < hi && !((selw >> (16 * k + t)) & 1u);
+    // logits
+    float lg[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      v4i b0, b1;
+      decode_b2(kw[k].x, kw[k].y, b0, b1);
+      v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, v4i{0, 0, 0, 0}, 0, 0, 0);
+      D = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, D, 0, 0, 0);
+      lg[k] = ok[k] ? logit_from<G>(D, ksc[k], scale, sumq, hl) : -INFINITY;
+    }
+    // online softmax: maximum over the row of 16 lanes (one head)
+    float mx = fmaxf(lg[0], lg[1]);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    const float mnew = fmaxf(m, mx);
+    // weight scale: keep delta * 2^sexp below 2^14 over the chunk
+    float dmax = fmaxf(ok[0] ? vsc[0].y : 0.f, ok[1] ? vsc[1].y : 0.f);
+    dmax = wave_max(dmax);
+    int need = sexp;
+    if (dmax > 0.f) {
+      int e2;
+      frexpf(dmax, &e2);
+      need = 14 - e2;
+    }
+    const bool grow = __ballot(mnew > m) != 0ull;
+    if (grow || need < sexp) {
+      const float alpha = mnew > m ? (m == -INFINITY ? 0.f : expf(m - mnew)) : 1.f;
+      lsum *= alpha;
+      t1 *= alpha;
+      const int hc = n < 2 * G ? n % G : 0;
+      float f = __shfl(alpha, 16 * hc);
+      if (need < sexp && sexp != 127) f = __builtin_ldexpf(f, need - sexp);
+      if (need < sexp) sexp = need;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] *= f;
+      m = mnew;
+    }
+    const int se = sexp == 127 ? 0 : sexp;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const float pk = lg[k] == -INFINITY ? 0.f : expf(lg[k] - m);
+      lsum += pk;
+      t1 = fmaf(pk, fmaf(0.5f, vsc[k].y, vsc[k].x), t1);
+      const float wv = __builtin_ldexpf(pk * vsc[k].y, se);
+      const _Float16 whi = (_Float16)wv;
+      const _Float16 wlo = (_Float16)(wv - (float)whi);
+      if (hl < G) {
+        s.wt[wid][hl][16 * k + t] = whi;
+        s.wt[wid][G + hl][16 * k + t] = wlo;
+      }
+    }
+    wave_barrier();
+    const v8h bw = *reinterpret_cast<const v8h*>(&s.wt[wid][n][8 * rg]);
+    uint32_t P[4], Q[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      P[v] = __builtin_amdgcn_perm(vw[2 * v + 1], vw[2 * v], psel);
+      Q[v] = P[v] >> 10;
+    }
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+      const uint32_t mk = 0x00030003u << (2 * (tt <= 4 ? tt : tt - 5));
+      v4u av;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) av[v] = (tt <= 4 ? P[v] : Q[v]) & mk;
+      acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, av), bw, acc[tt], 0, 0, 0);
+    }
+    wave_barrier();
+    cur = nxt;
+  }
+
+  // wave totals: l and the scalar term per head (row sums), P.V per head
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) {
+    lsum += __shfl_xor(lsum, o);
+    t1 += __shfl_xor(t1, o);
+  }
+  if (hl < G && t == 0) {
+    s.mw[wid][hl] = m;
+    s.lw[wid][hl] = lsum;
+  }
+  const float t1n = __shfl(t1, 16 * (n < G ? n : 0));
+  const int se = sexp == 127 ? 0 : sexp;
+#pragma unroll
+  for (int tt = 0; tt < 8; ++tt) {
+    const float f = __builtin_ldexpf(1.0f, 24 - 2 * (tt <= 4 ? tt : tt - 5) - se);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float v = acc[tt][j] + __shfl_xor(acc[tt][j], G);
+      if (n < G) s.accw[wid][n][32 * rg + 8 * j + tt] = fmaf(v, f, t1n);
+    }
+  }
+  __syncthreads();
+  float* part = p.part + ((int64_t)kvh * (p.n_sel_blk + p.n_split) + p.n_sel_blk + split) * G * kPartStride;
+  write_partial<G>(part, s.mw, s.lw, s.accw);
+}
+
+template <int G>
+__global__ void __launch_bounds__(256) attend_mfma(DecodeParams p) {
+  __shared__ __align__(16) uint8_t smem[cmax(sizeof(SelLds<2, G>), sizeof(MfmaLds<G>))];
+  if ((int)blockIdx.x < p.n_sel_blk)
+    selected_block<2, G>(p, blockIdx.x, blockIdx.y, smem);
+  else
+    base_split_mfma<G>(p, blockIdx.x - p.n_sel_blk, blockIdx.y, smem);
+}
+
+bool launch_score_mfma(const DecodeParams& p, dim3 grid, hipStream_t st) {
+  if (p.b != 2) return false;
+  switch (p.grp) {
+    case 1: hipLaunchKernelGGL((score_mfma<1>), grid, dim3(256), 0, st, p); return true;
+    case 2: hipLaunchKernelGGL((score_mfma<2>), grid, dim3(256), 0, st, p); return true;
+    case 4: hipLaunchKernelGGL((score_mfma<4>), grid, dim3(256), 0, st, p); return true;
+  }
+  return false;
+}
+
+bool launch_attend_mfma(const DecodeParams& p, dim3 grid, hipStream_t st) {
+  if (p.b != 2) return false;
+  switch (p.grp) {
+    case 1: hipLaunchKernelGGL((attend_mfma<1>), grid, dim3(256), 0, st, p); return true;
+    case 2: hipLaunchKernelGGL((attend_mfma<2>), grid, dim3(256), 0, st, p); return true;
+    case 4: hipLaunchKernelGGL((attend_mfma<4>), grid, dim3(256), 0, st, p); return true;
+  }
+  return false;
+}
+
+}  // namespace sfk

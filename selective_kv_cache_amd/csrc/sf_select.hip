@@ -1,0 +1,244 @@
+// Per-KV-head top-T selection (the "refine the highest-scoring tokens for
+// each KV head" step of the page "StrataFlux -- Selective precision streaming
+// -- What does it mean?", paragraph "Which tiles count ...").
+//
+// Order: score descending, then token index ascending (ties at the cut go to
+// the lower index); with N <= T every token is selected.  Scores are compared
+// through their order-preserving 32-bit keys (sfk::score_key).
+//
+// Three radix levels of the key, all exact:
+//   level 1 (bits 31..20): histogram built by the score kernel;
+//   select_scan (many work-groups per (sequence, KV head), one chunk of
+//     kSelChunk tokens each): derive the boundary bin b1, write the chunk's
+//     selection-bitmap words for tokens above b1, and copy the chunk's
+//     tokens inside b1 (candidates) into the chunk's own segment of the
+//     candidate buffer with their count;
+//   select_resolve (one work-group per (sequence, KV head)): histogram the
+//     candidates' level-2 digit (bits 19..8), find the boundary b2, mark the
+//     candidates above it and resolve those left in (b1, b2) by (key bits 7..0
+//     descending, token ascending) with an LDS radix select; then list the
+//     selection in ascending token order.
+// The kernel boundary orders the two phases: no global atomics, no fences.
+#include "sf_decode_kernels.h"
+
+namespace sfk {
+
+constexpr int kResThreads = 1024;
+constexpr int kFinMax = 4096;   // level-3 candidates kept in LDS
+
+// 40-bit rank value of a level-3 candidate: low key byte over the inverted
+// token index (larger ranks first; no two candidates are equal).
+__device__ inline uint64_t fin_value(uint2 c) {
+  return ((uint64_t)(c.x & 0xFFu) << 32) | (uint64_t)(0xFFFFFFFFu - c.y);
+}
+
+__global__ void __launch_bounds__(kSelThreads) select_scan(DecodeParams p) {
+  __shared__ uint32_t h[kHistBins];
+  __shared__ uint32_t scan_lds[kSelThreads / 64];
+  __shared__ int sh_bin;
+  __shared__ uint32_t sh_need, sh_cnt;
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int kvh = blockIdx.y;
+  int64_t lo, hi;
+  int first;
+  const int seq = locate_unit(p.seq_off, p.batch, p.sel_chunk, blockIdx.x, false, 0, lo, hi, first);
+  const int chunk = blockIdx.x - first;
+  const int64_t a = p.seq_off[seq];
+  const int64_t n = p.seq_off[seq + 1] - a;
+  const int64_t tn = n < p.top_t ? n : (int64_t)p.top_t;
+  const bool all = (tn == n);
+  const int64_t sk = (int64_t)seq * p.hkv + kvh;
+  uint32_t* bm = p.bitmap + sk * p.bm_words;
+  const float* sc = p.scores + (int64_t)kvh * p.ntot + (a - p.off0);
+  uint2* cand = p.cand + sk * p.max_seq + lo;     // this chunk's segment
+
+  if (!all) {
+    const uint32_t* h1 = p.hist + sk * kHistBins;
+    for (int i = tid; i < kHistBins; i += kSelThreads) h[i] = h1[i];
+    if (tid == 0) sh_cnt = 0u;
+    __syncthreads();
+    find_threshold<kSelThreads, kHistBins>(h, (uint32_t)tn, scan_lds, &sh_bin, &sh_need);
+  }
+  const uint32_t b1 = all ? 0u : (uint32_t)sh_bin;
+  for (int64_t base = lo; base < hi; base += kSelThreads) {
+    const int64_t i = base + tid;
+    const bool valid = i < hi;
+    bool s = false, cnd = false;
+    uint32_t key = 0;
+    if (valid) {
+      if (all) {
+        s = true;
+      } else {
+        key = score_key(sc[i]);
+        const uint32_t bin = key >> (32 - kHistBits);
+        s = bin > b1;
+        cnd = bin == b1;
+      }
+    }
+    const uint64_t bal = __ballot(s);
+    if (lane == 0) {
+      const int64_t w = (base + wid * 64) >> 5;
+      bm[w] = (uint32_t)bal;
+      bm[w + 1] = (uint32_t)(bal >> 32);
+    }
+    const uint64_t cb = __ballot(cnd);
+    if (cb) {
+      uint32_t at = 0;
+      if (lane == 0) at = atomicAdd(&sh_cnt, (uint32_t)__popcll(cb));
+      at = __shfl(at, 0);
+      if (cnd) cand[at + (uint32_t)__popcll(cb & ((1ull << lane) - 1ull))] = make_uint2(key, (uint32_t)i);
+    }
+  }
+  __syncthreads();
+  if (tid == 0) p.counters[sk * p.cnt_stride + chunk] = all ? 0u : sh_cnt;
+}
+
+__global__ void __launch_bounds__(kResThreads) select_resolve(DecodeParams p) {
+  __shared__ uint32_t h[kHistBins];
+  __shared__ uint32_t scan_lds[kResThreads / 64];
+  __shared__ uint32_t rh[256];
+  __shared__ uint2 fin[kFinMax];
+  __shared__ uint32_t segc[kMaxSelChunks];
+  __shared__ int sh_bin;
+  __shared__ uint32_t sh_need, sh_fin;
+
+  const int tid = threadIdx.x;
+  const int64_t sk = blockIdx.x;
+  const int seq = (int)(sk / p.hkv);
+  const int64_t a = p.seq_off[seq];
+  const int64_t n = p.seq_off[seq + 1] - a;
+  const int64_t tn = n < p.top_t ? n : (int64_t)p.top_t;
+  const bool all = (tn == n);
+  uint32_t* bm = p.bitmap + sk * p.bm_words;
+  const uint2* cand = p.cand + sk * p.max_seq;
+  const int nch = (int)((n + p.sel_chunk - 1) / p.sel_chunk);
+
+  if (!all) {
+    // level 1 again (same result as select_scan), then the candidates' level-2 digits
+    const uint32_t* h1 = p.hist + sk * kHistBins;
+    for (int i = tid; i < kHistBins; i += kResThreads) h[i] = h1[i];
+    for (int i = tid; i < nch; i += kResThreads) segc[i] = p.counters[sk * p.cnt_stride + i];
+    if (tid == 0) sh_fin = 0u;
+    __syncthreads();
+    find_threshold<kResThreads, kHistBins>(h, (uint32_t)tn, scan_lds, &sh_bin, &sh_need);
+    const uint32_t need1 = sh_need;
+    for (int i = tid; i < kHistBins; i += kResThreads) h[i] = 0u;
+    __syncthreads();
+    for (int c = 0; c < nch; ++c) {
+      const uint2* seg = cand + (int64_t)c * p.sel_chunk;
+      for (uint32_t j = tid; j < segc[c]; j += kResThreads) atomicAdd(&h[(seg[j].x >> 8) & 0xFFFu], 1u);
+    }
+    __syncthreads();
+    find_threshold<kResThreads, kHistBins>(h, need1, scan_lds, &sh_bin, &sh_need);
+    const uint32_t b2 = (uint32_t)sh_bin, need2 = sh_need;
+    for (int c = 0; c < nch; ++c) {
+      const uint2* seg = cand + (int64_t)c * p.sel_chunk;
+      for (uint32_t j = tid; j < segc[c]; j += kResThreads) {
+        const uint2 cv = seg[j];
+        const uint32_t mid = (cv.x >> 8) & 0xFFFu;
+        if (mid > b2) {
+          atomicOr(&bm[cv.y >> 5], 1u << (cv.y & 31u));
+        } else if (mid == b2) {
+          const uint32_t k = atomicAdd(&sh_fin, 1u);
+          if (k < kFinMax) fin[k] = cv;
+        }
+      }
+    }
+    __syncthreads();
+    const uint32_t m = sh_fin;
+    // level 3: the need2 largest (low key byte, inverted token) among the
+    // candidates sharing the top 24 key bits; radix over 40 bits, 8 per pass
+    uint64_t prefix = 0, mask = 0;
+    uint32_t need = need2;
+    for (int shift = 32; shift >= 0; shift -= 8) {
+      for (int i = tid; i < 256; i += kResThreads) rh[i] = 0u;
+      __syncthreads();
+      if (m <= kFinMax) {
+        for (uint32_t c = tid; c < m; c += kResThreads) {
+          const uint64_t v = fin_value(fin[c]);
+          if ((v & mask) == prefix) atomicAdd(&rh[(v >> shift) & 0xFFu], 1u);
+        }
+      } else {
+        for (int c = 0; c < nch; ++c) {
+          const uint2* seg = cand + (int64_t)c * p.sel_chunk;
+          for (uint32_t j = tid; j < segc[c]; j += kResThreads) {
+            const uint2 cv = seg[j];
+            const uint64_t v = fin_value(cv);
+            if (((cv.x >> 8) & 0xFFFu) == b2 && (v & mask) == prefix) atomicAdd(&rh[(v >> shift) & 0xFFu], 1u);
+          }
+        }
+      }
+      __syncthreads();
+      const uint32_t mine = tid < 256 ? rh[255 - tid] : 0u;
+      uint32_t tot;
+      const uint32_t above = block_exclusive_scan<kResThreads>(mine, scan_lds, tot);
+      if (tid < 256 && above < need && need <= above + mine) {
+        sh_bin = 255 - tid;
+        sh_need = need - above;
+      }
+      __syncthreads();
+      const int d = sh_bin;
+      const uint32_t left = sh_need;
+      const bool whole = rh[d] == left;     // the bucket is taken entirely
+      prefix |= (uint64_t)d << shift;
+      mask |= 0xFFull << shift;
+      need = left;
+      __syncthreads();
+      if (whole) break;
+    }
+    if (m <= kFinMax) {
+      for (uint32_t c = tid; c < m; c += kResThreads) {
+        const uint2 cv = fin[c];
+        if ((fin_value(cv) & mask) >= prefix) atomicOr(&bm[cv.y >> 5], 1u << (cv.y & 31u));
+      }
+    } else {
+      for (int c = 0; c < nch; ++c) {
+        const uint2* seg = cand + (int64_t)c * p.sel_chunk;
+        for (uint32_t j = tid; j < segc[c]; j += kResThreads) {
+          const uint2 cv = seg[j];
+          if (((cv.x >> 8) & 0xFFFu) == b2 && (fin_value(cv) & mask) >= prefix)
+            atomicOr(&bm[cv.y >> 5], 1u << (cv.y & 31u));
+        }
+      }
+    }
+    __threadfence_block();
+    __syncthreads();
+  }
+
+  // List the selection in ascending token order.
+  const int64_t nw = (n + 31) >> 5;
+  const int64_t per = (nw + kResThreads - 1) / kResThreads;
+  const int64_t w0 = tid * per < nw ? tid * per : nw;
+  const int64_t w1 = w0 + per < nw ? w0 + per : nw;
+  uint32_t cnt = 0;
+  for (int64_t w = w0; w < w1; ++w) cnt += __popc(bm[w]);
+  uint32_t tot;
+  uint32_t pos = block_exclusive_scan<kResThreads>(cnt, scan_lds, tot);
+  int32_t* sel = p.sel + sk * p.top_t;
+  int32_t* selo = p.sel_out ? p.sel_out + sk * p.top_t : nullptr;
+  for (int64_t w = w0; w < w1; ++w) {
+    uint32_t bits = bm[w];
+    while (bits) {
+      const int bit = __ffs(bits) - 1;
+      bits &= bits - 1u;
+      const int32_t idx = (int32_t)((w << 5) + bit);
+      if (pos < (uint32_t)p.top_t) {
+        sel[pos] = idx;
+        if (selo) selo[pos] = idx;
+      }
+      ++pos;
+    }
+  }
+  for (int64_t j = tn + tid; j < p.top_t; j += kResThreads) {
+    sel[j] = -1;
+    if (selo) selo[j] = -1;
+  }
+}
+
+void launch_select(const DecodeParams& p, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL(select_scan, grid, dim3(kSelThreads), 0, st, p);
+  hipLaunchKernelGGL(select_resolve, dim3(p.batch * p.hkv), dim3(kResThreads), 0, st, p);
+}
+
+}  // namespace sfk

@@ -79,7 +79,7 @@ class Decoder:
 
     def step(self, cache: LayerCache, q: torch.Tensor, out: Optional[torch.Tensor] = None,
              sel_out: Optional[torch.Tensor] = None, scores_out: Optional[torch.Tensor] = None,
-             want_stats: bool = False, score_events=None, stream=None):
+             want_stats: bool = False, events=None, stream=None):
         if out is None:
             out = torch.empty((self.batch, self.g.n_q_heads, self.g.head_dim), dtype=torch.float32,
                               device=self.device)
@@ -87,6 +87,6 @@ class Decoder:
                               k_codes=cache.k_codes, k_scales=cache.k_scales, v_codes=cache.v_codes,
                               v_scales=cache.v_scales, cap=cache.cap, store=cache.store,
                               top_t=self.top_t, out=out, workspace=self.workspace, sel_out=sel_out,
-                              scores_out=scores_out, want_stats=want_stats, score_events=score_events,
+                              scores_out=scores_out, want_stats=want_stats, events=events,
                               stream=stream)
         return (out, st) if want_stats else out
