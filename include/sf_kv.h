@@ -150,6 +150,13 @@ typedef struct sf_step_stats {
   int64_t h2d_bytes;  /* refinement bytes copied host -> device            */
 } sf_step_stats;
 
+/* sf_decode_args.flags: the score-key histogram at the start of the workspace
+ * is already zero, so the step skips clearing it.  Every successful step
+ * leaves it zero; it holds for a workspace that the previous successful step
+ * used with the same batch size and KV-head count, or that the caller
+ * zero-filled.  Do not pass it after a failed step. */
+#define SF_DECODE_HIST_CLEAN 1
+
 typedef struct sf_decode_args {
   int32_t batch;                 /* B >= 1 sequences                                    */
   const int64_t* seq_off_host;   /* host [B+1], nondecreasing, every sequence non-empty,
@@ -172,7 +179,7 @@ typedef struct sf_decode_args {
   sf_step_stats* stats;          /* optional host; filled when the call returns         */
   void* workspace;               /* device scratch of sf_decode_workspace_size() bytes  */
   size_t workspace_bytes;
-  int32_t flags;                 /* 0 (reserved)                                        */
+  int32_t flags;                 /* 0 or SF_DECODE_HIST_CLEAN                           */
   void* events[4];               /* optional hipEvent_t recorded on `stream` before and
                                     after the score kernel ([0], [1]) and before and
                                     after the attention kernel ([2], [3]); NULL = none.
@@ -202,7 +209,9 @@ sf_status sf_decode_workspace_size(const sf_geom* geom, int32_t batch, int64_t t
  * again and the refinement rows of the selection), combine.  Device-tier
  * stores and T == 0 need no host round trip; a host-pinned store synchronizes
  * the stream once per call to learn which rows to fetch.
- * The workspace need not be initialised; its contents are undefined after.
+ * The workspace need not be initialised (unless SF_DECODE_HIST_CLEAN is
+ * passed); apart from the histogram it leaves zero, its contents are
+ * undefined after the call.
  */
 sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* args, void* stream);
 

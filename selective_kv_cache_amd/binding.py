@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(HERE, "libsf_kv.so")
 SF_OK, SF_ERR_INVALID_ARG, SF_ERR_UNSUPPORTED, SF_ERR_HIP, SF_ERR_OOM, SF_ERR_TIMEOUT = 0, -1, -2, -3, -4, -5
 SF_TIER_DEVICE, SF_TIER_HOST_PINNED = 0, 1
 SF_K, SF_V = 0, 1
+SF_DECODE_HIST_CLEAN = 1
 
 c_i32, c_i64, c_vp, c_size = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
 
@@ -153,7 +154,7 @@ def sf_decode_workspace_size(g: sf_geom, batch: int, total_tokens: int, max_seq_
 
 def sf_decode_step(g: sf_geom, *, seq_off_host: Sequence[int], seq_off_dev, q, k_codes, k_scales, v_codes,
                    v_scales, cap: int, store: Optional[int], top_t: int, out, workspace, sel_out=None,
-                   scores_out=None, want_stats: bool = False, events=None, stream=None):
+                   scores_out=None, want_stats: bool = False, events=None, stream=None, flags: int = 0):
     """One decode step; returns the step statistics as a dict when asked."""
     off = np.ascontiguousarray(np.asarray(seq_off_host, dtype=np.int64))
     a = sf_decode_args()
@@ -168,7 +169,7 @@ def sf_decode_step(g: sf_geom, *, seq_off_host: Sequence[int], seq_off_dev, q, k
     a.stats = ctypes.pointer(st) if want_stats else None
     a.workspace = _ptr(workspace)
     a.workspace_bytes = workspace.numel() * workspace.element_size()
-    a.flags = 0
+    a.flags = flags
     if events is not None:       # (score begin, score end, attend begin, attend end), None allowed
         for i, e in enumerate(events):
             a.events[i] = None if e is None else (e.cuda_event if hasattr(e, "cuda_event") else e)

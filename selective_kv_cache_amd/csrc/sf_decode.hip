@@ -73,8 +73,10 @@ Carve carve(const sf_geom& g, int32_t batch, int64_t total_tokens, int64_t max_s
   const int64_t t = top_t > 0 ? top_t : 1;
   Carve c{};
   size_t at = 0;
-  c.scores = at; at += align256((size_t)hkv * total_tokens * 4);
+  // the histogram comes first: its place depends on (batch, hkv) only, so a
+  // workspace that a step left with a zero histogram can be reused as such
   c.hist = at; at += align256((size_t)batch * hkv * kHistBins * 4);
+  c.scores = at; at += align256((size_t)hkv * total_tokens * 4);
   c.counters = at; at += align256((size_t)batch * hkv * ((max_seq_tokens + kSelChunk - 1) / kSelChunk) * 4);
   c.cand = at; at += align256((size_t)batch * hkv * max_seq_tokens * 8);
   c.bitmap = at; at += align256((size_t)batch * hkv * bm_words * 4);
@@ -119,7 +121,7 @@ extern "C" sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* a
   if (s != SF_OK) return s;
   if (!a || a->batch <= 0 || !a->seq_off_host || !a->seq_off_dev || !a->q || !a->k_codes ||
       !a->k_scales || !a->v_codes || !a->v_scales || !a->out || !a->workspace || a->cap <= 0 ||
-      a->top_t < 0 || a->flags != 0 || (!a->events[0] != !a->events[1]) || (!a->events[2] != !a->events[3]))
+      a->top_t < 0 || (a->flags & ~SF_DECODE_HIST_CLEAN) != 0 || (!a->events[0] != !a->events[1]) || (!a->events[2] != !a->events[3]))
     return SF_ERR_INVALID_ARG;
   const int32_t B = a->batch;
   const int64_t* off = a->seq_off_host;
@@ -208,10 +210,13 @@ extern "C" sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* a
   }
 
   hipStream_t hs = (hipStream_t)stream;
-  const int64_t nzero = (int64_t)B * p.hkv * kHistBins;
-  hipLaunchKernelGGL(zero_words, dim3((unsigned)std::min<int64_t>((nzero + 255) / 256, 1024)), dim3(256), 0, hs,
-                     reinterpret_cast<uint32_t*>(ws + c.hist), nzero);
-  SF_LAUNCH_CHECK("zero_words");
+  if (a->top_t > 0 && !(a->flags & SF_DECODE_HIST_CLEAN)) {
+    // select_resolve clears the histogram again once it has been read
+    const int64_t nzero = (int64_t)B * p.hkv * kHistBins;
+    hipLaunchKernelGGL(zero_words, dim3((unsigned)std::min<int64_t>((nzero + 255) / 256, 1024)), dim3(256), 0, hs,
+                       reinterpret_cast<uint32_t*>(ws + c.hist), nzero);
+    SF_LAUNCH_CHECK("zero_words");
+  }
   if (a->events[0]) SF_HIP_CHECK(hipEventRecord((hipEvent_t)a->events[0], hs));
   if (!launch_score(p, dim3(n_score, p.hkv), hs)) return SF_ERR_UNSUPPORTED;
   SF_LAUNCH_CHECK("score");

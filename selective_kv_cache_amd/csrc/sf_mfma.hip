@@ -127,6 +127,7 @@ __global__ void __launch_bounds__(256) score_mfma(DecodeParams p) {
   int first;
   const int seq = locate_unit(p.seq_off, p.batch, p.score_split, blockIdx.x, false, 0, lo, hi, first);
   const int64_t a = p.seq_off[seq];
+  const bool hist = p.top_t > 0;   // no selection, no histogram
   for (int i = tid; i < kHistBins; i += 256) lhist[i] = 0u;
   v4i a0, a1;
   prep_query<G>(p.q + ((int64_t)seq * p.hq + kvh * G) * kHeadDim, qp, a0, a1);
@@ -160,10 +161,11 @@ __global__ void __launch_bounds__(256) score_mfma(DecodeParams p) {
       lg = fmaxf(lg, __shfl_xor(lg, 32));
       if (hl == 0 && li[u] < hi) {
         scores[li[u]] = lg;
-        atomicAdd(&lhist[score_key(lg) >> (32 - kHistBits)], 1u);
+        if (hist) atomicAdd(&lhist[score_key(lg) >> (32 - kHistBits)], 1u);
       }
     }
   }
+  if (!hist) return;
   __syncthreads();
   uint32_t* gh = p.hist + ((int64_t)seq * p.hkv + kvh) * kHistBins;   // level-1 histogram
   for (int i = tid; i < kHistBins; i += 256) {

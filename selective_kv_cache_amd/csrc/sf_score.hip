@@ -40,6 +40,7 @@ __global__ void __launch_bounds__(256) score_valu(DecodeParams p) {
   const int64_t a = p.seq_off[seq];
   for (int i = tid; i < G * kHeadDim; i += 256)
     qs[i / kHeadDim][i % kHeadDim] = p.q[((int64_t)seq * p.hq + kvh * G) * kHeadDim + i];
+  const bool hist = p.top_t > 0;   // no selection, no histogram
   for (int i = tid; i < kHistBins; i += 256) lhist[i] = 0u;
   __syncthreads();
   if (tid < G) {
@@ -76,8 +77,9 @@ __global__ void __launch_bounds__(256) score_valu(DecodeParams p) {
     for (int h = 0; h < G; ++h)
       best = fmaxf(best, (sk.x * qsum[h] + sk.y * (dot[h] + 0.5f * qsum[h])) * kRsqrtD);
     scores[i] = best;
-    atomicAdd(&lhist[score_key(best) >> (32 - kHistBits)], 1u);
+    if (hist) atomicAdd(&lhist[score_key(best) >> (32 - kHistBits)], 1u);
   }
+  if (!hist) return;
   __syncthreads();
   uint32_t* gh = p.hist + ((int64_t)seq * p.hkv + kvh) * kHistBins;   // level-1 histogram
   for (int i = tid; i < kHistBins; i += 256) {

@@ -94,12 +94,26 @@ __global__ void __launch_bounds__(kSelThreads) select_scan(DecodeParams p) {
   if (tid == 0) p.counters[sk * p.cnt_stride + chunk] = all ? 0u : sh_cnt;
 }
 
+// Candidate j of a (sequence, KV head): segments of the chunks laid end to end
+// (prefix offsets in LDS, binary search over at most kMaxSelChunks entries).
+__device__ inline uint2 cand_at(const uint2* cand, const uint32_t* segoff, int nch, int32_t chunk_len, uint32_t j) {
+  int lo = 0, hi = nch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (segoff[mid] <= j) lo = mid; else hi = mid - 1;
+  }
+  return cand[(int64_t)lo * chunk_len + (j - segoff[lo])];
+}
+
+constexpr int kLdsBitmapWords = 16384;   // sequences up to 512K tokens keep the bitmap in LDS
+
 __global__ void __launch_bounds__(kResThreads) select_resolve(DecodeParams p) {
   __shared__ uint32_t h[kHistBins];
   __shared__ uint32_t scan_lds[kResThreads / 64];
   __shared__ uint32_t rh[256];
   __shared__ uint2 fin[kFinMax];
-  __shared__ uint32_t segc[kMaxSelChunks];
+  __shared__ uint32_t segoff[kMaxSelChunks + 1];
+  __shared__ uint32_t lbm[kLdsBitmapWords];
   __shared__ int sh_bin;
   __shared__ uint32_t sh_need, sh_fin;
 
@@ -110,64 +124,84 @@ __global__ void __launch_bounds__(kResThreads) select_resolve(DecodeParams p) {
   const int64_t n = p.seq_off[seq + 1] - a;
   const int64_t tn = n < p.top_t ? n : (int64_t)p.top_t;
   const bool all = (tn == n);
-  uint32_t* bm = p.bitmap + sk * p.bm_words;
+  uint32_t* gbm = p.bitmap + sk * p.bm_words;
   const uint2* cand = p.cand + sk * p.max_seq;
   const int nch = (int)((n + p.sel_chunk - 1) / p.sel_chunk);
+  const int64_t nw = (n + 31) >> 5;
+  const bool in_lds = nw <= kLdsBitmapWords;
+  uint32_t* bm = in_lds ? lbm : gbm;
+  if (in_lds)
+    for (int64_t w = tid; w < nw; w += kResThreads) lbm[w] = gbm[w];
 
+  // level 1 again (same result as select_scan); the global histogram is left
+  // zero for the next step
+  uint32_t* h1 = p.hist + sk * kHistBins;
+  for (int i = tid; i < kHistBins; i += kResThreads) {
+    if (!all) h[i] = h1[i];
+    h1[i] = 0u;
+  }
   if (!all) {
-    // level 1 again (same result as select_scan), then the candidates' level-2 digits
-    const uint32_t* h1 = p.hist + sk * kHistBins;
-    for (int i = tid; i < kHistBins; i += kResThreads) h[i] = h1[i];
-    for (int i = tid; i < nch; i += kResThreads) segc[i] = p.counters[sk * p.cnt_stride + i];
-    if (tid == 0) sh_fin = 0u;
+    // then the candidates' level-2 digits
+    // segment offsets: exclusive prefix of the per-chunk candidate counts
+    {
+      const int per = (nch + kResThreads - 1) / kResThreads;
+      uint32_t c = 0;
+      for (int k = tid * per; k < nch && k < (tid + 1) * per; ++k) c += p.counters[sk * p.cnt_stride + k];
+      uint32_t tot;
+      uint32_t run = block_exclusive_scan<kResThreads>(c, scan_lds, tot);
+      for (int k = tid * per; k < nch && k < (tid + 1) * per; ++k) {
+        segoff[k] = run;
+        run += p.counters[sk * p.cnt_stride + k];
+      }
+      if (tid == 0) {
+        segoff[nch] = tot;
+        sh_fin = 0u;
+      }
+    }
     __syncthreads();
+    const uint32_t ncand = segoff[nch];
     find_threshold<kResThreads, kHistBins>(h, (uint32_t)tn, scan_lds, &sh_bin, &sh_need);
     const uint32_t need1 = sh_need;
     for (int i = tid; i < kHistBins; i += kResThreads) h[i] = 0u;
     __syncthreads();
-    for (int c = 0; c < nch; ++c) {
-      const uint2* seg = cand + (int64_t)c * p.sel_chunk;
-      for (uint32_t j = tid; j < segc[c]; j += kResThreads) atomicAdd(&h[(seg[j].x >> 8) & 0xFFFu], 1u);
-    }
+    for (uint32_t j = tid; j < ncand; j += kResThreads)
+      atomicAdd(&h[(cand_at(cand, segoff, nch, p.sel_chunk, j).x >> 8) & 0xFFFu], 1u);
     __syncthreads();
     find_threshold<kResThreads, kHistBins>(h, need1, scan_lds, &sh_bin, &sh_need);
     const uint32_t b2 = (uint32_t)sh_bin, need2 = sh_need;
-    for (int c = 0; c < nch; ++c) {
-      const uint2* seg = cand + (int64_t)c * p.sel_chunk;
-      for (uint32_t j = tid; j < segc[c]; j += kResThreads) {
-        const uint2 cv = seg[j];
-        const uint32_t mid = (cv.x >> 8) & 0xFFFu;
-        if (mid > b2) {
-          atomicOr(&bm[cv.y >> 5], 1u << (cv.y & 31u));
-        } else if (mid == b2) {
-          const uint32_t k = atomicAdd(&sh_fin, 1u);
-          if (k < kFinMax) fin[k] = cv;
-        }
+    for (uint32_t j = tid; j < ncand; j += kResThreads) {
+      const uint2 cv = cand_at(cand, segoff, nch, p.sel_chunk, j);
+      const uint32_t mid = (cv.x >> 8) & 0xFFFu;
+      if (mid > b2) {
+        atomicOr(&bm[cv.y >> 5], 1u << (cv.y & 31u));
+      } else if (mid == b2) {
+        const uint32_t k = atomicAdd(&sh_fin, 1u);
+        if (k < kFinMax) fin[k] = cv;
       }
     }
     __syncthreads();
     const uint32_t m = sh_fin;
     // level 3: the need2 largest (low key byte, inverted token) among the
     // candidates sharing the top 24 key bits; radix over 40 bits, 8 per pass
+    auto get = [&](uint32_t j, bool& ok) -> uint64_t {
+      if (m <= kFinMax) {
+        ok = true;
+        return fin_value(fin[j]);
+      }
+      const uint2 cv = cand_at(cand, segoff, nch, p.sel_chunk, j);
+      ok = ((cv.x >> 8) & 0xFFFu) == b2;
+      return fin_value(cv);
+    };
+    const uint32_t cnt = m <= kFinMax ? m : ncand;
     uint64_t prefix = 0, mask = 0;
     uint32_t need = need2;
     for (int shift = 32; shift >= 0; shift -= 8) {
       for (int i = tid; i < 256; i += kResThreads) rh[i] = 0u;
       __syncthreads();
-      if (m <= kFinMax) {
-        for (uint32_t c = tid; c < m; c += kResThreads) {
-          const uint64_t v = fin_value(fin[c]);
-          if ((v & mask) == prefix) atomicAdd(&rh[(v >> shift) & 0xFFu], 1u);
-        }
-      } else {
-        for (int c = 0; c < nch; ++c) {
-          const uint2* seg = cand + (int64_t)c * p.sel_chunk;
-          for (uint32_t j = tid; j < segc[c]; j += kResThreads) {
-            const uint2 cv = seg[j];
-            const uint64_t v = fin_value(cv);
-            if (((cv.x >> 8) & 0xFFFu) == b2 && (v & mask) == prefix) atomicAdd(&rh[(v >> shift) & 0xFFu], 1u);
-          }
-        }
+      for (uint32_t j = tid; j < cnt; j += kResThreads) {
+        bool ok;
+        const uint64_t v = get(j, ok);
+        if (ok && (v & mask) == prefix) atomicAdd(&rh[(v >> shift) & 0xFFu], 1u);
       }
       __syncthreads();
       const uint32_t mine = tid < 256 ? rh[255 - tid] : 0u;
@@ -187,27 +221,17 @@ __global__ void __launch_bounds__(kResThreads) select_resolve(DecodeParams p) {
       __syncthreads();
       if (whole) break;
     }
-    if (m <= kFinMax) {
-      for (uint32_t c = tid; c < m; c += kResThreads) {
-        const uint2 cv = fin[c];
-        if ((fin_value(cv) & mask) >= prefix) atomicOr(&bm[cv.y >> 5], 1u << (cv.y & 31u));
-      }
-    } else {
-      for (int c = 0; c < nch; ++c) {
-        const uint2* seg = cand + (int64_t)c * p.sel_chunk;
-        for (uint32_t j = tid; j < segc[c]; j += kResThreads) {
-          const uint2 cv = seg[j];
-          if (((cv.x >> 8) & 0xFFFu) == b2 && (fin_value(cv) & mask) >= prefix)
-            atomicOr(&bm[cv.y >> 5], 1u << (cv.y & 31u));
-        }
-      }
+    for (uint32_t j = tid; j < cnt; j += kResThreads) {
+      bool ok;
+      const uint64_t v = get(j, ok);
+      const uint32_t tok = m <= kFinMax ? fin[j].y : cand_at(cand, segoff, nch, p.sel_chunk, j).y;
+      if (ok && (v & mask) >= prefix) atomicOr(&bm[tok >> 5], 1u << (tok & 31u));
     }
-    __threadfence_block();
-    __syncthreads();
   }
+  __syncthreads();
 
-  // List the selection in ascending token order.
-  const int64_t nw = (n + 31) >> 5;
+  // List the selection in ascending token order; the final bitmap goes back
+  // to global memory for the attention pass.
   const int64_t per = (nw + kResThreads - 1) / kResThreads;
   const int64_t w0 = tid * per < nw ? tid * per : nw;
   const int64_t w1 = w0 + per < nw ? w0 + per : nw;
@@ -219,6 +243,7 @@ __global__ void __launch_bounds__(kResThreads) select_resolve(DecodeParams p) {
   int32_t* selo = p.sel_out ? p.sel_out + sk * p.top_t : nullptr;
   for (int64_t w = w0; w < w1; ++w) {
     uint32_t bits = bm[w];
+    if (in_lds) gbm[w] = bits;
     while (bits) {
       const int bit = __ffs(bits) - 1;
       bits &= bits - 1u;

@@ -76,6 +76,7 @@ class Decoder:
         self.seq_off_dev = torch.as_tensor(self.seq_off, device=self.device)
         nbytes = B.sf_decode_workspace_size(g, self.batch, self.total, self.max_seq, top_t)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        self._hist_clean = False   # a successful step leaves the workspace histogram zero
 
     def step(self, cache: LayerCache, q: torch.Tensor, out: Optional[torch.Tensor] = None,
              sel_out: Optional[torch.Tensor] = None, scores_out: Optional[torch.Tensor] = None,
@@ -83,10 +84,13 @@ class Decoder:
         if out is None:
             out = torch.empty((self.batch, self.g.n_q_heads, self.g.head_dim), dtype=torch.float32,
                               device=self.device)
+        flags = B.SF_DECODE_HIST_CLEAN if self._hist_clean else 0
+        self._hist_clean = False
         st = B.sf_decode_step(self.g, seq_off_host=self.seq_off, seq_off_dev=self.seq_off_dev, q=q,
                               k_codes=cache.k_codes, k_scales=cache.k_scales, v_codes=cache.v_codes,
                               v_scales=cache.v_scales, cap=cache.cap, store=cache.store,
                               top_t=self.top_t, out=out, workspace=self.workspace, sel_out=sel_out,
                               scores_out=scores_out, want_stats=want_stats, events=events,
-                              stream=stream)
+                              stream=stream, flags=flags)
+        self._hist_clean = True
         return (out, st) if want_stats else out

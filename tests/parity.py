@@ -3,7 +3,7 @@ and through the oracle on the same seeded inputs, and compare."""
 from __future__ import annotations
 
 import dataclasses
-from typing import Dict, Optional, Sequence, Tuple
+from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -35,6 +35,13 @@ def geom_of(w: W.Workload):
 
 def run_gpu(w: W.Workload, k: np.ndarray, v: np.ndarray, q: np.ndarray, seq_off: Sequence[int],
             top_t: int, tier: int = 0, cap_extra: int = 0) -> GpuRun:
+    return run_gpu_steps(w, k, v, q[None], seq_off, top_t, tier=tier, cap_extra=cap_extra)[0]
+
+
+def run_gpu_steps(w: W.Workload, k: np.ndarray, v: np.ndarray, qs: np.ndarray, seq_off: Sequence[int],
+                  top_t: int, tier: int = 0, cap_extra: int = 0) -> List[GpuRun]:
+    """Decode steps with the queries qs[0], qs[1], ... on one cache and one
+    workspace (steps after the first reuse the histogram the last one cleared)."""
     import torch
     from selective_kv_cache_amd.kvcache import Decoder, LayerCache
     g = geom_of(w)
@@ -46,14 +53,18 @@ def run_gpu(w: W.Workload, k: np.ndarray, v: np.ndarray, q: np.ndarray, seq_off:
         vd = torch.as_tensor(v, device="cuda")
         refs = cache.append(kd, vd, 0, keep_refine=True)
         dec = Decoder(g, seq_off, top_t)
-        sel = torch.full((dec.batch, w.n_kv_heads, top_t), -7, dtype=torch.int32, device="cuda")
-        scores = torch.empty((w.n_kv_heads, dec.total), dtype=torch.float32, device="cuda")
-        out = dec.step(cache, torch.as_tensor(q, device="cuda"), sel_out=sel, scores_out=scores)
-        torch.cuda.synchronize()
         cpu = lambda t: None if t is None else t.cpu().numpy()
-        return GpuRun(out=cpu(out), sel=cpu(sel), scores=cpu(scores), k_codes=cpu(cache.k_codes),
-                      v_codes=cpu(cache.v_codes), k_scales=cpu(cache.k_scales), v_scales=cpu(cache.v_scales),
-                      k_ref=cpu(refs[0]) if refs else None, v_ref=cpu(refs[1]) if refs else None)
+        runs = []
+        for q in qs:
+            sel = torch.full((dec.batch, w.n_kv_heads, top_t), -7, dtype=torch.int32, device="cuda")
+            scores = torch.empty((w.n_kv_heads, dec.total), dtype=torch.float32, device="cuda")
+            out = dec.step(cache, torch.as_tensor(q, device="cuda"), sel_out=sel, scores_out=scores)
+            torch.cuda.synchronize()
+            runs.append(GpuRun(out=cpu(out), sel=cpu(sel), scores=cpu(scores), k_codes=cpu(cache.k_codes),
+                               v_codes=cpu(cache.v_codes), k_scales=cpu(cache.k_scales),
+                               v_scales=cpu(cache.v_scales), k_ref=cpu(refs[0]) if refs else None,
+                               v_ref=cpu(refs[1]) if refs else None))
+        return runs
     finally:
         cache.close()
 

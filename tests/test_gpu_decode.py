@@ -112,6 +112,18 @@ def test_deterministic_repeat():
     assert np.array_equal(a.sel, b.sel)
 
 
+def test_consecutive_steps_share_one_workspace():
+    # each step clears the selection histogram for the next one; a stale
+    # count would move the cut of a later step
+    w = W.small("steps", cfg_id=303, batch=2, n_q_heads=8, n_kv_heads=2, top_t=96, rho=0.5)
+    off = W.seq_offsets([2500, 1100])
+    k, v = W.layer_kv(w, 0, n_tok=int(off[-1]))
+    qs = W.queries(w, 0, 4)
+    runs = P.run_gpu_steps(w, k, v, qs, off, w.top_t)
+    for q, run in zip(qs, runs):
+        P.compare_layer(w, k, v, q, off, w.top_t, run, codec=False)
+
+
 def test_host_tier_matches_device_tier_and_cache_simulation():
     """Host-pinned store + device refinement cache over several steps of an
     AR(1) query process: outputs bit-identical to the device-resident store,
