@@ -23,6 +23,7 @@
 // The codes of 8 tokens at one element are gathered with one v_perm_b32 per
 // token pair, so the packed rows are read as they are stored.
 #include <math.h>
+#include <stddef.h>
 
 #include "sf_attend_common.h"
 
@@ -178,13 +179,92 @@ __global__ void __launch_bounds__(256) score_mfma(DecodeParams p) {
 // Base attention pass over one split (selected tokens left out): 4
 // wavefronts, chunks of 32 tokens (two logit tiles, one P.V step).
 // ---------------------------------------------------------------------------
+// The base pass streams its split through a per-wavefront ring of LDS stages
+// filled by direct global->LDS loads (global_load_lds: lane i's 16 or 4 bytes
+// land at stage offset 16*i or 4*i), so the loads in flight hold no
+// registers.  One stage is one 32-token chunk: K codes, V codes (1 KiB each,
+// as stored), K and V scales (256 B each).
+constexpr int kRing = 4;                       // stages per wavefront; kRing - 1 chunks in flight
+constexpr int kRingLoads = 4;                  // direct loads per stage
+constexpr int kMaxSplitWords = 4096 / 32;      // selection words of the longest split
+
+struct Stage {
+  uint8_t k[32 * 32];
+  uint8_t v[32 * 32];
+  float2 ks[32];
+  float2 vs[32];
+};
+
 template <int G>
 struct MfmaLds {
   QPrep<G> qp;
   alignas(16) _Float16 wt[4][16][32];   // per wave: P.V weights [column][token]
   float mw[4][G], lw[4][G];
-  float accw[4][G][kHeadDim];
+  uint32_t selw[kMaxSplitWords];        // the split's selection bitmap
+  union {
+    Stage ring[4][kRing];
+    float accw[4][G][kHeadDim];         // after the stream: per-wave P.V totals
+  } u;
 };
+
+typedef __attribute__((address_space(3))) void* lds_void_t;
+
+__device__ inline void dma16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t)l, 16, 0, 0);
+}
+__device__ inline void dma4(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t)l, 4, 0, 0);
+}
+
+__device__ inline uint32_t lds_addr(const void* l) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)l;
+}
+
+// One lane's operands of a stage.  The LDS reads are written in asm: a read
+// the compiler sees makes it wait for every direct load in flight (it cannot
+// tell the ring stages apart), which would serialise the stream.  The block
+// waits for its own reads before it ends, so every output is complete.
+struct StageRegs {
+  uint64_t kw[2];          // K code bytes of tiles 0, 1 (token t, bytes 8hl..8hl+7)
+  uint64_t ksc[2], vsc[2]; // (lo, delta) of tokens t, 16 + t
+  uint32_t vw[8];          // V dword vdw of tokens 8rg..8rg+7
+};
+
+__device__ inline void read_stage(uint32_t aK, uint32_t aS, uint32_t aV, StageRegs& r) {
+  asm volatile(
+      "ds_read_b64 %0, %14\n\t"
+      "ds_read_b64 %1, %14 offset:512\n\t"
+      "ds_read_b64 %2, %15\n\t"
+      "ds_read_b64 %3, %15 offset:128\n\t"
+      "ds_read_b64 %4, %15 offset:256\n\t"
+      "ds_read_b64 %5, %15 offset:384\n\t"
+      "ds_read_b32 %6, %16\n\t"
+      "ds_read_b32 %7, %16 offset:32\n\t"
+      "ds_read_b32 %8, %16 offset:64\n\t"
+      "ds_read_b32 %9, %16 offset:96\n\t"
+      "ds_read_b32 %10, %16 offset:128\n\t"
+      "ds_read_b32 %11, %16 offset:160\n\t"
+      "ds_read_b32 %12, %16 offset:192\n\t"
+      "ds_read_b32 %13, %16 offset:224\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r.kw[0]), "=&v"(r.kw[1]), "=&v"(r.ksc[0]), "=&v"(r.ksc[1]), "=&v"(r.vsc[0]), "=&v"(r.vsc[1]),
+        "=&v"(r.vw[0]), "=&v"(r.vw[1]), "=&v"(r.vw[2]), "=&v"(r.vw[3]), "=&v"(r.vw[4]), "=&v"(r.vw[5]),
+        "=&v"(r.vw[6]), "=&v"(r.vw[7])
+      : "v"(aK), "v"(aS), "v"(aV)
+      : "memory");
+}
+
+__device__ inline uint32_t lds_read_u32(uint32_t a) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(a) : "memory");
+  return v;
+}
+
+__device__ inline v8h lds_read_v8h(uint32_t a) {
+  v4u v;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(a) : "memory");
+  return __builtin_bit_cast(v8h, v);
+}
 
 template <int G>
 __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh, uint8_t* smem) {
@@ -196,65 +276,79 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   const int seq = locate_unit(p.seq_off, p.batch, p.split, split, false, 0, lo, hi, first);
   const int64_t a = p.seq_off[seq];
   const int64_t sk = (int64_t)seq * p.hkv + kvh;
-  const uint32_t* bm = p.bitmap + sk * p.bm_words;
   const bool masked = p.use_refine != 0;
+  const uint8_t* kbase = p.kc + ((int64_t)kvh * p.cap + a) * 32;
+  const uint8_t* vbase = p.vc + ((int64_t)kvh * p.cap + a) * 32;
+  const float* kscg = p.ks + ((int64_t)kvh * p.cap + a) * 2;
+  const float* vscg = p.vs + ((int64_t)kvh * p.cap + a) * 2;
+  const int nchunks = (int)((hi - lo + 31) / 32);
+  const int nmine = nchunks > wid ? (nchunks - wid + 3) / 4 : 0;   // chunks wid, wid+4, ...
+
+  // Stage i of this wave <- chunk wid + 4*i.  Lane L loads K/V bytes
+  // [16L, 16L+16) and scale word L of the chunk (token L/2); tokens past the
+  // split's end read its last token instead, and loads past the wave's last
+  // chunk repeat that token too, so every issue is four in-bounds loads.
+  auto issue = [&](int i) {
+    const int c = wid + 4 * i;
+    int64_t li = lo + 32 * (int64_t)c + (lane >> 1);
+    li = li < hi ? li : hi - 1;
+    Stage& st = s.u.ring[wid][i % kRing];
+    dma16(kbase + li * 32 + 16 * (lane & 1), st.k);
+    dma16(vbase + li * 32 + 16 * (lane & 1), st.v);
+    dma4(kscg + li * 2 + (lane & 1), st.ks);
+    dma4(vscg + li * 2 + (lane & 1), st.vs);
+  };
+#pragma unroll
+  for (int i = 0; i < kRing - 1; ++i) issue(i);
+
   for (int i = lane; i < 16 * 32; i += 64) (&s.wt[wid][0][0])[i] = (_Float16)0.f;
+  if (tid < kMaxSplitWords) {
+    const int64_t w0 = lo >> 5;                     // splits start on a word boundary
+    s.selw[tid] = (masked && tid < (nchunks)) ? p.bitmap[sk * p.bm_words + w0 + tid] : 0u;
+  }
   v4i a0, a1;
   prep_query<G>(p.q + ((int64_t)seq * p.hq + kvh * G) * kHeadDim, s.qp, a0, a1);
   const int t = lane & 15, hl = lane >> 4;        // logit layout: token t, head hl
   const int n = lane & 15, rg = lane >> 4;        // P.V layout: column n, element rows 4rg..4rg+3
   const float scale = s.qp.scale[hl < G ? hl : 0], sumq = s.qp.sumq[hl < G ? hl : 0];
-  const uint8_t* kbase = p.kc + (int64_t)kvh * p.cap * 32;
-  const uint8_t* vbase = p.vc + (int64_t)kvh * p.cap * 32;
-  const float2* kscg = reinterpret_cast<const float2*>(p.ks) + (int64_t)kvh * p.cap;
-  const float2* vscg = reinterpret_cast<const float2*>(p.vs) + (int64_t)kvh * p.cap;
   // v_perm_b32 selector: half (n & 1) of each of two dwords
   const uint32_t hsel = 2u * (uint32_t)(n & 1);
   const uint32_t psel = hsel | ((hsel + 1u) << 8) | ((hsel + 4u) << 16) | ((hsel + 5u) << 24);
   const int vdw = n >> 1;                         // dword of the V row holding elements 8n..8n+7
+
+  // LDS addresses of this lane's stage operands (offsets into a stage)
+  const uint32_t ring0 = lds_addr(&s.u.ring[wid][0]);
+  const uint32_t sel0 = lds_addr(&s.selw[0]);
+  const uint32_t wt0 = lds_addr(&s.wt[wid][n][8 * rg]);
+  const uint32_t offK = (uint32_t)(t * 32 + 8 * hl);
+  const uint32_t offS = (uint32_t)(offsetof(Stage, ks) + 8 * t);
+  const uint32_t offV = (uint32_t)(offsetof(Stage, v) + (8 * rg) * 32 + 4 * vdw);
+  static_assert(offsetof(Stage, vs) == offsetof(Stage, ks) + 256, "scale blocks are adjacent");
 
   float m = -INFINITY, lsum = 0.f, t1 = 0.f;
   int sexp = 127;                                 // weight scale 2^sexp; 127 = not set yet
   v4f acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
-  const int nchunks = (int)((hi - lo + 31) / 32);
-  // loads of one chunk: K codes and scales of the two logit tiles (token t),
-  // V scales (token t), V dwords (8 tokens of lane group rg), selection bits
-  struct ChunkLoad {
+  for (int i = 0; i < nmine; ++i) {
+    issue(i + kRing - 1);
+    // this wave's loads complete in order: all but the newest kRing - 1 stages
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kRingLoads * (kRing - 1)) : "memory");
+    const int c = wid + 4 * i;
+    const uint32_t sb = ring0 + (uint32_t)(i % kRing) * (uint32_t)sizeof(Stage);
+    const int64_t base = lo + 32 * (int64_t)c;
+    const uint32_t selw = lds_read_u32(sel0 + 4u * (uint32_t)c);
+    StageRegs R;
+    read_stage(sb + offK, sb + offS, sb + offV, R);
     uint2 kw[2];
     float2 ksc[2], vsc[2];
-    uint32_t vw[8];
-    uint32_t selw;
-  };
-  auto load_chunk = [&](int c, ChunkLoad& L) {
-    const int64_t base = lo + 32 * (int64_t)c;
-    L.selw = masked ? bm[base >> 5] : 0u;
+    const uint32_t* vw = R.vw;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const int64_t li = base + 16 * k + t;
-      const int64_t tok = a + (li < hi ? li : lo);
-      L.kw[k] = *reinterpret_cast<const uint2*>(kbase + tok * 32 + 8 * hl);
-      L.ksc[k] = kscg[tok];
-      L.vsc[k] = vscg[tok];
+      kw[k] = __builtin_bit_cast(uint2, R.kw[k]);
+      ksc[k] = __builtin_bit_cast(float2, R.ksc[k]);
+      vsc[k] = __builtin_bit_cast(float2, R.vsc[k]);
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int64_t li = base + 8 * rg + e;
-      const int64_t tok = a + (li < hi ? li : lo);
-      L.vw[e] = *reinterpret_cast<const uint32_t*>(vbase + tok * 32 + 4 * vdw);
-    }
-  };
-  ChunkLoad cur, nxt;
-  if (wid < nchunks) load_chunk(wid, cur);
-  for (int c = wid; c < nchunks; c += 4) {
-    if (c + 4 < nchunks) load_chunk(c + 4, nxt);     // next chunk's loads in flight meanwhile
-    const int64_t base = lo + 32 * (int64_t)c;
-    const uint32_t selw = cur.selw;
-    const uint2* kw = cur.kw;
-    const float2* ksc = cur.ksc;
-    const float2* vsc = cur.vsc;
-    const uint32_t* vw = cur.vw;
     bool ok[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) ok[k] = base + 16 * k + t < hi && !((selw >> (16 * k + t)) & 1u);
@@ -292,7 +386,7 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
       if (need < sexp && sexp != 127) f = __builtin_ldexpf(f, need - sexp);
       if (need < sexp) sexp = need;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] *= f;
+      for (int j = 0; j < 8; ++j) acc[j] *= f;
       m = mnew;
     }
     const int se = sexp == 127 ? 0 : sexp;
@@ -310,7 +404,7 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
       }
     }
     wave_barrier();
-    const v8h bw = *reinterpret_cast<const v8h*>(&s.wt[wid][n][8 * rg]);
+    const v8h bw = lds_read_v8h(wt0);
     uint32_t P[4], Q[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -326,8 +420,11 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
       acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, av), bw, acc[tt], 0, 0, 0);
     }
     wave_barrier();
-    cur = nxt;
   }
+  // the ring is reused below: no load of this wave may still be landing, and
+  // every wave must be done with its stages
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 
   // wave totals: l and the scalar term per head (row sums), P.V per head
 #pragma unroll
@@ -347,12 +444,12 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float v = acc[tt][j] + __shfl_xor(acc[tt][j], G);
-      if (n < G) s.accw[wid][n][32 * rg + 8 * j + tt] = fmaf(v, f, t1n);
+      if (n < G) s.u.accw[wid][n][32 * rg + 8 * j + tt] = fmaf(v, f, t1n);
     }
   }
   __syncthreads();
   float* part = p.part + ((int64_t)kvh * (p.n_sel_blk + p.n_split) + p.n_sel_blk + split) * G * kPartStride;
-  write_partial<G>(part, s.mw, s.lw, s.accw);
+  write_partial<G>(part, s.mw, s.lw, s.u.accw);
 }
 
 template <int G>
