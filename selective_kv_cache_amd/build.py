@@ -26,6 +26,10 @@ def command(out=LIB):
     return ["hipcc", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
             "-mcode-object-version=5",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # matrix-core accumulators in ordinary VGPRs: the online-softmax
+            # rescale then multiplies them in place instead of copying them
+            # out of and back into AGPRs every chunk
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
             "-Wno-unused-command-line-argument",
             "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
             *sources(), "-o", out]

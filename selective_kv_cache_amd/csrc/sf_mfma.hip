@@ -115,9 +115,26 @@ __device__ inline float logit_from(const v4i& D, float2 ksc, float scale, float 
   return hl < G ? lg : -INFINITY;
 }
 
+// The same logit with the 1/sqrt(D) (and any other constant factor) folded
+// into scale and sumq.
+__device__ inline float logit_scaled(const v4i& D, float2 ksc, float scale, float sumq) {
+  const float S = (float)D[0] + ((float)D[1] + ((float)D[2] + (float)D[3] * kInv254) * kInv254) * kInv254;
+  return fmaf(ksc.y, S * scale, fmaf(0.5f, ksc.y, ksc.x) * sumq);
+}
+
 // ---------------------------------------------------------------------------
-// Score pass: grid (n_score_split, hkv), 4 wavefronts; tiles of 16 tokens.
+// Score pass: grid (n_score_split, hkv), 4 wavefronts; tiles of 16 tokens,
+// kScoreU tiles per wave in flight.  The first tiles' loads are issued before
+// the query is prepared, and each batch's successor is loaded while the batch
+// is computed.
 // ---------------------------------------------------------------------------
+constexpr int kScoreU = 8;
+
+struct ScoreBatch {
+  uint2 w[kScoreU];
+  float2 sc[kScoreU];
+};
+
 template <int G>
 __global__ void __launch_bounds__(256) score_mfma(DecodeParams p) {
   __shared__ QPrep<G> qp;
@@ -128,43 +145,56 @@ __global__ void __launch_bounds__(256) score_mfma(DecodeParams p) {
   int first;
   const int seq = locate_unit(p.seq_off, p.batch, p.score_split, blockIdx.x, false, 0, lo, hi, first);
   const int64_t a = p.seq_off[seq];
+  const int t = lane & 15, hl = lane >> 4;
+  const int64_t t0 = (int64_t)kvh * p.cap + a + lo;            // first token row of the split
+  const uint8_t* kbase = p.kc + t0 * 32 + 8 * hl;
+  const float2* ksc = reinterpret_cast<const float2*>(p.ks) + t0;
+  const int nsp = (int)(hi - lo);
+  const int ntiles = (nsp + 15) / 16;
+  // tile k0 + 4u of this wave, token t (clamped into the split)
+  auto load = [&](int k0, ScoreBatch& B) {
+#pragma unroll
+    for (int u = 0; u < kScoreU; ++u) {
+      int rel = 16 * (k0 + 4 * u) + t;
+      rel = rel < nsp ? rel : nsp - 1;
+      B.w[u] = *reinterpret_cast<const uint2*>(kbase + (uint32_t)rel * 32u);
+      B.sc[u] = ksc[rel];
+    }
+  };
+  ScoreBatch cur, nxt;
+  if (wid < ntiles) load(wid, cur);
+
   const bool hist = p.top_t > 0;   // no selection, no histogram
   for (int i = tid; i < kHistBins; i += 256) lhist[i] = 0u;
   v4i a0, a1;
   prep_query<G>(p.q + ((int64_t)seq * p.hq + kvh * G) * kHeadDim, qp, a0, a1);
-  const int t = lane & 15, hl = lane >> 4;
   const float scale = qp.scale[hl < G ? hl : 0], sumq = qp.sumq[hl < G ? hl : 0];
-  const uint8_t* kbase = p.kc + (int64_t)kvh * p.cap * 32;
-  const float2* ksc = reinterpret_cast<const float2*>(p.ks) + (int64_t)kvh * p.cap;
-  float* scores = p.scores + (int64_t)kvh * p.ntot + (a - p.off0);
-  const int ntiles = (int)((hi - lo + 15) / 16);
-  constexpr int U = 8;
-  for (int k0 = wid; k0 < ntiles; k0 += 4 * U) {
-    uint2 w[U];
-    float2 sc[U];
-    int64_t li[U];
+  float* scores = p.scores + (int64_t)kvh * p.ntot + (a - p.off0) + lo;
+  auto compute = [&](int k0, const ScoreBatch& B) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      li[u] = lo + 16 * (int64_t)(k0 + 4 * u) + t;
-      const int64_t tok = a + (li[u] < hi ? li[u] : lo);
-      w[u] = *reinterpret_cast<const uint2*>(kbase + tok * 32 + 8 * hl);
-      sc[u] = ksc[tok];
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < kScoreU; ++u) {
       if (k0 + 4 * u >= ntiles) break;
       v4i b0, b1;
-      decode_b2(w[u].x, w[u].y, b0, b1);
+      decode_b2(B.w[u].x, B.w[u].y, b0, b1);
       v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, v4i{0, 0, 0, 0}, 0, 0, 0);
       D = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, D, 0, 0, 0);
-      float lg = logit_from<G>(D, sc[u], scale, sumq, hl);
+      float lg = logit_from<G>(D, B.sc[u], scale, sumq, hl);
       lg = fmaxf(lg, __shfl_xor(lg, 16));
       lg = fmaxf(lg, __shfl_xor(lg, 32));
-      if (hl == 0 && li[u] < hi) {
-        scores[li[u]] = lg;
+      const int rel = 16 * (k0 + 4 * u) + t;
+      if (hl == 0 && rel < nsp) {
+        scores[rel] = lg;
         if (hist) atomicAdd(&lhist[score_key(lg) >> (32 - kHistBits)], 1u);
       }
     }
+  };
+  constexpr int kStride = 4 * kScoreU;
+  for (int k0 = wid; k0 < ntiles; k0 += 2 * kStride) {
+    if (k0 + kStride < ntiles) load(k0 + kStride, nxt);
+    compute(k0, cur);
+    if (k0 + kStride >= ntiles) break;
+    if (k0 + 2 * kStride < ntiles) load(k0 + 2 * kStride, cur);
+    compute(k0 + kStride, nxt);
   }
   if (!hist) return;
   __syncthreads();
@@ -200,7 +230,6 @@ struct MfmaLds {
   QPrep<G> qp;
   alignas(16) _Float16 wt[4][16][32];   // per wave: P.V weights [column][token]
   float mw[4][G], lw[4][G];
-  uint32_t selw[kMaxSplitWords];        // the split's selection bitmap
   union {
     Stage ring[4][kRing];
     float accw[4][G][kHeadDim];         // after the stream: per-wave P.V totals
@@ -216,6 +245,19 @@ __device__ inline void dma4(const void* g, void* l) {
   __builtin_amdgcn_global_load_lds(g, (lds_void_t)l, 4, 0, 0);
 }
 
+// Maximum over the 16 lanes of a row (DPP row rotations, no LDS traffic).
+__device__ inline float row16_max(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false)));
+  return x;
+}
+
+__device__ inline float lane_value(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
 __device__ inline uint32_t lds_addr(const void* l) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)l;
 }
@@ -227,7 +269,7 @@ __device__ inline uint32_t lds_addr(const void* l) {
 struct StageRegs {
   uint64_t kw[2];          // K code bytes of tiles 0, 1 (token t, bytes 8hl..8hl+7)
   uint64_t ksc[2], vsc[2]; // (lo, delta) of tokens t, 16 + t
-  uint32_t vw[8];          // V dword vdw of tokens 8rg..8rg+7
+  uint32_t vw[8];          // V dword vdw of tokens 4rg+v (vw[2v]) and 16+4rg+v (vw[2v+1])
 };
 
 __device__ inline void read_stage(uint32_t aK, uint32_t aS, uint32_t aV, StageRegs& r) {
@@ -239,13 +281,13 @@ __device__ inline void read_stage(uint32_t aK, uint32_t aS, uint32_t aV, StageRe
       "ds_read_b64 %4, %15 offset:256\n\t"
       "ds_read_b64 %5, %15 offset:384\n\t"
       "ds_read_b32 %6, %16\n\t"
-      "ds_read_b32 %7, %16 offset:32\n\t"
-      "ds_read_b32 %8, %16 offset:64\n\t"
-      "ds_read_b32 %9, %16 offset:96\n\t"
-      "ds_read_b32 %10, %16 offset:128\n\t"
-      "ds_read_b32 %11, %16 offset:160\n\t"
-      "ds_read_b32 %12, %16 offset:192\n\t"
-      "ds_read_b32 %13, %16 offset:224\n\t"
+      "ds_read_b32 %7, %16 offset:512\n\t"
+      "ds_read_b32 %8, %16 offset:32\n\t"
+      "ds_read_b32 %9, %16 offset:544\n\t"
+      "ds_read_b32 %10, %16 offset:64\n\t"
+      "ds_read_b32 %11, %16 offset:576\n\t"
+      "ds_read_b32 %12, %16 offset:96\n\t"
+      "ds_read_b32 %13, %16 offset:608\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(r.kw[0]), "=&v"(r.kw[1]), "=&v"(r.ksc[0]), "=&v"(r.ksc[1]), "=&v"(r.vsc[0]), "=&v"(r.vsc[1]),
         "=&v"(r.vw[0]), "=&v"(r.vw[1]), "=&v"(r.vw[2]), "=&v"(r.vw[3]), "=&v"(r.vw[4]), "=&v"(r.vw[5]),
@@ -254,10 +296,8 @@ __device__ inline void read_stage(uint32_t aK, uint32_t aS, uint32_t aV, StageRe
       : "memory");
 }
 
-__device__ inline uint32_t lds_read_u32(uint32_t a) {
-  uint32_t v;
-  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(a) : "memory");
-  return v;
+__device__ inline void lds_write_u32(uint32_t a, uint32_t v) {
+  asm volatile("ds_write_b32 %0, %1" ::"v"(a), "v"(v) : "memory");
 }
 
 __device__ inline v8h lds_read_v8h(uint32_t a) {
@@ -277,11 +317,13 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   const int64_t a = p.seq_off[seq];
   const int64_t sk = (int64_t)seq * p.hkv + kvh;
   const bool masked = p.use_refine != 0;
-  const uint8_t* kbase = p.kc + ((int64_t)kvh * p.cap + a) * 32;
-  const uint8_t* vbase = p.vc + ((int64_t)kvh * p.cap + a) * 32;
-  const float* kscg = p.ks + ((int64_t)kvh * p.cap + a) * 2;
-  const float* vscg = p.vs + ((int64_t)kvh * p.cap + a) * 2;
-  const int nchunks = (int)((hi - lo + 31) / 32);
+  const int64_t t0 = (int64_t)kvh * p.cap + a + lo;            // first token row of the split
+  const uint8_t* kbase = p.kc + t0 * 32;
+  const uint8_t* vbase = p.vc + t0 * 32;
+  const float* kscg = p.ks + t0 * 2;
+  const float* vscg = p.vs + t0 * 2;
+  const int nsp = (int)(hi - lo);                               // tokens of the split (<= 4096)
+  const int nchunks = (nsp + 31) / 32;
   const int nmine = nchunks > wid ? (nchunks - wid + 3) / 4 : 0;   // chunks wid, wid+4, ...
 
   // Stage i of this wave <- chunk wid + 4*i.  Lane L loads K/V bytes
@@ -289,44 +331,53 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   // split's end read its last token instead, and loads past the wave's last
   // chunk repeat that token too, so every issue is four in-bounds loads.
   auto issue = [&](int i) {
-    const int c = wid + 4 * i;
-    int64_t li = lo + 32 * (int64_t)c + (lane >> 1);
-    li = li < hi ? li : hi - 1;
+    int rel = 32 * (wid + 4 * i) + (lane >> 1);
+    rel = rel < nsp ? rel : nsp - 1;
     Stage& st = s.u.ring[wid][i % kRing];
-    dma16(kbase + li * 32 + 16 * (lane & 1), st.k);
-    dma16(vbase + li * 32 + 16 * (lane & 1), st.v);
-    dma4(kscg + li * 2 + (lane & 1), st.ks);
-    dma4(vscg + li * 2 + (lane & 1), st.vs);
+    const uint32_t cb = (uint32_t)rel * 32u + 16u * (uint32_t)(lane & 1);
+    const uint32_t sb = (uint32_t)rel * 2u + (uint32_t)(lane & 1);
+    dma16(kbase + cb, st.k);
+    dma16(vbase + cb, st.v);
+    dma4(kscg + sb, st.ks);
+    dma4(vscg + sb, st.vs);
   };
 #pragma unroll
   for (int i = 0; i < kRing - 1; ++i) issue(i);
 
   for (int i = lane; i < 16 * 32; i += 64) (&s.wt[wid][0][0])[i] = (_Float16)0.f;
-  if (tid < kMaxSplitWords) {
-    const int64_t w0 = lo >> 5;                     // splits start on a word boundary
-    s.selw[tid] = (masked && tid < (nchunks)) ? p.bitmap[sk * p.bm_words + w0 + tid] : 0u;
-  }
+  // selection words of the split (one per chunk) in two registers: lane L
+  // holds those of chunks L and 64 + L; splits start on a word boundary
+  static_assert(kMaxSplitWords <= 128, "two words per lane");
+  const uint32_t* bmw = p.bitmap + sk * p.bm_words + (lo >> 5);
+  const uint32_t sw0 = masked && lane < nchunks ? bmw[lane] : 0u;
+  const uint32_t sw1 = masked && 64 + lane < nchunks ? bmw[64 + lane] : 0u;
   v4i a0, a1;
   prep_query<G>(p.q + ((int64_t)seq * p.hq + kvh * G) * kHeadDim, s.qp, a0, a1);
-  const int t = lane & 15, hl = lane >> 4;        // logit layout: token t, head hl
-  const int n = lane & 15, rg = lane >> 4;        // P.V layout: column n, element rows 4rg..4rg+3
-  const float scale = s.qp.scale[hl < G ? hl : 0], sumq = s.qp.sumq[hl < G ? hl : 0];
+  const int t = lane & 15, hl = lane >> 4;        // logit layout: token t (and 16 + t), head hl
+  const int n = lane & 15, rg = lane >> 4;        // P.V layout: column n, k-group rg
+  // logits in log2 units: exp2 of differences gives the softmax weights
+  constexpr float kLog2e = 1.4426950408889634f;
+  const float scale = s.qp.scale[hl < G ? hl : 0] * (kRsqrtD * kLog2e);
+  const float sumq = s.qp.sumq[hl < G ? hl : 0] * (kRsqrtD * kLog2e);
   // v_perm_b32 selector: half (n & 1) of each of two dwords
   const uint32_t hsel = 2u * (uint32_t)(n & 1);
   const uint32_t psel = hsel | ((hsel + 1u) << 8) | ((hsel + 4u) << 16) | ((hsel + 5u) << 24);
   const int vdw = n >> 1;                         // dword of the V row holding elements 8n..8n+7
 
-  // LDS addresses of this lane's stage operands (offsets into a stage)
+  // LDS addresses of this lane's stage operands.  P.V k index kappa = 2u + j
+  // stands for token 16j + u, so lane (n, rg) takes tokens 4rg..4rg+3 and
+  // 16+4rg..16+4rg+3, and a logit lane's two weights are adjacent.
   const uint32_t ring0 = lds_addr(&s.u.ring[wid][0]);
-  const uint32_t sel0 = lds_addr(&s.selw[0]);
   const uint32_t wt0 = lds_addr(&s.wt[wid][n][8 * rg]);
+  const uint32_t wts = lds_addr(&s.wt[wid][hl < G ? hl : 0][2 * t]);
   const uint32_t offK = (uint32_t)(t * 32 + 8 * hl);
   const uint32_t offS = (uint32_t)(offsetof(Stage, ks) + 8 * t);
-  const uint32_t offV = (uint32_t)(offsetof(Stage, v) + (8 * rg) * 32 + 4 * vdw);
+  const uint32_t offV = (uint32_t)(offsetof(Stage, v) + (4 * rg) * 32 + 4 * vdw);
   static_assert(offsetof(Stage, vs) == offsetof(Stage, ks) + 256, "scale blocks are adjacent");
 
   float m = -INFINITY, lsum = 0.f, t1 = 0.f;
   int sexp = 127;                                 // weight scale 2^sexp; 127 = not set yet
+  float wsc = 1.0f;                               // 2^sexp once set
   v4f acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -336,75 +387,73 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kRingLoads * (kRing - 1)) : "memory");
     const int c = wid + 4 * i;
     const uint32_t sb = ring0 + (uint32_t)(i % kRing) * (uint32_t)sizeof(Stage);
-    const int64_t base = lo + 32 * (int64_t)c;
-    const uint32_t selw = lds_read_u32(sel0 + 4u * (uint32_t)c);
+    const int rem = nsp - 32 * c;                 // tokens of this chunk inside the split
+    const uint32_t selw = (uint32_t)__builtin_amdgcn_readlane((int)(c < 64 ? sw0 : sw1), c & 63);
     StageRegs R;
     read_stage(sb + offK, sb + offS, sb + offV, R);
-    uint2 kw[2];
-    float2 ksc[2], vsc[2];
-    const uint32_t* vw = R.vw;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      kw[k] = __builtin_bit_cast(uint2, R.kw[k]);
-      ksc[k] = __builtin_bit_cast(float2, R.ksc[k]);
-      vsc[k] = __builtin_bit_cast(float2, R.vsc[k]);
-    }
     bool ok[2];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) ok[k] = base + 16 * k + t < hi && !((selw >> (16 * k + t)) & 1u);
-    // logits
+    for (int k = 0; k < 2; ++k) ok[k] = 16 * k + t < rem && !((selw >> (16 * k + t)) & 1u);
     float lg[2];
+    float2 vsc[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
+      const uint2 kw = __builtin_bit_cast(uint2, R.kw[k]);
+      const float2 ksc = __builtin_bit_cast(float2, R.ksc[k]);
+      vsc[k] = __builtin_bit_cast(float2, R.vsc[k]);
       v4i b0, b1;
-      decode_b2(kw[k].x, kw[k].y, b0, b1);
+      decode_b2(kw.x, kw.y, b0, b1);
       v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, v4i{0, 0, 0, 0}, 0, 0, 0);
       D = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, D, 0, 0, 0);
-      lg[k] = ok[k] ? logit_from<G>(D, ksc[k], scale, sumq, hl) : -INFINITY;
+      lg[k] = ok[k] && hl < G ? logit_scaled(D, ksc, scale, sumq) : -INFINITY;
     }
     // online softmax: maximum over the row of 16 lanes (one head)
-    float mx = fmaxf(lg[0], lg[1]);
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    const float mnew = fmaxf(m, mx);
-    // weight scale: keep delta * 2^sexp below 2^14 over the chunk
+    const float mnew = fmaxf(m, row16_max(fmaxf(lg[0], lg[1])));
+    // weight scale: keep delta * 2^sexp below 2^14 over the chunk; the
+    // chunk's largest delta is needed only when one reaches 2^(14 - sexp)
     float dmax = fmaxf(ok[0] ? vsc[0].y : 0.f, ok[1] ? vsc[1].y : 0.f);
-    dmax = wave_max(dmax);
     int need = sexp;
-    if (dmax > 0.f) {
+    if (__ballot(dmax > 0.f && (sexp == 127 || dmax >= __builtin_ldexpf(1.0f, 14 - sexp))) != 0ull) {
+      dmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max(dmax))));
       int e2;
       frexpf(dmax, &e2);
-      need = 14 - e2;
+      need = 14 - e2;       // wave-uniform, and so is sexp
     }
     const bool grow = __ballot(mnew > m) != 0ull;
     if (grow || need < sexp) {
-      const float alpha = mnew > m ? (m == -INFINITY ? 0.f : expf(m - mnew)) : 1.f;
+      const float alpha = mnew > m ? (m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mnew)) : 1.f;
       lsum *= alpha;
       t1 *= alpha;
       const int hc = n < 2 * G ? n % G : 0;
-      float f = __shfl(alpha, 16 * hc);
-      if (need < sexp && sexp != 127) f = __builtin_ldexpf(f, need - sexp);
-      if (need < sexp) sexp = need;
+      float f = lane_value(alpha, 0);
+#pragma unroll
+      for (int h = 1; h < G; ++h) f = hc == h ? lane_value(alpha, 16 * h) : f;
+      if (need < sexp) {
+        if (sexp != 127) f = __builtin_ldexpf(f, need - sexp);
+        sexp = need;
+        wsc = __builtin_ldexpf(1.0f, sexp);
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j) acc[j] *= f;
       m = mnew;
     }
-    const int se = sexp == 127 ? 0 : sexp;
+    float pk[2], wv[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const float pk = lg[k] == -INFINITY ? 0.f : expf(lg[k] - m);
-      lsum += pk;
-      t1 = fmaf(pk, fmaf(0.5f, vsc[k].y, vsc[k].x), t1);
-      const float wv = __builtin_ldexpf(pk * vsc[k].y, se);
-      const _Float16 whi = (_Float16)wv;
-      const _Float16 wlo = (_Float16)(wv - (float)whi);
-      if (hl < G) {
-        s.wt[wid][hl][16 * k + t] = whi;
-        s.wt[wid][G + hl][16 * k + t] = wlo;
-      }
+      pk[k] = lg[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lg[k] - m);
+      lsum += pk[k];
+      t1 = fmaf(pk[k], fmaf(0.5f, vsc[k].y, vsc[k].x), t1);
+      wv[k] = pk[k] * (vsc[k].y * wsc);
     }
-    wave_barrier();
+    // weights as fp16 hi + lo (truncated hi, exact remainder): 22 bits
+    const auto whi = __builtin_amdgcn_cvt_pkrtz(wv[0], wv[1]);
+    const auto wlo = __builtin_amdgcn_cvt_pkrtz(wv[0] - (float)whi[0], wv[1] - (float)whi[1]);
+    if (hl < G) {
+      lds_write_u32(wts, __builtin_bit_cast(uint32_t, whi));
+      lds_write_u32(wts + (uint32_t)(G * 32 * sizeof(_Float16)), __builtin_bit_cast(uint32_t, wlo));
+    }
     const v8h bw = lds_read_v8h(wt0);
+    const uint32_t* vw = R.vw;
     uint32_t P[4], Q[4];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -419,21 +468,21 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
       for (int v = 0; v < 4; ++v) av[v] = (tt <= 4 ? P[v] : Q[v]) & mk;
       acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, av), bw, acc[tt], 0, 0, 0);
     }
-    wave_barrier();
   }
   // the ring is reused below: no load of this wave may still be landing, and
   // every wave must be done with its stages
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  // wave totals: l and the scalar term per head (row sums), P.V per head
+  // wave totals: l and the scalar term per head (row sums), P.V per head;
+  // the maximum goes back to natural-log units
 #pragma unroll
   for (int o = 1; o < 16; o <<= 1) {
     lsum += __shfl_xor(lsum, o);
     t1 += __shfl_xor(t1, o);
   }
   if (hl < G && t == 0) {
-    s.mw[wid][hl] = m;
+    s.mw[wid][hl] = m * 0.6931471805599453f;
     s.lw[wid][hl] = lsum;
   }
   const float t1n = __shfl(t1, 16 * (n < G ? n : 0));

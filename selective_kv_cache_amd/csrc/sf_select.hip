@@ -52,6 +52,15 @@ __global__ void __launch_bounds__(kSelThreads) select_scan(DecodeParams p) {
   uint32_t* bm = p.bitmap + sk * p.bm_words;
   const float* sc = p.scores + (int64_t)kvh * p.ntot + (a - p.off0);
   uint2* cand = p.cand + sk * p.max_seq + lo;     // this chunk's segment
+  // the chunk's scores are loaded first, so that their latency overlaps the
+  // boundary search below
+  constexpr int kPer = kSelChunk / kSelThreads;
+  float sv[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int64_t i = lo + j * kSelThreads + tid;
+    sv[j] = (!all && i < hi) ? sc[i] : 0.f;
+  }
 
   if (!all) {
     const uint32_t* h1 = p.hist + sk * kHistBins;
@@ -61,7 +70,10 @@ __global__ void __launch_bounds__(kSelThreads) select_scan(DecodeParams p) {
     find_threshold<kSelThreads, kHistBins>(h, (uint32_t)tn, scan_lds, &sh_bin, &sh_need);
   }
   const uint32_t b1 = all ? 0u : (uint32_t)sh_bin;
-  for (int64_t base = lo; base < hi; base += kSelThreads) {
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int64_t base = lo + j * kSelThreads;
+    if (base >= hi) break;
     const int64_t i = base + tid;
     const bool valid = i < hi;
     bool s = false, cnd = false;
@@ -70,7 +82,7 @@ __global__ void __launch_bounds__(kSelThreads) select_scan(DecodeParams p) {
       if (all) {
         s = true;
       } else {
-        key = score_key(sc[i]);
+        key = score_key(sv[j]);
         const uint32_t bin = key >> (32 - kHistBits);
         s = bin > b1;
         cnd = bin == b1;
