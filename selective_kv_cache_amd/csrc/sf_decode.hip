@@ -77,6 +77,8 @@ Carve carve(const sf_geom& g, int32_t batch, int64_t total_tokens, int64_t max_s
   // workspace that a step left with a zero histogram can be reused as such
   c.hist = at; at += align256((size_t)batch * hkv * kHistBins * 4);
   c.scores = at; at += align256((size_t)hkv * total_tokens * 4);
+  // per-head logits; one chunk of slack for the attention pass's last loads
+  c.logits = at; at += align256((size_t)hkv * total_tokens * grp * 4 + 32 * 8 * 4);
   c.counters = at; at += align256((size_t)batch * hkv * ((max_seq_tokens + kSelChunk - 1) / kSelChunk) * 4);
   c.cand = at; at += align256((size_t)batch * hkv * max_seq_tokens * 8);
   c.bitmap = at; at += align256((size_t)batch * hkv * bm_words * 4);
@@ -189,6 +191,7 @@ extern "C" sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* a
   p.vc = a->v_codes;
   p.vs = a->v_scales;
   p.scores = a->scores_out ? a->scores_out : reinterpret_cast<float*>(ws + c.scores);
+  p.logits = reinterpret_cast<float*>(ws + c.logits);
   p.hist = reinterpret_cast<uint32_t*>(ws + c.hist);
   p.counters = reinterpret_cast<uint32_t*>(ws + c.counters);
   p.cand = reinterpret_cast<uint2*>(ws + c.cand);

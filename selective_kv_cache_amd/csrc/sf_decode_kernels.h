@@ -20,6 +20,7 @@ struct DecodeParams {
   const uint8_t* vc;
   const float* vs;
   float* scores;       // [hkv][ntot]
+  float* logits;       // [hkv][ntot][grp] per-head logits (matrix-core path)
   uint32_t* hist;      // [batch][hkv][kHistBins]: histogram of the scores' top key bits
   uint32_t* counters;  // [batch][hkv][cnt_stride]: candidates of each selection chunk
   uint2* cand;         // [batch][hkv][max_seq] (score key, token); chunk c's at c*sel_chunk

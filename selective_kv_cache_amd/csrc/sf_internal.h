@@ -26,7 +26,7 @@ __host__ __device__ inline uint32_t score_key(float s) {
 
 // Workspace carve-out (byte offsets from the workspace base).
 struct Carve {
-  size_t scores, hist, counters, cand, bitmap, sel, part, miss, total;
+  size_t scores, logits, hist, counters, cand, bitmap, sel, part, miss, total;
 };
 
 int32_t choose_split(int64_t total_tokens, int32_t n_kv_heads);

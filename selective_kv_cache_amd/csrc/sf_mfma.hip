@@ -123,119 +123,13 @@ __device__ inline float logit_scaled(const v4i& D, float2 ksc, float scale, floa
 }
 
 // ---------------------------------------------------------------------------
-// Score pass: grid (n_score_split, hkv), 4 wavefronts; tiles of 16 tokens,
-// kScoreU tiles per wave in flight.  The first tiles' loads are issued before
-// the query is prepared, and each batch's successor is loaded while the batch
-// is computed.
+// Direct global->LDS loads and asm LDS access, shared by both streaming
+// kernels.  global_load_lds puts lane i's 16 (or 4) bytes at offset 16*i (4*i)
+// of the destination, so loads in flight hold no registers.  LDS reads of
+// such buffers are written in asm: a read the compiler sees makes it wait for
+// every direct load in flight (it cannot tell ring stages apart), which would
+// serialise the stream.  Each asm read waits for itself before it ends.
 // ---------------------------------------------------------------------------
-constexpr int kScoreU = 8;
-
-struct ScoreBatch {
-  uint2 w[kScoreU];
-  float2 sc[kScoreU];
-};
-
-template <int G>
-__global__ void __launch_bounds__(256) score_mfma(DecodeParams p) {
-  __shared__ QPrep<G> qp;
-  __shared__ uint32_t lhist[kHistBins];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int kvh = blockIdx.y;
-  int64_t lo, hi;
-  int first;
-  const int seq = locate_unit(p.seq_off, p.batch, p.score_split, blockIdx.x, false, 0, lo, hi, first);
-  const int64_t a = p.seq_off[seq];
-  const int t = lane & 15, hl = lane >> 4;
-  const int64_t t0 = (int64_t)kvh * p.cap + a + lo;            // first token row of the split
-  const uint8_t* kbase = p.kc + t0 * 32 + 8 * hl;
-  const float2* ksc = reinterpret_cast<const float2*>(p.ks) + t0;
-  const int nsp = (int)(hi - lo);
-  const int ntiles = (nsp + 15) / 16;
-  // tile k0 + 4u of this wave, token t (clamped into the split)
-  auto load = [&](int k0, ScoreBatch& B) {
-#pragma unroll
-    for (int u = 0; u < kScoreU; ++u) {
-      int rel = 16 * (k0 + 4 * u) + t;
-      rel = rel < nsp ? rel : nsp - 1;
-      B.w[u] = *reinterpret_cast<const uint2*>(kbase + (uint32_t)rel * 32u);
-      B.sc[u] = ksc[rel];
-    }
-  };
-  ScoreBatch cur, nxt;
-  if (wid < ntiles) load(wid, cur);
-
-  const bool hist = p.top_t > 0;   // no selection, no histogram
-  for (int i = tid; i < kHistBins; i += 256) lhist[i] = 0u;
-  v4i a0, a1;
-  prep_query<G>(p.q + ((int64_t)seq * p.hq + kvh * G) * kHeadDim, qp, a0, a1);
-  const float scale = qp.scale[hl < G ? hl : 0], sumq = qp.sumq[hl < G ? hl : 0];
-  float* scores = p.scores + (int64_t)kvh * p.ntot + (a - p.off0) + lo;
-  auto compute = [&](int k0, const ScoreBatch& B) {
-#pragma unroll
-    for (int u = 0; u < kScoreU; ++u) {
-      if (k0 + 4 * u >= ntiles) break;
-      v4i b0, b1;
-      decode_b2(B.w[u].x, B.w[u].y, b0, b1);
-      v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, v4i{0, 0, 0, 0}, 0, 0, 0);
-      D = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, D, 0, 0, 0);
-      float lg = logit_from<G>(D, B.sc[u], scale, sumq, hl);
-      lg = fmaxf(lg, __shfl_xor(lg, 16));
-      lg = fmaxf(lg, __shfl_xor(lg, 32));
-      const int rel = 16 * (k0 + 4 * u) + t;
-      if (hl == 0 && rel < nsp) {
-        scores[rel] = lg;
-        if (hist) atomicAdd(&lhist[score_key(lg) >> (32 - kHistBits)], 1u);
-      }
-    }
-  };
-  constexpr int kStride = 4 * kScoreU;
-  for (int k0 = wid; k0 < ntiles; k0 += 2 * kStride) {
-    if (k0 + kStride < ntiles) load(k0 + kStride, nxt);
-    compute(k0, cur);
-    if (k0 + kStride >= ntiles) break;
-    if (k0 + 2 * kStride < ntiles) load(k0 + 2 * kStride, cur);
-    compute(k0 + kStride, nxt);
-  }
-  if (!hist) return;
-  __syncthreads();
-  uint32_t* gh = p.hist + ((int64_t)seq * p.hkv + kvh) * kHistBins;   // level-1 histogram
-  for (int i = tid; i < kHistBins; i += 256) {
-    const uint32_t c = lhist[i];
-    if (c) atomicAdd(&gh[i], c);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Base attention pass over one split (selected tokens left out): 4
-// wavefronts, chunks of 32 tokens (two logit tiles, one P.V step).
-// ---------------------------------------------------------------------------
-// The base pass streams its split through a per-wavefront ring of LDS stages
-// filled by direct global->LDS loads (global_load_lds: lane i's 16 or 4 bytes
-// land at stage offset 16*i or 4*i), so the loads in flight hold no
-// registers.  One stage is one 32-token chunk: K codes, V codes (1 KiB each,
-// as stored), K and V scales (256 B each).
-constexpr int kRing = 4;                       // stages per wavefront; kRing - 1 chunks in flight
-constexpr int kRingLoads = 4;                  // direct loads per stage
-constexpr int kMaxSplitWords = 4096 / 32;      // selection words of the longest split
-
-struct Stage {
-  uint8_t k[32 * 32];
-  uint8_t v[32 * 32];
-  float2 ks[32];
-  float2 vs[32];
-};
-
-template <int G>
-struct MfmaLds {
-  QPrep<G> qp;
-  alignas(16) _Float16 wt[4][16][32];   // per wave: P.V weights [column][token]
-  float mw[4][G], lw[4][G];
-  union {
-    Stage ring[4][kRing];
-    float accw[4][G][kHeadDim];         // after the stream: per-wave P.V totals
-  } u;
-};
-
 typedef __attribute__((address_space(3))) void* lds_void_t;
 
 __device__ inline void dma16(const void* g, void* l) {
@@ -262,38 +156,8 @@ __device__ inline uint32_t lds_addr(const void* l) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)l;
 }
 
-// One lane's operands of a stage.  The LDS reads are written in asm: a read
-// the compiler sees makes it wait for every direct load in flight (it cannot
-// tell the ring stages apart), which would serialise the stream.  The block
-// waits for its own reads before it ends, so every output is complete.
-struct StageRegs {
-  uint64_t kw[2];          // K code bytes of tiles 0, 1 (token t, bytes 8hl..8hl+7)
-  uint64_t ksc[2], vsc[2]; // (lo, delta) of tokens t, 16 + t
-  uint32_t vw[8];          // V dword vdw of tokens 4rg+v (vw[2v]) and 16+4rg+v (vw[2v+1])
-};
-
-__device__ inline void read_stage(uint32_t aK, uint32_t aS, uint32_t aV, StageRegs& r) {
-  asm volatile(
-      "ds_read_b64 %0, %14\n\t"
-      "ds_read_b64 %1, %14 offset:512\n\t"
-      "ds_read_b64 %2, %15\n\t"
-      "ds_read_b64 %3, %15 offset:128\n\t"
-      "ds_read_b64 %4, %15 offset:256\n\t"
-      "ds_read_b64 %5, %15 offset:384\n\t"
-      "ds_read_b32 %6, %16\n\t"
-      "ds_read_b32 %7, %16 offset:512\n\t"
-      "ds_read_b32 %8, %16 offset:32\n\t"
-      "ds_read_b32 %9, %16 offset:544\n\t"
-      "ds_read_b32 %10, %16 offset:64\n\t"
-      "ds_read_b32 %11, %16 offset:576\n\t"
-      "ds_read_b32 %12, %16 offset:96\n\t"
-      "ds_read_b32 %13, %16 offset:608\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r.kw[0]), "=&v"(r.kw[1]), "=&v"(r.ksc[0]), "=&v"(r.ksc[1]), "=&v"(r.vsc[0]), "=&v"(r.vsc[1]),
-        "=&v"(r.vw[0]), "=&v"(r.vw[1]), "=&v"(r.vw[2]), "=&v"(r.vw[3]), "=&v"(r.vw[4]), "=&v"(r.vw[5]),
-        "=&v"(r.vw[6]), "=&v"(r.vw[7])
-      : "v"(aK), "v"(aS), "v"(aV)
-      : "memory");
+__device__ inline void lds_add_u32(uint32_t a, uint32_t v) {
+  asm volatile("ds_add_u32 %0, %1" ::"v"(a), "v"(v) : "memory");
 }
 
 __device__ inline void lds_write_u32(uint32_t a, uint32_t v) {
@@ -306,9 +170,172 @@ __device__ inline v8h lds_read_v8h(uint32_t a) {
   return __builtin_bit_cast(v8h, v);
 }
 
+// ---------------------------------------------------------------------------
+// Score pass: grid (n_score_split, hkv), 4 wavefronts.  Each wave streams
+// 32-token chunks (two logit tiles) of its split through an LDS ring; the
+// per-head logits go to the logits buffer for the attention pass, their
+// maximum over the group to the scores and the level-1 histogram.
+// ---------------------------------------------------------------------------
+constexpr int kSRing = 4;                      // stages per wavefront
+constexpr int kSRingLoads = 2;                 // direct loads per stage
+
+struct SStage {
+  uint8_t k[32 * 32];
+  float2 ks[32];
+};
+
+template <int G>
+__global__ void __launch_bounds__(256) score_mfma(DecodeParams p) {
+  __shared__ QPrep<G> qp;
+  __shared__ uint32_t lhist[kHistBins];
+  __shared__ SStage ring[4][kSRing];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int kvh = blockIdx.y;
+  int64_t lo, hi;
+  int first;
+  const int seq = locate_unit(p.seq_off, p.batch, p.score_split, blockIdx.x, false, 0, lo, hi, first);
+  const int64_t a = p.seq_off[seq];
+  const int64_t t0 = (int64_t)kvh * p.cap + a + lo;            // first token row of the split
+  const uint8_t* kbase = p.kc + t0 * 32;
+  const float* kscg = p.ks + t0 * 2;
+  const int nsp = (int)(hi - lo);
+  const int nchunks = (nsp + 31) / 32;
+  const int nmine = nchunks > wid ? (nchunks - wid + 3) / 4 : 0;
+  // stage i <- chunk wid + 4i (tokens past the split read its last token;
+  // issues past the wave's last chunk repeat it)
+  auto issue = [&](int i) {
+    const int c = wid + 4 * i < nchunks ? wid + 4 * i : nchunks - 1;
+    int rel = 32 * c + (lane >> 1);
+    rel = rel < nsp ? rel : nsp - 1;
+    SStage& st = ring[wid][i % kSRing];
+    dma16(kbase + (uint32_t)rel * 32u + 16u * (uint32_t)(lane & 1), st.k);
+    dma4(kscg + (uint32_t)rel * 2u + (uint32_t)(lane & 1), st.ks);
+  };
+  const bool hist = p.top_t > 0;   // no selection, no histogram
+  for (int i = tid; i < kHistBins; i += 256) lhist[i] = 0u;
+#pragma unroll
+  for (int i = 0; i < kSRing - 1; ++i) issue(i);
+  v4i a0, a1;
+  prep_query<G>(p.q + ((int64_t)seq * p.hq + kvh * G) * kHeadDim, qp, a0, a1);
+  const int t = lane & 15, hl = lane >> 4;
+  const float scale = qp.scale[hl < G ? hl : 0], sumq = qp.sumq[hl < G ? hl : 0];
+  float* scores = p.scores + (int64_t)kvh * p.ntot + (a - p.off0) + lo;
+  float* lgo = p.logits + ((int64_t)kvh * p.ntot + (a - p.off0) + lo) * G;
+  const uint32_t ring0 = lds_addr(&ring[wid][0]);
+  const uint32_t offK = (uint32_t)(t * 32 + 8 * hl);
+  const uint32_t offS = (uint32_t)(offsetof(SStage, ks) + 8 * t);
+  const int hx = hl >> 1;                         // after the reduction: tile of this lane
+  const uint32_t hist0 = lds_addr(&lhist[0]);
+  for (int i = 0; i < nmine; ++i) {
+    issue(i + kSRing - 1);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSRingLoads * (kSRing - 1)) : "memory");
+    const int c = wid + 4 * i;
+    const uint32_t sb = ring0 + (uint32_t)(i % kSRing) * (uint32_t)sizeof(SStage);
+    uint64_t kw[2], ks[2];
+    asm volatile(
+        "ds_read_b64 %0, %4\n\t"
+        "ds_read_b64 %1, %4 offset:512\n\t"
+        "ds_read_b64 %2, %5\n\t"
+        "ds_read_b64 %3, %5 offset:128\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(kw[0]), "=&v"(kw[1]), "=&v"(ks[0]), "=&v"(ks[1])
+        : "v"(sb + offK), "v"(sb + offS)
+        : "memory");
+    float lg[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint2 w = __builtin_bit_cast(uint2, kw[k]);
+      v4i b0, b1;
+      decode_b2(w.x, w.y, b0, b1);
+      v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, v4i{0, 0, 0, 0}, 0, 0, 0);
+      D = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, D, 0, 0, 0);
+      lg[k] = logit_from<G>(D, __builtin_bit_cast(float2, ks[k]), scale, sumq, hl);
+      const int rel = 32 * c + 16 * k + t;
+      if (hl < G && rel < nsp) lgo[rel * G + hl] = lg[k];   // kept for the attention pass
+    }
+    // maximum over the heads, two tiles at once: after the first exchange a
+    // lane keeps tile hl/2 over heads {hl, hl^2}, after the second over all
+    const float r = __shfl_xor(hx ? lg[0] : lg[1], 32);
+    float y = fmaxf(hx ? lg[1] : lg[0], r);
+    y = fmaxf(y, __shfl_xor(y, 16));
+    const int rel = 32 * c + 16 * hx + t;
+    if ((hl & 1) == 0 && rel < nsp) {
+      scores[rel] = y;
+      if (hist) lds_add_u32(hist0 + 4u * (score_key(y) >> (32 - kHistBits)), 1u);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (!hist) return;
+  __syncthreads();
+  uint32_t* gh = p.hist + ((int64_t)seq * p.hkv + kvh) * kHistBins;   // level-1 histogram
+  for (int i = tid; i < kHistBins; i += 256) {
+    const uint32_t c = lhist[i];
+    if (c) atomicAdd(&gh[i], c);
+  }
+}
+
+// The base pass streams its split through a per-wavefront ring of LDS stages
+// filled by direct global->LDS loads (global_load_lds: lane i's 16 or 4 bytes
+// land at stage offset 16*i or 4*i), so the loads in flight hold no
+// registers.  One stage is one 32-token chunk: the per-head logits the score
+// pass left, V codes (1 KiB, as stored) and V scales (256 B).  K is not read
+// again.
+constexpr int kRing = 4;                       // stages per wavefront; kRing - 1 chunks in flight
+constexpr int kRingLoads = 3;                  // direct loads per stage
+
+template <int G>
+struct Stage {
+  float lg[32 * G];
+  uint8_t v[32 * 32];
+  float2 vs[32];
+};
+
+template <int G>
+struct MfmaLds {
+  alignas(16) _Float16 wt[4][16][32];   // per wave: P.V weights [column][kappa]
+  float mw[4][G], lw[4][G];
+  union {
+    Stage<G> ring[4][kRing];
+    float accw[4][G][kHeadDim];         // after the stream: per-wave P.V totals
+  } u;
+};
+
+// One lane's operands of a stage.  The LDS reads are written in asm: a read
+// the compiler sees makes it wait for every direct load in flight (it cannot
+// tell the ring stages apart), which would serialise the stream.  The block
+// waits for its own reads before it ends, so every output is complete.
+struct StageRegs {
+  float lg[2];             // logits of tokens t, 16 + t for head hl
+  uint64_t vsc[2];         // (lo, delta) of tokens t, 16 + t
+  uint32_t vw[8];          // V dword vdw of tokens 4rg+v (vw[2v]) and 16+4rg+v (vw[2v+1])
+};
+
+template <int G>
+__device__ inline void read_stage(uint32_t aL, uint32_t aS, uint32_t aV, StageRegs& r) {
+  asm volatile(
+      "ds_read_b32 %0, %12\n\t"
+      "ds_read_b32 %1, %12 offset:%15\n\t"
+      "ds_read_b64 %2, %13\n\t"
+      "ds_read_b64 %3, %13 offset:128\n\t"
+      "ds_read_b32 %4, %14\n\t"
+      "ds_read_b32 %5, %14 offset:512\n\t"
+      "ds_read_b32 %6, %14 offset:32\n\t"
+      "ds_read_b32 %7, %14 offset:544\n\t"
+      "ds_read_b32 %8, %14 offset:64\n\t"
+      "ds_read_b32 %9, %14 offset:576\n\t"
+      "ds_read_b32 %10, %14 offset:96\n\t"
+      "ds_read_b32 %11, %14 offset:608\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r.lg[0]), "=&v"(r.lg[1]), "=&v"(r.vsc[0]), "=&v"(r.vsc[1]), "=&v"(r.vw[0]), "=&v"(r.vw[1]),
+        "=&v"(r.vw[2]), "=&v"(r.vw[3]), "=&v"(r.vw[4]), "=&v"(r.vw[5]), "=&v"(r.vw[6]), "=&v"(r.vw[7])
+      : "v"(aL), "v"(aS), "v"(aV), "n"(16 * G * 4)
+      : "memory");
+}
+
 template <int G>
 __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh, uint8_t* smem) {
   using Lds = MfmaLds<G>;
+  using St = Stage<G>;
   Lds& s = *reinterpret_cast<Lds*>(smem);
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   int64_t lo, hi;
@@ -318,28 +345,27 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   const int64_t sk = (int64_t)seq * p.hkv + kvh;
   const bool masked = p.use_refine != 0;
   const int64_t t0 = (int64_t)kvh * p.cap + a + lo;            // first token row of the split
-  const uint8_t* kbase = p.kc + t0 * 32;
   const uint8_t* vbase = p.vc + t0 * 32;
-  const float* kscg = p.ks + t0 * 2;
   const float* vscg = p.vs + t0 * 2;
+  const uint8_t* lbase = reinterpret_cast<const uint8_t*>(p.logits + ((int64_t)kvh * p.ntot + (a - p.off0) + lo) * G);
   const int nsp = (int)(hi - lo);                               // tokens of the split (<= 4096)
   const int nchunks = (nsp + 31) / 32;
   const int nmine = nchunks > wid ? (nchunks - wid + 3) / 4 : 0;   // chunks wid, wid+4, ...
 
-  // Stage i of this wave <- chunk wid + 4*i.  Lane L loads K/V bytes
-  // [16L, 16L+16) and scale word L of the chunk (token L/2); tokens past the
-  // split's end read its last token instead, and loads past the wave's last
-  // chunk repeat that token too, so every issue is four in-bounds loads.
+  // Stage i of this wave <- chunk wid + 4*i.  Lane L loads V bytes
+  // [16L, 16L+16) and scale word L of the chunk (token L/2), lanes L < 8G
+  // the logits' bytes [16L, 16L+16).  Tokens past the split's end read its
+  // last token's V row (logits: the buffer has a chunk of slack), and loads
+  // past the wave's last chunk repeat the last chunk, so every issue is
+  // three in-bounds loads.
   auto issue = [&](int i) {
-    int rel = 32 * (wid + 4 * i) + (lane >> 1);
+    const int c = wid + 4 * i < nchunks ? wid + 4 * i : nchunks - 1;
+    int rel = 32 * c + (lane >> 1);
     rel = rel < nsp ? rel : nsp - 1;
-    Stage& st = s.u.ring[wid][i % kRing];
-    const uint32_t cb = (uint32_t)rel * 32u + 16u * (uint32_t)(lane & 1);
-    const uint32_t sb = (uint32_t)rel * 2u + (uint32_t)(lane & 1);
-    dma16(kbase + cb, st.k);
-    dma16(vbase + cb, st.v);
-    dma4(kscg + sb, st.ks);
-    dma4(vscg + sb, st.vs);
+    St& st = s.u.ring[wid][i % kRing];
+    if (lane < 8 * G) dma16(lbase + (uint32_t)c * (32u * G * 4u) + 16u * (uint32_t)lane, st.lg);
+    dma16(vbase + (uint32_t)rel * 32u + 16u * (uint32_t)(lane & 1), st.v);
+    dma4(vscg + (uint32_t)rel * 2u + (uint32_t)(lane & 1), st.vs);
   };
 #pragma unroll
   for (int i = 0; i < kRing - 1; ++i) issue(i);
@@ -347,18 +373,16 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   for (int i = lane; i < 16 * 32; i += 64) (&s.wt[wid][0][0])[i] = (_Float16)0.f;
   // selection words of the split (one per chunk) in two registers: lane L
   // holds those of chunks L and 64 + L; splits start on a word boundary
+  constexpr int kMaxSplitWords = 4096 / 32;
   static_assert(kMaxSplitWords <= 128, "two words per lane");
   const uint32_t* bmw = p.bitmap + sk * p.bm_words + (lo >> 5);
   const uint32_t sw0 = masked && lane < nchunks ? bmw[lane] : 0u;
   const uint32_t sw1 = masked && 64 + lane < nchunks ? bmw[64 + lane] : 0u;
-  v4i a0, a1;
-  prep_query<G>(p.q + ((int64_t)seq * p.hq + kvh * G) * kHeadDim, s.qp, a0, a1);
+  __syncthreads();
   const int t = lane & 15, hl = lane >> 4;        // logit layout: token t (and 16 + t), head hl
   const int n = lane & 15, rg = lane >> 4;        // P.V layout: column n, k-group rg
-  // logits in log2 units: exp2 of differences gives the softmax weights
-  constexpr float kLog2e = 1.4426950408889634f;
-  const float scale = s.qp.scale[hl < G ? hl : 0] * (kRsqrtD * kLog2e);
-  const float sumq = s.qp.sumq[hl < G ? hl : 0] * (kRsqrtD * kLog2e);
+  const int hlc = hl < G ? hl : 0;
+  constexpr float kLog2e = 1.4426950408889634f;   // softmax in log2 units
   // v_perm_b32 selector: half (n & 1) of each of two dwords
   const uint32_t hsel = 2u * (uint32_t)(n & 1);
   const uint32_t psel = hsel | ((hsel + 1u) << 8) | ((hsel + 4u) << 16) | ((hsel + 5u) << 24);
@@ -369,11 +393,10 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   // 16+4rg..16+4rg+3, and a logit lane's two weights are adjacent.
   const uint32_t ring0 = lds_addr(&s.u.ring[wid][0]);
   const uint32_t wt0 = lds_addr(&s.wt[wid][n][8 * rg]);
-  const uint32_t wts = lds_addr(&s.wt[wid][hl < G ? hl : 0][2 * t]);
-  const uint32_t offK = (uint32_t)(t * 32 + 8 * hl);
-  const uint32_t offS = (uint32_t)(offsetof(Stage, ks) + 8 * t);
-  const uint32_t offV = (uint32_t)(offsetof(Stage, v) + (4 * rg) * 32 + 4 * vdw);
-  static_assert(offsetof(Stage, vs) == offsetof(Stage, ks) + 256, "scale blocks are adjacent");
+  const uint32_t wts = lds_addr(&s.wt[wid][hlc][2 * t]);
+  const uint32_t offL = (uint32_t)(offsetof(St, lg) + 4 * (t * G + hlc));
+  const uint32_t offS = (uint32_t)(offsetof(St, vs) + 8 * t);
+  const uint32_t offV = (uint32_t)(offsetof(St, v) + (4 * rg) * 32 + 4 * vdw);
 
   float m = -INFINITY, lsum = 0.f, t1 = 0.f;
   int sexp = 127;                                 // weight scale 2^sexp; 127 = not set yet
@@ -386,32 +409,24 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
     // this wave's loads complete in order: all but the newest kRing - 1 stages
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kRingLoads * (kRing - 1)) : "memory");
     const int c = wid + 4 * i;
-    const uint32_t sb = ring0 + (uint32_t)(i % kRing) * (uint32_t)sizeof(Stage);
+    const uint32_t sb = ring0 + (uint32_t)(i % kRing) * (uint32_t)sizeof(St);
     const int rem = nsp - 32 * c;                 // tokens of this chunk inside the split
     const uint32_t selw = (uint32_t)__builtin_amdgcn_readlane((int)(c < 64 ? sw0 : sw1), c & 63);
     StageRegs R;
-    read_stage(sb + offK, sb + offS, sb + offV, R);
-    bool ok[2];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) ok[k] = 16 * k + t < rem && !((selw >> (16 * k + t)) & 1u);
+    read_stage<G>(sb + offL, sb + offS, sb + offV, R);
     float lg[2];
     float2 vsc[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const uint2 kw = __builtin_bit_cast(uint2, R.kw[k]);
-      const float2 ksc = __builtin_bit_cast(float2, R.ksc[k]);
-      vsc[k] = __builtin_bit_cast(float2, R.vsc[k]);
-      v4i b0, b1;
-      decode_b2(kw.x, kw.y, b0, b1);
-      v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, v4i{0, 0, 0, 0}, 0, 0, 0);
-      D = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, D, 0, 0, 0);
-      lg[k] = ok[k] && hl < G ? logit_scaled(D, ksc, scale, sumq) : -INFINITY;
+      const bool ok = hl < G && 16 * k + t < rem && !((selw >> (16 * k + t)) & 1u);
+      lg[k] = ok ? R.lg[k] * kLog2e : -INFINITY;
+      vsc[k] = ok ? __builtin_bit_cast(float2, R.vsc[k]) : make_float2(0.f, 0.f);
     }
     // online softmax: maximum over the row of 16 lanes (one head)
     const float mnew = fmaxf(m, row16_max(fmaxf(lg[0], lg[1])));
     // weight scale: keep delta * 2^sexp below 2^14 over the chunk; the
     // chunk's largest delta is needed only when one reaches 2^(14 - sexp)
-    float dmax = fmaxf(ok[0] ? vsc[0].y : 0.f, ok[1] ? vsc[1].y : 0.f);
+    float dmax = fmaxf(vsc[0].y, vsc[1].y);
     int need = sexp;
     if (__ballot(dmax > 0.f && (sexp == 127 || dmax >= __builtin_ldexpf(1.0f, 14 - sexp))) != 0ull) {
       dmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max(dmax))));
@@ -437,13 +452,13 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
       for (int j = 0; j < 8; ++j) acc[j] *= f;
       m = mnew;
     }
-    float pk[2], wv[2];
+    float wv[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      pk[k] = lg[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lg[k] - m);
-      lsum += pk[k];
-      t1 = fmaf(pk[k], fmaf(0.5f, vsc[k].y, vsc[k].x), t1);
-      wv[k] = pk[k] * (vsc[k].y * wsc);
+      const float pk = lg[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lg[k] - m);
+      lsum += pk;
+      t1 = fmaf(pk, fmaf(0.5f, vsc[k].y, vsc[k].x), t1);
+      wv[k] = pk * (vsc[k].y * wsc);
     }
     // weights as fp16 hi + lo (truncated hi, exact remainder): 22 bits
     const auto whi = __builtin_amdgcn_cvt_pkrtz(wv[0], wv[1]);
