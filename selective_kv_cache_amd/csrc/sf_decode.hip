@@ -79,7 +79,7 @@ Carve carve(const sf_geom& g, int32_t batch, int64_t total_tokens, int64_t max_s
   c.scores = at; at += align256((size_t)hkv * total_tokens * 4);
   // per-head logits; one chunk of slack for the attention pass's last loads
   c.logits = at; at += align256((size_t)hkv * total_tokens * grp * 4 + 32 * 8 * 4);
-  c.counters = at; at += align256((size_t)batch * hkv * ((max_seq_tokens + kSelChunk - 1) / kSelChunk) * 4);
+  c.counters = at; at += align256((size_t)batch * hkv * ((max_seq_tokens + kSelChunk - 1) / kSelChunk + 2) * 4);
   c.cand = at; at += align256((size_t)batch * hkv * max_seq_tokens * 8);
   c.bitmap = at; at += align256((size_t)batch * hkv * bm_words * 4);
   c.sel = at; at += align256((size_t)batch * hkv * t * 4);
@@ -179,7 +179,7 @@ extern "C" sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* a
   p.bm_words = (int32_t)(((max_seq + kSelThreads - 1) / kSelThreads) * (kSelThreads / 32));
   p.use_refine = refine ? 1 : 0;
   p.n_sel_blk = n_sel_blk;
-  p.cnt_stride = (int32_t)((max_seq + kSelChunk - 1) / kSelChunk);
+  p.cnt_stride = (int32_t)((max_seq + kSelChunk - 1) / kSelChunk) + 2;   // + level-1 boundary
   p.cap = a->cap;
   p.ntot = total;
   p.off0 = off[0];

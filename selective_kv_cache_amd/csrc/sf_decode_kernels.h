@@ -11,7 +11,7 @@ struct DecodeParams {
   int32_t n_score_split, n_split, bm_words;
   int32_t use_refine;                      // selected rows take their refinement codes
   int32_t n_sel_blk;                       // work-groups of selected tokens (kSelBlkTok each)
-  int32_t cnt_stride;                      // selection chunks per sequence (max)
+  int32_t cnt_stride;                      // selection chunks per sequence (max) + 2
   int64_t cap, ntot, off0, max_seq;
   const int64_t* seq_off;
   const float* q;
@@ -22,7 +22,8 @@ struct DecodeParams {
   float* scores;       // [hkv][ntot]
   float* logits;       // [hkv][ntot][grp] per-head logits (matrix-core path)
   uint32_t* hist;      // [batch][hkv][kHistBins]: histogram of the scores' top key bits
-  uint32_t* counters;  // [batch][hkv][cnt_stride]: candidates of each selection chunk
+  uint32_t* counters;  // [batch][hkv][cnt_stride]: candidates of each selection chunk,
+                       // then the level-1 boundary bin and the count still needed there
   uint2* cand;         // [batch][hkv][max_seq] (score key, token); chunk c's at c*sel_chunk
   uint32_t* bitmap;    // [batch][hkv][bm_words]
   int32_t* sel;        // [batch][hkv][top_t]

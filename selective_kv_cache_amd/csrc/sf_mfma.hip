@@ -311,24 +311,24 @@ struct StageRegs {
 };
 
 template <int G>
-__device__ inline void read_stage(uint32_t aL, uint32_t aS, uint32_t aV, StageRegs& r) {
+__device__ inline void read_stage(uint32_t aL, uint32_t aS, const uint32_t (&aV)[4], StageRegs& r) {
   asm volatile(
       "ds_read_b32 %0, %12\n\t"
-      "ds_read_b32 %1, %12 offset:%15\n\t"
+      "ds_read_b32 %1, %12 offset:%18\n\t"
       "ds_read_b64 %2, %13\n\t"
       "ds_read_b64 %3, %13 offset:128\n\t"
       "ds_read_b32 %4, %14\n\t"
       "ds_read_b32 %5, %14 offset:512\n\t"
-      "ds_read_b32 %6, %14 offset:32\n\t"
-      "ds_read_b32 %7, %14 offset:544\n\t"
-      "ds_read_b32 %8, %14 offset:64\n\t"
-      "ds_read_b32 %9, %14 offset:576\n\t"
-      "ds_read_b32 %10, %14 offset:96\n\t"
-      "ds_read_b32 %11, %14 offset:608\n\t"
+      "ds_read_b32 %6, %15\n\t"
+      "ds_read_b32 %7, %15 offset:512\n\t"
+      "ds_read_b32 %8, %16\n\t"
+      "ds_read_b32 %9, %16 offset:512\n\t"
+      "ds_read_b32 %10, %17\n\t"
+      "ds_read_b32 %11, %17 offset:512\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(r.lg[0]), "=&v"(r.lg[1]), "=&v"(r.vsc[0]), "=&v"(r.vsc[1]), "=&v"(r.vw[0]), "=&v"(r.vw[1]),
         "=&v"(r.vw[2]), "=&v"(r.vw[3]), "=&v"(r.vw[4]), "=&v"(r.vw[5]), "=&v"(r.vw[6]), "=&v"(r.vw[7])
-      : "v"(aL), "v"(aS), "v"(aV), "n"(16 * G * 4)
+      : "v"(aL), "v"(aS), "v"(aV[0]), "v"(aV[1]), "v"(aV[2]), "v"(aV[3]), "n"(16 * G * 4)
       : "memory");
 }
 
@@ -352,19 +352,24 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   const int nchunks = (nsp + 31) / 32;
   const int nmine = nchunks > wid ? (nchunks - wid + 3) / 4 : 0;   // chunks wid, wid+4, ...
 
-  // Stage i of this wave <- chunk wid + 4*i.  Lane L loads V bytes
-  // [16L, 16L+16) and scale word L of the chunk (token L/2), lanes L < 8G
-  // the logits' bytes [16L, 16L+16).  Tokens past the split's end read its
-  // last token's V row (logits: the buffer has a chunk of slack), and loads
-  // past the wave's last chunk repeat the last chunk, so every issue is
-  // three in-bounds loads.
+  // Stage i of this wave <- chunk wid + 4*i.  Lane L loads the scale word L
+  // of the chunk (token L/2), lanes L < 8G the logits' bytes [16L, 16L+16),
+  // and half L&1 of V row (L/2) ^ ((L/8) & 3): row r of the chunk sits at
+  // stage row r ^ ((r/4) & 3), so that the four rows one P.V read takes
+  // (4rg + v, rg = 0..3) fall in different LDS banks.  Tokens past the
+  // split's end read its last token's V row (logits: the buffer has a chunk
+  // of slack), and loads past the wave's last chunk repeat the last chunk, so
+  // every issue is three in-bounds loads.
+  const int vrow = (lane >> 1) ^ ((lane >> 3) & 3);
   auto issue = [&](int i) {
     const int c = wid + 4 * i < nchunks ? wid + 4 * i : nchunks - 1;
     int rel = 32 * c + (lane >> 1);
     rel = rel < nsp ? rel : nsp - 1;
+    int relv = 32 * c + vrow;
+    relv = relv < nsp ? relv : nsp - 1;
     St& st = s.u.ring[wid][i % kRing];
     if (lane < 8 * G) dma16(lbase + (uint32_t)c * (32u * G * 4u) + 16u * (uint32_t)lane, st.lg);
-    dma16(vbase + (uint32_t)rel * 32u + 16u * (uint32_t)(lane & 1), st.v);
+    dma16(vbase + (uint32_t)relv * 32u + 16u * (uint32_t)(lane & 1), st.v);
     dma4(vscg + (uint32_t)rel * 2u + (uint32_t)(lane & 1), st.vs);
   };
 #pragma unroll
@@ -396,7 +401,9 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   const uint32_t wts = lds_addr(&s.wt[wid][hlc][2 * t]);
   const uint32_t offL = (uint32_t)(offsetof(St, lg) + 4 * (t * G + hlc));
   const uint32_t offS = (uint32_t)(offsetof(St, vs) + 8 * t);
-  const uint32_t offV = (uint32_t)(offsetof(St, v) + (4 * rg) * 32 + 4 * vdw);
+  uint32_t offV[4];                               // token 4rg + v at stage row 4rg + (v ^ rg)
+#pragma unroll
+  for (int v = 0; v < 4; ++v) offV[v] = (uint32_t)(offsetof(St, v) + (4 * rg + (v ^ rg)) * 32 + 4 * vdw);
 
   float m = -INFINITY, lsum = 0.f, t1 = 0.f;
   int sexp = 127;                                 // weight scale 2^sexp; 127 = not set yet
@@ -413,7 +420,8 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
     const int rem = nsp - 32 * c;                 // tokens of this chunk inside the split
     const uint32_t selw = (uint32_t)__builtin_amdgcn_readlane((int)(c < 64 ? sw0 : sw1), c & 63);
     StageRegs R;
-    read_stage<G>(sb + offL, sb + offS, sb + offV, R);
+    const uint32_t aV[4] = {sb + offV[0], sb + offV[1], sb + offV[2], sb + offV[3]};
+    read_stage<G>(sb + offL, sb + offS, aV, R);
     float lg[2];
     float2 vsc[2];
 #pragma unroll

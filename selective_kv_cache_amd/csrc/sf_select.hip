@@ -25,6 +25,7 @@ namespace sfk {
 
 constexpr int kResThreads = 1024;
 constexpr int kFinMax = 4096;   // level-3 candidates kept in LDS
+constexpr int kRankMax = 128;   // up to this many, level 3 ranks directly
 
 // 40-bit rank value of a level-3 candidate: low key byte over the inverted
 // token index (larger ranks first; no two candidates are equal).
@@ -103,7 +104,13 @@ __global__ void __launch_bounds__(kSelThreads) select_scan(DecodeParams p) {
     }
   }
   __syncthreads();
-  if (tid == 0) p.counters[sk * p.cnt_stride + chunk] = all ? 0u : sh_cnt;
+  if (tid == 0) {
+    p.counters[sk * p.cnt_stride + chunk] = all ? 0u : sh_cnt;
+    if (chunk == 0 && !all) {   // the level-1 boundary, for the resolve kernel
+      p.counters[sk * p.cnt_stride + p.cnt_stride - 2] = b1;
+      p.counters[sk * p.cnt_stride + p.cnt_stride - 1] = sh_need;
+    }
+  }
 }
 
 // Candidate j of a (sequence, KV head): segments of the chunks laid end to end
@@ -118,16 +125,19 @@ __device__ inline uint2 cand_at(const uint2* cand, const uint32_t* segoff, int n
 }
 
 constexpr int kLdsBitmapWords = 16384;   // sequences up to 512K tokens keep the bitmap in LDS
+constexpr int kCandLds = 4096;           // candidates kept in LDS
 
 __global__ void __launch_bounds__(kResThreads) select_resolve(DecodeParams p) {
   __shared__ uint32_t h[kHistBins];
   __shared__ uint32_t scan_lds[kResThreads / 64];
   __shared__ uint32_t rh[256];
+  __shared__ uint2 cl[kCandLds];
   __shared__ uint2 fin[kFinMax];
   __shared__ uint32_t segoff[kMaxSelChunks + 1];
   __shared__ uint32_t lbm[kLdsBitmapWords];
   __shared__ int sh_bin;
   __shared__ uint32_t sh_need, sh_fin;
+  static_assert(kMaxSelChunks <= kResThreads, "one chunk count per thread");
 
   const int tid = threadIdx.x;
   const int64_t sk = blockIdx.x;
@@ -138,51 +148,48 @@ __global__ void __launch_bounds__(kResThreads) select_resolve(DecodeParams p) {
   const bool all = (tn == n);
   uint32_t* gbm = p.bitmap + sk * p.bm_words;
   const uint2* cand = p.cand + sk * p.max_seq;
+  const uint32_t* cnts = p.counters + sk * p.cnt_stride;
   const int nch = (int)((n + p.sel_chunk - 1) / p.sel_chunk);
   const int64_t nw = (n + 31) >> 5;
   const bool in_lds = nw <= kLdsBitmapWords;
   uint32_t* bm = in_lds ? lbm : gbm;
+
+  // Everything this kernel reads from the scan is loaded up front: the
+  // chunks' candidate counts, the level-1 boundary, the bitmap words.  The
+  // level-1 histogram is cleared for the next step.
+  const uint32_t my_cnt = (!all && tid < nch) ? cnts[tid] : 0u;
+  const uint32_t need1 = all ? 0u : cnts[p.cnt_stride - 1];
   if (in_lds)
     for (int64_t w = tid; w < nw; w += kResThreads) lbm[w] = gbm[w];
-
-  // level 1 again (same result as select_scan); the global histogram is left
-  // zero for the next step
   uint32_t* h1 = p.hist + sk * kHistBins;
   for (int i = tid; i < kHistBins; i += kResThreads) {
-    if (!all) h[i] = h1[i];
     h1[i] = 0u;
+    h[i] = 0u;
   }
   if (!all) {
-    // then the candidates' level-2 digits
     // segment offsets: exclusive prefix of the per-chunk candidate counts
-    {
-      const int per = (nch + kResThreads - 1) / kResThreads;
-      uint32_t c = 0;
-      for (int k = tid * per; k < nch && k < (tid + 1) * per; ++k) c += p.counters[sk * p.cnt_stride + k];
-      uint32_t tot;
-      uint32_t run = block_exclusive_scan<kResThreads>(c, scan_lds, tot);
-      for (int k = tid * per; k < nch && k < (tid + 1) * per; ++k) {
-        segoff[k] = run;
-        run += p.counters[sk * p.cnt_stride + k];
-      }
-      if (tid == 0) {
-        segoff[nch] = tot;
-        sh_fin = 0u;
-      }
+    uint32_t ncand;
+    const uint32_t run = block_exclusive_scan<kResThreads>(my_cnt, scan_lds, ncand);
+    if (tid < nch) segoff[tid] = run;
+    if (tid == 0) {
+      segoff[nch] = ncand;
+      sh_fin = 0u;
     }
     __syncthreads();
-    const uint32_t ncand = segoff[nch];
-    find_threshold<kResThreads, kHistBins>(h, (uint32_t)tn, scan_lds, &sh_bin, &sh_need);
-    const uint32_t need1 = sh_need;
-    for (int i = tid; i < kHistBins; i += kResThreads) h[i] = 0u;
-    __syncthreads();
-    for (uint32_t j = tid; j < ncand; j += kResThreads)
-      atomicAdd(&h[(cand_at(cand, segoff, nch, p.sel_chunk, j).x >> 8) & 0xFFFu], 1u);
+    const bool cand_lds = ncand <= (uint32_t)kCandLds;
+    // level 2: histogram of the candidates' middle 12 key bits (candidates
+    // are copied to LDS on the way)
+    for (uint32_t j = tid; j < ncand; j += kResThreads) {
+      const uint2 cv = cand_at(cand, segoff, nch, p.sel_chunk, j);
+      if (cand_lds) cl[j] = cv;
+      atomicAdd(&h[(cv.x >> 8) & 0xFFFu], 1u);
+    }
     __syncthreads();
     find_threshold<kResThreads, kHistBins>(h, need1, scan_lds, &sh_bin, &sh_need);
     const uint32_t b2 = (uint32_t)sh_bin, need2 = sh_need;
+    auto cget = [&](uint32_t j) -> uint2 { return cand_lds ? cl[j] : cand_at(cand, segoff, nch, p.sel_chunk, j); };
     for (uint32_t j = tid; j < ncand; j += kResThreads) {
-      const uint2 cv = cand_at(cand, segoff, nch, p.sel_chunk, j);
+      const uint2 cv = cget(j);
       const uint32_t mid = (cv.x >> 8) & 0xFFFu;
       if (mid > b2) {
         atomicOr(&bm[cv.y >> 5], 1u << (cv.y & 31u));
@@ -200,44 +207,54 @@ __global__ void __launch_bounds__(kResThreads) select_resolve(DecodeParams p) {
         ok = true;
         return fin_value(fin[j]);
       }
-      const uint2 cv = cand_at(cand, segoff, nch, p.sel_chunk, j);
+      const uint2 cv = cget(j);
       ok = ((cv.x >> 8) & 0xFFFu) == b2;
       return fin_value(cv);
     };
     const uint32_t cnt = m <= kFinMax ? m : ncand;
-    uint64_t prefix = 0, mask = 0;
-    uint32_t need = need2;
-    for (int shift = 32; shift >= 0; shift -= 8) {
-      for (int i = tid; i < 256; i += kResThreads) rh[i] = 0u;
-      __syncthreads();
+    if (m <= (uint32_t)kRankMax) {
+      // few left: rank each by counting the larger ones (all values differ)
+      if (tid < (int)m) {
+        const uint64_t v = fin_value(fin[tid]);
+        uint32_t rank = 0;
+        for (uint32_t k = 0; k < m; ++k) rank += fin_value(fin[k]) > v ? 1u : 0u;
+        if (rank < need2) atomicOr(&bm[fin[tid].y >> 5], 1u << (fin[tid].y & 31u));
+      }
+    } else {
+      uint64_t prefix = 0, mask = 0;
+      uint32_t need = need2;
+      for (int shift = 32; shift >= 0; shift -= 8) {
+        for (int i = tid; i < 256; i += kResThreads) rh[i] = 0u;
+        __syncthreads();
+        for (uint32_t j = tid; j < cnt; j += kResThreads) {
+          bool ok;
+          const uint64_t v = get(j, ok);
+          if (ok && (v & mask) == prefix) atomicAdd(&rh[(v >> shift) & 0xFFu], 1u);
+        }
+        __syncthreads();
+        const uint32_t mine = tid < 256 ? rh[255 - tid] : 0u;
+        uint32_t tot;
+        const uint32_t above = block_exclusive_scan<kResThreads>(mine, scan_lds, tot);
+        if (tid < 256 && above < need && need <= above + mine) {
+          sh_bin = 255 - tid;
+          sh_need = need - above;
+        }
+        __syncthreads();
+        const int d = sh_bin;
+        const uint32_t left = sh_need;
+        const bool whole = rh[d] == left;     // the bucket is taken entirely
+        prefix |= (uint64_t)d << shift;
+        mask |= 0xFFull << shift;
+        need = left;
+        __syncthreads();
+        if (whole) break;
+      }
       for (uint32_t j = tid; j < cnt; j += kResThreads) {
         bool ok;
         const uint64_t v = get(j, ok);
-        if (ok && (v & mask) == prefix) atomicAdd(&rh[(v >> shift) & 0xFFu], 1u);
+        const uint32_t tok = m <= kFinMax ? fin[j].y : cget(j).y;
+        if (ok && (v & mask) >= prefix) atomicOr(&bm[tok >> 5], 1u << (tok & 31u));
       }
-      __syncthreads();
-      const uint32_t mine = tid < 256 ? rh[255 - tid] : 0u;
-      uint32_t tot;
-      const uint32_t above = block_exclusive_scan<kResThreads>(mine, scan_lds, tot);
-      if (tid < 256 && above < need && need <= above + mine) {
-        sh_bin = 255 - tid;
-        sh_need = need - above;
-      }
-      __syncthreads();
-      const int d = sh_bin;
-      const uint32_t left = sh_need;
-      const bool whole = rh[d] == left;     // the bucket is taken entirely
-      prefix |= (uint64_t)d << shift;
-      mask |= 0xFFull << shift;
-      need = left;
-      __syncthreads();
-      if (whole) break;
-    }
-    for (uint32_t j = tid; j < cnt; j += kResThreads) {
-      bool ok;
-      const uint64_t v = get(j, ok);
-      const uint32_t tok = m <= kFinMax ? fin[j].y : cand_at(cand, segoff, nch, p.sel_chunk, j).y;
-      if (ok && (v & mask) >= prefix) atomicOr(&bm[tok >> 5], 1u << (tok & 31u));
     }
   }
   __syncthreads();
