@@ -44,13 +44,16 @@ def algorithmic_bytes(w, lens):
 
 
 def kernel_bytes(w, lens):
-    """Algorithmic bytes of one launch of each pass.  score: base K codes and
-    scales of every token, plus the query.  attend: base K and V codes and
-    scales, the refinement rows of the selected K and V, the query; the split
-    partials it writes are not counted."""
+    """The layer's algorithmic bytes, each credited to the one pass that moves
+    it.  score: base K codes and (lo, delta) of every token, and the query.
+    attend: base V codes and (lo, delta) of every token, the refinement rows
+    of the selected K and V, and the output.  Implementation bytes (the
+    per-head logits the score pass hands to the attention pass, partials, the
+    re-read of the selected tokens' base K rows) are not credited; the two sum
+    to algorithmic_bytes()."""
     d, b, r, hkv = w.head_dim, w.base_bits, w.refine_bits, w.n_kv_heads
     score = sum(n * hkv * (d * b // 8 + 8) + w.n_q_heads * d * 4 for n in lens)
-    attend = sum(2 * n * hkv * (d * b // 8 + 8) + 2 * min(w.top_t, n) * hkv * d * r // 8 + w.n_q_heads * d * 4
+    attend = sum(n * hkv * (d * b // 8 + 8) + 2 * min(w.top_t, n) * hkv * d * r // 8 + w.n_q_heads * d * 4
                  for n in lens)
     return {"score": score, "attend": attend}
 
@@ -112,24 +115,98 @@ def time_steps(model, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def time_kernels(model, steps):
-    """Average duration of the score and attention kernels, from HIP events
-    recorded around each of their launches on the decode stream."""
+def capture_step(model):
+    """The whole step (every layer's decode, device-tier store) captured as one
+    HIP graph: the library launches only kernels on the caller's stream and
+    allocates nothing per step, so a replay is the step without host launch
+    overhead."""
     import torch
-    mk = lambda: torch.cuda.Event(enable_timing=True)
-    evs = [[tuple(mk() for _ in range(4)) for _ in range(model.L)] for _ in range(steps)]
-    for row in evs:
-        for quad in row:
-            for e in quad:
-                e.record()          # materialise the events before handing them over
+    model.step()                     # leaves the workspace histogram clear
     torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        model.step()
+    torch.cuda.synchronize()
+    return graph
+
+
+def time_graph(graph, steps, warmup):
+    """Exactly `steps` back-to-back graph replays, synchronized on both sides,
+    with a HIP event between consecutive ones: (mean ms per step over the
+    whole timed region, per-step ms)."""
+    import torch
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record()
+    for i in range(steps):
+        graph.replay()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    return evs[0].elapsed_time(evs[-1]) / steps, per
+
+
+def achievable_read_gbps():
+    """Streaming read bandwidth of the box from a plain reduction over 4 GiB
+    (torch's kernel; context for the peak, not a measurement of this path)."""
+    import torch
+    x = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        x.sum()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        x.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    del x
+    return x_bytes_per_ms(4 << 30, ms)
+
+
+def x_bytes_per_ms(nbytes, ms):
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+KERNELS = ("score", "scan", "resolve", "attend", "combine")
+
+
+def time_kernels(model, steps):
+    """Average duration of each kernel of the step, from HIP events on the
+    decode stream: every kernel launch completes an event attached to its own
+    dispatch (created without the system-scope fence, so no cache write-back
+    is added after it), and a kernel's duration is the difference between its
+    event and the one of the kernel launched just before it."""
+    import torch
+    from selective_kv_cache_amd.binding import TimingEvent
+    evs = [[tuple(TimingEvent() for _ in KERNELS) for _ in range(model.L)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    # hold the stream with a spin kernel while the host queues every timed
+    # launch, so that the kernels run back to back instead of waiting on the
+    # host (each launch costs the host more than some kernels take)
+    torch.cuda._sleep(50_000_000)
     for s in range(steps):
         model.step(events=evs[s])
     torch.cuda.synchronize()
-    score = [q[0].elapsed_time(q[1]) for row in evs for q in row]
-    attend = [q[2].elapsed_time(q[3]) for row in evs for q in row]
-    return {"score": float(np.mean(score)), "attend": float(np.mean(attend)),
-            "score_median": float(np.median(score)), "attend_median": float(np.median(attend))}
+    flat = [quint for row in evs for quint in row]
+    dur = {k: [] for k in KERNELS}
+    for i, ev in enumerate(flat):
+        prev = flat[i - 1][4] if i else None          # combine of the layer before
+        for j, k in enumerate(KERNELS):
+            before = ev[j - 1] if j else prev
+            if before is not None:
+                dur[k].append(before.elapsed_ms(ev[j]))
+    for quint in flat:
+        for e in quint:
+            e.close()
+    out = {}
+    for k in KERNELS:
+        out[k] = float(np.mean(dur[k]))
+        out[k + "_median"] = float(np.median(dur[k]))
+    return out
 
 
 def cpu_baseline(w, layer_budget_s=30.0):
@@ -219,16 +296,36 @@ def main():
     tier = B.SF_TIER_DEVICE if args.tier == "device" else B.SF_TIER_HOST_PINNED
     log(f"setup {w.name}: {w.layers} layers, ctx {w.seq_lengths()[:4]}, tier {args.tier}")
     model = Model(w, tier)
-    log("timing steps")
-    ms = time_steps(model, args.steps, args.warmup)
-    log(f"{ms:.3f} ms/step; timing the score and attention kernels")
+    log("timing steps (eager launches)")
+    ms_eager = time_steps(model, args.steps, args.warmup)
+    launch = "eager"
+    ms, p50, p10, p90 = ms_eager, None, None, None
+    if tier == B.SF_TIER_DEVICE:
+        log(f"{ms_eager:.3f} ms/step eager; capturing the step as a HIP graph")
+        graph = capture_step(model)
+        ms, per = time_graph(graph, args.steps, args.warmup)
+        p50, p10, p90 = (float(np.percentile(per, q)) for q in (50, 10, 90))
+        launch = "hip_graph"
+        del graph
+    log(f"{ms:.3f} ms/step ({launch}); timing each kernel with HIP events")
     kt = time_kernels(model, max(2, args.steps // 4))
     model.close()
     del model
+    # Each event-timed launch waits on its predecessor's event, which costs
+    # the same fixed dispatch gap per kernel; the graph replay runs the same
+    # kernels back to back without events.  The gap is therefore the per-kernel
+    # share of (sum of event-timed kernels per layer - graph step per layer),
+    # and each kernel's duration is its event time less that gap.
+    raw_layer = sum(kt[k] for k in KERNELS)
+    gap = max(0.0, (raw_layer - ms / w.layers) / len(KERNELS)) if launch == "hip_graph" else 0.0
+    kt_raw = {k: kt[k] for k in KERNELS}
+    for k in KERNELS:
+        kt[k] -= gap
+        kt[k + "_median"] -= gap
 
     step_bytes = algorithmic_bytes(w, w.seq_lengths()) * w.layers
     kb = kernel_bytes(w, w.seq_lengths())
-    dom = max(("score", "attend"), key=lambda k: kt[k])
+    dom = max(kb, key=lambda k: kt[k])
     gbps = {k: kb[k] / (kt[k] * 1e-3) / 1e9 for k in kb}
     rec = {
         "metric": METRIC, "value": 1e3 / ms, "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
@@ -237,7 +334,8 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "ctx": w.ctx or list(w.ctx_range),
                    "layers": w.layers, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "base_bits": w.base_bits, "refine_bits": w.refine_bits,
-                   "top_t": w.top_t, "refinement_store": args.tier},
+                   "top_t": w.top_t, "refinement_store": args.tier, "launch": launch},
+        "ms_per_step_p50": p50, "ms_per_step_p10": p10, "ms_per_step_p90": p90, "eager_ms_per_step": ms_eager,
         "step_algorithmic_bytes": step_bytes,
         "step_hbm_gbps": step_bytes / (ms * 1e-3) / 1e9,
         "step_frac_of_peak": step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
@@ -246,24 +344,31 @@ def main():
                      "bytes_per_launch": kb[dom], "avg_launch_ms": kt[dom],
                      "kernels": {k: {"bytes_per_launch": kb[k], "avg_launch_ms": kt[k],
                                      "median_launch_ms": kt[k + "_median"], "achieved_gbps": gbps[k]}
-                                 for k in kb}},
+                                 for k in kb},
+                     "other_kernels_avg_ms": {k: kt[k] for k in KERNELS if k not in kb},
+                     "event_timing": {"raw_avg_ms": kt_raw, "dispatch_gap_ms": gap,
+                                      "note": "avg_launch_ms = event-timed duration less the per-kernel "
+                                              "dispatch gap, both from HIP events in this run"}},
     }
     if not args.no_secondary:
         sec = {}
         w2 = W.WORKLOADS["llama8b_32k"]
         log("secondary: llama8b_32k")
         m2 = Model(w2, B.SF_TIER_DEVICE)
-        ms2 = time_steps(m2, args.steps, args.warmup)
+        g2 = capture_step(m2)
+        ms2 = time_graph(g2, args.steps, args.warmup)[0]
+        del g2
         m2.close()
         del m2
         b2 = algorithmic_bytes(w2, w2.seq_lengths()) * w2.layers
-        sec["llama8b_32k"] = {"steps_per_s": 1e3 / ms2, "ms_per_step": ms2,
+        sec["llama8b_32k"] = {"steps_per_s": 1e3 / ms2, "ms_per_step": ms2, "launch": "hip_graph",
                               "step_hbm_gbps": b2 / (ms2 * 1e-3) / 1e9,
                               "step_frac_of_peak": b2 / (ms2 * 1e-3) / 1e9 / PEAK_HBM_GBPS}
         if w.host_store:
             log("secondary: host-pinned store")
             sec["host_store"] = host_tier_run(w, max(4, args.steps // 2), 2)
         rec["secondary"] = sec
+    rec["achievable_read_gbps"] = achievable_read_gbps()
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on a bounded sample)")
         rec["cpu_baseline"] = cpu_baseline(w)

@@ -180,10 +180,13 @@ typedef struct sf_decode_args {
   void* workspace;               /* device scratch of sf_decode_workspace_size() bytes  */
   size_t workspace_bytes;
   int32_t flags;                 /* 0 or SF_DECODE_HIST_CLEAN                           */
-  void* events[4];               /* optional hipEvent_t recorded on `stream` before and
-                                    after the score kernel ([0], [1]) and before and
-                                    after the attention kernel ([2], [3]); NULL = none.
-                                    Lets a caller time those kernels.                  */
+  void* events[5];               /* optional hipEvent_t (NULL = none), each completed with
+                                    one kernel of the step, in launch order: [0] score,
+                                    [1] selection scan, [2] selection resolve, [3]
+                                    attention, [4] combine.  The selection events are
+                                    not recorded when T == 0.  The difference of two
+                                    consecutive ones is the time of the kernel between
+                                    them (create them without the system-scope fence).  */
 } sf_decode_args;
 
 /* Scratch needed by sf_decode_step for this batch shape.

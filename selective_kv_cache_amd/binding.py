@@ -46,7 +46,7 @@ class sf_decode_args(ctypes.Structure):
                 ("v_scales", c_vp), ("cap", c_i64), ("store", c_vp), ("top_t", c_i32), ("out", c_vp),
                 ("sel_out", c_vp), ("scores_out", c_vp), ("stats", ctypes.POINTER(sf_step_stats)),
                 ("workspace", c_vp), ("workspace_bytes", c_size), ("flags", c_i32),
-                ("events", c_vp * 4)]
+                ("events", c_vp * 5)]
 
 
 class SfError(RuntimeError):
@@ -88,6 +88,45 @@ def load() -> ctypes.CDLL:
             getattr(lib, name).restype = c_i32
     _LIB = lib
     return lib
+
+
+class TimingEvent:
+    """A HIP event created without the system-scope fence (hipEventDisableSystemFence),
+    for the ``events`` of sf_decode_step: it times the kernel it is attached to,
+    not the cache write-back a fenced event adds after it."""
+
+    _hip: Optional[ctypes.CDLL] = None
+    _FLAGS = 0x20000000      # hipEventDisableSystemFence
+
+    @classmethod
+    def _runtime(cls) -> ctypes.CDLL:
+        if cls._hip is None:
+            load()                                     # torch first: one HIP runtime in the process
+            hip = ctypes.CDLL("libamdhip64.so.7")
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(c_vp), ctypes.c_uint]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), c_vp, c_vp]
+            hip.hipEventDestroy.argtypes = [c_vp]
+            cls._hip = hip
+        return cls._hip
+
+    def __init__(self):
+        h = c_vp()
+        rc = self._runtime().hipEventCreateWithFlags(ctypes.byref(h), self._FLAGS)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        self.handle = h.value
+
+    def elapsed_ms(self, end: "TimingEvent") -> float:
+        ms = ctypes.c_float()
+        rc = self._runtime().hipEventElapsedTime(ctypes.byref(ms), self.handle, end.handle)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def close(self) -> None:
+        if self.handle:
+            self._runtime().hipEventDestroy(self.handle)
+            self.handle = None
 
 
 def _check(status: int, what: str) -> None:
@@ -170,8 +209,9 @@ def sf_decode_step(g: sf_geom, *, seq_off_host: Sequence[int], seq_off_dev, q, k
     a.workspace = _ptr(workspace)
     a.workspace_bytes = workspace.numel() * workspace.element_size()
     a.flags = flags
-    if events is not None:       # (score begin, score end, attend begin, attend end), None allowed
+    if events is not None:       # completed with score, scan, resolve, attention, combine; None allowed
         for i, e in enumerate(events):
-            a.events[i] = None if e is None else (e.cuda_event if hasattr(e, "cuda_event") else e)
+            a.events[i] = None if e is None else (e.handle if hasattr(e, "handle") else
+                                                  e.cuda_event if hasattr(e, "cuda_event") else e)
     _check(load().sf_decode_step(ctypes.byref(g), ctypes.byref(a), _stream(stream)), "sf_decode_step")
     return st.as_dict() if want_stats else None

@@ -220,30 +220,30 @@ __global__ void __launch_bounds__(256) combine(DecodeParams p) {
 }
 
 template <int BB>
-static bool attend_g(const DecodeParams& p, dim3 grid, hipStream_t st) {
+static bool attend_g(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev) {
   switch (p.grp) {
-    case 1: hipLaunchKernelGGL((attend_valu<BB, 1>), grid, dim3(256), 0, st, p); return true;
-    case 2: hipLaunchKernelGGL((attend_valu<BB, 2>), grid, dim3(256), 0, st, p); return true;
-    case 4: hipLaunchKernelGGL((attend_valu<BB, 4>), grid, dim3(256), 0, st, p); return true;
-    case 8: hipLaunchKernelGGL((attend_valu<BB, 8>), grid, dim3(256), 0, st, p); return true;
+    case 1: sf_launch(attend_valu<BB, 1>, grid, dim3(256), st, ev, p); return true;
+    case 2: sf_launch(attend_valu<BB, 2>, grid, dim3(256), st, ev, p); return true;
+    case 4: sf_launch(attend_valu<BB, 4>, grid, dim3(256), st, ev, p); return true;
+    case 8: sf_launch(attend_valu<BB, 8>, grid, dim3(256), st, ev, p); return true;
   }
   return false;
 }
 
-bool launch_attend_mfma(const DecodeParams& p, dim3 grid, hipStream_t st);
+bool launch_attend_mfma(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev);
 
-bool launch_attend(const DecodeParams& p, dim3 grid, hipStream_t st) {
-  if (launch_attend_mfma(p, grid, st)) return true;
+bool launch_attend(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev) {
+  if (launch_attend_mfma(p, grid, st, ev)) return true;
   switch (p.b) {
-    case 2: return attend_g<2>(p, grid, st);
-    case 3: return attend_g<3>(p, grid, st);
-    case 4: return attend_g<4>(p, grid, st);
+    case 2: return attend_g<2>(p, grid, st, ev);
+    case 3: return attend_g<3>(p, grid, st, ev);
+    case 4: return attend_g<4>(p, grid, st, ev);
   }
   return false;
 }
 
-void launch_combine(const DecodeParams& p, hipStream_t st) {
-  hipLaunchKernelGGL(combine, dim3(p.batch * p.hq, kHeadDim / 32), dim3(256), 0, st, p);
+void launch_combine(const DecodeParams& p, hipStream_t st, KernelEvents ev) {
+  sf_launch(combine, dim3(p.batch * p.hq, kHeadDim / 32), dim3(256), st, ev, p);
 }
 
 }  // namespace sfk

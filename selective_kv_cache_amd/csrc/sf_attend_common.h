@@ -48,11 +48,11 @@ __device__ inline void quarter_dots(const uint32_t* kb, const uint32_t* kr, cons
 }
 
 // Merge the four wavefronts' (m, l, acc) of a 256-thread work-group into one
-// partial.  mw/lw [4][G], accw [4][G][D] in LDS; called by all 256 threads
-// after a barrier.
-template <int G>
+// partial.  mw/lw [4][G], accw [4][R >= G][D] in LDS (rows past G unused);
+// called by all 256 threads after a barrier.
+template <int G, int R = G>
 __device__ inline void write_partial(float* part, const float (*mw)[G], const float (*lw)[G],
-                                     const float (*accw)[G][kHeadDim]) {
+                                     const float (*accw)[R][kHeadDim]) {
   for (int i = threadIdx.x; i < G * kHeadDim; i += 256) {
     const int h = i / kHeadDim, d = i % kHeadDim;
     float M = -INFINITY;

@@ -123,7 +123,7 @@ extern "C" sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* a
   if (s != SF_OK) return s;
   if (!a || a->batch <= 0 || !a->seq_off_host || !a->seq_off_dev || !a->q || !a->k_codes ||
       !a->k_scales || !a->v_codes || !a->v_scales || !a->out || !a->workspace || a->cap <= 0 ||
-      a->top_t < 0 || (a->flags & ~SF_DECODE_HIST_CLEAN) != 0 || (!a->events[0] != !a->events[1]) || (!a->events[2] != !a->events[3]))
+      a->top_t < 0 || (a->flags & ~SF_DECODE_HIST_CLEAN) != 0)
     return SF_ERR_INVALID_ARG;
   const int32_t B = a->batch;
   const int64_t* off = a->seq_off_host;
@@ -220,12 +220,12 @@ extern "C" sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* a
                        reinterpret_cast<uint32_t*>(ws + c.hist), nzero);
     SF_LAUNCH_CHECK("zero_words");
   }
-  if (a->events[0]) SF_HIP_CHECK(hipEventRecord((hipEvent_t)a->events[0], hs));
-  if (!launch_score(p, dim3(n_score, p.hkv), hs)) return SF_ERR_UNSUPPORTED;
+  const auto stop = [&](int i) { return KernelEvents{nullptr, (hipEvent_t)a->events[i]}; };
+  if (!launch_score(p, dim3(n_score, p.hkv), hs, stop(0)))
+    return SF_ERR_UNSUPPORTED;
   SF_LAUNCH_CHECK("score");
-  if (a->events[1]) SF_HIP_CHECK(hipEventRecord((hipEvent_t)a->events[1], hs));
   if (a->top_t > 0) {
-    launch_select(p, dim3(n_sel, p.hkv), hs);
+    launch_select(p, dim3(n_sel, p.hkv), hs, stop(1), stop(2));
     SF_LAUNCH_CHECK("select_top_t");
   }
   if (a->stats) {
@@ -239,11 +239,10 @@ extern "C" sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* a
     if (s != SF_OK) return s;
     if (a->stats) a->stats->hits = a->stats->selected - a->stats->misses;
   }
-  if (a->events[2]) SF_HIP_CHECK(hipEventRecord((hipEvent_t)a->events[2], hs));
-  if (!launch_attend(p, dim3(n_sel_blk + n_split, p.hkv), hs)) return SF_ERR_UNSUPPORTED;
+  if (!launch_attend(p, dim3(n_sel_blk + n_split, p.hkv), hs, stop(3)))
+    return SF_ERR_UNSUPPORTED;
   SF_LAUNCH_CHECK("attend");
-  if (a->events[3]) SF_HIP_CHECK(hipEventRecord((hipEvent_t)a->events[3], hs));
-  launch_combine(p, hs);
+  launch_combine(p, hs, stop(4));
   SF_LAUNCH_CHECK("combine");
   return SF_OK;
 }

@@ -1,6 +1,8 @@
 // Device-side parameter block and helpers of the decode step.
 #pragma once
 
+#include <hip/hip_ext.h>
+
 #include "sf_internal.h"
 
 namespace sfk {
@@ -143,11 +145,27 @@ __device__ inline void find_threshold(const uint32_t* hist, uint32_t need, uint3
   __syncthreads();
 }
 
+// Optional events attached to a kernel's dispatch: `stop` completes with the
+// kernel itself (no marker packet after it); `start` is recorded just before
+// it.
+struct KernelEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+
+template <typename K>
+inline void sf_launch(K kernel, dim3 grid, dim3 block, hipStream_t st, KernelEvents ev, const DecodeParams& p) {
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, ev.start, ev.stop, 0, p);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, p);
+}
+
 // Launchers (one per stage source file).
-bool launch_score(const DecodeParams& p, dim3 grid, hipStream_t st);
-void launch_select(const DecodeParams& p, dim3 grid, hipStream_t st);
-bool launch_attend(const DecodeParams& p, dim3 grid, hipStream_t st);
-void launch_combine(const DecodeParams& p, hipStream_t st);
+bool launch_score(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev = {});
+void launch_select(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents scan_ev = {},
+                   KernelEvents resolve_ev = {});
+bool launch_attend(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev = {});
+void launch_combine(const DecodeParams& p, hipStream_t st, KernelEvents ev = {});
 
 constexpr int kSelThreads = 512;
 constexpr int32_t kSelChunk = 4096;

@@ -139,6 +139,15 @@ __device__ inline void dma4(const void* g, void* l) {
   __builtin_amdgcn_global_load_lds(g, (lds_void_t)l, 4, 0, 0);
 }
 
+// Sum over the 16 lanes of a row (DPP row rotations).
+__device__ inline float row16_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false));
+  return x;
+}
+
 // Maximum over the 16 lanes of a row (DPP row rotations, no LDS traffic).
 __device__ inline float row16_max(float x) {
   x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false)));
@@ -168,6 +177,17 @@ __device__ inline v8h lds_read_v8h(uint32_t a) {
   v4u v;
   asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v) : "v"(a) : "memory");
   return __builtin_bit_cast(v8h, v);
+}
+
+// Two 16-byte reads 1 KiB apart.
+__device__ inline void lds_read_2v8h(uint32_t a, v8h& x, v8h& y) {
+  v4u u, v;
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(u), "=&v"(v)
+               : "v"(a)
+               : "memory");
+  x = __builtin_bit_cast(v8h, u);
+  y = __builtin_bit_cast(v8h, v);
 }
 
 // ---------------------------------------------------------------------------
@@ -292,11 +312,11 @@ struct Stage {
 
 template <int G>
 struct MfmaLds {
-  alignas(16) _Float16 wt[4][16][32];   // per wave: P.V weights [column][kappa]
+  alignas(16) _Float16 wt[4][2][16][32];   // per wave: P.V weights, hi and lo parts [column][kappa]
   float mw[4][G], lw[4][G];
   union {
     Stage<G> ring[4][kRing];
-    float accw[4][G][kHeadDim];         // after the stream: per-wave P.V totals
+    float accw[4][G + 1][kHeadDim];        // after the stream: per-wave P.V totals (row G: unused lanes)
   } u;
 };
 
@@ -375,7 +395,7 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
 #pragma unroll
   for (int i = 0; i < kRing - 1; ++i) issue(i);
 
-  for (int i = lane; i < 16 * 32; i += 64) (&s.wt[wid][0][0])[i] = (_Float16)0.f;
+  for (int i = lane; i < 2 * 16 * 32; i += 64) (&s.wt[wid][0][0][0])[i] = (_Float16)0.f;
   // selection words of the split (one per chunk) in two registers: lane L
   // holds those of chunks L and 64 + L; splits start on a word boundary
   constexpr int kMaxSplitWords = 4096 / 32;
@@ -397,8 +417,9 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   // stands for token 16j + u, so lane (n, rg) takes tokens 4rg..4rg+3 and
   // 16+4rg..16+4rg+3, and a logit lane's two weights are adjacent.
   const uint32_t ring0 = lds_addr(&s.u.ring[wid][0]);
-  const uint32_t wt0 = lds_addr(&s.wt[wid][n][8 * rg]);
-  const uint32_t wts = lds_addr(&s.wt[wid][hlc][2 * t]);
+  const uint32_t wt0 = lds_addr(&s.wt[wid][0][n][8 * rg]);
+  const uint32_t wts = lds_addr(&s.wt[wid][0][hlc][2 * t]);
+  static_assert(sizeof(s.wt[0][0]) == 1024, "lo part 1 KiB after the hi part");
   const uint32_t offL = (uint32_t)(offsetof(St, lg) + 4 * (t * G + hlc));
   const uint32_t offS = (uint32_t)(offsetof(St, vs) + 8 * t);
   uint32_t offV[4];                               // token 4rg + v at stage row 4rg + (v ^ rg)
@@ -473,9 +494,10 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
     const auto wlo = __builtin_amdgcn_cvt_pkrtz(wv[0] - (float)whi[0], wv[1] - (float)whi[1]);
     if (hl < G) {
       lds_write_u32(wts, __builtin_bit_cast(uint32_t, whi));
-      lds_write_u32(wts + (uint32_t)(G * 32 * sizeof(_Float16)), __builtin_bit_cast(uint32_t, wlo));
+      lds_write_u32(wts + 1024u, __builtin_bit_cast(uint32_t, wlo));
     }
-    const v8h bw = lds_read_v8h(wt0);
+    v8h bhi, blo;
+    lds_read_2v8h(wt0, bhi, blo);
     const uint32_t* vw = R.vw;
     uint32_t P[4], Q[4];
 #pragma unroll
@@ -489,7 +511,8 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
       v4u av;
 #pragma unroll
       for (int v = 0; v < 4; ++v) av[v] = (tt <= 4 ? P[v] : Q[v]) & mk;
-      acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, av), bw, acc[tt], 0, 0, 0);
+      acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, av), bhi, acc[tt], 0, 0, 0);
+      acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, av), blo, acc[tt], 0, 0, 0);
     }
   }
   // the ring is reused below: no load of this wave may still be landing, and
@@ -497,31 +520,28 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  // wave totals: l and the scalar term per head (row sums), P.V per head;
-  // the maximum goes back to natural-log units
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) {
-    lsum += __shfl_xor(lsum, o);
-    t1 += __shfl_xor(t1, o);
-  }
+  // wave totals: l and the scalar term per head (row sums), P.V per head
+  // (column n = head n); the maximum goes back to natural-log units
+  lsum = row16_sum(lsum);
+  t1 = row16_sum(t1);
   if (hl < G && t == 0) {
     s.mw[wid][hl] = m * 0.6931471805599453f;
     s.lw[wid][hl] = lsum;
   }
-  const float t1n = __shfl(t1, 16 * (n < G ? n : 0));
+  float t1n = lane_value(t1, 0);
+#pragma unroll
+  for (int h = 1; h < G; ++h) t1n = n == h ? lane_value(t1, 16 * h) : t1n;
   const int se = sexp == 127 ? 0 : sexp;
+  const int nrow = n < G ? n : G;
 #pragma unroll
   for (int tt = 0; tt < 8; ++tt) {
     const float f = __builtin_ldexpf(1.0f, 24 - 2 * (tt <= 4 ? tt : tt - 5) - se);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float v = acc[tt][j] + __shfl_xor(acc[tt][j], G);
-      if (n < G) s.u.accw[wid][n][32 * rg + 8 * j + tt] = fmaf(v, f, t1n);
-    }
+    for (int j = 0; j < 4; ++j) s.u.accw[wid][nrow][32 * rg + 8 * j + tt] = fmaf(acc[tt][j], f, t1n);
   }
   __syncthreads();
   float* part = p.part + ((int64_t)kvh * (p.n_sel_blk + p.n_split) + p.n_sel_blk + split) * G * kPartStride;
-  write_partial<G>(part, s.mw, s.lw, s.u.accw);
+  write_partial<G, G + 1>(part, s.mw, s.lw, s.u.accw);
 }
 
 template <int G>
@@ -533,22 +553,22 @@ __global__ void __launch_bounds__(256) attend_mfma(DecodeParams p) {
     base_split_mfma<G>(p, blockIdx.x - p.n_sel_blk, blockIdx.y, smem);
 }
 
-bool launch_score_mfma(const DecodeParams& p, dim3 grid, hipStream_t st) {
+bool launch_score_mfma(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev) {
   if (p.b != 2) return false;
   switch (p.grp) {
-    case 1: hipLaunchKernelGGL((score_mfma<1>), grid, dim3(256), 0, st, p); return true;
-    case 2: hipLaunchKernelGGL((score_mfma<2>), grid, dim3(256), 0, st, p); return true;
-    case 4: hipLaunchKernelGGL((score_mfma<4>), grid, dim3(256), 0, st, p); return true;
+    case 1: sf_launch(score_mfma<1>, grid, dim3(256), st, ev, p); return true;
+    case 2: sf_launch(score_mfma<2>, grid, dim3(256), st, ev, p); return true;
+    case 4: sf_launch(score_mfma<4>, grid, dim3(256), st, ev, p); return true;
   }
   return false;
 }
 
-bool launch_attend_mfma(const DecodeParams& p, dim3 grid, hipStream_t st) {
+bool launch_attend_mfma(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev) {
   if (p.b != 2) return false;
   switch (p.grp) {
-    case 1: hipLaunchKernelGGL((attend_mfma<1>), grid, dim3(256), 0, st, p); return true;
-    case 2: hipLaunchKernelGGL((attend_mfma<2>), grid, dim3(256), 0, st, p); return true;
-    case 4: hipLaunchKernelGGL((attend_mfma<4>), grid, dim3(256), 0, st, p); return true;
+    case 1: sf_launch(attend_mfma<1>, grid, dim3(256), st, ev, p); return true;
+    case 2: sf_launch(attend_mfma<2>, grid, dim3(256), st, ev, p); return true;
+    case 4: sf_launch(attend_mfma<4>, grid, dim3(256), st, ev, p); return true;
   }
   return false;
 }

@@ -89,24 +89,24 @@ __global__ void __launch_bounds__(256) score_valu(DecodeParams p) {
 }
 
 template <int BB>
-static bool score_g(const DecodeParams& p, dim3 grid, hipStream_t st) {
+static bool score_g(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev) {
   switch (p.grp) {
-    case 1: hipLaunchKernelGGL((score_valu<BB, 1>), grid, dim3(256), 0, st, p); return true;
-    case 2: hipLaunchKernelGGL((score_valu<BB, 2>), grid, dim3(256), 0, st, p); return true;
-    case 4: hipLaunchKernelGGL((score_valu<BB, 4>), grid, dim3(256), 0, st, p); return true;
-    case 8: hipLaunchKernelGGL((score_valu<BB, 8>), grid, dim3(256), 0, st, p); return true;
+    case 1: sf_launch(score_valu<BB, 1>, grid, dim3(256), st, ev, p); return true;
+    case 2: sf_launch(score_valu<BB, 2>, grid, dim3(256), st, ev, p); return true;
+    case 4: sf_launch(score_valu<BB, 4>, grid, dim3(256), st, ev, p); return true;
+    case 8: sf_launch(score_valu<BB, 8>, grid, dim3(256), st, ev, p); return true;
   }
   return false;
 }
 
-bool launch_score_mfma(const DecodeParams& p, dim3 grid, hipStream_t st);
+bool launch_score_mfma(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev);
 
-bool launch_score(const DecodeParams& p, dim3 grid, hipStream_t st) {
-  if (launch_score_mfma(p, grid, st)) return true;
+bool launch_score(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev) {
+  if (launch_score_mfma(p, grid, st, ev)) return true;
   switch (p.b) {
-    case 2: return score_g<2>(p, grid, st);
-    case 3: return score_g<3>(p, grid, st);
-    case 4: return score_g<4>(p, grid, st);
+    case 2: return score_g<2>(p, grid, st, ev);
+    case 3: return score_g<3>(p, grid, st, ev);
+    case 4: return score_g<4>(p, grid, st, ev);
   }
   return false;
 }

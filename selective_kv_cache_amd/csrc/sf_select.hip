@@ -290,9 +290,9 @@ __global__ void __launch_bounds__(kResThreads) select_resolve(DecodeParams p) {
   }
 }
 
-void launch_select(const DecodeParams& p, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL(select_scan, grid, dim3(kSelThreads), 0, st, p);
-  hipLaunchKernelGGL(select_resolve, dim3(p.batch * p.hkv), dim3(kResThreads), 0, st, p);
+void launch_select(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents scan_ev, KernelEvents resolve_ev) {
+  sf_launch(select_scan, grid, dim3(kSelThreads), st, scan_ev, p);
+  sf_launch(select_resolve, dim3(p.batch * p.hkv), dim3(kResThreads), st, resolve_ev, p);
 }
 
 }  // namespace sfk

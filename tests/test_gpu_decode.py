@@ -124,6 +124,56 @@ def test_consecutive_steps_share_one_workspace():
         P.compare_layer(w, k, v, q, off, w.top_t, run, codec=False)
 
 
+def test_graph_replay_matches_eager():
+    # the device-tier step launches kernels only, so it can be captured; every
+    # replay, with eager steps and synchronisations in between, must equal the
+    # eager result bit for bit
+    import torch
+    from selective_kv_cache_amd.kvcache import Decoder, LayerCache
+    w = W.small("graph", cfg_id=304, batch=2, n_q_heads=8, n_kv_heads=2, refine_bits=4, top_t=100)
+    off = W.seq_offsets([3000, 1200])
+    g = P.geom_of(w)
+    caches, qs = [], []
+    try:
+        for layer in range(2):
+            c = LayerCache(g, int(off[-1]))
+            k, v = W.layer_kv(w, layer, n_tok=int(off[-1]))
+            c.append(torch.as_tensor(k, device="cuda"), torch.as_tensor(v, device="cuda"), 0)
+            caches.append(c)
+            qs.append(torch.as_tensor(W.query(w, layer), device="cuda"))
+        dec = Decoder(g, off, w.top_t)
+        outs = [torch.empty((2, 8, 128), dtype=torch.float32, device="cuda") for _ in range(2)]
+        sels = [torch.empty((2, 2, w.top_t), dtype=torch.int32, device="cuda") for _ in range(2)]
+
+        def step():
+            for layer in range(2):
+                dec.step(caches[layer], qs[layer], out=outs[layer], sel_out=sels[layer])
+
+        step()
+        torch.cuda.synchronize()
+        want = [o.cpu().numpy().copy() for o in outs]
+        want_sel = [x.cpu().numpy().copy() for x in sels]
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for rep in range(3):
+            for o in outs:
+                o.fill_(float("nan"))
+            graph.replay()
+            torch.cuda.synchronize()
+            for layer in range(2):
+                assert np.array_equal(outs[layer].cpu().numpy().view(np.uint32), want[layer].view(np.uint32)), rep
+                assert np.array_equal(sels[layer].cpu().numpy(), want_sel[layer]), rep
+            step()                      # eager work between replays
+            torch.cuda.synchronize()
+            for layer in range(2):
+                assert np.array_equal(outs[layer].cpu().numpy().view(np.uint32), want[layer].view(np.uint32))
+        del graph
+    finally:
+        for c in caches:
+            c.close()
+
+
 def test_host_tier_matches_device_tier_and_cache_simulation():
     """Host-pinned store + device refinement cache over several steps of an
     AR(1) query process: outputs bit-identical to the device-resident store,
