@@ -167,6 +167,34 @@ def achievable_read_gbps():
     return x_bytes_per_ms(4 << 30, ms)
 
 
+def source_hash():
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "selective_kv_cache_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of each kernel from the committed counter summary
+    (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by a copy of known size), or {}
+    when there is none or it was taken on other library sources."""
+    path = os.path.join(ROOT, "profiles", f"decode_step_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return {}
+    vals, sha = {}, None
+    with open(path) as fh:
+        for ln in fh:
+            if ln.startswith("source_sha256_16:"):
+                sha = ln.split(":", 1)[1].strip()
+            elif ln.startswith("traffic_bytes "):
+                k, v = ln[len("traffic_bytes "):].split(":")
+                vals[k.strip()] = float(v)
+    return vals if sha == source_hash() else {}
+
+
 def x_bytes_per_ms(nbytes, ms):
     return nbytes / (ms * 1e-3) / 1e9
 
@@ -282,6 +310,9 @@ def main():
     ap.add_argument("--tier", choices=["device", "host"], default="device")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only copy BYTES between two device buffers 3 times (reference for the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the decode step is measured on one GPU's share "
@@ -292,6 +323,14 @@ def main():
     from selective_kv_cache_amd import binding as B
     from selective_kv_cache_amd import workloads as W
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        src = torch.ones(args.calibrate_copy // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {args.calibrate_copy} bytes 3 times")
+        return
     w = W.WORKLOADS[args.workload]
     tier = B.SF_TIER_DEVICE if args.tier == "device" else B.SF_TIER_HOST_PINNED
     log(f"setup {w.name}: {w.layers} layers, ctx {w.seq_lengths()[:4]}, tier {args.tier}")
@@ -340,7 +379,8 @@ def main():
         "step_hbm_gbps": step_bytes / (ms * 1e-3) / 1e9,
         "step_frac_of_peak": step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "roofline": {"bound": "hbm", "achieved": gbps[dom], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": gbps[dom] / PEAK_HBM_GBPS, "traffic": None, "kernel": dom,
+                     "frac": gbps[dom] / PEAK_HBM_GBPS,
+                     "traffic": measured_traffic(w.name).get(dom + "_mfma"), "kernel": dom,
                      "bytes_per_launch": kb[dom], "avg_launch_ms": kt[dom],
                      "kernels": {k: {"bytes_per_launch": kb[k], "avg_launch_ms": kt[k],
                                      "median_launch_ms": kt[k + "_median"], "achieved_gbps": gbps[k]}

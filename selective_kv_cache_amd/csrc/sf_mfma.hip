@@ -165,6 +165,21 @@ __device__ inline uint32_t lds_addr(const void* l) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)l;
 }
 
+// Wait until at most `ahead` stages of PER direct loads each are still in
+// flight (a wave's vector loads complete in order).  `ahead` is wave-uniform
+// and at most 3.
+template <int PER>
+__device__ inline void wait_stages(int ahead) {
+  if (ahead >= 3)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * PER) : "memory");
+  else if (ahead == 2)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PER) : "memory");
+  else if (ahead == 1)
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER) : "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 __device__ inline void lds_add_u32(uint32_t a, uint32_t v) {
   asm volatile("ds_add_u32 %0, %1" ::"v"(a), "v"(v) : "memory");
 }
@@ -221,10 +236,10 @@ __global__ void __launch_bounds__(256) score_mfma(DecodeParams p) {
   const int nsp = (int)(hi - lo);
   const int nchunks = (nsp + 31) / 32;
   const int nmine = nchunks > wid ? (nchunks - wid + 3) / 4 : 0;
-  // stage i <- chunk wid + 4i (tokens past the split read its last token;
-  // issues past the wave's last chunk repeat it)
+  // stage i <- chunk wid + 4i of the wave's own chunks (tokens past the
+  // split read its last token)
   auto issue = [&](int i) {
-    const int c = wid + 4 * i < nchunks ? wid + 4 * i : nchunks - 1;
+    const int c = wid + 4 * i;
     int rel = 32 * c + (lane >> 1);
     rel = rel < nsp ? rel : nsp - 1;
     SStage& st = ring[wid][i % kSRing];
@@ -234,7 +249,8 @@ __global__ void __launch_bounds__(256) score_mfma(DecodeParams p) {
   const bool hist = p.top_t > 0;   // no selection, no histogram
   for (int i = tid; i < kHistBins; i += 256) lhist[i] = 0u;
 #pragma unroll
-  for (int i = 0; i < kSRing - 1; ++i) issue(i);
+  for (int i = 0; i < kSRing - 1; ++i)
+    if (i < nmine) issue(i);
   v4i a0, a1;
   prep_query<G>(p.q + ((int64_t)seq * p.hq + kvh * G) * kHeadDim, qp, a0, a1);
   const int t = lane & 15, hl = lane >> 4;
@@ -247,8 +263,8 @@ __global__ void __launch_bounds__(256) score_mfma(DecodeParams p) {
   const int hx = hl >> 1;                         // after the reduction: tile of this lane
   const uint32_t hist0 = lds_addr(&lhist[0]);
   for (int i = 0; i < nmine; ++i) {
-    issue(i + kSRing - 1);
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSRingLoads * (kSRing - 1)) : "memory");
+    if (i + kSRing - 1 < nmine) issue(i + kSRing - 1);
+    wait_stages<kSRingLoads>(min(kSRing - 1, nmine - 1 - i));
     const int c = wid + 4 * i;
     const uint32_t sb = ring0 + (uint32_t)(i % kSRing) * (uint32_t)sizeof(SStage);
     uint64_t kw[2], ks[2];
@@ -376,13 +392,13 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   // of the chunk (token L/2), lanes L < 8G the logits' bytes [16L, 16L+16),
   // and half L&1 of V row (L/2) ^ ((L/8) & 3): row r of the chunk sits at
   // stage row r ^ ((r/4) & 3), so that the four rows one P.V read takes
-  // (4rg + v, rg = 0..3) fall in different LDS banks.  Tokens past the
-  // split's end read its last token's V row (logits: the buffer has a chunk
-  // of slack), and loads past the wave's last chunk repeat the last chunk, so
-  // every issue is three in-bounds loads.
+  // (4rg + v, rg = 0..3) fall in different LDS banks.  Only the wave's own
+  // chunks are issued; tokens past the split's end read its last token's V
+  // row (logits: the buffer has a chunk of slack), so every load is in
+  // bounds.
   const int vrow = (lane >> 1) ^ ((lane >> 3) & 3);
   auto issue = [&](int i) {
-    const int c = wid + 4 * i < nchunks ? wid + 4 * i : nchunks - 1;
+    const int c = wid + 4 * i;
     int rel = 32 * c + (lane >> 1);
     rel = rel < nsp ? rel : nsp - 1;
     int relv = 32 * c + vrow;
@@ -393,13 +409,15 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
     dma4(vscg + (uint32_t)rel * 2u + (uint32_t)(lane & 1), st.vs);
   };
 #pragma unroll
-  for (int i = 0; i < kRing - 1; ++i) issue(i);
+  for (int i = 0; i < kRing - 1; ++i)
+    if (i < nmine) issue(i);
 
   for (int i = lane; i < 2 * 16 * 32; i += 64) (&s.wt[wid][0][0][0])[i] = (_Float16)0.f;
   // selection words of the split (one per chunk) in two registers: lane L
   // holds those of chunks L and 64 + L; splits start on a word boundary
   constexpr int kMaxSplitWords = 4096 / 32;
   static_assert(kMaxSplitWords <= 128, "two words per lane");
+  static_assert(kRing <= 4, "wait_stages covers up to 3 stages ahead");
   const uint32_t* bmw = p.bitmap + sk * p.bm_words + (lo >> 5);
   const uint32_t sw0 = masked && lane < nchunks ? bmw[lane] : 0u;
   const uint32_t sw1 = masked && 64 + lane < nchunks ? bmw[64 + lane] : 0u;
@@ -433,9 +451,10 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
   for (int i = 0; i < nmine; ++i) {
-    issue(i + kRing - 1);
-    // this wave's loads complete in order: all but the newest kRing - 1 stages
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kRingLoads * (kRing - 1)) : "memory");
+    if (i + kRing - 1 < nmine) issue(i + kRing - 1);
+    // this wave's loads complete in order: stage i is in once no more than
+    // the stages issued after it are outstanding
+    wait_stages<kRingLoads>(min(kRing - 1, nmine - 1 - i));
     const int c = wid + 4 * i;
     const uint32_t sb = ring0 + (uint32_t)(i % kRing) * (uint32_t)sizeof(St);
     const int rem = nsp - 32 * c;                 // tokens of this chunk inside the split
