@@ -36,10 +36,9 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 constexpr float kInv254 = 1.0f / 254.0f;
 
-// Element (within a lane group's 32) carried by byte j of the B operand of
-// logit MFMA i, for 2-bit codes: byte j = (dword >> 2*(j/4)) byte (j%4).
-__device__ inline int kdim2(int i, int j) { return 16 * i + (j >> 2) + 4 * (j & 3); }
-
+// 2-bit codes to the int8 B operands of the two logit MFMAs: byte b of
+// dword v of operand i carries element 16i + v + 4b of the lane group's 32
+// ((dword >> 2v) & 0x03030303 spreads four codes into four bytes).
 __device__ inline void decode_b2(uint32_t w0, uint32_t w1, v4i& b0, v4i& b1) {
   b0 = v4i{(int)(w0 & 0x03030303u), (int)((w0 >> 2) & 0x03030303u), (int)((w0 >> 4) & 0x03030303u),
            (int)((w0 >> 6) & 0x03030303u)};
@@ -47,64 +46,60 @@ __device__ inline void decode_b2(uint32_t w0, uint32_t w1, v4i& b0, v4i& b1) {
            (int)((w1 >> 6) & 0x03030303u)};
 }
 
-// Query digits and per-head constants, shared by both kernels.
-template <int G>
+// Query digits and per-head constants of the score pass.  The digits are
+// stored in A-operand order: op[h][k][g] holds the 32 bytes lane group g of
+// row (h, k) feeds its two MFMAs (operand i, dword v, byte b = element
+// 32g + 16i + v + 4b, matching decode_b2's element order).
 struct QPrep {
-  int8_t dig[4][4][kHeadDim];   // [head][digit][element]
-  float scale[4];               // s_h
-  float sumq[4];                // sum(q_h)
+  alignas(16) int8_t op[4][4][4][32];   // [head][digit][lane group][byte]
+  float scale[4];                        // s_h
+  float sumq[4];                         // sum(q_h)
 };
 
-// Work-group prologue: wave h < G turns query head h into digits.  Then each
-// lane builds its two A operands (row = 4*head + digit, 16 bytes = elements of
-// lane group l/16).
+// The query elements wave h < G turns into digits: elements 2*lane, 2*lane+1
+// of head h.  Loaded before anything else of the work-group so that their
+// latency overlaps the stream's first loads.
 template <int G>
-__device__ inline void prep_query(const float* q, QPrep<G>& qp, v4i& a0, v4i& a1) {
+__device__ inline float2 load_query(const float* q) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  if (wid < G) return *reinterpret_cast<const float2*>(q + wid * kHeadDim + 2 * lane);
+  return make_float2(0.f, 0.f);
+}
+
+// Work-group prologue: wave h < G turns query head h into 4 base-254 int8
+// digits, q = s * (d0 + d1/254 + d2/254^2 + d3/254^3), s = max|q|/127.  Then
+// each lane reads its two A operands (row = 4*head + digit, 16 bytes each of
+// lane group l/16) with two 16-byte LDS reads.
+template <int G>
+__device__ inline void prep_query(float2 x, QPrep& qp, v4i& a0, v4i& a1) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  if (wid < G) {
-    const float x0 = q[wid * kHeadDim + 2 * lane], x1 = q[wid * kHeadDim + 2 * lane + 1];
-    const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
-    const float sum = wave_sum(x0 + x1);
+  if (wid < 4) {
+    const float amax = wave_max(fmaxf(fabsf(x.x), fabsf(x.y)));
+    const float sum = wave_sum(x.x + x.y);
     const float sc = amax > 0.f ? amax / 127.0f : 1.0f;
-    const float xs[2] = {x0 / sc, x1 / sc};
+    const float xs[2] = {x.x / sc, x.y / sc};
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      float r = xs[e];
-      int8_t dg[4];
+      const int d = 2 * lane + e, g = d >> 5, r = d & 31;
+      const int pos = 16 * (r >> 4) + 4 * (r & 3) + ((r & 15) >> 2);
+      float rr = xs[e];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float d = fminf(fmaxf(rintf(r), -127.f), 127.f);
-        dg[k] = (int8_t)d;
-        r = (r - d) * 254.0f;
+        const float dg = fminf(fmaxf(rintf(rr), -127.f), 127.f);
+        qp.op[wid][k][g][pos] = wid < G ? (int8_t)dg : (int8_t)0;
+        rr = (rr - dg) * 254.0f;
       }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) qp.dig[wid][k][2 * lane + e] = dg[k];
     }
     if (lane == 0) {
-      qp.scale[wid] = sc;
-      qp.sumq[wid] = sum;
+      qp.scale[wid] = wid < G ? sc : 1.0f;
+      qp.sumq[wid] = wid < G ? sum : 0.f;
     }
   }
   __syncthreads();
-  const int m = lane & 15, h = m >> 2, k = m & 3, g = lane >> 4;
-  uint32_t w[8];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int j = 4 * v + b;
-        const int dim = 32 * g + kdim2(i, j);
-        const uint32_t byte = h < G ? (uint32_t)(uint8_t)qp.dig[h][k][dim] : 0u;
-        word |= byte << (8 * b);
-      }
-      w[4 * i + v] = word;
-    }
-  }
-  a0 = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-  a1 = v4i{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+  const int m = lane & 15, g = lane >> 4;
+  const v4i* src = reinterpret_cast<const v4i*>(&qp.op[m >> 2][m & 3][g][0]);
+  a0 = src[0];
+  a1 = src[1];
 }
 
 // Logit of (head l/16, token l%16) from the digit sums; -inf for heads >= G.
@@ -221,7 +216,7 @@ struct SStage {
 
 template <int G>
 __global__ void __launch_bounds__(256) score_mfma(DecodeParams p) {
-  __shared__ QPrep<G> qp;
+  __shared__ QPrep qp;
   __shared__ uint32_t lhist[kHistBins];
   __shared__ SStage ring[4][kSRing];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -229,6 +224,7 @@ __global__ void __launch_bounds__(256) score_mfma(DecodeParams p) {
   int64_t lo, hi;
   int first;
   const int seq = locate_unit(p.seq_off, p.batch, p.score_split, blockIdx.x, false, 0, lo, hi, first);
+  const float2 qx = load_query<G>(p.q + ((int64_t)seq * p.hq + kvh * G) * kHeadDim);
   const int64_t a = p.seq_off[seq];
   const int64_t t0 = (int64_t)kvh * p.cap + a + lo;            // first token row of the split
   const uint8_t* kbase = p.kc + t0 * 32;
@@ -252,7 +248,7 @@ __global__ void __launch_bounds__(256) score_mfma(DecodeParams p) {
   for (int i = 0; i < kSRing - 1; ++i)
     if (i < nmine) issue(i);
   v4i a0, a1;
-  prep_query<G>(p.q + ((int64_t)seq * p.hq + kvh * G) * kHeadDim, qp, a0, a1);
+  prep_query<G>(qx, qp, a0, a1);
   const int t = lane & 15, hl = lane >> 4;
   const float scale = qp.scale[hl < G ? hl : 0], sumq = qp.sumq[hl < G ? hl : 0];
   float* scores = p.scores + (int64_t)kvh * p.ntot + (a - p.off0) + lo;
