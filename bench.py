@@ -203,14 +203,15 @@ KERNELS = ("score", "scan", "resolve", "attend", "combine")
 
 
 def time_kernels(model, steps):
-    """Average duration of each kernel of the step, from HIP events on the
-    decode stream: every kernel launch completes an event attached to its own
-    dispatch (created without the system-scope fence, so no cache write-back
-    is added after it), and a kernel's duration is the difference between its
-    event and the one of the kernel launched just before it."""
+    """Average duration of each kernel of the step, from a pair of HIP events
+    around every launch: the start event is recorded just before the kernel's
+    dispatch, the stop event completes with it (both created without the
+    system-scope fence, so no cache write-back is added), and
+    elapsed(start, stop) is the kernel's time as it ran inside the step."""
     import torch
     from selective_kv_cache_amd.binding import TimingEvent
-    evs = [[tuple(TimingEvent() for _ in KERNELS) for _ in range(model.L)] for _ in range(steps)]
+    evs = [[tuple((TimingEvent(), TimingEvent()) for _ in KERNELS) for _ in range(model.L)]
+           for _ in range(steps)]
     torch.cuda.synchronize()
     # hold the stream with a spin kernel while the host queues every timed
     # launch, so that the kernels run back to back instead of waiting on the
@@ -219,17 +220,13 @@ def time_kernels(model, steps):
     for s in range(steps):
         model.step(events=evs[s])
     torch.cuda.synchronize()
-    flat = [quint for row in evs for quint in row]
     dur = {k: [] for k in KERNELS}
-    for i, ev in enumerate(flat):
-        prev = flat[i - 1][4] if i else None          # combine of the layer before
-        for j, k in enumerate(KERNELS):
-            before = ev[j - 1] if j else prev
-            if before is not None:
-                dur[k].append(before.elapsed_ms(ev[j]))
-    for quint in flat:
-        for e in quint:
-            e.close()
+    for row in evs:
+        for quint in row:
+            for k, (e0, e1) in zip(KERNELS, quint):
+                dur[k].append(e0.elapsed_ms(e1))
+                e0.close()
+                e1.close()
     out = {}
     for k in KERNELS:
         out[k] = float(np.mean(dur[k]))
@@ -350,18 +347,6 @@ def main():
     kt = time_kernels(model, max(2, args.steps // 4))
     model.close()
     del model
-    # Each event-timed launch waits on its predecessor's event, which costs
-    # the same fixed dispatch gap per kernel; the graph replay runs the same
-    # kernels back to back without events.  The gap is therefore the per-kernel
-    # share of (sum of event-timed kernels per layer - graph step per layer),
-    # and each kernel's duration is its event time less that gap.
-    raw_layer = sum(kt[k] for k in KERNELS)
-    gap = max(0.0, (raw_layer - ms / w.layers) / len(KERNELS)) if launch == "hip_graph" else 0.0
-    kt_raw = {k: kt[k] for k in KERNELS}
-    for k in KERNELS:
-        kt[k] -= gap
-        kt[k + "_median"] -= gap
-
     step_bytes = algorithmic_bytes(w, w.seq_lengths()) * w.layers
     kb = kernel_bytes(w, w.seq_lengths())
     dom = max(kb, key=lambda k: kt[k])
@@ -386,9 +371,7 @@ def main():
                                      "median_launch_ms": kt[k + "_median"], "achieved_gbps": gbps[k]}
                                  for k in kb},
                      "other_kernels_avg_ms": {k: kt[k] for k in KERNELS if k not in kb},
-                     "event_timing": {"raw_avg_ms": kt_raw, "dispatch_gap_ms": gap,
-                                      "note": "avg_launch_ms = event-timed duration less the per-kernel "
-                                              "dispatch gap, both from HIP events in this run"}},
+                     "event_timing": "start/stop HIP event pair around each launch, in this run"},
     }
     if not args.no_secondary:
         sec = {}

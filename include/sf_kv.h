@@ -180,13 +180,14 @@ typedef struct sf_decode_args {
   void* workspace;               /* device scratch of sf_decode_workspace_size() bytes  */
   size_t workspace_bytes;
   int32_t flags;                 /* 0 or SF_DECODE_HIST_CLEAN                           */
-  void* events[5];               /* optional hipEvent_t (NULL = none), each completed with
-                                    one kernel of the step, in launch order: [0] score,
-                                    [1] selection scan, [2] selection resolve, [3]
-                                    attention, [4] combine.  The selection events are
-                                    not recorded when T == 0.  The difference of two
-                                    consecutive ones is the time of the kernel between
-                                    them (create them without the system-scope fence).  */
+  void* start_events[5];         /* optional hipEvent_t pairs (NULL = none) that time the */
+  void* events[5];               /* step's kernels: start_events[k] is recorded just
+                                    before kernel k is dispatched, events[k] completes
+                                    with it: [0] score, [1] selection scan, [2] selection
+                                    resolve, [3] attention, [4] combine.  The selection
+                                    pair is not recorded when T == 0.  elapsed(start,
+                                    stop) is the kernel's time (create both without the
+                                    system-scope fence).                                */
 } sf_decode_args;
 
 /* Scratch needed by sf_decode_step for this batch shape.
@@ -217,6 +218,7 @@ sf_status sf_decode_workspace_size(const sf_geom* geom, int32_t batch, int64_t t
  * undefined after the call.
  */
 sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* args, void* stream);
+
 
 #ifdef __cplusplus
 }

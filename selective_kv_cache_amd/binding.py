@@ -46,7 +46,7 @@ class sf_decode_args(ctypes.Structure):
                 ("v_scales", c_vp), ("cap", c_i64), ("store", c_vp), ("top_t", c_i32), ("out", c_vp),
                 ("sel_out", c_vp), ("scores_out", c_vp), ("stats", ctypes.POINTER(sf_step_stats)),
                 ("workspace", c_vp), ("workspace_bytes", c_size), ("flags", c_i32),
-                ("events", c_vp * 5)]
+                ("start_events", c_vp * 5), ("events", c_vp * 5)]
 
 
 class SfError(RuntimeError):
@@ -209,9 +209,15 @@ def sf_decode_step(g: sf_geom, *, seq_off_host: Sequence[int], seq_off_dev, q, k
     a.workspace = _ptr(workspace)
     a.workspace_bytes = workspace.numel() * workspace.element_size()
     a.flags = flags
-    if events is not None:       # completed with score, scan, resolve, attention, combine; None allowed
+    if events is not None:
+        # (start, stop) pairs of score, scan, resolve, attention, combine; a
+        # stop alone, or None, allowed
+        h = lambda e: None if e is None else (e.handle if hasattr(e, "handle") else
+                                              e.cuda_event if hasattr(e, "cuda_event") else e)
         for i, e in enumerate(events):
-            a.events[i] = None if e is None else (e.handle if hasattr(e, "handle") else
-                                                  e.cuda_event if hasattr(e, "cuda_event") else e)
+            if isinstance(e, tuple):
+                a.start_events[i], a.events[i] = h(e[0]), h(e[1])
+            else:
+                a.events[i] = h(e)
     _check(load().sf_decode_step(ctypes.byref(g), ctypes.byref(a), _stream(stream)), "sf_decode_step")
     return st.as_dict() if want_stats else None

@@ -9,24 +9,24 @@
 // subdivide the bin the base code names.
 //
 // Kernel sequence on the caller's stream (one layer):
-//   zero_words     clear the score-key histogram
+//   zero_words     clear the score-key histogram (unless the caller vouches
+//                  that the last step left it zero)
 //   score          read the base K codes of every token: token score (max over
 //                  the GQA group of the scaled logit) and a histogram of the
 //                  scores' order-preserving keys
 //   select_scan,   per (sequence, KV head): the exact top-T (score desc,
 //   select_resolve token asc) as a bitmap and an ascending list
 //   [host-pinned store only: cache lookup, fetch of the misses, install]
-//   attend         read base K and V codes again (the per-layer K working set
-//                  fits the MI355X Infinity Cache, so the second read is
-//                  served on-chip) and run split-K online-softmax attention
-//                  with every selected row refined
+//   attend         read the per-head logits the score pass kept and the V
+//                  codes, and run split-K online-softmax attention with every
+//                  selected row refined
 //   combine        merge the split partials of each query head
 //
-// Refinement depends on the selection, and the selection on all scores
-// ("KV refinement adds a step that cannot overlap the surrounding attention",
-// same page, paragraph "Where it earns its keep"), so attention runs after
-// the selection; each token then enters the softmax once, with its final
-// logit and value.
+// Refinement depends on the selection, and the selection on all scores (the
+// same page, paragraph "Where it earns its keep", notes that the refinement
+// step cannot be overlapped with the attention around it), so attention runs
+// after the selection; each token then enters the softmax once, with its
+// final logit and value.
 #include <math.h>
 #include <string.h>
 
@@ -220,7 +220,7 @@ extern "C" sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* a
                        reinterpret_cast<uint32_t*>(ws + c.hist), nzero);
     SF_LAUNCH_CHECK("zero_words");
   }
-  const auto stop = [&](int i) { return KernelEvents{nullptr, (hipEvent_t)a->events[i]}; };
+  const auto stop = [&](int i) { return KernelEvents{(hipEvent_t)a->start_events[i], (hipEvent_t)a->events[i]}; };
   if (!launch_score(p, dim3(n_score, p.hkv), hs, stop(0)))
     return SF_ERR_UNSUPPORTED;
   SF_LAUNCH_CHECK("score");

@@ -25,6 +25,8 @@
 #include <math.h>
 #include <stddef.h>
 
+#include <type_traits>
+
 #include "sf_attend_common.h"
 
 namespace sfk {
@@ -249,8 +251,12 @@ __global__ void __launch_bounds__(256) score_mfma(DecodeParams p) {
     if (i < nmine) issue(i);
   v4i a0, a1;
   prep_query<G>(qx, qp, a0, a1);
+  // logits in log2 units (1/sqrt(D) and log2(e) folded into the per-head
+  // constants): the attention pass's softmax takes them as they are
+  constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
   const int t = lane & 15, hl = lane >> 4;
-  const float scale = qp.scale[hl < G ? hl : 0], sumq = qp.sumq[hl < G ? hl : 0];
+  const float scale = qp.scale[hl < G ? hl : 0] * (kRsqrtD * kLog2e);
+  const float sumq = qp.sumq[hl < G ? hl : 0] * (kRsqrtD * kLog2e);
   float* scores = p.scores + (int64_t)kvh * p.ntot + (a - p.off0) + lo;
   float* lgo = p.logits + ((int64_t)kvh * p.ntot + (a - p.off0) + lo) * G;
   const uint32_t ring0 = lds_addr(&ring[wid][0]);
@@ -281,9 +287,10 @@ __global__ void __launch_bounds__(256) score_mfma(DecodeParams p) {
       decode_b2(w.x, w.y, b0, b1);
       v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, v4i{0, 0, 0, 0}, 0, 0, 0);
       D = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, D, 0, 0, 0);
-      lg[k] = logit_from<G>(D, __builtin_bit_cast(float2, ks[k]), scale, sumq, hl);
+      const float x = logit_scaled(D, __builtin_bit_cast(float2, ks[k]), scale, sumq);
+      lg[k] = hl < G ? x : -INFINITY;
       const int rel = 32 * c + 16 * k + t;
-      if (hl < G && rel < nsp) lgo[rel * G + hl] = lg[k];   // kept for the attention pass
+      if (hl < G && rel < nsp) lgo[rel * G + hl] = x;   // kept for the attention pass
     }
     // maximum over the heads, two tiles at once: after the first exchange a
     // lane keeps tile hl/2 over heads {hl, hl^2}, after the second over all
@@ -292,11 +299,13 @@ __global__ void __launch_bounds__(256) score_mfma(DecodeParams p) {
     y = fmaxf(y, __shfl_xor(y, 16));
     const int rel = 32 * c + 16 * hx + t;
     if ((hl & 1) == 0 && rel < nsp) {
+      y *= kLn2;                                  // the score in natural units
       scores[rel] = y;
       if (hist) lds_add_u32(hist0 + 4u * (score_key(y) >> (32 - kHistBits)), 1u);
     }
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // the histogram adds (asm, not waited for) complete before the barrier
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   if (!hist) return;
   __syncthreads();
   uint32_t* gh = p.hist + ((int64_t)seq * p.hkv + kvh) * kHistBins;   // level-1 histogram
@@ -324,43 +333,89 @@ struct Stage {
 
 template <int G>
 struct MfmaLds {
-  alignas(16) _Float16 wt[4][2][16][32];   // per wave: P.V weights, hi and lo parts [column][kappa]
+  alignas(16) _Float16 wt[4][2 * G][32];   // per wave: P.V weights [column][kappa]: hi parts, then lo parts
+  alignas(16) _Float16 wzero[8];           // weight columns >= 2G read zeros
   float mw[4][G], lw[4][G];
   union {
     Stage<G> ring[4][kRing];
-    float accw[4][G + 1][kHeadDim];        // after the stream: per-wave P.V totals (row G: unused lanes)
+    float accw[4][2 * G][kHeadDim];        // after the stream: per-wave P.V, hi and lo columns
   } u;
 };
+
+// Maximum over the 16 lanes of a row: four DPP row rotations, each folded
+// into its v_max (s_nop 1 covers the VALU-write to DPP-read hazard).
+__device__ inline float row16_max_dpp(float x) {
+  float y;
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %1, %1 row_ror:8 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_ror:4 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_ror:2 row_mask:0xf bank_mask:0xf\n\t"
+      "s_nop 1\n\t"
+      "v_max_f32_dpp %0, %0, %0 row_ror:1 row_mask:0xf bank_mask:0xf"
+      : "=&v"(y)
+      : "v"(x));
+  return y;
+}
+
+// Buffer loads straight to LDS: a raw buffer resource (base, byte range) in
+// SGPRs, a per-lane byte offset that stays fixed and a wave-uniform one that
+// walks the chunks, so issuing a stage costs no vector instructions.  Reads
+// past the range return zeros (the hardware's range check), which is how the
+// split's last chunk stays inside the split.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ inline void bdma16(rsrc_t r, uint32_t voff, uint32_t soff, void* l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t)l, 16, voff, soff, 0, 0);
+}
+__device__ inline void bdma4(rsrc_t r, uint32_t voff, uint32_t soff, void* l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t)l, 4, voff, soff, 0, 0);
+}
+
+// v_cndmask with a wave-uniform 64-bit lane mask (SGPR pair): lane l takes
+// yes where bit l of mask is set, else no.
+__device__ inline float lane_select(uint64_t mask, float yes, float no) {
+  float r;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(no), "v"(yes), "s"(mask));
+  return r;
+}
 
 // One lane's operands of a stage.  The LDS reads are written in asm: a read
 // the compiler sees makes it wait for every direct load in flight (it cannot
 // tell the ring stages apart), which would serialise the stream.  The block
-// waits for its own reads before it ends, so every output is complete.
+// waits for its own reads before it ends, so every output is complete.  OFF
+// is the stage's byte offset in the wave's ring (an immediate of each read).
 struct StageRegs {
   float lg[2];             // logits of tokens t, 16 + t for head hl
   uint64_t vsc[2];         // (lo, delta) of tokens t, 16 + t
   uint32_t vw[8];          // V dword vdw of tokens 4rg+v (vw[2v]) and 16+4rg+v (vw[2v+1])
 };
 
-template <int G>
+template <int G, int OFF>
 __device__ inline void read_stage(uint32_t aL, uint32_t aS, const uint32_t (&aV)[4], StageRegs& r) {
   asm volatile(
-      "ds_read_b32 %0, %12\n\t"
-      "ds_read_b32 %1, %12 offset:%18\n\t"
-      "ds_read_b64 %2, %13\n\t"
-      "ds_read_b64 %3, %13 offset:128\n\t"
-      "ds_read_b32 %4, %14\n\t"
-      "ds_read_b32 %5, %14 offset:512\n\t"
-      "ds_read_b32 %6, %15\n\t"
-      "ds_read_b32 %7, %15 offset:512\n\t"
-      "ds_read_b32 %8, %16\n\t"
-      "ds_read_b32 %9, %16 offset:512\n\t"
-      "ds_read_b32 %10, %17\n\t"
-      "ds_read_b32 %11, %17 offset:512\n\t"
+      "ds_read_b32 %0, %12 offset:%18\n\t"
+      "ds_read_b32 %1, %12 offset:%19\n\t"
+      "ds_read_b64 %2, %13 offset:%18\n\t"
+      "ds_read_b64 %3, %13 offset:%20\n\t"
+      "ds_read_b32 %4, %14 offset:%18\n\t"
+      "ds_read_b32 %5, %14 offset:%21\n\t"
+      "ds_read_b32 %6, %15 offset:%18\n\t"
+      "ds_read_b32 %7, %15 offset:%21\n\t"
+      "ds_read_b32 %8, %16 offset:%18\n\t"
+      "ds_read_b32 %9, %16 offset:%21\n\t"
+      "ds_read_b32 %10, %17 offset:%18\n\t"
+      "ds_read_b32 %11, %17 offset:%21\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(r.lg[0]), "=&v"(r.lg[1]), "=&v"(r.vsc[0]), "=&v"(r.vsc[1]), "=&v"(r.vw[0]), "=&v"(r.vw[1]),
         "=&v"(r.vw[2]), "=&v"(r.vw[3]), "=&v"(r.vw[4]), "=&v"(r.vw[5]), "=&v"(r.vw[6]), "=&v"(r.vw[7])
-      : "v"(aL), "v"(aS), "v"(aV[0]), "v"(aV[1]), "v"(aV[2]), "v"(aV[3]), "n"(16 * G * 4)
+      : "v"(aL), "v"(aS), "v"(aV[0]), "v"(aV[1]), "v"(aV[2]), "v"(aV[3]), "n"(OFF), "n"(OFF + 16 * G * 4),
+        "n"(OFF + 128), "n"(OFF + 512)
       : "memory");
 }
 
@@ -369,7 +424,8 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   using Lds = MfmaLds<G>;
   using St = Stage<G>;
   Lds& s = *reinterpret_cast<Lds*>(smem);
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   int64_t lo, hi;
   int first;
   const int seq = locate_unit(p.seq_off, p.batch, p.split, split, false, 0, lo, hi, first);
@@ -377,9 +433,6 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   const int64_t sk = (int64_t)seq * p.hkv + kvh;
   const bool masked = p.use_refine != 0;
   const int64_t t0 = (int64_t)kvh * p.cap + a + lo;            // first token row of the split
-  const uint8_t* vbase = p.vc + t0 * 32;
-  const float* vscg = p.vs + t0 * 2;
-  const uint8_t* lbase = reinterpret_cast<const uint8_t*>(p.logits + ((int64_t)kvh * p.ntot + (a - p.off0) + lo) * G);
   const int nsp = (int)(hi - lo);                               // tokens of the split (<= 4096)
   const int nchunks = (nsp + 31) / 32;
   const int nmine = nchunks > wid ? (nchunks - wid + 3) / 4 : 0;   // chunks wid, wid+4, ...
@@ -388,32 +441,30 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   // of the chunk (token L/2), lanes L < 8G the logits' bytes [16L, 16L+16),
   // and half L&1 of V row (L/2) ^ ((L/8) & 3): row r of the chunk sits at
   // stage row r ^ ((r/4) & 3), so that the four rows one P.V read takes
-  // (4rg + v, rg = 0..3) fall in different LDS banks.  Only the wave's own
-  // chunks are issued; tokens past the split's end read its last token's V
-  // row (logits: the buffer has a chunk of slack), so every load is in
-  // bounds.
-  const int vrow = (lane >> 1) ^ ((lane >> 3) & 3);
-  auto issue = [&](int i) {
-    const int c = wid + 4 * i;
-    int rel = 32 * c + (lane >> 1);
-    rel = rel < nsp ? rel : nsp - 1;
-    int relv = 32 * c + vrow;
-    relv = relv < nsp ? relv : nsp - 1;
-    St& st = s.u.ring[wid][i % kRing];
-    if (lane < 8 * G) dma16(lbase + (uint32_t)c * (32u * G * 4u) + 16u * (uint32_t)lane, st.lg);
-    dma16(vbase + (uint32_t)relv * 32u + 16u * (uint32_t)(lane & 1), st.v);
-    dma4(vscg + (uint32_t)rel * 2u + (uint32_t)(lane & 1), st.vs);
+  // (4rg + v, rg = 0..3) fall in different LDS banks.  The resources end at
+  // the split's end: tokens past it read as zeros.
+  const rsrc_t rV = make_rsrc(p.vc + t0 * 32, (uint32_t)nsp * 32u);
+  const rsrc_t rS = make_rsrc(p.vs + t0 * 2, (uint32_t)nsp * 8u);
+  const rsrc_t rL = make_rsrc(p.logits + ((int64_t)kvh * p.ntot + (a - p.off0) + lo) * G, (uint32_t)nsp * G * 4u);
+  const uint32_t oV = (uint32_t)(((lane >> 1) ^ ((lane >> 3) & 3)) * 32 + 16 * (lane & 1));
+  const uint32_t oS = 4u * (uint32_t)lane, oL = 16u * (uint32_t)lane;
+  auto issue = [&](int i, St& st) {
+    const uint32_t c = (uint32_t)(wid + 4 * i);
+    if (lane < 8 * G) bdma16(rL, oL, c * (32u * G * 4u), st.lg);
+    bdma16(rV, oV, c * 1024u, st.v);
+    bdma4(rS, oS, c * 256u, st.vs);
   };
-#pragma unroll
-  for (int i = 0; i < kRing - 1; ++i)
-    if (i < nmine) issue(i);
+  static_assert(kRing == 4, "the stream loop is unrolled by the ring depth");
+  if (0 < nmine) issue(0, s.u.ring[wid][0]);
+  if (1 < nmine) issue(1, s.u.ring[wid][1]);
+  if (2 < nmine) issue(2, s.u.ring[wid][2]);
 
-  for (int i = lane; i < 2 * 16 * 32; i += 64) (&s.wt[wid][0][0][0])[i] = (_Float16)0.f;
+  for (int i = lane; i < 2 * G * 32; i += 64) (&s.wt[wid][0][0])[i] = (_Float16)0.f;
+  if (tid < 8) s.wzero[tid] = (_Float16)0.f;
   // selection words of the split (one per chunk) in two registers: lane L
   // holds those of chunks L and 64 + L; splits start on a word boundary
   constexpr int kMaxSplitWords = 4096 / 32;
   static_assert(kMaxSplitWords <= 128, "two words per lane");
-  static_assert(kRing <= 4, "wait_stages covers up to 3 stages ahead");
   const uint32_t* bmw = p.bitmap + sk * p.bm_words + (lo >> 5);
   const uint32_t sw0 = masked && lane < nchunks ? bmw[lane] : 0u;
   const uint32_t sw1 = masked && 64 + lane < nchunks ? bmw[64 + lane] : 0u;
@@ -421,66 +472,83 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   const int t = lane & 15, hl = lane >> 4;        // logit layout: token t (and 16 + t), head hl
   const int n = lane & 15, rg = lane >> 4;        // P.V layout: column n, k-group rg
   const int hlc = hl < G ? hl : 0;
-  constexpr float kLog2e = 1.4426950408889634f;   // softmax in log2 units
   // v_perm_b32 selector: half (n & 1) of each of two dwords
   const uint32_t hsel = 2u * (uint32_t)(n & 1);
   const uint32_t psel = hsel | ((hsel + 1u) << 8) | ((hsel + 4u) << 16) | ((hsel + 5u) << 24);
   const int vdw = n >> 1;                         // dword of the V row holding elements 8n..8n+7
 
-  // LDS addresses of this lane's stage operands.  P.V k index kappa = 2u + j
-  // stands for token 16j + u, so lane (n, rg) takes tokens 4rg..4rg+3 and
-  // 16+4rg..16+4rg+3, and a logit lane's two weights are adjacent.
+  // LDS addresses of this lane's stage operands (stage 0; the stage's offset
+  // is an immediate of each read).  P.V k index kappa = 2u + j stands for
+  // token 16j + u, so lane (n, rg) takes tokens 4rg..4rg+3 and
+  // 16+4rg..16+4rg+3, and a logit lane's two weights are adjacent.  Weight
+  // column h < G holds head h's hi parts, column G + h its lo parts, so one
+  // product per tile takes both.
   const uint32_t ring0 = lds_addr(&s.u.ring[wid][0]);
-  const uint32_t wt0 = lds_addr(&s.wt[wid][0][n][8 * rg]);
-  const uint32_t wts = lds_addr(&s.wt[wid][0][hlc][2 * t]);
-  static_assert(sizeof(s.wt[0][0]) == 1024, "lo part 1 KiB after the hi part");
-  const uint32_t offL = (uint32_t)(offsetof(St, lg) + 4 * (t * G + hlc));
-  const uint32_t offS = (uint32_t)(offsetof(St, vs) + 8 * t);
-  uint32_t offV[4];                               // token 4rg + v at stage row 4rg + (v ^ rg)
+  const uint32_t wtR = n < 2 * G ? lds_addr(&s.wt[wid][n][8 * rg]) : lds_addr(&s.wzero[0]);
+  const uint32_t wtHi = lds_addr(&s.wt[wid][hlc][2 * t]), wtLo = lds_addr(&s.wt[wid][G + hlc][2 * t]);
+  const uint32_t aL = ring0 + (uint32_t)(offsetof(St, lg) + 4 * (t * G + hlc));
+  const uint32_t aS = ring0 + (uint32_t)(offsetof(St, vs) + 8 * t);
+  uint32_t aV[4];                                 // token 4rg + v at stage row 4rg + (v ^ rg)
 #pragma unroll
-  for (int v = 0; v < 4; ++v) offV[v] = (uint32_t)(offsetof(St, v) + (4 * rg + (v ^ rg)) * 32 + 4 * vdw);
+  for (int v = 0; v < 4; ++v) aV[v] = ring0 + (uint32_t)(offsetof(St, v) + (4 * rg + (v ^ rg)) * 32 + 4 * vdw);
+  // rows hl < G hold heads; the others take no part
+  const uint64_t rows = G >= 4 ? ~0ull : (1ull << (16 * G)) - 1ull;
+  const float ninf = -INFINITY;
 
-  float m = -INFINITY, lsum = 0.f, t1 = 0.f;
+  // running maximum: a finite floor below every logit until a token takes
+  // part, so exp2(logit - m) is 0 (not NaN) for the -inf of tokens left out
+  constexpr float kFloor = -1e30f;
+  constexpr int kSlack = 6;                       // weights up to 2^kSlack (log2 units of the reference)
+  float m = kFloor, lsum = 0.f, t1 = 0.f;
   int sexp = 127;                                 // weight scale 2^sexp; 127 = not set yet
   float wsc = 1.0f;                               // 2^sexp once set
   v4f acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
-  for (int i = 0; i < nmine; ++i) {
-    if (i + kRing - 1 < nmine) issue(i + kRing - 1);
+
+  auto body = [&](auto kc, int i) {
+    constexpr int k = decltype(kc)::value;        // stage of chunk i
+    if (i + 3 < nmine) issue(i + 3, s.u.ring[wid][(k + 3) & 3]);
     // this wave's loads complete in order: stage i is in once no more than
     // the stages issued after it are outstanding
     wait_stages<kRingLoads>(min(kRing - 1, nmine - 1 - i));
     const int c = wid + 4 * i;
-    const uint32_t sb = ring0 + (uint32_t)(i % kRing) * (uint32_t)sizeof(St);
     const int rem = nsp - 32 * c;                 // tokens of this chunk inside the split
-    const uint32_t selw = (uint32_t)__builtin_amdgcn_readlane((int)(c < 64 ? sw0 : sw1), c & 63);
+    // the chunk's tokens that take part (unmarked, inside the split) as lane
+    // masks: bit l of mk[j] for lane l = (row, t): token 16 j + t
+    uint32_t vm = ~(uint32_t)__builtin_amdgcn_readlane((int)(c < 64 ? sw0 : sw1), c & 63);
+    if (rem < 32) vm &= (1u << rem) - 1u;
+    const uint32_t y0 = (vm & 0xFFFFu) | (vm << 16), y1 = (vm >> 16) | (vm & 0xFFFF0000u);
+    const uint64_t mk[2] = {((uint64_t)y0 | ((uint64_t)y0 << 32)) & rows, ((uint64_t)y1 | ((uint64_t)y1 << 32)) & rows};
     StageRegs R;
-    const uint32_t aV[4] = {sb + offV[0], sb + offV[1], sb + offV[2], sb + offV[3]};
-    read_stage<G>(sb + offL, sb + offS, aV, R);
+    read_stage<G, k * (int)sizeof(St)>(aL, aS, aV, R);
+    // logits (log2 units, as the score pass kept them); -inf where the token
+    // takes no part
     float lg[2];
     float2 vsc[2];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const bool ok = hl < G && 16 * k + t < rem && !((selw >> (16 * k + t)) & 1u);
-      lg[k] = ok ? R.lg[k] * kLog2e : -INFINITY;
-      vsc[k] = ok ? __builtin_bit_cast(float2, R.vsc[k]) : make_float2(0.f, 0.f);
+    for (int j = 0; j < 2; ++j) {
+      lg[j] = lane_select(mk[j], R.lg[j], ninf);
+      vsc[j] = __builtin_bit_cast(float2, R.vsc[j]);
     }
-    // online softmax: maximum over the row of 16 lanes (one head)
-    const float mnew = fmaxf(m, row16_max(fmaxf(lg[0], lg[1])));
-    // weight scale: keep delta * 2^sexp below 2^14 over the chunk; the
-    // chunk's largest delta is needed only when one reaches 2^(14 - sexp)
-    float dmax = fmaxf(vsc[0].y, vsc[1].y);
+    // online softmax with a lazy reference: m moves (and the sums are
+    // rescaled) only when a logit exceeds it by more than kSlack, so the
+    // weights stay below 2^kSlack and most chunks need no row maximum
+    const float xm = fmaxf(lg[0], lg[1]);
+    const bool grow = __ballot(xm > m + kSlack) != 0ull;
+    const float mnew = grow ? fmaxf(m, row16_max_dpp(xm)) : m;
+    // weight scale: keep delta * 2^sexp below 2^(14 - kSlack) over the
+    // chunk; the chunk's largest delta is needed only when one reaches it
+    float dmax = fmaxf(lane_select(mk[0], vsc[0].y, 0.f), lane_select(mk[1], vsc[1].y, 0.f));
     int need = sexp;
-    if (__ballot(dmax > 0.f && (sexp == 127 || dmax >= __builtin_ldexpf(1.0f, 14 - sexp))) != 0ull) {
+    if (__ballot(dmax > 0.f && (sexp == 127 || dmax >= __builtin_ldexpf(1.0f, 14 - kSlack - sexp))) != 0ull) {
       dmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max(dmax))));
       int e2;
       frexpf(dmax, &e2);
-      need = 14 - e2;       // wave-uniform, and so is sexp
+      need = 14 - kSlack - e2;   // wave-uniform, and so is sexp
     }
-    const bool grow = __ballot(mnew > m) != 0ull;
     if (grow || need < sexp) {
-      const float alpha = mnew > m ? (m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mnew)) : 1.f;
+      const float alpha = mnew > m ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;   // 0 from the floor
       lsum *= alpha;
       t1 *= alpha;
       const int hc = n < 2 * G ? n % G : 0;
@@ -498,21 +566,21 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
     }
     float wv[2];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const float pk = lg[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lg[k] - m);
+    for (int j = 0; j < 2; ++j) {
+      const float pk = __builtin_amdgcn_exp2f(lg[j] - m);   // exp2(-inf) = 0: tokens left out
       lsum += pk;
-      t1 = fmaf(pk, fmaf(0.5f, vsc[k].y, vsc[k].x), t1);
-      wv[k] = pk * (vsc[k].y * wsc);
+      t1 = fmaf(pk, fmaf(0.5f, vsc[j].y, vsc[j].x), t1);
+      wv[j] = pk * (vsc[j].y * wsc);
     }
-    // weights as fp16 hi + lo (truncated hi, exact remainder): 22 bits
+    // weights as fp16 hi + lo (truncated hi, exact remainder): 22 bits, the
+    // two parts in separate columns of one product
     const auto whi = __builtin_amdgcn_cvt_pkrtz(wv[0], wv[1]);
     const auto wlo = __builtin_amdgcn_cvt_pkrtz(wv[0] - (float)whi[0], wv[1] - (float)whi[1]);
     if (hl < G) {
-      lds_write_u32(wts, __builtin_bit_cast(uint32_t, whi));
-      lds_write_u32(wts + 1024u, __builtin_bit_cast(uint32_t, wlo));
+      lds_write_u32(wtHi, __builtin_bit_cast(uint32_t, whi));
+      lds_write_u32(wtLo, __builtin_bit_cast(uint32_t, wlo));
     }
-    v8h bhi, blo;
-    lds_read_2v8h(wt0, bhi, blo);
+    const v8h bw = lds_read_v8h(wtR);
     const uint32_t* vw = R.vw;
     uint32_t P[4], Q[4];
 #pragma unroll
@@ -522,41 +590,69 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
     }
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
-      const uint32_t mk = 0x00030003u << (2 * (tt <= 4 ? tt : tt - 5));
+      const uint32_t msk = 0x00030003u << (2 * (tt <= 4 ? tt : tt - 5));
       v4u av;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) av[v] = (tt <= 4 ? P[v] : Q[v]) & mk;
-      acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, av), bhi, acc[tt], 0, 0, 0);
-      acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, av), blo, acc[tt], 0, 0, 0);
+      for (int v = 0; v < 4; ++v) av[v] = (tt <= 4 ? P[v] : Q[v]) & msk;
+      acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, av), bw, acc[tt], 0, 0, 0);
     }
+  };
+  for (int i = 0; i < nmine; i += 4) {
+    body(std::integral_constant<int, 0>{}, i);
+    if (i + 1 < nmine) body(std::integral_constant<int, 1>{}, i + 1);
+    if (i + 2 < nmine) body(std::integral_constant<int, 2>{}, i + 2);
+    if (i + 3 < nmine) body(std::integral_constant<int, 3>{}, i + 3);
   }
   // the ring is reused below: no load of this wave may still be landing, and
   // every wave must be done with its stages
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  // wave totals: l and the scalar term per head (row sums), P.V per head
-  // (column n = head n); the maximum goes back to natural-log units
+  // wave totals: l and the scalar term per head (row sums), P.V per column
+  // (column n < G: head n's hi part, G + h: its lo part); the maximum goes
+  // back to natural-log units
   lsum = row16_sum(lsum);
   t1 = row16_sum(t1);
   if (hl < G && t == 0) {
-    s.mw[wid][hl] = m * 0.6931471805599453f;
+    s.mw[wid][hl] = m == kFloor ? -INFINITY : m * 0.6931471805599453f;   // -inf: no token took part
     s.lw[wid][hl] = lsum;
   }
-  float t1n = lane_value(t1, 0);
+  float t1n = 0.f;                                // the scalar term goes with the hi column
 #pragma unroll
-  for (int h = 1; h < G; ++h) t1n = n == h ? lane_value(t1, 16 * h) : t1n;
+  for (int h = 0; h < G; ++h) t1n = n == h ? lane_value(t1, 16 * h) : t1n;
   const int se = sexp == 127 ? 0 : sexp;
-  const int nrow = n < G ? n : G;
+  if (n < 2 * G) {
 #pragma unroll
-  for (int tt = 0; tt < 8; ++tt) {
-    const float f = __builtin_ldexpf(1.0f, 24 - 2 * (tt <= 4 ? tt : tt - 5) - se);
+    for (int tt = 0; tt < 8; ++tt) {
+      const float f = __builtin_ldexpf(1.0f, 24 - 2 * (tt <= 4 ? tt : tt - 5) - se);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s.u.accw[wid][nrow][32 * rg + 8 * j + tt] = fmaf(acc[tt][j], f, t1n);
+      for (int j = 0; j < 4; ++j) s.u.accw[wid][n][32 * rg + 8 * j + tt] = fmaf(acc[tt][j], f, t1n);
+    }
   }
   __syncthreads();
+  // the work-group's partial: the waves' (m, l, acc) merged, hi + lo columns
   float* part = p.part + ((int64_t)kvh * (p.n_sel_blk + p.n_split) + p.n_sel_blk + split) * G * kPartStride;
-  write_partial<G, G + 1>(part, s.mw, s.lw, s.u.accw);
+  for (int i = tid; i < G * kHeadDim; i += 256) {
+    const int h = i / kHeadDim, d = i % kHeadDim;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s.mw[w][h]);
+    float A = 0.f, L = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if (s.mw[w][h] == -INFINITY) continue;
+        const float e = expf(s.mw[w][h] - M);
+        A += e * (s.u.accw[w][h][d] + s.u.accw[w][G + h][d]);
+        L += e * s.lw[w][h];
+      }
+    }
+    part[h * kPartStride + d] = A;
+    if (d == 0) {
+      part[h * kPartStride + kHeadDim] = M;
+      part[h * kPartStride + kHeadDim + 1] = L;
+    }
+  }
 }
 
 template <int G>
