@@ -202,6 +202,31 @@ __device__ inline void lds_read_2v8h(uint32_t a, v8h& x, v8h& y) {
   y = __builtin_bit_cast(v8h, v);
 }
 
+// Buffer loads straight to LDS: a raw buffer resource (base, byte range) in
+// SGPRs, a per-lane byte offset that stays fixed and a wave-uniform one that
+// walks the chunks, so issuing a stage costs no vector instructions.  Reads
+// past the range return zeros (the hardware's range check), which is how the
+// split's last chunk stays inside the split.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ inline void bdma16(rsrc_t r, uint32_t voff, uint32_t soff, void* l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t)l, 16, voff, soff, 0, 0);
+}
+__device__ inline void bdma4(rsrc_t r, uint32_t voff, uint32_t soff, void* l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t)l, 4, voff, soff, 0, 0);
+}
+
+// v_cndmask with a wave-uniform 64-bit lane mask (SGPR pair): lane l takes
+// yes where bit l of mask is set, else no.
+__device__ inline float lane_select(uint64_t mask, float yes, float no) {
+  float r;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(no), "v"(yes), "s"(mask));
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // Score pass: grid (n_score_split, hkv), 4 wavefronts.  Each wave streams
 // 32-token chunks (two logit tiles) of its split through an LDS ring; the
@@ -216,12 +241,29 @@ struct SStage {
   float2 ks[32];
 };
 
+// Maximum over the four rows of two tiles at once: x0, x1 are a lane's
+// values of tiles 0 and 1; the result holds tile 0's maximum over lanes
+// l, l ^ 16, l ^ 32, l ^ 48 in rows 0 and 1 and tile 1's in rows 2 and 3.
+// permlane32_swap(x0, x1) returns (rows 0-1 of x0 | rows 0-1 of x1) and
+// (rows 2-3 of x0 | rows 2-3 of x1), so their maximum pairs each lane's tile
+// with the other half's; permlane16_swap does the same across rows 0-1 and
+// 2-3.  One v_max each (the values are never signalling NaNs).
+__device__ inline float max_two_tiles(float x0, float x1) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x0), __float_as_uint(x1), false, false);
+  float y;
+  asm("v_max_f32 %0, %1, %2" : "=v"(y) : "v"(__uint_as_float(r[0])), "v"(__uint_as_float(r[1])));
+  auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  asm("v_max_f32 %0, %1, %2" : "=v"(y) : "v"(__uint_as_float(q[0])), "v"(__uint_as_float(q[1])));
+  return y;
+}
+
 template <int G>
 __global__ void __launch_bounds__(256) score_mfma(DecodeParams p) {
   __shared__ QPrep qp;
   __shared__ uint32_t lhist[kHistBins];
   __shared__ SStage ring[4][kSRing];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kvh = blockIdx.y;
   int64_t lo, hi;
   int first;
@@ -229,26 +271,26 @@ __global__ void __launch_bounds__(256) score_mfma(DecodeParams p) {
   const float2 qx = load_query<G>(p.q + ((int64_t)seq * p.hq + kvh * G) * kHeadDim);
   const int64_t a = p.seq_off[seq];
   const int64_t t0 = (int64_t)kvh * p.cap + a + lo;            // first token row of the split
-  const uint8_t* kbase = p.kc + t0 * 32;
-  const float* kscg = p.ks + t0 * 2;
   const int nsp = (int)(hi - lo);
   const int nchunks = (nsp + 31) / 32;
   const int nmine = nchunks > wid ? (nchunks - wid + 3) / 4 : 0;
-  // stage i <- chunk wid + 4i of the wave's own chunks (tokens past the
-  // split read its last token)
-  auto issue = [&](int i) {
-    const int c = wid + 4 * i;
-    int rel = 32 * c + (lane >> 1);
-    rel = rel < nsp ? rel : nsp - 1;
-    SStage& st = ring[wid][i % kSRing];
-    dma16(kbase + (uint32_t)rel * 32u + 16u * (uint32_t)(lane & 1), st.k);
-    dma4(kscg + (uint32_t)rel * 2u + (uint32_t)(lane & 1), st.ks);
+  // stage i <- chunk wid + 4i of the wave's own chunks: lane L loads half
+  // L&1 of K row L/2 and scale word L; the resources end at the split's end
+  // (tokens past it read as zeros)
+  const rsrc_t rK = make_rsrc(p.kc + t0 * 32, (uint32_t)nsp * 32u);
+  const rsrc_t rS = make_rsrc(p.ks + t0 * 2, (uint32_t)nsp * 8u);
+  const uint32_t oK = 16u * (uint32_t)lane, oS = 4u * (uint32_t)lane;
+  auto issue = [&](int i, SStage& st) {
+    const uint32_t c = (uint32_t)(wid + 4 * i);
+    bdma16(rK, oK, c * 1024u, st.k);
+    bdma4(rS, oS, c * 256u, st.ks);
   };
   const bool hist = p.top_t > 0;   // no selection, no histogram
   for (int i = tid; i < kHistBins; i += 256) lhist[i] = 0u;
-#pragma unroll
-  for (int i = 0; i < kSRing - 1; ++i)
-    if (i < nmine) issue(i);
+  static_assert(kSRing == 4, "the stream loop is unrolled by the ring depth");
+  if (0 < nmine) issue(0, ring[wid][0]);
+  if (1 < nmine) issue(1, ring[wid][1]);
+  if (2 < nmine) issue(2, ring[wid][2]);
   v4i a0, a1;
   prep_query<G>(qx, qp, a0, a1);
   // logits in log2 units (1/sqrt(D) and log2(e) folded into the per-head
@@ -260,49 +302,57 @@ __global__ void __launch_bounds__(256) score_mfma(DecodeParams p) {
   float* scores = p.scores + (int64_t)kvh * p.ntot + (a - p.off0) + lo;
   float* lgo = p.logits + ((int64_t)kvh * p.ntot + (a - p.off0) + lo) * G;
   const uint32_t ring0 = lds_addr(&ring[wid][0]);
-  const uint32_t offK = (uint32_t)(t * 32 + 8 * hl);
-  const uint32_t offS = (uint32_t)(offsetof(SStage, ks) + 8 * t);
-  const int hx = hl >> 1;                         // after the reduction: tile of this lane
+  const uint32_t aK = ring0 + (uint32_t)(t * 32 + 8 * hl);
+  const uint32_t aS = ring0 + (uint32_t)(offsetof(SStage, ks) + 8 * t);
+  const int hx = hl >> 1;                         // the tile a lane writes the score of
   const uint32_t hist0 = lds_addr(&lhist[0]);
-  for (int i = 0; i < nmine; ++i) {
-    if (i + kSRing - 1 < nmine) issue(i + kSRing - 1);
+  auto body = [&](auto kc, int i) {
+    constexpr int k = decltype(kc)::value;        // stage of chunk i
+    constexpr int OFF = k * (int)sizeof(SStage);
+    if (i + 3 < nmine) issue(i + 3, ring[wid][(k + 3) & 3]);
+    // this wave's loads complete in order: stage i is in once no more than
+    // the stages issued after it are outstanding (stores only add to the count)
     wait_stages<kSRingLoads>(min(kSRing - 1, nmine - 1 - i));
     const int c = wid + 4 * i;
-    const uint32_t sb = ring0 + (uint32_t)(i % kSRing) * (uint32_t)sizeof(SStage);
     uint64_t kw[2], ks[2];
     asm volatile(
-        "ds_read_b64 %0, %4\n\t"
-        "ds_read_b64 %1, %4 offset:512\n\t"
-        "ds_read_b64 %2, %5\n\t"
-        "ds_read_b64 %3, %5 offset:128\n\t"
+        "ds_read_b64 %0, %4 offset:%6\n\t"
+        "ds_read_b64 %1, %4 offset:%7\n\t"
+        "ds_read_b64 %2, %5 offset:%6\n\t"
+        "ds_read_b64 %3, %5 offset:%8\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(kw[0]), "=&v"(kw[1]), "=&v"(ks[0]), "=&v"(ks[1])
-        : "v"(sb + offK), "v"(sb + offS)
+        : "v"(aK), "v"(aS), "n"(OFF), "n"(OFF + 512), "n"(OFF + 128)
         : "memory");
+    const bool full = 32 * c + 32 <= nsp;         // every token of the chunk inside the split
     float lg[2];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const uint2 w = __builtin_bit_cast(uint2, kw[k]);
+    for (int j = 0; j < 2; ++j) {
+      const uint2 w = __builtin_bit_cast(uint2, kw[j]);
       v4i b0, b1;
       decode_b2(w.x, w.y, b0, b1);
       v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, v4i{0, 0, 0, 0}, 0, 0, 0);
       D = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, D, 0, 0, 0);
-      const float x = logit_scaled(D, __builtin_bit_cast(float2, ks[k]), scale, sumq);
-      lg[k] = hl < G ? x : -INFINITY;
-      const int rel = 32 * c + 16 * k + t;
-      if (hl < G && rel < nsp) lgo[rel * G + hl] = x;   // kept for the attention pass
+      const float x = logit_scaled(D, __builtin_bit_cast(float2, ks[j]), scale, sumq);
+      lg[j] = hl < G ? x : -INFINITY;
+      const int rel = 32 * c + 16 * j + t;
+      if (hl < G && (full || rel < nsp)) lgo[rel * G + hl] = x;   // kept for the attention pass
     }
-    // maximum over the heads, two tiles at once: after the first exchange a
-    // lane keeps tile hl/2 over heads {hl, hl^2}, after the second over all
-    const float r = __shfl_xor(hx ? lg[0] : lg[1], 32);
-    float y = fmaxf(hx ? lg[1] : lg[0], r);
-    y = fmaxf(y, __shfl_xor(y, 16));
+    // maximum over the heads, two tiles at once: lane (t, hl) keeps tile
+    // hl/2 (token 16 (hl/2) + t)
+    const float y = max_two_tiles(lg[0], lg[1]);
     const int rel = 32 * c + 16 * hx + t;
-    if ((hl & 1) == 0 && rel < nsp) {
-      y *= kLn2;                                  // the score in natural units
-      scores[rel] = y;
-      if (hist) lds_add_u32(hist0 + 4u * (score_key(y) >> (32 - kHistBits)), 1u);
+    if ((hl & 1) == 0 && (full || rel < nsp)) {
+      const float sc = y * kLn2;                  // the score in natural units
+      scores[rel] = sc;
+      if (hist) lds_add_u32(hist0 + 4u * (score_key(sc) >> (32 - kHistBits)), 1u);
     }
+  };
+  for (int i = 0; i < nmine; i += 4) {
+    body(std::integral_constant<int, 0>{}, i);
+    if (i + 1 < nmine) body(std::integral_constant<int, 1>{}, i + 1);
+    if (i + 2 < nmine) body(std::integral_constant<int, 2>{}, i + 2);
+    if (i + 3 < nmine) body(std::integral_constant<int, 3>{}, i + 3);
   }
   // the histogram adds (asm, not waited for) complete before the barrier
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
@@ -358,31 +408,6 @@ __device__ inline float row16_max_dpp(float x) {
       : "=&v"(y)
       : "v"(x));
   return y;
-}
-
-// Buffer loads straight to LDS: a raw buffer resource (base, byte range) in
-// SGPRs, a per-lane byte offset that stays fixed and a wave-uniform one that
-// walks the chunks, so issuing a stage costs no vector instructions.  Reads
-// past the range return zeros (the hardware's range check), which is how the
-// split's last chunk stays inside the split.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-__device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ inline void bdma16(rsrc_t r, uint32_t voff, uint32_t soff, void* l) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t)l, 16, voff, soff, 0, 0);
-}
-__device__ inline void bdma4(rsrc_t r, uint32_t voff, uint32_t soff, void* l) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t)l, 4, voff, soff, 0, 0);
-}
-
-// v_cndmask with a wave-uniform 64-bit lane mask (SGPR pair): lane l takes
-// yes where bit l of mask is set, else no.
-__device__ inline float lane_select(uint64_t mask, float yes, float no) {
-  float r;
-  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(no), "v"(yes), "s"(mask));
-  return r;
 }
 
 // One lane's operands of a stage.  The LDS reads are written in asm: a read
@@ -492,7 +517,7 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
 #pragma unroll
   for (int v = 0; v < 4; ++v) aV[v] = ring0 + (uint32_t)(offsetof(St, v) + (4 * rg + (v ^ rg)) * 32 + 4 * vdw);
   // rows hl < G hold heads; the others take no part
-  const uint64_t rows = G >= 4 ? ~0ull : (1ull << (16 * G)) - 1ull;
+  const uint64_t rows = G >= 4 ? ~0ull : (1ull << (16 * (G & 3))) - 1ull;
   const float ninf = -INFINITY;
 
   // running maximum: a finite floor below every logit until a token takes
