@@ -167,7 +167,7 @@ __global__ void __launch_bounds__(256) attend_valu(DecodeParams p) {
 // accumulation reads of different partials are independent of each other.
 __global__ void __launch_bounds__(256) combine(DecodeParams p) {
   __shared__ float red[4];
-  __shared__ float ew[kCombineMax];
+  __shared__ float ew[kCombineMax], lw[kCombineMax];
   __shared__ float snum[8][32];
   const int s = blockIdx.x / p.hq, h = blockIdx.x % p.hq;
   const int kvh = h / p.grp, hg = h % p.grp;
@@ -186,10 +186,21 @@ __global__ void __launch_bounds__(256) combine(DecodeParams p) {
   const float* base = p.part + (int64_t)kvh * (p.n_sel_blk + p.n_split) * stride + hg * kPartStride;
   const int np = ns + nb;
   auto row = [&](int x) { return x < ns ? base + (sb + x) * stride : base + (p.n_sel_blk + bb + x - ns) * stride; };
+  // every load at once: thread (sl, dl)'s first kPre accumulator values, and
+  // the (m, l) of the partials it scans; the weights e^{m_x - M} follow in LDS
+  constexpr int kPre = 16;
+  float av[kPre];
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) {
+    const int x = sl + 8 * k;
+    av[k] = x < np ? row(x)[d] : 0.f;
+  }
   float M = -INFINITY;
   for (int x = tid; x < np; x += 256) {
-    const float mx = row(x)[kHeadDim];
+    const float* r = row(x);
+    const float mx = r[kHeadDim];
     ew[x] = mx;
+    lw[x] = r[kHeadDim + 1];
     M = fmaxf(M, mx);
   }
   M = wave_max(M);
@@ -201,14 +212,18 @@ __global__ void __launch_bounds__(256) combine(DecodeParams p) {
     const float mx = ew[x];
     const float e = mx == -INFINITY ? 0.f : expf(mx - M);   // -inf: a split whose tokens were all selected
     ew[x] = e;
-    den = fmaf(e, row(x)[kHeadDim + 1], den);
+    den = fmaf(e, lw[x], den);
   }
   den = wave_sum(den);
   __syncthreads();
   if ((tid & 63) == 0) red[tid >> 6] = den;
   float num = 0.f;
-#pragma unroll 8
-  for (int x = sl; x < np; x += 8) num = fmaf(ew[x], row(x)[d], num);
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) {
+    const int x = sl + 8 * k;
+    if (x < np) num = fmaf(ew[x], av[k], num);
+  }
+  for (int x = sl + 8 * kPre; x < np; x += 8) num = fmaf(ew[x], row(x)[d], num);
   snum[sl][dl] = num;
   __syncthreads();
   if (sl == 0) {
