@@ -44,8 +44,8 @@ __device__ inline void base_split_valu(const DecodeParams& p, int split, int kvh
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   int64_t lo, hi;
   int first;
-  const int seq = locate_unit(p.seq_off, p.batch, p.split, split, false, 0, lo, hi, first);
-  const int64_t a = p.seq_off[seq];
+  const int seq = locate_unit(p, p.split, split, false, lo, hi, first);
+  const int64_t a = seq_at(p, seq);
   const int64_t sk = (int64_t)seq * p.hkv + kvh;
   const uint32_t* bm = p.bitmap + sk * p.bm_words;
   const bool masked = p.use_refine != 0;
@@ -175,11 +175,11 @@ __global__ void __launch_bounds__(256) combine(DecodeParams p) {
   const int d = blockIdx.y * 32 + dl;
   int sb = 0, bb = 0;
   for (int i = 0; i < s; ++i) {
-    const int64_t n = p.seq_off[i + 1] - p.seq_off[i];
+    const int64_t n = seq_at(p, i + 1) - seq_at(p, i);
     bb += (int)((n + p.split - 1) / p.split);
     if (p.use_refine) sb += (int)(((n < p.top_t ? n : p.top_t) + kSelBlkTok - 1) / kSelBlkTok);
   }
-  const int64_t n = p.seq_off[s + 1] - p.seq_off[s];
+  const int64_t n = seq_at(p, s + 1) - seq_at(p, s);
   const int nb = (int)((n + p.split - 1) / p.split);
   const int ns = p.use_refine ? (int)(((n < p.top_t ? n : p.top_t) + kSelBlkTok - 1) / kSelBlkTok) : 0;
   const int64_t stride = (int64_t)p.grp * kPartStride;

@@ -99,8 +99,8 @@ __device__ inline void selected_block(const DecodeParams& p, int blk, int kvh, u
   const int tk = lane >> 2, qd = lane & 3;
   int64_t lo, hi;
   int first;
-  const int seq = locate_unit(p.seq_off, p.batch, kSelBlkTok, blk, true, p.top_t, lo, hi, first);
-  const int64_t a = p.seq_off[seq];
+  const int seq = locate_unit(p, kSelBlkTok, blk, true, lo, hi, first);
+  const int64_t a = seq_at(p, seq);
   const int64_t sk = (int64_t)seq * p.hkv + kvh;
   const int r = p.r;
   const float sub = __builtin_ldexpf(1.0f, -r);

@@ -58,16 +58,27 @@ __device__ inline float wave_sum(float v) {
   return v;
 }
 
+// Offset of sequence s (0 <= s <= batch).  A single sequence's offsets are
+// in the parameter block (off0, off0 + ntot), so that a kernel's first memory
+// accesses need not wait for a load of the offsets.
+__device__ inline int64_t seq_at(const DecodeParams& p, int s) {
+  if (p.batch == 1) return s == 0 ? p.off0 : p.off0 + p.ntot;
+  return p.seq_off[s];
+}
+
 // Unit x of a flat enumeration where sequence s contributes ceil(len_s / unit)
 // units, len_s = n_s (tokens) or min(T, n_s) (selected tokens) when `sel_len`.
 // Returns the sequence and the unit's [lo, hi) range in sequence-local terms;
 // `first` receives the flat index of the sequence's first unit.
-__device__ inline int locate_unit(const int64_t* off, int batch, int64_t unit, int x, bool sel_len,
-                                  int64_t top_t, int64_t& lo, int64_t& hi, int& first) {
+__device__ inline int locate_unit(const DecodeParams& p, int64_t unit, int x, bool sel_len, int64_t& lo,
+                                  int64_t& hi, int& first) {
   int base = 0;
-  for (int s = 0; s < batch; ++s) {
-    int64_t len = off[s + 1] - off[s];
-    if (sel_len) len = len < top_t ? len : top_t;
+  int64_t o0 = seq_at(p, 0);
+  for (int s = 0; s < p.batch; ++s) {
+    const int64_t o1 = seq_at(p, s + 1);
+    int64_t len = o1 - o0;
+    o0 = o1;
+    if (sel_len) len = len < p.top_t ? len : (int64_t)p.top_t;
     const int n = (int)((len + unit - 1) / unit);
     if (x < base + n) {
       lo = (int64_t)(x - base) * unit;
@@ -140,6 +151,55 @@ __device__ inline void find_threshold(const uint32_t* hist, uint32_t need, uint3
         break;
       }
       cum += hist[b];
+    }
+  }
+  __syncthreads();
+}
+
+// find_threshold computed by wavefront 0 alone, without block-wide scans
+// (the other wavefronts wait at the closing barrier).  `hist` is 16-byte
+// aligned LDS, 256 <= NB <= 4096.  Lane l first sums bins
+// [NB - PER (l + 1), NB - PER l), PER = NB / 64; the lane whose range holds
+// the boundary is found from the prefix over lanes, then its PER bins are
+// taken one per lane.
+template <int NB>
+__device__ inline void find_threshold_wave(const uint32_t* hist, uint32_t need, int* out_bin, uint32_t* out_need) {
+  static_assert(NB % 256 == 0 && NB <= 4096, "one bin per lane in the second step");
+  constexpr int PER = NB / 64, Q = PER / 4;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const uint4* h4 = reinterpret_cast<const uint4*>(hist) + (NB / 4 - Q * (lane + 1));
+    uint32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < Q; ++i) {
+      // rotated start: neighbouring lanes read different LDS banks
+      const uint4 x = h4[(i + lane) % Q];
+      s += x.x + x.y + x.z + x.w;
+    }
+    uint32_t inc = s;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(inc, o);
+      if (lane >= o) inc += y;
+    }
+    const uint64_t hit = __ballot(inc - s < need && need <= inc);
+    if (hit) {
+      const int L = __ffsll((unsigned long long)hit) - 1;
+      const uint32_t above = __shfl(inc - s, L);
+      const int top = NB - PER * L;
+      const uint32_t c = lane < PER ? hist[top - 1 - lane] : 0u;
+      uint32_t cum = c;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(cum, o);
+        if (lane >= o) cum += y;
+      }
+      const uint64_t hit2 = __ballot(above + cum >= need);
+      const int j = __ffsll((unsigned long long)hit2) - 1;
+      if (lane == j) {
+        *out_bin = top - 1 - j;
+        *out_need = need - (above + cum - c);
+      }
     }
   }
   __syncthreads();

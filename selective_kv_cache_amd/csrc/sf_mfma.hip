@@ -267,9 +267,9 @@ __global__ void __launch_bounds__(256) score_mfma(DecodeParams p) {
   const int kvh = blockIdx.y;
   int64_t lo, hi;
   int first;
-  const int seq = locate_unit(p.seq_off, p.batch, p.score_split, blockIdx.x, false, 0, lo, hi, first);
+  const int seq = locate_unit(p, p.score_split, blockIdx.x, false, lo, hi, first);
   const float2 qx = load_query<G>(p.q + ((int64_t)seq * p.hq + kvh * G) * kHeadDim);
-  const int64_t a = p.seq_off[seq];
+  const int64_t a = seq_at(p, seq);
   const int64_t t0 = (int64_t)kvh * p.cap + a + lo;            // first token row of the split
   const int nsp = (int)(hi - lo);
   const int nchunks = (nsp + 31) / 32;
@@ -453,8 +453,8 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   int64_t lo, hi;
   int first;
-  const int seq = locate_unit(p.seq_off, p.batch, p.split, split, false, 0, lo, hi, first);
-  const int64_t a = p.seq_off[seq];
+  const int seq = locate_unit(p, p.split, split, false, lo, hi, first);
+  const int64_t a = seq_at(p, seq);
   const int64_t sk = (int64_t)seq * p.hkv + kvh;
   const bool masked = p.use_refine != 0;
   const int64_t t0 = (int64_t)kvh * p.cap + a + lo;            // first token row of the split

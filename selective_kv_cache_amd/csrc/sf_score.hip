@@ -36,8 +36,8 @@ __global__ void __launch_bounds__(256) score_valu(DecodeParams p) {
   const int kvh = blockIdx.y;
   int64_t lo, hi;
   int first;
-  const int seq = locate_unit(p.seq_off, p.batch, p.score_split, blockIdx.x, false, 0, lo, hi, first);
-  const int64_t a = p.seq_off[seq];
+  const int seq = locate_unit(p, p.score_split, blockIdx.x, false, lo, hi, first);
+  const int64_t a = seq_at(p, seq);
   for (int i = tid; i < G * kHeadDim; i += 256)
     qs[i / kHeadDim][i % kHeadDim] = p.q[((int64_t)seq * p.hq + kvh * G) * kHeadDim + i];
   const bool hist = p.top_t > 0;   // no selection, no histogram

@@ -34,8 +34,7 @@ __device__ inline uint64_t fin_value(uint2 c) {
 }
 
 __global__ void __launch_bounds__(kSelThreads) select_scan(DecodeParams p) {
-  __shared__ uint32_t h[kHistBins];
-  __shared__ uint32_t scan_lds[kSelThreads / 64];
+  __shared__ __align__(16) uint32_t h[kHistBins];
   __shared__ int sh_bin;
   __shared__ uint32_t sh_need, sh_cnt;
 
@@ -43,10 +42,10 @@ __global__ void __launch_bounds__(kSelThreads) select_scan(DecodeParams p) {
   const int kvh = blockIdx.y;
   int64_t lo, hi;
   int first;
-  const int seq = locate_unit(p.seq_off, p.batch, p.sel_chunk, blockIdx.x, false, 0, lo, hi, first);
+  const int seq = locate_unit(p, p.sel_chunk, blockIdx.x, false, lo, hi, first);
   const int chunk = blockIdx.x - first;
-  const int64_t a = p.seq_off[seq];
-  const int64_t n = p.seq_off[seq + 1] - a;
+  const int64_t a = seq_at(p, seq);
+  const int64_t n = seq_at(p, seq + 1) - a;
   const int64_t tn = n < p.top_t ? n : (int64_t)p.top_t;
   const bool all = (tn == n);
   const int64_t sk = (int64_t)seq * p.hkv + kvh;
@@ -68,7 +67,7 @@ __global__ void __launch_bounds__(kSelThreads) select_scan(DecodeParams p) {
     for (int i = tid; i < kHistBins; i += kSelThreads) h[i] = h1[i];
     if (tid == 0) sh_cnt = 0u;
     __syncthreads();
-    find_threshold<kSelThreads, kHistBins>(h, (uint32_t)tn, scan_lds, &sh_bin, &sh_need);
+    find_threshold_wave<kHistBins>(h, (uint32_t)tn, &sh_bin, &sh_need);
   }
   const uint32_t b1 = all ? 0u : (uint32_t)sh_bin;
 #pragma unroll
@@ -124,68 +123,111 @@ __device__ inline uint2 cand_at(const uint2* cand, const uint32_t* segoff, int n
   return cand[(int64_t)lo * chunk_len + (j - segoff[lo])];
 }
 
-constexpr int kLdsBitmapWords = 16384;   // sequences up to 512K tokens keep the bitmap in LDS
+constexpr int kLdsBitmapWords = 16384;   // bitmaps up to 512K tokens are kept in LDS
 constexpr int kCandLds = 4096;           // candidates kept in LDS
+constexpr int kBmQuads = kLdsBitmapWords / 4 / kResThreads;   // 16-byte bitmap pieces per thread
 
 __global__ void __launch_bounds__(kResThreads) select_resolve(DecodeParams p) {
-  __shared__ uint32_t h[kHistBins];
+  __shared__ __align__(16) uint32_t h[kHistBins];
   __shared__ uint32_t scan_lds[kResThreads / 64];
   __shared__ uint32_t rh[256];
   __shared__ uint2 cl[kCandLds];
   __shared__ uint2 fin[kFinMax];
   __shared__ uint32_t segoff[kMaxSelChunks + 1];
-  __shared__ uint32_t lbm[kLdsBitmapWords];
+  __shared__ __align__(16) uint32_t lbm[kLdsBitmapWords];
   __shared__ int sh_bin;
   __shared__ uint32_t sh_need, sh_fin;
   static_assert(kMaxSelChunks <= kResThreads, "one chunk count per thread");
 
   const int tid = threadIdx.x;
   const int64_t sk = blockIdx.x;
-  const int seq = (int)(sk / p.hkv);
-  const int64_t a = p.seq_off[seq];
-  const int64_t n = p.seq_off[seq + 1] - a;
-  const int64_t tn = n < p.top_t ? n : (int64_t)p.top_t;
-  const bool all = (tn == n);
   uint32_t* gbm = p.bitmap + sk * p.bm_words;
   const uint2* cand = p.cand + sk * p.max_seq;
   const uint32_t* cnts = p.counters + sk * p.cnt_stride;
+  // Everything this kernel reads from the scan is loaded up front, before the
+  // sequence's length is known (every read is inside the per-head areas):
+  // the chunks' candidate counts, the level-1 boundary, the bitmap words.
+  const bool in_lds = p.bm_words <= kLdsBitmapWords;
+  const int nqb = p.bm_words >> 2;   // bm_words is a multiple of 16
+  uint4 bq[kBmQuads];
+  if (in_lds) {
+    const uint4* g4 = reinterpret_cast<const uint4*>(gbm);
+#pragma unroll
+    for (int k = 0; k < kBmQuads; ++k) {
+      const int qi = tid + k * kResThreads;
+      bq[k] = qi < nqb ? g4[qi] : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  uint32_t my_cnt = tid < p.cnt_stride - 2 ? cnts[tid] : 0u;
+  const uint32_t need1 = cnts[p.cnt_stride - 1];
+
+  const int seq = (int)(sk / p.hkv);
+  const int64_t a = seq_at(p, seq);
+  const int64_t n = seq_at(p, seq + 1) - a;
+  const int64_t tn = n < p.top_t ? n : (int64_t)p.top_t;
+  const bool all = (tn == n);
   const int nch = (int)((n + p.sel_chunk - 1) / p.sel_chunk);
   const int64_t nw = (n + 31) >> 5;
-  const bool in_lds = nw <= kLdsBitmapWords;
   uint32_t* bm = in_lds ? lbm : gbm;
+  my_cnt = (!all && tid < nch) ? my_cnt : 0u;
 
-  // Everything this kernel reads from the scan is loaded up front: the
-  // chunks' candidate counts, the level-1 boundary, the bitmap words.  The
-  // level-1 histogram is cleared for the next step.
-  const uint32_t my_cnt = (!all && tid < nch) ? cnts[tid] : 0u;
-  const uint32_t need1 = all ? 0u : cnts[p.cnt_stride - 1];
-  if (in_lds)
-    for (int64_t w = tid; w < nw; w += kResThreads) lbm[w] = gbm[w];
+  // the level-1 histogram is cleared for the next step
   uint32_t* h1 = p.hist + sk * kHistBins;
   for (int i = tid; i < kHistBins; i += kResThreads) {
     h1[i] = 0u;
     h[i] = 0u;
   }
+  if (in_lds) {
+    uint4* l4 = reinterpret_cast<uint4*>(lbm);
+#pragma unroll
+    for (int k = 0; k < kBmQuads; ++k) {
+      const int qi = tid + k * kResThreads;
+      if (qi < nqb) l4[qi] = bq[k];
+    }
+  }
   if (!all) {
     // segment offsets: exclusive prefix of the per-chunk candidate counts
-    uint32_t ncand;
-    const uint32_t run = block_exclusive_scan<kResThreads>(my_cnt, scan_lds, ncand);
-    if (tid < nch) segoff[tid] = run;
-    if (tid == 0) {
-      segoff[nch] = ncand;
-      sh_fin = 0u;
+    if (nch <= 64) {
+      if (tid < 64) {
+        uint32_t inc = my_cnt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t y = __shfl_up(inc, o);
+          if (tid >= o) inc += y;
+        }
+        if (tid < nch) segoff[tid] = inc - my_cnt;
+        if (tid == nch - 1) segoff[nch] = inc;
+      }
+    } else {
+      uint32_t tot;
+      const uint32_t run = block_exclusive_scan<kResThreads>(my_cnt, scan_lds, tot);
+      if (tid < nch) segoff[tid] = run;
+      if (tid == 0) segoff[nch] = tot;
     }
+    if (tid == 0) sh_fin = 0u;
     __syncthreads();
+    const uint32_t ncand = segoff[nch];
     const bool cand_lds = ncand <= (uint32_t)kCandLds;
     // level 2: histogram of the candidates' middle 12 key bits (candidates
-    // are copied to LDS on the way)
-    for (uint32_t j = tid; j < ncand; j += kResThreads) {
-      const uint2 cv = cand_at(cand, segoff, nch, p.sel_chunk, j);
-      if (cand_lds) cl[j] = cv;
-      atomicAdd(&h[(cv.x >> 8) & 0xFFFu], 1u);
+    // are copied to LDS on the way); loads in groups of four
+    for (uint32_t j0 = tid; j0 < ncand; j0 += 4 * kResThreads) {
+      uint2 cv[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t j = j0 + k * kResThreads;
+        cv[k] = j < ncand ? cand_at(cand, segoff, nch, p.sel_chunk, j) : make_uint2(0u, 0u);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t j = j0 + k * kResThreads;
+        if (j < ncand) {
+          if (cand_lds) cl[j] = cv[k];
+          atomicAdd(&h[(cv[k].x >> 8) & 0xFFFu], 1u);
+        }
+      }
     }
     __syncthreads();
-    find_threshold<kResThreads, kHistBins>(h, need1, scan_lds, &sh_bin, &sh_need);
+    find_threshold_wave<kHistBins>(h, need1, &sh_bin, &sh_need);
     const uint32_t b2 = (uint32_t)sh_bin, need2 = sh_need;
     auto cget = [&](uint32_t j) -> uint2 { return cand_lds ? cl[j] : cand_at(cand, segoff, nch, p.sel_chunk, j); };
     for (uint32_t j = tid; j < ncand; j += kResThreads) {
@@ -261,18 +303,10 @@ __global__ void __launch_bounds__(kResThreads) select_resolve(DecodeParams p) {
 
   // List the selection in ascending token order; the final bitmap goes back
   // to global memory for the attention pass.
-  const int64_t per = (nw + kResThreads - 1) / kResThreads;
-  const int64_t w0 = tid * per < nw ? tid * per : nw;
-  const int64_t w1 = w0 + per < nw ? w0 + per : nw;
-  uint32_t cnt = 0;
-  for (int64_t w = w0; w < w1; ++w) cnt += __popc(bm[w]);
-  uint32_t tot;
-  uint32_t pos = block_exclusive_scan<kResThreads>(cnt, scan_lds, tot);
   int32_t* sel = p.sel + sk * p.top_t;
   int32_t* selo = p.sel_out ? p.sel_out + sk * p.top_t : nullptr;
-  for (int64_t w = w0; w < w1; ++w) {
-    uint32_t bits = bm[w];
-    if (in_lds) gbm[w] = bits;
+  uint32_t pos = 0;
+  auto emit = [&](uint32_t bits, int64_t w) {
     while (bits) {
       const int bit = __ffs(bits) - 1;
       bits &= bits - 1u;
@@ -283,6 +317,43 @@ __global__ void __launch_bounds__(kResThreads) select_resolve(DecodeParams p) {
       }
       ++pos;
     }
+  };
+  uint32_t tot;
+  if (in_lds) {
+    // thread t: 16-byte pieces [t qp, (t + 1) qp) of the bitmap (qp <= kBmQuads);
+    // the pieces' words past the sequence's last word hold no bits
+    const int nq = (int)((nw + 3) >> 2);
+    const int qp = (nq + kResThreads - 1) / kResThreads;
+    const uint4* l4 = reinterpret_cast<const uint4*>(lbm);
+    uint4* g4 = reinterpret_cast<uint4*>(gbm);
+    uint4 mine[kBmQuads];
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int k = 0; k < kBmQuads; ++k) {
+      const int qi = tid * qp + k;
+      mine[k] = (k < qp && qi < nq) ? l4[qi] : make_uint4(0u, 0u, 0u, 0u);
+      cnt += __popc(mine[k].x) + __popc(mine[k].y) + __popc(mine[k].z) + __popc(mine[k].w);
+    }
+    pos = block_exclusive_scan<kResThreads>(cnt, scan_lds, tot);
+#pragma unroll
+    for (int k = 0; k < kBmQuads; ++k) {
+      const int qi = tid * qp + k;
+      if (k < qp && qi < nq) {
+        g4[qi] = mine[k];
+        emit(mine[k].x, 4 * (int64_t)qi);
+        emit(mine[k].y, 4 * (int64_t)qi + 1);
+        emit(mine[k].z, 4 * (int64_t)qi + 2);
+        emit(mine[k].w, 4 * (int64_t)qi + 3);
+      }
+    }
+  } else {
+    const int64_t per = (nw + kResThreads - 1) / kResThreads;
+    const int64_t w0 = tid * per < nw ? tid * per : nw;
+    const int64_t w1 = w0 + per < nw ? w0 + per : nw;
+    uint32_t cnt = 0;
+    for (int64_t w = w0; w < w1; ++w) cnt += __popc(bm[w]);
+    pos = block_exclusive_scan<kResThreads>(cnt, scan_lds, tot);
+    for (int64_t w = w0; w < w1; ++w) emit(bm[w], w);
   }
   for (int64_t j = tn + tid; j < p.top_t; j += kResThreads) {
     sel[j] = -1;

@@ -64,8 +64,8 @@ cache_lookup(DecodeParams p, int32_t* slot_tok, int32_t* stamp, int32_t* tok_slo
   const int tid = threadIdx.x;
   const int64_t sk = blockIdx.x;
   const int seq = (int)(sk / p.hkv), kvh = (int)(sk % p.hkv);
-  const int64_t a = p.seq_off[seq];
-  const int64_t n = p.seq_off[seq + 1] - a;
+  const int64_t a = seq_at(p, seq);
+  const int64_t n = seq_at(p, seq + 1) - a;
   const int32_t tn = (int32_t)(n < p.top_t ? n : p.top_t);
   const int32_t* sel = p.sel + sk * p.top_t;
   int32_t* st_tok = slot_tok + sk * p.slots;
