@@ -203,7 +203,7 @@ __global__ void __launch_bounds__(256) combine(DecodeParams p) {
     lw[x] = r[kHeadDim + 1];
     M = fmaxf(M, mx);
   }
-  M = wave_max(M);
+  M = wave_max_dpp(M);
   if ((tid & 63) == 0) red[tid >> 6] = M;
   __syncthreads();
   M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
@@ -214,7 +214,7 @@ __global__ void __launch_bounds__(256) combine(DecodeParams p) {
     ew[x] = e;
     den = fmaf(e, lw[x], den);
   }
-  den = wave_sum(den);
+  den = wave_sum_dpp(den);
   __syncthreads();
   if ((tid & 63) == 0) red[tid >> 6] = den;
   float num = 0.f;

@@ -58,6 +58,57 @@ __device__ inline float wave_sum(float v) {
   return v;
 }
 
+// Cross-lane steps through DPP (data-parallel primitives: a VALU operand taken
+// from another lane of the same 16-lane row) and lane reads into scalar
+// registers, instead of LDS permutes.  All 64 lanes must be active.
+template <int CTRL>
+__device__ inline uint32_t dpp_u32(uint32_t fill, uint32_t x) {
+  // lanes whose source lies outside their row keep `fill`
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)fill, (int)x, CTRL, 0xF, 0xF, false);
+}
+
+// Inclusive prefix sum over the wavefront (lane 0 first): row_shr 1, 2, 4, 8
+// inside each row, then the rows' totals.
+__device__ inline uint32_t wave_inclusive_scan(uint32_t x) {
+  x += dpp_u32<0x111>(0u, x);
+  x += dpp_u32<0x112>(0u, x);
+  x += dpp_u32<0x114>(0u, x);
+  x += dpp_u32<0x118>(0u, x);
+  const uint32_t r0 = __builtin_amdgcn_readlane(x, 15);
+  const uint32_t r1 = r0 + __builtin_amdgcn_readlane(x, 31);
+  const uint32_t r2 = r1 + __builtin_amdgcn_readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row == 0 ? 0u : row == 1 ? r0 : row == 2 ? r1 : r2);
+}
+
+// Maximum and sum over the wavefront, the same value in every lane: quad
+// permutes and row mirrors reduce each row, then the four row results.
+__device__ inline float row_fold_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+}
+__device__ inline float wave_max_dpp(float v) {
+  v = row_fold_max(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+__device__ inline float wave_sum_dpp(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 // Offset of sequence s (0 <= s <= batch).  A single sequence's offsets are
 // in the parameter block (off0, off0 + ntot), so that a kernel's first memory
 // accesses need not wait for a load of the offsets.
@@ -107,12 +158,7 @@ __device__ inline uint32_t code_at(const uint32_t* words, int d) {
 template <int NT>
 __device__ inline uint32_t block_exclusive_scan(uint32_t v, uint32_t* lds, uint32_t& total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_inclusive_scan(v);
   if (lane == 63) lds[wid] = x;
   __syncthreads();
   uint32_t base = 0, tot = 0;
@@ -176,24 +222,14 @@ __device__ inline void find_threshold_wave(const uint32_t* hist, uint32_t need, 
       const uint4 x = h4[(i + lane) % Q];
       s += x.x + x.y + x.z + x.w;
     }
-    uint32_t inc = s;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = __shfl_up(inc, o);
-      if (lane >= o) inc += y;
-    }
+    const uint32_t inc = wave_inclusive_scan(s);
     const uint64_t hit = __ballot(inc - s < need && need <= inc);
     if (hit) {
       const int L = __ffsll((unsigned long long)hit) - 1;
-      const uint32_t above = __shfl(inc - s, L);
+      const uint32_t above = __builtin_amdgcn_readlane(inc - s, L);
       const int top = NB - PER * L;
       const uint32_t c = lane < PER ? hist[top - 1 - lane] : 0u;
-      uint32_t cum = c;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(cum, o);
-        if (lane >= o) cum += y;
-      }
+      const uint32_t cum = wave_inclusive_scan(c);
       const uint64_t hit2 = __ballot(above + cum >= need);
       const int j = __ffsll((unsigned long long)hit2) - 1;
       if (lane == j) {

@@ -70,10 +70,14 @@ __global__ void __launch_bounds__(kSelThreads) select_scan(DecodeParams p) {
     find_threshold_wave<kHistBins>(h, (uint32_t)tn, &sh_bin, &sh_need);
   }
   const uint32_t b1 = all ? 0u : (uint32_t)sh_bin;
+  // bitmap words of the tokens above b1; the candidates' ballots are kept so
+  // that each wavefront reserves its candidate slots with one LDS atomic
+  uint64_t cbal[kPer];
+  uint32_t ckey[kPer];
+  uint32_t wave_cnt = 0;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int64_t base = lo + j * kSelThreads;
-    if (base >= hi) break;
     const int64_t i = base + tid;
     const bool valid = i < hi;
     bool s = false, cnd = false;
@@ -89,17 +93,25 @@ __global__ void __launch_bounds__(kSelThreads) select_scan(DecodeParams p) {
       }
     }
     const uint64_t bal = __ballot(s);
-    if (lane == 0) {
+    if (lane == 0 && base < hi) {
       const int64_t w = (base + wid * 64) >> 5;
       bm[w] = (uint32_t)bal;
       bm[w + 1] = (uint32_t)(bal >> 32);
     }
-    const uint64_t cb = __ballot(cnd);
-    if (cb) {
-      uint32_t at = 0;
-      if (lane == 0) at = atomicAdd(&sh_cnt, (uint32_t)__popcll(cb));
-      at = __shfl(at, 0);
-      if (cnd) cand[at + (uint32_t)__popcll(cb & ((1ull << lane) - 1ull))] = make_uint2(key, (uint32_t)i);
+    cbal[j] = __ballot(cnd);
+    ckey[j] = key;
+    wave_cnt += (uint32_t)__popcll(cbal[j]);
+  }
+  if (wave_cnt) {
+    uint32_t at = 0;
+    if (lane == 0) at = atomicAdd(&sh_cnt, wave_cnt);
+    at = __builtin_amdgcn_readlane(at, 0);
+    const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      if ((cbal[j] >> lane) & 1ull)
+        cand[at + (uint32_t)__popcll(cbal[j] & below)] = make_uint2(ckey[j], (uint32_t)(lo + j * kSelThreads + tid));
+      at += (uint32_t)__popcll(cbal[j]);
     }
   }
   __syncthreads();
@@ -189,12 +201,7 @@ __global__ void __launch_bounds__(kResThreads) select_resolve(DecodeParams p) {
     // segment offsets: exclusive prefix of the per-chunk candidate counts
     if (nch <= 64) {
       if (tid < 64) {
-        uint32_t inc = my_cnt;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint32_t y = __shfl_up(inc, o);
-          if (tid >= o) inc += y;
-        }
+        const uint32_t inc = wave_inclusive_scan(my_cnt);
         if (tid < nch) segoff[tid] = inc - my_cnt;
         if (tid == nch - 1) segoff[nch] = inc;
       }
