@@ -138,6 +138,11 @@ __device__ inline uint2 cand_at(const uint2* cand, const uint32_t* segoff, int n
 constexpr int kLdsBitmapWords = 16384;   // bitmaps up to 512K tokens are kept in LDS
 constexpr int kCandLds = 4096;           // candidates kept in LDS
 constexpr int kBmQuads = kLdsBitmapWords / 4 / kResThreads;   // 16-byte bitmap pieces per thread
+// Candidates loaded before their counts are known: the first kSpecCand of
+// each of the first kSpecChunks chunks (kResThreads / kSpecChunks threads per
+// chunk, two each).
+constexpr int kSpecChunks = 32, kSpecCand = 64;
+static_assert(kSpecChunks * kSpecCand == 2 * kResThreads, "two speculative candidates per thread");
 
 __global__ void __launch_bounds__(kResThreads) select_resolve(DecodeParams p) {
   __shared__ __align__(16) uint32_t h[kHistBins];
@@ -148,7 +153,7 @@ __global__ void __launch_bounds__(kResThreads) select_resolve(DecodeParams p) {
   __shared__ uint32_t segoff[kMaxSelChunks + 1];
   __shared__ __align__(16) uint32_t lbm[kLdsBitmapWords];
   __shared__ int sh_bin;
-  __shared__ uint32_t sh_need, sh_fin;
+  __shared__ uint32_t sh_need, sh_fin, sh_spill;
   static_assert(kMaxSelChunks <= kResThreads, "one chunk count per thread");
 
   const int tid = threadIdx.x;
@@ -172,6 +177,13 @@ __global__ void __launch_bounds__(kResThreads) select_resolve(DecodeParams p) {
   }
   uint32_t my_cnt = tid < p.cnt_stride - 2 ? cnts[tid] : 0u;
   const uint32_t need1 = cnts[p.cnt_stride - 1];
+  const int sp_c = tid / (kResThreads / kSpecChunks), sp_i = tid % (kResThreads / kSpecChunks);
+  uint2 spec[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int64_t at = (int64_t)sp_c * p.sel_chunk + sp_i + k * (kResThreads / kSpecChunks);
+    spec[k] = (sp_c < p.cnt_stride - 2 && at < p.max_seq) ? cand[at] : make_uint2(0u, 0u);
+  }
 
   const int seq = (int)(sk / p.hkv);
   const int64_t a = seq_at(p, seq);
@@ -198,38 +210,60 @@ __global__ void __launch_bounds__(kResThreads) select_resolve(DecodeParams p) {
     }
   }
   if (!all) {
-    // segment offsets: exclusive prefix of the per-chunk candidate counts
+    // segment offsets: exclusive prefix of the per-chunk candidate counts;
+    // sh_spill says whether some candidate lies outside the speculative loads
     if (nch <= 64) {
       if (tid < 64) {
         const uint32_t inc = wave_inclusive_scan(my_cnt);
         if (tid < nch) segoff[tid] = inc - my_cnt;
         if (tid == nch - 1) segoff[nch] = inc;
+        const uint64_t big = __ballot(my_cnt > (uint32_t)kSpecCand);
+        if (tid == 0) sh_spill = (big != 0 || nch > kSpecChunks) ? 1u : 0u;
       }
     } else {
       uint32_t tot;
       const uint32_t run = block_exclusive_scan<kResThreads>(my_cnt, scan_lds, tot);
       if (tid < nch) segoff[tid] = run;
-      if (tid == 0) segoff[nch] = tot;
+      if (tid == 0) {
+        segoff[nch] = tot;
+        sh_spill = 1u;
+      }
     }
     if (tid == 0) sh_fin = 0u;
     __syncthreads();
     const uint32_t ncand = segoff[nch];
     const bool cand_lds = ncand <= (uint32_t)kCandLds;
     // level 2: histogram of the candidates' middle 12 key bits (candidates
-    // are copied to LDS on the way); loads in groups of four
-    for (uint32_t j0 = tid; j0 < ncand; j0 += 4 * kResThreads) {
-      uint2 cv[4];
+    // are copied to LDS on the way)
+    if (!sh_spill) {
+      // every candidate is among the speculative loads (and fits in LDS)
+      const uint32_t cc = sp_c < nch ? segoff[sp_c + 1] - segoff[sp_c] : 0u;
+      const uint32_t o = sp_c < nch ? segoff[sp_c] : 0u;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t j = j0 + k * kResThreads;
-        cv[k] = j < ncand ? cand_at(cand, segoff, nch, p.sel_chunk, j) : make_uint2(0u, 0u);
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t i = sp_i + k * (kResThreads / kSpecChunks);
+        if (i < cc) {
+          cl[o + i] = spec[k];
+          atomicAdd(&h[(spec[k].x >> 8) & 0xFFFu], 1u);
+        }
       }
+    } else {
+      // candidate j found by a search over the segment offsets; loads in
+      // groups of four
+      for (uint32_t j0 = tid; j0 < ncand; j0 += 4 * kResThreads) {
+        uint2 cv[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t j = j0 + k * kResThreads;
-        if (j < ncand) {
-          if (cand_lds) cl[j] = cv[k];
-          atomicAdd(&h[(cv[k].x >> 8) & 0xFFFu], 1u);
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t j = j0 + k * kResThreads;
+          cv[k] = j < ncand ? cand_at(cand, segoff, nch, p.sel_chunk, j) : make_uint2(0u, 0u);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t j = j0 + k * kResThreads;
+          if (j < ncand) {
+            if (cand_lds) cl[j] = cv[k];
+            atomicAdd(&h[(cv[k].x >> 8) & 0xFFFu], 1u);
+          }
         }
       }
     }
