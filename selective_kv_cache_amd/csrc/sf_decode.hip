@@ -57,11 +57,11 @@ int32_t choose_split(int64_t total_tokens, int32_t n_kv_heads) {
   return s;
 }
 
-// Tokens per score work-group: about 1024 work-groups.
-int32_t choose_score_split(int64_t total_tokens, int32_t n_kv_heads) {
+// Tokens per score work-group: about `groups` work-groups.
+int32_t choose_score_split(int64_t total_tokens, int32_t n_kv_heads, int32_t groups) {
   const int64_t work = total_tokens * n_kv_heads;
   int32_t s = 256;
-  while (s < 4096 && work / s > 1024) s *= 2;
+  while (s < 16384 && work / s > groups) s *= 2;
   return s;
 }
 
@@ -148,7 +148,11 @@ extern "C" sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* a
       return SF_ERR_INVALID_ARG;
   }
   const int32_t split = choose_split(total, geom->n_kv_heads);
-  const int32_t score_split = choose_score_split(total, geom->n_kv_heads);
+  // the matrix-core score pass runs kScoreWaves wavefronts per work-group,
+  // the other 4: about 4096 wavefronts either way
+  const int32_t grp = geom->n_q_heads / geom->n_kv_heads;
+  const bool score_mfma = geom->base_bits == 2 && (grp == 1 || grp == 2 || grp == 4);
+  const int32_t score_split = choose_score_split(total, geom->n_kv_heads, score_mfma ? 4096 / kScoreWaves : 1024);
   const Carve c = carve(*geom, B, total, max_seq, a->top_t, part_bound(total, B, split, a->top_t));
   if (a->workspace_bytes < c.total) return SF_ERR_INVALID_ARG;
   if (max_seq / split + 1 + (a->top_t + kSelBlkTok - 1) / kSelBlkTok > kCombineMax) return SF_ERR_UNSUPPORTED;

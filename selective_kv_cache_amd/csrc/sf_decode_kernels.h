@@ -263,6 +263,7 @@ void launch_select(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvent
 bool launch_attend(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev = {});
 void launch_combine(const DecodeParams& p, hipStream_t st, KernelEvents ev = {});
 
+constexpr int kScoreWaves = 16;         // wavefronts per score work-group (matrix-core path)
 constexpr int kSelThreads = 512;
 constexpr int32_t kSelChunk = 4096;
 constexpr int32_t kMaxSelChunks = 512;   // longest sequence: kMaxSelChunks * kSelChunk tokens

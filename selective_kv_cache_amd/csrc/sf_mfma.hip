@@ -228,7 +228,7 @@ __device__ inline float lane_select(uint64_t mask, float yes, float no) {
 }
 
 // ---------------------------------------------------------------------------
-// Score pass: grid (n_score_split, hkv), 4 wavefronts.  Each wave streams
+// Score pass: grid (n_score_split, hkv), NW wavefronts.  Each wave streams
 // 32-token chunks (two logit tiles) of its split through an LDS ring; the
 // per-head logits go to the logits buffer for the attention pass, their
 // maximum over the group to the scores and the level-1 histogram.
@@ -257,11 +257,12 @@ __device__ inline float max_two_tiles(float x0, float x1) {
   return y;
 }
 
-template <int G>
-__global__ void __launch_bounds__(256) score_mfma(DecodeParams p) {
+template <int G, int NW>
+__global__ void __launch_bounds__(64 * NW) score_mfma(DecodeParams p) {
+  static_assert(NW >= 4, "waves 0-3 prepare the query digits");
   __shared__ QPrep qp;
   __shared__ uint32_t lhist[kHistBins];
-  __shared__ SStage ring[4][kSRing];
+  __shared__ SStage ring[NW][kSRing];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kvh = blockIdx.y;
@@ -273,20 +274,20 @@ __global__ void __launch_bounds__(256) score_mfma(DecodeParams p) {
   const int64_t t0 = (int64_t)kvh * p.cap + a + lo;            // first token row of the split
   const int nsp = (int)(hi - lo);
   const int nchunks = (nsp + 31) / 32;
-  const int nmine = nchunks > wid ? (nchunks - wid + 3) / 4 : 0;
-  // stage i <- chunk wid + 4i of the wave's own chunks: lane L loads half
+  const int nmine = nchunks > wid ? (nchunks - wid + NW - 1) / NW : 0;
+  // stage i <- chunk wid + NW i of the wave's own chunks: lane L loads half
   // L&1 of K row L/2 and scale word L; the resources end at the split's end
   // (tokens past it read as zeros)
   const rsrc_t rK = make_rsrc(p.kc + t0 * 32, (uint32_t)nsp * 32u);
   const rsrc_t rS = make_rsrc(p.ks + t0 * 2, (uint32_t)nsp * 8u);
   const uint32_t oK = 16u * (uint32_t)lane, oS = 4u * (uint32_t)lane;
   auto issue = [&](int i, SStage& st) {
-    const uint32_t c = (uint32_t)(wid + 4 * i);
+    const uint32_t c = (uint32_t)(wid + NW * i);
     bdma16(rK, oK, c * 1024u, st.k);
     bdma4(rS, oS, c * 256u, st.ks);
   };
   const bool hist = p.top_t > 0;   // no selection, no histogram
-  for (int i = tid; i < kHistBins; i += 256) lhist[i] = 0u;
+  for (int i = tid; i < kHistBins; i += 64 * NW) lhist[i] = 0u;
   static_assert(kSRing == 4, "the stream loop is unrolled by the ring depth");
   if (0 < nmine) issue(0, ring[wid][0]);
   if (1 < nmine) issue(1, ring[wid][1]);
@@ -313,7 +314,7 @@ __global__ void __launch_bounds__(256) score_mfma(DecodeParams p) {
     // this wave's loads complete in order: stage i is in once no more than
     // the stages issued after it are outstanding (stores only add to the count)
     wait_stages<kSRingLoads>(min(kSRing - 1, nmine - 1 - i));
-    const int c = wid + 4 * i;
+    const int c = wid + NW * i;
     uint64_t kw[2], ks[2];
     asm volatile(
         "ds_read_b64 %0, %4 offset:%6\n\t"
@@ -359,7 +360,7 @@ __global__ void __launch_bounds__(256) score_mfma(DecodeParams p) {
   if (!hist) return;
   __syncthreads();
   uint32_t* gh = p.hist + ((int64_t)seq * p.hkv + kvh) * kHistBins;   // level-1 histogram
-  for (int i = tid; i < kHistBins; i += 256) {
+  for (int i = tid; i < kHistBins; i += 64 * NW) {
     const uint32_t c = lhist[i];
     if (c) atomicAdd(&gh[i], c);
   }
@@ -692,9 +693,9 @@ __global__ void __launch_bounds__(256) attend_mfma(DecodeParams p) {
 bool launch_score_mfma(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev) {
   if (p.b != 2) return false;
   switch (p.grp) {
-    case 1: sf_launch(score_mfma<1>, grid, dim3(256), st, ev, p); return true;
-    case 2: sf_launch(score_mfma<2>, grid, dim3(256), st, ev, p); return true;
-    case 4: sf_launch(score_mfma<4>, grid, dim3(256), st, ev, p); return true;
+    case 1: sf_launch(score_mfma<1, kScoreWaves>, grid, dim3(64 * kScoreWaves), st, ev, p); return true;
+    case 2: sf_launch(score_mfma<2, kScoreWaves>, grid, dim3(64 * kScoreWaves), st, ev, p); return true;
+    case 4: sf_launch(score_mfma<4, kScoreWaves>, grid, dim3(64 * kScoreWaves), st, ev, p); return true;
   }
   return false;
 }
