@@ -4,7 +4,7 @@
 // paragraph "Which tiles count ...": every token takes part in attention;
 // unselected ones at the low-bit base value.  The work-groups of this kernel
 // are of two kinds:
-//   blockIdx.x <  n_sel_blk : refined terms of kSelBlkTok selected tokens
+//   blockIdx.x <  n_sel_blk : refined terms of p.sel_blk_tok selected tokens
 //                             (selected_block, sf_attend_common.h);
 //   blockIdx.x >= n_sel_blk : one split of tokens at base precision, with the
 //                             selected tokens left out.
@@ -150,14 +150,14 @@ __device__ inline void base_split_valu(const DecodeParams& p, int split, int kvh
   }
   __syncthreads();
   float* part = p.part + ((int64_t)kvh * (p.n_sel_blk + p.n_split) + p.n_sel_blk + split) * G * kPartStride;
-  write_partial<G>(part, s.mw, s.lw, s.accw);
+  write_partial<G, 4>(part, s.mw, s.lw, s.accw);
 }
 
 template <int BB, int G>
 __global__ void __launch_bounds__(256) attend_valu(DecodeParams p) {
-  __shared__ __align__(16) uint8_t smem[cmax(sizeof(SelLds<BB, G>), sizeof(ValuLds<BB, G>))];
+  __shared__ __align__(16) uint8_t smem[cmax(sizeof(SelLds<BB, G, 4>), sizeof(ValuLds<BB, G>))];
   if ((int)blockIdx.x < p.n_sel_blk)
-    selected_block<BB, G>(p, blockIdx.x, blockIdx.y, smem);
+    selected_block<BB, G, 4>(p, blockIdx.x, blockIdx.y, smem);
   else
     base_split_valu<BB, G>(p, blockIdx.x - p.n_sel_blk, blockIdx.y, smem);
 }
@@ -177,11 +177,11 @@ __global__ void __launch_bounds__(256) combine(DecodeParams p) {
   for (int i = 0; i < s; ++i) {
     const int64_t n = seq_at(p, i + 1) - seq_at(p, i);
     bb += (int)((n + p.split - 1) / p.split);
-    if (p.use_refine) sb += (int)(((n < p.top_t ? n : p.top_t) + kSelBlkTok - 1) / kSelBlkTok);
+    if (p.use_refine) sb += (int)(((n < p.top_t ? n : p.top_t) + p.sel_blk_tok - 1) / p.sel_blk_tok);
   }
   const int64_t n = seq_at(p, s + 1) - seq_at(p, s);
   const int nb = (int)((n + p.split - 1) / p.split);
-  const int ns = p.use_refine ? (int)(((n < p.top_t ? n : p.top_t) + kSelBlkTok - 1) / kSelBlkTok) : 0;
+  const int ns = p.use_refine ? (int)(((n < p.top_t ? n : p.top_t) + p.sel_blk_tok - 1) / p.sel_blk_tok) : 0;
   const int64_t stride = (int64_t)p.grp * kPartStride;
   const float* base = p.part + (int64_t)kvh * (p.n_sel_blk + p.n_split) * stride + hg * kPartStride;
   const int np = ns + nb;

@@ -47,19 +47,19 @@ __device__ inline void quarter_dots(const uint32_t* kb, const uint32_t* kr, cons
   }
 }
 
-// Merge the four wavefronts' (m, l, acc) of a 256-thread work-group into one
-// partial.  mw/lw [4][G], accw [4][R >= G][D] in LDS (rows past G unused);
-// called by all 256 threads after a barrier.
-template <int G, int R = G>
+// Merge the NW wavefronts' (m, l, acc) of a work-group into one partial.
+// mw/lw [NW][G], accw [NW][R >= G][D] in LDS (rows past G unused); called by
+// all 64 NW threads after a barrier.
+template <int G, int NW, int R = G>
 __device__ inline void write_partial(float* part, const float (*mw)[G], const float (*lw)[G],
                                      const float (*accw)[R][kHeadDim]) {
-  for (int i = threadIdx.x; i < G * kHeadDim; i += 256) {
+  for (int i = threadIdx.x; i < G * kHeadDim; i += 64 * NW) {
     const int h = i / kHeadDim, d = i % kHeadDim;
     float M = -INFINITY;
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, mw[w][h]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, mw[w][h]);
     float A = 0.f, L = 0.f;
     if (M != -INFINITY) {
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < NW; ++w) {
         if (mw[w][h] == -INFINITY) continue;
         const float e = expf(mw[w][h] - M);
         A += e * accw[w][h][d];
@@ -74,39 +74,39 @@ __device__ inline void write_partial(float* part, const float (*mw)[G], const fl
   }
 }
 
-// Selected tokens of one (sequence, KV head): kSelBlkTok of them per
-// work-group, 4 wavefronts x 16 tokens, 4 lanes (a quarter of head_dim each)
-// per token.  Writes the partial of the refined terms.
-template <int BB, int G>
+// Selected tokens of one (sequence, KV head): 16 NW of them per work-group
+// (p.sel_blk_tok), NW wavefronts x 16 tokens, 4 lanes (a quarter of head_dim
+// each) per token.  Writes the partial of the refined terms.
+template <int BB, int G, int NW>
 struct SelLds {
   float qs[G][kHeadDim];
   float qsum[G];
-  uint32_t vt[4][16][4 * BB + 1];
-  uint32_t vr[4][16][33];
-  float2 vsc[4][16];
-  float wt[4][G][16];
-  float mred[4][G], mall[4][G], lw[4][G];
-  float accw[4][G][kHeadDim];
+  uint32_t vt[NW][16][4 * BB + 1];
+  uint32_t vr[NW][16][33];
+  float2 vsc[NW][16];
+  float wt[NW][G][16];
+  float mred[NW][G], mall[NW][G], lw[NW][G];
+  float accw[NW][G][kHeadDim];
 };
 
-template <int BB, int G>
+template <int BB, int G, int NW>
 __device__ inline void selected_block(const DecodeParams& p, int blk, int kvh, uint8_t* smem) {
   constexpr int W = 4 * BB;
-  using Lds = SelLds<BB, G>;
+  using Lds = SelLds<BB, G, NW>;
   Lds& s = *reinterpret_cast<Lds*>(smem);
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int tk = lane >> 2, qd = lane & 3;
   int64_t lo, hi;
   int first;
-  const int seq = locate_unit(p, kSelBlkTok, blk, true, lo, hi, first);
+  const int seq = locate_unit(p, 16 * NW, blk, true, lo, hi, first);
   const int64_t a = seq_at(p, seq);
   const int64_t sk = (int64_t)seq * p.hkv + kvh;
   const int r = p.r;
   const float sub = __builtin_ldexpf(1.0f, -r);
   const uint32_t rmask = (1u << r) - 1u;
 
-  for (int i = tid; i < G * kHeadDim; i += 256)
+  for (int i = tid; i < G * kHeadDim; i += 64 * NW)
     s.qs[i / kHeadDim][i % kHeadDim] = p.q[((int64_t)seq * p.hq + kvh * G) * kHeadDim + i];
   __syncthreads();
   if (tid < G) {
@@ -181,7 +181,9 @@ __device__ inline void selected_block(const DecodeParams& p, int blk, int kvh, u
   float acc[G][2];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float M = fmaxf(fmaxf(s.mred[0][h], s.mred[1][h]), fmaxf(s.mred[2][h], s.mred[3][h]));
+    float M = s.mred[0][h];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, s.mred[w][h]);
     const float e = valid ? expf(lr[h] - M) : 0.f;
     if (qd == 0) s.wt[wid][h][tk] = e;
     const float ls = wave_sum(qd == 0 ? e : 0.f);
@@ -218,7 +220,7 @@ __device__ inline void selected_block(const DecodeParams& p, int blk, int kvh, u
   }
   __syncthreads();
   float* part = p.part + ((int64_t)kvh * (p.n_sel_blk + p.n_split) + blk) * G * kPartStride;
-  write_partial<G>(part, s.mall, s.lw, s.accw);
+  write_partial<G, NW>(part, s.mall, s.lw, s.accw);
 }
 
 }  // namespace sfk

@@ -48,13 +48,26 @@ __global__ void zero_words(uint32_t* p, int64_t n) {
 // ---------------------------------------------------------------------------
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Tokens per attention work-group: about 512 work-groups over the chip (a
-// few per CU), few enough partials to keep the combine small.
-int32_t choose_split(int64_t total_tokens, int32_t n_kv_heads) {
+// Tokens per attention work-group of base tokens: about `groups` of them
+// over the chip (a few wavefronts per SIMD), few enough partials to keep the
+// combine small.  At most 4096 (the base passes' selection-word layout).
+int32_t choose_split(int64_t total_tokens, int32_t n_kv_heads, int32_t groups) {
   const int64_t work = total_tokens * n_kv_heads;
   int32_t s = 256;
-  while (s < 4096 && work / s > 512) s *= 2;
+  while (s < 4096 && work / s > groups) s *= 2;
   return s;
+}
+
+// The attention pass's shape: the matrix-core form (2-bit base codes, GQA
+// groups of 1, 2 or 4) runs kAttendWaves wavefronts per work-group, the VALU
+// form 4; about 2048 wavefronts of base tokens either way.
+struct AttendShape {
+  int32_t split, sel_blk_tok;
+};
+static AttendShape attend_shape(const sf_geom& g, int64_t total_tokens) {
+  const int32_t grp = g.n_q_heads / g.n_kv_heads;
+  const int waves = (g.base_bits == 2 && (grp == 1 || grp == 2 || grp == 4)) ? kAttendWaves : 4;
+  return AttendShape{choose_split(total_tokens, g.n_kv_heads, 2048 / waves), 16 * waves};
 }
 
 // Tokens per score work-group: about `groups` work-groups.
@@ -112,7 +125,8 @@ extern "C" sf_status sf_decode_workspace_size(const sf_geom* geom, int32_t batch
       max_seq_tokens > total_tokens)
     return SF_ERR_INVALID_ARG;
   if (max_seq_tokens > (int64_t)kMaxSelChunks * kSelChunk) return SF_ERR_UNSUPPORTED;
-  const int32_t split = choose_split(total_tokens, geom->n_kv_heads);
+  // the bound of the form with the most partials: smallest splits, 4 waves
+  const int32_t split = choose_split(total_tokens, geom->n_kv_heads, 512);
   *bytes = carve(*geom, batch, total_tokens, max_seq_tokens, top_t, part_bound(total_tokens, batch, split, top_t)).total;
   return SF_OK;
 }
@@ -147,7 +161,8 @@ extern "C" sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* a
     if (st->tier == SF_TIER_HOST_PINNED && (B > st->max_seqs || a->top_t > st->slots))
       return SF_ERR_INVALID_ARG;
   }
-  const int32_t split = choose_split(total, geom->n_kv_heads);
+  const AttendShape ash = attend_shape(*geom, total);
+  const int32_t split = ash.split;
   // the matrix-core score pass runs kScoreWaves wavefronts per work-group,
   // the other 4: about 4096 wavefronts either way
   const int32_t grp = geom->n_q_heads / geom->n_kv_heads;
@@ -155,7 +170,7 @@ extern "C" sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* a
   const int32_t score_split = choose_score_split(total, geom->n_kv_heads, score_mfma ? 4096 / kScoreWaves : 1024);
   const Carve c = carve(*geom, B, total, max_seq, a->top_t, part_bound(total, B, split, a->top_t));
   if (a->workspace_bytes < c.total) return SF_ERR_INVALID_ARG;
-  if (max_seq / split + 1 + (a->top_t + kSelBlkTok - 1) / kSelBlkTok > kCombineMax) return SF_ERR_UNSUPPORTED;
+  if (max_seq / split + 1 + (a->top_t + ash.sel_blk_tok - 1) / ash.sel_blk_tok > kCombineMax) return SF_ERR_UNSUPPORTED;
 
   int32_t n_split = 0, n_score = 0, n_sel = 0, n_sel_blk = 0;
   for (int i = 0; i < B; ++i) {
@@ -163,7 +178,7 @@ extern "C" sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* a
     n_split += (int32_t)((n + split - 1) / split);
     n_score += (int32_t)((n + score_split - 1) / score_split);
     n_sel += (int32_t)((n + kSelChunk - 1) / kSelChunk);
-    if (refine) n_sel_blk += (int32_t)((std::min<int64_t>(n, a->top_t) + kSelBlkTok - 1) / kSelBlkTok);
+    if (refine) n_sel_blk += (int32_t)((std::min<int64_t>(n, a->top_t) + ash.sel_blk_tok - 1) / ash.sel_blk_tok);
   }
 
   uint8_t* ws = static_cast<uint8_t*>(a->workspace);
@@ -183,6 +198,7 @@ extern "C" sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* a
   p.bm_words = (int32_t)(((max_seq + kSelThreads - 1) / kSelThreads) * (kSelThreads / 32));
   p.use_refine = refine ? 1 : 0;
   p.n_sel_blk = n_sel_blk;
+  p.sel_blk_tok = ash.sel_blk_tok;
   p.cnt_stride = (int32_t)((max_seq + kSelChunk - 1) / kSelChunk) + 2;   // + level-1 boundary
   p.cap = a->cap;
   p.ntot = total;

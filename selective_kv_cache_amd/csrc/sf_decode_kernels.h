@@ -12,7 +12,8 @@ struct DecodeParams {
   int32_t score_split, split, sel_chunk;   // tokens per score / attention / selection work-group
   int32_t n_score_split, n_split, bm_words;
   int32_t use_refine;                      // selected rows take their refinement codes
-  int32_t n_sel_blk;                       // work-groups of selected tokens (kSelBlkTok each)
+  int32_t n_sel_blk;                       // work-groups of selected tokens (sel_blk_tok each)
+  int32_t sel_blk_tok;                     // selected tokens per attention work-group: 16 per wavefront
   int32_t cnt_stride;                      // selection chunks per sequence (max) + 2
   int64_t cap, ntot, off0, max_seq;
   const int64_t* seq_off;
@@ -267,7 +268,8 @@ constexpr int kScoreWaves = 16;         // wavefronts per score work-group (matr
 constexpr int kSelThreads = 512;
 constexpr int32_t kSelChunk = 4096;
 constexpr int32_t kMaxSelChunks = 512;   // longest sequence: kMaxSelChunks * kSelChunk tokens
-constexpr int32_t kSelBlkTok = 64;     // selected tokens per attention work-group
+constexpr int32_t kSelBlkTok = 64;     // selected tokens per attention work-group of 4 wavefronts (the fewest)
+constexpr int kAttendWaves = 4;         // wavefronts per attention work-group (matrix-core path)
 constexpr int kCombineMax = 2048;      // partials per (sequence, query head)
 
 }  // namespace sfk

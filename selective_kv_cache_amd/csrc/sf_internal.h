@@ -29,7 +29,7 @@ struct Carve {
   size_t scores, logits, hist, counters, cand, bitmap, sel, part, miss, total;
 };
 
-int32_t choose_split(int64_t total_tokens, int32_t n_kv_heads);
+int32_t choose_split(int64_t total_tokens, int32_t n_kv_heads, int32_t groups);
 int32_t choose_score_split(int64_t total_tokens, int32_t n_kv_heads, int32_t groups);
 Carve carve(const sf_geom& g, int32_t batch, int64_t total_tokens, int64_t max_seq_tokens,
             int32_t top_t, int32_t n_split_bound);

@@ -382,14 +382,14 @@ struct Stage {
   float2 vs[32];
 };
 
-template <int G>
+template <int G, int NW>
 struct MfmaLds {
-  alignas(16) _Float16 wt[4][2 * G][32];   // per wave: P.V weights [column][kappa]: hi parts, then lo parts
-  alignas(16) _Float16 wzero[8];           // weight columns >= 2G read zeros
-  float mw[4][G], lw[4][G];
+  alignas(16) _Float16 wt[NW][2 * G][32];   // per wave: P.V weights [column][kappa]: hi parts, then lo parts
+  alignas(16) _Float16 wzero[8];            // weight columns >= 2G read zeros
+  float mw[NW][G], lw[NW][G];
   union {
-    Stage<G> ring[4][kRing];
-    float accw[4][2 * G][kHeadDim];        // after the stream: per-wave P.V, hi and lo columns
+    Stage<G> ring[NW][kRing];
+    float accw[NW][2 * G][kHeadDim];        // after the stream: per-wave P.V, hi and lo columns
   } u;
 };
 
@@ -445,9 +445,9 @@ __device__ inline void read_stage(uint32_t aL, uint32_t aS, const uint32_t (&aV)
       : "memory");
 }
 
-template <int G>
+template <int G, int NW>
 __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh, uint8_t* smem) {
-  using Lds = MfmaLds<G>;
+  using Lds = MfmaLds<G, NW>;
   using St = Stage<G>;
   Lds& s = *reinterpret_cast<Lds*>(smem);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -461,9 +461,9 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   const int64_t t0 = (int64_t)kvh * p.cap + a + lo;            // first token row of the split
   const int nsp = (int)(hi - lo);                               // tokens of the split (<= 4096)
   const int nchunks = (nsp + 31) / 32;
-  const int nmine = nchunks > wid ? (nchunks - wid + 3) / 4 : 0;   // chunks wid, wid+4, ...
+  const int nmine = nchunks > wid ? (nchunks - wid + NW - 1) / NW : 0;   // chunks wid, wid+NW, ...
 
-  // Stage i of this wave <- chunk wid + 4*i.  Lane L loads the scale word L
+  // Stage i of this wave <- chunk wid + NW*i.  Lane L loads the scale word L
   // of the chunk (token L/2), lanes L < 8G the logits' bytes [16L, 16L+16),
   // and half L&1 of V row (L/2) ^ ((L/8) & 3): row r of the chunk sits at
   // stage row r ^ ((r/4) & 3), so that the four rows one P.V read takes
@@ -475,7 +475,7 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   const uint32_t oV = (uint32_t)(((lane >> 1) ^ ((lane >> 3) & 3)) * 32 + 16 * (lane & 1));
   const uint32_t oS = 4u * (uint32_t)lane, oL = 16u * (uint32_t)lane;
   auto issue = [&](int i, St& st) {
-    const uint32_t c = (uint32_t)(wid + 4 * i);
+    const uint32_t c = (uint32_t)(wid + NW * i);
     if (lane < 8 * G) bdma16(rL, oL, c * (32u * G * 4u), st.lg);
     bdma16(rV, oV, c * 1024u, st.v);
     bdma4(rS, oS, c * 256u, st.vs);
@@ -538,7 +538,7 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
     // this wave's loads complete in order: stage i is in once no more than
     // the stages issued after it are outstanding
     wait_stages<kRingLoads>(min(kRing - 1, nmine - 1 - i));
-    const int c = wid + 4 * i;
+    const int c = wid + NW * i;
     const int rem = nsp - 32 * c;                 // tokens of this chunk inside the split
     // the chunk's tokens that take part (unmarked, inside the split) as lane
     // masks: bit l of mk[j] for lane l = (row, t): token 16 j + t
@@ -658,15 +658,15 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   __syncthreads();
   // the work-group's partial: the waves' (m, l, acc) merged, hi + lo columns
   float* part = p.part + ((int64_t)kvh * (p.n_sel_blk + p.n_split) + p.n_sel_blk + split) * G * kPartStride;
-  for (int i = tid; i < G * kHeadDim; i += 256) {
+  for (int i = tid; i < G * kHeadDim; i += 64 * NW) {
     const int h = i / kHeadDim, d = i % kHeadDim;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, s.mw[w][h]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, s.mw[w][h]);
     float A = 0.f, L = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < NW; ++w) {
         if (s.mw[w][h] == -INFINITY) continue;
         const float e = expf(s.mw[w][h] - M);
         A += e * (s.u.accw[w][h][d] + s.u.accw[w][G + h][d]);
@@ -681,13 +681,13 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   }
 }
 
-template <int G>
-__global__ void __launch_bounds__(256) attend_mfma(DecodeParams p) {
-  __shared__ __align__(16) uint8_t smem[cmax(sizeof(SelLds<2, G>), sizeof(MfmaLds<G>))];
+template <int G, int NW>
+__global__ void __launch_bounds__(64 * NW) attend_mfma(DecodeParams p) {
+  __shared__ __align__(16) uint8_t smem[cmax(sizeof(SelLds<2, G, NW>), sizeof(MfmaLds<G, NW>))];
   if ((int)blockIdx.x < p.n_sel_blk)
-    selected_block<2, G>(p, blockIdx.x, blockIdx.y, smem);
+    selected_block<2, G, NW>(p, blockIdx.x, blockIdx.y, smem);
   else
-    base_split_mfma<G>(p, blockIdx.x - p.n_sel_blk, blockIdx.y, smem);
+    base_split_mfma<G, NW>(p, blockIdx.x - p.n_sel_blk, blockIdx.y, smem);
 }
 
 bool launch_score_mfma(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev) {
@@ -703,9 +703,9 @@ bool launch_score_mfma(const DecodeParams& p, dim3 grid, hipStream_t st, KernelE
 bool launch_attend_mfma(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev) {
   if (p.b != 2) return false;
   switch (p.grp) {
-    case 1: sf_launch(attend_mfma<1>, grid, dim3(256), st, ev, p); return true;
-    case 2: sf_launch(attend_mfma<2>, grid, dim3(256), st, ev, p); return true;
-    case 4: sf_launch(attend_mfma<4>, grid, dim3(256), st, ev, p); return true;
+    case 1: sf_launch(attend_mfma<1, kAttendWaves>, grid, dim3(64 * kAttendWaves), st, ev, p); return true;
+    case 2: sf_launch(attend_mfma<2, kAttendWaves>, grid, dim3(64 * kAttendWaves), st, ev, p); return true;
+    case 4: sf_launch(attend_mfma<4, kAttendWaves>, grid, dim3(64 * kAttendWaves), st, ev, p); return true;
   }
   return false;
 }
