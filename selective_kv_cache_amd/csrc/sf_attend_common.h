@@ -28,12 +28,13 @@ __device__ inline const uint32_t* refine_row(const DecodeParams& p, int64_t sk, 
 }
 
 // Dot products of one quarter of head_dim (32 elements) with the G query
-// heads: base codes (BB bits) and refinement codes (R bits).
+// heads: base codes (BB bits), refinement codes (R bits), and the sum of the
+// query elements.
 template <int BB, int R, int G>
 __device__ inline void quarter_dots(const uint32_t* kb, const uint32_t* kr, const float* qs, int qd, float* dc,
-                                    float* ds) {
+                                    float* ds, float* dq) {
 #pragma unroll
-  for (int h = 0; h < G; ++h) dc[h] = ds[h] = 0.f;
+  for (int h = 0; h < G; ++h) dc[h] = ds[h] = dq[h] = 0.f;
 #pragma unroll
   for (int d = 0; d < 32; ++d) {
     const float c = (float)code_at<BB>(kb, d);
@@ -43,8 +44,15 @@ __device__ inline void quarter_dots(const uint32_t* kb, const uint32_t* kr, cons
       const float qv = qs[h * kHeadDim + qd * 32 + d];
       dc[h] = fmaf(qv, c, dc[h]);
       ds[h] = fmaf(qv, s, ds[h]);
+      dq[h] += qv;
     }
   }
+}
+
+// Sum over the four lanes of a quad (DPP quad permutes).
+__device__ inline float quad_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
 }
 
 // Merge the NW wavefronts' (m, l, acc) of a work-group into one partial.
@@ -80,7 +88,6 @@ __device__ inline void write_partial(float* part, const float (*mw)[G], const fl
 template <int BB, int G, int NW>
 struct SelLds {
   float qs[G][kHeadDim];
-  float qsum[G];
   uint32_t vt[NW][16][4 * BB + 1];
   uint32_t vr[NW][16][33];
   float2 vsc[NW][16];
@@ -106,73 +113,71 @@ __device__ inline void selected_block(const DecodeParams& p, int blk, int kvh, u
   const float sub = __builtin_ldexpf(1.0f, -r);
   const uint32_t rmask = (1u << r) - 1u;
 
+  // the query and the token's index, then every row of the token at once:
+  // K and V codes, their refinement rows and scales (two dependent memory
+  // round trips in all)
   for (int i = tid; i < G * kHeadDim; i += 64 * NW)
     s.qs[i / kHeadDim][i % kHeadDim] = p.q[((int64_t)seq * p.hq + kvh * G) * kHeadDim + i];
-  __syncthreads();
-  if (tid < G) {
-    float acc = 0.f;
-    for (int d = 0; d < kHeadDim; ++d) acc += s.qs[tid][d];
-    s.qsum[tid] = acc;
-  }
   const int64_t j = lo + wid * 16 + tk;
   const bool valid = j < hi;
   const int64_t tok = valid ? a + p.sel[sk * p.top_t + j] : 0;
-  uint32_t kb[BB], kr[9];
-  float2 ksc = make_float2(0.f, 0.f);
+  uint32_t kb[BB], kr[9], vb[BB], vr[8];
+  float2 ksc = make_float2(0.f, 0.f), vsc = make_float2(0.f, 0.f);
 #pragma unroll
-  for (int i = 0; i < BB; ++i) kb[i] = 0u;
+  for (int i = 0; i < BB; ++i) kb[i] = vb[i] = 0u;
 #pragma unroll
   for (int i = 0; i < 9; ++i) kr[i] = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) vr[i] = 0u;
   if (valid) {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(p.kc + ((int64_t)kvh * p.cap + tok) * (16 * BB)) + qd * BB;
+    const int64_t row = (int64_t)kvh * p.cap + tok;
+    const uint32_t* srck = reinterpret_cast<const uint32_t*>(p.kc + row * (16 * BB)) + qd * BB;
+    const uint32_t* srcv = reinterpret_cast<const uint32_t*>(p.vc + row * (16 * BB)) + qd * BB;
+    const uint32_t* rk = refine_row(p, sk, kvh, tok, 0) + qd * r;
+    const uint32_t* rv = refine_row(p, sk, kvh, tok, 1) + qd * r;
 #pragma unroll
-    for (int i = 0; i < BB; ++i) kb[i] = src[i];
-    const uint32_t* rs = refine_row(p, sk, kvh, tok, 0) + qd * r;
+    for (int i = 0; i < BB; ++i) {
+      kb[i] = srck[i];
+      vb[i] = srcv[i];
+    }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) kr[i] = i < r ? rs[i] : 0u;
-    ksc = reinterpret_cast<const float2*>(p.ks)[(int64_t)kvh * p.cap + tok];
+    for (int i = 0; i < 8; ++i) {
+      kr[i] = i < r ? rk[i] : 0u;
+      vr[i] = i < r ? rv[i] : 0u;
+    }
+    ksc = reinterpret_cast<const float2*>(p.ks)[row];
+    vsc = reinterpret_cast<const float2*>(p.vs)[row];
   }
   __syncthreads();
-  float dc[G], ds[G];
+  float dc[G], ds[G], dq[G];
   switch (r) {
-    case 1: quarter_dots<BB, 1, G>(kb, kr, &s.qs[0][0], qd, dc, ds); break;
-    case 2: quarter_dots<BB, 2, G>(kb, kr, &s.qs[0][0], qd, dc, ds); break;
-    case 3: quarter_dots<BB, 3, G>(kb, kr, &s.qs[0][0], qd, dc, ds); break;
-    case 4: quarter_dots<BB, 4, G>(kb, kr, &s.qs[0][0], qd, dc, ds); break;
-    case 5: quarter_dots<BB, 5, G>(kb, kr, &s.qs[0][0], qd, dc, ds); break;
-    case 6: quarter_dots<BB, 6, G>(kb, kr, &s.qs[0][0], qd, dc, ds); break;
-    case 7: quarter_dots<BB, 7, G>(kb, kr, &s.qs[0][0], qd, dc, ds); break;
-    default: quarter_dots<BB, 8, G>(kb, kr, &s.qs[0][0], qd, dc, ds); break;
+    case 1: quarter_dots<BB, 1, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
+    case 2: quarter_dots<BB, 2, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
+    case 3: quarter_dots<BB, 3, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
+    case 4: quarter_dots<BB, 4, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
+    case 5: quarter_dots<BB, 5, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
+    case 6: quarter_dots<BB, 6, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
+    case 7: quarter_dots<BB, 7, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
+    default: quarter_dots<BB, 8, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
   }
   float lr[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    dc[h] += __shfl_xor(dc[h], 1);
-    dc[h] += __shfl_xor(dc[h], 2);
-    ds[h] += __shfl_xor(ds[h], 1);
-    ds[h] += __shfl_xor(ds[h], 2);
-    lr[h] = (ksc.x * s.qsum[h] + ksc.y * (dc[h] + (ds[h] + 0.5f * s.qsum[h]) * sub)) * kRsqrtD;
-    const float mv = wave_max(valid ? lr[h] : -INFINITY);
+    const float qsum = quad_sum(dq[h]);
+    lr[h] = (ksc.x * qsum + ksc.y * (quad_sum(dc[h]) + (quad_sum(ds[h]) + 0.5f * qsum) * sub)) * kRsqrtD;
+    const float mv = wave_max_dpp(valid ? lr[h] : -INFINITY);
     if (lane == 0) s.mred[wid][h] = mv;
   }
   {
     uint32_t* dstb = &s.vt[wid][tk][qd * BB];
     uint32_t* dstr = &s.vr[wid][tk][qd * r];
-    if (valid) {
-      const uint32_t* src =
-          reinterpret_cast<const uint32_t*>(p.vc + ((int64_t)kvh * p.cap + tok) * (16 * BB)) + qd * BB;
 #pragma unroll
-      for (int i = 0; i < BB; ++i) dstb[i] = src[i];
-      const uint32_t* rs = refine_row(p, sk, kvh, tok, 1) + qd * r;
-      for (int i = 0; i < r; ++i) dstr[i] = rs[i];
-      if (qd == 0) s.vsc[wid][tk] = reinterpret_cast<const float2*>(p.vs)[(int64_t)kvh * p.cap + tok];
-    } else {
+    for (int i = 0; i < BB; ++i) dstb[i] = vb[i];
 #pragma unroll
-      for (int i = 0; i < BB; ++i) dstb[i] = 0u;
-      for (int i = 0; i < r; ++i) dstr[i] = 0u;
-      if (qd == 0) s.vsc[wid][tk] = make_float2(0.f, 0.f);
-    }
+    for (int i = 0; i < 8; ++i)
+      if (i < r) dstr[i] = vr[i];
     if (qd == 0) {
+      s.vsc[wid][tk] = vsc;
       s.vt[wid][tk][W] = 0u;
       s.vr[wid][tk][4 * r] = 0u;
     }
@@ -186,7 +191,7 @@ __device__ inline void selected_block(const DecodeParams& p, int blk, int kvh, u
     for (int w = 1; w < NW; ++w) M = fmaxf(M, s.mred[w][h]);
     const float e = valid ? expf(lr[h] - M) : 0.f;
     if (qd == 0) s.wt[wid][h][tk] = e;
-    const float ls = wave_sum(qd == 0 ? e : 0.f);
+    const float ls = wave_sum_dpp(qd == 0 ? e : 0.f);
     if (lane == 0) {
       s.lw[wid][h] = ls;
       s.mall[wid][h] = M;       // all waves share the work-group maximum

@@ -219,6 +219,22 @@ __device__ inline void bdma4(rsrc_t r, uint32_t voff, uint32_t soff, void* l) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t)l, 4, voff, soff, 0, 0);
 }
 
+// Issue priority by progress: a wavefront with more of its stream left gets
+// a higher priority (s_setprio 0-3), so that the work-groups sharing a CU
+// finish together instead of in dispatch order (the arbiter otherwise
+// favours the oldest wavefronts).  `left` and `total` are wave-uniform.
+__device__ inline void progress_priority(int left, int total) {
+  const int q = (4 * left) / total;
+  if (q >= 3)
+    __builtin_amdgcn_s_setprio(3);
+  else if (q == 2)
+    __builtin_amdgcn_s_setprio(2);
+  else if (q == 1)
+    __builtin_amdgcn_s_setprio(1);
+  else
+    __builtin_amdgcn_s_setprio(0);
+}
+
 // v_cndmask with a wave-uniform 64-bit lane mask (SGPR pair): lane l takes
 // yes where bit l of mask is set, else no.
 __device__ inline float lane_select(uint64_t mask, float yes, float no) {
@@ -350,11 +366,13 @@ __global__ void __launch_bounds__(64 * NW) score_mfma(DecodeParams p) {
     }
   };
   for (int i = 0; i < nmine; i += 4) {
+    progress_priority(nmine - i, nmine);
     body(std::integral_constant<int, 0>{}, i);
     if (i + 1 < nmine) body(std::integral_constant<int, 1>{}, i + 1);
     if (i + 2 < nmine) body(std::integral_constant<int, 2>{}, i + 2);
     if (i + 3 < nmine) body(std::integral_constant<int, 3>{}, i + 3);
   }
+  __builtin_amdgcn_s_setprio(0);
   // the histogram adds (asm, not waited for) complete before the barrier
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   if (!hist) return;
@@ -389,7 +407,8 @@ struct MfmaLds {
   float mw[NW][G], lw[NW][G];
   union {
     Stage<G> ring[NW][kRing];
-    float accw[NW][2 * G][kHeadDim];        // after the stream: per-wave P.V, hi and lo columns
+    float accw[NW][2 * G][kHeadDim + 1];    // after the stream: per-wave P.V, hi and lo columns
+                                            // (rows padded by a word: the 16 columns one write spans hit different banks)
   } u;
 };
 
@@ -624,11 +643,13 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
     }
   };
   for (int i = 0; i < nmine; i += 4) {
+    progress_priority(nmine - i, nmine);
     body(std::integral_constant<int, 0>{}, i);
     if (i + 1 < nmine) body(std::integral_constant<int, 1>{}, i + 1);
     if (i + 2 < nmine) body(std::integral_constant<int, 2>{}, i + 2);
     if (i + 3 < nmine) body(std::integral_constant<int, 3>{}, i + 3);
   }
+  __builtin_amdgcn_s_setprio(0);
   // the ring is reused below: no load of this wave may still be landing, and
   // every wave must be done with its stages
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
