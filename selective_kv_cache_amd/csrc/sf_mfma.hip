@@ -163,18 +163,32 @@ __device__ inline uint32_t lds_addr(const void* l) {
 }
 
 // Wait until at most `ahead` stages of PER direct loads each are still in
-// flight (a wave's vector loads complete in order).  `ahead` is wave-uniform
-// and at most 3.
-template <int PER>
+// flight (a wave's vector loads complete in order).  `ahead` is wave-uniform;
+// A is its largest value.
+template <int PER, int A>
 __device__ inline void wait_stages(int ahead) {
-  if (ahead >= 3)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * PER) : "memory");
-  else if (ahead == 2)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PER) : "memory");
-  else if (ahead == 1)
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER) : "memory");
-  else
+  static_assert(A * PER < 64, "vmcnt holds 6 bits");
+  if constexpr (A == 0) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    if (ahead >= A)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(A * PER) : "memory");
+    else
+      wait_stages<PER, A - 1>(ahead);
+  }
+}
+
+// One round of a ring loop: f(stage K, chunk i + K) for the stages K < R
+// whose chunk exists, with K a compile-time constant (the stage's LDS offset
+// becomes an immediate of its reads).
+template <int R, int K = 0, typename F>
+__device__ inline void ring_round(F& f, int i, int n) {
+  if constexpr (K < R) {
+    if (i + K < n) {
+      f(std::integral_constant<int, K>{}, i + K);
+      ring_round<R, K + 1>(f, i, n);
+    }
+  }
 }
 
 __device__ inline void lds_add_u32(uint32_t a, uint32_t v) {
@@ -304,10 +318,9 @@ __global__ void __launch_bounds__(64 * NW) score_mfma(DecodeParams p) {
   };
   const bool hist = p.top_t > 0;   // no selection, no histogram
   for (int i = tid; i < kHistBins; i += 64 * NW) lhist[i] = 0u;
-  static_assert(kSRing == 4, "the stream loop is unrolled by the ring depth");
-  if (0 < nmine) issue(0, ring[wid][0]);
-  if (1 < nmine) issue(1, ring[wid][1]);
-  if (2 < nmine) issue(2, ring[wid][2]);
+#pragma unroll
+  for (int k = 0; k < kSRing - 1; ++k)
+    if (k < nmine) issue(k, ring[wid][k]);
   v4i a0, a1;
   prep_query<G>(qx, qp, a0, a1);
   // logits in log2 units (1/sqrt(D) and log2(e) folded into the per-head
@@ -326,10 +339,10 @@ __global__ void __launch_bounds__(64 * NW) score_mfma(DecodeParams p) {
   auto body = [&](auto kc, int i) {
     constexpr int k = decltype(kc)::value;        // stage of chunk i
     constexpr int OFF = k * (int)sizeof(SStage);
-    if (i + 3 < nmine) issue(i + 3, ring[wid][(k + 3) & 3]);
+    if (i + kSRing - 1 < nmine) issue(i + kSRing - 1, ring[wid][(k + kSRing - 1) % kSRing]);
     // this wave's loads complete in order: stage i is in once no more than
     // the stages issued after it are outstanding (stores only add to the count)
-    wait_stages<kSRingLoads>(min(kSRing - 1, nmine - 1 - i));
+    wait_stages<kSRingLoads, kSRing - 1>(min(kSRing - 1, nmine - 1 - i));
     const int c = wid + NW * i;
     uint64_t kw[2], ks[2];
     asm volatile(
@@ -365,12 +378,9 @@ __global__ void __launch_bounds__(64 * NW) score_mfma(DecodeParams p) {
       if (hist) lds_add_u32(hist0 + 4u * (score_key(sc) >> (32 - kHistBits)), 1u);
     }
   };
-  for (int i = 0; i < nmine; i += 4) {
+  for (int i = 0; i < nmine; i += kSRing) {
     progress_priority(nmine - i, nmine);
-    body(std::integral_constant<int, 0>{}, i);
-    if (i + 1 < nmine) body(std::integral_constant<int, 1>{}, i + 1);
-    if (i + 2 < nmine) body(std::integral_constant<int, 2>{}, i + 2);
-    if (i + 3 < nmine) body(std::integral_constant<int, 3>{}, i + 3);
+    ring_round<kSRing>(body, i, nmine);
   }
   __builtin_amdgcn_s_setprio(0);
   // the histogram adds (asm, not waited for) complete before the barrier
@@ -499,10 +509,9 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
     bdma16(rV, oV, c * 1024u, st.v);
     bdma4(rS, oS, c * 256u, st.vs);
   };
-  static_assert(kRing == 4, "the stream loop is unrolled by the ring depth");
-  if (0 < nmine) issue(0, s.u.ring[wid][0]);
-  if (1 < nmine) issue(1, s.u.ring[wid][1]);
-  if (2 < nmine) issue(2, s.u.ring[wid][2]);
+#pragma unroll
+  for (int k = 0; k < kRing - 1; ++k)
+    if (k < nmine) issue(k, s.u.ring[wid][k]);
 
   for (int i = lane; i < 2 * G * 32; i += 64) (&s.wt[wid][0][0])[i] = (_Float16)0.f;
   if (tid < 8) s.wzero[tid] = (_Float16)0.f;
@@ -553,10 +562,10 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
 
   auto body = [&](auto kc, int i) {
     constexpr int k = decltype(kc)::value;        // stage of chunk i
-    if (i + 3 < nmine) issue(i + 3, s.u.ring[wid][(k + 3) & 3]);
+    if (i + kRing - 1 < nmine) issue(i + kRing - 1, s.u.ring[wid][(k + kRing - 1) % kRing]);
     // this wave's loads complete in order: stage i is in once no more than
     // the stages issued after it are outstanding
-    wait_stages<kRingLoads>(min(kRing - 1, nmine - 1 - i));
+    wait_stages<kRingLoads, kRing - 1>(min(kRing - 1, nmine - 1 - i));
     const int c = wid + NW * i;
     const int rem = nsp - 32 * c;                 // tokens of this chunk inside the split
     // the chunk's tokens that take part (unmarked, inside the split) as lane
@@ -642,12 +651,9 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
       acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, av), bw, acc[tt], 0, 0, 0);
     }
   };
-  for (int i = 0; i < nmine; i += 4) {
+  for (int i = 0; i < nmine; i += kRing) {
     progress_priority(nmine - i, nmine);
-    body(std::integral_constant<int, 0>{}, i);
-    if (i + 1 < nmine) body(std::integral_constant<int, 1>{}, i + 1);
-    if (i + 2 < nmine) body(std::integral_constant<int, 2>{}, i + 2);
-    if (i + 3 < nmine) body(std::integral_constant<int, 3>{}, i + 3);
+    ring_round<kRing>(body, i, nmine);
   }
   __builtin_amdgcn_s_setprio(0);
   // the ring is reused below: no load of this wave may still be landing, and
