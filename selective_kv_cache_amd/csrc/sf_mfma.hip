@@ -366,9 +366,7 @@ __global__ void __launch_bounds__(64 * NW) score_mfma(DecodeParams p) {
       const float x = logit_scaled(D, __builtin_bit_cast(float2, ks[j]), scale, sumq);
       lg[j] = hl < G ? x : -INFINITY;
       const int rel = 32 * c + 16 * j + t;
-      // kept for the attention pass; streaming (non-temporal) stores leave
-      // few dirty L2 lines to write back when the pass ends
-      if (hl < G && (full || rel < nsp)) __builtin_nontemporal_store(x, &lgo[rel * G + hl]);
+      if (hl < G && (full || rel < nsp)) lgo[rel * G + hl] = x;   // kept for the attention pass
     }
     // maximum over the heads, two tiles at once: lane (t, hl) keeps tile
     // hl/2 (token 16 (hl/2) + t)
@@ -376,7 +374,7 @@ __global__ void __launch_bounds__(64 * NW) score_mfma(DecodeParams p) {
     const int rel = 32 * c + 16 * hx + t;
     if ((hl & 1) == 0 && (full || rel < nsp)) {
       const float sc = y * kLn2;                  // the score in natural units
-      __builtin_nontemporal_store(sc, &scores[rel]);
+      scores[rel] = sc;
       if (hist) lds_add_u32(hist0 + 4u * (score_key(sc) >> (32 - kHistBits)), 1u);
     }
   };
