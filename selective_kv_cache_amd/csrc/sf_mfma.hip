@@ -662,12 +662,12 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   __syncthreads();
 
   // wave totals: l and the scalar term per head (row sums), P.V per column
-  // (column n < G: head n's hi part, G + h: its lo part); the maximum goes
-  // back to natural-log units
+  // (column n < G: head n's hi part, G + h: its lo part); maxima stay in
+  // log2 units until the partial is written
   lsum = row16_sum(lsum);
   t1 = row16_sum(t1);
   if (hl < G && t == 0) {
-    s.mw[wid][hl] = m == kFloor ? -INFINITY : m * 0.6931471805599453f;   // -inf: no token took part
+    s.mw[wid][hl] = m == kFloor ? -INFINITY : m;   // -inf: no token took part
     s.lw[wid][hl] = lsum;
   }
   float t1n = 0.f;                                // the scalar term goes with the hi column
@@ -694,15 +694,14 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        if (s.mw[w][h] == -INFINITY) continue;
-        const float e = expf(s.mw[w][h] - M);
+        const float e = __builtin_amdgcn_exp2f(s.mw[w][h] - M);   // 0 for a wave without tokens
         A += e * (s.u.accw[w][h][d] + s.u.accw[w][G + h][d]);
         L += e * s.lw[w][h];
       }
     }
     part[h * kPartStride + d] = A;
     if (d == 0) {
-      part[h * kPartStride + kHeadDim] = M;
+      part[h * kPartStride + kHeadDim] = M * 0.6931471805599453f;   // natural-log units
       part[h * kPartStride + kHeadDim + 1] = L;
     }
   }
