@@ -234,28 +234,40 @@ def time_kernels(model, steps):
     return out
 
 
-def cpu_baseline(w, layer_budget_s=30.0):
-    """The oracle timed on the host on a bounded sample: one layer's decode
-    (all KV heads of every sequence), scaled to whole-model steps/s."""
+def cpu_baseline(w, min_s=10.0, max_s=30.0, n_layers=3):
+    """The oracle timed on the host on a bounded sample: the decode of the
+    first n_layers layers (all KV heads of every sequence), layer after layer
+    and again until at least min_s of timed work (stopping at max_s), scaled
+    to whole-model steps/s."""
     import torch
     import oracle.kv_oracle as O
     from selective_kv_cache_amd import workloads as W
     lens = w.seq_lengths()
     off = W.seq_offsets(lens)
-    k, v = W.layer_kv(w, 0, device="cuda")
-    k, v = k.cpu().numpy(), v.cpu().numpy()
-    q = W.query(w, 0)
-    cache = O.quantize_cache(k, v, w.base_bits, w.refine_bits)     # setup, not timed
-    del k, v
+    layers = []
+    for l in range(min(n_layers, w.layers)):
+        k, v = W.layer_kv(w, l, device="cuda")
+        k, v = k.cpu().numpy(), v.cpu().numpy()
+        layers.append((W.query(w, l), O.quantize_cache(k, v, w.base_bits, w.refine_bits)))   # setup, not timed
+        del k, v
     heads = [(s, h) for s in range(w.batch) for h in range(w.n_kv_heads)]
-    t0 = time.perf_counter()
-    done = 0
-    for sh in heads:
-        O.decode_step(q, cache, off, w.top_t, heads=[sh])
-        done += 1
-        if time.perf_counter() - t0 > layer_budget_s:
+    dt, done, full = 0.0, 0, 0
+    while dt < min_s:
+        for q, cache in layers:
+            for sh in heads:
+                t0 = time.perf_counter()
+                O.decode_step(q, cache, off, w.top_t, heads=[sh])
+                dt += time.perf_counter() - t0
+                done += 1
+                if dt > max_s:
+                    break
+            if dt > max_s:
+                break
+            full += 1
+            if dt >= min_s:
+                break
+        if dt > max_s:
             break
-    dt = time.perf_counter() - t0
     layer_s = dt * len(heads) / done
     try:
         from threadpoolctl import threadpool_info
@@ -263,8 +275,9 @@ def cpu_baseline(w, layer_budget_s=30.0):
     except Exception:
         threads = 1
     return {"value": 1.0 / (layer_s * w.layers), "unit": "steps/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"layer 0 of {w.name}: {done}/{len(heads)} (sequence, KV head) units timed "
-                      f"({dt:.1f} s), scaled to {w.layers} layers; numpy fp64 oracle, quantization excluded"}
+            "sample": f"layers 0-{len(layers) - 1} of {w.name}, in turn: {done} (sequence, KV head) units "
+                      f"({full} whole layers) timed, {dt:.1f} s, scaled to {w.layers} layers; numpy fp64 "
+                      f"oracle, quantization excluded"}
 
 
 def host_tier_run(w, steps, warmup):

@@ -63,8 +63,13 @@ __global__ void __launch_bounds__(kSelThreads) select_scan(DecodeParams p) {
   }
 
   if (!all) {
-    const uint32_t* h1 = p.hist + sk * kHistBins;
-    for (int i = tid; i < kHistBins; i += kSelThreads) h[i] = h1[i];
+    // the level-1 histogram in 16-byte pieces, every load issued before the
+    // first LDS store
+    static_assert(kHistBins == 8 * kSelThreads, "two 16-byte pieces per thread");
+    const uint4* h1 = reinterpret_cast<const uint4*>(p.hist + sk * kHistBins);
+    const uint4 x0 = h1[tid], x1 = h1[tid + kSelThreads];
+    reinterpret_cast<uint4*>(h)[tid] = x0;
+    reinterpret_cast<uint4*>(h)[tid + kSelThreads] = x1;
     if (tid == 0) sh_cnt = 0u;
     __syncthreads();
     find_threshold_wave<kHistBins>(h, (uint32_t)tn, &sh_bin, &sh_need);
