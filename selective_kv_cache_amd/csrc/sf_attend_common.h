@@ -49,6 +49,24 @@ __device__ inline void quarter_dots(const uint32_t* kb, const uint32_t* kr, cons
   }
 }
 
+// The refinement-code part alone: q . s over one quarter of head_dim, and the
+// sum of the query elements.
+template <int R, int G>
+__device__ inline void quarter_dots_ref(const uint32_t* kr, const float* qs, int qd, float* ds, float* dq) {
+#pragma unroll
+  for (int h = 0; h < G; ++h) ds[h] = dq[h] = 0.f;
+#pragma unroll
+  for (int d = 0; d < 32; ++d) {
+    const float s = (float)code_at<R>(kr, d);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float qv = qs[h * kHeadDim + qd * 32 + d];
+      ds[h] = fmaf(qv, s, ds[h]);
+      dq[h] += qv;
+    }
+  }
+}
+
 // Sum over the four lanes of a quad (DPP quad permutes).
 __device__ inline float quad_sum(float x) {
   x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
@@ -82,6 +100,27 @@ __device__ inline void write_partial(float* part, const float (*mw)[G], const fl
   }
 }
 
+// write_partial for waves that share one maximum (mall[w][h] equal for all w):
+// the accumulators and sums add without rescaling.
+template <int G, int NW>
+__device__ inline void write_partial_shared(float* part, const float (*mall)[G], const float (*lw)[G],
+                                            const float (*accw)[G][kHeadDim]) {
+  for (int i = threadIdx.x; i < G * kHeadDim; i += 64 * NW) {
+    const int h = i / kHeadDim, d = i % kHeadDim;
+    float A = 0.f, L = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      A += accw[w][h][d];
+      L += lw[w][h];
+    }
+    part[h * kPartStride + d] = A;
+    if (d == 0) {
+      part[h * kPartStride + kHeadDim] = mall[0][h];
+      part[h * kPartStride + kHeadDim + 1] = L;
+    }
+  }
+}
+
 // Selected tokens of one (sequence, KV head): 16 NW of them per work-group
 // (p.sel_blk_tok), NW wavefronts x 16 tokens, 4 lanes (a quarter of head_dim
 // each) per token.  Writes the partial of the refined terms.
@@ -96,7 +135,13 @@ struct SelLds {
   float accw[NW][G][kHeadDim];
 };
 
-template <int BB, int G, int NW>
+//
+// With LG, the score pass left every token's base logits (log2 units) in
+// p.logits, and the refined logit is that base logit plus the refinement's
+// change: with sub = 2^-r,
+//   refined - base = delta / sqrt(D) * (sub * (q . s) + (sub - 1) * sum(q) / 2),
+// so the K base codes are not read again.
+template <int BB, int G, int NW, bool LG>
 __device__ inline void selected_block(const DecodeParams& p, int blk, int kvh, uint8_t* smem) {
   constexpr int W = 4 * BB;
   using Lds = SelLds<BB, G, NW>;
@@ -122,7 +167,10 @@ __device__ inline void selected_block(const DecodeParams& p, int blk, int kvh, u
   const bool valid = j < hi;
   const int64_t tok = valid ? a + p.sel[sk * p.top_t + j] : 0;
   uint32_t kb[BB], kr[9], vb[BB], vr[8];
+  float lgb[G];                   // base logits from the score pass (LG)
   float2 ksc = make_float2(0.f, 0.f), vsc = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int h = 0; h < G; ++h) lgb[h] = 0.f;
 #pragma unroll
   for (int i = 0; i < BB; ++i) kb[i] = vb[i] = 0u;
 #pragma unroll
@@ -135,9 +183,14 @@ __device__ inline void selected_block(const DecodeParams& p, int blk, int kvh, u
     const uint32_t* srcv = reinterpret_cast<const uint32_t*>(p.vc + row * (16 * BB)) + qd * BB;
     const uint32_t* rk = refine_row(p, sk, kvh, tok, 0) + qd * r;
     const uint32_t* rv = refine_row(p, sk, kvh, tok, 1) + qd * r;
+    if (LG) {
+      const float* lgs = p.logits + ((int64_t)kvh * p.ntot + (tok - p.off0)) * G;
+#pragma unroll
+      for (int h = 0; h < G; ++h) lgb[h] = lgs[h];
+    }
 #pragma unroll
     for (int i = 0; i < BB; ++i) {
-      kb[i] = srck[i];
+      if (!LG) kb[i] = srck[i];
       vb[i] = srcv[i];
     }
 #pragma unroll
@@ -150,21 +203,38 @@ __device__ inline void selected_block(const DecodeParams& p, int blk, int kvh, u
   }
   __syncthreads();
   float dc[G], ds[G], dq[G];
-  switch (r) {
-    case 1: quarter_dots<BB, 1, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
-    case 2: quarter_dots<BB, 2, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
-    case 3: quarter_dots<BB, 3, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
-    case 4: quarter_dots<BB, 4, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
-    case 5: quarter_dots<BB, 5, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
-    case 6: quarter_dots<BB, 6, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
-    case 7: quarter_dots<BB, 7, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
-    default: quarter_dots<BB, 8, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
+  if (LG) {
+    switch (r) {
+      case 1: quarter_dots_ref<1, G>(kr, &s.qs[0][0], qd, ds, dq); break;
+      case 2: quarter_dots_ref<2, G>(kr, &s.qs[0][0], qd, ds, dq); break;
+      case 3: quarter_dots_ref<3, G>(kr, &s.qs[0][0], qd, ds, dq); break;
+      case 4: quarter_dots_ref<4, G>(kr, &s.qs[0][0], qd, ds, dq); break;
+      case 5: quarter_dots_ref<5, G>(kr, &s.qs[0][0], qd, ds, dq); break;
+      case 6: quarter_dots_ref<6, G>(kr, &s.qs[0][0], qd, ds, dq); break;
+      case 7: quarter_dots_ref<7, G>(kr, &s.qs[0][0], qd, ds, dq); break;
+      default: quarter_dots_ref<8, G>(kr, &s.qs[0][0], qd, ds, dq); break;
+    }
+  } else {
+    switch (r) {
+      case 1: quarter_dots<BB, 1, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
+      case 2: quarter_dots<BB, 2, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
+      case 3: quarter_dots<BB, 3, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
+      case 4: quarter_dots<BB, 4, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
+      case 5: quarter_dots<BB, 5, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
+      case 6: quarter_dots<BB, 6, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
+      case 7: quarter_dots<BB, 7, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
+      default: quarter_dots<BB, 8, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
+    }
   }
   float lr[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const float qsum = quad_sum(dq[h]);
-    lr[h] = (ksc.x * qsum + ksc.y * (quad_sum(dc[h]) + (quad_sum(ds[h]) + 0.5f * qsum) * sub)) * kRsqrtD;
+    if (LG)
+      lr[h] = fmaf(lgb[h], 0.6931471805599453f,
+                   ksc.y * kRsqrtD * fmaf(sub, quad_sum(ds[h]), 0.5f * (sub - 1.0f) * qsum));
+    else
+      lr[h] = (ksc.x * qsum + ksc.y * (quad_sum(dc[h]) + (quad_sum(ds[h]) + 0.5f * qsum) * sub)) * kRsqrtD;
     const float mv = wave_max_dpp(valid ? lr[h] : -INFINITY);
     if (lane == 0) s.mred[wid][h] = mv;
   }
@@ -225,7 +295,7 @@ __device__ inline void selected_block(const DecodeParams& p, int blk, int kvh, u
   }
   __syncthreads();
   float* part = p.part + ((int64_t)kvh * (p.n_sel_blk + p.n_split) + blk) * G * kPartStride;
-  write_partial<G, NW>(part, s.mall, s.lw, s.accw);
+  write_partial_shared<G, NW>(part, s.mall, s.lw, s.accw);
 }
 
 }  // namespace sfk
