@@ -155,9 +155,9 @@ __device__ inline void base_split_valu(const DecodeParams& p, int split, int kvh
 
 template <int BB, int G>
 __global__ void __launch_bounds__(256) attend_valu(DecodeParams p) {
-  __shared__ __align__(16) uint8_t smem[cmax(sizeof(SelLds<BB, G, 4>), sizeof(ValuLds<BB, G>))];
+  __shared__ __align__(16) uint8_t smem[cmax(sizeof(SelLds<BB, G, 4, 16>), sizeof(ValuLds<BB, G>))];
   if ((int)blockIdx.x < p.n_sel_blk)
-    selected_block<BB, G, 4, false>(p, blockIdx.x, blockIdx.y, smem);
+    selected_block_any<BB, G, 4, false>(p, blockIdx.x, blockIdx.y, smem);
   else
     base_split_valu<BB, G>(p, blockIdx.x - p.n_sel_blk, blockIdx.y, smem);
 }

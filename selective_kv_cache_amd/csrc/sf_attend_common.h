@@ -121,19 +121,75 @@ __device__ inline void write_partial_shared(float* part, const float (*mall)[G],
   }
 }
 
-// Selected tokens of one (sequence, KV head): 16 NW of them per work-group
-// (p.sel_blk_tok), NW wavefronts x 16 tokens, 4 lanes (a quarter of head_dim
-// each) per token.  Writes the partial of the refined terms.
-template <int BB, int G, int NW>
+// Selected tokens of one (sequence, KV head): NW wavefronts x TPW tokens per
+// work-group (p.sel_blk_tok = NW TPW).  The rows of a wave's TPW tokens are
+// loaded by 4 lanes per token (a quarter row each) into LDS; the logits are
+// computed by LPT = 64 / TPW lanes per token, each over EPL = 128 / LPT
+// elements (fewer tokens per wave: shorter chains per lane); P.V takes 2
+// output elements per lane over the wave's tokens.  Writes the partial of the
+// refined terms.
+template <int BB, int G, int NW, int TPW>
 struct SelLds {
   float qs[G][kHeadDim];
-  uint32_t vt[NW][16][4 * BB + 1];
-  uint32_t vr[NW][16][33];
-  float2 vsc[NW][16];
-  float wt[NW][G][16];
+  uint32_t kq[NW][TPW][33];          // K refinement rows (r <= 8: 32 words + a zero word)
+  uint32_t kbq[NW][TPW][4 * BB + 1]; // K base codes (when the logits are recomputed)
+  uint32_t vt[NW][TPW][4 * BB + 1];
+  uint32_t vr[NW][TPW][33];
+  float2 vsc[NW][TPW], ksc[NW][TPW];
+  float lgt[NW][TPW][G];             // base logits from the score pass
+  float wt[NW][G][TPW];
   float mred[NW][G], mall[NW][G], lw[NW][G];
   float accw[NW][G][kHeadDim];
 };
+
+// The EPL codes (W bits each) from element e0 of an LDS row, shifted so that
+// the first one sits at bit 0 of the returned words (EPL W <= 256 bits).
+template <int W, int EPL>
+__device__ inline void row_window(const uint32_t* row, int e0, uint32_t (&out)[EPL * W / 32 + 1]) {
+  const int bit = e0 * W, wo = bit >> 5, sh = bit & 31;
+#pragma unroll
+  for (int j = 0; j < EPL * W / 32 + 1; ++j) {
+    const uint32_t lo = row[wo + j], hi = j + 1 < EPL * W / 32 + 1 || sh ? row[wo + j + 1] : 0u;
+    out[j] = sh ? (lo >> sh) | (hi << (32 - sh)) : lo;
+  }
+}
+
+// Sum over the LPT lanes of a token (LPT = 4: a quad, 16: a DPP row); every
+// lane of the group receives it.
+template <int LPT>
+__device__ inline float token_sum(float x) {
+  x = quad_sum(x);
+  if constexpr (LPT == 16) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
+  }
+  return x;
+}
+
+// Dot products of lane's EPL elements [e0, e0 + EPL) with the G query heads:
+// base codes (BB bits, when !LG), refinement codes (R bits) and the query
+// sum.
+template <int BB, int R, int G, int EPL, bool LG>
+__device__ inline void lane_dots(const uint32_t* kbrow, const uint32_t* krrow, const float* qs, int e0, float* dc,
+                                 float* ds, float* dq) {
+  uint32_t kb[EPL * BB / 32 + 1], kr[EPL * R / 32 + 1];
+  if (!LG) row_window<BB, EPL>(kbrow, e0, kb);
+  row_window<R, EPL>(krrow, e0, kr);
+#pragma unroll
+  for (int h = 0; h < G; ++h) dc[h] = ds[h] = dq[h] = 0.f;
+#pragma unroll
+  for (int d = 0; d < EPL; ++d) {
+    const float sv = (float)code_at<R>(kr, d);
+    const float cv = LG ? 0.f : (float)code_at<BB>(kb, d);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float qv = qs[h * kHeadDim + e0 + d];
+      if (!LG) dc[h] = fmaf(qv, cv, dc[h]);
+      ds[h] = fmaf(qv, sv, ds[h]);
+      dq[h] += qv;
+    }
+  }
+}
 
 //
 // With LG, the score pass left every token's base logits (log2 units) in
@@ -141,127 +197,132 @@ struct SelLds {
 // change: with sub = 2^-r,
 //   refined - base = delta / sqrt(D) * (sub * (q . s) + (sub - 1) * sum(q) / 2),
 // so the K base codes are not read again.
-template <int BB, int G, int NW, bool LG>
+template <int BB, int G, int NW, bool LG, int TPW>
 __device__ inline void selected_block(const DecodeParams& p, int blk, int kvh, uint8_t* smem) {
-  constexpr int W = 4 * BB;
-  using Lds = SelLds<BB, G, NW>;
+  constexpr int W = 4 * BB, LPT = 64 / TPW, EPL = kHeadDim / LPT;
+  static_assert(TPW == 4 || TPW == 16, "4 or 16 lanes per token");
+  using Lds = SelLds<BB, G, NW, TPW>;
   Lds& s = *reinterpret_cast<Lds*>(smem);
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int tk = lane >> 2, qd = lane & 3;
   int64_t lo, hi;
   int first;
-  const int seq = locate_unit(p, 16 * NW, blk, true, lo, hi, first);
+  const int seq = locate_unit(p, NW * TPW, blk, true, lo, hi, first);
   const int64_t a = seq_at(p, seq);
   const int64_t sk = (int64_t)seq * p.hkv + kvh;
   const int r = p.r;
   const float sub = __builtin_ldexpf(1.0f, -r);
   const uint32_t rmask = (1u << r) - 1u;
 
-  // the query and the token's index, then every row of the token at once:
-  // K and V codes, their refinement rows and scales (two dependent memory
-  // round trips in all)
+  // the query and the tokens' indices, then every row of the tokens at once
+  // (two dependent memory round trips): lane (tl, qd) < 4 TPW loads quarter
+  // qd of token tl's rows
   for (int i = tid; i < G * kHeadDim; i += 64 * NW)
     s.qs[i / kHeadDim][i % kHeadDim] = p.q[((int64_t)seq * p.hq + kvh * G) * kHeadDim + i];
-  const int64_t j = lo + wid * 16 + tk;
-  const bool valid = j < hi;
-  const int64_t tok = valid ? a + p.sel[sk * p.top_t + j] : 0;
-  uint32_t kb[BB], kr[9], vb[BB], vr[8];
-  float lgb[G];                   // base logits from the score pass (LG)
-  float2 ksc = make_float2(0.f, 0.f), vsc = make_float2(0.f, 0.f);
+  {
+    const int tl = lane >> 2, qd = lane & 3;
+    const int64_t j = lo + wid * TPW + tl;
+    const bool loader = lane < 4 * TPW;
+    const bool valid = loader && j < hi;
+    const int64_t tok = valid ? a + p.sel[sk * p.top_t + j] : 0;
+    uint32_t kb[BB], kr[8], vb[BB], vr[8];
+    float lg[G];
+    float2 ksc = make_float2(0.f, 0.f), vsc = make_float2(0.f, 0.f);
 #pragma unroll
-  for (int h = 0; h < G; ++h) lgb[h] = 0.f;
+    for (int i = 0; i < BB; ++i) kb[i] = vb[i] = 0u;
 #pragma unroll
-  for (int i = 0; i < BB; ++i) kb[i] = vb[i] = 0u;
+    for (int i = 0; i < 8; ++i) kr[i] = vr[i] = 0u;
 #pragma unroll
-  for (int i = 0; i < 9; ++i) kr[i] = 0u;
+    for (int h = 0; h < G; ++h) lg[h] = 0.f;
+    if (valid) {
+      const int64_t row = (int64_t)kvh * p.cap + tok;
+      const uint32_t* srck = reinterpret_cast<const uint32_t*>(p.kc + row * (16 * BB)) + qd * BB;
+      const uint32_t* srcv = reinterpret_cast<const uint32_t*>(p.vc + row * (16 * BB)) + qd * BB;
+      const uint32_t* rk = refine_row(p, sk, kvh, tok, 0) + qd * r;
+      const uint32_t* rv = refine_row(p, sk, kvh, tok, 1) + qd * r;
+      if (LG) {
+        const float* lgs = p.logits + ((int64_t)kvh * p.ntot + (tok - p.off0)) * G;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) vr[i] = 0u;
-  if (valid) {
-    const int64_t row = (int64_t)kvh * p.cap + tok;
-    const uint32_t* srck = reinterpret_cast<const uint32_t*>(p.kc + row * (16 * BB)) + qd * BB;
-    const uint32_t* srcv = reinterpret_cast<const uint32_t*>(p.vc + row * (16 * BB)) + qd * BB;
-    const uint32_t* rk = refine_row(p, sk, kvh, tok, 0) + qd * r;
-    const uint32_t* rv = refine_row(p, sk, kvh, tok, 1) + qd * r;
-    if (LG) {
-      const float* lgs = p.logits + ((int64_t)kvh * p.ntot + (tok - p.off0)) * G;
+        for (int h = 0; h < G; ++h) lg[h] = lgs[h];
+      }
 #pragma unroll
-      for (int h = 0; h < G; ++h) lgb[h] = lgs[h];
+      for (int i = 0; i < BB; ++i) {
+        if (!LG) kb[i] = srck[i];
+        vb[i] = srcv[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        kr[i] = i < r ? rk[i] : 0u;
+        vr[i] = i < r ? rv[i] : 0u;
+      }
+      ksc = reinterpret_cast<const float2*>(p.ks)[row];
+      vsc = reinterpret_cast<const float2*>(p.vs)[row];
     }
+    if (loader) {
 #pragma unroll
-    for (int i = 0; i < BB; ++i) {
-      if (!LG) kb[i] = srck[i];
-      vb[i] = srcv[i];
-    }
+      for (int i = 0; i < BB; ++i) {
+        s.kbq[wid][tl][qd * BB + i] = kb[i];
+        s.vt[wid][tl][qd * BB + i] = vb[i];
+      }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      kr[i] = i < r ? rk[i] : 0u;
-      vr[i] = i < r ? rv[i] : 0u;
+      for (int i = 0; i < 8; ++i)
+        if (i < r) {
+          s.kq[wid][tl][qd * r + i] = kr[i];
+          s.vr[wid][tl][qd * r + i] = vr[i];
+        }
+      if (qd == 0) {
+        s.kbq[wid][tl][W] = s.vt[wid][tl][W] = 0u;
+        for (int i = 4 * r; i < 33; ++i) s.kq[wid][tl][i] = s.vr[wid][tl][i] = 0u;
+        s.ksc[wid][tl] = ksc;
+        s.vsc[wid][tl] = vsc;
+#pragma unroll
+        for (int h = 0; h < G; ++h) s.lgt[wid][tl][h] = lg[h];
+      }
     }
-    ksc = reinterpret_cast<const float2*>(p.ks)[row];
-    vsc = reinterpret_cast<const float2*>(p.vs)[row];
   }
   __syncthreads();
+
+  // the logits: lane (tc, e) over elements [e EPL, e EPL + EPL) of token tc
+  const int tc = lane / LPT, e0 = (lane % LPT) * EPL;
+  const bool valid = lo + wid * TPW + tc < hi;
   float dc[G], ds[G], dq[G];
-  if (LG) {
-    switch (r) {
-      case 1: quarter_dots_ref<1, G>(kr, &s.qs[0][0], qd, ds, dq); break;
-      case 2: quarter_dots_ref<2, G>(kr, &s.qs[0][0], qd, ds, dq); break;
-      case 3: quarter_dots_ref<3, G>(kr, &s.qs[0][0], qd, ds, dq); break;
-      case 4: quarter_dots_ref<4, G>(kr, &s.qs[0][0], qd, ds, dq); break;
-      case 5: quarter_dots_ref<5, G>(kr, &s.qs[0][0], qd, ds, dq); break;
-      case 6: quarter_dots_ref<6, G>(kr, &s.qs[0][0], qd, ds, dq); break;
-      case 7: quarter_dots_ref<7, G>(kr, &s.qs[0][0], qd, ds, dq); break;
-      default: quarter_dots_ref<8, G>(kr, &s.qs[0][0], qd, ds, dq); break;
-    }
-  } else {
-    switch (r) {
-      case 1: quarter_dots<BB, 1, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
-      case 2: quarter_dots<BB, 2, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
-      case 3: quarter_dots<BB, 3, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
-      case 4: quarter_dots<BB, 4, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
-      case 5: quarter_dots<BB, 5, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
-      case 6: quarter_dots<BB, 6, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
-      case 7: quarter_dots<BB, 7, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
-      default: quarter_dots<BB, 8, G>(kb, kr, &s.qs[0][0], qd, dc, ds, dq); break;
-    }
+  const uint32_t* kbrow = &s.kbq[wid][tc][0];
+  const uint32_t* krrow = &s.kq[wid][tc][0];
+  switch (r) {
+    case 1: lane_dots<BB, 1, G, EPL, LG>(kbrow, krrow, &s.qs[0][0], e0, dc, ds, dq); break;
+    case 2: lane_dots<BB, 2, G, EPL, LG>(kbrow, krrow, &s.qs[0][0], e0, dc, ds, dq); break;
+    case 3: lane_dots<BB, 3, G, EPL, LG>(kbrow, krrow, &s.qs[0][0], e0, dc, ds, dq); break;
+    case 4: lane_dots<BB, 4, G, EPL, LG>(kbrow, krrow, &s.qs[0][0], e0, dc, ds, dq); break;
+    case 5: lane_dots<BB, 5, G, EPL, LG>(kbrow, krrow, &s.qs[0][0], e0, dc, ds, dq); break;
+    case 6: lane_dots<BB, 6, G, EPL, LG>(kbrow, krrow, &s.qs[0][0], e0, dc, ds, dq); break;
+    case 7: lane_dots<BB, 7, G, EPL, LG>(kbrow, krrow, &s.qs[0][0], e0, dc, ds, dq); break;
+    default: lane_dots<BB, 8, G, EPL, LG>(kbrow, krrow, &s.qs[0][0], e0, dc, ds, dq); break;
   }
+  const float2 ksc = s.ksc[wid][tc];
   float lr[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float qsum = quad_sum(dq[h]);
+    const float qsum = token_sum<LPT>(dq[h]);
     if (LG)
-      lr[h] = fmaf(lgb[h], 0.6931471805599453f,
-                   ksc.y * kRsqrtD * fmaf(sub, quad_sum(ds[h]), 0.5f * (sub - 1.0f) * qsum));
+      lr[h] = fmaf(s.lgt[wid][tc][h], 0.6931471805599453f,
+                   ksc.y * kRsqrtD * fmaf(sub, token_sum<LPT>(ds[h]), 0.5f * (sub - 1.0f) * qsum));
     else
-      lr[h] = (ksc.x * qsum + ksc.y * (quad_sum(dc[h]) + (quad_sum(ds[h]) + 0.5f * qsum) * sub)) * kRsqrtD;
+      lr[h] = (ksc.x * qsum + ksc.y * (token_sum<LPT>(dc[h]) + (token_sum<LPT>(ds[h]) + 0.5f * qsum) * sub)) *
+              kRsqrtD;
     const float mv = wave_max_dpp(valid ? lr[h] : -INFINITY);
     if (lane == 0) s.mred[wid][h] = mv;
   }
-  {
-    uint32_t* dstb = &s.vt[wid][tk][qd * BB];
-    uint32_t* dstr = &s.vr[wid][tk][qd * r];
-#pragma unroll
-    for (int i = 0; i < BB; ++i) dstb[i] = vb[i];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (i < r) dstr[i] = vr[i];
-    if (qd == 0) {
-      s.vsc[wid][tk] = vsc;
-      s.vt[wid][tk][W] = 0u;
-      s.vr[wid][tk][4 * r] = 0u;
-    }
-  }
   __syncthreads();
   float acc[G][2];
+  const bool lead = lane % LPT == 0;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float M = s.mred[0][h];
 #pragma unroll
     for (int w = 1; w < NW; ++w) M = fmaxf(M, s.mred[w][h]);
-    const float e = valid ? expf(lr[h] - M) : 0.f;
-    if (qd == 0) s.wt[wid][h][tk] = e;
-    const float ls = wave_sum_dpp(qd == 0 ? e : 0.f);
+    const float ew = valid ? expf(lr[h] - M) : 0.f;
+    if (lead) s.wt[wid][h][tc] = ew;
+    const float ls = wave_sum_dpp(lead ? ew : 0.f);
     if (lane == 0) {
       s.lw[wid][h] = ls;
       s.mall[wid][h] = M;       // all waves share the work-group maximum
@@ -271,7 +332,8 @@ __device__ inline void selected_block(const DecodeParams& p, int blk, int kvh, u
   wave_barrier();
   const int cpos = 2 * lane * BB, cwi = cpos >> 5, csh = cpos & 31;
   const int rpos = 2 * lane * r, rwi = rpos >> 5, rsh = rpos & 31;
-  for (int jj = 0; jj < 16; ++jj) {
+#pragma unroll 4
+  for (int jj = 0; jj < TPW; ++jj) {
     const uint64_t cwin = (uint64_t)s.vt[wid][jj][cwi] | ((uint64_t)s.vt[wid][jj][cwi + 1] << 32);
     const uint32_t cc = (uint32_t)(cwin >> csh);
     const uint64_t rwin = (uint64_t)s.vr[wid][jj][rwi] | ((uint64_t)s.vr[wid][jj][rwi + 1] << 32);
@@ -296,6 +358,15 @@ __device__ inline void selected_block(const DecodeParams& p, int blk, int kvh, u
   __syncthreads();
   float* part = p.part + ((int64_t)kvh * (p.n_sel_blk + p.n_split) + blk) * G * kPartStride;
   write_partial_shared<G, NW>(part, s.mall, s.lw, s.accw);
+}
+
+// The selected block's shape chosen on the host: p.sel_blk_tok = NW TPW.
+template <int BB, int G, int NW, bool LG>
+__device__ inline void selected_block_any(const DecodeParams& p, int blk, int kvh, uint8_t* smem) {
+  if (p.sel_blk_tok == NW * 4)
+    selected_block<BB, G, NW, LG, 4>(p, blk, kvh, smem);
+  else
+    selected_block<BB, G, NW, LG, 16>(p, blk, kvh, smem);
 }
 
 }  // namespace sfk

@@ -62,12 +62,12 @@ int32_t choose_split(int64_t total_tokens, int32_t n_kv_heads, int32_t groups) {
 // groups of 1, 2 or 4) runs kAttendWaves wavefronts per work-group, the VALU
 // form 4; about 2048 wavefronts of base tokens either way.
 struct AttendShape {
-  int32_t split, sel_blk_tok;
+  int32_t split;
 };
 static AttendShape attend_shape(const sf_geom& g, int64_t total_tokens) {
   const int32_t grp = g.n_q_heads / g.n_kv_heads;
   const int waves = (g.base_bits == 2 && (grp == 1 || grp == 2 || grp == 4)) ? kAttendWaves : 4;
-  return AttendShape{choose_split(total_tokens, g.n_kv_heads, 2048 / waves), 16 * waves};
+  return AttendShape{choose_split(total_tokens, g.n_kv_heads, 2048 / waves)};
 }
 
 // Tokens per score work-group: about `groups` work-groups.
@@ -105,7 +105,17 @@ Carve carve(const sf_geom& g, int32_t batch, int64_t total_tokens, int64_t max_s
 // Upper bound of the partials of a step: splits of every sequence plus the
 // selected-token work-groups.
 static int32_t part_bound(int64_t total, int32_t batch, int32_t split, int32_t top_t) {
-  return (int32_t)(total / split + batch) + batch * ((top_t + kSelBlkTok - 1) / kSelBlkTok);
+  return (int32_t)(total / split + batch) + batch * ((top_t + kSelBlkTokMin - 1) / kSelBlkTokMin);
+}
+
+// Compute units of the current device (the selected blocks' size depends on
+// how many work-groups fit at once).
+static int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
 }
 
 }  // namespace sfk
@@ -170,16 +180,25 @@ extern "C" sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* a
   const int32_t score_split = choose_score_split(total, geom->n_kv_heads, score_mfma ? 4096 / kScoreWaves : 1024);
   const Carve c = carve(*geom, B, total, max_seq, a->top_t, part_bound(total, B, split, a->top_t));
   if (a->workspace_bytes < c.total) return SF_ERR_INVALID_ARG;
-  if (max_seq / split + 1 + (a->top_t + ash.sel_blk_tok - 1) / ash.sel_blk_tok > kCombineMax) return SF_ERR_UNSUPPORTED;
-
-  int32_t n_split = 0, n_score = 0, n_sel = 0, n_sel_blk = 0;
+  int32_t n_split = 0, n_score = 0, n_sel = 0, n_small = 0;
   for (int i = 0; i < B; ++i) {
     const int64_t n = off[i + 1] - off[i];
     n_split += (int32_t)((n + split - 1) / split);
     n_score += (int32_t)((n + score_split - 1) / score_split);
     n_sel += (int32_t)((n + kSelChunk - 1) / kSelChunk);
-    if (refine) n_sel_blk += (int32_t)((std::min<int64_t>(n, a->top_t) + ash.sel_blk_tok - 1) / ash.sel_blk_tok);
+    if (refine) n_small += (int32_t)((std::min<int64_t>(n, a->top_t) + kSelBlkTokMin - 1) / kSelBlkTokMin);
   }
+  static_assert(kAttendWaves == 4 && kSelBlkTokMin == 4 * 4 && kSelBlkTok == 4 * 16,
+                "selected blocks: 4 wavefronts of 4 or 16 tokens");
+  // selected blocks of 16 tokens (shorter per-lane chains) when the attention
+  // launch still fits three work-groups per CU with them, else of 64
+  static const int cus = device_cus();
+  const int32_t sel_blk_tok =
+      (int64_t)(n_small + n_split) * geom->n_kv_heads <= 3 * (int64_t)cus ? kSelBlkTokMin : kSelBlkTok;
+  int32_t n_sel_blk = 0;
+  for (int i = 0; i < B && refine; ++i)
+    n_sel_blk += (int32_t)((std::min<int64_t>(off[i + 1] - off[i], a->top_t) + sel_blk_tok - 1) / sel_blk_tok);
+  if (max_seq / split + 1 + (a->top_t + sel_blk_tok - 1) / sel_blk_tok > kCombineMax) return SF_ERR_UNSUPPORTED;
 
   uint8_t* ws = static_cast<uint8_t*>(a->workspace);
   DecodeParams p{};
@@ -198,7 +217,7 @@ extern "C" sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* a
   p.bm_words = (int32_t)(((max_seq + kSelThreads - 1) / kSelThreads) * (kSelThreads / 32));
   p.use_refine = refine ? 1 : 0;
   p.n_sel_blk = n_sel_blk;
-  p.sel_blk_tok = ash.sel_blk_tok;
+  p.sel_blk_tok = sel_blk_tok;
   p.cnt_stride = (int32_t)((max_seq + kSelChunk - 1) / kSelChunk) + 2;   // + level-1 boundary
   p.cap = a->cap;
   p.ntot = total;

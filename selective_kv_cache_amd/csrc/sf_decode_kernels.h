@@ -268,7 +268,8 @@ constexpr int kScoreWaves = 16;         // wavefronts per score work-group (matr
 constexpr int kSelThreads = 512;
 constexpr int32_t kSelChunk = 4096;
 constexpr int32_t kMaxSelChunks = 512;   // longest sequence: kMaxSelChunks * kSelChunk tokens
-constexpr int32_t kSelBlkTok = 64;     // selected tokens per attention work-group of 4 wavefronts (the fewest)
+constexpr int32_t kSelBlkTok = 64;     // selected tokens per attention work-group: 4 wavefronts x 16 tokens,
+constexpr int32_t kSelBlkTokMin = 16;  // or 4 wavefronts x 4 tokens when those work-groups still fit
 constexpr int kAttendWaves = 4;         // wavefronts per attention work-group (matrix-core path)
 constexpr int kCombineMax = 2048;      // partials per (sequence, query head)
 

@@ -709,9 +709,9 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
 
 template <int G, int NW>
 __global__ void __launch_bounds__(64 * NW) attend_mfma(DecodeParams p) {
-  __shared__ __align__(16) uint8_t smem[cmax(sizeof(SelLds<2, G, NW>), sizeof(MfmaLds<G, NW>))];
+  __shared__ __align__(16) uint8_t smem[cmax(sizeof(SelLds<2, G, NW, 16>), sizeof(MfmaLds<G, NW>))];
   if ((int)blockIdx.x < p.n_sel_blk)
-    selected_block<2, G, NW, true>(p, blockIdx.x, blockIdx.y, smem);
+    selected_block_any<2, G, NW, true>(p, blockIdx.x, blockIdx.y, smem);
   else
     base_split_mfma<G, NW>(p, blockIdx.x - p.n_sel_blk, blockIdx.y, smem);
 }

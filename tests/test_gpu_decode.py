@@ -49,6 +49,7 @@ SMALL = [
     dict(ctx=256, top_t=256),                                                  # N == T
     dict(ctx=1, top_t=4),                                                      # one token
     dict(ctx=5000, refine_bits=8, top_t=256, n_q_heads=8, n_kv_heads=2),
+    dict(ctx=20_000, n_q_heads=32, n_kv_heads=8, base_bits=3, refine_bits=2, top_t=2048),  # 64-token selected blocks
     dict(ctx=300_000, n_q_heads=2, n_kv_heads=1, top_t=1000),                 # > 64 selection chunks
     dict(ctx=600_000, n_q_heads=2, n_kv_heads=1, top_t=3000),                 # bitmap beyond LDS
 ]
