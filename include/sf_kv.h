@@ -106,10 +106,11 @@ sf_status sf_kv_quantize(const sf_geom* geom, const float* x, int64_t n_tok,
  * link, no cache); SF_TIER_HOST_PINNED keeps them in pinned host memory and
  * gives each (sequence slot, KV head) a device cache of `cache_slots` rows
  * that reuses fetched bits across steps (paragraph "The map app also loads
- * tiles ..."): a selected resident is a hit; each miss is copied over the
- * link with hipMemcpyAsync on a side stream and installed in a free slot,
- * else in place of the resident not selected now that was selected longest
- * ago (lower token index first).  Misses are waited for (policy "wait").
+ * tiles ..."): a selected resident is a hit; each miss is read over the link
+ * by a kernel, straight from the pinned store, into a free slot, else in
+ * place of the resident not selected now that was selected longest ago
+ * (lower token index first).  Misses are waited for (policy "wait"); the
+ * step involves no host work and no synchronization.
  * All memory is allocated by sf_store_create and freed by sf_store_destroy.
  * A store must not be used from two streams at once.
  * ------------------------------------------------------------------------- */
@@ -176,7 +177,9 @@ typedef struct sf_decode_args {
                                     (relative to the sequence start), ascending, -1 pad */
   float* scores_out;             /* optional device [Hkv][seq_off[B]-seq_off[0]] fp32:
                                     the token scores the selection used                 */
-  sf_step_stats* stats;          /* optional host; filled when the call returns         */
+  sf_step_stats* stats;          /* optional host; filled when the call returns (for the
+                                    host tier the call then waits for the step's miss
+                                    lists: pass NULL to keep the step asynchronous)     */
   void* workspace;               /* device scratch of sf_decode_workspace_size() bytes  */
   size_t workspace_bytes;
   int32_t flags;                 /* 0 or SF_DECODE_HIST_CLEAN                           */

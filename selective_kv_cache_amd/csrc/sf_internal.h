@@ -58,11 +58,8 @@ struct sf_store_s {
   int32_t* stamp;          // [max_seqs][Hkv][slots] last step the token was selected
   int32_t step;
   // staging for fetched rows and the miss lists
-  uint8_t* h_stage;        // pinned [max_seqs*Hkv*slots][2][row_bytes]
-  uint8_t* d_stage;        // device, same
-  int32_t* h_miss;         // pinned: [max_seqs*Hkv] counts, then [max_seqs*Hkv][slots] tokens
-  hipStream_t side;
-  hipEvent_t ev_side;
+  const uint8_t* host_rows_dev;   // host_rows as the device addresses it
+  int32_t* h_miss;         // pinned: the miss lists, copied back only for statistics
 };
 
 #define SF_HIP_CHECK(call)                                   \

@@ -14,16 +14,17 @@
 //                 first, then the slots of residents not selected now, oldest
 //                 stamp first (lower token index first); the miss list
 //                 (token, slot) goes to the workspace
-//   host          copies the miss lists device -> pinned host, gathers the K
-//                 and V refinement rows of every miss from the pinned store
-//                 into a pinned staging buffer, and copies it host -> device
-//                 with hipMemcpyAsync on the store's side stream
-//   cache_install (device, after the side stream's event): rows -> slots
-// Policy on a miss: wait (the step uses every selected refinement).
+//   cache_fetch   (device, many work-groups per (sequence, KV head)): the K
+//                 and V refinement rows of every miss are read over the link
+//                 straight from the pinned store (mapped into the device's
+//                 address space), 16 bytes per lane with several reads in
+//                 flight, into the miss's slot
+// No host step and no synchronization, unless the caller asks for the step's
+// statistics.  Policy on a miss: wait (the step uses every selected
+// refinement).
 #include <string.h>
 
 #include <algorithm>
-#include <vector>
 
 #include "sf_decode_kernels.h"
 
@@ -160,23 +161,38 @@ cache_lookup(DecodeParams p, int32_t* slot_tok, int32_t* stamp, int32_t* tok_slo
   }
 }
 
-// Copy staged rows into their cache slots: one work-group per (sequence, KV
-// head); `first` gives the staging offset of each group's misses.
+// Read the missed rows from the pinned store into their cache slots: grid
+// (sequence x KV head, kFetchWGs); 16-byte pieces (a row is D r / 8 bytes, a
+// multiple of 16), kFetchUnroll reads in flight per lane.
+constexpr int kFetchWGs = 16;
+constexpr int kFetchUnroll = 4;
 __global__ void __launch_bounds__(256)
-cache_install(const int32_t* miss, const int32_t* first, int32_t top_t, int32_t slots, int32_t rb,
-              const uint8_t* stage, uint8_t* cache_data) {
+cache_fetch(const int32_t* miss, int32_t top_t, int32_t hkv, int64_t cap, int32_t slots, int32_t rb,
+            const uint8_t* host_rows, uint8_t* cache_data) {
   const int64_t sk = blockIdx.x;
+  const int kvh = (int)(sk % hkv);
   const int32_t* m = miss + sk * 2 * (int64_t)(top_t + 1);
-  const int32_t nm = m[0];
-  const int64_t f = first[sk];
-  const int words = rb / 4;   // per row
-  for (int64_t i = threadIdx.x; i < (int64_t)nm * 2 * words; i += blockDim.x) {
-    const int64_t k = i / (2 * words);
-    const int64_t rest = i - k * 2 * words;
-    const int32_t slot = m[2 + 2 * k + 1];
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(stage + (f + k) * 2 * (int64_t)rb);
-    uint32_t* dst = reinterpret_cast<uint32_t*>(cache_data + ((sk * slots + slot) * 2) * (int64_t)rb);
-    dst[rest] = src[rest];
+  const int64_t pieces = rb / 16;                  // per row
+  const int64_t items = (int64_t)m[0] * 2 * pieces;
+  const int64_t step = (int64_t)gridDim.y * blockDim.x;
+  for (int64_t i0 = (int64_t)blockIdx.y * blockDim.x + threadIdx.x; i0 < items; i0 += kFetchUnroll * step) {
+    uint4 v[kFetchUnroll];
+    int64_t dst[kFetchUnroll];
+#pragma unroll
+    for (int u = 0; u < kFetchUnroll; ++u) {
+      const int64_t i = i0 + u * step;
+      dst[u] = -1;
+      if (i < items) {
+        const int64_t k = i / (2 * pieces), rest = i - k * 2 * pieces;
+        const int which = (int)(rest / pieces), piece = (int)(rest - which * pieces);
+        const int64_t tok = m[2 + 2 * k], slot = m[2 + 2 * k + 1];
+        v[u] = reinterpret_cast<const uint4*>(host_rows + (((int64_t)which * hkv + kvh) * cap + tok) * rb)[piece];
+        dst[u] = (((sk * slots + slot) * 2 + which) * rb) / 16 + piece;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kFetchUnroll; ++u)
+      if (dst[u] >= 0) reinterpret_cast<uint4*>(cache_data)[dst[u]] = v[u];
   }
 }
 
@@ -192,11 +208,7 @@ static void free_store(sf_store_s* s) {
   if (s->tok_slot) (void)hipFree(s->tok_slot);
   if (s->slot_tok) (void)hipFree(s->slot_tok);
   if (s->stamp) (void)hipFree(s->stamp);
-  if (s->h_stage) (void)hipHostFree(s->h_stage);
-  if (s->d_stage) (void)hipFree(s->d_stage);
   if (s->h_miss) (void)hipHostFree(s->h_miss);
-  if (s->ev_side) (void)hipEventDestroy(s->ev_side);
-  if (s->side) (void)hipStreamDestroy(s->side);
   delete s;
 }
 
@@ -237,6 +249,7 @@ extern "C" sf_status sf_store_create(const sf_geom* geom, int64_t cap_tokens, in
     const int64_t nslots = (int64_t)max_seqs * hkv * s->slots;
     SF_ALLOC(hipHostMalloc((void**)&s->host_rows, rows_bytes, hipHostMallocDefault));
     memset(s->host_rows, 0, rows_bytes);
+    SF_ALLOC(hipHostGetDevicePointer((void**)&s->host_rows_dev, s->host_rows, 0));
     SF_ALLOC(hipMalloc((void**)&s->cache_data, (size_t)nslots * 2 * s->row_bytes));
     SF_ALLOC(hipMalloc((void**)&s->tok_slot, (size_t)hkv * cap_tokens * 4));
     SF_ALLOC(hipMalloc((void**)&s->slot_tok, (size_t)nslots * 4));
@@ -244,12 +257,8 @@ extern "C" sf_status sf_store_create(const sf_geom* geom, int64_t cap_tokens, in
     SF_ALLOC(hipMemset(s->tok_slot, 0xFF, (size_t)hkv * cap_tokens * 4));
     SF_ALLOC(hipMemset(s->slot_tok, 0xFF, (size_t)nslots * 4));
     SF_ALLOC(hipMemset(s->stamp, 0xFF, (size_t)nslots * 4));
-    SF_ALLOC(hipHostMalloc((void**)&s->h_stage, (size_t)nslots * 2 * s->row_bytes, hipHostMallocDefault));
-    SF_ALLOC(hipMalloc((void**)&s->d_stage, (size_t)nslots * 2 * s->row_bytes));
     SF_ALLOC(hipHostMalloc((void**)&s->h_miss, (size_t)max_seqs * hkv * (2 * (s->slots + 1) + 1) * 4,
                            hipHostMallocDefault));
-    SF_ALLOC(hipStreamCreateWithFlags(&s->side, hipStreamNonBlocking));
-    SF_ALLOC(hipEventCreateWithFlags(&s->ev_side, hipEventDisableTiming));
   }
 #undef SF_ALLOC
   *out = s;
@@ -320,44 +329,18 @@ sf_status sf_store_fetch(sf_store s, const DecodeParams& p, int32_t* miss_dev, h
   hipLaunchKernelGGL(cache_lookup, dim3((unsigned)groups), dim3(kLookupThreads), lds, st, p, s->slot_tok,
                      s->stamp, s->tok_slot, step, sort_n, miss_dev);
   SF_LAUNCH_CHECK("cache_lookup");
-  const size_t stride = 2 * (size_t)(p.top_t + 1);
-  SF_HIP_CHECK(hipMemcpyAsync(s->h_miss, miss_dev, groups * stride * 4, hipMemcpyDeviceToHost, st));
-  SF_HIP_CHECK(hipStreamSynchronize(st));
-
-  const int64_t rb = s->row_bytes;
-  const int64_t cap = s->cap;
-  std::vector<int32_t> first(groups);
-  int64_t total = 0;
-  for (int64_t g = 0; g < groups; ++g) {
-    const int32_t* m = s->h_miss + g * stride;
-    const int kvh = (int)(g % hkv);
-    first[g] = (int32_t)total;
-    for (int32_t k = 0; k < m[0]; ++k) {
-      const int64_t tok = m[2 + 2 * k];
-      uint8_t* dst = s->h_stage + (total + k) * 2 * rb;
-      memcpy(dst, s->host_rows + ((int64_t)(0 * hkv + kvh) * cap + tok) * rb, rb);
-      memcpy(dst + rb, s->host_rows + ((int64_t)(1 * hkv + kvh) * cap + tok) * rb, rb);
-    }
-    total += m[0];
-  }
-  if (total > 0) {
-    SF_HIP_CHECK(hipMemcpyAsync(s->d_stage, s->h_stage, (size_t)total * 2 * rb, hipMemcpyHostToDevice, s->side));
-    SF_HIP_CHECK(hipEventRecord(s->ev_side, s->side));
-    SF_HIP_CHECK(hipStreamWaitEvent(st, s->ev_side, 0));
-  }
+  hipLaunchKernelGGL(cache_fetch, dim3((unsigned)groups, kFetchWGs), dim3(256), 0, st, miss_dev, p.top_t, hkv,
+                     s->cap, s->slots, (int32_t)s->row_bytes, s->host_rows_dev, s->cache_data);
+  SF_LAUNCH_CHECK("cache_fetch");
   if (stats) {
+    // the miss counts, for the caller's statistics (this synchronizes)
+    const size_t stride = 2 * (size_t)(p.top_t + 1);
+    SF_HIP_CHECK(hipMemcpyAsync(s->h_miss, miss_dev, groups * stride * 4, hipMemcpyDeviceToHost, st));
+    SF_HIP_CHECK(hipStreamSynchronize(st));
+    int64_t total = 0;
+    for (int64_t g = 0; g < groups; ++g) total += s->h_miss[g * stride];
     stats->misses = total;
-    stats->h2d_bytes = total * 2 * rb;
-  }
-  if (total > 0) {
-    // staging offsets per group, written behind the miss lists in the workspace
-    int32_t* h_first = s->h_miss + groups * stride;
-    memcpy(h_first, first.data(), groups * 4);
-    int32_t* d_first = miss_dev + groups * stride;
-    SF_HIP_CHECK(hipMemcpyAsync(d_first, h_first, groups * 4, hipMemcpyHostToDevice, st));
-    hipLaunchKernelGGL(cache_install, dim3((unsigned)groups), dim3(256), 0, st, miss_dev, d_first, p.top_t,
-                       s->slots, (int32_t)rb, s->d_stage, s->cache_data);
-    SF_LAUNCH_CHECK("cache_install");
+    stats->h2d_bytes = total * 2 * s->row_bytes;
   }
   return SF_OK;
 }
