@@ -50,17 +50,21 @@ __global__ void cache_invalidate(int32_t* slot_tok, int32_t* tok_slot, int64_t n
 }
 
 constexpr int kLookupThreads = 1024;
-constexpr int kMaxSlots = 4096;   // keeps the lookup's sort in LDS (<= 64 KiB)
+constexpr int kMaxSlots = 4096;   // keeps the lookup's keys and lists in LDS (<= 96 KiB)
 
-// One work-group per (sequence, KV head).  Dynamic LDS: sort keys (pow2 >=
-// slots) as uint64 plus one miss flag per selected token.
+// One work-group per (sequence, KV head).  Dynamic LDS: the slots' victim
+// keys (uint64) and selected-resident flags, the misses' ranks and the victim
+// list (top_t each).
 __global__ void __launch_bounds__(kLookupThreads)
-cache_lookup(DecodeParams p, int32_t* slot_tok, int32_t* stamp, int32_t* tok_slot, int32_t step, int32_t sort_n,
-             int32_t* miss) {
-  extern __shared__ uint64_t keys[];
-  uint32_t* flag = reinterpret_cast<uint32_t*>(keys + sort_n);   // [slots]: 1 = selected resident
+cache_lookup(DecodeParams p, int32_t* slot_tok, int32_t* stamp, int32_t* tok_slot, int32_t step, int32_t* miss) {
+  extern __shared__ uint64_t keys[];                              // [slots]: victim keys
+  uint32_t* flag = reinterpret_cast<uint32_t*>(keys + p.slots);   // [slots]: 1 = selected resident
   int32_t* mrank = reinterpret_cast<int32_t*>(flag + p.slots);    // [top_t]: rank among misses, -1 = hit
-  __shared__ uint32_t cnt[kLookupThreads];
+  int32_t* vlist = mrank + p.top_t;                               // [top_t]: victim slots in slot order
+  __shared__ uint32_t cnt[kLookupThreads / 64];
+  __shared__ uint32_t rh[256];
+  __shared__ uint64_t sh_prefix, sh_mask;
+  __shared__ uint32_t sh_left, sh_whole;
 
   const int tid = threadIdx.x;
   const int64_t sk = blockIdx.x;
@@ -75,16 +79,27 @@ cache_lookup(DecodeParams p, int32_t* slot_tok, int32_t* stamp, int32_t* tok_slo
 
   for (int i = tid; i < p.slots; i += kLookupThreads) flag[i] = 0u;
   __syncthreads();
-  // hits are stamped; misses flagged
-  for (int j = tid; j < tn; j += kLookupThreads) {
-    const int64_t g = a + sel[j];
-    const int32_t slot = ts[g];
-    if (slot >= 0) {
-      st_stamp[slot] = step;
-      flag[slot] = 1u;
-      mrank[j] = -1;
-    } else {
-      mrank[j] = 0;
+  // hits are stamped; misses flagged (the loads of a thread's tokens are
+  // issued together: top_t <= slots <= kMaxSlots)
+  static_assert(kMaxSlots <= 4 * kLookupThreads, "four selected tokens per thread at most");
+  int32_t slot4[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int j = tid + u * kLookupThreads;
+    slot4[u] = j < tn ? ts[a + sel[j]] : -1;
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int j = tid + u * kLookupThreads;
+    if (j < tn) {
+      const int32_t slot = slot4[u];
+      if (slot >= 0) {
+        st_stamp[slot] = step;
+        flag[slot] = 1u;
+        mrank[j] = -1;
+      } else {
+        mrank[j] = 0;
+      }
     }
   }
   __syncthreads();
@@ -93,65 +108,98 @@ cache_lookup(DecodeParams p, int32_t* slot_tok, int32_t* stamp, int32_t* tok_slo
   const int j0 = tid * per, j1 = std::min(j0 + per, (int)tn);
   uint32_t c = 0;
   for (int j = j0; j < j1; ++j) c += (mrank[j] == 0);
-  cnt[tid] = c;
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t run = 0;
-    for (int t = 0; t < kLookupThreads; ++t) {
-      const uint32_t v = cnt[t];
-      cnt[t] = run;
-      run += v;
-    }
-    miss[sk * 2 * (int64_t)(p.top_t + 1)] = (int32_t)run;
-  }
-  __syncthreads();
-  uint32_t rk = cnt[tid];
+  uint32_t nmiss;
+  uint32_t rk = block_exclusive_scan<kLookupThreads>(c, cnt, nmiss);
+  if (tid == 0) miss[sk * 2 * (int64_t)(p.top_t + 1)] = (int32_t)nmiss;
   for (int j = j0; j < j1; ++j)
     if (mrank[j] == 0) mrank[j] = (int32_t)(rk++);
-  // victim order: free slots (by slot), then non-selected residents by (stamp, token)
-  for (int i = tid; i < sort_n; i += kLookupThreads) {
+  // Victims: free slots first, then the residents not selected now, oldest
+  // stamp first (lower token first): the nmiss smallest of the keys
+  //   free slot i: i;   resident: 2^62 | (stamp + 1) << 31 | token;
+  // hits and selected slots take no part (~0).  Every key differs, so the
+  // nmiss-th smallest, found by an 8-bit radix select, splits them exactly;
+  // the victims are then listed in slot order (which miss takes which
+  // victim does not change what stays cached).
+  for (int i = tid; i < p.slots; i += kLookupThreads) {
     uint64_t k = ~0ull;
-    if (i < p.slots) {
-      const int32_t tok = st_tok[i];
-      if (tok < 0)
-        k = (uint64_t)i;
-      else if (!flag[i])
-        k = (1ull << 62) | ((uint64_t)(uint32_t)(st_stamp[i] + 1) << 31) | (uint64_t)(uint32_t)tok;
-    }
+    const int32_t tok = st_tok[i];
+    if (tok < 0)
+      k = (uint64_t)i;
+    else if (!flag[i])
+      k = (1ull << 62) | ((uint64_t)(uint32_t)(st_stamp[i] + 1) << 31) | (uint64_t)(uint32_t)tok;
     keys[i] = k;
   }
+  if (tid == 0) {
+    sh_prefix = 0ull;
+    sh_mask = 0ull;
+    sh_left = nmiss;
+    sh_whole = nmiss == 0 ? 1u : 0u;
+  }
   __syncthreads();
-  for (int size = 2; size <= sort_n; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < sort_n; i += kLookupThreads) {
-        const int partner = i ^ stride;
-        if (partner > i) {
-          const bool up = (i & size) == 0;
-          const uint64_t x = keys[i], y = keys[partner];
-          if ((x > y) == up) {
-            keys[i] = y;
-            keys[partner] = x;
+  for (int shift = 56; shift >= 0 && !sh_whole; shift -= 8) {
+    for (int i = tid; i < 256; i += kLookupThreads) rh[i] = 0u;
+    __syncthreads();
+    const uint64_t pre = sh_prefix, msk = sh_mask;
+    for (int i = tid; i < p.slots; i += kLookupThreads) {
+      const uint64_t k = keys[i];
+      if (k != ~0ull && (k & msk) == pre) atomicAdd(&rh[(k >> shift) & 0xFFu], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // bucket holding the sh_left-th smallest: inclusive prefix over the
+      // 256 buckets, 4 per lane in ascending order
+      uint32_t c4[4], sum = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        c4[u] = rh[4 * tid + u];
+        sum += c4[u];
+      }
+      const uint32_t inc = wave_inclusive_scan(sum), left = sh_left;
+      uint32_t below = inc - sum;
+      const uint64_t hit = __ballot(below < left && left <= inc);
+      if (hit && tid == __ffsll((unsigned long long)hit) - 1) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (below < left && left <= below + c4[u]) {
+            sh_prefix = pre | ((uint64_t)(4 * tid + u) << shift);
+            sh_mask = msk | (0xFFull << shift);
+            sh_left = left - below;
+            sh_whole = (c4[u] == left - below) ? 1u : 0u;
+            break;
           }
+          below += c4[u];
         }
       }
-      __syncthreads();
+    }
+    __syncthreads();
+  }
+  // the victims in slot order
+  const uint64_t vpre = sh_prefix, vmsk = sh_mask;
+  const int sper = (p.slots + kLookupThreads - 1) / kLookupThreads;
+  const int s0 = tid * sper, s1 = std::min(s0 + sper, p.slots);
+  uint32_t nv = 0;
+  for (int i = s0; i < s1; ++i) {
+    const uint64_t k = keys[i];
+    nv += (nmiss > 0 && k != ~0ull && (k & vmsk) <= vpre) ? 1u : 0u;
+  }
+  uint32_t vtot;
+  uint32_t vpos = block_exclusive_scan<kLookupThreads>(nv, cnt, vtot);
+  for (int i = s0; i < s1; ++i) {
+    const uint64_t k = keys[i];
+    if (nmiss > 0 && k != ~0ull && (k & vmsk) <= vpre) {
+      if (vpos < (uint32_t)p.top_t) vlist[vpos] = i;
+      ++vpos;
     }
   }
+  __syncthreads();
   // install the mapping of each miss into its victim slot
   int32_t* ml = miss + sk * 2 * (int64_t)(p.top_t + 1) + 2;
   for (int j = tid; j < tn; j += kLookupThreads) {
     const int32_t k = mrank[j];
-    if (k < 0) continue;
-    const uint64_t key = keys[k];
-    if (key == ~0ull) continue;   // fewer victims than misses: cannot happen with slots >= T
-    int32_t slot;
-    if (key < (1ull << 62)) {
-      slot = (int32_t)key;
-    } else {
-      const int32_t old = (int32_t)(key & 0x7FFFFFFFull);
-      slot = ts[old];
-      ts[old] = -1;
-    }
+    if (k < 0 || k >= (int32_t)vtot) continue;   // fewer victims than misses: cannot happen with slots >= T
+    const int32_t slot = vlist[k];
+    const uint64_t key = keys[slot];
+    if (key >= (1ull << 62)) ts[(int32_t)(key & 0x7FFFFFFFull)] = -1;   // the resident leaves
     const int32_t g = (int32_t)(a + sel[j]);
     st_tok[slot] = g;
     st_stamp[slot] = step;
@@ -322,12 +370,10 @@ sf_status sf_store_fetch(sf_store s, const DecodeParams& p, int32_t* miss_dev, h
                          sf_step_stats* stats) {
   const int32_t B = p.batch, hkv = p.hkv;
   const int64_t groups = (int64_t)B * hkv;
-  int sort_n = 1;
-  while (sort_n < s->slots) sort_n <<= 1;
-  const size_t lds = (size_t)sort_n * 8 + (size_t)s->slots * 4 + (size_t)p.top_t * 4;
+  const size_t lds = (size_t)s->slots * 12 + (size_t)p.top_t * 8;
   const int32_t step = s->step++;
   hipLaunchKernelGGL(cache_lookup, dim3((unsigned)groups), dim3(kLookupThreads), lds, st, p, s->slot_tok,
-                     s->stamp, s->tok_slot, step, sort_n, miss_dev);
+                     s->stamp, s->tok_slot, step, miss_dev);
   SF_LAUNCH_CHECK("cache_lookup");
   hipLaunchKernelGGL(cache_fetch, dim3((unsigned)groups, kFetchWGs), dim3(256), 0, st, miss_dev, p.top_t, hkv,
                      s->cap, s->slots, (int32_t)s->row_bytes, s->host_rows_dev, s->cache_data);
