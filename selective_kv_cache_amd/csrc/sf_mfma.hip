@@ -18,10 +18,13 @@
 // the first term a per-head scalar, the second a [heads x tokens] x
 // [tokens x 128] product on v_mfma_f32_16x16x32_f16: the weights p*delta go in
 // as fp16 hi + lo pieces (22 significant bits), the 2-bit codes as fp16
-// subnormals taken straight from the packed bits (a code c at mantissa bit
-// 2t reads as c * 2^(2t-24), exactly; the power of two is undone per tile).
-// The codes of 8 tokens at one element are gathered with one v_perm_b32 per
-// token pair, so the packed rows are read as they are stored.
+// subnormals taken from the packed bits with a shift and a mask (a code c at
+// mantissa bit k reads as c * 2^(k-24), exactly; the power of two is undone
+// per tile).  Every code is placed at bit k >= 4: measured on gfx950, the
+// product's sums lose precision on the smallest subnormals (codes at bit 0
+// gave errors near 1e-4 of the result, bit 2 near 2e-5, bits 4-8 the fp32
+// level, 1e-6).  The codes of 8 tokens at one element are gathered with one
+// v_perm_b32 per token pair, so the packed rows are read as they are stored.
 #include <math.h>
 #include <stddef.h>
 
@@ -474,6 +477,10 @@ __device__ inline void read_stage(uint32_t aL, uint32_t aS, const uint32_t (&aV)
       : "memory");
 }
 
+// Mantissa bit at which the P.V product takes code tt (0-7) of a token's
+// 8-element group.
+constexpr int code_bit(int tt) { return tt < 2 ? 2 * tt + 4 : tt < 5 ? 2 * tt : 2 * tt - 6; }
+
 template <int G, int NW>
 __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh, uint8_t* smem) {
   using Lds = MfmaLds<G, NW>;
@@ -636,18 +643,19 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
     }
     const v8h bw = lds_read_v8h(wtR);
     const uint32_t* vw = R.vw;
-    uint32_t P[4], Q[4];
+    // each 16-bit half of P holds the 8 codes (2 bits each, code tt at bit
+    // 2tt) of one token; code tt goes in at mantissa bit code_bit(tt) >= 4:
+    // codes 0-1 from P << 4, 2-4 from P, 5-7 from P >> 6 (the masks keep
+    // each half's own bits)
+    uint32_t P[4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      P[v] = __builtin_amdgcn_perm(vw[2 * v + 1], vw[2 * v], psel);
-      Q[v] = P[v] >> 10;
-    }
+    for (int v = 0; v < 4; ++v) P[v] = __builtin_amdgcn_perm(vw[2 * v + 1], vw[2 * v], psel);
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
-      const uint32_t msk = 0x00030003u << (2 * (tt <= 4 ? tt : tt - 5));
+      const uint32_t msk = 0x00030003u << code_bit(tt);
       v4u av;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) av[v] = (tt <= 4 ? P[v] : Q[v]) & msk;
+      for (int v = 0; v < 4; ++v) av[v] = (tt < 2 ? P[v] << 4 : tt < 5 ? P[v] : P[v] >> 6) & msk;
       acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, av), bw, acc[tt], 0, 0, 0);
     }
   };
@@ -677,7 +685,7 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   if (n < 2 * G) {
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
-      const float f = __builtin_ldexpf(1.0f, 24 - 2 * (tt <= 4 ? tt : tt - 5) - se);
+      const float f = __builtin_ldexpf(1.0f, 24 - code_bit(tt) - se);
 #pragma unroll
       for (int j = 0; j < 4; ++j) s.u.accw[wid][n][32 * rg + 8 * j + tt] = fmaf(acc[tt][j], f, t1n);
     }

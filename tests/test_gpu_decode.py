@@ -55,6 +55,15 @@ SMALL = [
 ]
 
 
+def test_base_pass_precision():
+    """Every token at base precision (T = 0), so the whole result comes from
+    the base pass's matrix-core P.V product: within 1e-4 of the oracle.  The
+    2-bit codes enter that product at fp16 mantissa bits >= 4; with codes at
+    bit 0 its error on this case was 2.5e-4 (measured 1.8e-5 after)."""
+    _, st = _case(W.small(cfg_id=228, ctx=1000, top_t=0))
+    assert st["max_out_err"] <= 1e-4, st
+
+
 @pytest.mark.parametrize("i", range(len(SMALL)), ids=[",".join(f"{k}={v}" for k, v in o.items()) for o in SMALL])
 def test_small_shapes(i):
     _case(W.small(cfg_id=220 + i, **SMALL[i]))
