@@ -318,6 +318,66 @@ def host_tier_run(w, steps, warmup):
         m.close()
 
 
+def reuse_run(w, stats):
+    """Multi-step reuse run: every layer's cache starts at w.ctx tokens with its
+    refinement rows in pinned host memory; each of w.steps steps appends one
+    token to every layer (quantized on the GPU, its refinement rows put in the
+    store) and decodes with that step's AR(1) query over the grown context.
+    Eager launches; with ``stats`` every decode call waits for its miss lists
+    (hit rate and bytes), otherwise nothing waits on the host but the appends'
+    copies to the store."""
+    import torch
+    from selective_kv_cache_amd import binding as B
+    from selective_kv_cache_amd import workloads as W
+    from selective_kv_cache_amd.kvcache import Decoder, LayerCache
+    g = B.geom(w.head_dim, w.n_q_heads, w.n_kv_heads, w.base_bits, w.refine_bits)
+    n0, steps = w.ctx, w.steps
+    caches, qs, app = [], [], []
+    try:
+        for l in range(w.layers):
+            c = LayerCache(g, n0 + steps, tier=B.SF_TIER_HOST_PINNED, max_seqs=1, cache_slots=2 * w.top_t)
+            caches.append(c)
+            k, v = W.layer_kv(w, l, device="cuda")
+            c.append(k, v, 0)
+            del k, v
+            qs.append(torch.as_tensor(W.queries(w, l, steps), device="cuda"))
+            kv = [W.appended_kv(w, l, t) for t in range(steps)]
+            app.append((torch.as_tensor(np.stack([x[0] for x in kv]), device="cuda"),
+                        torch.as_tensor(np.stack([x[1] for x in kv]), device="cuda")))
+        dec = Decoder(g, W.seq_offsets([n0 + 1]), w.top_t)
+        outs = [torch.empty((1, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+                for _ in range(w.layers)]
+        tot = {"selected": 0, "hits": 0, "misses": 0, "h2d_bytes": 0}
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(steps):
+            dec.set_offsets([0, n0 + t + 1])
+            for l in range(w.layers):
+                caches[l].append(app[l][0][t], app[l][1][t], n0 + t)
+                res = dec.step(caches[l], qs[l][t], out=outs[l], want_stats=stats)
+                if stats:
+                    for k2 in tot:
+                        tot[k2] += res[1][k2]
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / steps
+        return dt, tot
+    finally:
+        for c in caches:
+            c.close()
+
+
+def reuse_record(w):
+    dt, _ = reuse_run(w, stats=False)
+    _, tot = reuse_run(w, stats=True)
+    return {"workload": w.name, "store": "host_pinned", "query_process": f"AR(1) rho={w.rho}",
+            "ctx": [w.ctx + 1, w.ctx + w.steps], "steps": w.steps, "layers": w.layers,
+            "launch": "eager", "ms_per_step": dt * 1e3, "steps_per_s": 1.0 / dt,
+            "hit_rate": tot["hits"] / max(tot["selected"], 1),
+            "h2d_bytes_per_step": tot["h2d_bytes"] / w.steps,
+            "per_step": "append one token to every layer (GPU quantization, refinement rows into the "
+                        "pinned store), then decode every layer"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -410,6 +470,8 @@ def main():
         if w.host_store:
             log("secondary: host-pinned store")
             sec["host_store"] = host_tier_run(w, max(4, args.steps // 2), 2)
+        log("secondary: multi-step reuse run (llama8b_reuse)")
+        sec["reuse"] = reuse_record(W.WORKLOADS["llama8b_reuse"])
         rec["secondary"] = sec
     rec["achievable_read_gbps"] = achievable_read_gbps()
     if not args.no_cpu_baseline:

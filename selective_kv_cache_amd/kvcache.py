@@ -78,6 +78,27 @@ class Decoder:
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         self._hist_clean = False   # a successful step leaves the workspace histogram zero
 
+    def set_offsets(self, seq_off: Sequence[int]) -> None:
+        """Point the decoder at new sequence offsets (a context that grew).
+        The workspace is reallocated, with a quarter to spare, only when the
+        new shape needs more; a reallocated workspace starts uncleared."""
+        self.seq_off = np.asarray(seq_off, dtype=np.int64)
+        lens = np.diff(self.seq_off)
+        batch = len(lens)
+        self.total = int(self.seq_off[-1] - self.seq_off[0])
+        self.max_seq = int(lens.max())
+        if batch != self.batch:
+            self.batch = batch
+            self._hist_clean = False
+        if self.seq_off_dev.numel() == self.seq_off.size:
+            self.seq_off_dev.copy_(torch.as_tensor(self.seq_off))
+        else:
+            self.seq_off_dev = torch.as_tensor(self.seq_off, device=self.device)
+        nbytes = B.sf_decode_workspace_size(self.g, self.batch, self.total, self.max_seq, self.top_t)
+        if nbytes > self.workspace.numel():
+            self.workspace = torch.empty(nbytes + nbytes // 4, dtype=torch.uint8, device=self.device)
+            self._hist_clean = False
+
     def step(self, cache: LayerCache, q: torch.Tensor, out: Optional[torch.Tensor] = None,
              sel_out: Optional[torch.Tensor] = None, scores_out: Optional[torch.Tensor] = None,
              want_stats: bool = False, events=None, stream=None):

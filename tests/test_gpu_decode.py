@@ -231,6 +231,62 @@ def test_host_tier_matches_device_tier_and_cache_simulation():
         host.close()
 
 
+def test_append_steps_host_tier():
+    """Multi-step reuse run, reduced: each step appends one token (quantized on
+    the GPU, its refinement rows put in the pinned store) and decodes over the
+    grown context with an AR(1) query.  Every step: codes, scales and
+    refinement rows of all tokens so far, scores, selection and output against
+    the oracle on the same tokens; host-tier output bit-identical to the
+    device tier's; hits and misses equal to the oracle's cache simulation."""
+    import torch
+    from selective_kv_cache_amd import binding as B
+    from selective_kv_cache_amd.kvcache import Decoder, LayerCache
+    w = W.small("reuse5", cfg_id=305, ctx=2000, n_q_heads=8, n_kv_heads=2, base_bits=3, refine_bits=2,
+                top_t=128, rho=0.9)
+    steps, n0 = 6, 2000
+    g = P.geom_of(w)
+    k, v = W.layer_kv(w, 0)
+    qs = W.queries(w, 0, steps)
+    dev = LayerCache(g, n0 + steps, tier=B.SF_TIER_DEVICE)
+    host = LayerCache(g, n0 + steps, tier=B.SF_TIER_HOST_PINNED, max_seqs=1, cache_slots=2 * w.top_t)
+    try:
+        cuda = lambda x: torch.as_tensor(x, device="cuda")
+        kr, vr = dev.append(cuda(k), cuda(v), 0, keep_refine=True)
+        host.append(cuda(k), cuda(v), 0)
+        sims = [O.CacheSim(2 * w.top_t) for _ in range(w.n_kv_heads)]
+        for t in range(steps):
+            ka, va = W.appended_kv(w, 0, t)
+            kra, vra = dev.append(cuda(ka), cuda(va), n0 + t, keep_refine=True)
+            host.append(cuda(ka), cuda(va), n0 + t)
+            kr, vr = torch.cat([kr, kra], 1), torch.cat([vr, vra], 1)
+            k, v = np.concatenate([k, ka]), np.concatenate([v, va])
+            n = n0 + t + 1
+            off = W.seq_offsets([n])
+            dec = Decoder(g, off, w.top_t)
+            q = cuda(qs[t])
+            sel = torch.full((1, w.n_kv_heads, w.top_t), -7, dtype=torch.int32, device="cuda")
+            scores = torch.empty((w.n_kv_heads, n), dtype=torch.float32, device="cuda")
+            o_dev = dec.step(dev, q, sel_out=sel, scores_out=scores)
+            o_host, st = dec.step(host, q, want_stats=True)
+            torch.cuda.synchronize()
+            assert np.array_equal(o_dev.cpu().numpy().view(np.uint32), o_host.cpu().numpy().view(np.uint32)), t
+            cpu = lambda x: x.cpu().numpy()
+            run = P.GpuRun(out=cpu(o_dev), sel=cpu(sel), scores=cpu(scores), k_codes=cpu(dev.k_codes),
+                           v_codes=cpu(dev.v_codes), k_scales=cpu(dev.k_scales), v_scales=cpu(dev.v_scales),
+                           k_ref=cpu(kr), v_ref=cpu(vr))
+            stats = P.compare_layer(w, k, v, qs[t], off, w.top_t, run)
+            hits = misses = 0
+            for h in range(w.n_kv_heads):
+                hh, mm = sims[h].step(run.sel[0, h], t)
+                hits, misses = hits + hh, misses + mm
+            assert (st["hits"], st["misses"]) == (hits, misses), (t, st, hits, misses)
+            assert st["h2d_bytes"] == O.fetched_bytes(misses, w.head_dim, w.refine_bits)
+            print(t, n, st, stats, flush=True)
+    finally:
+        dev.close()
+        host.close()
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("name,heads", [("llama8b_32k", [(0, 0), (0, 7)]), ("llama8b_128k", [(0, 3)]),
                                         ("qwen8b_b16", [(0, 0), (15, 5)])])
