@@ -132,8 +132,10 @@ sf_status sf_store_destroy(sf_store store);
  *   which        SF_K or SF_V
  *   refine_rows  device, [Hkv][n_tok][D*r/8]
  * Rows already cached on the device for those tokens are invalidated.
- * For SF_TIER_HOST_PINNED the call copies device -> host and returns after
- * the copy has completed (the stream is synchronized).
+ * Stream-ordered for both tiers, nothing waits on the host: refine_rows must
+ * stay valid until `stream` has run the copy.  For SF_TIER_HOST_PINNED a
+ * kernel writes the rows into the pinned store through its mapped device
+ * address (and invalidates in the same launch).
  */
 sf_status sf_refine_store(sf_store store, int32_t which, const uint8_t* refine_rows,
                           int64_t tok_begin, int64_t n_tok, void* stream);
@@ -212,10 +214,13 @@ sf_status sf_decode_workspace_size(const sf_geom* geom, int32_t batch, int64_t t
  *      Ktilde = lo + c * delta + (s + 1/2) * delta / 2^r;
  *   4. out_h = softmax over all tokens of q_h . K* / sqrt(D), applied to V*,
  *      with K*, V* refined for selected tokens and base-precision otherwise.
- * Kernels: score (reads the K codes), select, attention (reads K and V codes
- * again and the refinement rows of the selection), combine.  Device-tier
- * stores and T == 0 need no host round trip; a host-pinned store synchronizes
- * the stream once per call to learn which rows to fetch.
+ * Kernels: score (reads the K codes), select, attention (reads the V codes
+ * and, for 2-bit base codes with G <= 4, the per-head logits the score pass
+ * left, else the K codes again; and the refinement rows of the selection),
+ * combine; a host-pinned
+ * store adds, after the selection, the cache lookup and a kernel that reads
+ * the missed rows over the link.  No call waits on the host unless `stats`
+ * is given with a host-pinned store.
  * The workspace need not be initialised (unless SF_DECODE_HIST_CLEAN is
  * passed); apart from the histogram it leaves zero, its contents are
  * undefined after the call.

@@ -58,7 +58,7 @@ struct sf_store_s {
   int32_t* stamp;          // [max_seqs][Hkv][slots] last step the token was selected
   int32_t step;
   // staging for fetched rows and the miss lists
-  const uint8_t* host_rows_dev;   // host_rows as the device addresses it
+  uint8_t* host_rows_dev;   // host_rows as the device addresses it
   int32_t* h_miss;         // pinned: the miss lists, copied back only for statistics
 };
 

@@ -35,13 +35,24 @@ __global__ void fill_i32(int32_t* p, int64_t n, int32_t v) {
     p[i] = v;
 }
 
-// Forget cached rows of tokens [t0, t1) (their refinement was rewritten).
-__global__ void cache_invalidate(int32_t* slot_tok, int32_t* tok_slot, int64_t n_slots_total, int32_t slots,
-                                 int32_t hkv, int64_t cap, int64_t t0, int64_t t1) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_slots_total;
-       i += (int64_t)gridDim.x * blockDim.x) {
+// Put refinement rows [Hkv][n_tok][rb] of tokens [t0, t0 + n_tok) into the
+// pinned store through its mapped address (16-byte stores over the link, rb
+// is a multiple of 16), and forget cached rows of those tokens (their
+// refinement was rewritten).
+__global__ void store_put(const uint8_t* rows, int64_t n_tok, int64_t t0, int32_t hkv, int64_t cap, int32_t rb,
+                          int32_t which, uint8_t* host_rows, int32_t* slot_tok, int32_t* tok_slot,
+                          int64_t n_slots_total, int32_t slots) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t pieces = rb / 16, per_head = n_tok * pieces;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < hkv * per_head; i += stride) {
+    const int64_t h = i / per_head, rest = i - h * per_head;
+    const int64_t t = rest / pieces, pc = rest - t * pieces;
+    const uint4 v = reinterpret_cast<const uint4*>(rows + (h * n_tok + t) * rb)[pc];
+    reinterpret_cast<uint4*>(host_rows + (((int64_t)which * hkv + h) * cap + t0 + t) * rb)[pc] = v;
+  }
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_slots_total; i += stride) {
     const int32_t tok = slot_tok[i];
-    if (tok >= t0 && tok < t1) {
+    if (tok >= t0 && tok < t0 + n_tok) {
       const int64_t kvh = (i / slots) % hkv;
       tok_slot[kvh * cap + tok] = -1;
       slot_tok[i] = -1;
@@ -338,15 +349,12 @@ extern "C" sf_status sf_refine_store(sf_store s, int32_t which, const uint8_t* r
                                   hipMemcpyDeviceToDevice, hs));
     return SF_OK;
   }
-  uint8_t* dst = s->host_rows + ((size_t)which * hkv * s->cap + tok_begin) * rb;
-  SF_HIP_CHECK(hipMemcpy2DAsync(dst, (size_t)s->cap * rb, refine_rows, width, width, hkv,
-                                hipMemcpyDeviceToHost, hs));
   const int64_t nslots = (int64_t)s->max_seqs * hkv * s->slots;
-  hipLaunchKernelGGL(cache_invalidate, dim3((unsigned)std::min<int64_t>((nslots + 255) / 256, 1024)), dim3(256), 0,
-                     hs, s->slot_tok, s->tok_slot, nslots, s->slots, (int32_t)hkv, s->cap, tok_begin,
-                     tok_begin + n_tok);
-  SF_LAUNCH_CHECK("cache_invalidate");
-  SF_HIP_CHECK(hipStreamSynchronize(hs));
+  const int64_t work = std::max<int64_t>(hkv * n_tok * (int64_t)(rb / 16), nslots);
+  hipLaunchKernelGGL(store_put, dim3((unsigned)std::min<int64_t>((work + 255) / 256, 1024)), dim3(256), 0, hs,
+                     refine_rows, n_tok, tok_begin, (int32_t)hkv, s->cap, (int32_t)rb, which, s->host_rows_dev,
+                     s->slot_tok, s->tok_slot, nslots, s->slots);
+  SF_LAUNCH_CHECK("store_put");
   return SF_OK;
 }
 
