@@ -318,14 +318,16 @@ def host_tier_run(w, steps, warmup):
         m.close()
 
 
-def reuse_run(w, stats):
+def reuse_run(w, stats, skip=False, sample_every=0):
     """Multi-step reuse run: every layer's cache starts at w.ctx tokens with its
     refinement rows in pinned host memory; each of w.steps steps appends one
     token to every layer (quantized on the GPU, its refinement rows put in the
     store) and decodes with that step's AR(1) query over the grown context.
     Eager launches; with ``stats`` every decode call waits for its miss lists
-    (hit rate and bytes), otherwise nothing waits on the host but the appends'
-    copies to the store."""
+    (hit rate and bytes), otherwise nothing waits on the host.  ``skip``:
+    policy "skip" on a refinement-cache miss.  With ``sample_every`` > 0 the
+    outputs of every layer at steps sample_every - 1, 2 sample_every - 1, ...
+    are returned as well (copied after the timed region ends)."""
     import torch
     from selective_kv_cache_amd import binding as B
     from selective_kv_cache_amd import workloads as W
@@ -348,34 +350,48 @@ def reuse_run(w, stats):
         outs = [torch.empty((1, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
                 for _ in range(w.layers)]
         tot = {"selected": 0, "hits": 0, "misses": 0, "h2d_bytes": 0}
+        kept = []
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for t in range(steps):
             dec.set_offsets([0, n0 + t + 1])
+            keep = sample_every > 0 and (t + 1) % sample_every == 0
             for l in range(w.layers):
                 caches[l].append(app[l][0][t], app[l][1][t], n0 + t)
-                res = dec.step(caches[l], qs[l][t], out=outs[l], want_stats=stats)
+                out = torch.empty_like(outs[l]) if keep else outs[l]
+                res = dec.step(caches[l], qs[l][t], out=out, want_stats=stats, skip_misses=skip)
+                if keep:
+                    kept.append(out)
                 if stats:
                     for k2 in tot:
                         tot[k2] += res[1][k2]
         torch.cuda.synchronize()
         dt = (time.perf_counter() - t0) / steps
-        return dt, tot
+        return dt, tot, [x.cpu().numpy() for x in kept]
     finally:
         for c in caches:
             c.close()
 
 
 def reuse_record(w):
-    dt, _ = reuse_run(w, stats=False)
-    _, tot = reuse_run(w, stats=True)
+    """The multi-step reuse run under the two policies on a miss: "wait"
+    (every selected token refined) and "skip" (misses at base precision this
+    step, fetched beside the attention for later steps), with the skip run's
+    output difference from the wait run on every layer at every 16th step."""
+    dt, _, o_wait = reuse_run(w, stats=False, sample_every=16)
+    _, tot, _ = reuse_run(w, stats=True)
+    dt_s, _, o_skip = reuse_run(w, stats=False, skip=True, sample_every=16)
+    diff = np.concatenate([np.abs(a - b).ravel() for a, b in zip(o_skip, o_wait)])
     return {"workload": w.name, "store": "host_pinned", "query_process": f"AR(1) rho={w.rho}",
             "ctx": [w.ctx + 1, w.ctx + w.steps], "steps": w.steps, "layers": w.layers,
             "launch": "eager", "ms_per_step": dt * 1e3, "steps_per_s": 1.0 / dt,
             "hit_rate": tot["hits"] / max(tot["selected"], 1),
             "h2d_bytes_per_step": tot["h2d_bytes"] / w.steps,
             "per_step": "append one token to every layer (GPU quantization, refinement rows into the "
-                        "pinned store), then decode every layer"}
+                        "pinned store), then decode every layer",
+            "skip_on_miss": {"ms_per_step": dt_s * 1e3, "steps_per_s": 1.0 / dt_s,
+                             "out_diff_vs_wait_max": float(diff.max()), "out_diff_vs_wait_mean": float(diff.mean()),
+                             "compared": f"every layer's output at every 16th step ({len(o_skip)} outputs)"}}
 
 
 def main():

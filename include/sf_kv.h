@@ -160,6 +160,20 @@ typedef struct sf_step_stats {
  * zero-filled.  Do not pass it after a failed step. */
 #define SF_DECODE_HIST_CLEAN 1
 
+/* sf_decode_args.flags: policy "skip" on a refinement-cache miss (page
+ * "StrataFlux -- Selective precision streaming -- What does it mean?",
+ * paragraph "The map app also loads tiles ...": on a miss the runtime may
+ * use the low-bit value now while the bits are loaded for later steps).
+ * With a host-pinned store, a selected token whose refinement rows are not
+ * cached takes part in this step at base precision; its rows are read over
+ * the link on the store's own side stream, beside the attention, and
+ * installed for later steps (the store's next call waits for that read).
+ * Hits, misses and bytes are counted as under the default policy, "wait",
+ * where every miss is fetched before the attention.  No effect with a
+ * device-tier store (nothing misses).  A step with this flag must not be
+ * captured into a graph (it forks onto the side stream). */
+#define SF_DECODE_SKIP_MISSES 2
+
 typedef struct sf_decode_args {
   int32_t batch;                 /* B >= 1 sequences                                    */
   const int64_t* seq_off_host;   /* host [B+1], nondecreasing, every sequence non-empty,
@@ -184,7 +198,7 @@ typedef struct sf_decode_args {
                                     lists: pass NULL to keep the step asynchronous)     */
   void* workspace;               /* device scratch of sf_decode_workspace_size() bytes  */
   size_t workspace_bytes;
-  int32_t flags;                 /* 0 or SF_DECODE_HIST_CLEAN                           */
+  int32_t flags;                 /* 0, SF_DECODE_HIST_CLEAN, SF_DECODE_SKIP_MISSES       */
   void* start_events[5];         /* optional hipEvent_t pairs (NULL = none) that time the */
   void* events[5];               /* step's kernels: start_events[k] is recorded just
                                     before kernel k is dispatched, events[k] completes

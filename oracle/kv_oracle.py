@@ -215,21 +215,25 @@ class HeadResult:
 
 
 def decode_head(q_group: np.ndarray, kc: QuantRows, vc: QuantRows, t: int,
-                sel: Optional[np.ndarray] = None) -> HeadResult:
+                sel: Optional[np.ndarray] = None, refined: Optional[np.ndarray] = None) -> HeadResult:
     """One (sequence, KV head): score, select, refine the selection, attend.
 
     ``kc``/``vc`` hold the head's rows [N][D].  ``sel`` overrides the
     selection (used to check the attention step for another valid selection
-    when two selections differ only at a tie within the allowed tolerance)."""
+    when two selections differ only at a tie within the allowed tolerance).
+    ``refined`` (O8, the skip policy) names the selected tokens whose
+    refinement is at hand; the others take part at base precision.  By
+    default every selected token is refined."""
     k_hat = dequant_base(kc)
     v_hat = dequant_base(vc)
     s = token_scores(q_group, k_hat)
     sel = select_top_t(s, t) if sel is None else np.sort(np.asarray(sel, dtype=np.int64))
+    ref = sel if refined is None else np.sort(np.asarray(refined, dtype=np.int64))
     k_star = k_hat.copy()
     v_star = v_hat.copy()
-    if sel.size:
-        k_star[sel] = dequant_refined(_take(kc, sel))
-        v_star[sel] = dequant_refined(_take(vc, sel))
+    if ref.size:
+        k_star[ref] = dequant_refined(_take(kc, ref))
+        v_star[ref] = dequant_refined(_take(vc, ref))
     return HeadResult(scores=s, sel=sel, out=attend(q_group, k_star, v_star))
 
 
@@ -290,6 +294,13 @@ class CacheSim:
 
     def step(self, sel: np.ndarray, t: int) -> Tuple[int, int]:
         """Apply one step's selection; returns (hits, misses)."""
+        hits, misses = self.step_tokens(sel, t)
+        return len(hits), len(misses)
+
+    def step_tokens(self, sel: np.ndarray, t: int) -> Tuple[List[int], List[int]]:
+        """Apply one step's selection; returns the hit and the missed tokens
+        (ascending).  Under the skip policy (O8) the hits are the tokens that
+        step refines."""
         sel = [int(x) for x in np.sort(np.asarray(sel))]
         if len(sel) > self.n_slots:
             raise ValueError("cache smaller than the selection")
@@ -307,8 +318,17 @@ class CacheSim:
         for x, slot in zip(misses, victims):
             self.slot_tok[slot] = x
             self.stamp[slot] = t
-        return len(hits), len(misses)
+        return hits, misses
 
+
+# ---------------------------------------------------------------------------
+# O8: policy on a miss (EXPLAINER, "The map app also loads tiles ...": on a
+# miss the runtime may wait for the bits, or use the low-bit value now while
+# the bits are loaded for later steps).  "wait" is O6 with every selected
+# token refined.  "skip": the step refines only the hits of O6's lookup; the
+# misses take part at base precision and are installed in the cache all the
+# same (they are there at the next step): decode_head(..., refined=hits).
+# ---------------------------------------------------------------------------
 
 def fetched_bytes(misses: int, head_dim: int, r: int) -> int:
     """Bytes that cross the link for ``misses`` tokens: K and V refinement rows."""

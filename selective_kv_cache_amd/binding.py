@@ -20,6 +20,7 @@ SF_OK, SF_ERR_INVALID_ARG, SF_ERR_UNSUPPORTED, SF_ERR_HIP, SF_ERR_OOM, SF_ERR_TI
 SF_TIER_DEVICE, SF_TIER_HOST_PINNED = 0, 1
 SF_K, SF_V = 0, 1
 SF_DECODE_HIST_CLEAN = 1
+SF_DECODE_SKIP_MISSES = 2
 
 c_i32, c_i64, c_vp, c_size = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
 

@@ -136,6 +136,7 @@ struct SelLds {
   uint32_t vt[NW][TPW][4 * BB + 1];
   uint32_t vr[NW][TPW][33];
   float2 vsc[NW][TPW], ksc[NW][TPW];
+  float hsub[NW][TPW];               // 2^-r, or 1 for a skipped miss (base precision)
   float lgt[NW][TPW][G];             // base logits from the score pass
   float wt[NW][G][TPW];
   float mred[NW][G], mall[NW][G], lw[NW][G];
@@ -224,7 +225,12 @@ __device__ inline void selected_block(const DecodeParams& p, int blk, int kvh, u
     const int64_t j = lo + wid * TPW + tl;
     const bool loader = lane < 4 * TPW;
     const bool valid = loader && j < hi;
-    const int64_t tok = valid ? a + p.sel[sk * p.top_t + j] : 0;
+    // a selected token marked as ~token (a refinement-cache miss under the
+    // skip policy) takes part at base precision: no refinement rows, and
+    // its sub-bin factor 1 with zero codes gives the bin centre
+    const int32_t e = valid ? p.sel[sk * p.top_t + j] : 0;
+    const bool refined = e >= 0;
+    const int64_t tok = a + (e >= 0 ? e : ~e);
     uint32_t kb[BB], kr[8], vb[BB], vr[8];
     float lg[G];
     float2 ksc = make_float2(0.f, 0.f), vsc = make_float2(0.f, 0.f);
@@ -238,8 +244,8 @@ __device__ inline void selected_block(const DecodeParams& p, int blk, int kvh, u
       const int64_t row = (int64_t)kvh * p.cap + tok;
       const uint32_t* srck = reinterpret_cast<const uint32_t*>(p.kc + row * (16 * BB)) + qd * BB;
       const uint32_t* srcv = reinterpret_cast<const uint32_t*>(p.vc + row * (16 * BB)) + qd * BB;
-      const uint32_t* rk = refine_row(p, sk, kvh, tok, 0) + qd * r;
-      const uint32_t* rv = refine_row(p, sk, kvh, tok, 1) + qd * r;
+      const uint32_t* rk = refined ? refine_row(p, sk, kvh, tok, 0) + qd * r : nullptr;
+      const uint32_t* rv = refined ? refine_row(p, sk, kvh, tok, 1) + qd * r : nullptr;
       if (LG) {
         const float* lgs = p.logits + ((int64_t)kvh * p.ntot + (tok - p.off0)) * G;
 #pragma unroll
@@ -252,8 +258,8 @@ __device__ inline void selected_block(const DecodeParams& p, int blk, int kvh, u
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        kr[i] = i < r ? rk[i] : 0u;
-        vr[i] = i < r ? rv[i] : 0u;
+        kr[i] = refined && i < r ? rk[i] : 0u;
+        vr[i] = refined && i < r ? rv[i] : 0u;
       }
       ksc = reinterpret_cast<const float2*>(p.ks)[row];
       vsc = reinterpret_cast<const float2*>(p.vs)[row];
@@ -275,6 +281,7 @@ __device__ inline void selected_block(const DecodeParams& p, int blk, int kvh, u
         for (int i = 4 * r; i < 33; ++i) s.kq[wid][tl][i] = s.vr[wid][tl][i] = 0u;
         s.ksc[wid][tl] = ksc;
         s.vsc[wid][tl] = vsc;
+        s.hsub[wid][tl] = refined ? sub : 1.0f;
 #pragma unroll
         for (int h = 0; h < G; ++h) s.lgt[wid][tl][h] = lg[h];
       }
@@ -299,15 +306,16 @@ __device__ inline void selected_block(const DecodeParams& p, int blk, int kvh, u
     default: lane_dots<BB, 8, G, EPL, LG>(kbrow, krrow, &s.qs[0][0], e0, dc, ds, dq); break;
   }
   const float2 ksc = s.ksc[wid][tc];
+  const float hs = s.hsub[wid][tc];
   float lr[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const float qsum = token_sum<LPT>(dq[h]);
     if (LG)
       lr[h] = fmaf(s.lgt[wid][tc][h], 0.6931471805599453f,
-                   ksc.y * kRsqrtD * fmaf(sub, token_sum<LPT>(ds[h]), 0.5f * (sub - 1.0f) * qsum));
+                   ksc.y * kRsqrtD * fmaf(hs, token_sum<LPT>(ds[h]), 0.5f * (hs - 1.0f) * qsum));
     else
-      lr[h] = (ksc.x * qsum + ksc.y * (token_sum<LPT>(dc[h]) + (token_sum<LPT>(ds[h]) + 0.5f * qsum) * sub)) *
+      lr[h] = (ksc.x * qsum + ksc.y * (token_sum<LPT>(dc[h]) + (token_sum<LPT>(ds[h]) + 0.5f * qsum) * hs)) *
               kRsqrtD;
     const float mv = wave_max_dpp(valid ? lr[h] : -INFINITY);
     if (lane == 0) s.mred[wid][h] = mv;
@@ -341,8 +349,9 @@ __device__ inline void selected_block(const DecodeParams& p, int blk, int kvh, u
     const float c0 = (float)(cc & ((1u << BB) - 1u)), c1 = (float)((cc >> BB) & ((1u << BB) - 1u));
     const float s0 = (float)(rr & rmask), s1 = (float)((rr >> r) & rmask);
     const float2 sc = s.vsc[wid][jj];
-    const float v0 = fmaf((s0 + 0.5f) * sub, sc.y, fmaf(c0, sc.y, sc.x));
-    const float v1 = fmaf((s1 + 0.5f) * sub, sc.y, fmaf(c1, sc.y, sc.x));
+    const float hj = s.hsub[wid][jj];
+    const float v0 = fmaf((s0 + 0.5f) * hj, sc.y, fmaf(c0, sc.y, sc.x));
+    const float v1 = fmaf((s1 + 0.5f) * hj, sc.y, fmaf(c1, sc.y, sc.x));
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float w = s.wt[wid][h][jj];

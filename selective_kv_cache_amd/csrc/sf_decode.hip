@@ -97,7 +97,6 @@ Carve carve(const sf_geom& g, int32_t batch, int64_t total_tokens, int64_t max_s
   c.bitmap = at; at += align256((size_t)batch * hkv * bm_words * 4);
   c.sel = at; at += align256((size_t)batch * hkv * t * 4);
   c.part = at; at += align256((size_t)hkv * n_part_bound * grp * kPartStride * 4);
-  c.miss = at; at += align256((size_t)batch * hkv * (2 * (t + 1) + 1) * 4);
   c.total = at;
   return c;
 }
@@ -123,8 +122,7 @@ static int device_cus() {
 using namespace sfk;
 
 // Host-tier fetch (sf_store.hip): lookup, copy of the misses, install.
-sf_status sf_store_fetch(sf_store store, const DecodeParams& p, int32_t* miss_dev, hipStream_t st,
-                         sf_step_stats* stats);
+sf_status sf_store_fetch(sf_store store, const DecodeParams& p, hipStream_t st, bool skip, sf_step_stats* stats);
 
 extern "C" sf_status sf_decode_workspace_size(const sf_geom* geom, int32_t batch, int64_t total_tokens,
                                               int64_t max_seq_tokens, int32_t top_t, size_t* bytes) {
@@ -147,7 +145,7 @@ extern "C" sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* a
   if (s != SF_OK) return s;
   if (!a || a->batch <= 0 || !a->seq_off_host || !a->seq_off_dev || !a->q || !a->k_codes ||
       !a->k_scales || !a->v_codes || !a->v_scales || !a->out || !a->workspace || a->cap <= 0 ||
-      a->top_t < 0 || (a->flags & ~SF_DECODE_HIST_CLEAN) != 0)
+      a->top_t < 0 || (a->flags & ~(SF_DECODE_HIST_CLEAN | SF_DECODE_SKIP_MISSES)) != 0)
     return SF_ERR_INVALID_ARG;
   const int32_t B = a->batch;
   const int64_t* off = a->seq_off_host;
@@ -274,7 +272,7 @@ extern "C" sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* a
     a->stats->selected = sel * p.hkv;
   }
   if (refine && a->store->tier == SF_TIER_HOST_PINNED) {
-    s = sf_store_fetch(a->store, p, reinterpret_cast<int32_t*>(ws + c.miss), hs, a->stats);
+    s = sf_store_fetch(a->store, p, hs, (a->flags & SF_DECODE_SKIP_MISSES) != 0, a->stats);
     if (s != SF_OK) return s;
     if (a->stats) a->stats->hits = a->stats->selected - a->stats->misses;
   }

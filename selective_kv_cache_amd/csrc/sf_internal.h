@@ -26,7 +26,7 @@ __host__ __device__ inline uint32_t score_key(float s) {
 
 // Workspace carve-out (byte offsets from the workspace base).
 struct Carve {
-  size_t scores, logits, hist, counters, cand, bitmap, sel, part, miss, total;
+  size_t scores, logits, hist, counters, cand, bitmap, sel, part, total;
 };
 
 int32_t choose_split(int64_t total_tokens, int32_t n_kv_heads, int32_t groups);
@@ -60,6 +60,12 @@ struct sf_store_s {
   // staging for fetched rows and the miss lists
   uint8_t* host_rows_dev;   // host_rows as the device addresses it
   int32_t* h_miss;         // pinned: the miss lists, copied back only for statistics
+  int32_t* miss;           // [max_seqs][Hkv][2 (slots + 1)]: the last lookup's miss lists
+  // skip-on-miss steps fetch on a side stream (default priority); the next
+  // call on the store waits for `fetched` when `fetch_pending`
+  hipStream_t side;
+  hipEvent_t looked_up, fetched;
+  int32_t fetch_pending;
 };
 
 #define SF_HIP_CHECK(call)                                   \

@@ -67,7 +67,8 @@ constexpr int kMaxSlots = 4096;   // keeps the lookup's keys and lists in LDS (<
 // keys (uint64) and selected-resident flags, the misses' ranks and the victim
 // list (top_t each).
 __global__ void __launch_bounds__(kLookupThreads)
-cache_lookup(DecodeParams p, int32_t* slot_tok, int32_t* stamp, int32_t* tok_slot, int32_t step, int32_t* miss) {
+cache_lookup(DecodeParams p, int32_t* slot_tok, int32_t* stamp, int32_t* tok_slot, int32_t step, int32_t* miss,
+             int32_t mark_misses) {
   extern __shared__ uint64_t keys[];                              // [slots]: victim keys
   uint32_t* flag = reinterpret_cast<uint32_t*>(keys + p.slots);   // [slots]: 1 = selected resident
   int32_t* mrank = reinterpret_cast<int32_t*>(flag + p.slots);    // [top_t]: rank among misses, -1 = hit
@@ -217,6 +218,9 @@ cache_lookup(DecodeParams p, int32_t* slot_tok, int32_t* stamp, int32_t* tok_slo
     ts[g] = slot;
     ml[2 * k] = g;
     ml[2 * k + 1] = slot;
+    // skip on a miss: the attention takes this token at base precision (its
+    // rows arrive for later steps); the entry is marked as ~token
+    if (mark_misses) const_cast<int32_t*>(sel)[j] = ~sel[j];
   }
 }
 
@@ -268,6 +272,10 @@ static void free_store(sf_store_s* s) {
   if (s->slot_tok) (void)hipFree(s->slot_tok);
   if (s->stamp) (void)hipFree(s->stamp);
   if (s->h_miss) (void)hipHostFree(s->h_miss);
+  if (s->miss) (void)hipFree(s->miss);
+  if (s->looked_up) (void)hipEventDestroy(s->looked_up);
+  if (s->fetched) (void)hipEventDestroy(s->fetched);
+  if (s->side) (void)hipStreamDestroy(s->side);
   delete s;
 }
 
@@ -318,6 +326,10 @@ extern "C" sf_status sf_store_create(const sf_geom* geom, int64_t cap_tokens, in
     SF_ALLOC(hipMemset(s->stamp, 0xFF, (size_t)nslots * 4));
     SF_ALLOC(hipHostMalloc((void**)&s->h_miss, (size_t)max_seqs * hkv * (2 * (s->slots + 1) + 1) * 4,
                            hipHostMallocDefault));
+    SF_ALLOC(hipMalloc((void**)&s->miss, (size_t)max_seqs * hkv * (2 * (s->slots + 1) + 1) * 4));
+    SF_ALLOC(hipStreamCreateWithFlags(&s->side, hipStreamNonBlocking));
+    SF_ALLOC(hipEventCreateWithFlags(&s->looked_up, hipEventDisableTiming));
+    SF_ALLOC(hipEventCreateWithFlags(&s->fetched, hipEventDisableTiming));
   }
 #undef SF_ALLOC
   *out = s;
@@ -329,6 +341,15 @@ extern "C" sf_status sf_store_destroy(sf_store store) {
   if (!store) return SF_ERR_INVALID_ARG;
   (void)hipDeviceSynchronize();
   free_store(store);
+  return SF_OK;
+}
+
+// A skip-step fetch still in flight on the side stream: `st` waits for it.
+static sf_status wait_side_fetch(sf_store_s* s, hipStream_t st) {
+  if (s->fetch_pending) {
+    SF_HIP_CHECK(hipStreamWaitEvent(st, s->fetched, 0));
+    s->fetch_pending = 0;
+  }
   return SF_OK;
 }
 
@@ -349,6 +370,8 @@ extern "C" sf_status sf_refine_store(sf_store s, int32_t which, const uint8_t* r
                                   hipMemcpyDeviceToDevice, hs));
     return SF_OK;
   }
+  const sf_status ws = wait_side_fetch(s, hs);
+  if (ws != SF_OK) return ws;
   const int64_t nslots = (int64_t)s->max_seqs * hkv * s->slots;
   const int64_t work = std::max<int64_t>(hkv * n_tok * (int64_t)(rb / 16), nslots);
   hipLaunchKernelGGL(store_put, dim3((unsigned)std::min<int64_t>((work + 255) / 256, 1024)), dim3(256), 0, hs,
@@ -363,6 +386,8 @@ extern "C" sf_status sf_store_clear_cache(sf_store s, void* stream) {
   if (!s) return SF_ERR_INVALID_ARG;
   if (s->tier != SF_TIER_HOST_PINNED) return SF_OK;
   hipStream_t hs = (hipStream_t)stream;
+  const sf_status ws = wait_side_fetch(s, hs);
+  if (ws != SF_OK) return ws;
   const int64_t hkv = s->g.n_kv_heads;
   const int64_t nslots = (int64_t)s->max_seqs * hkv * s->slots;
   hipLaunchKernelGGL(fill_i32, dim3(1024), dim3(256), 0, hs, s->tok_slot, hkv * s->cap, -1);
@@ -372,20 +397,37 @@ extern "C" sf_status sf_store_clear_cache(sf_store s, void* stream) {
   return SF_OK;
 }
 
-// Host tier: look up the selection in the device cache, fetch the misses over
-// the link and install them.  Synchronizes `st` once to read the miss lists.
-sf_status sf_store_fetch(sf_store s, const DecodeParams& p, int32_t* miss_dev, hipStream_t st,
-                         sf_step_stats* stats) {
+// Host tier: look up the selection in the device cache, install the misses
+// and fetch their rows over the link.  Policy "wait": the fetch runs on `st`
+// before the attention.  Policy "skip": the lookup marks the misses in the
+// selection list (the attention takes them at base precision) and the fetch
+// runs on the store's side stream, overlapping the rest of the step; the
+// store's next call waits for it.  Nothing waits on the host unless `stats`.
+sf_status sf_store_fetch(sf_store s, const DecodeParams& p, hipStream_t st, bool skip, sf_step_stats* stats) {
   const int32_t B = p.batch, hkv = p.hkv;
   const int64_t groups = (int64_t)B * hkv;
   const size_t lds = (size_t)s->slots * 12 + (size_t)p.top_t * 8;
   const int32_t step = s->step++;
+  int32_t* miss_dev = s->miss;
+  // the previous skip step's fetch reads the miss lists and fills slots
+  const sf_status ws = wait_side_fetch(s, st);
+  if (ws != SF_OK) return ws;
   hipLaunchKernelGGL(cache_lookup, dim3((unsigned)groups), dim3(kLookupThreads), lds, st, p, s->slot_tok,
-                     s->stamp, s->tok_slot, step, miss_dev);
+                     s->stamp, s->tok_slot, step, miss_dev, skip ? 1 : 0);
   SF_LAUNCH_CHECK("cache_lookup");
-  hipLaunchKernelGGL(cache_fetch, dim3((unsigned)groups, kFetchWGs), dim3(256), 0, st, miss_dev, p.top_t, hkv,
+  hipStream_t fs = st;
+  if (skip) {
+    SF_HIP_CHECK(hipEventRecord(s->looked_up, st));
+    SF_HIP_CHECK(hipStreamWaitEvent(s->side, s->looked_up, 0));
+    fs = s->side;
+  }
+  hipLaunchKernelGGL(cache_fetch, dim3((unsigned)groups, kFetchWGs), dim3(256), 0, fs, miss_dev, p.top_t, hkv,
                      s->cap, s->slots, (int32_t)s->row_bytes, s->host_rows_dev, s->cache_data);
   SF_LAUNCH_CHECK("cache_fetch");
+  if (skip) {
+    SF_HIP_CHECK(hipEventRecord(s->fetched, s->side));
+    s->fetch_pending = 1;
+  }
   if (stats) {
     // the miss counts, for the caller's statistics (this synchronizes)
     const size_t stride = 2 * (size_t)(p.top_t + 1);

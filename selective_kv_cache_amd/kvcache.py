@@ -101,11 +101,15 @@ class Decoder:
 
     def step(self, cache: LayerCache, q: torch.Tensor, out: Optional[torch.Tensor] = None,
              sel_out: Optional[torch.Tensor] = None, scores_out: Optional[torch.Tensor] = None,
-             want_stats: bool = False, events=None, stream=None):
+             want_stats: bool = False, events=None, stream=None, skip_misses: bool = False):
+        """One decode step of one layer.  ``skip_misses``: policy "skip" on
+        a refinement-cache miss (SF_DECODE_SKIP_MISSES)."""
         if out is None:
             out = torch.empty((self.batch, self.g.n_q_heads, self.g.head_dim), dtype=torch.float32,
                               device=self.device)
         flags = B.SF_DECODE_HIST_CLEAN if self._hist_clean else 0
+        if skip_misses:
+            flags |= B.SF_DECODE_SKIP_MISSES
         self._hist_clean = False
         st = B.sf_decode_step(self.g, seq_off_host=self.seq_off, seq_off_dev=self.seq_off_dev, q=q,
                               k_codes=cache.k_codes, k_scales=cache.k_scales, v_codes=cache.v_codes,

@@ -287,6 +287,65 @@ def test_append_steps_host_tier():
         host.close()
 
 
+def test_skip_misses_host_tier():
+    """Policy "skip" on a miss over AR(1) steps, a token appended before each:
+    the output against the oracle with only the cache's hits refined (the
+    misses at base precision), hits and misses as the oracle's cache
+    simulation, and, at a step where nothing misses (the last query
+    repeated), bit-identical to the "wait" policy."""
+    import torch
+    from selective_kv_cache_amd import binding as B
+    from selective_kv_cache_amd.kvcache import Decoder, LayerCache
+    w = W.small("skip", cfg_id=306, ctx=2500, n_q_heads=8, n_kv_heads=2, base_bits=2, refine_bits=4,
+                top_t=128, rho=0.9)
+    steps, n0 = 5, 2500
+    g = P.geom_of(w)
+    k, v = W.layer_kv(w, 0)
+    qs = W.queries(w, 0, steps)
+    qs = np.concatenate([qs, qs[-1:]])                     # the last query again: every selected token cached
+    mk = lambda: LayerCache(g, n0 + steps + 1, tier=B.SF_TIER_HOST_PINNED, max_seqs=1,
+                            cache_slots=2 * w.top_t)
+    wait, skip = mk(), mk()
+    try:
+        cuda = lambda x: torch.as_tensor(x, device="cuda")
+        for c in (wait, skip):
+            c.append(cuda(k), cuda(v), 0)
+        sims = [O.CacheSim(2 * w.top_t) for _ in range(w.n_kv_heads)]
+        n = n0
+        for t in range(qs.shape[0]):
+            if t < steps:
+                ka, va = W.appended_kv(w, 0, t)
+                for c in (wait, skip):
+                    c.append(cuda(ka), cuda(va), n)
+                k, v = np.concatenate([k, ka]), np.concatenate([v, va])
+                n += 1
+            dec = Decoder(g, W.seq_offsets([n]), w.top_t)
+            q = cuda(qs[t])
+            sel = torch.full((1, w.n_kv_heads, w.top_t), -7, dtype=torch.int32, device="cuda")
+            o_wait = dec.step(wait, q).cpu().numpy()
+            o_skip, st = dec.step(skip, q, sel_out=sel, want_stats=True, skip_misses=True)
+            o_skip, sel = o_skip.cpu().numpy(), sel.cpu().numpy()
+            oc = O.quantize_cache(k, v, w.base_bits, w.refine_bits)
+            hits = misses = 0
+            worst = 0.0
+            for h in range(w.n_kv_heads):
+                hit_toks, miss_toks = sims[h].step_tokens(sel[0, h], t)
+                hits, misses = hits + len(hit_toks), misses + len(miss_toks)
+                qg = qs[t][0, h * w.group:(h + 1) * w.group]
+                ref = O.decode_head(qg, O._rows(oc.k, h, 0, n), O._rows(oc.v, h, 0, n), w.top_t,
+                                    sel=sel[0, h], refined=np.asarray(hit_toks, dtype=np.int64))
+                worst = max(worst, float(np.abs(o_skip[0, h * w.group:(h + 1) * w.group] - ref.out).max()))
+            assert worst <= P.OUT_ATOL, (t, worst)
+            assert (st["hits"], st["misses"]) == (hits, misses), (t, st, hits, misses)
+            if misses == 0:
+                assert np.array_equal(o_skip.view(np.uint32), o_wait.view(np.uint32)), t
+            print(t, n, st, "max err", worst, "vs wait", float(np.abs(o_skip - o_wait).max()), flush=True)
+        assert misses == 0                                    # the repeated query hit everything
+    finally:
+        wait.close()
+        skip.close()
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("name,heads", [("llama8b_32k", [(0, 0), (0, 7)]), ("llama8b_128k", [(0, 3)]),
                                         ("qwen8b_b16", [(0, 0), (15, 5)])])

@@ -270,9 +270,39 @@ def pin_cache_invariants():
         assert sim.step(sel, step) == (t, 0)
 
 
+def pin_skip_policy():
+    """Policy "skip" (O8).  With nothing cached the step refines nothing: the
+    T=0 step, pinned by textbook attention above.  With the whole selection
+    cached it is the "wait" step.  The hits of a hand-traced 4-slot cache are
+    those the trace gives (free slots first, then the oldest stamp, then the
+    lower token)."""
+    x_k, x_v = _rows(21, 120, 64), _rows(22, 120, 64, outliers=0)
+    q = np.random.default_rng(23).standard_normal((2, 64))
+    kc, vc = O.quantize_rows(x_k, 2, 2), O.quantize_rows(x_v, 2, 2)
+    t = 10
+    wait = O.decode_head(q, kc, vc, t)
+    cold = O.decode_head(q, kc, vc, t, refined=np.zeros(0, dtype=np.int64))
+    np.testing.assert_array_equal(cold.sel, wait.sel)
+    np.testing.assert_allclose(cold.out, O.decode_head(q, kc, vc, 0).out, rtol=0, atol=1e-12)
+    assert np.abs(cold.out - wait.out).max() > 1e-6          # refinement changes the result
+    sim = O.CacheSim(2 * t)
+    assert sim.step_tokens(wait.sel, 0) == ([], wait.sel.tolist())
+    hits, misses = sim.step_tokens(wait.sel, 1)               # the same selection: all cached
+    assert hits == wait.sel.tolist() and misses == []
+    np.testing.assert_array_equal(O.decode_head(q, kc, vc, t, refined=np.asarray(hits)).out, wait.out)
+    sim = O.CacheSim(4)
+    trace = [([0, 1], [], [0, 1]),       # slots 0, 1 free
+             ([1, 2], [1], [2]),         # slot 2 free
+             ([2, 3, 4], [2], [3, 4]),   # slot 3 free, then token 0 (stamp 0) leaves
+             ([0, 1], [1], [0])]         # tokens 2, 3, 4 all stamp 2: token 2 leaves
+    for step, (sel, h, m) in enumerate(trace):
+        assert sim.step_tokens(np.asarray(sel), step) == (h, m), step
+    assert sorted(sim.residents()) == [0, 1, 3, 4]
+
+
 PINS = [pin_toy_example, pin_packing, pin_quant_bounds, pin_nested_equals_direct, pin_flat_row,
         pin_scores_bruteforce, pin_select_bruteforce, pin_attend_textbook, pin_attend_converges,
-        pin_decode_bruteforce, pin_gqa_mapping, pin_cache_trace, pin_cache_invariants]
+        pin_decode_bruteforce, pin_gqa_mapping, pin_cache_trace, pin_cache_invariants, pin_skip_policy]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
