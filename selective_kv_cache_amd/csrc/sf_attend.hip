@@ -173,11 +173,24 @@ __global__ void __launch_bounds__(256) combine(DecodeParams p) {
   const int kvh = h / p.grp, hg = h % p.grp;
   const int tid = threadIdx.x, dl = tid & 31, sl = tid >> 5;
   const int d = blockIdx.y * 32 + dl;
+  // partials of the sequences before s: base splits bb, selected blocks sb
+  // (up to 63 sequences: lane i reads sequence i's length, one round trip)
   int sb = 0, bb = 0;
-  for (int i = 0; i < s; ++i) {
-    const int64_t n = seq_at(p, i + 1) - seq_at(p, i);
-    bb += (int)((n + p.split - 1) / p.split);
-    if (p.use_refine) sb += (int)(((n < p.top_t ? n : p.top_t) + p.sel_blk_tok - 1) / p.sel_blk_tok);
+  if (p.batch > 1 && p.batch < 64) {
+    const int lane = tid & 63;
+    const bool in = lane < s;
+    const int64_t n = in ? p.seq_off[lane + 1] - p.seq_off[lane] : 0;
+    const uint32_t nb = in ? (uint32_t)((n + p.split - 1) / p.split) : 0u;
+    const uint32_t ns = in && p.use_refine ? (uint32_t)(((n < p.top_t ? n : p.top_t) + p.sel_blk_tok - 1) / p.sel_blk_tok)
+                                          : 0u;
+    bb = (int)__builtin_amdgcn_readlane(wave_inclusive_scan(nb), 63);
+    sb = (int)__builtin_amdgcn_readlane(wave_inclusive_scan(ns), 63);
+  } else {
+    for (int i = 0; i < s; ++i) {
+      const int64_t n = seq_at(p, i + 1) - seq_at(p, i);
+      bb += (int)((n + p.split - 1) / p.split);
+      if (p.use_refine) sb += (int)(((n < p.top_t ? n : p.top_t) + p.sel_blk_tok - 1) / p.sel_blk_tok);
+    }
   }
   const int64_t n = seq_at(p, s + 1) - seq_at(p, s);
   const int nb = (int)((n + p.split - 1) / p.split);
