@@ -20,8 +20,13 @@
 //                 address space), 16 bytes per lane with several reads in
 //                 flight, into the miss's slot
 // No host step and no synchronization, unless the caller asks for the step's
-// statistics.  Policy on a miss: wait (the step uses every selected
-// refinement).
+// statistics.  Policy on a miss (same page, paragraph "The map app also loads
+// tiles ..."): "wait", the fetch runs before the attention and the step uses
+// every selected refinement; or "skip", the lookup marks the misses in the
+// selection list, the attention takes them at base precision, and the fetch
+// runs on the store's side stream for later steps.
+// Appends (sf_refine_store) write the new rows into the pinned store with a
+// kernel, through the store's mapped address, and drop cached copies.
 #include <string.h>
 
 #include <algorithm>

@@ -346,6 +346,46 @@ def test_skip_misses_host_tier():
         skip.close()
 
 
+def test_host_tier_rewrite_invalidates_cached_rows():
+    """Rewriting tokens whose refinement rows the device cache holds (the same
+    K, new V stored over them, so the selection stays the same): the next step
+    misses exactly on the rewritten selected tokens and refetches them, and its
+    output equals a device-tier store holding the rewritten rows, bit for bit."""
+    import torch
+    from selective_kv_cache_amd import binding as B
+    from selective_kv_cache_amd.kvcache import Decoder, LayerCache
+    w = W.small("rewrite", cfg_id=307, ctx=1500, n_q_heads=8, n_kv_heads=2, base_bits=2, refine_bits=4,
+                top_t=96)
+    g = P.geom_of(w)
+    k, v = W.layer_kv(w, 0)
+    q = W.query(w, 0)
+    dev = LayerCache(g, 1500, tier=B.SF_TIER_DEVICE)
+    host = LayerCache(g, 1500, tier=B.SF_TIER_HOST_PINNED, max_seqs=1, cache_slots=2 * w.top_t)
+    try:
+        cuda = lambda x: torch.as_tensor(x, device="cuda")
+        for c in (dev, host):
+            c.append(cuda(k), cuda(v), 0)
+        dec = Decoder(g, W.seq_offsets([1500]), w.top_t)
+        sel = torch.empty((1, w.n_kv_heads, w.top_t), dtype=torch.int32, device="cuda")
+        dec.step(host, cuda(q), sel_out=sel)                 # caches the selection's rows
+        chosen = np.unique(sel.cpu().numpy())
+        lo, hi = int(chosen[0]), int(chosen[0]) + 64            # a run of tokens, some of them cached
+        rng = np.random.default_rng(11)
+        v2 = v.copy()
+        v2[lo:hi] = rng.standard_normal(v2[lo:hi].shape).astype(np.float32)
+        for c in (dev, host):
+            c.append(cuda(k[lo:hi]), cuda(v2[lo:hi]), lo)
+        sel_np = sel.cpu().numpy()[0]
+        rewritten = sum(int(((sel_np[h] >= lo) & (sel_np[h] < hi)).sum()) for h in range(w.n_kv_heads))
+        o_dev = dec.step(dev, cuda(q)).cpu().numpy()
+        o_host, st = dec.step(host, cuda(q), want_stats=True)
+        assert rewritten > 0 and st["misses"] == rewritten, (rewritten, st)
+        assert np.array_equal(o_dev.view(np.uint32), o_host.cpu().numpy().view(np.uint32))
+    finally:
+        dev.close()
+        host.close()
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("name,heads", [("llama8b_32k", [(0, 0), (0, 7)]), ("llama8b_128k", [(0, 3)]),
                                         ("qwen8b_b16", [(0, 0), (15, 5)])])
