@@ -165,6 +165,7 @@ __global__ void __launch_bounds__(256) attend_valu(DecodeParams p) {
 // combine: grid (B * Hq, 4); a work-group takes 32 of the head's 128 output
 // elements.  Every partial's weight e^{m_x - M} is staged in LDS first, so the
 // accumulation reads of different partials are independent of each other.
+template <bool Batched>
 __global__ void __launch_bounds__(256) combine(DecodeParams p) {
   __shared__ float red[4];
   __shared__ float ew[kCombineMax], lw[kCombineMax];
@@ -174,9 +175,10 @@ __global__ void __launch_bounds__(256) combine(DecodeParams p) {
   const int tid = threadIdx.x, dl = tid & 31, sl = tid >> 5;
   const int d = blockIdx.y * 32 + dl;
   // partials of the sequences before s: base splits bb, selected blocks sb
-  // (up to 63 sequences: lane i reads sequence i's length, one round trip)
+  // (the Batched form, up to 63 sequences: lane i reads sequence i's length,
+  // one memory round trip)
   int sb = 0, bb = 0;
-  if (p.batch > 1 && p.batch < 64) {
+  if (Batched && p.batch < 64) {
     const int lane = tid & 63;
     const bool in = lane < s;
     const int64_t n = in ? p.seq_off[lane + 1] - p.seq_off[lane] : 0;
@@ -271,7 +273,10 @@ bool launch_attend(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvent
 }
 
 void launch_combine(const DecodeParams& p, hipStream_t st, KernelEvents ev) {
-  sf_launch(combine, dim3(p.batch * p.hq, kHeadDim / 32), dim3(256), st, ev, p);
+  if (p.batch > 1)
+    sf_launch(combine<true>, dim3(p.batch * p.hq, kHeadDim / 32), dim3(256), st, ev, p);
+  else
+    sf_launch(combine<false>, dim3(p.batch * p.hq, kHeadDim / 32), dim3(256), st, ev, p);
 }
 
 }  // namespace sfk

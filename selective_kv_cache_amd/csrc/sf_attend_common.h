@@ -198,7 +198,7 @@ __device__ inline void lane_dots(const uint32_t* kbrow, const uint32_t* krrow, c
 // change: with sub = 2^-r,
 //   refined - base = delta / sqrt(D) * (sub * (q . s) + (sub - 1) * sum(q) / 2),
 // so the K base codes are not read again.
-template <int BB, int G, int NW, bool LG, int TPW>
+template <int BB, int G, int NW, bool LG, int TPW, bool Batched = false>
 __device__ inline void selected_block(const DecodeParams& p, int blk, int kvh, uint8_t* smem) {
   constexpr int W = 4 * BB, LPT = 64 / TPW, EPL = kHeadDim / LPT;
   static_assert(TPW == 4 || TPW == 16, "4 or 16 lanes per token");
@@ -208,7 +208,7 @@ __device__ inline void selected_block(const DecodeParams& p, int blk, int kvh, u
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   int64_t lo, hi;
   int first;
-  const int seq = locate_unit(p, NW * TPW, blk, true, lo, hi, first);
+  const int seq = locate_unit<Batched>(p, NW * TPW, blk, true, lo, hi, first);
   const int64_t a = seq_at(p, seq);
   const int64_t sk = (int64_t)seq * p.hkv + kvh;
   const int r = p.r;
@@ -370,12 +370,12 @@ __device__ inline void selected_block(const DecodeParams& p, int blk, int kvh, u
 }
 
 // The selected block's shape chosen on the host: p.sel_blk_tok = NW TPW.
-template <int BB, int G, int NW, bool LG>
+template <int BB, int G, int NW, bool LG, bool Batched = false>
 __device__ inline void selected_block_any(const DecodeParams& p, int blk, int kvh, uint8_t* smem) {
   if (p.sel_blk_tok == NW * 4)
-    selected_block<BB, G, NW, LG, 4>(p, blk, kvh, smem);
+    selected_block<BB, G, NW, LG, 4, Batched>(p, blk, kvh, smem);
   else
-    selected_block<BB, G, NW, LG, 16>(p, blk, kvh, smem);
+    selected_block<BB, G, NW, LG, 16, Batched>(p, blk, kvh, smem);
 }
 
 }  // namespace sfk

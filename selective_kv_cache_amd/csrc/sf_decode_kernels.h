@@ -123,33 +123,38 @@ __device__ inline int64_t seq_at(const DecodeParams& p, int s) {
 // Returns the sequence and the unit's [lo, hi) range in sequence-local terms;
 // `first` receives the flat index of the sequence's first unit.
 //
-// Called by whole wavefronts (every lane active).  A batch of 2 to 63
-// sequences is searched in one memory round trip: lane i reads offsets i and
-// i + 1, a wave prefix sum of the unit counts and a ballot name the sequence;
-// longer batches walk the offsets one sequence at a time.
+// Called by whole wavefronts (every lane active).  The Batched form (the
+// kernels' instantiation for steps of several sequences) searches a batch of
+// 2 to 63 sequences in one memory round trip: lane i reads offsets i and
+// i + 1, a wave prefix sum of the unit counts and a ballot name the sequence.
+// Otherwise the offsets are walked one sequence at a time (a single
+// sequence's come from the parameter block, no load).
+template <bool Batched = false>
 __device__ inline int locate_unit(const DecodeParams& p, int64_t unit, int x, bool sel_len, int64_t& lo,
                                   int64_t& hi, int& first) {
-  if (p.batch > 1 && p.batch < 64) {
-    const int lane = threadIdx.x & 63;
-    const bool in = lane < p.batch;
-    int64_t len = in ? p.seq_off[lane + 1] - p.seq_off[lane] : 0;
-    if (sel_len) len = len < p.top_t ? len : (int64_t)p.top_t;
-    const uint32_t n = in ? (uint32_t)((len + unit - 1) / unit) : 0u;
-    const uint32_t incl = wave_inclusive_scan(n);
-    const uint64_t m = __ballot(in && (uint32_t)x < incl);
-    if (m == 0ull) {
-      lo = hi = 0;
-      first = (int)__builtin_amdgcn_readlane(incl, 63);
-      return -1;
+  if constexpr (Batched) {
+    if (p.batch < 64) {
+      const int lane = threadIdx.x & 63;
+      const bool in = lane < p.batch;
+      int64_t len = in ? p.seq_off[lane + 1] - p.seq_off[lane] : 0;
+      if (sel_len) len = len < p.top_t ? len : (int64_t)p.top_t;
+      const uint32_t n = in ? (uint32_t)((len + unit - 1) / unit) : 0u;
+      const uint32_t incl = wave_inclusive_scan(n);
+      const uint64_t m = __ballot(in && (uint32_t)x < incl);
+      if (m == 0ull) {
+        lo = hi = 0;
+        first = (int)__builtin_amdgcn_readlane(incl, 63);
+        return -1;
+      }
+      const int s = __ffsll((unsigned long long)m) - 1;
+      const int base = (int)__builtin_amdgcn_readlane(incl - n, s);
+      const int64_t ls = (int64_t)(((uint64_t)__builtin_amdgcn_readlane((uint32_t)((uint64_t)len >> 32), s) << 32) |
+                                   (uint64_t)__builtin_amdgcn_readlane((uint32_t)len, s));
+      lo = (int64_t)(x - base) * unit;
+      hi = lo + unit < ls ? lo + unit : ls;
+      first = base;
+      return s;
     }
-    const int s = __ffsll((unsigned long long)m) - 1;
-    const int base = (int)__builtin_amdgcn_readlane(incl - n, s);
-    const int64_t ls = (int64_t)(((uint64_t)__builtin_amdgcn_readlane((uint32_t)((uint64_t)len >> 32), s) << 32) |
-                                 (uint64_t)__builtin_amdgcn_readlane((uint32_t)len, s));
-    lo = (int64_t)(x - base) * unit;
-    hi = lo + unit < ls ? lo + unit : ls;
-    first = base;
-    return s;
   }
   int base = 0;
   int64_t o0 = seq_at(p, 0);

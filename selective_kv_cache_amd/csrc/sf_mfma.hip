@@ -290,7 +290,7 @@ __device__ inline float max_two_tiles(float x0, float x1) {
   return y;
 }
 
-template <int G, int NW>
+template <int G, int NW, bool Batched>
 __global__ void __launch_bounds__(64 * NW) score_mfma(DecodeParams p) {
   static_assert(NW >= 4, "waves 0-3 prepare the query digits");
   __shared__ QPrep qp;
@@ -301,7 +301,7 @@ __global__ void __launch_bounds__(64 * NW) score_mfma(DecodeParams p) {
   const int kvh = blockIdx.y;
   int64_t lo, hi;
   int first;
-  const int seq = locate_unit(p, p.score_split, blockIdx.x, false, lo, hi, first);
+  const int seq = locate_unit<Batched>(p, p.score_split, blockIdx.x, false, lo, hi, first);
   const float2 qx = load_query<G>(p.q + ((int64_t)seq * p.hq + kvh * G) * kHeadDim);
   const int64_t a = seq_at(p, seq);
   const int64_t t0 = (int64_t)kvh * p.cap + a + lo;            // first token row of the split
@@ -481,7 +481,7 @@ __device__ inline void read_stage(uint32_t aL, uint32_t aS, const uint32_t (&aV)
 // 8-element group.
 constexpr int code_bit(int tt) { return tt < 2 ? 2 * tt + 4 : tt < 5 ? 2 * tt : 2 * tt - 6; }
 
-template <int G, int NW>
+template <int G, int NW, bool Batched>
 __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh, uint8_t* smem) {
   using Lds = MfmaLds<G, NW>;
   using St = Stage<G>;
@@ -490,7 +490,7 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   int64_t lo, hi;
   int first;
-  const int seq = locate_unit(p, p.split, split, false, lo, hi, first);
+  const int seq = locate_unit<Batched>(p, p.split, split, false, lo, hi, first);
   const int64_t a = seq_at(p, seq);
   const int64_t sk = (int64_t)seq * p.hkv + kvh;
   const bool masked = p.use_refine != 0;
@@ -715,33 +715,45 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   }
 }
 
-template <int G, int NW>
+template <int G, int NW, bool Batched>
 __global__ void __launch_bounds__(64 * NW) attend_mfma(DecodeParams p) {
   __shared__ __align__(16) uint8_t smem[cmax(sizeof(SelLds<2, G, NW, 16>), sizeof(MfmaLds<G, NW>))];
   if ((int)blockIdx.x < p.n_sel_blk)
-    selected_block_any<2, G, NW, true>(p, blockIdx.x, blockIdx.y, smem);
+    selected_block_any<2, G, NW, true, Batched>(p, blockIdx.x, blockIdx.y, smem);
   else
-    base_split_mfma<G, NW>(p, blockIdx.x - p.n_sel_blk, blockIdx.y, smem);
+    base_split_mfma<G, NW, Batched>(p, blockIdx.x - p.n_sel_blk, blockIdx.y, smem);
 }
 
-bool launch_score_mfma(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev) {
-  if (p.b != 2) return false;
+template <bool Batched>
+static bool launch_score_mfma_b(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev) {
   switch (p.grp) {
-    case 1: sf_launch(score_mfma<1, kScoreWaves>, grid, dim3(64 * kScoreWaves), st, ev, p); return true;
-    case 2: sf_launch(score_mfma<2, kScoreWaves>, grid, dim3(64 * kScoreWaves), st, ev, p); return true;
-    case 4: sf_launch(score_mfma<4, kScoreWaves>, grid, dim3(64 * kScoreWaves), st, ev, p); return true;
+    case 1: sf_launch(score_mfma<1, kScoreWaves, Batched>, grid, dim3(64 * kScoreWaves), st, ev, p); return true;
+    case 2: sf_launch(score_mfma<2, kScoreWaves, Batched>, grid, dim3(64 * kScoreWaves), st, ev, p); return true;
+    case 4: sf_launch(score_mfma<4, kScoreWaves, Batched>, grid, dim3(64 * kScoreWaves), st, ev, p); return true;
   }
   return false;
+}
+
+template <bool Batched>
+static bool launch_attend_mfma_b(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev) {
+  switch (p.grp) {
+    case 1: sf_launch(attend_mfma<1, kAttendWaves, Batched>, grid, dim3(64 * kAttendWaves), st, ev, p); return true;
+    case 2: sf_launch(attend_mfma<2, kAttendWaves, Batched>, grid, dim3(64 * kAttendWaves), st, ev, p); return true;
+    case 4: sf_launch(attend_mfma<4, kAttendWaves, Batched>, grid, dim3(64 * kAttendWaves), st, ev, p); return true;
+  }
+  return false;
+}
+
+// Single-sequence steps take the instantiations without the batched
+// sequence search, so that their kernels' start stays as short as it can be.
+bool launch_score_mfma(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev) {
+  if (p.b != 2) return false;
+  return p.batch > 1 ? launch_score_mfma_b<true>(p, grid, st, ev) : launch_score_mfma_b<false>(p, grid, st, ev);
 }
 
 bool launch_attend_mfma(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev) {
   if (p.b != 2) return false;
-  switch (p.grp) {
-    case 1: sf_launch(attend_mfma<1, kAttendWaves>, grid, dim3(64 * kAttendWaves), st, ev, p); return true;
-    case 2: sf_launch(attend_mfma<2, kAttendWaves>, grid, dim3(64 * kAttendWaves), st, ev, p); return true;
-    case 4: sf_launch(attend_mfma<4, kAttendWaves>, grid, dim3(64 * kAttendWaves), st, ev, p); return true;
-  }
-  return false;
+  return p.batch > 1 ? launch_attend_mfma_b<true>(p, grid, st, ev) : launch_attend_mfma_b<false>(p, grid, st, ev);
 }
 
 }  // namespace sfk

@@ -33,6 +33,7 @@ __device__ inline uint64_t fin_value(uint2 c) {
   return ((uint64_t)(c.x & 0xFFu) << 32) | (uint64_t)(0xFFFFFFFFu - c.y);
 }
 
+template <bool Batched>
 __global__ void __launch_bounds__(kSelThreads) select_scan(DecodeParams p) {
   __shared__ __align__(16) uint32_t h[kHistBins];
   __shared__ int sh_bin;
@@ -42,7 +43,7 @@ __global__ void __launch_bounds__(kSelThreads) select_scan(DecodeParams p) {
   const int kvh = blockIdx.y;
   int64_t lo, hi;
   int first;
-  const int seq = locate_unit(p, p.sel_chunk, blockIdx.x, false, lo, hi, first);
+  const int seq = locate_unit<Batched>(p, p.sel_chunk, blockIdx.x, false, lo, hi, first);
   const int chunk = blockIdx.x - first;
   const int64_t a = seq_at(p, seq);
   const int64_t n = seq_at(p, seq + 1) - a;
@@ -408,7 +409,10 @@ __global__ void __launch_bounds__(kResThreads) select_resolve(DecodeParams p) {
 }
 
 void launch_select(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents scan_ev, KernelEvents resolve_ev) {
-  sf_launch(select_scan, grid, dim3(kSelThreads), st, scan_ev, p);
+  if (p.batch > 1)
+    sf_launch(select_scan<true>, grid, dim3(kSelThreads), st, scan_ev, p);
+  else
+    sf_launch(select_scan<false>, grid, dim3(kSelThreads), st, scan_ev, p);
   sf_launch(select_resolve, dim3(p.batch * p.hkv), dim3(kResThreads), st, resolve_ev, p);
 }
 
