@@ -387,7 +387,7 @@ def test_host_tier_rewrite_invalidates_cached_rows():
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name,heads", [("llama8b_32k", [(0, 0), (0, 7)]), ("llama8b_128k", [(0, 3)]),
+@pytest.mark.parametrize("name,heads", [("llama8b_32k", [(0, 0), (0, 7)]), ("llama8b_128k", [(0, 0), (0, 3), (0, 6)]),
                                         ("qwen8b_b16", [(0, 0), (15, 5)])])
 def test_full_size_layer_sampled_heads(name, heads):
     """Full-size layer in the benchmark's launch configuration; the oracle
@@ -399,3 +399,45 @@ def test_full_size_layer_sampled_heads(name, heads):
     print(f"full size {name}: tokens={int(off[-1])}", flush=True)
     run = P.run_gpu(w, k, v, q, off, w.top_t)
     print(P.compare_layer(w, k, v, q, off, w.top_t, run, heads=heads), flush=True)
+
+
+@pytest.mark.slow
+def test_full_size_host_tier_128k():
+    """The 128K layer with its refinement store in pinned host memory, as the
+    long-context workload keeps it, over two AR(1) steps in the benchmark's
+    launch configuration: outputs bit-identical to the device-resident store,
+    hits and misses equal to the oracle's cache simulation."""
+    import torch
+    from selective_kv_cache_amd import binding as B
+    from selective_kv_cache_amd.kvcache import Decoder, LayerCache
+    w0 = W.WORKLOADS["llama8b_128k"]
+    w = W.Workload(**{**w0.__dict__, "rho": 0.9})
+    g = P.geom_of(w)
+    n = w.ctx
+    k, v = W.layer_kv(w, 0, device="cuda")
+    qs = W.queries(w, 0, 2)
+    dev = LayerCache(g, n, tier=B.SF_TIER_DEVICE)
+    host = LayerCache(g, n, tier=B.SF_TIER_HOST_PINNED, max_seqs=1, cache_slots=2 * w.top_t)
+    try:
+        dev.append(k, v, 0)
+        host.append(k, v, 0)
+        del k, v
+        dec = Decoder(g, W.seq_offsets([n]), w.top_t)
+        sims = [O.CacheSim(2 * w.top_t) for _ in range(w.n_kv_heads)]
+        sel = torch.empty((1, w.n_kv_heads, w.top_t), dtype=torch.int32, device="cuda")
+        for t in range(qs.shape[0]):
+            q = torch.as_tensor(qs[t], device="cuda")
+            o_dev = dec.step(dev, q).cpu().numpy()
+            o_host, st = dec.step(host, q, sel_out=sel, want_stats=True)
+            assert np.array_equal(o_dev.view(np.uint32), o_host.cpu().numpy().view(np.uint32)), t
+            s_np = sel.cpu().numpy()[0]
+            hits = misses = 0
+            for h in range(w.n_kv_heads):
+                hh, mm = sims[h].step(s_np[h], t)
+                hits, misses = hits + hh, misses + mm
+            assert (st["hits"], st["misses"]) == (hits, misses), (t, st, hits, misses)
+            assert st["h2d_bytes"] == O.fetched_bytes(misses, w.head_dim, w.refine_bits)
+            print(t, st, flush=True)
+    finally:
+        dev.close()
+        host.close()
