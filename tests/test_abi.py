@@ -137,3 +137,35 @@ def test_store_rejects_before_allocation():
     assert lib.sf_store_create(ctypes.byref(g0), 100, 1, 0, 0, ctypes.byref(h)) == B.SF_ERR_INVALID_ARG
     assert lib.sf_refine_store(None, 0, None, 0, 1, None) == B.SF_ERR_INVALID_ARG
     assert lib.sf_store_destroy(None) == B.SF_ERR_INVALID_ARG
+
+
+def test_decoder_follows_a_growing_context():
+    """Decoder.set_offsets (the multi-step run's growing context): offsets and
+    sizes follow, the workspace is reallocated only when the new shape needs
+    more (with a quarter to spare), and a reallocated one starts uncleared.
+    Host logic only: buffers on the CPU, no step is run."""
+    import numpy as np
+    from selective_kv_cache_amd.kvcache import Decoder
+    _lib()
+    g = B.geom(128, 32, 8, 3, 2)
+    dec = Decoder(g, [0, 8193], 512, device="cpu")
+    size0 = dec.workspace.numel()
+    assert size0 == B.sf_decode_workspace_size(g, 1, 8193, 8193, 512)
+    dec._hist_clean = True
+    dec.set_offsets([0, 8194])
+    need = B.sf_decode_workspace_size(g, 1, 8194, 8194, 512)
+    assert (dec.total, dec.max_seq, dec.batch) == (8194, 8194, 1)
+    assert dec.seq_off_dev.tolist() == [0, 8194]
+    if need <= size0:
+        assert dec.workspace.numel() == size0 and dec._hist_clean
+    else:
+        assert dec.workspace.numel() == need + need // 4 and not dec._hist_clean
+    dec._hist_clean = True
+    dec.set_offsets([0, 40000])                              # well beyond: must grow
+    need = B.sf_decode_workspace_size(g, 1, 40000, 40000, 512)
+    assert dec.workspace.numel() == need + need // 4 and not dec._hist_clean
+    dec._hist_clean = True
+    dec.set_offsets([0, 30000])                              # smaller again: kept
+    assert dec.workspace.numel() == need + need // 4 and dec._hist_clean
+    dec.set_offsets(np.array([0, 100, 300]))                 # another batch size: not clean
+    assert dec.batch == 2 and not dec._hist_clean and dec.seq_off_dev.tolist() == [0, 100, 300]
