@@ -252,6 +252,14 @@ __device__ inline void progress_priority(int left, int total) {
     __builtin_amdgcn_s_setprio(0);
 }
 
+// A store written through the L2 (device scope): the score pass's logits and
+// scores then leave no dirty lines for the end of the kernel to write back,
+// which on a short pass (32K tokens per head) was a large share of its time;
+// they still reach the memory-side cache, where the next passes read them.
+__device__ inline void store_through(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // v_cndmask with a wave-uniform 64-bit lane mask (SGPR pair): lane l takes
 // yes where bit l of mask is set, else no.
 __device__ inline float lane_select(uint64_t mask, float yes, float no) {
@@ -369,7 +377,7 @@ __global__ void __launch_bounds__(64 * NW) score_mfma(DecodeParams p) {
       const float x = logit_scaled(D, __builtin_bit_cast(float2, ks[j]), scale, sumq);
       lg[j] = hl < G ? x : -INFINITY;
       const int rel = 32 * c + 16 * j + t;
-      if (hl < G && (full || rel < nsp)) lgo[rel * G + hl] = x;   // kept for the attention pass
+      if (hl < G && (full || rel < nsp)) store_through(&lgo[rel * G + hl], x);   // kept for the attention pass
     }
     // maximum over the heads, two tiles at once: lane (t, hl) keeps tile
     // hl/2 (token 16 (hl/2) + t)
@@ -377,7 +385,7 @@ __global__ void __launch_bounds__(64 * NW) score_mfma(DecodeParams p) {
     const int rel = 32 * c + 16 * hx + t;
     if ((hl & 1) == 0 && (full || rel < nsp)) {
       const float sc = y * kLn2;                  // the score in natural units
-      scores[rel] = sc;
+      store_through(&scores[rel], sc);
       if (hist) lds_add_u32(hist0 + 4u * (score_key(sc) >> (32 - kHistBits)), 1u);
     }
   };
