@@ -56,7 +56,8 @@ typedef enum sf_status {
   SF_ERR_UNSUPPORTED = -2, /* valid but not built for (e.g. head_dim != 128)  */
   SF_ERR_HIP = -3,         /* a HIP call failed                                */
   SF_ERR_OOM = -4,         /* device or pinned host allocation failed          */
-  SF_ERR_TIMEOUT = -5      /* a bounded wait on the refinement link expired    */
+  SF_ERR_TIMEOUT = -5,     /* a bounded wait on the device expired             */
+  SF_ERR_STATE = -6        /* a consistency check of the store failed          */
 } sf_status;
 
 /* Attention geometry and code widths.  Supported: head_dim == 128;
@@ -119,9 +120,19 @@ typedef struct sf_store_s* sf_store;
 enum { SF_TIER_DEVICE = 0, SF_TIER_HOST_PINNED = 1 };
 enum { SF_K = 0, SF_V = 1 };
 
-/* cap_tokens: token capacity (same pitch as the caches); max_seqs: batch
- * slots with a cache of their own; cache_slots: rows per (seq, KV head) cache,
- * must be >= every top_t used with the store (ignored for SF_TIER_DEVICE). */
+/* cap_tokens: token capacity, the row pitch of the caches the store is used
+ * with (sf_decode_args.cap must equal it); max_seqs: batch slots with a cache
+ * of their own; cache_slots: rows per (seq, KV head) cache, 1 <= cache_slots
+ * <= 4096 and >= every top_t used with the store (so a host-tier store serves
+ * T <= 4096; with the usual 2T slots, T <= 2048).  cache_slots is ignored for
+ * SF_TIER_DEVICE.  Returns SF_ERR_OOM, with nothing left allocated, when a
+ * device or pinned host allocation is refused.
+ *
+ * Batch positions (host tier): the cache of batch position s serves the tokens
+ * [seq_off[s], seq_off[s+1]) of the steps that use it.  A position must keep
+ * its token range from step to step (a sequence may grow at its end); after
+ * the batch is reordered or sequences are dropped, call sf_store_clear_cache.
+ * A token whose cached rows belong to another position's cache is a miss. */
 sf_status sf_store_create(const sf_geom* geom, int64_t cap_tokens, int32_t max_seqs,
                           int32_t tier, int32_t cache_slots, sf_store* out);
 sf_status sf_store_destroy(sf_store store);
@@ -142,6 +153,14 @@ sf_status sf_refine_store(sf_store store, int32_t which, const uint8_t* refine_r
 
 /* Drop every cached refinement row (next step misses on every selection). */
 sf_status sf_store_clear_cache(sf_store store, void* stream);
+
+/* Debug check of the store (synchronizes `stream`): for a host-pinned store,
+ * every token -> slot entry of the device cache must name a slot of its KV
+ * head that holds that token, and no decode step since the last check may
+ * have found a selected token without its cached rows.  Returns SF_OK, or
+ * SF_ERR_STATE (and clears the recorded error).  A device-tier store always
+ * passes. */
+sf_status sf_store_check(sf_store store, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Decode step.

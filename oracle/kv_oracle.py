@@ -263,15 +263,6 @@ def decode_step(q: np.ndarray, cache: QuantCache, seq_off: Sequence[int], t: int
     return res
 
 
-def gather_out(res: Dict[Tuple[int, int], HeadResult], n_b: int, n_q: int, n_kv: int, d: int) -> np.ndarray:
-    """Assemble per-head outputs into [B][Hq][D] fp32."""
-    g = n_q // n_kv
-    out = np.zeros((n_b, n_q, d), dtype=np.float32)
-    for (s, h), r in res.items():
-        out[s, h * g:(h + 1) * g] = r.out.astype(np.float32)
-    return out
-
-
 # ---------------------------------------------------------------------------
 # O6: reuse of fetched refinement bits across decode steps (EXPLAINER, "The
 # map app also loads tiles": fetched bits are kept and reused because

@@ -16,7 +16,8 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsf_kv.so")
 
-SF_OK, SF_ERR_INVALID_ARG, SF_ERR_UNSUPPORTED, SF_ERR_HIP, SF_ERR_OOM, SF_ERR_TIMEOUT = 0, -1, -2, -3, -4, -5
+SF_OK, SF_ERR_INVALID_ARG, SF_ERR_UNSUPPORTED, SF_ERR_HIP, SF_ERR_OOM, SF_ERR_TIMEOUT, SF_ERR_STATE = \
+    0, -1, -2, -3, -4, -5, -6
 SF_TIER_DEVICE, SF_TIER_HOST_PINNED = 0, 1
 SF_K, SF_V = 0, 1
 SF_DECODE_HIST_CLEAN = 1
@@ -25,8 +26,8 @@ SF_DECODE_SKIP_MISSES = 2
 c_i32, c_i64, c_vp, c_size = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
 
 EXPORTS = ("sf_status_string", "sf_last_error_string", "sf_kv_quantize", "sf_store_create",
-           "sf_store_destroy", "sf_refine_store", "sf_store_clear_cache", "sf_decode_workspace_size",
-           "sf_decode_step")
+           "sf_store_destroy", "sf_refine_store", "sf_store_clear_cache", "sf_store_check",
+           "sf_decode_workspace_size", "sf_decode_step")
 
 
 class sf_geom(ctypes.Structure):
@@ -82,6 +83,7 @@ def load() -> ctypes.CDLL:
     lib.sf_store_destroy.argtypes = [c_vp]
     lib.sf_refine_store.argtypes = [c_vp, c_i32, c_vp, c_i64, c_i64, c_vp]
     lib.sf_store_clear_cache.argtypes = [c_vp, c_vp]
+    lib.sf_store_check.argtypes = [c_vp, c_vp]
     lib.sf_decode_workspace_size.argtypes = [G, c_i32, c_i64, c_i64, c_i32, ctypes.POINTER(c_size)]
     lib.sf_decode_step.argtypes = [G, ctypes.POINTER(sf_decode_args), c_vp]
     for name in EXPORTS:
@@ -182,6 +184,11 @@ def sf_refine_store(store: int, which: int, refine_rows, tok_begin: int, n_tok: 
 
 def sf_store_clear_cache(store: int, stream=None) -> None:
     _check(load().sf_store_clear_cache(store, _stream(stream)), "sf_store_clear_cache")
+
+
+def sf_store_check(store: int, stream=None) -> int:
+    """Debug check of the store; returns the status (SF_OK or SF_ERR_STATE)."""
+    return int(load().sf_store_check(store, _stream(stream)))
 
 
 def sf_decode_workspace_size(g: sf_geom, batch: int, total_tokens: int, max_seq_tokens: int,

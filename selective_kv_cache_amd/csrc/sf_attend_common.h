@@ -19,12 +19,19 @@ constexpr float kRsqrtD = 0.08838834764831845f;   // 1 / sqrt(128)
 constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 
 // Refinement row (rb bytes) of token `tok`: K when which == 0, V when 1.
+// Host tier: the token's global cache slot (installed by the lookup of this
+// step).  A slot outside this (sequence, KV head)'s cache means the tables are
+// inconsistent: the store's error word records it (sf_store_check reports it)
+// and the first slot of the cache is read instead.
 __device__ inline const uint32_t* refine_row(const DecodeParams& p, int64_t sk, int kvh, int64_t tok, int which) {
   if (p.ref_rows)
     return reinterpret_cast<const uint32_t*>(p.ref_rows + (((int64_t)which * p.hkv + kvh) * p.cap + tok) * p.rb);
-  int32_t slot = p.tok_slot[(int64_t)kvh * p.cap + tok];
-  slot = slot < 0 ? 0 : slot;   // installed by the lookup; never negative when consistent
-  return reinterpret_cast<const uint32_t*>(p.cache_data + ((sk * p.slots + slot) * 2 + which) * (int64_t)p.rb);
+  int64_t gs = p.tok_slot[(int64_t)kvh * p.cap + tok];
+  if (gs < sk * p.slots || gs >= (sk + 1) * p.slots) {
+    if (p.store_err) atomicOr(p.store_err, 1);
+    gs = sk * p.slots;
+  }
+  return reinterpret_cast<const uint32_t*>(p.cache_data + (gs * 2 + which) * (int64_t)p.rb);
 }
 
 // Dot products of one quarter of head_dim (32 elements) with the G query

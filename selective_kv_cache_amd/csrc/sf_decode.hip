@@ -163,8 +163,9 @@ extern "C" sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* a
   if (refine) {
     if (!a->store) return SF_ERR_INVALID_ARG;
     const sf_store_s* st = a->store;
+    // the kernels index the store's rows and tables with the caches' pitch
     if (st->g.head_dim != geom->head_dim || st->g.n_kv_heads != geom->n_kv_heads ||
-        st->g.refine_bits != geom->refine_bits || st->cap < off[B])
+        st->g.refine_bits != geom->refine_bits || st->cap != a->cap)
       return SF_ERR_INVALID_ARG;
     if (st->tier == SF_TIER_HOST_PINNED && (B > st->max_seqs || a->top_t > st->slots))
       return SF_ERR_INVALID_ARG;
@@ -246,6 +247,7 @@ extern "C" sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* a
     } else {
       p.cache_data = st->cache_data;
       p.tok_slot = st->tok_slot;
+      p.store_err = st->err;
     }
   }
 

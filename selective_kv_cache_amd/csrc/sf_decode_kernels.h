@@ -36,7 +36,8 @@ struct DecodeParams {
   // refinement rows: device tier store, or host-tier device cache
   const uint8_t* ref_rows;    // [2][hkv][cap][rb] or NULL
   const uint8_t* cache_data;  // [max_seqs][hkv][slots][2][rb] or NULL
-  const int32_t* tok_slot;    // [hkv][cap]
+  const int32_t* tok_slot;    // [hkv][cap] global slot id (seq * hkv + kvh) * slots + slot, -1 if none
+  int32_t* store_err;         // host tier: the store's error word (inconsistent cache tables)
   int32_t slots, rb;
   float* out;          // [batch][hq][D]
 };

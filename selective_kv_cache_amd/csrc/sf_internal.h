@@ -53,7 +53,10 @@ struct sf_store_s {
   uint8_t* host_rows;
   // host tier: device refinement cache per (sequence slot, KV head)
   uint8_t* cache_data;     // [max_seqs][Hkv][slots][2][row_bytes]
-  int32_t* tok_slot;       // [Hkv][cap] slot caching the token, -1 if none
+  int32_t* tok_slot;       // [Hkv][cap] global slot id caching the token, -1 if none
+                           // (id (seq * Hkv + kvh) * slots + slot)
+  int32_t* err;            // device error word: 1 = a refinement row was missing from the cache,
+                           // 2 = the check found the slot <-> token tables inconsistent
   int32_t* slot_tok;       // [max_seqs][Hkv][slots] token in the slot, -1 if free
   int32_t* stamp;          // [max_seqs][Hkv][slots] last step the token was selected
   int32_t step;

@@ -105,7 +105,8 @@ extern "C" const char* sf_status_string(sf_status s) {
     case SF_ERR_UNSUPPORTED: return "SF_ERR_UNSUPPORTED: configuration not supported";
     case SF_ERR_HIP: return "SF_ERR_HIP: a HIP call failed";
     case SF_ERR_OOM: return "SF_ERR_OOM: allocation failed";
-    case SF_ERR_TIMEOUT: return "SF_ERR_TIMEOUT: refinement link wait expired";
+    case SF_ERR_TIMEOUT: return "SF_ERR_TIMEOUT: a bounded wait on the device expired";
+    case SF_ERR_STATE: return "SF_ERR_STATE: store consistency check failed";
   }
   return "unknown sf_status";
 }

@@ -59,8 +59,29 @@ __global__ void store_put(const uint8_t* rows, int64_t n_tok, int64_t t0, int32_
     const int32_t tok = slot_tok[i];
     if (tok >= t0 && tok < t0 + n_tok) {
       const int64_t kvh = (i / slots) % hkv;
-      tok_slot[kvh * cap + tok] = -1;
+      atomicCAS(&tok_slot[kvh * cap + tok], (int32_t)i, -1);   // i is the slot's global id
       slot_tok[i] = -1;
+    }
+  }
+}
+
+// Consistency of the cache tables (debug check): every token entry names a
+// slot of its KV head that holds the token, and every occupied slot holds a
+// token inside the capacity.  (A slot may still hold a token whose entry names
+// another batch position's slot, after the batch was reordered: that copy is
+// never read.)  A violation sets bit 2 of the error word.
+__global__ void check_tables(const int32_t* slot_tok, const int32_t* tok_slot, int64_t n_slots_total, int32_t slots,
+                             int32_t hkv, int64_t cap, int32_t* err) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_slots_total; i += stride) {
+    const int32_t tok = slot_tok[i];
+    if (tok >= cap) atomicOr(err, 2);
+  }
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < hkv * cap; i += stride) {
+    const int32_t g = tok_slot[i];
+    if (g >= 0) {
+      const int64_t kvh = i / cap, tok = i - kvh * cap;
+      if (g >= n_slots_total || (g / slots) % hkv != kvh || slot_tok[g] != (int32_t)tok) atomicOr(err, 2);
     }
   }
 }
@@ -93,17 +114,26 @@ cache_lookup(DecodeParams p, int32_t* slot_tok, int32_t* stamp, int32_t* tok_slo
   int32_t* st_tok = slot_tok + sk * p.slots;
   int32_t* st_stamp = stamp + sk * p.slots;
   int32_t* ts = tok_slot + (int64_t)kvh * p.cap;
+  const int32_t gbase = (int32_t)(sk * p.slots);   // this cache's first global slot id
 
   for (int i = tid; i < p.slots; i += kLookupThreads) flag[i] = 0u;
   __syncthreads();
   // hits are stamped; misses flagged (the loads of a thread's tokens are
-  // issued together: top_t <= slots <= kMaxSlots)
+  // issued together: top_t <= slots <= kMaxSlots).  tok_slot holds global slot
+  // ids; a token counts as a hit only when its id lies in this (sequence,
+  // KV head)'s cache and that slot holds the token.
   static_assert(kMaxSlots <= 4 * kLookupThreads, "four selected tokens per thread at most");
   int32_t slot4[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int j = tid + u * kLookupThreads;
-    slot4[u] = j < tn ? ts[a + sel[j]] : -1;
+    const int32_t gs = j < tn ? ts[a + sel[j]] : -1;
+    slot4[u] = (gs >= gbase && gs < gbase + p.slots) ? gs - gbase : -1;
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int j = tid + u * kLookupThreads;
+    if (j < tn && slot4[u] >= 0 && st_tok[slot4[u]] != (int32_t)(a + sel[j])) slot4[u] = -1;
   }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -216,11 +246,12 @@ cache_lookup(DecodeParams p, int32_t* slot_tok, int32_t* stamp, int32_t* tok_slo
     if (k < 0 || k >= (int32_t)vtot) continue;   // fewer victims than misses: cannot happen with slots >= T
     const int32_t slot = vlist[k];
     const uint64_t key = keys[slot];
-    if (key >= (1ull << 62)) ts[(int32_t)(key & 0x7FFFFFFFull)] = -1;   // the resident leaves
+    if (key >= (1ull << 62))   // the resident leaves (its token's entry, if it still names this slot)
+      atomicCAS(&ts[(int32_t)(key & 0x7FFFFFFFull)], gbase + slot, -1);
     const int32_t g = (int32_t)(a + sel[j]);
     st_tok[slot] = g;
     st_stamp[slot] = step;
-    ts[g] = slot;
+    ts[g] = gbase + slot;
     ml[2 * k] = g;
     ml[2 * k + 1] = slot;
     // skip on a miss: the attention takes this token at base precision (its
@@ -277,6 +308,7 @@ static void free_store(sf_store_s* s) {
   if (s->slot_tok) (void)hipFree(s->slot_tok);
   if (s->stamp) (void)hipFree(s->stamp);
   if (s->h_miss) (void)hipHostFree(s->h_miss);
+  if (s->err) (void)hipFree(s->err);
   if (s->miss) (void)hipFree(s->miss);
   if (s->looked_up) (void)hipEventDestroy(s->looked_up);
   if (s->fetched) (void)hipEventDestroy(s->fetched);
@@ -293,6 +325,9 @@ extern "C" sf_status sf_store_create(const sf_geom* geom, int64_t cap_tokens, in
   if (tier != SF_TIER_DEVICE && tier != SF_TIER_HOST_PINNED) return SF_ERR_INVALID_ARG;
   if (geom->refine_bits == 0) return SF_ERR_INVALID_ARG;
   if (tier == SF_TIER_HOST_PINNED && (cache_slots <= 0 || cache_slots > kMaxSlots)) return SF_ERR_INVALID_ARG;
+  // global slot ids are int32
+  if (tier == SF_TIER_HOST_PINNED && (int64_t)max_seqs * geom->n_kv_heads * cache_slots > 0x7fffffffLL)
+    return SF_ERR_INVALID_ARG;
   *out = nullptr;
   sf_store_s* s = new sf_store_s();
   memset(s, 0, sizeof(*s));
@@ -336,6 +371,8 @@ extern "C" sf_status sf_store_create(const sf_geom* geom, int64_t cap_tokens, in
     SF_ALLOC(hipEventCreateWithFlags(&s->looked_up, hipEventDisableTiming));
     SF_ALLOC(hipEventCreateWithFlags(&s->fetched, hipEventDisableTiming));
   }
+  SF_ALLOC(hipMalloc((void**)&s->err, 4));
+  SF_ALLOC(hipMemset(s->err, 0, 4));
 #undef SF_ALLOC
   *out = s;
   return SF_OK;
@@ -400,6 +437,27 @@ extern "C" sf_status sf_store_clear_cache(sf_store s, void* stream) {
   hipLaunchKernelGGL(fill_i32, dim3(256), dim3(256), 0, hs, s->stamp, nslots, -1);
   SF_LAUNCH_CHECK("fill_i32");
   return SF_OK;
+}
+
+extern "C" sf_status sf_store_check(sf_store s, void* stream) {
+  clear_error();
+  if (!s) return SF_ERR_INVALID_ARG;
+  hipStream_t hs = (hipStream_t)stream;
+  const sf_status ws = wait_side_fetch(s, hs);
+  if (ws != SF_OK) return ws;
+  if (s->tier == SF_TIER_HOST_PINNED) {
+    const int64_t nslots = (int64_t)s->max_seqs * s->g.n_kv_heads * s->slots;
+    hipLaunchKernelGGL(check_tables, dim3(256), dim3(256), 0, hs, s->slot_tok, s->tok_slot, nslots, s->slots,
+                       (int32_t)s->g.n_kv_heads, s->cap, s->err);
+    SF_LAUNCH_CHECK("check_tables");
+  }
+  int32_t e = 0;
+  SF_HIP_CHECK(hipMemcpyAsync(&e, s->err, 4, hipMemcpyDeviceToHost, hs));
+  SF_HIP_CHECK(hipStreamSynchronize(hs));
+  if (e == 0) return SF_OK;
+  SF_HIP_CHECK(hipMemsetAsync(s->err, 0, 4, hs));
+  SF_HIP_CHECK(hipStreamSynchronize(hs));
+  return SF_ERR_STATE;
 }
 
 // Host tier: look up the selection in the device cache, install the misses

@@ -140,4 +140,5 @@ def compare_layer(w: W.Workload, k, v, q, seq_off, top_t: int, run: GpuRun,
         o_err = np.abs(run.out[s, h * g:(h + 1) * g].astype(np.float64) - ref.out).max()
         assert o_err <= OUT_ATOL, f"output error {o_err} at {(s, h)}"
         worst_out = max(worst_out, float(o_err))
-    return {"max_out_err": worst_out, "max_score_err_over_tol": worst_score, "selections_differing": differ}
+    return {"max_out_err": worst_out, "max_score_err_over_tol": worst_score, "selections_differing": differ,
+            "units": len(res)}

@@ -41,7 +41,8 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = _lib()
-    for st in (B.SF_OK, B.SF_ERR_INVALID_ARG, B.SF_ERR_UNSUPPORTED, B.SF_ERR_HIP, B.SF_ERR_OOM, B.SF_ERR_TIMEOUT):
+    for st in (B.SF_OK, B.SF_ERR_INVALID_ARG, B.SF_ERR_UNSUPPORTED, B.SF_ERR_HIP, B.SF_ERR_OOM, B.SF_ERR_TIMEOUT,
+               B.SF_ERR_STATE):
         assert lib.sf_status_string(st)
 
 
@@ -133,10 +134,13 @@ def test_store_rejects_before_allocation():
     assert lib.sf_store_create(ctypes.byref(g), 100, 1, 7, 0, ctypes.byref(h)) == B.SF_ERR_INVALID_ARG
     assert lib.sf_store_create(ctypes.byref(g), 100, 1, 1, 0, ctypes.byref(h)) == B.SF_ERR_INVALID_ARG
     assert lib.sf_store_create(ctypes.byref(g), 100, 1, 1, 1 << 20, ctypes.byref(h)) == B.SF_ERR_INVALID_ARG
+    # global cache slot ids must fit in int32: max_seqs x Hkv x slots < 2^31
+    assert lib.sf_store_create(ctypes.byref(g), 100, 1 << 17, 1, 4096, ctypes.byref(h)) == B.SF_ERR_INVALID_ARG
     g0 = _g(refine_bits=0)
     assert lib.sf_store_create(ctypes.byref(g0), 100, 1, 0, 0, ctypes.byref(h)) == B.SF_ERR_INVALID_ARG
     assert lib.sf_refine_store(None, 0, None, 0, 1, None) == B.SF_ERR_INVALID_ARG
     assert lib.sf_store_destroy(None) == B.SF_ERR_INVALID_ARG
+    assert lib.sf_store_check(None, None) == B.SF_ERR_INVALID_ARG
 
 
 def test_decoder_follows_a_growing_context():

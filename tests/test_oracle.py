@@ -244,12 +244,31 @@ def pin_gqa_mapping():
 
 
 def pin_cache_trace():
+    """The hand-worked cache trace: hits, misses and residents per step, and
+    the bytes each step moves over the link (worked by hand from the row
+    size), summed over the trace."""
     g = _golden("cache_lru.json")
+    d, r = g["bytes_head_dim"], g["bytes_refine_bits"]
     sim = O.CacheSim(g["slots"])
+    total = 0
     for t, st in enumerate(g["steps"]):
         hits, misses = sim.step(np.asarray(st["sel"]), t)
         assert (hits, misses) == (st["hits"], st["misses"]), (t, hits, misses)
         assert sorted(sim.residents()) == st["residents"], (t, sorted(sim.residents()))
+        assert O.fetched_bytes(misses, d, r) == st["link_bytes"], (t, misses)
+        total += O.fetched_bytes(misses, d, r)
+    assert total == g["total_link_bytes"]
+
+
+def pin_link_bytes_are_packed_rows():
+    """A missed token moves exactly its packed K and V refinement rows: the
+    byte count equals the length of the rows pack_bits produces."""
+    rng = np.random.default_rng(15)
+    for d, r in [(128, 2), (128, 4), (128, 8), (64, 3)]:
+        rows = rng.integers(0, 2 ** r, size=(2, d))
+        packed = O.pack_bits(rows, r)
+        for misses in (0, 1, 7):
+            assert O.fetched_bytes(misses, d, r) == misses * packed.size, (d, r, misses)
 
 
 def pin_cache_invariants():
@@ -302,17 +321,13 @@ def pin_skip_policy():
 
 PINS = [pin_toy_example, pin_packing, pin_quant_bounds, pin_nested_equals_direct, pin_flat_row,
         pin_scores_bruteforce, pin_select_bruteforce, pin_attend_textbook, pin_attend_converges,
-        pin_decode_bruteforce, pin_gqa_mapping, pin_cache_trace, pin_cache_invariants, pin_skip_policy]
+        pin_decode_bruteforce, pin_gqa_mapping, pin_cache_trace, pin_link_bytes_are_packed_rows,
+        pin_cache_invariants, pin_skip_policy]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
 def test_pin(pin):
     pin()
-
-
-def test_fetched_bytes():
-    # c3-shaped layer: T=2048 tokens, D=128, r=4 -> 2 rows of 64 B per token
-    assert O.fetched_bytes(2048, 128, 4) == 2048 * 2 * 64
 
 
 # ------------------------------------------------- planted mistakes (CPU only)
@@ -419,6 +434,10 @@ def _mut_cache_evict_newest(self, sel, t):
     return len(hits), len(misses)
 
 
+def _mut_fetched_bytes_one_row(misses, head_dim, r):
+    return misses * head_dim * r // 8
+
+
 MUTATIONS = [
     ("dequant_base", _mut_base_no_half),
     ("dequant_refined", _mut_refined_no_half),
@@ -430,6 +449,7 @@ MUTATIONS = [
     ("quantize_rows", _mut_quant_round),
     ("quantize_rows", _mut_quant_swapped_fields),
     ("decode_head", _mut_decode_refines_unselected),
+    ("fetched_bytes", _mut_fetched_bytes_one_row),
 ]
 
 
