@@ -260,6 +260,27 @@ sf_status sf_decode_workspace_size(const sf_geom* geom, int32_t batch, int64_t t
  */
 sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* args, void* stream);
 
+/*
+ * sf_decode_step_noalloc -- sf_decode_step for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same step, with the scratch it needs taken from a buffer
+ * the library holds in device memory instead of args->workspace
+ * (args->workspace and args->workspace_bytes are ignored, and so is
+ * SF_DECODE_HIST_CLEAN: the buffer's histograms are cleared by every call).
+ * The call allocates nothing: no hipMalloc, hipFree or allocating library
+ * routine.  The buffer, sf_decode_noalloc_max_bytes() bytes per GPU, is held
+ * from the library's first use on a GPU until the process ends; a step whose
+ * sf_decode_workspace_size() exceeds it is refused with SF_ERR_UNSUPPORTED
+ * before anything is enqueued (use sf_decode_step with a workspace of its
+ * own).  All calls on one GPU share that GPU's buffer: calls that overlap on
+ * one GPU (several streams or threads) race on it and must be serialized by
+ * the caller.  Everything else is as sf_decode_step.
+ */
+sf_status sf_decode_step_noalloc(const sf_geom* geom, const sf_decode_args* args, void* stream);
+
+/* Size of the device buffer of sf_decode_step_noalloc (64 MiB). */
+size_t sf_decode_noalloc_max_bytes(void);
+
 
 #ifdef __cplusplus
 }

@@ -27,7 +27,8 @@ c_i32, c_i64, c_vp, c_size = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ct
 
 EXPORTS = ("sf_status_string", "sf_last_error_string", "sf_kv_quantize", "sf_store_create",
            "sf_store_destroy", "sf_refine_store", "sf_store_clear_cache", "sf_store_check",
-           "sf_decode_workspace_size", "sf_decode_step")
+           "sf_decode_workspace_size", "sf_decode_step", "sf_decode_step_noalloc",
+           "sf_decode_noalloc_max_bytes")
 
 
 class sf_geom(ctypes.Structure):
@@ -86,9 +87,12 @@ def load() -> ctypes.CDLL:
     lib.sf_store_check.argtypes = [c_vp, c_vp]
     lib.sf_decode_workspace_size.argtypes = [G, c_i32, c_i64, c_i64, c_i32, ctypes.POINTER(c_size)]
     lib.sf_decode_step.argtypes = [G, ctypes.POINTER(sf_decode_args), c_vp]
+    lib.sf_decode_step_noalloc.argtypes = [G, ctypes.POINTER(sf_decode_args), c_vp]
+    lib.sf_decode_noalloc_max_bytes.argtypes = []
     for name in EXPORTS:
-        if name not in ("sf_status_string", "sf_last_error_string"):
+        if name not in ("sf_status_string", "sf_last_error_string", "sf_decode_noalloc_max_bytes"):
             getattr(lib, name).restype = c_i32
+    lib.sf_decode_noalloc_max_bytes.restype = c_size
     _LIB = lib
     return lib
 
@@ -199,10 +203,17 @@ def sf_decode_workspace_size(g: sf_geom, batch: int, total_tokens: int, max_seq_
     return int(n.value)
 
 
+def sf_decode_noalloc_max_bytes() -> int:
+    return int(load().sf_decode_noalloc_max_bytes())
+
+
 def sf_decode_step(g: sf_geom, *, seq_off_host: Sequence[int], seq_off_dev, q, k_codes, k_scales, v_codes,
                    v_scales, cap: int, store: Optional[int], top_t: int, out, workspace, sel_out=None,
-                   scores_out=None, want_stats: bool = False, events=None, stream=None, flags: int = 0):
-    """One decode step; returns the step statistics as a dict when asked."""
+                   scores_out=None, want_stats: bool = False, events=None, stream=None, flags: int = 0,
+                   noalloc: bool = False):
+    """One decode step; returns the step statistics as a dict when asked.
+    ``noalloc``: sf_decode_step_noalloc (the library's scratch; ``workspace``
+    may then be None)."""
     off = np.ascontiguousarray(np.asarray(seq_off_host, dtype=np.int64))
     a = sf_decode_args()
     a.batch = len(off) - 1
@@ -215,7 +226,7 @@ def sf_decode_step(g: sf_geom, *, seq_off_host: Sequence[int], seq_off_dev, q, k
     st = sf_step_stats()
     a.stats = ctypes.pointer(st) if want_stats else None
     a.workspace = _ptr(workspace)
-    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     a.flags = flags
     if events is not None:
         # (start, stop) pairs of score, scan, resolve, attention, combine; a
@@ -227,5 +238,7 @@ def sf_decode_step(g: sf_geom, *, seq_off_host: Sequence[int], seq_off_dev, q, k
                 a.start_events[i], a.events[i] = h(e[0]), h(e[1])
             else:
                 a.events[i] = h(e)
-    _check(load().sf_decode_step(ctypes.byref(g), ctypes.byref(a), _stream(stream)), "sf_decode_step")
+    fn = load().sf_decode_step_noalloc if noalloc else load().sf_decode_step
+    _check(fn(ctypes.byref(g), ctypes.byref(a), _stream(stream)),
+           "sf_decode_step_noalloc" if noalloc else "sf_decode_step")
     return st.as_dict() if want_stats else None

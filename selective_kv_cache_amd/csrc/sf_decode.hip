@@ -139,12 +139,15 @@ extern "C" sf_status sf_decode_workspace_size(const sf_geom* geom, int32_t batch
   return SF_OK;
 }
 
-extern "C" sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* a, void* stream) {
+// The decode step on a given workspace (the caller's, or the library's static
+// scratch for sf_decode_step_noalloc).
+sf_status sf_decode_step_ws(const sf_geom* geom, const sf_decode_args* a, void* workspace, size_t workspace_bytes,
+                            void* stream) {
   clear_error();
   sf_status s = sf_check_geom(geom);
   if (s != SF_OK) return s;
   if (!a || a->batch <= 0 || !a->seq_off_host || !a->seq_off_dev || !a->q || !a->k_codes ||
-      !a->k_scales || !a->v_codes || !a->v_scales || !a->out || !a->workspace || a->cap <= 0 ||
+      !a->k_scales || !a->v_codes || !a->v_scales || !a->out || !workspace || a->cap <= 0 ||
       a->top_t < 0 || (a->flags & ~(SF_DECODE_HIST_CLEAN | SF_DECODE_SKIP_MISSES)) != 0)
     return SF_ERR_INVALID_ARG;
   const int32_t B = a->batch;
@@ -178,7 +181,7 @@ extern "C" sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* a
   const bool score_mfma = geom->base_bits == 2 && (grp == 1 || grp == 2 || grp == 4);
   const int32_t score_split = choose_score_split(total, geom->n_kv_heads, score_mfma ? 4096 / kScoreWaves : 1024);
   const Carve c = carve(*geom, B, total, max_seq, a->top_t, part_bound(total, B, split, a->top_t));
-  if (a->workspace_bytes < c.total) return SF_ERR_INVALID_ARG;
+  if (workspace_bytes < c.total) return SF_ERR_INVALID_ARG;
   int32_t n_split = 0, n_score = 0, n_sel = 0, n_small = 0;
   for (int i = 0; i < B; ++i) {
     const int64_t n = off[i + 1] - off[i];
@@ -199,7 +202,7 @@ extern "C" sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* a
     n_sel_blk += (int32_t)((std::min<int64_t>(off[i + 1] - off[i], a->top_t) + sel_blk_tok - 1) / sel_blk_tok);
   if (max_seq / split + 1 + (a->top_t + sel_blk_tok - 1) / sel_blk_tok > kCombineMax) return SF_ERR_UNSUPPORTED;
 
-  uint8_t* ws = static_cast<uint8_t*>(a->workspace);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
   DecodeParams p{};
   p.batch = B;
   p.hq = geom->n_q_heads;
@@ -284,4 +287,9 @@ extern "C" sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* a
   launch_combine(p, hs, stop(4));
   SF_LAUNCH_CHECK("combine");
   return SF_OK;
+}
+
+extern "C" sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* a, void* stream) {
+  if (!a) return SF_ERR_INVALID_ARG;
+  return sf_decode_step_ws(geom, a, a->workspace, a->workspace_bytes, stream);
 }

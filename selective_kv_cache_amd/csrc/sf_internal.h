@@ -15,6 +15,7 @@ constexpr int kPartStride = kHeadDim + 2;  // one partial: acc[D], m, l
 
 void set_hip_error(hipError_t e, const char* where);
 void clear_error();
+void set_error_text(const char* what);
 
 // Order-preserving map of an fp32 score to uint32 (larger score -> larger
 // key); -0 and +0 map to the same key.

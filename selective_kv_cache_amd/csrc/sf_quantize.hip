@@ -23,6 +23,7 @@ void set_hip_error(hipError_t e, const char* where) {
   snprintf(g_err, sizeof(g_err), "%s: %s", where, hipGetErrorString(e));
 }
 void clear_error() { g_err[0] = 0; }
+void set_error_text(const char* what) { snprintf(g_err, sizeof(g_err), "%s", what); }
 
 __device__ inline void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
