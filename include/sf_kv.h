@@ -193,6 +193,16 @@ typedef struct sf_step_stats {
  * captured into a graph (it forks onto the side stream). */
 #define SF_DECODE_SKIP_MISSES 2
 
+/* sf_decode_args.flags: run the step as its five kernels (score, selection
+ * scan, selection resolve, attention, combine) even where the single-launch
+ * form applies.  The single-launch form is taken for 2-bit base codes, GQA
+ * groups of 1, 2 or 4, a device-tier store (or none), policy "wait", and
+ * steps whose work-groups (ranges of at most 4,096 tokens of one KV head) are
+ * all resident on the device at once; it reads the K and V codes once and
+ * gives the same selection and outputs within the tolerances of the
+ * multi-pass form (different summation order). */
+#define SF_DECODE_MULTI_PASS 4
+
 typedef struct sf_decode_args {
   int32_t batch;                 /* B >= 1 sequences                                    */
   const int64_t* seq_off_host;   /* host [B+1], nondecreasing, every sequence non-empty,
@@ -217,15 +227,17 @@ typedef struct sf_decode_args {
                                     lists: pass NULL to keep the step asynchronous)     */
   void* workspace;               /* device scratch of sf_decode_workspace_size() bytes  */
   size_t workspace_bytes;
-  int32_t flags;                 /* 0, SF_DECODE_HIST_CLEAN, SF_DECODE_SKIP_MISSES       */
+  int32_t flags;                 /* 0 or SF_DECODE_HIST_CLEAN | SF_DECODE_SKIP_MISSES |
+                                    SF_DECODE_MULTI_PASS                                */
   void* start_events[5];         /* optional hipEvent_t pairs (NULL = none) that time the */
   void* events[5];               /* step's kernels: start_events[k] is recorded just
                                     before kernel k is dispatched, events[k] completes
                                     with it: [0] score, [1] selection scan, [2] selection
                                     resolve, [3] attention, [4] combine.  The selection
-                                    pair is not recorded when T == 0.  elapsed(start,
-                                    stop) is the kernel's time (create both without the
-                                    system-scope fence).                                */
+                                    pair is not recorded when T == 0.  A single-launch
+                                    step records pair [0] only, around its one kernel.
+                                    elapsed(start, stop) is the kernel's time (create
+                                    both without the system-scope fence).               */
 } sf_decode_args;
 
 /* Scratch needed by sf_decode_step for this batch shape.
@@ -259,6 +271,19 @@ sf_status sf_decode_workspace_size(const sf_geom* geom, int32_t batch, int64_t t
  * undefined after the call.
  */
 sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* args, void* stream);
+
+/*
+ * sf_decode_check -- status of the steps run on a workspace (NULL: the
+ * scratch of sf_decode_step_noalloc on the current device).  Synchronizes
+ * `stream`.  The single-launch form waits inside its kernel for the other
+ * work-groups of a KV head; those waits are bounded (about 0.2 s), and
+ * one that expires (its work-groups were not all resident, e.g. beside other
+ * work on the device) leaves that step's outputs undefined and is recorded in
+ * the workspace.  Returns SF_ERR_TIMEOUT if any step since the workspace was
+ * last cleared (a step without SF_DECODE_HIST_CLEAN clears it) recorded one,
+ * and clears the record; else SF_OK.
+ */
+sf_status sf_decode_check(void* workspace, void* stream);
 
 /*
  * sf_decode_step_noalloc -- sf_decode_step for callers that cannot allocate

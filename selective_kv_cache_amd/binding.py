@@ -22,13 +22,14 @@ SF_TIER_DEVICE, SF_TIER_HOST_PINNED = 0, 1
 SF_K, SF_V = 0, 1
 SF_DECODE_HIST_CLEAN = 1
 SF_DECODE_SKIP_MISSES = 2
+SF_DECODE_MULTI_PASS = 4
 
 c_i32, c_i64, c_vp, c_size = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
 
 EXPORTS = ("sf_status_string", "sf_last_error_string", "sf_kv_quantize", "sf_store_create",
            "sf_store_destroy", "sf_refine_store", "sf_store_clear_cache", "sf_store_check",
            "sf_decode_workspace_size", "sf_decode_step", "sf_decode_step_noalloc",
-           "sf_decode_noalloc_max_bytes")
+           "sf_decode_noalloc_max_bytes", "sf_decode_check")
 
 
 class sf_geom(ctypes.Structure):
@@ -89,6 +90,7 @@ def load() -> ctypes.CDLL:
     lib.sf_decode_step.argtypes = [G, ctypes.POINTER(sf_decode_args), c_vp]
     lib.sf_decode_step_noalloc.argtypes = [G, ctypes.POINTER(sf_decode_args), c_vp]
     lib.sf_decode_noalloc_max_bytes.argtypes = []
+    lib.sf_decode_check.argtypes = [c_vp, c_vp]
     for name in EXPORTS:
         if name not in ("sf_status_string", "sf_last_error_string", "sf_decode_noalloc_max_bytes"):
             getattr(lib, name).restype = c_i32
@@ -201,6 +203,11 @@ def sf_decode_workspace_size(g: sf_geom, batch: int, total_tokens: int, max_seq_
     _check(load().sf_decode_workspace_size(ctypes.byref(g), batch, total_tokens, max_seq_tokens, top_t,
                                            ctypes.byref(n)), "sf_decode_workspace_size")
     return int(n.value)
+
+
+def sf_decode_check(workspace=None, stream=None) -> int:
+    """Status of the steps run on ``workspace`` (None: the no-alloc scratch)."""
+    return int(load().sf_decode_check(_ptr(workspace), _stream(stream)))
 
 
 def sf_decode_noalloc_max_bytes() -> int:

@@ -86,9 +86,16 @@ Carve carve(const sf_geom& g, int32_t batch, int64_t total_tokens, int64_t max_s
   const int64_t t = top_t > 0 ? top_t : 1;
   Carve c{};
   size_t at = 0;
-  // the histogram comes first: its place depends on (batch, hkv) only, so a
-  // workspace that a step left with a zero histogram can be reused as such
-  c.hist = at; at += align256((size_t)batch * hkv * kHistBins * 4);
+  // what must be zero between steps comes first (its place depends on
+  // (batch, hkv) only, so a workspace that a step left clean can be reused as
+  // such): the status word, then per (sequence, KV head) the selection
+  // histograms and counters (the single-launch path's blocks of kFZWords
+  // words; the multi-pass path's level-1 histograms are the first
+  // batch * hkv * kHistBins words of the same region)
+  c.status = at; at += 256;
+  c.hist = at; at += align256((size_t)batch * hkv * kFZWords * 4);
+  c.zero_end = at;
+  c.ftie = at; at += align256((size_t)batch * hkv * ((max_seq_tokens + kFusedMinR - 1) / kFusedMinR) * 4);
   c.scores = at; at += align256((size_t)hkv * total_tokens * 4);
   // per-head logits; one chunk of slack for the attention pass's last loads
   c.logits = at; at += align256((size_t)hkv * total_tokens * grp * 4 + 32 * 8 * 4);
@@ -104,7 +111,9 @@ Carve carve(const sf_geom& g, int32_t batch, int64_t total_tokens, int64_t max_s
 // Upper bound of the partials of a step: splits of every sequence plus the
 // selected-token work-groups.
 static int32_t part_bound(int64_t total, int32_t batch, int32_t split, int32_t top_t) {
-  return (int32_t)(total / split + batch) + batch * ((top_t + kSelBlkTokMin - 1) / kSelBlkTokMin);
+  const int64_t multi = total / split + batch + (int64_t)batch * ((top_t + kSelBlkTokMin - 1) / kSelBlkTokMin);
+  const int64_t fused = total / kFusedMinR + batch;   // single-launch ranges
+  return (int32_t)(multi > fused ? multi : fused);
 }
 
 // Compute units of the current device (the selected blocks' size depends on
@@ -148,7 +157,7 @@ sf_status sf_decode_step_ws(const sf_geom* geom, const sf_decode_args* a, void* 
   if (s != SF_OK) return s;
   if (!a || a->batch <= 0 || !a->seq_off_host || !a->seq_off_dev || !a->q || !a->k_codes ||
       !a->k_scales || !a->v_codes || !a->v_scales || !a->out || !workspace || a->cap <= 0 ||
-      a->top_t < 0 || (a->flags & ~(SF_DECODE_HIST_CLEAN | SF_DECODE_SKIP_MISSES)) != 0)
+      a->top_t < 0 || (a->flags & ~(SF_DECODE_HIST_CLEAN | SF_DECODE_SKIP_MISSES | SF_DECODE_MULTI_PASS)) != 0)
     return SF_ERR_INVALID_ARG;
   const int32_t B = a->batch;
   const int64_t* off = a->seq_off_host;
@@ -182,6 +191,23 @@ sf_status sf_decode_step_ws(const sf_geom* geom, const sf_decode_args* a, void* 
   const int32_t score_split = choose_score_split(total, geom->n_kv_heads, score_mfma ? 4096 / kScoreWaves : 1024);
   const Carve c = carve(*geom, B, total, max_seq, a->top_t, part_bound(total, B, split, a->top_t));
   if (workspace_bytes < c.total) return SF_ERR_INVALID_ARG;
+  // The single-launch path: 2-bit base codes, groups of 1, 2 or 4, the
+  // refinement rows in HBM (or none), and every work-group of the launch
+  // resident at once: the smallest range R (a multiple of kFusedMinR) whose
+  // work-groups fit the device.
+  int32_t fr = 0, n_units = 0;
+  if (!(a->flags & (SF_DECODE_MULTI_PASS | SF_DECODE_SKIP_MISSES)) && score_mfma &&
+      !(refine && a->store->tier == SF_TIER_HOST_PINNED)) {
+    const int cap = fused_capacity(grp, B > 1);
+    for (int32_t R = kFusedMinR; R <= kFusedRmax && !fr; R += kFusedMinR) {
+      int64_t u = 0;
+      for (int i = 0; i < B; ++i) u += (off[i + 1] - off[i] + R - 1) / R;
+      if (u * geom->n_kv_heads <= cap) {
+        fr = R;
+        n_units = (int32_t)u;
+      }
+    }
+  }
   int32_t n_split = 0, n_score = 0, n_sel = 0, n_small = 0;
   for (int i = 0; i < B; ++i) {
     const int64_t n = off[i + 1] - off[i];
@@ -241,6 +267,13 @@ sf_status sf_decode_step_ws(const sf_geom* geom, const sf_decode_args* a, void* 
   p.sel_out = a->sel_out;
   p.part = reinterpret_cast<float*>(ws + c.part);
   p.out = a->out;
+  p.fr = fr;
+  p.fscores = a->scores_out ? 1 : 0;
+  p.fsel = a->sel_out ? 1 : 0;
+  p.ftie_stride = (int32_t)((max_seq + kFusedMinR - 1) / kFusedMinR);
+  p.fz = reinterpret_cast<uint32_t*>(ws + c.hist);
+  p.ftie = reinterpret_cast<uint32_t*>(ws + c.ftie);
+  p.fstatus = reinterpret_cast<uint32_t*>(ws + c.status);
   if (refine) {
     sf_store_s* st = a->store;
     p.rb = st->row_bytes;
@@ -255,14 +288,27 @@ sf_status sf_decode_step_ws(const sf_geom* geom, const sf_decode_args* a, void* 
   }
 
   hipStream_t hs = (hipStream_t)stream;
-  if (a->top_t > 0 && !(a->flags & SF_DECODE_HIST_CLEAN)) {
-    // select_resolve clears the histogram again once it has been read
-    const int64_t nzero = (int64_t)B * p.hkv * kHistBins;
+  if (!(a->flags & SF_DECODE_HIST_CLEAN)) {
+    // every successful step leaves this region zero again: select_resolve
+    // clears its histograms once read, the single-launch path's last
+    // work-group of each head its histograms and counters
+    const int64_t nzero = (int64_t)(c.zero_end / 4);
     hipLaunchKernelGGL(zero_words, dim3((unsigned)std::min<int64_t>((nzero + 255) / 256, 1024)), dim3(256), 0, hs,
-                       reinterpret_cast<uint32_t*>(ws + c.hist), nzero);
+                       reinterpret_cast<uint32_t*>(ws), nzero);
     SF_LAUNCH_CHECK("zero_words");
   }
   const auto stop = [&](int i) { return KernelEvents{(hipEvent_t)a->start_events[i], (hipEvent_t)a->events[i]}; };
+  if (fr) {
+    if (a->stats) {
+      memset(a->stats, 0, sizeof(*a->stats));
+      int64_t sel = 0;
+      for (int i = 0; i < B; ++i) sel += std::min<int64_t>(off[i + 1] - off[i], a->top_t);
+      a->stats->selected = sel * p.hkv;
+    }
+    if (!launch_fused(p, dim3(n_units, p.hkv), hs, stop(0))) return SF_ERR_UNSUPPORTED;
+    SF_LAUNCH_CHECK("fused_decode");
+    return SF_OK;
+  }
   if (!launch_score(p, dim3(n_score, p.hkv), hs, stop(0)))
     return SF_ERR_UNSUPPORTED;
   SF_LAUNCH_CHECK("score");
@@ -292,4 +338,25 @@ sf_status sf_decode_step_ws(const sf_geom* geom, const sf_decode_args* a, void* 
 extern "C" sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* a, void* stream) {
   if (!a) return SF_ERR_INVALID_ARG;
   return sf_decode_step_ws(geom, a, a->workspace, a->workspace_bytes, stream);
+}
+
+// The workspace's status word (the library's scratch when `workspace` is NULL).
+sf_status sf_noalloc_scratch(void** out);
+
+extern "C" sf_status sf_decode_check(void* workspace, void* stream) {
+  clear_error();
+  void* ws = workspace;
+  if (!ws) {
+    const sf_status s = sf_noalloc_scratch(&ws);
+    if (s != SF_OK) return s;
+  }
+  hipStream_t hs = (hipStream_t)stream;
+  uint32_t st = 0;
+  SF_HIP_CHECK(hipMemcpyAsync(&st, ws, 4, hipMemcpyDeviceToHost, hs));
+  SF_HIP_CHECK(hipStreamSynchronize(hs));
+  if (st == 0) return SF_OK;
+  const uint32_t zero = 0;
+  SF_HIP_CHECK(hipMemcpyAsync(ws, &zero, 4, hipMemcpyHostToDevice, hs));
+  SF_HIP_CHECK(hipStreamSynchronize(hs));
+  return SF_ERR_TIMEOUT;
 }

@@ -40,6 +40,14 @@ struct DecodeParams {
   int32_t* store_err;         // host tier: the store's error word (inconsistent cache tables)
   int32_t slots, rb;
   float* out;          // [batch][hq][D]
+  // single-launch (fused) path
+  int32_t fr;          // tokens per work-group
+  int32_t fscores;     // write the scores to `scores` (the caller asked for them)
+  int32_t fsel;        // write the selection to sel_out
+  int32_t ftie_stride; // work-groups per (sequence, KV head) at most
+  uint32_t* fz;        // [batch][hkv][kFZWords]: histograms and counters, zero between steps
+  uint32_t* ftie;      // [batch][hkv][ftie_stride]: tie counts of the work-groups
+  uint32_t* fstatus;   // the workspace's status word (bit 0: a bounded wait expired)
 };
 
 __device__ inline void wave_barrier() {
@@ -305,5 +313,14 @@ constexpr int32_t kSelBlkTok = 64;     // selected tokens per attention work-gro
 constexpr int32_t kSelBlkTokMin = 16;  // or 4 wavefronts x 4 tokens when those work-groups still fit
 constexpr int kAttendWaves = 4;         // wavefronts per attention work-group (matrix-core path)
 constexpr int kCombineMax = 2048;      // partials per (sequence, query head)
+
+// Single-launch path: per (sequence, KV head) zero region of the level-1,
+// level-2 and level-3 histograms and the counters (barrier arrivals, done).
+constexpr int kFZH1 = 0, kFZH2 = kHistBins, kFZH3 = 2 * kHistBins, kFZC = 2 * kHistBins + 256;
+constexpr int kFZWords = kFZC + 16;
+constexpr int kFusedRmax = 4096;        // tokens per work-group at most
+constexpr int kFusedMinR = 256;         // and at least (a multiple of it)
+bool launch_fused(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev);
+int fused_capacity(int grp, bool batched);   // co-resident work-groups on the device
 
 }  // namespace sfk

@@ -1,0 +1,853 @@
+// The decode step of one layer in a single launch (2-bit base codes, GQA
+// groups of 1, 2 or 4 query heads).
+//
+// Method: page "StrataFlux -- Selective precision streaming -- What does it
+// mean?".  Paragraph "Which tiles count ...": every cached token is scored
+// from the resident low-bit keys, the highest-scoring tokens of each KV head
+// are refined, everything else takes part at low precision.  Paragraph "What
+// travels over the link ...": r refinement bits subdivide the bin the base
+// code names.  Paragraph "Where it earns its keep ...": which tokens to refine
+// depends on the scores themselves, so the refinement cannot be overlapped
+// with the attention around it.
+//
+// The launch is one wave of work-groups that are all resident at once (the
+// host checks the device's capacity).  Work-group (range j, KV head k) of
+// sequence s owns tokens [j R, j R + R) of that head, R <= 4096:
+//   A  stream the range's K codes once (LDS ring of direct loads), compute
+//      the G per-head logits on the matrix cores and keep them in LDS
+//      (16 KiB per 1,024 tokens at G = 4), histogram the score keys' top 12
+//      bits, add the histogram into the head's global one;
+//   B  wait for the head's other work-groups (a counter in device memory),
+//      find the boundary bin of the exact top-T from the global histogram:
+//      tokens above it are selected, tokens below it are not, tokens in it
+//      are candidates; levels 2 and 3 (the next 12 and the last 8 key bits)
+//      and, for exactly equal scores, the lower token index settle the
+//      candidates the same way, each level one more wait, taken only when
+//      the level above leaves the boundary bin split;
+//   C  stream the range's V codes once: every token that is neither selected
+//      nor a candidate of level 1 enters the online softmax at base precision
+//      (logits from LDS, P.V on the matrix cores as in the two-pass form);
+//   D  the selected tokens (refined logit and value from their refinement
+//      rows) and the level-1 candidates not selected (base precision) of the
+//      range are added on the vector units; the range's partial (m, l,
+//      acc[D]) per query head goes to device memory;
+//   E  the last work-group of the head to finish merges the partials into
+//      the output, lists the selection when asked, and clears the head's
+//      histograms and counters for the next step.
+// Every term of the softmax is positive: each token enters exactly once,
+// with its final logit and value.  K and V are read once; the logits never
+// leave the compute unit.
+//
+// Coherence between work-groups without cache write-backs: everything one
+// work-group hands to another is written with device-scope stores or
+// atomics (they bypass the non-coherent L2), each wavefront waits for its
+// stores before the work-group arrives at a counter, and readers use
+// device-scope loads after an acquire.  Waits are bounded: a wait that
+// expires (the work-groups were not all resident) sets the status word
+// (sf_decode_check reports it) and ends the work-group.
+#include "sf_mfma_common.h"
+
+namespace sfk {
+
+constexpr int kFW = 16;          // wavefronts per work-group
+constexpr int kFRing = 3;        // ring stages per wavefront (2 chunks in flight)
+constexpr int kFTPW = 4;         // special tokens per wavefront per round
+constexpr int kFSpinLimit = 1 << 18;   // bounded waits: about 0.2 s
+
+struct FStage {
+  uint8_t c[32 * 32];            // codes of one 32-token chunk, as stored
+  float2 s[32];                  // its (lo, delta)
+};
+
+template <int G>
+struct FSpec {                   // staging of one round of special tokens
+  float qs[G][kHeadDim];
+  uint32_t kq[kFW][kFTPW][33];   // K refinement rows (r <= 8: 32 words + a zero word)
+  uint32_t vt[kFW][kFTPW][9];    // V base codes (2 bits: 8 words + a zero word)
+  uint32_t vr[kFW][kFTPW][33];   // V refinement rows
+  float2 vsc[kFW][kFTPW], ksc[kFW][kFTPW];
+  float hsub[kFW][kFTPW];        // 2^-r when refined, 1 at base precision
+  float lgt[kFW][kFTPW][G];      // base logits (log2 units)
+  float wt[kFW][G][kFTPW];
+  uint16_t list[kFusedRmax];     // the range's special tokens
+};
+
+template <int G>
+struct FusedLds {
+  float lg[kFusedRmax * G];                  // per-head logits, log2 units, [token][head]
+  union {
+    struct {
+      FStage ring[kFW][kFRing];
+      uint32_t hist[kHistBins];
+    } st;                                    // streaming and selection
+    struct {
+      float accb[kFW][G][kHeadDim];          // per-wave base P.V (hi + lo)
+      union {
+        FSpec<G> sp;
+        float accs[kFW][G][kHeadDim];        // per-wave special-token P.V
+      } x;
+    } mg;
+  } u;
+  QPrep qp;
+  alignas(16) _Float16 wt[kFW][2 * G][32];   // P.V weights: hi parts, then lo parts
+  alignas(16) _Float16 wzero[8];
+  uint32_t excl[kFusedRmax / 32];            // tokens outside the base pass
+  uint32_t sel[kFusedRmax / 32];             // selected tokens
+  uint32_t cand[kFusedRmax / 32];            // candidates still undecided
+  float mb[kFW][G], lb[kFW][G], ms[kFW][G], ls[kFW][G];
+  float mstar[G];
+  uint32_t scan[kFW];
+  int sh_bin;
+  uint32_t sh_need, sh_flag, sh_count;
+};
+
+__device__ inline uint32_t ld_dev(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float ld_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void st_dev(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Arrive at `ctr` and wait until `expected` work-groups have.  Every wave has
+// its device-scope stores and atomics complete before the work-group arrives.
+// Returns false (status word set) when the wait expired.
+template <int G>
+__device__ inline bool group_wait(FusedLds<G>& s, uint32_t* ctr, uint32_t expected, uint32_t* status) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    atomicAdd(ctr, 1u);
+    uint32_t ok = 1u;
+    int spins = 0;
+    while (ld_dev(ctr) < expected) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kFSpinLimit) {
+        atomicOr(status, 1u);
+        ok = 0u;
+        break;
+      }
+    }
+    s.sh_flag = ok;
+  }
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return s.sh_flag != 0u;
+}
+
+// Key of a token's score from its logits in LDS: the same fp32 operations as
+// the score computation of phase A (maximum over the group, times ln 2).
+template <int G>
+__device__ inline uint32_t token_key(const float* lg, int t) {
+  float y = lg[t * G];
+#pragma unroll
+  for (int h = 1; h < G; ++h) y = fmaxf(y, lg[t * G + h]);
+  return score_key(y * 0.6931471805599453f);
+}
+
+// Reads of one V stage: the two tokens' logits (dynamic LDS addresses), the
+// scales and the V dwords at the stage's offset OFF (immediates).
+template <int OFF>
+__device__ inline void read_vstage(uint32_t aL0, uint32_t aL1, uint32_t aS, const uint32_t (&aV)[4], float (&lgv)[2],
+                                   uint64_t (&vsc)[2], uint32_t (&vw)[8]) {
+  asm volatile(
+      "ds_read_b32 %0, %12\n\t"
+      "ds_read_b32 %1, %13\n\t"
+      "ds_read_b64 %2, %14 offset:%19\n\t"
+      "ds_read_b64 %3, %14 offset:%20\n\t"
+      "ds_read_b32 %4, %15 offset:%19\n\t"
+      "ds_read_b32 %5, %15 offset:%21\n\t"
+      "ds_read_b32 %6, %16 offset:%19\n\t"
+      "ds_read_b32 %7, %16 offset:%21\n\t"
+      "ds_read_b32 %8, %17 offset:%19\n\t"
+      "ds_read_b32 %9, %17 offset:%21\n\t"
+      "ds_read_b32 %10, %18 offset:%19\n\t"
+      "ds_read_b32 %11, %18 offset:%21\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(lgv[0]), "=&v"(lgv[1]), "=&v"(vsc[0]), "=&v"(vsc[1]), "=&v"(vw[0]), "=&v"(vw[1]), "=&v"(vw[2]),
+        "=&v"(vw[3]), "=&v"(vw[4]), "=&v"(vw[5]), "=&v"(vw[6]), "=&v"(vw[7])
+      : "v"(aL0), "v"(aL1), "v"(aS), "v"(aV[0]), "v"(aV[1]), "v"(aV[2]), "v"(aV[3]), "n"(OFF), "n"(OFF + 128),
+        "n"(OFF + 512)
+      : "memory");
+}
+
+// Phase D: the range's special tokens (excl bits) in rounds of kFW x kFTPW,
+// each wavefront keeping its own online softmax (natural units).  A token
+// takes its refinement rows when its sel bit is set, else the base value.
+template <int G>
+__device__ inline void special_tokens(const DecodeParams& p, FusedLds<G>& s, int seq, int kvh, int64_t row0,
+                                      int nw, float (&m_run)[G], float (&l_run)[G], float (&acc)[G][2]) {
+  FSpec<G>& sp = s.u.mg.x.sp;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  // the list of special tokens, ascending
+  const uint32_t word = tid < nw ? s.excl[tid] : 0u;
+  uint32_t total;
+  uint32_t pos = block_exclusive_scan<64 * kFW>((uint32_t)__popc(word), s.scan, total);
+  for (uint32_t bits = word; bits; bits &= bits - 1u) sp.list[pos++] = (uint16_t)(32 * tid + __ffs(bits) - 1);
+  for (int i = tid; i < G * kHeadDim; i += 64 * kFW)
+    sp.qs[i / kHeadDim][i % kHeadDim] = p.q[((int64_t)seq * p.hq + kvh * G) * kHeadDim + i];
+  __syncthreads();
+  const int r = p.r;
+  const float sub = __builtin_ldexpf(1.0f, -r);
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m_run[h] = -1e30f;
+    l_run[h] = 0.f;
+    acc[h][0] = acc[h][1] = 0.f;
+  }
+  constexpr int LPT = 64 / kFTPW, EPL = kHeadDim / LPT;
+  const int rounds = (int)((total + kFW * kFTPW - 1) / (kFW * kFTPW));
+  for (int rd = 0; rd < rounds; ++rd) {
+    {
+      // lane (tl, qd) < 4 kFTPW loads quarter qd of token tl's rows
+      const int tl = lane >> 2, qd = lane & 3;
+      const uint32_t j = (uint32_t)(rd * kFW * kFTPW + wid * kFTPW + tl);
+      const bool loader = lane < 4 * kFTPW;
+      const bool valid = loader && j < total;
+      const int off = valid ? sp.list[j] : 0;
+      const bool refined = valid && ((s.sel[off >> 5] >> (off & 31)) & 1u);
+      uint32_t vb[2] = {0u, 0u}, kr[8], vr[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kr[i] = vr[i] = 0u;
+      float2 ksc = make_float2(0.f, 0.f), vsc = make_float2(0.f, 0.f);
+      if (valid) {
+        const int64_t row = row0 + off;                       // kvh * cap + token
+        const uint32_t* srcv = reinterpret_cast<const uint32_t*>(p.vc + row * 32) + qd * 2;
+        vb[0] = srcv[0];
+        vb[1] = srcv[1];
+        if (refined) {
+          const int64_t tok = row - (int64_t)kvh * p.cap;
+          const uint32_t* rk =
+              reinterpret_cast<const uint32_t*>(p.ref_rows + ((int64_t)kvh * p.cap + tok) * p.rb) + qd * r;
+          const uint32_t* rv =
+              reinterpret_cast<const uint32_t*>(p.ref_rows + (((int64_t)p.hkv + kvh) * p.cap + tok) * p.rb) + qd * r;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            kr[i] = i < r ? rk[i] : 0u;
+            vr[i] = i < r ? rv[i] : 0u;
+          }
+        }
+        ksc = reinterpret_cast<const float2*>(p.ks)[row];
+        vsc = reinterpret_cast<const float2*>(p.vs)[row];
+      }
+      if (loader) {
+        sp.vt[wid][tl][qd * 2] = vb[0];
+        sp.vt[wid][tl][qd * 2 + 1] = vb[1];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if (i < r) {
+            sp.kq[wid][tl][qd * r + i] = kr[i];
+            sp.vr[wid][tl][qd * r + i] = vr[i];
+          }
+        if (qd == 0) {
+          sp.vt[wid][tl][8] = 0u;
+          for (int i = 4 * r; i < 33; ++i) sp.kq[wid][tl][i] = sp.vr[wid][tl][i] = 0u;
+          sp.ksc[wid][tl] = ksc;
+          sp.vsc[wid][tl] = vsc;
+          sp.hsub[wid][tl] = refined ? sub : 1.0f;
+#pragma unroll
+          for (int h = 0; h < G; ++h) sp.lgt[wid][tl][h] = valid ? s.lg[off * G + h] : 0.f;
+        }
+      }
+    }
+    wave_barrier();
+    // logits: lane (tc, e) over elements [e EPL, e EPL + EPL) of token tc
+    const int tc = lane / LPT, e0 = (lane % LPT) * EPL;
+    const bool valid = (uint32_t)(rd * kFW * kFTPW + wid * kFTPW + tc) < total;
+    float dc[G], ds[G], dq[G];
+    const uint32_t* krrow = &sp.kq[wid][tc][0];
+    switch (r) {
+      case 1: lane_dots<2, 1, G, EPL, true>(nullptr, krrow, &sp.qs[0][0], e0, dc, ds, dq); break;
+      case 2: lane_dots<2, 2, G, EPL, true>(nullptr, krrow, &sp.qs[0][0], e0, dc, ds, dq); break;
+      case 3: lane_dots<2, 3, G, EPL, true>(nullptr, krrow, &sp.qs[0][0], e0, dc, ds, dq); break;
+      case 4: lane_dots<2, 4, G, EPL, true>(nullptr, krrow, &sp.qs[0][0], e0, dc, ds, dq); break;
+      case 5: lane_dots<2, 5, G, EPL, true>(nullptr, krrow, &sp.qs[0][0], e0, dc, ds, dq); break;
+      case 6: lane_dots<2, 6, G, EPL, true>(nullptr, krrow, &sp.qs[0][0], e0, dc, ds, dq); break;
+      case 7: lane_dots<2, 7, G, EPL, true>(nullptr, krrow, &sp.qs[0][0], e0, dc, ds, dq); break;
+      default: lane_dots<2, 8, G, EPL, true>(nullptr, krrow, &sp.qs[0][0], e0, dc, ds, dq); break;
+    }
+    const float2 ksc = sp.ksc[wid][tc];
+    const float hs = sp.hsub[wid][tc];
+    const bool lead = lane % LPT == 0;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float qsum = token_sum<LPT>(dq[h]);
+      const float lr = fmaf(sp.lgt[wid][tc][h], 0.6931471805599453f,
+                            ksc.y * kRsqrtD * fmaf(hs, token_sum<LPT>(ds[h]), 0.5f * (hs - 1.0f) * qsum));
+      const float mw = wave_max_dpp(valid ? lr : -INFINITY);
+      const float mnew = fmaxf(m_run[h], mw);
+      const float alpha = __expf(m_run[h] - mnew);
+      const float ew = valid ? __expf(lr - mnew) : 0.f;
+      if (lead) sp.wt[wid][h][tc] = ew;
+      l_run[h] = fmaf(l_run[h], alpha, wave_sum_dpp(lead ? ew : 0.f));
+      acc[h][0] *= alpha;
+      acc[h][1] *= alpha;
+      m_run[h] = mnew;
+    }
+    wave_barrier();
+    const int cpos = 4 * lane, cwi = cpos >> 5, csh = cpos & 31;
+    const int rpos = 2 * lane * r, rwi = rpos >> 5, rsh = rpos & 31;
+    const uint32_t rmask = (1u << r) - 1u;
+#pragma unroll
+    for (int jj = 0; jj < kFTPW; ++jj) {
+      const uint32_t cc = sp.vt[wid][jj][cwi] >> csh;
+      const uint64_t rwin = (uint64_t)sp.vr[wid][jj][rwi] | ((uint64_t)sp.vr[wid][jj][rwi + 1] << 32);
+      const uint32_t rr = (uint32_t)(rwin >> rsh);
+      const float c0 = (float)(cc & 3u), c1 = (float)((cc >> 2) & 3u);
+      const float s0 = (float)(rr & rmask), s1 = (float)((rr >> r) & rmask);
+      const float2 sc = sp.vsc[wid][jj];
+      const float hj = sp.hsub[wid][jj];
+      const float v0 = fmaf((s0 + 0.5f) * hj, sc.y, fmaf(c0, sc.y, sc.x));
+      const float v1 = fmaf((s1 + 0.5f) * hj, sc.y, fmaf(c1, sc.y, sc.x));
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float w = sp.wt[wid][h][jj];
+        acc[h][0] = fmaf(w, v0, acc[h][0]);
+        acc[h][1] = fmaf(w, v1, acc[h][1]);
+      }
+    }
+    wave_barrier();
+  }
+}
+
+template <int G, bool Batched>
+__global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
+  __shared__ __align__(16) uint8_t fsmem[sizeof(FusedLds<G>)];
+  FusedLds<G>& s = *reinterpret_cast<FusedLds<G>*>(fsmem);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kvh = blockIdx.y;
+  int64_t lo, hi;
+  int first;
+  const int seq = locate_unit<Batched>(p, p.fr, blockIdx.x, false, lo, hi, first);
+  const float2 qx = load_query<G>(p.q + ((int64_t)seq * p.hq + kvh * G) * kHeadDim);
+  const int64_t a = seq_at(p, seq);
+  const int64_t n_s = seq_at(p, seq + 1) - a;
+  const int wi = blockIdx.x - first;                          // this work-group's place in the head
+  const uint32_t nwg = (uint32_t)((n_s + p.fr - 1) / p.fr);  // work-groups of the head
+  const int64_t sk = (int64_t)seq * p.hkv + kvh;
+  uint32_t* Z = p.fz + sk * kFZWords;
+  const int64_t t0 = (int64_t)kvh * p.cap + a + lo;           // first row of the range
+  const int nsp = (int)(hi - lo);
+  const int nchunks = (nsp + 31) / 32;
+  const int nw = nchunks;                                     // selection words of the range
+  const int nmine = nchunks > wid ? (nchunks - wid + kFW - 1) / kFW : 0;
+  const int64_t tn = n_s < p.top_t ? n_s : (int64_t)p.top_t;
+  const bool select = p.top_t > 0;
+  const bool all = select && tn == n_s;                       // every token is selected
+  const bool use_hist = select && !all;
+  constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
+
+  // ---- A: K once; logits into LDS; histogram of the score keys -------------
+  const rsrc_t rK = make_rsrc(p.kc + t0 * 32, (uint32_t)nsp * 32u);
+  const rsrc_t rKS = make_rsrc(p.ks + t0 * 2, (uint32_t)nsp * 8u);
+  const uint32_t oK = 16u * (uint32_t)lane, oS = 4u * (uint32_t)lane;
+  auto issueK = [&](int i, FStage& st) {
+    const uint32_t c = (uint32_t)(wid + kFW * i);
+    bdma16(rK, oK, c * 1024u, st.c);
+    bdma4(rKS, oS, c * 256u, st.s);
+  };
+  for (int i = tid; i < kHistBins; i += 64 * kFW) s.u.st.hist[i] = 0u;
+#pragma unroll
+  for (int k = 0; k < kFRing - 1; ++k)
+    if (k < nmine) issueK(k, s.u.st.ring[wid][k]);
+  v4i a0, a1;
+  prep_query<G>(qx, s.qp, a0, a1);
+  {
+    const int t = lane & 15, hl = lane >> 4;
+    const float scale = s.qp.scale[hl < G ? hl : 0] * (kRsqrtD * kLog2e);
+    const float sumq = s.qp.sumq[hl < G ? hl : 0] * (kRsqrtD * kLog2e);
+    float* scores = p.scores + (int64_t)kvh * p.ntot + (a - p.off0) + lo;
+    const uint32_t ring0 = lds_addr(&s.u.st.ring[wid][0]);
+    const uint32_t aK = ring0 + (uint32_t)(t * 32 + 8 * hl);
+    const uint32_t aS = ring0 + (uint32_t)(offsetof(FStage, s) + 8 * t);
+    const int hx = hl >> 1;
+    const uint32_t hist0 = lds_addr(&s.u.st.hist[0]);
+    const uint32_t lg0 = lds_addr(&s.lg[0]);
+    auto body = [&](auto kc, int i) {
+      constexpr int k = decltype(kc)::value;
+      constexpr int OFF = k * (int)sizeof(FStage);
+      if (i + kFRing - 1 < nmine) issueK(i + kFRing - 1, s.u.st.ring[wid][(k + kFRing - 1) % kFRing]);
+      wait_stages<2, kFRing - 1>(min(kFRing - 1, nmine - 1 - i));
+      const int c = wid + kFW * i;
+      uint64_t kw[2], ks[2];
+      asm volatile(
+          "ds_read_b64 %0, %4 offset:%6\n\t"
+          "ds_read_b64 %1, %4 offset:%7\n\t"
+          "ds_read_b64 %2, %5 offset:%6\n\t"
+          "ds_read_b64 %3, %5 offset:%8\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(kw[0]), "=&v"(kw[1]), "=&v"(ks[0]), "=&v"(ks[1])
+          : "v"(aK), "v"(aS), "n"(OFF), "n"(OFF + 512), "n"(OFF + 128)
+          : "memory");
+      const bool full = 32 * c + 32 <= nsp;
+      float lgv[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint2 w = __builtin_bit_cast(uint2, kw[j]);
+        v4i b0, b1;
+        decode_b2(w.x, w.y, b0, b1);
+        v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, v4i{0, 0, 0, 0}, 0, 0, 0);
+        D = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, D, 0, 0, 0);
+        const float x = logit_scaled(D, __builtin_bit_cast(float2, ks[j]), scale, sumq);
+        lgv[j] = hl < G ? x : -INFINITY;
+        const int rel = 32 * c + 16 * j + t;
+        if (hl < G && (full || rel < nsp)) lds_write_u32(lg0 + 4u * (uint32_t)(rel * G + hl), __float_as_uint(x));
+      }
+      const float y = max_two_tiles(lgv[0], lgv[1]);
+      const int rel = 32 * c + 16 * hx + t;
+      if ((hl & 1) == 0 && (full || rel < nsp)) {
+        const float sc = y * kLn2;
+        if (p.fscores) store_through(&scores[rel], sc);
+        if (use_hist) lds_add_u32(hist0 + 4u * (score_key(sc) >> (32 - kHistBits)), 1u);
+      }
+    };
+    for (int i = 0; i < nmine; i += kFRing) {
+      progress_priority(nmine - i, nmine);
+      ring_round<kFRing>(body, i, nmine);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  }
+  __syncthreads();
+
+  // ---- B: the exact top-T of the head ----------------------------------------
+  uint32_t* hist = s.u.st.hist;
+  // the range's selection words: lane 0 of each wave writes the two words of
+  // the wave's 64 tokens per round
+  for (int w = tid; w < kFusedRmax / 32; w += 64 * kFW) s.excl[w] = s.sel[w] = s.cand[w] = 0u;
+  __syncthreads();
+  if (all) {
+    for (int w = tid; w < nw; w += 64 * kFW) {
+      const int rem = nsp - 32 * w;
+      const uint32_t m = rem >= 32 ? ~0u : (1u << rem) - 1u;
+      s.excl[w] = s.sel[w] = m;
+    }
+  } else if (use_hist) {
+    for (int i = tid; i < kHistBins; i += 64 * kFW) {
+      const uint32_t c = hist[i];
+      if (c) atomicAdd(&Z[kFZH1 + i], c);
+    }
+    if (!group_wait(s, &Z[kFZC + 0], nwg, p.fstatus)) return;
+    for (int i = tid; i < kHistBins; i += 64 * kFW) hist[i] = ld_dev(&Z[kFZH1 + i]);
+    __syncthreads();
+    find_threshold_wave<kHistBins>(hist, (uint32_t)tn, &s.sh_bin, &s.sh_need);
+    const uint32_t b1 = (uint32_t)s.sh_bin, need1 = s.sh_need;
+    const bool lvl2 = hist[b1] != need1;       // the boundary bin is split
+    __syncthreads();
+    if (lvl2)
+      for (int i = tid; i < kHistBins; i += 64 * kFW) hist[i] = 0u;
+    __syncthreads();
+    // level 1: above b1 selected, in b1 candidates (all selected when b1 is
+    // taken whole), below b1 not selected; level-2 digits of the candidates
+    for (int base = 0; base < nsp; base += 64 * kFW) {
+      const int t = base + tid;
+      bool above = false, in = false;
+      if (t < nsp) {
+        const uint32_t key = token_key<G>(s.lg, t);
+        const uint32_t bin = key >> (32 - kHistBits);
+        above = bin > b1;
+        in = bin == b1;
+        if (in && lvl2) atomicAdd(&hist[(key >> 8) & 0xFFFu], 1u);
+      }
+      const uint64_t be = __ballot(above || in), bs = __ballot(above || (in && !lvl2)), bc = __ballot(in && lvl2);
+      if (lane == 0) {
+        const int w = (base + 64 * wid) >> 5;
+        if (w < kFusedRmax / 32) {
+          s.excl[w] = (uint32_t)be;
+          s.sel[w] = (uint32_t)bs;
+          s.cand[w] = (uint32_t)bc;
+          s.excl[w + 1] = (uint32_t)(be >> 32);
+          s.sel[w + 1] = (uint32_t)(bs >> 32);
+          s.cand[w + 1] = (uint32_t)(bc >> 32);
+        }
+      }
+    }
+    __syncthreads();
+    if (lvl2) {
+      // ---- level 2: the next 12 key bits of the candidates
+      for (int i = tid; i < kHistBins; i += 64 * kFW) {
+        const uint32_t c = hist[i];
+        if (c) atomicAdd(&Z[kFZH2 + i], c);
+      }
+      if (!group_wait(s, &Z[kFZC + 1], nwg, p.fstatus)) return;
+      for (int i = tid; i < kHistBins; i += 64 * kFW) hist[i] = ld_dev(&Z[kFZH2 + i]);
+      __syncthreads();
+      find_threshold_wave<kHistBins>(hist, need1, &s.sh_bin, &s.sh_need);
+      const uint32_t b2 = (uint32_t)s.sh_bin, need2 = s.sh_need;
+      const bool lvl3 = hist[b2] != need2;
+      __syncthreads();
+      if (lvl3 && tid < 256) hist[tid] = 0u;
+      __syncthreads();
+      if (tid < nw) {
+        uint32_t selw = s.sel[tid], next = 0u;
+        for (uint32_t bits = s.cand[tid]; bits; bits &= bits - 1u) {
+          const int bit = __ffs(bits) - 1;
+          const uint32_t key = token_key<G>(s.lg, 32 * tid + bit);
+          const uint32_t mid = (key >> 8) & 0xFFFu;
+          if (mid > b2 || (mid == b2 && !lvl3)) {
+            selw |= 1u << bit;
+          } else if (mid == b2) {
+            next |= 1u << bit;
+            atomicAdd(&hist[key & 0xFFu], 1u);
+          }
+        }
+        s.sel[tid] = selw;
+        s.cand[tid] = next;
+      }
+      __syncthreads();
+      if (lvl3) {
+        // ---- level 3: the last 8 key bits
+        if (tid < 256) {
+          const uint32_t c = hist[tid];
+          if (c) atomicAdd(&Z[kFZH3 + tid], c);
+        }
+        if (!group_wait(s, &Z[kFZC + 2], nwg, p.fstatus)) return;
+        if (tid < 256) hist[tid] = ld_dev(&Z[kFZH3 + tid]);
+        __syncthreads();
+        find_threshold_wave<256>(hist, need2, &s.sh_bin, &s.sh_need);
+        const uint32_t b3 = (uint32_t)s.sh_bin, need3 = s.sh_need;
+        const bool lvl4 = hist[b3] != need3;
+        __syncthreads();
+        uint32_t ties = 0u;
+        if (tid < nw) {
+          uint32_t selw = s.sel[tid];
+          for (uint32_t bits = s.cand[tid]; bits; bits &= bits - 1u) {
+            const int bit = __ffs(bits) - 1;
+            const uint32_t low = token_key<G>(s.lg, 32 * tid + bit) & 0xFFu;
+            if (low > b3 || (low == b3 && !lvl4))
+              selw |= 1u << bit;
+            else if (low == b3)
+              ties |= 1u << bit;
+          }
+          s.sel[tid] = selw;
+        }
+        if (lvl4) {
+          // ---- equal scores: the lower token index first
+          uint32_t mine_total;
+          const uint32_t rank0 = block_exclusive_scan<64 * kFW>((uint32_t)__popc(ties), s.scan, mine_total);
+          if (tid == 0) st_dev(&p.ftie[sk * p.ftie_stride + wi], mine_total);
+          if (!group_wait(s, &Z[kFZC + 3], nwg, p.fstatus)) return;
+          if (tid == 0) {
+            uint32_t before = 0u;
+            for (int j = 0; j < wi; ++j) before += ld_dev(&p.ftie[sk * p.ftie_stride + j]);
+            s.sh_count = before;
+          }
+          __syncthreads();
+          const uint32_t before = s.sh_count;
+          const uint32_t take = need3 > before ? need3 - before : 0u;   // ties of this range still taken
+          if (tid < nw) {
+            uint32_t rank = rank0, selw = s.sel[tid];
+            for (uint32_t bits = ties; bits; bits &= bits - 1u, ++rank)
+              if (rank < take) selw |= 1u << (__ffs(bits) - 1);
+            s.sel[tid] = selw;
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
+  if (select && p.fsel && tid < nw) st_dev(&p.bitmap[sk * p.bm_words + (lo >> 5) + tid], s.sel[tid]);
+
+  // ---- C: V once; unselected non-candidate tokens at base precision ---------
+  const bool masked = select && p.use_refine != 0;
+  const rsrc_t rV = make_rsrc(p.vc + t0 * 32, (uint32_t)nsp * 32u);
+  const rsrc_t rVS = make_rsrc(p.vs + t0 * 2, (uint32_t)nsp * 8u);
+  // half L&1 of V row (L/2) ^ ((L/8) & 3): the four rows one P.V read takes
+  // fall in different LDS banks
+  const uint32_t oV = (uint32_t)(((lane >> 1) ^ ((lane >> 3) & 3)) * 32 + 16 * (lane & 1));
+  auto issueV = [&](int i, FStage& st) {
+    const uint32_t c = (uint32_t)(wid + kFW * i);
+    bdma16(rV, oV, c * 1024u, st.c);
+    bdma4(rVS, oS, c * 256u, st.s);
+  };
+  __syncthreads();   // the ring and histogram are free
+#pragma unroll
+  for (int k = 0; k < kFRing - 1; ++k)
+    if (k < nmine) issueV(k, s.u.st.ring[wid][k]);
+  for (int i = lane; i < 2 * G * 32; i += 64) (&s.wt[wid][0][0])[i] = (_Float16)0.f;
+  if (tid < 8) s.wzero[tid] = (_Float16)0.f;
+  const uint32_t sw0 = masked && lane < nw ? s.excl[lane] : 0u;
+  const uint32_t sw1 = masked && 64 + lane < nw ? s.excl[64 + lane] : 0u;
+  __syncthreads();
+  const int t = lane & 15, hl = lane >> 4;        // logit layout: token t (and 16 + t), head hl
+  const int n = lane & 15, rg = lane >> 4;        // P.V layout: column n, k-group rg
+  const int hlc = hl < G ? hl : 0;
+  const uint32_t hsel = 2u * (uint32_t)(n & 1);
+  const uint32_t psel = hsel | ((hsel + 1u) << 8) | ((hsel + 4u) << 16) | ((hsel + 5u) << 24);
+  const int vdw = n >> 1;
+  const uint32_t ring0 = lds_addr(&s.u.st.ring[wid][0]);
+  const uint32_t wtR = n < 2 * G ? lds_addr(&s.wt[wid][n][8 * rg]) : lds_addr(&s.wzero[0]);
+  const uint32_t wtHi = lds_addr(&s.wt[wid][hlc][2 * t]), wtLo = lds_addr(&s.wt[wid][G + hlc][2 * t]);
+  const uint32_t lgA = lds_addr(&s.lg[0]) + 4u * (uint32_t)(t * G + hlc);
+  const uint32_t aS = ring0 + (uint32_t)(offsetof(FStage, s) + 8 * t);
+  uint32_t aV[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) aV[v] = ring0 + (uint32_t)(offsetof(FStage, c) + (4 * rg + (v ^ rg)) * 32 + 4 * vdw);
+  const uint64_t rows = G >= 4 ? ~0ull : (1ull << (16 * (G & 3))) - 1ull;
+  const float ninf = -INFINITY;
+  constexpr float kFloor = -1e30f;
+  constexpr int kSlack = 6;
+  float m = kFloor, lsum = 0.f, t1 = 0.f;
+  int sexp = 127;
+  float wsc = 1.0f;
+  v4f acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  auto body = [&](auto kc, int i) {
+    constexpr int k = decltype(kc)::value;
+    if (i + kFRing - 1 < nmine) issueV(i + kFRing - 1, s.u.st.ring[wid][(k + kFRing - 1) % kFRing]);
+    wait_stages<2, kFRing - 1>(min(kFRing - 1, nmine - 1 - i));
+    const int c = wid + kFW * i;
+    const int rem = nsp - 32 * c;
+    uint32_t vm = ~(uint32_t)__builtin_amdgcn_readlane((int)(c < 64 ? sw0 : sw1), c & 63);
+    if (rem < 32) vm &= (1u << rem) - 1u;
+    const uint32_t y0 = (vm & 0xFFFFu) | (vm << 16), y1 = (vm >> 16) | (vm & 0xFFFF0000u);
+    const uint64_t mk[2] = {((uint64_t)y0 | ((uint64_t)y0 << 32)) & rows, ((uint64_t)y1 | ((uint64_t)y1 << 32)) & rows};
+    float lgr[2];
+    uint64_t vsr[2];
+    uint32_t vw[8];
+    const uint32_t aL0 = lgA + 4u * (uint32_t)(32 * c * G), aL1 = aL0 + 4u * (uint32_t)(16 * G);
+    read_vstage<k * (int)sizeof(FStage)>(aL0, aL1, aS, aV, lgr, vsr, vw);
+    float lgx[2];
+    float2 vsc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      lgx[j] = lane_select(mk[j], lgr[j], ninf);
+      vsc[j] = __builtin_bit_cast(float2, vsr[j]);
+    }
+    const float xm = fmaxf(lgx[0], lgx[1]);
+    const bool grow = __ballot(xm > m + kSlack) != 0ull;
+    const float mnew = grow ? fmaxf(m, row16_max_dpp(xm)) : m;
+    float dmax = fmaxf(lane_select(mk[0], vsc[0].y, 0.f), lane_select(mk[1], vsc[1].y, 0.f));
+    int need = sexp;
+    if (__ballot(dmax > 0.f && (sexp == 127 || dmax >= __builtin_ldexpf(1.0f, 14 - kSlack - sexp))) != 0ull) {
+      dmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max(dmax))));
+      int e2;
+      frexpf(dmax, &e2);
+      need = 14 - kSlack - e2;
+    }
+    if (grow || need < sexp) {
+      const float alpha = mnew > m ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;
+      lsum *= alpha;
+      t1 *= alpha;
+      const int hc = n < 2 * G ? n % G : 0;
+      float f = lane_value(alpha, 0);
+#pragma unroll
+      for (int h = 1; h < G; ++h) {
+        // read with every lane active (a lane read inside the selection
+        // could run where lane 16 h is off)
+        const float ah = lane_value(alpha, 16 * h);
+        f = hc == h ? ah : f;
+      }
+      if (need < sexp) {
+        if (sexp != 127) f = __builtin_ldexpf(f, need - sexp);
+        sexp = need;
+        wsc = __builtin_ldexpf(1.0f, sexp);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] *= f;
+      m = mnew;
+    }
+    float wv[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float pk = __builtin_amdgcn_exp2f(lgx[j] - m);
+      lsum += pk;
+      t1 = fmaf(pk, fmaf(0.5f, vsc[j].y, vsc[j].x), t1);
+      wv[j] = pk * (vsc[j].y * wsc);
+    }
+    const auto whi = __builtin_amdgcn_cvt_pkrtz(wv[0], wv[1]);
+    const auto wlo = __builtin_amdgcn_cvt_pkrtz(wv[0] - (float)whi[0], wv[1] - (float)whi[1]);
+    if (hl < G) {
+      lds_write_u32(wtHi, __builtin_bit_cast(uint32_t, whi));
+      lds_write_u32(wtLo, __builtin_bit_cast(uint32_t, wlo));
+    }
+    const v8h bw = lds_read_v8h(wtR);
+    uint32_t P[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) P[v] = __builtin_amdgcn_perm(vw[2 * v + 1], vw[2 * v], psel);
+#pragma unroll
+    for (int tt = 0; tt < 8; ++tt) {
+      const uint32_t msk = 0x00030003u << code_bit(tt);
+      v4u av;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) av[v] = (tt < 2 ? P[v] << 4 : tt < 5 ? P[v] : P[v] >> 6) & msk;
+      acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, av), bw, acc[tt], 0, 0, 0);
+    }
+  };
+  for (int i = 0; i < nmine; i += kFRing) {
+    progress_priority(nmine - i, nmine);
+    ring_round<kFRing>(body, i, nmine);
+  }
+  __builtin_amdgcn_s_setprio(0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();   // the ring is reused below
+
+  // the wave's base partial: l and the scalar term per head (row sums), P.V
+  // columns hi + lo summed per head (lane n < G takes lane n + G's lo part)
+  lsum = row16_sum(lsum);
+  t1 = row16_sum(t1);
+  if (hl < G && t == 0) {
+    s.mb[wid][hl] = m == kFloor ? -INFINITY : m;
+    s.lb[wid][hl] = lsum;
+  }
+  // lane n in [G, 2G) holds head n - G's lo column; row_shr:G brings it the
+  // hi column of lane n - G, and the scalar term goes with it
+  float t1h = 0.f;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float th = lane_value(t1, 16 * h);   // every lane active (see the rescale above)
+    t1h = n - G == h ? th : t1h;
+  }
+  const int se = sexp == 127 ? 0 : sexp;
+#pragma unroll
+  for (int tt = 0; tt < 8; ++tt) {
+    const float f = __builtin_ldexpf(1.0f, 24 - code_bit(tt) - se);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float x = acc[tt][j] * f;
+      const float hi_part =
+          __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + G, 0xF, 0xF, false));
+      if (n >= G && n < 2 * G) s.u.mg.accb[wid][n - G][32 * rg + 8 * j + tt] = x + hi_part + t1h;
+    }
+  }
+
+  // ---- D: special tokens (selected, refined; level-1 candidates left out) --
+  float msn[G], lsn[G], accs[G][2];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    msn[h] = -1e30f;
+    lsn[h] = 0.f;
+    accs[h][0] = accs[h][1] = 0.f;
+  }
+  if (masked) special_tokens<G>(p, s, seq, kvh, t0, nw, msn, lsn, accs);
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    s.u.mg.x.accs[wid][h][2 * lane] = accs[h][0];
+    s.u.mg.x.accs[wid][h][2 * lane + 1] = accs[h][1];
+    if (lane == 0) {
+      s.ms[wid][h] = lsn[h] > 0.f ? msn[h] * kLog2e : -INFINITY;   // log2 units, as the base pass
+      s.ls[wid][h] = lsn[h];
+    }
+  }
+  __syncthreads();
+
+  // ---- the range's partial ----------------------------------------------------
+  float* part = p.part + ((int64_t)kvh * gridDim.x + blockIdx.x) * G * kPartStride;
+  for (int i = tid; i < G * kHeadDim; i += 64 * kFW) {
+    const int h = i / kHeadDim, d = i % kHeadDim;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kFW; ++w) M = fmaxf(M, fmaxf(s.mb[w][h], s.ms[w][h]));
+    float A = 0.f, L = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll 4
+      for (int w = 0; w < kFW; ++w) {
+        const float eb = __builtin_amdgcn_exp2f(s.mb[w][h] - M), es = __builtin_amdgcn_exp2f(s.ms[w][h] - M);
+        A = fmaf(eb, s.u.mg.accb[w][h][d], fmaf(es, s.u.mg.x.accs[w][h][d], A));
+        L = fmaf(eb, s.lb[w][h], fmaf(es, s.ls[w][h], L));
+      }
+    }
+    st_dev(&part[h * kPartStride + d], A);
+    if (d == 0) {
+      st_dev(&part[h * kPartStride + kHeadDim], M);
+      st_dev(&part[h * kPartStride + kHeadDim + 1], L);
+    }
+  }
+
+  // ---- E: the head's last work-group merges -------------------------------
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) s.sh_flag = atomicAdd(&Z[kFZC + 4], 1u) == nwg - 1u ? 1u : 0u;
+  __syncthreads();
+  if (!s.sh_flag) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const float* part0 = p.part + ((int64_t)kvh * gridDim.x + first) * G * kPartStride;
+  if (tid < G) {
+    float M = -INFINITY;
+    for (uint32_t w = 0; w < nwg; ++w) M = fmaxf(M, ld_dev(&part0[(w * G + tid) * kPartStride + kHeadDim]));
+    s.mstar[tid] = M;
+  }
+  __syncthreads();
+  for (int i = tid; i < G * kHeadDim; i += 64 * kFW) {
+    const int h = i / kHeadDim, d = i % kHeadDim;
+    const float M = s.mstar[h];
+    float num = 0.f, den = 0.f;
+    for (uint32_t w = 0; w < nwg; ++w) {
+      const float* pw = part0 + (w * G + h) * kPartStride;
+      const float mw = ld_dev(&pw[kHeadDim]);
+      const float e = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
+      num = fmaf(e, ld_dev(&pw[d]), num);
+      den = fmaf(e, ld_dev(&pw[kHeadDim + 1]), den);
+    }
+    p.out[((int64_t)seq * p.hq + kvh * G + h) * kHeadDim + d] = num / den;
+  }
+  if (select && p.fsel) {
+    // the selection, ascending, from the ranges' words
+    const uint32_t* bm = p.bitmap + sk * p.bm_words;
+    const int64_t nwh = (n_s + 31) >> 5;
+    const int64_t per = (nwh + 64 * kFW - 1) / (64 * kFW);
+    const int64_t w0 = tid * per < nwh ? tid * per : nwh, w1 = w0 + per < nwh ? w0 + per : nwh;
+    uint32_t cnt = 0;
+    for (int64_t w = w0; w < w1; ++w) cnt += __popc(ld_dev(&bm[w]));
+    uint32_t tot;
+    uint32_t pos = block_exclusive_scan<64 * kFW>(cnt, s.scan, tot);
+    int32_t* selo = p.sel_out + sk * p.top_t;
+    for (int64_t w = w0; w < w1; ++w)
+      for (uint32_t bits = ld_dev(&bm[w]); bits; bits &= bits - 1u, ++pos)
+        if (pos < (uint32_t)p.top_t) selo[pos] = (int32_t)((w << 5) + __ffs(bits) - 1);
+    for (int64_t j = tn + tid; j < p.top_t; j += 64 * kFW) selo[j] = -1;
+  }
+  // the head's histograms and counters, zero for the next step
+  for (int i = tid; i < kFZWords; i += 64 * kFW) st_dev(&Z[i], 0u);
+}
+
+template <int G, bool Batched>
+static int fused_capacity_g() {
+  static const int cap = [] {
+    int per_cu = 0, dev = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fused_decode<G, Batched>, 64 * kFW, 0) != hipSuccess ||
+        hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    return per_cu * cus;
+  }();
+  return cap;
+}
+
+int fused_capacity(int grp, bool batched) {
+  switch (grp) {
+    case 1: return batched ? fused_capacity_g<1, true>() : fused_capacity_g<1, false>();
+    case 2: return batched ? fused_capacity_g<2, true>() : fused_capacity_g<2, false>();
+    case 4: return batched ? fused_capacity_g<4, true>() : fused_capacity_g<4, false>();
+  }
+  return 0;
+}
+
+template <int G, bool Batched>
+static void launch_fused_g(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev) {
+  auto kern = fused_decode<G, Batched>;
+  if (ev.start || ev.stop)
+    hipExtLaunchKernelGGL(kern, grid, dim3(64 * kFW), 0, st, ev.start, ev.stop, 0, p);
+  else
+    hipLaunchKernelGGL(kern, grid, dim3(64 * kFW), 0, st, p);
+}
+
+bool launch_fused(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev) {
+  const bool b = p.batch > 1;
+  switch (p.grp) {
+    case 1: b ? launch_fused_g<1, true>(p, grid, st, ev) : launch_fused_g<1, false>(p, grid, st, ev); return true;
+    case 2: b ? launch_fused_g<2, true>(p, grid, st, ev) : launch_fused_g<2, false>(p, grid, st, ev); return true;
+    case 4: b ? launch_fused_g<4, true>(p, grid, st, ev) : launch_fused_g<4, false>(p, grid, st, ev); return true;
+  }
+  return false;
+}
+
+}  // namespace sfk

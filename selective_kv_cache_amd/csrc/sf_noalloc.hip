@@ -43,6 +43,8 @@ static sf_status scratch_ptr(void** out) {
 
 }  // namespace sfk
 
+sf_status sf_noalloc_scratch(void** out) { return sfk::scratch_ptr(out); }
+
 sf_status sf_decode_step_ws(const sf_geom* geom, const sf_decode_args* a, void* workspace, size_t workspace_bytes,
                             void* stream);
 

@@ -78,6 +78,10 @@ class Decoder:
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         self._hist_clean = False   # a successful step leaves the workspace histogram zero
 
+    def check(self) -> int:
+        """sf_decode_check on this decoder's workspace (synchronizes)."""
+        return B.sf_decode_check(self.workspace)
+
     def set_offsets(self, seq_off: Sequence[int]) -> None:
         """Point the decoder at new sequence offsets (a context that grew).
         The workspace is reallocated, with a quarter to spare, only when the
@@ -101,15 +105,19 @@ class Decoder:
 
     def step(self, cache: LayerCache, q: torch.Tensor, out: Optional[torch.Tensor] = None,
              sel_out: Optional[torch.Tensor] = None, scores_out: Optional[torch.Tensor] = None,
-             want_stats: bool = False, events=None, stream=None, skip_misses: bool = False):
+             want_stats: bool = False, events=None, stream=None, skip_misses: bool = False,
+             multi_pass: bool = False):
         """One decode step of one layer.  ``skip_misses``: policy "skip" on
-        a refinement-cache miss (SF_DECODE_SKIP_MISSES)."""
+        a refinement-cache miss (SF_DECODE_SKIP_MISSES); ``multi_pass``: the
+        five-kernel form even where the single launch applies."""
         if out is None:
             out = torch.empty((self.batch, self.g.n_q_heads, self.g.head_dim), dtype=torch.float32,
                               device=self.device)
         flags = B.SF_DECODE_HIST_CLEAN if self._hist_clean else 0
         if skip_misses:
             flags |= B.SF_DECODE_SKIP_MISSES
+        if multi_pass:
+            flags |= B.SF_DECODE_MULTI_PASS
         self._hist_clean = False
         st = B.sf_decode_step(self.g, seq_off_host=self.seq_off, seq_off_dev=self.seq_off_dev, q=q,
                               k_codes=cache.k_codes, k_scales=cache.k_scales, v_codes=cache.v_codes,

@@ -34,14 +34,18 @@ def geom_of(w: W.Workload):
 
 
 def run_gpu(w: W.Workload, k: np.ndarray, v: np.ndarray, q: np.ndarray, seq_off: Sequence[int],
-            top_t: int, tier: int = 0, cap_extra: int = 0) -> GpuRun:
-    return run_gpu_steps(w, k, v, q[None], seq_off, top_t, tier=tier, cap_extra=cap_extra)[0]
+            top_t: int, tier: int = 0, cap_extra: int = 0, multi_pass: bool = False) -> GpuRun:
+    return run_gpu_steps(w, k, v, q[None], seq_off, top_t, tier=tier, cap_extra=cap_extra,
+                         multi_pass=multi_pass)[0]
 
 
 def run_gpu_steps(w: W.Workload, k: np.ndarray, v: np.ndarray, qs: np.ndarray, seq_off: Sequence[int],
-                  top_t: int, tier: int = 0, cap_extra: int = 0) -> List[GpuRun]:
+                  top_t: int, tier: int = 0, cap_extra: int = 0, multi_pass: bool = False) -> List[GpuRun]:
     """Decode steps with the queries qs[0], qs[1], ... on one cache and one
-    workspace (steps after the first reuse the histogram the last one cleared)."""
+    workspace (steps after the first reuse the histograms the last one
+    cleared).  ``multi_pass``: the five-kernel form even where the single
+    launch applies."""
+    from selective_kv_cache_amd import binding as B
     import torch
     from selective_kv_cache_amd.kvcache import Decoder, LayerCache
     g = geom_of(w)
@@ -58,8 +62,10 @@ def run_gpu_steps(w: W.Workload, k: np.ndarray, v: np.ndarray, qs: np.ndarray, s
         for q in qs:
             sel = torch.full((dec.batch, w.n_kv_heads, top_t), -7, dtype=torch.int32, device="cuda")
             scores = torch.empty((w.n_kv_heads, dec.total), dtype=torch.float32, device="cuda")
-            out = dec.step(cache, torch.as_tensor(q, device="cuda"), sel_out=sel, scores_out=scores)
+            out = dec.step(cache, torch.as_tensor(q, device="cuda"), sel_out=sel, scores_out=scores,
+                           multi_pass=multi_pass)
             torch.cuda.synchronize()
+            assert dec.check() == B.SF_OK, "a bounded wait of the step expired"
             runs.append(GpuRun(out=cpu(out), sel=cpu(sel), scores=cpu(scores), k_codes=cpu(cache.k_codes),
                                v_codes=cpu(cache.v_codes), k_scales=cpu(cache.k_scales),
                                v_scales=cpu(cache.v_scales), k_ref=cpu(refs[0]) if refs else None,

@@ -122,7 +122,7 @@ def test_decode_rejects_before_launch():
     a.cap, a.top_t = 1000, 0
     a.workspace_bytes = 16                                   # workspace too small
     assert lib.sf_decode_step(ctypes.byref(g), ctypes.byref(a), None) == B.SF_ERR_INVALID_ARG
-    a.workspace_bytes, a.flags = 1 << 30, 7                  # reserved flags
+    a.workspace_bytes, a.flags = 1 << 30, 8                  # reserved flags
     assert lib.sf_decode_step(ctypes.byref(g), ctypes.byref(a), None) == B.SF_ERR_INVALID_ARG
 
 

@@ -14,7 +14,7 @@ from selective_kv_cache_amd import workloads as W
 pytestmark = pytest.mark.gpu
 
 
-def _case(w, top_t=None, layer=0, heads=None, dup=None, flat_rows=(), tier=0):
+def _case(w, top_t=None, layer=0, heads=None, dup=None, flat_rows=(), tier=0, multi_pass=False):
     lens = w.seq_lengths()
     off = W.seq_offsets(lens)
     k, v = W.layer_kv(w, layer)
@@ -26,7 +26,7 @@ def _case(w, top_t=None, layer=0, heads=None, dup=None, flat_rows=(), tier=0):
     q = W.query(w, layer)
     t = w.top_t if top_t is None else top_t
     print(f"case {w.name}: lens={lens[:4]}.. b={w.base_bits} r={w.refine_bits} T={t} G={w.group}", flush=True)
-    run = P.run_gpu(w, k, v, q, off, t, tier=tier)
+    run = P.run_gpu(w, k, v, q, off, t, tier=tier, multi_pass=multi_pass)
     stats = P.compare_layer(w, k, v, q, off, t, run, heads=heads)
     print(stats, flush=True)
     return run, stats
@@ -64,9 +64,13 @@ def test_base_pass_precision():
     assert st["max_out_err"] <= 1e-4, st
 
 
+@pytest.mark.parametrize("form", ["single", "multi"])
 @pytest.mark.parametrize("i", range(len(SMALL)), ids=[",".join(f"{k}={v}" for k, v in o.items()) for o in SMALL])
-def test_small_shapes(i):
-    _case(W.small(cfg_id=220 + i, **SMALL[i]))
+def test_small_shapes(i, form):
+    """Each shape through the single-launch form (where it applies: 2-bit base
+    codes, groups of 1, 2 or 4, work-groups resident at once; the others take
+    the five kernels anyway) and through the five-kernel form."""
+    _case(W.small(cfg_id=220 + i, **SMALL[i]), multi_pass=form == "multi")
 
 
 def test_varlen_batch():
@@ -210,7 +214,7 @@ def test_host_tier_matches_device_tier_and_cache_simulation():
         sel = torch.empty((1, w.n_kv_heads, w.top_t), dtype=torch.int32, device="cuda")
         for t in range(qs.shape[0]):
             qd = torch.as_tensor(qs[t], device="cuda")
-            o_dev = dec.step(dev, qd).cpu().numpy()
+            o_dev = dec.step(dev, qd, multi_pass=True).cpu().numpy()
             o_host, st = dec.step(host, qd, sel_out=sel, want_stats=True)
             o_host = o_host.cpu().numpy()
             assert np.array_equal(o_dev.view(np.uint32), o_host.view(np.uint32)), t
@@ -266,7 +270,7 @@ def test_append_steps_host_tier():
             q = cuda(qs[t])
             sel = torch.full((1, w.n_kv_heads, w.top_t), -7, dtype=torch.int32, device="cuda")
             scores = torch.empty((w.n_kv_heads, n), dtype=torch.float32, device="cuda")
-            o_dev = dec.step(dev, q, sel_out=sel, scores_out=scores)
+            o_dev = dec.step(dev, q, sel_out=sel, scores_out=scores, multi_pass=True)
             o_host, st = dec.step(host, q, want_stats=True)
             torch.cuda.synchronize()
             assert np.array_equal(o_dev.cpu().numpy().view(np.uint32), o_host.cpu().numpy().view(np.uint32)), t
@@ -377,7 +381,7 @@ def test_host_tier_rewrite_invalidates_cached_rows():
             c.append(cuda(k[lo:hi]), cuda(v2[lo:hi]), lo)
         sel_np = sel.cpu().numpy()[0]
         rewritten = sum(int(((sel_np[h] >= lo) & (sel_np[h] < hi)).sum()) for h in range(w.n_kv_heads))
-        o_dev = dec.step(dev, cuda(q)).cpu().numpy()
+        o_dev = dec.step(dev, cuda(q), multi_pass=True).cpu().numpy()
         o_host, st = dec.step(host, cuda(q), want_stats=True)
         assert rewritten > 0 and st["misses"] == rewritten, (rewritten, st)
         assert np.array_equal(o_dev.view(np.uint32), o_host.cpu().numpy().view(np.uint32))
@@ -388,17 +392,19 @@ def test_host_tier_rewrite_invalidates_cached_rows():
 
 @pytest.mark.slow
 @pytest.mark.timeout(600)
+@pytest.mark.parametrize("form", ["single", "multi"])
 @pytest.mark.parametrize("name", ["llama8b_32k", "llama8b_128k", "qwen8b_b16"])
-def test_full_size_layer_all_heads(name):
-    """Full-size layer in the benchmark's launch configuration; the oracle
-    checks every (sequence, KV head) pair: codes and scales bit-exact, scores,
+def test_full_size_layer_all_heads(name, form):
+    """Full-size layer in the benchmark's launch configuration (the single
+    launch where it applies; the five kernels with "multi"); the oracle checks
+    every (sequence, KV head) pair: codes and scales bit-exact, scores,
     selection and output."""
     w = W.WORKLOADS[name]
     off = W.seq_offsets(w.seq_lengths())
     k, v = W.layer_kv(w, 0)
     q = W.query(w, 0)
-    print(f"full size {name}: tokens={int(off[-1])}", flush=True)
-    run = P.run_gpu(w, k, v, q, off, w.top_t)
+    print(f"full size {name} ({form}): tokens={int(off[-1])}", flush=True)
+    run = P.run_gpu(w, k, v, q, off, w.top_t, multi_pass=form == "multi")
     st = P.compare_layer(w, k, v, q, off, w.top_t, run)
     print(st, flush=True)
     assert st["units"] == w.batch * w.n_kv_heads
@@ -431,7 +437,7 @@ def _two_seq_host_run(w, lens, steps, skip=False):
             q = cuda(qs[t])
             sel = torch.full((2, w.n_kv_heads, w.top_t), -7, dtype=torch.int32, device="cuda")
             scores = torch.empty((w.n_kv_heads, n), dtype=torch.float32, device="cuda")
-            o_dev = dec.step(dev, q, sel_out=sel, scores_out=scores).cpu().numpy()
+            o_dev = dec.step(dev, q, sel_out=sel, scores_out=scores, multi_pass=True).cpu().numpy()
             sel_np = sel.cpu().numpy()
             o_host, st = dec.step(host, q, want_stats=True, skip_misses=skip)
             o_host = o_host.cpu().numpy()
@@ -482,7 +488,7 @@ def test_host_tier_two_sequences_and_reorder():
         g = P.geom_of(w)
         dec = Decoder(g, [int(off[1]), int(off[2])], w.top_t)
         q = torch.as_tensor(qs[-1][1:2], device="cuda")
-        o_dev = dec.step(dev, q).cpu().numpy()
+        o_dev = dec.step(dev, q, multi_pass=True).cpu().numpy()
         o_host, st = dec.step(host, q, want_stats=True)
         assert st["misses"] == st["selected"] and st["hits"] == 0, st
         assert np.array_equal(o_dev.view(np.uint32), o_host.cpu().numpy().view(np.uint32))
@@ -668,7 +674,7 @@ def test_full_size_host_tier_128k():
         sel = torch.empty((1, w.n_kv_heads, w.top_t), dtype=torch.int32, device="cuda")
         for t in range(qs.shape[0]):
             q = torch.as_tensor(qs[t], device="cuda")
-            o_dev = dec.step(dev, q).cpu().numpy()
+            o_dev = dec.step(dev, q, multi_pass=True).cpu().numpy()
             o_host, st = dec.step(host, q, sel_out=sel, want_stats=True)
             assert np.array_equal(o_dev.view(np.uint32), o_host.cpu().numpy().view(np.uint32)), t
             s_np = sel.cpu().numpy()[0]
