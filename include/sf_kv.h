@@ -272,6 +272,12 @@ sf_status sf_decode_workspace_size(const sf_geom* geom, int32_t batch, int64_t t
  */
 sf_status sf_decode_step(const sf_geom* geom, const sf_decode_args* args, void* stream);
 
+/* The form sf_decode_step would take for these arguments, without running
+ * it: *kernels = 1 (the single launch) or 5 (score, selection scan and
+ * resolve, attention, combine).  Only geometry, batch, offsets, top_t, store
+ * and flags are read. */
+sf_status sf_decode_form(const sf_geom* geom, const sf_decode_args* args, int32_t* kernels);
+
 /*
  * sf_decode_check -- status of the steps run on a workspace (NULL: the
  * scratch of sf_decode_step_noalloc on the current device).  Synchronizes
@@ -306,6 +312,18 @@ sf_status sf_decode_step_noalloc(const sf_geom* geom, const sf_decode_args* args
 /* Size of the device buffer of sf_decode_step_noalloc (64 MiB). */
 size_t sf_decode_noalloc_max_bytes(void);
 
+
+/*
+ * sf_stream_read -- measurement utility: read `bytes` of device memory at
+ * `buf` once (16-byte pieces, `blocks` work-groups of 256 threads in a
+ * grid-stride loop), the reference for the bandwidth a streaming kernel can
+ * reach on the device.  `sink` (device, `blocks` words) is written only where
+ * a work-group's fold of the data equals `never` (pass a value the data rules
+ * out).  buf 16-byte aligned, bytes a multiple of 16.  Asynchronous on
+ * `stream`.
+ */
+sf_status sf_stream_read(const void* buf, size_t bytes, uint32_t never, uint32_t* sink, int32_t blocks,
+                         void* stream);
 
 #ifdef __cplusplus
 }

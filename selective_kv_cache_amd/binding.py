@@ -29,7 +29,7 @@ c_i32, c_i64, c_vp, c_size = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ct
 EXPORTS = ("sf_status_string", "sf_last_error_string", "sf_kv_quantize", "sf_store_create",
            "sf_store_destroy", "sf_refine_store", "sf_store_clear_cache", "sf_store_check",
            "sf_decode_workspace_size", "sf_decode_step", "sf_decode_step_noalloc",
-           "sf_decode_noalloc_max_bytes", "sf_decode_check")
+           "sf_decode_noalloc_max_bytes", "sf_decode_check", "sf_stream_read", "sf_decode_form")
 
 
 class sf_geom(ctypes.Structure):
@@ -91,6 +91,8 @@ def load() -> ctypes.CDLL:
     lib.sf_decode_step_noalloc.argtypes = [G, ctypes.POINTER(sf_decode_args), c_vp]
     lib.sf_decode_noalloc_max_bytes.argtypes = []
     lib.sf_decode_check.argtypes = [c_vp, c_vp]
+    lib.sf_stream_read.argtypes = [c_vp, c_size, ctypes.c_uint32, c_vp, c_i32, c_vp]
+    lib.sf_decode_form.argtypes = [G, ctypes.POINTER(sf_decode_args), ctypes.POINTER(c_i32)]
     for name in EXPORTS:
         if name not in ("sf_status_string", "sf_last_error_string", "sf_decode_noalloc_max_bytes"):
             getattr(lib, name).restype = c_i32
@@ -205,9 +207,25 @@ def sf_decode_workspace_size(g: sf_geom, batch: int, total_tokens: int, max_seq_
     return int(n.value)
 
 
+def sf_decode_form(g: sf_geom, seq_off_host: Sequence[int], top_t: int, store: Optional[int], flags: int = 0) -> int:
+    """Kernels per step of sf_decode_step for these arguments: 1 or 5."""
+    off = np.ascontiguousarray(np.asarray(seq_off_host, dtype=np.int64))
+    a = sf_decode_args()
+    a.batch = len(off) - 1
+    a.seq_off_host = off.ctypes.data_as(ctypes.POINTER(c_i64))
+    a.store, a.top_t, a.flags = store, top_t, flags
+    k = c_i32()
+    _check(load().sf_decode_form(ctypes.byref(g), ctypes.byref(a), ctypes.byref(k)), "sf_decode_form")
+    return int(k.value)
+
+
 def sf_decode_check(workspace=None, stream=None) -> int:
     """Status of the steps run on ``workspace`` (None: the no-alloc scratch)."""
     return int(load().sf_decode_check(_ptr(workspace), _stream(stream)))
+
+
+def sf_stream_read(buf, nbytes: int, never: int, sink, blocks: int, stream=None) -> None:
+    _check(load().sf_stream_read(_ptr(buf), nbytes, never, _ptr(sink), blocks, _stream(stream)), "sf_stream_read")
 
 
 def sf_decode_noalloc_max_bytes() -> int:

@@ -162,11 +162,15 @@ __device__ inline void row_window(const uint32_t* row, int e0, uint32_t (&out)[E
   }
 }
 
-// Sum over the LPT lanes of a token (LPT = 4: a quad, 16: a DPP row); every
-// lane of the group receives it.
+// Sum over the LPT lanes of a token (LPT = 4: a quad, 8: two quads, 16: a DPP
+// row); every lane of the group receives it.
 template <int LPT>
 __device__ inline float token_sum(float x) {
   x = quad_sum(x);
+  if constexpr (LPT == 8) {
+    // the other quad of the eight lanes (swizzle: lane ^ 4)
+    x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x101F));
+  }
   if constexpr (LPT == 16) {
     x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
     x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));

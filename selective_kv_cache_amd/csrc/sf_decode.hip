@@ -130,6 +130,48 @@ static int device_cus() {
 
 using namespace sfk;
 
+// The single-launch path: 2-bit base codes, groups of 1, 2 or 4, the
+// refinement rows in HBM (or none), policy "wait", and every work-group of
+// the launch resident at once: the smallest range R (a multiple of
+// kFusedMinR) whose work-groups fit the device.  Returns R (0: the five
+// kernels) and the work-groups per KV head in `n_units`.
+static int32_t fused_plan(const sf_geom& g, const sf_decode_args& a, bool refine, int32_t* n_units) {
+  const int32_t grp = g.n_q_heads / g.n_kv_heads;
+  *n_units = 0;
+  if ((a.flags & (SF_DECODE_MULTI_PASS | SF_DECODE_SKIP_MISSES)) || g.base_bits != 2 ||
+      !(grp == 1 || grp == 2 || grp == 4) || (refine && a.store->tier == SF_TIER_HOST_PINNED))
+    return 0;
+  const int cap = fused_capacity(grp, a.batch > 1);
+  const int64_t* off = a.seq_off_host;
+  for (int32_t R = kFusedMinR; R <= kFusedRmax; R += kFusedMinR) {
+    int64_t u = 0, umax = 0;
+    for (int i = 0; i < a.batch; ++i) {
+      const int64_t ui = (off[i + 1] - off[i] + R - 1) / R;
+      u += ui;
+      umax = ui > umax ? ui : umax;
+    }
+    if (u * g.n_kv_heads <= cap && umax <= kFusedMaxRanges) {
+      *n_units = (int32_t)u;
+      return R;
+    }
+  }
+  return 0;
+}
+
+extern "C" sf_status sf_decode_form(const sf_geom* geom, const sf_decode_args* a, int32_t* kernels) {
+  clear_error();
+  sf_status s = sf_check_geom(geom);
+  if (s != SF_OK) return s;
+  if (!a || !kernels || a->batch <= 0 || !a->seq_off_host || a->top_t < 0) return SF_ERR_INVALID_ARG;
+  for (int i = 0; i < a->batch; ++i)
+    if (a->seq_off_host[i + 1] - a->seq_off_host[i] <= 0) return SF_ERR_INVALID_ARG;
+  const bool refine = a->top_t > 0 && geom->refine_bits > 0;
+  if (refine && !a->store) return SF_ERR_INVALID_ARG;
+  int32_t n_units = 0;
+  *kernels = fused_plan(*geom, *a, refine, &n_units) ? 1 : 5;
+  return SF_OK;
+}
+
 // Host-tier fetch (sf_store.hip): lookup, copy of the misses, install.
 sf_status sf_store_fetch(sf_store store, const DecodeParams& p, hipStream_t st, bool skip, sf_step_stats* stats);
 
@@ -191,23 +233,8 @@ sf_status sf_decode_step_ws(const sf_geom* geom, const sf_decode_args* a, void* 
   const int32_t score_split = choose_score_split(total, geom->n_kv_heads, score_mfma ? 4096 / kScoreWaves : 1024);
   const Carve c = carve(*geom, B, total, max_seq, a->top_t, part_bound(total, B, split, a->top_t));
   if (workspace_bytes < c.total) return SF_ERR_INVALID_ARG;
-  // The single-launch path: 2-bit base codes, groups of 1, 2 or 4, the
-  // refinement rows in HBM (or none), and every work-group of the launch
-  // resident at once: the smallest range R (a multiple of kFusedMinR) whose
-  // work-groups fit the device.
-  int32_t fr = 0, n_units = 0;
-  if (!(a->flags & (SF_DECODE_MULTI_PASS | SF_DECODE_SKIP_MISSES)) && score_mfma &&
-      !(refine && a->store->tier == SF_TIER_HOST_PINNED)) {
-    const int cap = fused_capacity(grp, B > 1);
-    for (int32_t R = kFusedMinR; R <= kFusedRmax && !fr; R += kFusedMinR) {
-      int64_t u = 0;
-      for (int i = 0; i < B; ++i) u += (off[i + 1] - off[i] + R - 1) / R;
-      if (u * geom->n_kv_heads <= cap) {
-        fr = R;
-        n_units = (int32_t)u;
-      }
-    }
-  }
+  int32_t n_units = 0;
+  const int32_t fr = fused_plan(*geom, *a, refine, &n_units);
   int32_t n_split = 0, n_score = 0, n_sel = 0, n_small = 0;
   for (int i = 0; i < B; ++i) {
     const int64_t n = off[i + 1] - off[i];

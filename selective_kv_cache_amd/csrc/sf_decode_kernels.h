@@ -320,6 +320,7 @@ constexpr int kFZH1 = 0, kFZH2 = kHistBins, kFZH3 = 2 * kHistBins, kFZC = 2 * kH
 constexpr int kFZWords = kFZC + 16;
 constexpr int kFusedRmax = 4096;        // tokens per work-group at most
 constexpr int kFusedMinR = 256;         // and at least (a multiple of it)
+constexpr int kFusedMaxRanges = 512;    // work-groups per (sequence, KV head) at most
 bool launch_fused(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev);
 int fused_capacity(int grp, bool batched);   // co-resident work-groups on the device
 

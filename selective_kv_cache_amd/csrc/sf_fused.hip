@@ -50,9 +50,14 @@
 namespace sfk {
 
 constexpr int kFW = 16;          // wavefronts per work-group
-constexpr int kFRing = 3;        // ring stages per wavefront (2 chunks in flight)
-constexpr int kFTPW = 4;         // special tokens per wavefront per round
+constexpr int kFVW = 12;         // of them streaming V in phase C,
+constexpr int kFSW = kFW - kFVW; // and taking the selected tokens beside them
+constexpr int kFRing = 3;        // phase A: ring stages per wavefront (2 chunks in flight)
+constexpr int kFRingV = kFW * kFRing / kFVW;   // phase C: 4 stages per streaming wavefront
+constexpr int kFTPW = 8;         // selected tokens per special wavefront per round
 constexpr int kFSpinLimit = 1 << 18;   // bounded waits: about 0.2 s
+static_assert(kFRingV * kFVW == kFW * kFRing, "phase C's ring is phase A's");
+static_assert(2 * kFusedMaxRanges + kHeadDim <= kFW * kHeadDim, "merge arrays fit in the wave partials");
 
 struct FStage {
   uint8_t c[32 * 32];            // codes of one 32-token chunk, as stored
@@ -60,16 +65,15 @@ struct FStage {
 };
 
 template <int G>
-struct FSpec {                   // staging of one round of special tokens
+struct FSpec {                   // the special wavefronts' staging (in the histogram's place)
   float qs[G][kHeadDim];
-  uint32_t kq[kFW][kFTPW][33];   // K refinement rows (r <= 8: 32 words + a zero word)
-  uint32_t vt[kFW][kFTPW][9];    // V base codes (2 bits: 8 words + a zero word)
-  uint32_t vr[kFW][kFTPW][33];   // V refinement rows
-  float2 vsc[kFW][kFTPW], ksc[kFW][kFTPW];
-  float hsub[kFW][kFTPW];        // 2^-r when refined, 1 at base precision
-  float lgt[kFW][kFTPW][G];      // base logits (log2 units)
-  float wt[kFW][G][kFTPW];
-  uint16_t list[kFusedRmax];     // the range's special tokens
+  uint32_t kq[kFSW][kFTPW][33];  // K refinement rows (r <= 8: 32 words + a zero word)
+  uint32_t vt[kFSW][kFTPW][9];   // V base codes (2 bits: 8 words + a zero word)
+  uint32_t vr[kFSW][kFTPW][33];  // V refinement rows
+  float2 vsc[kFSW][kFTPW], ksc[kFSW][kFTPW];
+  float lgt[kFSW][kFTPW][G];     // base logits (log2 units)
+  float wt[kFSW][G][kFTPW];
+  uint16_t pre[kFusedRmax / 32 + 1];   // selected tokens before each selection word
 };
 
 template <int G>
@@ -77,24 +81,20 @@ struct FusedLds {
   float lg[kFusedRmax * G];                  // per-head logits, log2 units, [token][head]
   union {
     struct {
-      FStage ring[kFW][kFRing];
-      uint32_t hist[kHistBins];
-    } st;                                    // streaming and selection
-    struct {
-      float accb[kFW][G][kHeadDim];          // per-wave base P.V (hi + lo)
+      FStage ring[kFW * kFRing];             // A: [wave][kFRing]; C: [streaming wave][kFRingV]
       union {
-        FSpec<G> sp;
-        float accs[kFW][G][kHeadDim];        // per-wave special-token P.V
-      } x;
-    } mg;
+        uint32_t hist[kHistBins];            // selection
+        FSpec<G> sp;                         // phase C
+      } h;
+    } st;
+    float acc[kFW][G][kHeadDim];             // per-wave partials: P.V of the wave's tokens
   } u;
   QPrep qp;
   alignas(16) _Float16 wt[kFW][2 * G][32];   // P.V weights: hi parts, then lo parts
   alignas(16) _Float16 wzero[8];
-  uint32_t excl[kFusedRmax / 32];            // tokens outside the base pass
   uint32_t sel[kFusedRmax / 32];             // selected tokens
   uint32_t cand[kFusedRmax / 32];            // candidates still undecided
-  float mb[kFW][G], lb[kFW][G], ms[kFW][G], ls[kFW][G];
+  float mw[kFW][G], lw[kFW][G];              // per-wave partials: maxima (log2 units), sums
   float mstar[G];
   uint32_t scan[kFW];
   int sh_bin;
@@ -107,6 +107,21 @@ __device__ inline uint32_t ld_dev(const uint32_t* p) {
 __device__ inline float ld_dev(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Device-scope (sc1) loads through a buffer resource: coherent across the
+// XCDs' caches like the atomic loads above, but plain loads to the compiler,
+// so that many can be in flight at once.
+__device__ inline uint4 ld_dev4(rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 16));
+}
+__device__ inline float ld_devf(rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, 16));
+}
+// Copy n words (n a multiple of 4, 4 n <= 16 * blockDim) of device memory into LDS.
+__device__ inline void copy_dev_words(uint32_t* lds, const uint32_t* g, int n) {
+  const rsrc_t r = make_rsrc(g, (uint32_t)n * 4u);
+  if ((int)threadIdx.x < n / 4) reinterpret_cast<uint4*>(lds)[threadIdx.x] = ld_dev4(r, 16u * threadIdx.x);
+}
+
 __device__ inline void st_dev(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -136,7 +151,6 @@ __device__ inline bool group_wait(FusedLds<G>& s, uint32_t* ctr, uint32_t expect
     s.sh_flag = ok;
   }
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   return s.sh_flag != 0u;
 }
 
@@ -176,24 +190,22 @@ __device__ inline void read_vstage(uint32_t aL0, uint32_t aL1, uint32_t aS, cons
       : "memory");
 }
 
-// Phase D: the range's special tokens (excl bits) in rounds of kFW x kFTPW,
-// each wavefront keeping its own online softmax (natural units).  A token
-// takes its refinement rows when its sel bit is set, else the base value.
+// Phase C, special wavefront sw (0 .. kFSW-1): the range's selected tokens
+// with their refined keys and values, kFTPW at a time (tokens sw kFTPW ..
+// of each round of kFSW kFTPW), in the wave's own online softmax (natural
+// units).  sp.pre holds the selected tokens before each selection word.
 template <int G>
-__device__ inline void special_tokens(const DecodeParams& p, FusedLds<G>& s, int seq, int kvh, int64_t row0,
-                                      int nw, float (&m_run)[G], float (&l_run)[G], float (&acc)[G][2]) {
-  FSpec<G>& sp = s.u.mg.x.sp;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  // the list of special tokens, ascending
-  const uint32_t word = tid < nw ? s.excl[tid] : 0u;
-  uint32_t total;
-  uint32_t pos = block_exclusive_scan<64 * kFW>((uint32_t)__popc(word), s.scan, total);
-  for (uint32_t bits = word; bits; bits &= bits - 1u) sp.list[pos++] = (uint16_t)(32 * tid + __ffs(bits) - 1);
-  for (int i = tid; i < G * kHeadDim; i += 64 * kFW)
-    sp.qs[i / kHeadDim][i % kHeadDim] = p.q[((int64_t)seq * p.hq + kvh * G) * kHeadDim + i];
-  __syncthreads();
+__device__ inline void special_wave(const DecodeParams& p, FusedLds<G>& s, int sw, int seq, int kvh, int64_t row0,
+                                    int nw, uint32_t total, float (&m_run)[G], float (&l_run)[G],
+                                    float (&acc)[G][2]) {
+  FSpec<G>& sp = s.u.st.h.sp;
+  const int lane = threadIdx.x & 63;
   const int r = p.r;
   const float sub = __builtin_ldexpf(1.0f, -r);
+  // every special wavefront writes the whole query (the same values): it then
+  // reads only what it wrote itself
+  for (int i = lane; i < G * kHeadDim; i += 64)
+    sp.qs[i / kHeadDim][i % kHeadDim] = p.q[((int64_t)seq * p.hq + kvh * G) * kHeadDim + i];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m_run[h] = -1e30f;
@@ -201,66 +213,75 @@ __device__ inline void special_tokens(const DecodeParams& p, FusedLds<G>& s, int
     acc[h][0] = acc[h][1] = 0.f;
   }
   constexpr int LPT = 64 / kFTPW, EPL = kHeadDim / LPT;
-  const int rounds = (int)((total + kFW * kFTPW - 1) / (kFW * kFTPW));
-  for (int rd = 0; rd < rounds; ++rd) {
+  const uint32_t per_round = kFSW * kFTPW;
+  const uint32_t rounds = (total + per_round - 1) / per_round;
+  for (uint32_t rd = 0; rd < rounds; ++rd) {
     {
       // lane (tl, qd) < 4 kFTPW loads quarter qd of token tl's rows
       const int tl = lane >> 2, qd = lane & 3;
-      const uint32_t j = (uint32_t)(rd * kFW * kFTPW + wid * kFTPW + tl);
+      const uint32_t j = rd * per_round + (uint32_t)(sw * kFTPW + tl);
       const bool loader = lane < 4 * kFTPW;
       const bool valid = loader && j < total;
-      const int off = valid ? sp.list[j] : 0;
-      const bool refined = valid && ((s.sel[off >> 5] >> (off & 31)) & 1u);
+      int off = 0;
+      if (valid) {
+        // the word holding the j-th selected token (the first w with
+        // pre[w + 1] > j; pre[nw] is the total), then its bit
+        int lo_w = 0, hi_w = nw - 1;
+        while (lo_w < hi_w) {
+          const int mid = (lo_w + hi_w) >> 1;
+          if (sp.pre[mid + 1] > j) hi_w = mid; else lo_w = mid + 1;
+        }
+        uint32_t bits = s.sel[lo_w];
+        for (uint32_t k = sp.pre[lo_w]; k < j; ++k) bits &= bits - 1u;
+        off = 32 * lo_w + __ffs(bits) - 1;
+      }
       uint32_t vb[2] = {0u, 0u}, kr[8], vr[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) kr[i] = vr[i] = 0u;
       float2 ksc = make_float2(0.f, 0.f), vsc = make_float2(0.f, 0.f);
       if (valid) {
         const int64_t row = row0 + off;                       // kvh * cap + token
+        const int64_t tok = row - (int64_t)kvh * p.cap;
         const uint32_t* srcv = reinterpret_cast<const uint32_t*>(p.vc + row * 32) + qd * 2;
         vb[0] = srcv[0];
         vb[1] = srcv[1];
-        if (refined) {
-          const int64_t tok = row - (int64_t)kvh * p.cap;
-          const uint32_t* rk =
-              reinterpret_cast<const uint32_t*>(p.ref_rows + ((int64_t)kvh * p.cap + tok) * p.rb) + qd * r;
-          const uint32_t* rv =
-              reinterpret_cast<const uint32_t*>(p.ref_rows + (((int64_t)p.hkv + kvh) * p.cap + tok) * p.rb) + qd * r;
+        const uint32_t* rk =
+            reinterpret_cast<const uint32_t*>(p.ref_rows + ((int64_t)kvh * p.cap + tok) * p.rb) + qd * r;
+        const uint32_t* rv =
+            reinterpret_cast<const uint32_t*>(p.ref_rows + (((int64_t)p.hkv + kvh) * p.cap + tok) * p.rb) + qd * r;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            kr[i] = i < r ? rk[i] : 0u;
-            vr[i] = i < r ? rv[i] : 0u;
-          }
+        for (int i = 0; i < 8; ++i) {
+          kr[i] = i < r ? rk[i] : 0u;
+          vr[i] = i < r ? rv[i] : 0u;
         }
         ksc = reinterpret_cast<const float2*>(p.ks)[row];
         vsc = reinterpret_cast<const float2*>(p.vs)[row];
       }
       if (loader) {
-        sp.vt[wid][tl][qd * 2] = vb[0];
-        sp.vt[wid][tl][qd * 2 + 1] = vb[1];
+        sp.vt[sw][tl][qd * 2] = vb[0];
+        sp.vt[sw][tl][qd * 2 + 1] = vb[1];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
           if (i < r) {
-            sp.kq[wid][tl][qd * r + i] = kr[i];
-            sp.vr[wid][tl][qd * r + i] = vr[i];
+            sp.kq[sw][tl][qd * r + i] = kr[i];
+            sp.vr[sw][tl][qd * r + i] = vr[i];
           }
         if (qd == 0) {
-          sp.vt[wid][tl][8] = 0u;
-          for (int i = 4 * r; i < 33; ++i) sp.kq[wid][tl][i] = sp.vr[wid][tl][i] = 0u;
-          sp.ksc[wid][tl] = ksc;
-          sp.vsc[wid][tl] = vsc;
-          sp.hsub[wid][tl] = refined ? sub : 1.0f;
+          sp.vt[sw][tl][8] = 0u;
+          for (int i = 4 * r; i < 33; ++i) sp.kq[sw][tl][i] = sp.vr[sw][tl][i] = 0u;
+          sp.ksc[sw][tl] = ksc;
+          sp.vsc[sw][tl] = vsc;
 #pragma unroll
-          for (int h = 0; h < G; ++h) sp.lgt[wid][tl][h] = valid ? s.lg[off * G + h] : 0.f;
+          for (int h = 0; h < G; ++h) sp.lgt[sw][tl][h] = valid ? s.lg[off * G + h] : 0.f;
         }
       }
     }
     wave_barrier();
     // logits: lane (tc, e) over elements [e EPL, e EPL + EPL) of token tc
     const int tc = lane / LPT, e0 = (lane % LPT) * EPL;
-    const bool valid = (uint32_t)(rd * kFW * kFTPW + wid * kFTPW + tc) < total;
+    const bool valid = rd * per_round + (uint32_t)(sw * kFTPW + tc) < total;
     float dc[G], ds[G], dq[G];
-    const uint32_t* krrow = &sp.kq[wid][tc][0];
+    const uint32_t* krrow = &sp.kq[sw][tc][0];
     switch (r) {
       case 1: lane_dots<2, 1, G, EPL, true>(nullptr, krrow, &sp.qs[0][0], e0, dc, ds, dq); break;
       case 2: lane_dots<2, 2, G, EPL, true>(nullptr, krrow, &sp.qs[0][0], e0, dc, ds, dq); break;
@@ -271,44 +292,59 @@ __device__ inline void special_tokens(const DecodeParams& p, FusedLds<G>& s, int
       case 7: lane_dots<2, 7, G, EPL, true>(nullptr, krrow, &sp.qs[0][0], e0, dc, ds, dq); break;
       default: lane_dots<2, 8, G, EPL, true>(nullptr, krrow, &sp.qs[0][0], e0, dc, ds, dq); break;
     }
-    const float2 ksc = sp.ksc[wid][tc];
-    const float hs = sp.hsub[wid][tc];
+    const float2 ksc = sp.ksc[sw][tc];
     const bool lead = lane % LPT == 0;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float qsum = token_sum<LPT>(dq[h]);
-      const float lr = fmaf(sp.lgt[wid][tc][h], 0.6931471805599453f,
-                            ksc.y * kRsqrtD * fmaf(hs, token_sum<LPT>(ds[h]), 0.5f * (hs - 1.0f) * qsum));
-      const float mw = wave_max_dpp(valid ? lr : -INFINITY);
-      const float mnew = fmaxf(m_run[h], mw);
+      // refined - base = delta / sqrt(D) (2^-r q.s + (2^-r - 1) sum(q) / 2)
+      const float lr = fmaf(sp.lgt[sw][tc][h], 0.6931471805599453f,
+                            ksc.y * kRsqrtD * fmaf(sub, token_sum<LPT>(ds[h]), 0.5f * (sub - 1.0f) * qsum));
+      const float mwv = wave_max_dpp(valid ? lr : -INFINITY);
+      const float mnew = fmaxf(m_run[h], mwv);
       const float alpha = __expf(m_run[h] - mnew);
       const float ew = valid ? __expf(lr - mnew) : 0.f;
-      if (lead) sp.wt[wid][h][tc] = ew;
+      if (lead) sp.wt[sw][h][tc] = ew;
       l_run[h] = fmaf(l_run[h], alpha, wave_sum_dpp(lead ? ew : 0.f));
       acc[h][0] *= alpha;
       acc[h][1] *= alpha;
       m_run[h] = mnew;
     }
     wave_barrier();
+    // P.V: lane takes output elements 2 lane and 2 lane + 1; the round's
+    // reads first, then the products
     const int cpos = 4 * lane, cwi = cpos >> 5, csh = cpos & 31;
     const int rpos = 2 * lane * r, rwi = rpos >> 5, rsh = rpos & 31;
     const uint32_t rmask = (1u << r) - 1u;
+    constexpr int kHalf = kFTPW / 2;
 #pragma unroll
-    for (int jj = 0; jj < kFTPW; ++jj) {
-      const uint32_t cc = sp.vt[wid][jj][cwi] >> csh;
-      const uint64_t rwin = (uint64_t)sp.vr[wid][jj][rwi] | ((uint64_t)sp.vr[wid][jj][rwi + 1] << 32);
-      const uint32_t rr = (uint32_t)(rwin >> rsh);
-      const float c0 = (float)(cc & 3u), c1 = (float)((cc >> 2) & 3u);
-      const float s0 = (float)(rr & rmask), s1 = (float)((rr >> r) & rmask);
-      const float2 sc = sp.vsc[wid][jj];
-      const float hj = sp.hsub[wid][jj];
-      const float v0 = fmaf((s0 + 0.5f) * hj, sc.y, fmaf(c0, sc.y, sc.x));
-      const float v1 = fmaf((s1 + 0.5f) * hj, sc.y, fmaf(c1, sc.y, sc.x));
+    for (int j0 = 0; j0 < kFTPW; j0 += kHalf) {
+      uint32_t cw[kHalf], rw0[kHalf], rw1[kHalf];
+      float2 scv[kHalf];
+      float wv[kHalf][G];
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float w = sp.wt[wid][h][jj];
-        acc[h][0] = fmaf(w, v0, acc[h][0]);
-        acc[h][1] = fmaf(w, v1, acc[h][1]);
+      for (int jj = 0; jj < kHalf; ++jj) {
+        cw[jj] = sp.vt[sw][j0 + jj][cwi];
+        rw0[jj] = sp.vr[sw][j0 + jj][rwi];
+        rw1[jj] = sp.vr[sw][j0 + jj][rwi + 1];
+        scv[jj] = sp.vsc[sw][j0 + jj];
+#pragma unroll
+        for (int h = 0; h < G; ++h) wv[jj][h] = sp.wt[sw][h][j0 + jj];
+      }
+#pragma unroll
+      for (int jj = 0; jj < kHalf; ++jj) {
+        const uint32_t cc = cw[jj] >> csh;
+        const uint32_t rr = (uint32_t)((((uint64_t)rw1[jj] << 32) | rw0[jj]) >> rsh);
+        const float c0 = (float)(cc & 3u), c1 = (float)((cc >> 2) & 3u);
+        const float s0 = (float)(rr & rmask), s1 = (float)((rr >> r) & rmask);
+        const float2 sc = scv[jj];
+        const float v0 = fmaf((s0 + 0.5f) * sub, sc.y, fmaf(c0, sc.y, sc.x));
+        const float v1 = fmaf((s1 + 0.5f) * sub, sc.y, fmaf(c1, sc.y, sc.x));
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          acc[h][0] = fmaf(wv[jj][h], v0, acc[h][0]);
+          acc[h][1] = fmaf(wv[jj][h], v1, acc[h][1]);
+        }
       }
     }
     wave_barrier();
@@ -352,10 +388,10 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
     bdma16(rK, oK, c * 1024u, st.c);
     bdma4(rKS, oS, c * 256u, st.s);
   };
-  for (int i = tid; i < kHistBins; i += 64 * kFW) s.u.st.hist[i] = 0u;
+  for (int i = tid; i < kHistBins; i += 64 * kFW) s.u.st.h.hist[i] = 0u;
 #pragma unroll
   for (int k = 0; k < kFRing - 1; ++k)
-    if (k < nmine) issueK(k, s.u.st.ring[wid][k]);
+    if (k < nmine) issueK(k, s.u.st.ring[wid * kFRing + k]);
   v4i a0, a1;
   prep_query<G>(qx, s.qp, a0, a1);
   {
@@ -363,16 +399,16 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
     const float scale = s.qp.scale[hl < G ? hl : 0] * (kRsqrtD * kLog2e);
     const float sumq = s.qp.sumq[hl < G ? hl : 0] * (kRsqrtD * kLog2e);
     float* scores = p.scores + (int64_t)kvh * p.ntot + (a - p.off0) + lo;
-    const uint32_t ring0 = lds_addr(&s.u.st.ring[wid][0]);
+    const uint32_t ring0 = lds_addr(&s.u.st.ring[wid * kFRing]);
     const uint32_t aK = ring0 + (uint32_t)(t * 32 + 8 * hl);
     const uint32_t aS = ring0 + (uint32_t)(offsetof(FStage, s) + 8 * t);
     const int hx = hl >> 1;
-    const uint32_t hist0 = lds_addr(&s.u.st.hist[0]);
+    const uint32_t hist0 = lds_addr(&s.u.st.h.hist[0]);
     const uint32_t lg0 = lds_addr(&s.lg[0]);
     auto body = [&](auto kc, int i) {
       constexpr int k = decltype(kc)::value;
       constexpr int OFF = k * (int)sizeof(FStage);
-      if (i + kFRing - 1 < nmine) issueK(i + kFRing - 1, s.u.st.ring[wid][(k + kFRing - 1) % kFRing]);
+      if (i + kFRing - 1 < nmine) issueK(i + kFRing - 1, s.u.st.ring[wid * kFRing + (k + kFRing - 1) % kFRing]);
       wait_stages<2, kFRing - 1>(min(kFRing - 1, nmine - 1 - i));
       const int c = wid + kFW * i;
       uint64_t kw[2], ks[2];
@@ -417,16 +453,17 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
   __syncthreads();
 
   // ---- B: the exact top-T of the head ----------------------------------------
-  uint32_t* hist = s.u.st.hist;
+  uint32_t* hist = s.u.st.h.hist;
+  bool used2 = false, used3 = false;   // histogram levels taken (cleared at the end)
   // the range's selection words: lane 0 of each wave writes the two words of
   // the wave's 64 tokens per round
-  for (int w = tid; w < kFusedRmax / 32; w += 64 * kFW) s.excl[w] = s.sel[w] = s.cand[w] = 0u;
+  for (int w = tid; w < kFusedRmax / 32; w += 64 * kFW) s.sel[w] = s.cand[w] = 0u;
   __syncthreads();
   if (all) {
     for (int w = tid; w < nw; w += 64 * kFW) {
       const int rem = nsp - 32 * w;
       const uint32_t m = rem >= 32 ? ~0u : (1u << rem) - 1u;
-      s.excl[w] = s.sel[w] = m;
+      s.sel[w] = m;
     }
   } else if (use_hist) {
     for (int i = tid; i < kHistBins; i += 64 * kFW) {
@@ -434,11 +471,12 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
       if (c) atomicAdd(&Z[kFZH1 + i], c);
     }
     if (!group_wait(s, &Z[kFZC + 0], nwg, p.fstatus)) return;
-    for (int i = tid; i < kHistBins; i += 64 * kFW) hist[i] = ld_dev(&Z[kFZH1 + i]);
+    copy_dev_words(hist, &Z[kFZH1], kHistBins);
     __syncthreads();
     find_threshold_wave<kHistBins>(hist, (uint32_t)tn, &s.sh_bin, &s.sh_need);
     const uint32_t b1 = (uint32_t)s.sh_bin, need1 = s.sh_need;
     const bool lvl2 = hist[b1] != need1;       // the boundary bin is split
+    used2 = lvl2;
     __syncthreads();
     if (lvl2)
       for (int i = tid; i < kHistBins; i += 64 * kFW) hist[i] = 0u;
@@ -455,14 +493,12 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
         in = bin == b1;
         if (in && lvl2) atomicAdd(&hist[(key >> 8) & 0xFFFu], 1u);
       }
-      const uint64_t be = __ballot(above || in), bs = __ballot(above || (in && !lvl2)), bc = __ballot(in && lvl2);
+      const uint64_t bs = __ballot(above || (in && !lvl2)), bc = __ballot(in && lvl2);
       if (lane == 0) {
         const int w = (base + 64 * wid) >> 5;
         if (w < kFusedRmax / 32) {
-          s.excl[w] = (uint32_t)be;
           s.sel[w] = (uint32_t)bs;
           s.cand[w] = (uint32_t)bc;
-          s.excl[w + 1] = (uint32_t)(be >> 32);
           s.sel[w + 1] = (uint32_t)(bs >> 32);
           s.cand[w + 1] = (uint32_t)(bc >> 32);
         }
@@ -476,11 +512,12 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
         if (c) atomicAdd(&Z[kFZH2 + i], c);
       }
       if (!group_wait(s, &Z[kFZC + 1], nwg, p.fstatus)) return;
-      for (int i = tid; i < kHistBins; i += 64 * kFW) hist[i] = ld_dev(&Z[kFZH2 + i]);
+      copy_dev_words(hist, &Z[kFZH2], kHistBins);
       __syncthreads();
       find_threshold_wave<kHistBins>(hist, need1, &s.sh_bin, &s.sh_need);
       const uint32_t b2 = (uint32_t)s.sh_bin, need2 = s.sh_need;
       const bool lvl3 = hist[b2] != need2;
+      used3 = lvl3;
       __syncthreads();
       if (lvl3 && tid < 256) hist[tid] = 0u;
       __syncthreads();
@@ -508,7 +545,7 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
           if (c) atomicAdd(&Z[kFZH3 + tid], c);
         }
         if (!group_wait(s, &Z[kFZC + 2], nwg, p.fstatus)) return;
-        if (tid < 256) hist[tid] = ld_dev(&Z[kFZH3 + tid]);
+        copy_dev_words(hist, &Z[kFZH3], 256);
         __syncthreads();
         find_threshold_wave<256>(hist, need2, &s.sh_bin, &s.sh_need);
         const uint32_t b3 = (uint32_t)s.sh_bin, need3 = s.sh_need;
@@ -533,13 +570,10 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
           const uint32_t rank0 = block_exclusive_scan<64 * kFW>((uint32_t)__popc(ties), s.scan, mine_total);
           if (tid == 0) st_dev(&p.ftie[sk * p.ftie_stride + wi], mine_total);
           if (!group_wait(s, &Z[kFZC + 3], nwg, p.fstatus)) return;
-          if (tid == 0) {
-            uint32_t before = 0u;
-            for (int j = 0; j < wi; ++j) before += ld_dev(&p.ftie[sk * p.ftie_stride + j]);
-            s.sh_count = before;
-          }
-          __syncthreads();
-          const uint32_t before = s.sh_count;
+          // ties in the head's ranges before this one
+          uint32_t before;
+          (void)block_exclusive_scan<64 * kFW>(tid < wi ? ld_dev(&p.ftie[sk * p.ftie_stride + tid]) : 0u, s.scan,
+                                               before);
           const uint32_t take = need3 > before ? need3 - before : 0u;   // ties of this range still taken
           if (tid < nw) {
             uint32_t rank = rank0, selw = s.sel[tid];
@@ -554,205 +588,239 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
   }
   if (select && p.fsel && tid < nw) st_dev(&p.bitmap[sk * p.bm_words + (lo >> 5) + tid], s.sel[tid]);
 
-  // ---- C: V once; unselected non-candidate tokens at base precision ---------
+  // ---- C: V once (kFVW wavefronts); the selected tokens beside it (kFSW) ----
   const bool masked = select && p.use_refine != 0;
-  const rsrc_t rV = make_rsrc(p.vc + t0 * 32, (uint32_t)nsp * 32u);
-  const rsrc_t rVS = make_rsrc(p.vs + t0 * 2, (uint32_t)nsp * 8u);
-  // half L&1 of V row (L/2) ^ ((L/8) & 3): the four rows one P.V read takes
-  // fall in different LDS banks
-  const uint32_t oV = (uint32_t)(((lane >> 1) ^ ((lane >> 3) & 3)) * 32 + 16 * (lane & 1));
-  auto issueV = [&](int i, FStage& st) {
-    const uint32_t c = (uint32_t)(wid + kFW * i);
-    bdma16(rV, oV, c * 1024u, st.c);
-    bdma4(rVS, oS, c * 256u, st.s);
-  };
-  __syncthreads();   // the ring and histogram are free
-#pragma unroll
-  for (int k = 0; k < kFRing - 1; ++k)
-    if (k < nmine) issueV(k, s.u.st.ring[wid][k]);
+  __syncthreads();   // the ring and the histogram are free
+  FSpec<G>& sp = s.u.st.h.sp;
+  if (masked) {
+    const uint32_t word = tid < nw ? s.sel[tid] : 0u;
+    uint32_t total;
+    const uint32_t pos = block_exclusive_scan<64 * kFW>((uint32_t)__popc(word), s.scan, total);
+    if (tid < nw) sp.pre[tid] = (uint16_t)pos;
+    if (tid == 0) {
+      sp.pre[nw] = (uint16_t)total;
+      s.sh_count = total;
+    }
+  }
   for (int i = lane; i < 2 * G * 32; i += 64) (&s.wt[wid][0][0])[i] = (_Float16)0.f;
   if (tid < 8) s.wzero[tid] = (_Float16)0.f;
-  const uint32_t sw0 = masked && lane < nw ? s.excl[lane] : 0u;
-  const uint32_t sw1 = masked && 64 + lane < nw ? s.excl[64 + lane] : 0u;
   __syncthreads();
   const int t = lane & 15, hl = lane >> 4;        // logit layout: token t (and 16 + t), head hl
   const int n = lane & 15, rg = lane >> 4;        // P.V layout: column n, k-group rg
-  const int hlc = hl < G ? hl : 0;
-  const uint32_t hsel = 2u * (uint32_t)(n & 1);
-  const uint32_t psel = hsel | ((hsel + 1u) << 8) | ((hsel + 4u) << 16) | ((hsel + 5u) << 24);
-  const int vdw = n >> 1;
-  const uint32_t ring0 = lds_addr(&s.u.st.ring[wid][0]);
-  const uint32_t wtR = n < 2 * G ? lds_addr(&s.wt[wid][n][8 * rg]) : lds_addr(&s.wzero[0]);
-  const uint32_t wtHi = lds_addr(&s.wt[wid][hlc][2 * t]), wtLo = lds_addr(&s.wt[wid][G + hlc][2 * t]);
-  const uint32_t lgA = lds_addr(&s.lg[0]) + 4u * (uint32_t)(t * G + hlc);
-  const uint32_t aS = ring0 + (uint32_t)(offsetof(FStage, s) + 8 * t);
-  uint32_t aV[4];
+  // each wave's partial, kept in registers until the ring is free: a
+  // streaming wave's P.V (lanes n in [G, 2G)), maximum and sum; a special
+  // wave's running softmax
+  float out[8][4];
+  float mx = -INFINITY, ls = 0.f;
+  float msn[G], lsn[G], accs[G][2];
+  if (wid < kFVW) {
+    const rsrc_t rV = make_rsrc(p.vc + t0 * 32, (uint32_t)nsp * 32u);
+    const rsrc_t rVS = make_rsrc(p.vs + t0 * 2, (uint32_t)nsp * 8u);
+    const int nv = nchunks > wid ? (nchunks - wid + kFVW - 1) / kFVW : 0;   // chunks wid, wid + kFVW, ...
+    // half L&1 of V row (L/2) ^ ((L/8) & 3): the four rows one P.V read
+    // takes fall in different LDS banks
+    const uint32_t oV = (uint32_t)(((lane >> 1) ^ ((lane >> 3) & 3)) * 32 + 16 * (lane & 1));
+    FStage* ring = &s.u.st.ring[wid * kFRingV];
+    auto issueV = [&](int i, FStage& st) {
+      const uint32_t c = (uint32_t)(wid + kFVW * i);
+      bdma16(rV, oV, c * 1024u, st.c);
+      bdma4(rVS, oS, c * 256u, st.s);
+    };
 #pragma unroll
-  for (int v = 0; v < 4; ++v) aV[v] = ring0 + (uint32_t)(offsetof(FStage, c) + (4 * rg + (v ^ rg)) * 32 + 4 * vdw);
-  const uint64_t rows = G >= 4 ? ~0ull : (1ull << (16 * (G & 3))) - 1ull;
-  const float ninf = -INFINITY;
-  constexpr float kFloor = -1e30f;
-  constexpr int kSlack = 6;
-  float m = kFloor, lsum = 0.f, t1 = 0.f;
-  int sexp = 127;
-  float wsc = 1.0f;
-  v4f acc[8];
+    for (int k = 0; k < kFRingV - 1; ++k)
+      if (k < nv) issueV(k, ring[k]);
+    // the selection words of the range: lane L holds words L and 64 + L
+    const uint32_t sw0 = masked && lane < nw ? s.sel[lane] : 0u;
+    const uint32_t sw1 = masked && 64 + lane < nw ? s.sel[64 + lane] : 0u;
+    const int hlc = hl < G ? hl : 0;
+    const uint32_t hsel = 2u * (uint32_t)(n & 1);
+    const uint32_t psel = hsel | ((hsel + 1u) << 8) | ((hsel + 4u) << 16) | ((hsel + 5u) << 24);
+    const int vdw = n >> 1;
+    const uint32_t ring0 = lds_addr(ring);
+    const uint32_t wtR = n < 2 * G ? lds_addr(&s.wt[wid][n][8 * rg]) : lds_addr(&s.wzero[0]);
+    const uint32_t wtHi = lds_addr(&s.wt[wid][hlc][2 * t]), wtLo = lds_addr(&s.wt[wid][G + hlc][2 * t]);
+    const uint32_t lgA = lds_addr(&s.lg[0]) + 4u * (uint32_t)(t * G + hlc);
+    const uint32_t aS = ring0 + (uint32_t)(offsetof(FStage, s) + 8 * t);
+    uint32_t aV[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
-  auto body = [&](auto kc, int i) {
-    constexpr int k = decltype(kc)::value;
-    if (i + kFRing - 1 < nmine) issueV(i + kFRing - 1, s.u.st.ring[wid][(k + kFRing - 1) % kFRing]);
-    wait_stages<2, kFRing - 1>(min(kFRing - 1, nmine - 1 - i));
-    const int c = wid + kFW * i;
-    const int rem = nsp - 32 * c;
-    uint32_t vm = ~(uint32_t)__builtin_amdgcn_readlane((int)(c < 64 ? sw0 : sw1), c & 63);
-    if (rem < 32) vm &= (1u << rem) - 1u;
-    const uint32_t y0 = (vm & 0xFFFFu) | (vm << 16), y1 = (vm >> 16) | (vm & 0xFFFF0000u);
-    const uint64_t mk[2] = {((uint64_t)y0 | ((uint64_t)y0 << 32)) & rows, ((uint64_t)y1 | ((uint64_t)y1 << 32)) & rows};
-    float lgr[2];
-    uint64_t vsr[2];
-    uint32_t vw[8];
-    const uint32_t aL0 = lgA + 4u * (uint32_t)(32 * c * G), aL1 = aL0 + 4u * (uint32_t)(16 * G);
-    read_vstage<k * (int)sizeof(FStage)>(aL0, aL1, aS, aV, lgr, vsr, vw);
-    float lgx[2];
-    float2 vsc[2];
+    for (int v = 0; v < 4; ++v) aV[v] = ring0 + (uint32_t)(offsetof(FStage, c) + (4 * rg + (v ^ rg)) * 32 + 4 * vdw);
+    const uint64_t rows = G >= 4 ? ~0ull : (1ull << (16 * (G & 3))) - 1ull;
+    const float ninf = -INFINITY;
+    constexpr float kFloor = -1e30f;
+    constexpr int kSlack = 6;
+    float m = kFloor, lsum = 0.f, t1 = 0.f;
+    int sexp = 127;
+    float wsc = 1.0f;
+    v4f acc[8];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      lgx[j] = lane_select(mk[j], lgr[j], ninf);
-      vsc[j] = __builtin_bit_cast(float2, vsr[j]);
-    }
-    const float xm = fmaxf(lgx[0], lgx[1]);
-    const bool grow = __ballot(xm > m + kSlack) != 0ull;
-    const float mnew = grow ? fmaxf(m, row16_max_dpp(xm)) : m;
-    float dmax = fmaxf(lane_select(mk[0], vsc[0].y, 0.f), lane_select(mk[1], vsc[1].y, 0.f));
-    int need = sexp;
-    if (__ballot(dmax > 0.f && (sexp == 127 || dmax >= __builtin_ldexpf(1.0f, 14 - kSlack - sexp))) != 0ull) {
-      dmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max(dmax))));
-      int e2;
-      frexpf(dmax, &e2);
-      need = 14 - kSlack - e2;
-    }
-    if (grow || need < sexp) {
-      const float alpha = mnew > m ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;
-      lsum *= alpha;
-      t1 *= alpha;
-      const int hc = n < 2 * G ? n % G : 0;
-      float f = lane_value(alpha, 0);
+    for (int i = 0; i < 8; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+    auto body = [&](auto kc, int i) {
+      constexpr int k = decltype(kc)::value;
+      if (i + kFRingV - 1 < nv) issueV(i + kFRingV - 1, ring[(k + kFRingV - 1) % kFRingV]);
+      wait_stages<2, kFRingV - 1>(min(kFRingV - 1, nv - 1 - i));
+      const int c = wid + kFVW * i;
+      const int rem = nsp - 32 * c;
+      uint32_t vm = ~(uint32_t)__builtin_amdgcn_readlane((int)(c < 64 ? sw0 : sw1), c & 63);
+      if (rem < 32) vm &= (1u << rem) - 1u;
+      const uint32_t y0 = (vm & 0xFFFFu) | (vm << 16), y1 = (vm >> 16) | (vm & 0xFFFF0000u);
+      const uint64_t mk[2] = {((uint64_t)y0 | ((uint64_t)y0 << 32)) & rows,
+                              ((uint64_t)y1 | ((uint64_t)y1 << 32)) & rows};
+      float lgr[2];
+      uint64_t vsr[2];
+      uint32_t vw[8];
+      const uint32_t aL0 = lgA + 4u * (uint32_t)(32 * c * G), aL1 = aL0 + 4u * (uint32_t)(16 * G);
+      read_vstage<k * (int)sizeof(FStage)>(aL0, aL1, aS, aV, lgr, vsr, vw);
+      float lgx[2];
+      float2 vsc[2];
 #pragma unroll
-      for (int h = 1; h < G; ++h) {
-        // read with every lane active (a lane read inside the selection
-        // could run where lane 16 h is off)
-        const float ah = lane_value(alpha, 16 * h);
-        f = hc == h ? ah : f;
+      for (int j = 0; j < 2; ++j) {
+        lgx[j] = lane_select(mk[j], lgr[j], ninf);
+        vsc[j] = __builtin_bit_cast(float2, vsr[j]);
       }
-      if (need < sexp) {
-        if (sexp != 127) f = __builtin_ldexpf(f, need - sexp);
-        sexp = need;
-        wsc = __builtin_ldexpf(1.0f, sexp);
+      // online softmax with a lazy reference: m moves (and the sums are
+      // rescaled) only when a logit exceeds it by more than kSlack
+      const float xm = fmaxf(lgx[0], lgx[1]);
+      const bool grow = __ballot(xm > m + kSlack) != 0ull;
+      const float mnew = grow ? fmaxf(m, row16_max_dpp(xm)) : m;
+      float dmax = fmaxf(lane_select(mk[0], vsc[0].y, 0.f), lane_select(mk[1], vsc[1].y, 0.f));
+      int need = sexp;
+      if (__ballot(dmax > 0.f && (sexp == 127 || dmax >= __builtin_ldexpf(1.0f, 14 - kSlack - sexp))) != 0ull) {
+        dmax = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max(dmax))));
+        int e2;
+        frexpf(dmax, &e2);
+        need = 14 - kSlack - e2;
       }
+      if (grow || need < sexp) {
+        const float alpha = mnew > m ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;
+        lsum *= alpha;
+        t1 *= alpha;
+        const int hc = n < 2 * G ? n % G : 0;
+        float f = lane_value(alpha, 0);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] *= f;
-      m = mnew;
-    }
-    float wv[2];
+        for (int h = 1; h < G; ++h) {
+          // read with every lane active (a lane read inside the selection
+          // could run where lane 16 h is off)
+          const float ah = lane_value(alpha, 16 * h);
+          f = hc == h ? ah : f;
+        }
+        if (need < sexp) {
+          if (sexp != 127) f = __builtin_ldexpf(f, need - sexp);
+          sexp = need;
+          wsc = __builtin_ldexpf(1.0f, sexp);
+        }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const float pk = __builtin_amdgcn_exp2f(lgx[j] - m);
-      lsum += pk;
-      t1 = fmaf(pk, fmaf(0.5f, vsc[j].y, vsc[j].x), t1);
-      wv[j] = pk * (vsc[j].y * wsc);
-    }
-    const auto whi = __builtin_amdgcn_cvt_pkrtz(wv[0], wv[1]);
-    const auto wlo = __builtin_amdgcn_cvt_pkrtz(wv[0] - (float)whi[0], wv[1] - (float)whi[1]);
-    if (hl < G) {
-      lds_write_u32(wtHi, __builtin_bit_cast(uint32_t, whi));
-      lds_write_u32(wtLo, __builtin_bit_cast(uint32_t, wlo));
-    }
-    const v8h bw = lds_read_v8h(wtR);
-    uint32_t P[4];
+        for (int j = 0; j < 8; ++j) acc[j] *= f;
+        m = mnew;
+      }
+      float wv[2];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) P[v] = __builtin_amdgcn_perm(vw[2 * v + 1], vw[2 * v], psel);
+      for (int j = 0; j < 2; ++j) {
+        const float pk = __builtin_amdgcn_exp2f(lgx[j] - m);
+        lsum += pk;
+        t1 = fmaf(pk, fmaf(0.5f, vsc[j].y, vsc[j].x), t1);
+        wv[j] = pk * (vsc[j].y * wsc);
+      }
+      const auto whi = __builtin_amdgcn_cvt_pkrtz(wv[0], wv[1]);
+      const auto wlo = __builtin_amdgcn_cvt_pkrtz(wv[0] - (float)whi[0], wv[1] - (float)whi[1]);
+      if (hl < G) {
+        lds_write_u32(wtHi, __builtin_bit_cast(uint32_t, whi));
+        lds_write_u32(wtLo, __builtin_bit_cast(uint32_t, wlo));
+      }
+      const v8h bw = lds_read_v8h(wtR);
+      uint32_t P[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) P[v] = __builtin_amdgcn_perm(vw[2 * v + 1], vw[2 * v], psel);
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        const uint32_t msk = 0x00030003u << code_bit(tt);
+        v4u av;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) av[v] = (tt < 2 ? P[v] << 4 : tt < 5 ? P[v] : P[v] >> 6) & msk;
+        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, av), bw, acc[tt], 0, 0, 0);
+      }
+    };
+    for (int i = 0; i < nv; i += kFRingV) {
+      progress_priority(nv - i, nv);
+      ring_round<kFRingV>(body, i, nv);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // the wave's row sums (l and the scalar term per head); lane n in
+    // [G, 2G) holds head n - G's lo column, row_shr:G brings it the hi
+    // column of lane n - G, and the scalar term goes with it
+    lsum = row16_sum(lsum);
+    t1 = row16_sum(t1);
+    float t1h = 0.f;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float th = lane_value(t1, 16 * h);   // every lane active (see the rescale above)
+      t1h = n - G == h ? th : t1h;
+    }
+    const int se = sexp == 127 ? 0 : sexp;
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
-      const uint32_t msk = 0x00030003u << code_bit(tt);
-      v4u av;
+      const float f = __builtin_ldexpf(1.0f, 24 - code_bit(tt) - se);
 #pragma unroll
-      for (int v = 0; v < 4; ++v) av[v] = (tt < 2 ? P[v] << 4 : tt < 5 ? P[v] : P[v] >> 6) & msk;
-      acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, av), bw, acc[tt], 0, 0, 0);
+      for (int j = 0; j < 4; ++j) {
+        const float x = acc[tt][j] * f;
+        const float hi_part =
+            __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + G, 0xF, 0xF, false));
+        out[tt][j] = x + hi_part + t1h;
+      }
     }
-  };
-  for (int i = 0; i < nmine; i += kFRing) {
-    progress_priority(nmine - i, nmine);
-    ring_round<kFRing>(body, i, nmine);
-  }
-  __builtin_amdgcn_s_setprio(0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();   // the ring is reused below
-
-  // the wave's base partial: l and the scalar term per head (row sums), P.V
-  // columns hi + lo summed per head (lane n < G takes lane n + G's lo part)
-  lsum = row16_sum(lsum);
-  t1 = row16_sum(t1);
-  if (hl < G && t == 0) {
-    s.mb[wid][hl] = m == kFloor ? -INFINITY : m;
-    s.lb[wid][hl] = lsum;
-  }
-  // lane n in [G, 2G) holds head n - G's lo column; row_shr:G brings it the
-  // hi column of lane n - G, and the scalar term goes with it
-  float t1h = 0.f;
+    mx = m == kFloor ? -INFINITY : m;
+    ls = lsum;
+  } else {
+    if (masked) {
+      special_wave<G>(p, s, wid - kFVW, seq, kvh, t0, nw, s.sh_count, msn, lsn, accs);
+    } else {
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float th = lane_value(t1, 16 * h);   // every lane active (see the rescale above)
-    t1h = n - G == h ? th : t1h;
-  }
-  const int se = sexp == 127 ? 0 : sexp;
-#pragma unroll
-  for (int tt = 0; tt < 8; ++tt) {
-    const float f = __builtin_ldexpf(1.0f, 24 - code_bit(tt) - se);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float x = acc[tt][j] * f;
-      const float hi_part =
-          __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 + G, 0xF, 0xF, false));
-      if (n >= G && n < 2 * G) s.u.mg.accb[wid][n - G][32 * rg + 8 * j + tt] = x + hi_part + t1h;
+      for (int h = 0; h < G; ++h) {
+        msn[h] = -1e30f;
+        lsn[h] = 0.f;
+        accs[h][0] = accs[h][1] = 0.f;
+      }
     }
   }
-
-  // ---- D: special tokens (selected, refined; level-1 candidates left out) --
-  float msn[G], lsn[G], accs[G][2];
+  __syncthreads();   // every wave is done with the ring and the staging
+  if (wid < kFVW) {
+    if (hl < G && t == 0) {
+      s.mw[wid][hl] = mx;
+      s.lw[wid][hl] = ls;
+    }
+    if (n >= G && n < 2 * G) {
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    msn[h] = -1e30f;
-    lsn[h] = 0.f;
-    accs[h][0] = accs[h][1] = 0.f;
-  }
-  if (masked) special_tokens<G>(p, s, seq, kvh, t0, nw, msn, lsn, accs);
-  __syncthreads();
+      for (int tt = 0; tt < 8; ++tt)
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    s.u.mg.x.accs[wid][h][2 * lane] = accs[h][0];
-    s.u.mg.x.accs[wid][h][2 * lane + 1] = accs[h][1];
-    if (lane == 0) {
-      s.ms[wid][h] = lsn[h] > 0.f ? msn[h] * kLog2e : -INFINITY;   // log2 units, as the base pass
-      s.ls[wid][h] = lsn[h];
+        for (int j = 0; j < 4; ++j) s.u.acc[wid][n - G][32 * rg + 8 * j + tt] = out[tt][j];
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      s.u.acc[wid][h][2 * lane] = accs[h][0];
+      s.u.acc[wid][h][2 * lane + 1] = accs[h][1];
+      if (lane == 0) {
+        s.mw[wid][h] = lsn[h] > 0.f ? msn[h] * kLog2e : -INFINITY;   // log2 units, as the stream's
+        s.lw[wid][h] = lsn[h];
+      }
     }
   }
   __syncthreads();
 
-  // ---- the range's partial ----------------------------------------------------
+  // ---- D: the range's partial: the waves' partials merged -------------------
   float* part = p.part + ((int64_t)kvh * gridDim.x + blockIdx.x) * G * kPartStride;
   for (int i = tid; i < G * kHeadDim; i += 64 * kFW) {
     const int h = i / kHeadDim, d = i % kHeadDim;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kFW; ++w) M = fmaxf(M, fmaxf(s.mb[w][h], s.ms[w][h]));
+    for (int w = 0; w < kFW; ++w) M = fmaxf(M, s.mw[w][h]);
     float A = 0.f, L = 0.f;
     if (M != -INFINITY) {
 #pragma unroll 4
       for (int w = 0; w < kFW; ++w) {
-        const float eb = __builtin_amdgcn_exp2f(s.mb[w][h] - M), es = __builtin_amdgcn_exp2f(s.ms[w][h] - M);
-        A = fmaf(eb, s.u.mg.accb[w][h][d], fmaf(es, s.u.mg.x.accs[w][h][d], A));
-        L = fmaf(eb, s.lb[w][h], fmaf(es, s.ls[w][h], L));
+        const float e = __builtin_amdgcn_exp2f(s.mw[w][h] - M);   // 0 for a wave without tokens
+        A = fmaf(e, s.u.acc[w][h][d], A);
+        L = fmaf(e, s.lw[w][h], L);
       }
     }
     st_dev(&part[h * kPartStride + d], A);
@@ -768,45 +836,82 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
   if (tid == 0) s.sh_flag = atomicAdd(&Z[kFZC + 4], 1u) == nwg - 1u ? 1u : 0u;
   __syncthreads();
   if (!s.sh_flag) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  // the head's partials in one round of loads: (m, l) of every range and
+  // head into LDS by the first G nwg threads (the host keeps nwg <=
+  // kFusedMaxRanges, which fits these arrays), and at the same time each
+  // output element's accumulators by two threads, half the ranges each
   const float* part0 = p.part + ((int64_t)kvh * gridDim.x + first) * G * kPartStride;
+  const rsrc_t rP = make_rsrc(part0, nwg * (uint32_t)(G * kPartStride * 4));
+  float* mwg = reinterpret_cast<float*>(&s.u.acc[0][0][0]);   // [G][nwg] maxima, then weights
+  float* lwg = mwg + G * nwg;                                   // [G][nwg] sums
+  float* half = lwg + G * nwg;                                  // [G][kHeadDim] second halves
+  for (int i = tid; i < G * (int)nwg; i += 64 * kFW) {
+    const int h = i / nwg, w = i % nwg;
+    const uint32_t o = (uint32_t)((w * G + h) * kPartStride + kHeadDim) * 4u;
+    mwg[i] = ld_devf(rP, o);
+    lwg[i] = ld_devf(rP, o + 4u);
+  }
+  const int io = tid % (G * kHeadDim), hlf = tid / (G * kHeadDim);   // G * kHeadDim <= 512 outputs
+  const int ho = io / kHeadDim, dout = io % kHeadDim;
+  const uint32_t w0 = hlf ? nwg / 2 : 0u, w1 = hlf ? nwg : nwg / 2;
+  constexpr int kMaxHalf = kFusedMaxRanges / 2;
+  float xa[kMaxHalf < 32 ? kMaxHalf : 32];
+  const bool summer = tid < 2 * G * kHeadDim;
+  // the first 32 ranges of the thread's half are loaded before the barrier
+#pragma unroll
+  for (int j = 0; j < 32; ++j)
+    xa[j] = summer && w0 + j < w1 ? ld_devf(rP, (uint32_t)(((w0 + j) * G + ho) * kPartStride + dout) * 4u) : 0.f;
+  __syncthreads();
   if (tid < G) {
     float M = -INFINITY;
-    for (uint32_t w = 0; w < nwg; ++w) M = fmaxf(M, ld_dev(&part0[(w * G + tid) * kPartStride + kHeadDim]));
+    for (uint32_t w = 0; w < nwg; ++w) M = fmaxf(M, mwg[tid * nwg + w]);
     s.mstar[tid] = M;
   }
   __syncthreads();
-  for (int i = tid; i < G * kHeadDim; i += 64 * kFW) {
-    const int h = i / kHeadDim, d = i % kHeadDim;
-    const float M = s.mstar[h];
-    float num = 0.f, den = 0.f;
-    for (uint32_t w = 0; w < nwg; ++w) {
-      const float* pw = part0 + (w * G + h) * kPartStride;
-      const float mw = ld_dev(&pw[kHeadDim]);
-      const float e = mw == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-      num = fmaf(e, ld_dev(&pw[d]), num);
-      den = fmaf(e, ld_dev(&pw[kHeadDim + 1]), den);
-    }
-    p.out[((int64_t)seq * p.hq + kvh * G + h) * kHeadDim + d] = num / den;
+  for (int i = tid; i < G * (int)nwg; i += 64 * kFW) {
+    const float mv = mwg[i];
+    mwg[i] = mv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv - s.mstar[i / nwg]);
+  }
+  __syncthreads();
+  float num = 0.f;
+  if (summer) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j)
+      if (w0 + j < w1) num = fmaf(mwg[ho * nwg + w0 + j], xa[j], num);
+    for (uint32_t w = w0 + 32; w < w1; ++w)
+      num = fmaf(mwg[ho * nwg + w], ld_devf(rP, (uint32_t)((w * G + ho) * kPartStride + dout) * 4u), num);
+    if (hlf) half[io] = num;
+  }
+  __syncthreads();
+  if (tid < G * kHeadDim) {
+    float den = 0.f;
+    for (uint32_t w = 0; w < nwg; ++w) den = fmaf(mwg[ho * nwg + w], lwg[ho * nwg + w], den);
+    p.out[((int64_t)seq * p.hq + kvh * G + ho) * kHeadDim + dout] = (num + half[io]) / den;
   }
   if (select && p.fsel) {
     // the selection, ascending, from the ranges' words
     const uint32_t* bm = p.bitmap + sk * p.bm_words;
     const int64_t nwh = (n_s + 31) >> 5;
     const int64_t per = (nwh + 64 * kFW - 1) / (64 * kFW);
-    const int64_t w0 = tid * per < nwh ? tid * per : nwh, w1 = w0 + per < nwh ? w0 + per : nwh;
+    const int64_t ww0 = tid * per < nwh ? tid * per : nwh, ww1 = ww0 + per < nwh ? ww0 + per : nwh;
     uint32_t cnt = 0;
-    for (int64_t w = w0; w < w1; ++w) cnt += __popc(ld_dev(&bm[w]));
+    for (int64_t w = ww0; w < ww1; ++w) cnt += __popc(ld_dev(&bm[w]));
     uint32_t tot;
     uint32_t pos = block_exclusive_scan<64 * kFW>(cnt, s.scan, tot);
     int32_t* selo = p.sel_out + sk * p.top_t;
-    for (int64_t w = w0; w < w1; ++w)
+    for (int64_t w = ww0; w < ww1; ++w)
       for (uint32_t bits = ld_dev(&bm[w]); bits; bits &= bits - 1u, ++pos)
         if (pos < (uint32_t)p.top_t) selo[pos] = (int32_t)((w << 5) + __ffs(bits) - 1);
     for (int64_t j = tn + tid; j < p.top_t; j += 64 * kFW) selo[j] = -1;
   }
-  // the head's histograms and counters, zero for the next step
-  for (int i = tid; i < kFZWords; i += 64 * kFW) st_dev(&Z[i], 0u);
+  // the head's histograms and counters, zero for the next step (the levels
+  // taken: every work-group of the head took the same)
+  for (int i = tid; i < kHistBins; i += 64 * kFW) {
+    if (use_hist) st_dev(&Z[kFZH1 + i], 0u);
+    if (used2) st_dev(&Z[kFZH2 + i], 0u);
+  }
+  if (used3 && tid < 256) st_dev(&Z[kFZH3 + tid], 0u);
+  if (tid < 16) st_dev(&Z[kFZC + tid], 0u);
 }
 
 template <int G, bool Batched>

@@ -78,6 +78,11 @@ class Decoder:
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         self._hist_clean = False   # a successful step leaves the workspace histogram zero
 
+    def form(self, cache: "LayerCache", multi_pass: bool = False) -> int:
+        """Kernels per step (1: single launch, 5) for this cache."""
+        return B.sf_decode_form(self.g, self.seq_off, self.top_t, cache.store,
+                                B.SF_DECODE_MULTI_PASS if multi_pass else 0)
+
     def check(self) -> int:
         """sf_decode_check on this decoder's workspace (synchronizes)."""
         return B.sf_decode_check(self.workspace)
