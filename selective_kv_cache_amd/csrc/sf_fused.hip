@@ -54,7 +54,7 @@ constexpr int kFVW = 12;         // of them streaming V in phase C,
 constexpr int kFSW = kFW - kFVW; // and taking the selected tokens beside them
 constexpr int kFRing = 3;        // phase A: ring stages per wavefront (2 chunks in flight)
 constexpr int kFRingV = kFW * kFRing / kFVW;   // phase C: 4 stages per streaming wavefront
-constexpr int kFTPW = 8;         // selected tokens per special wavefront per round
+constexpr int kFTPW = 16;        // tokens per batch of a special wavefront (4 lanes each)
 constexpr int kFSpinLimit = 1 << 18;   // bounded waits: about 0.2 s
 static_assert(kFRingV * kFVW == kFW * kFRing, "phase C's ring is phase A's");
 static_assert(2 * kFusedMaxRanges + kHeadDim <= kFW * kHeadDim, "merge arrays fit in the wave partials");
@@ -67,13 +67,11 @@ struct FStage {
 template <int G>
 struct FSpec {                   // the special wavefronts' staging (in the histogram's place)
   float qs[G][kHeadDim];
-  uint32_t kq[kFSW][kFTPW][33];  // K refinement rows (r <= 8: 32 words + a zero word)
   uint32_t vt[kFSW][kFTPW][9];   // V base codes (2 bits: 8 words + a zero word)
-  uint32_t vr[kFSW][kFTPW][33];  // V refinement rows
-  float2 vsc[kFSW][kFTPW], ksc[kFSW][kFTPW];
-  float lgt[kFSW][kFTPW][G];     // base logits (log2 units)
+  uint32_t vr[kFSW][kFTPW][33];  // V refinement rows (r <= 8: 32 words + a zero word; zero at base precision)
+  float2 vsc[kFSW][kFTPW];       // V (lo, delta)
+  float2 vfr[kFSW][kFTPW];       // value = lo + delta (c + s x + y): (x, y) = (2^-r, 2^-r / 2), or (0, 1/2)
   float wt[kFSW][G][kFTPW];
-  uint16_t pre[kFusedRmax / 32 + 1];   // selected tokens before each selection word
 };
 
 template <int G>
@@ -83,22 +81,27 @@ struct FusedLds {
     struct {
       FStage ring[kFW * kFRing];             // A: [wave][kFRing]; C: [streaming wave][kFRingV]
       union {
-        uint32_t hist[kHistBins];            // selection
+        uint32_t hist[kHistBins];            // level 1 of the selection
         FSpec<G> sp;                         // phase C
       } h;
     } st;
     float acc[kFW][G][kHeadDim];             // per-wave partials: P.V of the wave's tokens
   } u;
   QPrep qp;
-  alignas(16) _Float16 wt[kFW][2 * G][32];   // P.V weights: hi parts, then lo parts
+  alignas(16) _Float16 wt[kFVW][2 * G][32];  // P.V weights of the streaming waves: hi parts, then lo parts
   alignas(16) _Float16 wzero[8];
-  uint32_t sel[kFusedRmax / 32];             // selected tokens
-  uint32_t cand[kFusedRmax / 32];            // candidates still undecided
+  uint32_t sel[kFusedRmax / 32];             // selected at level 1 (above the boundary bin, or the whole bin)
+  uint32_t cand[kFusedRmax / 32];            // in the level-1 boundary bin, left to the later levels
+  uint32_t csel[kFusedRmax / 32];            // candidates the later levels selected
+  uint16_t pre1[kFusedRmax / 32 + 1];        // selected tokens before each word
+  uint16_t pre2[kFusedRmax / 32 + 1];        // candidates before each word
   float mw[kFW][G], lw[kFW][G];              // per-wave partials: maxima (log2 units), sums
   float mstar[G];
   uint32_t scan[kFW];
   int sh_bin;
-  uint32_t sh_need, sh_flag, sh_count;
+  uint32_t sh_need, sh_flag;
+  uint32_t n1, n2;                           // lengths of the two lists
+  uint32_t sel_done, used3;                  // candidates settled; level 3 taken
 };
 
 __device__ inline uint32_t ld_dev(const uint32_t* p) {
@@ -190,165 +193,313 @@ __device__ inline void read_vstage(uint32_t aL0, uint32_t aL1, uint32_t aS, cons
       : "memory");
 }
 
-// Phase C, special wavefront sw (0 .. kFSW-1): the range's selected tokens
-// with their refined keys and values, kFTPW at a time (tokens sw kFTPW ..
-// of each round of kFSW kFTPW), in the wave's own online softmax (natural
-// units).  sp.pre holds the selected tokens before each selection word.
-template <int G>
-__device__ inline void special_wave(const DecodeParams& p, FusedLds<G>& s, int sw, int seq, int kvh, int64_t row0,
-                                    int nw, uint32_t total, float (&m_run)[G], float (&l_run)[G],
-                                    float (&acc)[G][2]) {
-  FSpec<G>& sp = s.u.st.h.sp;
-  const int lane = threadIdx.x & 63;
-  const int r = p.r;
-  const float sub = __builtin_ldexpf(1.0f, -r);
-  // every special wavefront writes the whole query (the same values): it then
-  // reads only what it wrote itself
-  for (int i = lane; i < G * kHeadDim; i += 64)
-    sp.qs[i / kHeadDim][i % kHeadDim] = p.q[((int64_t)seq * p.hq + kvh * G) * kHeadDim + i];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m_run[h] = -1e30f;
-    l_run[h] = 0.f;
-    acc[h][0] = acc[h][1] = 0.f;
+// Arrive at `ctr` and wait until `expected` work-groups have, for one
+// wavefront alone (the selector of phase C): its device-scope stores and
+// atomics complete first.  Returns false (status word set) when the wait
+// expired.
+__device__ inline bool wave_group_wait(uint32_t* ctr, uint32_t expected, uint32_t* status) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  uint32_t ok = 1u;
+  if ((threadIdx.x & 63) == 0) {
+    atomicAdd(ctr, 1u);
+    int spins = 0;
+    while (ld_dev(ctr) < expected) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kFSpinLimit) {
+        atomicOr(status, 1u);
+        ok = 0u;
+        break;
+      }
+    }
   }
-  constexpr int LPT = 64 / kFTPW, EPL = kHeadDim / LPT;
-  const uint32_t per_round = kFSW * kFTPW;
-  const uint32_t rounds = (total + per_round - 1) / per_round;
-  for (uint32_t rd = 0; rd < rounds; ++rd) {
-    {
-      // lane (tl, qd) < 4 kFTPW loads quarter qd of token tl's rows
-      const int tl = lane >> 2, qd = lane & 3;
-      const uint32_t j = rd * per_round + (uint32_t)(sw * kFTPW + tl);
-      const bool loader = lane < 4 * kFTPW;
-      const bool valid = loader && j < total;
-      int off = 0;
-      if (valid) {
-        // the word holding the j-th selected token (the first w with
-        // pre[w + 1] > j; pre[nw] is the total), then its bit
-        int lo_w = 0, hi_w = nw - 1;
-        while (lo_w < hi_w) {
-          const int mid = (lo_w + hi_w) >> 1;
-          if (sp.pre[mid + 1] > j) hi_w = mid; else lo_w = mid + 1;
+  return __builtin_amdgcn_readfirstlane(ok) != 0u;
+}
+
+// The boundary bin of a histogram of NB bins in device memory, counted from
+// the top bin down, by one wavefront: bin b with count(bins > b) < need <=
+// count(bins >= b), the number still needed inside b, and b's count (every
+// lane receives them).  Lane l first sums bins [NB - PER (l + 1), NB - PER l)
+// (device-scope loads); the lane whose range holds the boundary is found
+// from the prefix over lanes, then its PER bins are loaded one per lane.
+// Needs 1 <= need <= the histogram's total.
+template <int NB>
+__device__ inline void find_threshold_dev(const uint32_t* hist, uint32_t need, int& bin, uint32_t& need_out,
+                                          uint32_t& count) {
+  static_assert(NB % 256 == 0 && NB <= 4096, "PER = NB / 64 bins per lane, a multiple of 4");
+  constexpr int PER = NB / 64, Q = PER / 4;
+  const int lane = threadIdx.x & 63;
+  const rsrc_t r = make_rsrc(hist, NB * 4u);
+  uint32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < Q; ++i) {
+    const uint4 x = ld_dev4(r, 4u * (uint32_t)(NB - PER * (lane + 1)) + 16u * i);
+    sum += x.x + x.y + x.z + x.w;
+  }
+  const uint32_t inc = wave_inclusive_scan(sum);
+  const uint64_t hit = __ballot(inc - sum < need && need <= inc);
+  const int L = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
+  const uint32_t above = __builtin_amdgcn_readlane(inc - sum, L);
+  // lane j takes bin NB - PER L - 1 - j
+  const uint32_t c = lane < PER ? __builtin_bit_cast(uint32_t, ld_devf(r, 4u * (uint32_t)(NB - PER * L - 1 - lane))) : 0u;
+  const uint32_t cum = wave_inclusive_scan(c);
+  const uint64_t hit2 = __ballot(lane < PER && above + cum >= need);
+  const int j = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit2) - 1);
+  bin = NB - PER * L - 1 - j;
+  count = __builtin_amdgcn_readlane(c, j);
+  need_out = need - above - __builtin_amdgcn_readlane(cum - c, j);
+}
+
+// Levels 2 and 3 of the selection and the index ties, by one wavefront (the
+// selector), while the other wavefronts stream V: the level-1 candidates of
+// the range (s.cand) are settled into s.csel.  Level 2 histograms the next
+// 12 key bits of the head's candidates, level 3 the last 8 bits of those in
+// the level-2 boundary bin, straight into the head's histograms in device
+// memory (a range holds few candidates); exactly equal scores go to the
+// lower token index.  Each level is one more wait, taken only when the level
+// above leaves its boundary bin split (the same for every work-group of the
+// head).  Lane l holds words l and 64 + l.
+template <int G>
+__device__ inline void select_candidates(const DecodeParams& p, FusedLds<G>& s, uint32_t* Z, int nw, uint32_t nwg,
+                                         uint32_t need1, int64_t sk, int wi) {
+  const int lane = threadIdx.x & 63;
+  uint32_t cw[2], selw[2] = {0u, 0u}, next[2] = {0u, 0u};
+#pragma unroll
+  for (int k = 0; k < 2; ++k) cw[k] = 64 * k + lane < nw ? s.cand[64 * k + lane] : 0u;
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    for (uint32_t bits = cw[k]; bits; bits &= bits - 1u) {
+      const int t = 32 * (64 * k + lane) + __ffs(bits) - 1;
+      atomicAdd(&Z[kFZH2 + ((token_key<G>(s.lg, t) >> 8) & 0xFFFu)], 1u);
+    }
+  if (wave_group_wait(&Z[kFZC + 1], nwg, p.fstatus)) {
+    int b2;
+    uint32_t need2, cnt2;
+    find_threshold_dev<kHistBins>(&Z[kFZH2], need1, b2, need2, cnt2);
+    const bool lvl3 = cnt2 != need2;
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      for (uint32_t bits = cw[k]; bits; bits &= bits - 1u) {
+        const int bit = __ffs(bits) - 1;
+        const uint32_t key = token_key<G>(s.lg, 32 * (64 * k + lane) + bit);
+        const int mid = (int)((key >> 8) & 0xFFFu);
+        if (mid > b2 || (mid == b2 && !lvl3)) {
+          selw[k] |= 1u << bit;
+        } else if (mid == b2) {
+          next[k] |= 1u << bit;
+          atomicAdd(&Z[kFZH3 + (key & 0xFFu)], 1u);
         }
-        uint32_t bits = s.sel[lo_w];
-        for (uint32_t k = sp.pre[lo_w]; k < j; ++k) bits &= bits - 1u;
-        off = 32 * lo_w + __ffs(bits) - 1;
       }
-      uint32_t vb[2] = {0u, 0u}, kr[8], vr[8];
+    if (lvl3) {
+      if (lane == 0) s.used3 = 1u;
+      if (wave_group_wait(&Z[kFZC + 2], nwg, p.fstatus)) {
+        int b3;
+        uint32_t need3, cnt3;
+        find_threshold_dev<256>(&Z[kFZH3], need2, b3, need3, cnt3);
+        const bool lvl4 = cnt3 != need3;
+        uint32_t ties[2] = {0u, 0u};
 #pragma unroll
-      for (int i = 0; i < 8; ++i) kr[i] = vr[i] = 0u;
-      float2 ksc = make_float2(0.f, 0.f), vsc = make_float2(0.f, 0.f);
-      if (valid) {
-        const int64_t row = row0 + off;                       // kvh * cap + token
-        const int64_t tok = row - (int64_t)kvh * p.cap;
-        const uint32_t* srcv = reinterpret_cast<const uint32_t*>(p.vc + row * 32) + qd * 2;
-        vb[0] = srcv[0];
-        vb[1] = srcv[1];
-        const uint32_t* rk =
-            reinterpret_cast<const uint32_t*>(p.ref_rows + ((int64_t)kvh * p.cap + tok) * p.rb) + qd * r;
-        const uint32_t* rv =
-            reinterpret_cast<const uint32_t*>(p.ref_rows + (((int64_t)p.hkv + kvh) * p.cap + tok) * p.rb) + qd * r;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          kr[i] = i < r ? rk[i] : 0u;
-          vr[i] = i < r ? rv[i] : 0u;
-        }
-        ksc = reinterpret_cast<const float2*>(p.ks)[row];
-        vsc = reinterpret_cast<const float2*>(p.vs)[row];
-      }
-      if (loader) {
-        sp.vt[sw][tl][qd * 2] = vb[0];
-        sp.vt[sw][tl][qd * 2 + 1] = vb[1];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if (i < r) {
-            sp.kq[sw][tl][qd * r + i] = kr[i];
-            sp.vr[sw][tl][qd * r + i] = vr[i];
+        for (int k = 0; k < 2; ++k)
+          for (uint32_t bits = next[k]; bits; bits &= bits - 1u) {
+            const int bit = __ffs(bits) - 1;
+            const int low = (int)(token_key<G>(s.lg, 32 * (64 * k + lane) + bit) & 0xFFu);
+            if (low > b3 || (low == b3 && !lvl4))
+              selw[k] |= 1u << bit;
+            else if (low == b3)
+              ties[k] |= 1u << bit;
           }
-        if (qd == 0) {
-          sp.vt[sw][tl][8] = 0u;
-          for (int i = 4 * r; i < 33; ++i) sp.kq[sw][tl][i] = sp.vr[sw][tl][i] = 0u;
-          sp.ksc[sw][tl] = ksc;
-          sp.vsc[sw][tl] = vsc;
+        if (lvl4) {
+          // rank of each tie in the range (words in token order: lane, then
+          // 64 + lane), the range's count to the head, then the ties of the
+          // head's ranges before this one
+          const uint32_t c0 = (uint32_t)__popc(ties[0]), c1 = (uint32_t)__popc(ties[1]);
+          const uint32_t i0 = wave_inclusive_scan(c0), i1 = wave_inclusive_scan(c1);
+          const uint32_t t0 = __builtin_amdgcn_readlane(i0, 63);
+          uint32_t rank[2] = {i0 - c0, t0 + i1 - c1};
+          if (lane == 0) st_dev(&p.ftie[sk * p.ftie_stride + wi], t0 + __builtin_amdgcn_readlane(i1, 63));
+          if (wave_group_wait(&Z[kFZC + 3], nwg, p.fstatus)) {
+            uint32_t before = 0u;
+            for (int w = lane; w < wi; w += 64) before += ld_dev(&p.ftie[sk * p.ftie_stride + w]);
+            before = __builtin_amdgcn_readlane(wave_inclusive_scan(before), 63);
+            const uint32_t take = need3 > before ? need3 - before : 0u;   // ties of this range still taken
 #pragma unroll
-          for (int h = 0; h < G; ++h) sp.lgt[sw][tl][h] = valid ? s.lg[off * G + h] : 0.f;
+            for (int k = 0; k < 2; ++k)
+              for (uint32_t bits = ties[k]; bits; bits &= bits - 1u, ++rank[k])
+                if (rank[k] < take) selw[k] |= 1u << (__ffs(bits) - 1);
+          }
         }
       }
     }
-    wave_barrier();
-    // logits: lane (tc, e) over elements [e EPL, e EPL + EPL) of token tc
-    const int tc = lane / LPT, e0 = (lane % LPT) * EPL;
-    const bool valid = rd * per_round + (uint32_t)(sw * kFTPW + tc) < total;
-    float dc[G], ds[G], dq[G];
-    const uint32_t* krrow = &sp.kq[sw][tc][0];
-    switch (r) {
-      case 1: lane_dots<2, 1, G, EPL, true>(nullptr, krrow, &sp.qs[0][0], e0, dc, ds, dq); break;
-      case 2: lane_dots<2, 2, G, EPL, true>(nullptr, krrow, &sp.qs[0][0], e0, dc, ds, dq); break;
-      case 3: lane_dots<2, 3, G, EPL, true>(nullptr, krrow, &sp.qs[0][0], e0, dc, ds, dq); break;
-      case 4: lane_dots<2, 4, G, EPL, true>(nullptr, krrow, &sp.qs[0][0], e0, dc, ds, dq); break;
-      case 5: lane_dots<2, 5, G, EPL, true>(nullptr, krrow, &sp.qs[0][0], e0, dc, ds, dq); break;
-      case 6: lane_dots<2, 6, G, EPL, true>(nullptr, krrow, &sp.qs[0][0], e0, dc, ds, dq); break;
-      case 7: lane_dots<2, 7, G, EPL, true>(nullptr, krrow, &sp.qs[0][0], e0, dc, ds, dq); break;
-      default: lane_dots<2, 8, G, EPL, true>(nullptr, krrow, &sp.qs[0][0], e0, dc, ds, dq); break;
-    }
-    const float2 ksc = sp.ksc[sw][tc];
-    const bool lead = lane % LPT == 0;
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    if (64 * k + lane < nw) s.csel[64 * k + lane] = selw[k];
+}
+
+// q . s over quarter qd of head_dim for each of the G heads, from the lane's
+// R-bit refinement codes in registers: four codes at a time, each taken by
+// every head (few registers live).
+template <int R, int G>
+__device__ inline void quarter_qs(const uint32_t (&kr)[8], const float* qs, int qd, float (&ds)[G]) {
+#pragma unroll
+  for (int h = 0; h < G; ++h) ds[h] = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float c0 = (float)code_at<R>(kr, 4 * i), c1 = (float)code_at<R>(kr, 4 * i + 1);
+    const float c2 = (float)code_at<R>(kr, 4 * i + 2), c3 = (float)code_at<R>(kr, 4 * i + 3);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float qsum = token_sum<LPT>(dq[h]);
-      // refined - base = delta / sqrt(D) (2^-r q.s + (2^-r - 1) sum(q) / 2)
-      const float lr = fmaf(sp.lgt[sw][tc][h], 0.6931471805599453f,
-                            ksc.y * kRsqrtD * fmaf(sub, token_sum<LPT>(ds[h]), 0.5f * (sub - 1.0f) * qsum));
-      const float mwv = wave_max_dpp(valid ? lr : -INFINITY);
-      const float mnew = fmaxf(m_run[h], mwv);
-      const float alpha = __expf(m_run[h] - mnew);
-      const float ew = valid ? __expf(lr - mnew) : 0.f;
-      if (lead) sp.wt[sw][h][tc] = ew;
-      l_run[h] = fmaf(l_run[h], alpha, wave_sum_dpp(lead ? ew : 0.f));
-      acc[h][0] *= alpha;
-      acc[h][1] *= alpha;
-      m_run[h] = mnew;
+      const float4 v = reinterpret_cast<const float4*>(qs + h * kHeadDim + 32 * qd)[i];
+      ds[h] = fmaf(v.x, c0, ds[h]);
+      ds[h] = fmaf(v.y, c1, ds[h]);
+      ds[h] = fmaf(v.z, c2, ds[h]);
+      ds[h] = fmaf(v.w, c3, ds[h]);
     }
-    wave_barrier();
-    // P.V: lane takes output elements 2 lane and 2 lane + 1; the round's
-    // reads first, then the products
-    const int cpos = 4 * lane, cwi = cpos >> 5, csh = cpos & 31;
-    const int rpos = 2 * lane * r, rwi = rpos >> 5, rsh = rpos & 31;
-    const uint32_t rmask = (1u << r) - 1u;
-    constexpr int kHalf = kFTPW / 2;
-#pragma unroll
-    for (int j0 = 0; j0 < kFTPW; j0 += kHalf) {
-      uint32_t cw[kHalf], rw0[kHalf], rw1[kHalf];
-      float2 scv[kHalf];
-      float wv[kHalf][G];
-#pragma unroll
-      for (int jj = 0; jj < kHalf; ++jj) {
-        cw[jj] = sp.vt[sw][j0 + jj][cwi];
-        rw0[jj] = sp.vr[sw][j0 + jj][rwi];
-        rw1[jj] = sp.vr[sw][j0 + jj][rwi + 1];
-        scv[jj] = sp.vsc[sw][j0 + jj];
-#pragma unroll
-        for (int h = 0; h < G; ++h) wv[jj][h] = sp.wt[sw][h][j0 + jj];
-      }
-#pragma unroll
-      for (int jj = 0; jj < kHalf; ++jj) {
-        const uint32_t cc = cw[jj] >> csh;
-        const uint32_t rr = (uint32_t)((((uint64_t)rw1[jj] << 32) | rw0[jj]) >> rsh);
-        const float c0 = (float)(cc & 3u), c1 = (float)((cc >> 2) & 3u);
-        const float s0 = (float)(rr & rmask), s1 = (float)((rr >> r) & rmask);
-        const float2 sc = scv[jj];
-        const float v0 = fmaf((s0 + 0.5f) * sub, sc.y, fmaf(c0, sc.y, sc.x));
-        const float v1 = fmaf((s1 + 0.5f) * sub, sc.y, fmaf(c1, sc.y, sc.x));
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          acc[h][0] = fmaf(wv[jj][h], v0, acc[h][0]);
-          acc[h][1] = fmaf(wv[jj][h], v1, acc[h][1]);
-        }
-      }
-    }
-    wave_barrier();
   }
+}
+
+// One batch of a special wavefront sw: tokens j0 .. j0 + cnt - 1 (cnt <=
+// kFTPW) of list lst (0: the level-1 selected tokens, all refined; 1: the
+// level-1 candidates, refined when the later levels selected them, else at
+// base precision) enter the wave's online softmax (natural units).  Lane
+// (tl, qd) takes quarter qd (elements 32 qd .. 32 qd + 31) of token tl: its K
+// refinement codes stay in registers for the logit, its V codes go through
+// LDS to the P.V, where the lane holds output elements 2 lane and 2 lane + 1.
+template <int G>
+__device__ inline void special_batch(const DecodeParams& p, FusedLds<G>& s, int sw, int lst, uint32_t j0, int cnt,
+                                     int kvh, int64_t row0, int nw, const float (&qsum)[G], float (&m_run)[G],
+                                     float (&l_run)[G], float (&acc)[G][2]) {
+  FSpec<G>& sp = s.u.st.h.sp;
+  const int lane = threadIdx.x & 63, tl = lane >> 2, qd = lane & 3;
+  const int r = p.r;
+  const float sub = __builtin_ldexpf(1.0f, -r);
+  const bool valid = tl < cnt;
+  const uint32_t* words = lst ? s.cand : s.sel;
+  const uint16_t* pre = lst ? s.pre2 : s.pre1;
+  int off = 0;
+  bool refined = false;
+  if (valid) {
+    // the word holding the j-th token of the list (the first w with
+    // pre[w + 1] > j; pre[nw] is the list's length), then its bit
+    const uint32_t j = j0 + (uint32_t)tl;
+    int lo_w = 0, hi_w = nw - 1;
+    while (lo_w < hi_w) {
+      const int mid = (lo_w + hi_w) >> 1;
+      if (pre[mid + 1] > j) hi_w = mid; else lo_w = mid + 1;
+    }
+    uint32_t bits = words[lo_w];
+    for (uint32_t k = pre[lo_w]; k < j; ++k) bits &= bits - 1u;
+    const int bit = __ffs(bits) - 1;
+    off = 32 * lo_w + bit;
+    refined = lst == 0 || ((s.csel[lo_w] >> bit) & 1u) != 0u;
+  }
+  uint32_t vb[2] = {0u, 0u}, kr[8], vr[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) kr[i] = vr[i] = 0u;
+  float2 vsc = make_float2(0.f, 0.f);
+  float kd = 0.f;
+  float lgt[G];
+  if (valid) {
+    const int64_t row = row0 + off;                       // kvh * cap + token
+    const uint32_t* srcv = reinterpret_cast<const uint32_t*>(p.vc + row * 32) + qd * 2;
+    vb[0] = srcv[0];
+    vb[1] = srcv[1];
+    vsc = reinterpret_cast<const float2*>(p.vs)[row];
+    if (refined) {
+      const int64_t tok = row - (int64_t)kvh * p.cap;
+      const uint32_t* rk =
+          reinterpret_cast<const uint32_t*>(p.ref_rows + ((int64_t)kvh * p.cap + tok) * p.rb) + qd * r;
+      const uint32_t* rv =
+          reinterpret_cast<const uint32_t*>(p.ref_rows + (((int64_t)p.hkv + kvh) * p.cap + tok) * p.rb) + qd * r;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        kr[i] = i < r ? rk[i] : 0u;
+        vr[i] = i < r ? rv[i] : 0u;
+      }
+      kd = reinterpret_cast<const float2*>(p.ks)[row].y;
+    }
+  }
+  // the V rows into the wave's staging (zeros for a token past cnt) first,
+  // so that only the K codes stay live through the logit
+  sp.vt[sw][tl][2 * qd] = vb[0];
+  sp.vt[sw][tl][2 * qd + 1] = vb[1];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (i < r) sp.vr[sw][tl][qd * r + i] = vr[i];
+  const bool lead = qd == 0;
+  if (lead) {
+    sp.vt[sw][tl][8] = 0u;
+    for (int i = 4 * r; i < 33; ++i) sp.vr[sw][tl][i] = 0u;
+    sp.vsc[sw][tl] = vsc;
+    sp.vfr[sw][tl] = refined ? make_float2(sub, 0.5f * sub) : make_float2(0.f, 0.5f);
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) lgt[h] = valid ? s.lg[off * G + h] : 0.f;
+  // logits: the quarter's q . s, summed over the token's four lanes
+  float ds[G];
+  switch (r) {
+    case 1: quarter_qs<1, G>(kr, &sp.qs[0][0], qd, ds); break;
+    case 2: quarter_qs<2, G>(kr, &sp.qs[0][0], qd, ds); break;
+    case 3: quarter_qs<3, G>(kr, &sp.qs[0][0], qd, ds); break;
+    case 4: quarter_qs<4, G>(kr, &sp.qs[0][0], qd, ds); break;
+    case 5: quarter_qs<5, G>(kr, &sp.qs[0][0], qd, ds); break;
+    case 6: quarter_qs<6, G>(kr, &sp.qs[0][0], qd, ds); break;
+    case 7: quarter_qs<7, G>(kr, &sp.qs[0][0], qd, ds); break;
+    default: quarter_qs<8, G>(kr, &sp.qs[0][0], qd, ds); break;
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    // refined - base = delta / sqrt(D) (2^-r q.s + (2^-r - 1) sum(q) / 2)
+    const float lr = refined ? fmaf(lgt[h], 0.6931471805599453f,
+                                    kd * kRsqrtD * fmaf(sub, quad_sum(ds[h]), 0.5f * (sub - 1.0f) * qsum[h]))
+                             : lgt[h] * 0.6931471805599453f;
+    const float mwv = wave_max_dpp(valid ? lr : -INFINITY);
+    const float mnew = fmaxf(m_run[h], mwv);
+    const float alpha = __expf(m_run[h] - mnew);
+    const float ew = valid ? __expf(lr - mnew) : 0.f;
+    if (lead) sp.wt[sw][h][tl] = ew;
+    l_run[h] = fmaf(l_run[h], alpha, wave_sum_dpp(lead ? ew : 0.f));
+    acc[h][0] *= alpha;
+    acc[h][1] *= alpha;
+    m_run[h] = mnew;
+  }
+  wave_barrier();
+  // P.V: the reads of four tokens, then their products
+  const int cpos = 4 * lane, cwi = cpos >> 5, csh = cpos & 31;
+  const int rpos = 2 * lane * r, rwi = rpos >> 5, rsh = rpos & 31;
+  const uint32_t rmask = (1u << r) - 1u;
+  constexpr int kPart = 4;
+#pragma unroll 1
+  for (int j1 = 0; j1 < kFTPW; j1 += kPart) {
+    uint32_t cwd[kPart], rw0[kPart], rw1[kPart];
+    float2 scv[kPart], frv[kPart];
+    float wv[kPart][G];
+#pragma unroll
+    for (int jj = 0; jj < kPart; ++jj) {
+      cwd[jj] = sp.vt[sw][j1 + jj][cwi];
+      rw0[jj] = sp.vr[sw][j1 + jj][rwi];
+      rw1[jj] = sp.vr[sw][j1 + jj][rwi + 1];
+      scv[jj] = sp.vsc[sw][j1 + jj];
+      frv[jj] = sp.vfr[sw][j1 + jj];
+#pragma unroll
+      for (int h = 0; h < G; ++h) wv[jj][h] = sp.wt[sw][h][j1 + jj];
+    }
+#pragma unroll
+    for (int jj = 0; jj < kPart; ++jj) {
+      const uint32_t cc = cwd[jj] >> csh;
+      const uint32_t rr = (uint32_t)((((uint64_t)rw1[jj] << 32) | rw0[jj]) >> rsh);
+      const float c0 = (float)(cc & 3u), c1 = (float)((cc >> 2) & 3u);
+      const float s0 = (float)(rr & rmask), s1 = (float)((rr >> r) & rmask);
+      const float2 sc = scv[jj], fr = frv[jj];
+      const float v0 = fmaf(fmaf(s0, fr.x, fr.y), sc.y, fmaf(c0, sc.y, sc.x));
+      const float v1 = fmaf(fmaf(s1, fr.x, fr.y), sc.y, fmaf(c1, sc.y, sc.x));
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        acc[h][0] = fmaf(wv[jj][h], v0, acc[h][0]);
+        acc[h][1] = fmaf(wv[jj][h], v1, acc[h][1]);
+      }
+    }
+  }
+  wave_barrier();
 }
 
 template <int G, bool Batched>
@@ -452,18 +603,16 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
   }
   __syncthreads();
 
-  // ---- B: the exact top-T of the head ----------------------------------------
+  // ---- B: level 1 of the exact top-T of the head ---------------------------
   uint32_t* hist = s.u.st.h.hist;
-  bool used2 = false, used3 = false;   // histogram levels taken (cleared at the end)
-  // the range's selection words: lane 0 of each wave writes the two words of
-  // the wave's 64 tokens per round
-  for (int w = tid; w < kFusedRmax / 32; w += 64 * kFW) s.sel[w] = s.cand[w] = 0u;
+  bool lvl2 = false;   // the level-1 boundary bin is split (the later levels run)
+  uint32_t need1 = 0u;
+  for (int w = tid; w < kFusedRmax / 32; w += 64 * kFW) s.sel[w] = s.cand[w] = s.csel[w] = 0u;
   __syncthreads();
   if (all) {
     for (int w = tid; w < nw; w += 64 * kFW) {
       const int rem = nsp - 32 * w;
-      const uint32_t m = rem >= 32 ? ~0u : (1u << rem) - 1u;
-      s.sel[w] = m;
+      s.sel[w] = rem >= 32 ? ~0u : (1u << rem) - 1u;
     }
   } else if (use_hist) {
     for (int i = tid; i < kHistBins; i += 64 * kFW) {
@@ -474,24 +623,18 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
     copy_dev_words(hist, &Z[kFZH1], kHistBins);
     __syncthreads();
     find_threshold_wave<kHistBins>(hist, (uint32_t)tn, &s.sh_bin, &s.sh_need);
-    const uint32_t b1 = (uint32_t)s.sh_bin, need1 = s.sh_need;
-    const bool lvl2 = hist[b1] != need1;       // the boundary bin is split
-    used2 = lvl2;
-    __syncthreads();
-    if (lvl2)
-      for (int i = tid; i < kHistBins; i += 64 * kFW) hist[i] = 0u;
-    __syncthreads();
-    // level 1: above b1 selected, in b1 candidates (all selected when b1 is
-    // taken whole), below b1 not selected; level-2 digits of the candidates
+    const uint32_t b1 = (uint32_t)s.sh_bin;
+    need1 = s.sh_need;
+    lvl2 = hist[b1] != need1;
+    // above b1 selected, in b1 candidates (all selected when b1 is taken
+    // whole), below b1 not selected
     for (int base = 0; base < nsp; base += 64 * kFW) {
       const int t = base + tid;
       bool above = false, in = false;
       if (t < nsp) {
-        const uint32_t key = token_key<G>(s.lg, t);
-        const uint32_t bin = key >> (32 - kHistBits);
+        const uint32_t bin = token_key<G>(s.lg, t) >> (32 - kHistBits);
         above = bin > b1;
         in = bin == b1;
-        if (in && lvl2) atomicAdd(&hist[(key >> 8) & 0xFFFu], 1u);
       }
       const uint64_t bs = __ballot(above || (in && !lvl2)), bc = __ballot(in && lvl2);
       if (lane == 0) {
@@ -504,105 +647,38 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
         }
       }
     }
-    __syncthreads();
-    if (lvl2) {
-      // ---- level 2: the next 12 key bits of the candidates
-      for (int i = tid; i < kHistBins; i += 64 * kFW) {
-        const uint32_t c = hist[i];
-        if (c) atomicAdd(&Z[kFZH2 + i], c);
-      }
-      if (!group_wait(s, &Z[kFZC + 1], nwg, p.fstatus)) return;
-      copy_dev_words(hist, &Z[kFZH2], kHistBins);
-      __syncthreads();
-      find_threshold_wave<kHistBins>(hist, need1, &s.sh_bin, &s.sh_need);
-      const uint32_t b2 = (uint32_t)s.sh_bin, need2 = s.sh_need;
-      const bool lvl3 = hist[b2] != need2;
-      used3 = lvl3;
-      __syncthreads();
-      if (lvl3 && tid < 256) hist[tid] = 0u;
-      __syncthreads();
-      if (tid < nw) {
-        uint32_t selw = s.sel[tid], next = 0u;
-        for (uint32_t bits = s.cand[tid]; bits; bits &= bits - 1u) {
-          const int bit = __ffs(bits) - 1;
-          const uint32_t key = token_key<G>(s.lg, 32 * tid + bit);
-          const uint32_t mid = (key >> 8) & 0xFFFu;
-          if (mid > b2 || (mid == b2 && !lvl3)) {
-            selw |= 1u << bit;
-          } else if (mid == b2) {
-            next |= 1u << bit;
-            atomicAdd(&hist[key & 0xFFu], 1u);
-          }
-        }
-        s.sel[tid] = selw;
-        s.cand[tid] = next;
-      }
-      __syncthreads();
-      if (lvl3) {
-        // ---- level 3: the last 8 key bits
-        if (tid < 256) {
-          const uint32_t c = hist[tid];
-          if (c) atomicAdd(&Z[kFZH3 + tid], c);
-        }
-        if (!group_wait(s, &Z[kFZC + 2], nwg, p.fstatus)) return;
-        copy_dev_words(hist, &Z[kFZH3], 256);
-        __syncthreads();
-        find_threshold_wave<256>(hist, need2, &s.sh_bin, &s.sh_need);
-        const uint32_t b3 = (uint32_t)s.sh_bin, need3 = s.sh_need;
-        const bool lvl4 = hist[b3] != need3;
-        __syncthreads();
-        uint32_t ties = 0u;
-        if (tid < nw) {
-          uint32_t selw = s.sel[tid];
-          for (uint32_t bits = s.cand[tid]; bits; bits &= bits - 1u) {
-            const int bit = __ffs(bits) - 1;
-            const uint32_t low = token_key<G>(s.lg, 32 * tid + bit) & 0xFFu;
-            if (low > b3 || (low == b3 && !lvl4))
-              selw |= 1u << bit;
-            else if (low == b3)
-              ties |= 1u << bit;
-          }
-          s.sel[tid] = selw;
-        }
-        if (lvl4) {
-          // ---- equal scores: the lower token index first
-          uint32_t mine_total;
-          const uint32_t rank0 = block_exclusive_scan<64 * kFW>((uint32_t)__popc(ties), s.scan, mine_total);
-          if (tid == 0) st_dev(&p.ftie[sk * p.ftie_stride + wi], mine_total);
-          if (!group_wait(s, &Z[kFZC + 3], nwg, p.fstatus)) return;
-          // ties in the head's ranges before this one
-          uint32_t before;
-          (void)block_exclusive_scan<64 * kFW>(tid < wi ? ld_dev(&p.ftie[sk * p.ftie_stride + tid]) : 0u, s.scan,
-                                               before);
-          const uint32_t take = need3 > before ? need3 - before : 0u;   // ties of this range still taken
-          if (tid < nw) {
-            uint32_t rank = rank0, selw = s.sel[tid];
-            for (uint32_t bits = ties; bits; bits &= bits - 1u, ++rank)
-              if (rank < take) selw |= 1u << (__ffs(bits) - 1);
-            s.sel[tid] = selw;
-          }
-        }
-        __syncthreads();
-      }
-    }
   }
-  if (select && p.fsel && tid < nw) st_dev(&p.bitmap[sk * p.bm_words + (lo >> 5) + tid], s.sel[tid]);
+  __syncthreads();
 
-  // ---- C: V once (kFVW wavefronts); the selected tokens beside it (kFSW) ----
+  // ---- C: V once (kFVW wavefronts) beside the selection's later levels and
+  // the selected tokens (kFSW) ---------------------------------------------
+  // the V stream takes every token that is neither selected nor a candidate
+  // at level 1; the two lists (selected, candidates) go to the special
+  // wavefronts in batches of kFTPW
   const bool masked = select && p.use_refine != 0;
-  __syncthreads();   // the ring and the histogram are free
-  FSpec<G>& sp = s.u.st.h.sp;
   if (masked) {
-    const uint32_t word = tid < nw ? s.sel[tid] : 0u;
+    const uint32_t v = tid < nw ? (uint32_t)__popc(s.sel[tid]) | ((uint32_t)__popc(s.cand[tid]) << 16) : 0u;
     uint32_t total;
-    const uint32_t pos = block_exclusive_scan<64 * kFW>((uint32_t)__popc(word), s.scan, total);
-    if (tid < nw) sp.pre[tid] = (uint16_t)pos;
-    if (tid == 0) {
-      sp.pre[nw] = (uint16_t)total;
-      s.sh_count = total;
+    const uint32_t pos = block_exclusive_scan<64 * kFW>(v, s.scan, total);   // two 16-bit counts (<= 4096 each)
+    if (tid < nw) {
+      s.pre1[tid] = (uint16_t)(pos & 0xFFFFu);
+      s.pre2[tid] = (uint16_t)(pos >> 16);
     }
+    if (tid == 0) {
+      s.pre1[nw] = (uint16_t)(total & 0xFFFFu);
+      s.pre2[nw] = (uint16_t)(total >> 16);
+      s.n1 = total & 0xFFFFu;
+      s.n2 = total >> 16;
+    }
+  } else if (tid == 0) {
+    s.n1 = s.n2 = 0u;
   }
-  for (int i = lane; i < 2 * G * 32; i += 64) (&s.wt[wid][0][0])[i] = (_Float16)0.f;
+  if (tid == 0) {
+    s.sel_done = lvl2 ? 0u : 1u;
+    s.used3 = 0u;
+  }
+  if (wid < kFVW)
+    for (int i = lane; i < 2 * G * 32; i += 64) (&s.wt[wid][0][0])[i] = (_Float16)0.f;
   if (tid < 8) s.wzero[tid] = (_Float16)0.f;
   __syncthreads();
   const int t = lane & 15, hl = lane >> 4;        // logit layout: token t (and 16 + t), head hl
@@ -629,9 +705,9 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
 #pragma unroll
     for (int k = 0; k < kFRingV - 1; ++k)
       if (k < nv) issueV(k, ring[k]);
-    // the selection words of the range: lane L holds words L and 64 + L
-    const uint32_t sw0 = masked && lane < nw ? s.sel[lane] : 0u;
-    const uint32_t sw1 = masked && 64 + lane < nw ? s.sel[64 + lane] : 0u;
+    // the tokens the special wavefronts take: lane L holds words L and 64 + L
+    const uint32_t sw0 = masked && lane < nw ? s.sel[lane] | s.cand[lane] : 0u;
+    const uint32_t sw1 = masked && 64 + lane < nw ? s.sel[64 + lane] | s.cand[64 + lane] : 0u;
     const int hlc = hl < G ? hl : 0;
     const uint32_t hsel = 2u * (uint32_t)(n & 1);
     const uint32_t psel = hsel | ((hsel + 1u) << 8) | ((hsel + 4u) << 16) | ((hsel + 5u) << 24);
@@ -771,14 +847,48 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
     mx = m == kFloor ? -INFINITY : m;
     ls = lsum;
   } else {
+    const int sw = wid - kFVW;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      msn[h] = -1e30f;
+      lsn[h] = 0.f;
+      accs[h][0] = accs[h][1] = 0.f;
+    }
+    if (sw == 0) {
+      // the selector: the candidates settled, the range's selection words to
+      // device memory when asked, then the candidates' list opened
+      if (lvl2) select_candidates<G>(p, s, Z, nw, nwg, need1, sk, wi);
+      if (select && p.fsel)
+        for (int w = lane; w < nw; w += 64) st_dev(&p.bitmap[sk * p.bm_words + (lo >> 5) + w], s.sel[w] | s.csel[w]);
+      if (lvl2) __hip_atomic_store(&s.sel_done, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
     if (masked) {
-      special_wave<G>(p, s, wid - kFVW, seq, kvh, t0, nw, s.sh_count, msn, lsn, accs);
-    } else {
+      // every special wavefront writes the whole query (the same values): it
+      // then reads only what it wrote itself
+      float qsum[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        msn[h] = -1e30f;
-        lsn[h] = 0.f;
-        accs[h][0] = accs[h][1] = 0.f;
+        const float* qh = p.q + ((int64_t)seq * p.hq + kvh * G + h) * kHeadDim;
+        const float q0 = qh[lane], q1 = qh[64 + lane];
+        s.u.st.h.sp.qs[h][lane] = q0;
+        s.u.st.h.sp.qs[h][64 + lane] = q1;
+        qsum[h] = wave_sum_dpp(q0 + q1);
+      }
+      wave_barrier();
+      // batches round-robin, fixed for the head (so that the sums do not
+      // depend on timing): the selected list over the wavefronts other than
+      // the selector while the later levels run, the candidates over all
+      for (int lst = 0; lst < 2; ++lst) {
+        if (lst == 1)
+          while (__hip_atomic_load(&s.sel_done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0u)
+            __builtin_amdgcn_s_sleep(2);
+        const uint32_t len = lst ? s.n2 : s.n1;
+        const int nwk = lst == 0 && lvl2 ? kFSW - 1 : kFSW;
+        const int me = lst == 0 && lvl2 ? sw - 1 : sw;
+        if (me < 0) continue;
+        for (uint32_t j0 = (uint32_t)(kFTPW * me); j0 < len; j0 += (uint32_t)(kFTPW * nwk))
+          special_batch<G>(p, s, sw, lst, j0, (int)min((uint32_t)kFTPW, len - j0), kvh, t0, nw, qsum, msn, lsn,
+                           accs);
       }
     }
   }
@@ -908,9 +1018,9 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
   // taken: every work-group of the head took the same)
   for (int i = tid; i < kHistBins; i += 64 * kFW) {
     if (use_hist) st_dev(&Z[kFZH1 + i], 0u);
-    if (used2) st_dev(&Z[kFZH2 + i], 0u);
+    if (lvl2) st_dev(&Z[kFZH2 + i], 0u);
   }
-  if (used3 && tid < 256) st_dev(&Z[kFZH3 + tid], 0u);
+  if (s.used3 && tid < 256) st_dev(&Z[kFZH3 + tid], 0u);
   if (tid < 16) st_dev(&Z[kFZC + tid], 0u);
 }
 
