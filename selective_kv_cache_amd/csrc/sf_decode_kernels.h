@@ -314,10 +314,16 @@ constexpr int32_t kSelBlkTokMin = 16;  // or 4 wavefronts x 4 tokens when those 
 constexpr int kAttendWaves = 4;         // wavefronts per attention work-group (matrix-core path)
 constexpr int kCombineMax = 2048;      // partials per (sequence, query head)
 
-// Single-launch path: per (sequence, KV head) zero region of the level-1,
-// level-2 and level-3 histograms and the counters (barrier arrivals, done).
+// Single-launch path: per (sequence, KV head) region of the level-1,
+// level-2 and level-3 histograms and the counters (barrier arrivals, done),
+// zero between steps, then the level-1 candidates' list (a slot of keys and
+// one of token indices per work-group, and each work-group's count; not
+// cleared).
+constexpr int kFListMax = 4096;         // list entries of a head (slots of kFListMax / ranges each)
+constexpr int kFListRanges = 64;        // work-groups per head the list serves at most
 constexpr int kFZH1 = 0, kFZH2 = kHistBins, kFZH3 = 2 * kHistBins, kFZC = 2 * kHistBins + 256;
-constexpr int kFZWords = kFZC + 16;
+constexpr int kFZL = kFZC + 16;         // keys; tokens at kFZL + kFListMax; counts at kFZL + 2 kFListMax
+constexpr int kFZWords = kFZL + 2 * kFListMax + kFListRanges;
 constexpr int kFusedRmax = 4096;        // tokens per work-group at most
 constexpr int kFusedMinR = 256;         // and at least (a multiple of it)
 constexpr int kFusedMaxRanges = 512;    // work-groups per (sequence, KV head) at most

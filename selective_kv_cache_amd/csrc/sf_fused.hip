@@ -20,17 +20,20 @@
 //   B  wait for the head's other work-groups (a counter in device memory),
 //      find the boundary bin of the exact top-T from the global histogram:
 //      tokens above it are selected, tokens below it are not, tokens in it
-//      are candidates; levels 2 and 3 (the next 12 and the last 8 key bits)
-//      and, for exactly equal scores, the lower token index settle the
-//      candidates the same way, each level one more wait, taken only when
-//      the level above leaves the boundary bin split;
-//   C  stream the range's V codes once: every token that is neither selected
-//      nor a candidate of level 1 enters the online softmax at base precision
-//      (logits from LDS, P.V on the matrix cores as in the two-pass form);
-//   D  the selected tokens (refined logit and value from their refinement
-//      rows) and the level-1 candidates not selected (base precision) of the
-//      range are added on the vector units; the range's partial (m, l,
-//      acc[D]) per query head goes to device memory;
+//      are candidates (all selected when the bin is taken whole);
+//   B' candidates: every work-group writes their keys and token indices to
+//      its slot of the head's list in device memory; after one more wait
+//      each reads the whole list and takes the exact boundary key by a radix
+//      select in LDS, ties to the lower token index (when a range overflows
+//      its slot, the next 12 and the last 8 key bits settle them through
+//      histograms in device memory, one wait per level);
+//   C  12 wavefronts stream the range's V codes once: every token that is
+//      not selected enters the online softmax at base precision (logits
+//      from LDS, P.V on the matrix cores as in the two-pass form); beside
+//      them 4 wavefronts take the selected tokens in batches of 16 (refined
+//      logit and value from their refinement rows, on the vector units);
+//   D  the wavefronts' partials merge into the range's partial (m, l,
+//      acc[D]) per query head, written to device memory;
 //   E  the last work-group of the head to finish merges the partials into
 //      the output, lists the selection when asked, and clears the head's
 //      histograms and counters for the next step.
@@ -42,21 +45,22 @@
 // work-group hands to another is written with device-scope stores or
 // atomics (they bypass the non-coherent L2), each wavefront waits for its
 // stores before the work-group arrives at a counter, and readers use
-// device-scope loads after an acquire.  Waits are bounded: a wait that
-// expires (the work-groups were not all resident) sets the status word
-// (sf_decode_check reports it) and ends the work-group.
+// device-scope loads (which miss the L2) once the counter is complete.
+// Waits are bounded: a wait that expires (the work-groups were not all
+// resident) sets the status word (sf_decode_check reports it) and ends the
+// work-group.
 #include "sf_mfma_common.h"
 
 namespace sfk {
 
 constexpr int kFW = 16;          // wavefronts per work-group
 constexpr int kFVW = 12;         // of them streaming V in phase C,
-constexpr int kFSW = kFW - kFVW; // and taking the selected tokens beside them
+constexpr int kFSW = kFW - kFVW; // and refining the selected tokens beside them
 constexpr int kFRing = 3;        // phase A: ring stages per wavefront (2 chunks in flight)
 constexpr int kFRingV = kFW * kFRing / kFVW;   // phase C: 4 stages per streaming wavefront
-constexpr int kFTPW = 16;        // tokens per batch of a special wavefront (4 lanes each)
-constexpr int kFSpinLimit = 1 << 18;   // bounded waits: about 0.2 s
+constexpr int kFTPW = 16;        // selected tokens per batch of a refining wavefront (4 lanes each)
 static_assert(kFRingV * kFVW == kFW * kFRing, "phase C's ring is phase A's");
+constexpr int kFSpinLimit = 1 << 18;   // bounded waits: about 0.2 s
 static_assert(2 * kFusedMaxRanges + kHeadDim <= kFW * kHeadDim, "merge arrays fit in the wave partials");
 
 struct FStage {
@@ -65,12 +69,10 @@ struct FStage {
 };
 
 template <int G>
-struct FSpec {                   // the special wavefronts' staging (in the histogram's place)
-  float qs[G][kHeadDim];
+struct FSpec {                   // the refining wavefronts' staging (in the histogram's place)
   uint32_t vt[kFSW][kFTPW][9];   // V base codes (2 bits: 8 words + a zero word)
-  uint32_t vr[kFSW][kFTPW][33];  // V refinement rows (r <= 8: 32 words + a zero word; zero at base precision)
+  uint32_t vr[kFSW][kFTPW][33];  // V refinement rows (r <= 8: 32 words + a zero word)
   float2 vsc[kFSW][kFTPW];       // V (lo, delta)
-  float2 vfr[kFSW][kFTPW];       // value = lo + delta (c + s x + y): (x, y) = (2^-r, 2^-r / 2), or (0, 1/2)
   float wt[kFSW][G][kFTPW];
 };
 
@@ -82,26 +84,28 @@ struct FusedLds {
       FStage ring[kFW * kFRing];             // A: [wave][kFRing]; C: [streaming wave][kFRingV]
       union {
         uint32_t hist[kHistBins];            // level 1 of the selection
-        FSpec<G> sp;                         // phase C
+        FSpec<G> sp;                         // C: the selected tokens' staging
       } h;
     } st;
-    float acc[kFW][G][kHeadDim];             // per-wave partials: P.V of the wave's tokens
+    float acc[kFW][G][kHeadDim];             // per-wave partials (after C)
   } u;
+  float qs[G][kHeadDim];                     // the query (C)
   QPrep qp;
-  alignas(16) _Float16 wt[kFVW][2 * G][32];  // P.V weights of the streaming waves: hi parts, then lo parts
+  alignas(16) _Float16 wt[kFW][2 * G][32];   // P.V weights of the stream: hi parts, then lo parts
   alignas(16) _Float16 wzero[8];
-  uint32_t sel[kFusedRmax / 32];             // selected at level 1 (above the boundary bin, or the whole bin)
+  uint32_t sel[kFusedRmax / 32];             // selected (at level 1, then settled by the later levels)
   uint32_t cand[kFusedRmax / 32];            // in the level-1 boundary bin, left to the later levels
-  uint32_t csel[kFusedRmax / 32];            // candidates the later levels selected
+  uint32_t csel[kFusedRmax / 32];            // candidates the histogram levels selected
   uint16_t pre1[kFusedRmax / 32 + 1];        // selected tokens before each word
-  uint16_t pre2[kFusedRmax / 32 + 1];        // candidates before each word
+  uint32_t lcnt[kFListRanges];               // candidates of each range of the head
   float mw[kFW][G], lw[kFW][G];              // per-wave partials: maxima (log2 units), sums
   float mstar[G];
   uint32_t scan[kFW];
   int sh_bin;
   uint32_t sh_need, sh_flag;
-  uint32_t n1, n2;                           // lengths of the two lists
-  uint32_t sel_done, used3;                  // candidates settled; level 3 taken
+  uint32_t shist[256];                       // radix histogram of the candidates' keys
+  uint32_t sh_cnt, n1;                       // boundary key's count; selected tokens of the range
+  uint32_t used3;                            // level 3 taken
 };
 
 __device__ inline uint32_t ld_dev(const uint32_t* p) {
@@ -194,8 +198,9 @@ __device__ inline void read_vstage(uint32_t aL0, uint32_t aL1, uint32_t aS, cons
 }
 
 // Arrive at `ctr` and wait until `expected` work-groups have, for one
-// wavefront alone (the selector of phase C): its device-scope stores and
-// atomics complete first.  Returns false (status word set) when the wait
+// wavefront alone (wavefront 0 in the histogram levels, the others wait at
+// the work-group's barrier): its device-scope stores and atomics complete
+// first.  Returns false (status word set) when the wait
 // expired.
 __device__ inline bool wave_group_wait(uint32_t* ctr, uint32_t expected, uint32_t* status) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -249,90 +254,101 @@ __device__ inline void find_threshold_dev(const uint32_t* hist, uint32_t need, i
   need_out = need - above - __builtin_amdgcn_readlane(cum - c, j);
 }
 
-// Levels 2 and 3 of the selection and the index ties, by one wavefront (the
-// selector), while the other wavefronts stream V: the level-1 candidates of
-// the range (s.cand) are settled into s.csel.  Level 2 histograms the next
-// 12 key bits of the head's candidates, level 3 the last 8 bits of those in
-// the level-2 boundary bin, straight into the head's histograms in device
-// memory (a range holds few candidates); exactly equal scores go to the
-// lower token index.  Each level is one more wait, taken only when the level
-// above leaves its boundary bin split (the same for every work-group of the
-// head).  Lane l holds words l and 64 + l.
-template <int G>
-__device__ inline void select_candidates(const DecodeParams& p, FusedLds<G>& s, uint32_t* Z, int nw, uint32_t nwg,
-                                         uint32_t need1, int64_t sk, int wi) {
+// Boundary bin of an LDS histogram of NB bins (16 or 256) by one
+// wavefront, from the top bin down: the bin d with count(bins > d) < need <=
+// count(bins >= d), count(bins > d) and d's count (uniform).
+template <int NB>
+__device__ inline void wave_boundary(const uint32_t* h, uint32_t need, int& d, uint32_t& above, uint32_t& cnt) {
+  constexpr int PER = NB >= 64 ? NB / 64 : 1, LANES = NB / PER;
   const int lane = threadIdx.x & 63;
-  uint32_t cw[2], selw[2] = {0u, 0u}, next[2] = {0u, 0u};
+  uint32_t v[PER], sum = 0u;
 #pragma unroll
-  for (int k = 0; k < 2; ++k) cw[k] = 64 * k + lane < nw ? s.cand[64 * k + lane] : 0u;
+  for (int i = 0; i < PER; ++i) {
+    v[i] = lane < LANES ? h[NB - PER * (lane + 1) + i] : 0u;
+    sum += v[i];
+  }
+  const uint32_t inc = wave_inclusive_scan(sum);
+  const uint64_t hit = __ballot(inc - sum < need && need <= inc);
+  const int L = __builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)hit) - 1);
+  uint32_t cum = __builtin_amdgcn_readlane(inc - sum, L);
+  d = -1;
+  above = cnt = 0u;
+#pragma unroll
+  for (int i = PER - 1; i >= 0; --i) {
+    const uint32_t b = __builtin_amdgcn_readlane(v[i], L);
+    if (d < 0 && cum + b >= need) {
+      d = NB - PER * (L + 1) + i;
+      above = cum;
+      cnt = b;
+    }
+    cum += b;
+  }
+}
+
+// Levels 2 and 3 of the selection and the index ties through the head's
+// histograms in device memory, by wavefront 0: the fallback when a range
+// has more level-1 candidates than its slot of the list.  The level-2
+// histogram is complete (every work-group added its candidates before the
+// wait at Z[kFZC + 1]).
+template <int G>
+__device__ inline void select_by_histograms(const DecodeParams& p, FusedLds<G>& s, uint32_t* Z, const uint32_t (&cw)[2],
+                                            uint32_t (&selw)[2], uint32_t nwg, uint32_t need1, int64_t sk, int wi) {
+  const int lane = threadIdx.x & 63;
+  uint32_t next[2] = {0u, 0u};
+  int b2;
+  uint32_t need2, cnt2;
+  find_threshold_dev<kHistBins>(&Z[kFZH2], need1, b2, need2, cnt2);
+  const bool lvl3 = cnt2 != need2;
 #pragma unroll
   for (int k = 0; k < 2; ++k)
     for (uint32_t bits = cw[k]; bits; bits &= bits - 1u) {
-      const int t = 32 * (64 * k + lane) + __ffs(bits) - 1;
-      atomicAdd(&Z[kFZH2 + ((token_key<G>(s.lg, t) >> 8) & 0xFFFu)], 1u);
-    }
-  if (wave_group_wait(&Z[kFZC + 1], nwg, p.fstatus)) {
-    int b2;
-    uint32_t need2, cnt2;
-    find_threshold_dev<kHistBins>(&Z[kFZH2], need1, b2, need2, cnt2);
-    const bool lvl3 = cnt2 != need2;
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
-      for (uint32_t bits = cw[k]; bits; bits &= bits - 1u) {
-        const int bit = __ffs(bits) - 1;
-        const uint32_t key = token_key<G>(s.lg, 32 * (64 * k + lane) + bit);
-        const int mid = (int)((key >> 8) & 0xFFFu);
-        if (mid > b2 || (mid == b2 && !lvl3)) {
-          selw[k] |= 1u << bit;
-        } else if (mid == b2) {
-          next[k] |= 1u << bit;
-          atomicAdd(&Z[kFZH3 + (key & 0xFFu)], 1u);
-        }
-      }
-    if (lvl3) {
-      if (lane == 0) s.used3 = 1u;
-      if (wave_group_wait(&Z[kFZC + 2], nwg, p.fstatus)) {
-        int b3;
-        uint32_t need3, cnt3;
-        find_threshold_dev<256>(&Z[kFZH3], need2, b3, need3, cnt3);
-        const bool lvl4 = cnt3 != need3;
-        uint32_t ties[2] = {0u, 0u};
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-          for (uint32_t bits = next[k]; bits; bits &= bits - 1u) {
-            const int bit = __ffs(bits) - 1;
-            const int low = (int)(token_key<G>(s.lg, 32 * (64 * k + lane) + bit) & 0xFFu);
-            if (low > b3 || (low == b3 && !lvl4))
-              selw[k] |= 1u << bit;
-            else if (low == b3)
-              ties[k] |= 1u << bit;
-          }
-        if (lvl4) {
-          // rank of each tie in the range (words in token order: lane, then
-          // 64 + lane), the range's count to the head, then the ties of the
-          // head's ranges before this one
-          const uint32_t c0 = (uint32_t)__popc(ties[0]), c1 = (uint32_t)__popc(ties[1]);
-          const uint32_t i0 = wave_inclusive_scan(c0), i1 = wave_inclusive_scan(c1);
-          const uint32_t t0 = __builtin_amdgcn_readlane(i0, 63);
-          uint32_t rank[2] = {i0 - c0, t0 + i1 - c1};
-          if (lane == 0) st_dev(&p.ftie[sk * p.ftie_stride + wi], t0 + __builtin_amdgcn_readlane(i1, 63));
-          if (wave_group_wait(&Z[kFZC + 3], nwg, p.fstatus)) {
-            uint32_t before = 0u;
-            for (int w = lane; w < wi; w += 64) before += ld_dev(&p.ftie[sk * p.ftie_stride + w]);
-            before = __builtin_amdgcn_readlane(wave_inclusive_scan(before), 63);
-            const uint32_t take = need3 > before ? need3 - before : 0u;   // ties of this range still taken
-#pragma unroll
-            for (int k = 0; k < 2; ++k)
-              for (uint32_t bits = ties[k]; bits; bits &= bits - 1u, ++rank[k])
-                if (rank[k] < take) selw[k] |= 1u << (__ffs(bits) - 1);
-          }
-        }
+      const int bit = __ffs(bits) - 1;
+      const uint32_t key = token_key<G>(s.lg, 32 * (64 * k + lane) + bit);
+      const int mid = (int)((key >> 8) & 0xFFFu);
+      if (mid > b2 || (mid == b2 && !lvl3)) {
+        selw[k] |= 1u << bit;
+      } else if (mid == b2) {
+        next[k] |= 1u << bit;
+        atomicAdd(&Z[kFZH3 + (key & 0xFFu)], 1u);
       }
     }
-  }
+  if (!lvl3) return;
+  if (lane == 0) s.used3 = 1u;
+  if (!wave_group_wait(&Z[kFZC + 2], nwg, p.fstatus)) return;
+  int b3;
+  uint32_t need3, cnt3;
+  find_threshold_dev<256>(&Z[kFZH3], need2, b3, need3, cnt3);
+  const bool lvl4 = cnt3 != need3;
+  uint32_t ties[2] = {0u, 0u};
 #pragma unroll
   for (int k = 0; k < 2; ++k)
-    if (64 * k + lane < nw) s.csel[64 * k + lane] = selw[k];
+    for (uint32_t bits = next[k]; bits; bits &= bits - 1u) {
+      const int bit = __ffs(bits) - 1;
+      const int low = (int)(token_key<G>(s.lg, 32 * (64 * k + lane) + bit) & 0xFFu);
+      if (low > b3 || (low == b3 && !lvl4))
+        selw[k] |= 1u << bit;
+      else if (low == b3)
+        ties[k] |= 1u << bit;
+    }
+  if (!lvl4) return;
+  // rank of each tie in the range (words in token order: lane, then 64 +
+  // lane), the range's count to the head, then the ties of the head's
+  // ranges before this one
+  const uint32_t c0 = (uint32_t)__popc(ties[0]), c1 = (uint32_t)__popc(ties[1]);
+  const uint32_t i0 = wave_inclusive_scan(c0), i1 = wave_inclusive_scan(c1);
+  const uint32_t t0 = __builtin_amdgcn_readlane(i0, 63);
+  const uint32_t mine = t0 + __builtin_amdgcn_readlane(i1, 63);
+  uint32_t rank[2] = {i0 - c0, t0 + i1 - c1};
+  if (lane == 0) st_dev(&p.ftie[sk * p.ftie_stride + wi], mine);
+  if (!wave_group_wait(&Z[kFZC + 3], nwg, p.fstatus)) return;
+  uint32_t before = 0u;
+  for (int w = lane; w < wi; w += 64) before += ld_dev(&p.ftie[sk * p.ftie_stride + w]);
+  before = __builtin_amdgcn_readlane(wave_inclusive_scan(before), 63);
+  const uint32_t take = need3 > before ? need3 - before : 0u;   // ties of this range still taken
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    for (uint32_t bits = ties[k]; bits; bits &= bits - 1u, ++rank[k])
+      if (rank[k] < take) selw[k] |= 1u << (__ffs(bits) - 1);
 }
 
 // q . s over quarter qd of head_dim for each of the G heads, from the lane's
@@ -357,131 +373,135 @@ __device__ inline void quarter_qs(const uint32_t (&kr)[8], const float* qs, int 
   }
 }
 
-// One batch of a special wavefront sw: tokens j0 .. j0 + cnt - 1 (cnt <=
-// kFTPW) of list lst (0: the level-1 selected tokens, all refined; 1: the
-// level-1 candidates, refined when the later levels selected them, else at
-// base precision) enter the wave's online softmax (natural units).  Lane
-// (tl, qd) takes quarter qd (elements 32 qd .. 32 qd + 31) of token tl: its K
-// refinement codes stay in registers for the logit, its V codes go through
-// LDS to the P.V, where the lane holds output elements 2 lane and 2 lane + 1.
+// Rows of a batch of selected tokens held in registers between their fetch
+// and their use: lane (tl, qd) holds quarter qd (elements 32 qd .. 32 qd +
+// 31) of token tl.
+struct SelRows {
+  uint32_t vb[2], kr[8], vr[8];   // V base codes, K and V refinement codes (r words each)
+  float2 vsc;                     // V (lo, delta)
+  float kd;                       // K delta
+  int off;                        // the token within the range
+};
+
+// Fetch the rows of the range's selected tokens j0 .. j0 + cnt - 1 (cnt <=
+// kFTPW, in token order).
 template <int G>
-__device__ inline void special_batch(const DecodeParams& p, FusedLds<G>& s, int sw, int lst, uint32_t j0, int cnt,
-                                     int kvh, int64_t row0, int nw, const float (&qsum)[G], float (&m_run)[G],
-                                     float (&l_run)[G], float (&acc)[G][2]) {
+__device__ inline void sel_fetch(const DecodeParams& p, const FusedLds<G>& s, uint32_t j0, int cnt, int kvh,
+                                 int64_t row0, int nw, SelRows& rw) {
+  const int lane = threadIdx.x & 63, tl = lane >> 2, qd = lane & 3;
+  const int r = p.r;
+  rw.vb[0] = rw.vb[1] = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) rw.kr[i] = rw.vr[i] = 0u;
+  rw.vsc = make_float2(0.f, 0.f);
+  rw.kd = 0.f;
+  rw.off = 0;
+  if (tl >= cnt) return;
+  // the word holding the j-th selected token (the first w with pre1[w + 1] >
+  // j; pre1[nw] is the count), then its bit
+  const uint32_t j = j0 + (uint32_t)tl;
+  int lo_w = 0, hi_w = nw - 1;
+  while (lo_w < hi_w) {
+    const int mid = (lo_w + hi_w) >> 1;
+    if (s.pre1[mid + 1] > j) hi_w = mid; else lo_w = mid + 1;
+  }
+  uint32_t bits = s.sel[lo_w];
+  for (uint32_t k = s.pre1[lo_w]; k < j; ++k) bits &= bits - 1u;
+  rw.off = 32 * lo_w + __ffs(bits) - 1;
+  const int64_t row = row0 + rw.off;                     // kvh * cap + token
+  const int64_t tok = row - (int64_t)kvh * p.cap;
+  const uint32_t* srcv = reinterpret_cast<const uint32_t*>(p.vc + row * 32) + qd * 2;
+  rw.vb[0] = srcv[0];
+  rw.vb[1] = srcv[1];
+  rw.vsc = reinterpret_cast<const float2*>(p.vs)[row];
+  const uint32_t* rk = reinterpret_cast<const uint32_t*>(p.ref_rows + ((int64_t)kvh * p.cap + tok) * p.rb) + qd * r;
+  const uint32_t* rv =
+      reinterpret_cast<const uint32_t*>(p.ref_rows + (((int64_t)p.hkv + kvh) * p.cap + tok) * p.rb) + qd * r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    rw.kr[i] = i < r ? rk[i] : 0u;
+    rw.vr[i] = i < r ? rv[i] : 0u;
+  }
+  rw.kd = reinterpret_cast<const float2*>(p.ks)[row].y;
+}
+
+// A fetched batch of cnt selected tokens enters refining wavefront w's online softmax
+// (natural units) with refined keys and values: the refined logit from the
+// base logit in LDS plus the refinement's change, the quarter dots summed
+// over the token's four lanes; the V rows through the wave's staging to the
+// P.V, where the lane holds output elements 2 lane and 2 lane + 1.
+template <int G>
+__device__ inline void sel_compute(const DecodeParams& p, FusedLds<G>& s, int w, const SelRows& rw, int cnt,
+                                   const float (&qsum)[G], float (&m_run)[G], float (&l_run)[G],
+                                   float (&acc)[G][2]) {
+  static_assert(kFTPW * 4 == 64, "four lanes a token");
   FSpec<G>& sp = s.u.st.h.sp;
   const int lane = threadIdx.x & 63, tl = lane >> 2, qd = lane & 3;
   const int r = p.r;
   const float sub = __builtin_ldexpf(1.0f, -r);
   const bool valid = tl < cnt;
-  const uint32_t* words = lst ? s.cand : s.sel;
-  const uint16_t* pre = lst ? s.pre2 : s.pre1;
-  int off = 0;
-  bool refined = false;
-  if (valid) {
-    // the word holding the j-th token of the list (the first w with
-    // pre[w + 1] > j; pre[nw] is the list's length), then its bit
-    const uint32_t j = j0 + (uint32_t)tl;
-    int lo_w = 0, hi_w = nw - 1;
-    while (lo_w < hi_w) {
-      const int mid = (lo_w + hi_w) >> 1;
-      if (pre[mid + 1] > j) hi_w = mid; else lo_w = mid + 1;
-    }
-    uint32_t bits = words[lo_w];
-    for (uint32_t k = pre[lo_w]; k < j; ++k) bits &= bits - 1u;
-    const int bit = __ffs(bits) - 1;
-    off = 32 * lo_w + bit;
-    refined = lst == 0 || ((s.csel[lo_w] >> bit) & 1u) != 0u;
-  }
-  uint32_t vb[2] = {0u, 0u}, kr[8], vr[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) kr[i] = vr[i] = 0u;
-  float2 vsc = make_float2(0.f, 0.f);
-  float kd = 0.f;
-  float lgt[G];
-  if (valid) {
-    const int64_t row = row0 + off;                       // kvh * cap + token
-    const uint32_t* srcv = reinterpret_cast<const uint32_t*>(p.vc + row * 32) + qd * 2;
-    vb[0] = srcv[0];
-    vb[1] = srcv[1];
-    vsc = reinterpret_cast<const float2*>(p.vs)[row];
-    if (refined) {
-      const int64_t tok = row - (int64_t)kvh * p.cap;
-      const uint32_t* rk =
-          reinterpret_cast<const uint32_t*>(p.ref_rows + ((int64_t)kvh * p.cap + tok) * p.rb) + qd * r;
-      const uint32_t* rv =
-          reinterpret_cast<const uint32_t*>(p.ref_rows + (((int64_t)p.hkv + kvh) * p.cap + tok) * p.rb) + qd * r;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        kr[i] = i < r ? rk[i] : 0u;
-        vr[i] = i < r ? rv[i] : 0u;
-      }
-      kd = reinterpret_cast<const float2*>(p.ks)[row].y;
-    }
-  }
-  // the V rows into the wave's staging (zeros for a token past cnt) first,
-  // so that only the K codes stay live through the logit
-  sp.vt[sw][tl][2 * qd] = vb[0];
-  sp.vt[sw][tl][2 * qd + 1] = vb[1];
+  // the V rows into the wave's staging first (zeros for a token past cnt)
+  sp.vt[w][tl][2 * qd] = rw.vb[0];
+  sp.vt[w][tl][2 * qd + 1] = rw.vb[1];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    if (i < r) sp.vr[sw][tl][qd * r + i] = vr[i];
+    if (i < r) sp.vr[w][tl][qd * r + i] = rw.vr[i];
   const bool lead = qd == 0;
   if (lead) {
-    sp.vt[sw][tl][8] = 0u;
-    for (int i = 4 * r; i < 33; ++i) sp.vr[sw][tl][i] = 0u;
-    sp.vsc[sw][tl] = vsc;
-    sp.vfr[sw][tl] = refined ? make_float2(sub, 0.5f * sub) : make_float2(0.f, 0.5f);
+    sp.vt[w][tl][8] = 0u;
+    for (int i = 4 * r; i < 33; ++i) sp.vr[w][tl][i] = 0u;
+    sp.vsc[w][tl] = rw.vsc;
   }
+  float lgt[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) lgt[h] = valid ? s.lg[off * G + h] : 0.f;
-  // logits: the quarter's q . s, summed over the token's four lanes
+  for (int h = 0; h < G; ++h) lgt[h] = valid ? s.lg[rw.off * G + h] : 0.f;
   float ds[G];
   switch (r) {
-    case 1: quarter_qs<1, G>(kr, &sp.qs[0][0], qd, ds); break;
-    case 2: quarter_qs<2, G>(kr, &sp.qs[0][0], qd, ds); break;
-    case 3: quarter_qs<3, G>(kr, &sp.qs[0][0], qd, ds); break;
-    case 4: quarter_qs<4, G>(kr, &sp.qs[0][0], qd, ds); break;
-    case 5: quarter_qs<5, G>(kr, &sp.qs[0][0], qd, ds); break;
-    case 6: quarter_qs<6, G>(kr, &sp.qs[0][0], qd, ds); break;
-    case 7: quarter_qs<7, G>(kr, &sp.qs[0][0], qd, ds); break;
-    default: quarter_qs<8, G>(kr, &sp.qs[0][0], qd, ds); break;
+    case 1: quarter_qs<1, G>(rw.kr, &s.qs[0][0], qd, ds); break;
+    case 2: quarter_qs<2, G>(rw.kr, &s.qs[0][0], qd, ds); break;
+    case 3: quarter_qs<3, G>(rw.kr, &s.qs[0][0], qd, ds); break;
+    case 4: quarter_qs<4, G>(rw.kr, &s.qs[0][0], qd, ds); break;
+    case 5: quarter_qs<5, G>(rw.kr, &s.qs[0][0], qd, ds); break;
+    case 6: quarter_qs<6, G>(rw.kr, &s.qs[0][0], qd, ds); break;
+    case 7: quarter_qs<7, G>(rw.kr, &s.qs[0][0], qd, ds); break;
+    default: quarter_qs<8, G>(rw.kr, &s.qs[0][0], qd, ds); break;
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     // refined - base = delta / sqrt(D) (2^-r q.s + (2^-r - 1) sum(q) / 2)
-    const float lr = refined ? fmaf(lgt[h], 0.6931471805599453f,
-                                    kd * kRsqrtD * fmaf(sub, quad_sum(ds[h]), 0.5f * (sub - 1.0f) * qsum[h]))
-                             : lgt[h] * 0.6931471805599453f;
+    const float lr =
+        fmaf(lgt[h], 0.6931471805599453f, rw.kd * kRsqrtD * fmaf(sub, quad_sum(ds[h]), 0.5f * (sub - 1.0f) * qsum[h]));
     const float mwv = wave_max_dpp(valid ? lr : -INFINITY);
     const float mnew = fmaxf(m_run[h], mwv);
     const float alpha = __expf(m_run[h] - mnew);
     const float ew = valid ? __expf(lr - mnew) : 0.f;
-    if (lead) sp.wt[sw][h][tl] = ew;
+    if (lead) sp.wt[w][h][tl] = ew;
     l_run[h] = fmaf(l_run[h], alpha, wave_sum_dpp(lead ? ew : 0.f));
     acc[h][0] *= alpha;
     acc[h][1] *= alpha;
     m_run[h] = mnew;
   }
   wave_barrier();
-  // P.V: the reads of four tokens, then their products
+  // P.V: the reads of four tokens, then their products; value = lo + delta
+  // (c + (s + 1/2) 2^-r)
   const int cpos = 4 * lane, cwi = cpos >> 5, csh = cpos & 31;
   const int rpos = 2 * lane * r, rwi = rpos >> 5, rsh = rpos & 31;
   const uint32_t rmask = (1u << r) - 1u;
+  const float hsub = 0.5f * sub;
   constexpr int kPart = 4;
 #pragma unroll 1
   for (int j1 = 0; j1 < kFTPW; j1 += kPart) {
     uint32_t cwd[kPart], rw0[kPart], rw1[kPart];
-    float2 scv[kPart], frv[kPart];
+    float2 scv[kPart];
     float wv[kPart][G];
 #pragma unroll
     for (int jj = 0; jj < kPart; ++jj) {
-      cwd[jj] = sp.vt[sw][j1 + jj][cwi];
-      rw0[jj] = sp.vr[sw][j1 + jj][rwi];
-      rw1[jj] = sp.vr[sw][j1 + jj][rwi + 1];
-      scv[jj] = sp.vsc[sw][j1 + jj];
-      frv[jj] = sp.vfr[sw][j1 + jj];
+      cwd[jj] = sp.vt[w][j1 + jj][cwi];
+      rw0[jj] = sp.vr[w][j1 + jj][rwi];
+      rw1[jj] = sp.vr[w][j1 + jj][rwi + 1];
+      scv[jj] = sp.vsc[w][j1 + jj];
 #pragma unroll
-      for (int h = 0; h < G; ++h) wv[jj][h] = sp.wt[sw][h][j1 + jj];
+      for (int h = 0; h < G; ++h) wv[jj][h] = sp.wt[w][h][j1 + jj];
     }
 #pragma unroll
     for (int jj = 0; jj < kPart; ++jj) {
@@ -489,9 +509,9 @@ __device__ inline void special_batch(const DecodeParams& p, FusedLds<G>& s, int 
       const uint32_t rr = (uint32_t)((((uint64_t)rw1[jj] << 32) | rw0[jj]) >> rsh);
       const float c0 = (float)(cc & 3u), c1 = (float)((cc >> 2) & 3u);
       const float s0 = (float)(rr & rmask), s1 = (float)((rr >> r) & rmask);
-      const float2 sc = scv[jj], fr = frv[jj];
-      const float v0 = fmaf(fmaf(s0, fr.x, fr.y), sc.y, fmaf(c0, sc.y, sc.x));
-      const float v1 = fmaf(fmaf(s1, fr.x, fr.y), sc.y, fmaf(c1, sc.y, sc.x));
+      const float2 sc = scv[jj];
+      const float v0 = fmaf(fmaf(s0, sub, hsub), sc.y, fmaf(c0, sc.y, sc.x));
+      const float v1 = fmaf(fmaf(s1, sub, hsub), sc.y, fmaf(c1, sc.y, sc.x));
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         acc[h][0] = fmaf(wv[jj][h], v0, acc[h][0]);
@@ -606,7 +626,7 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
   // ---- B: level 1 of the exact top-T of the head ---------------------------
   uint32_t* hist = s.u.st.h.hist;
   bool lvl2 = false;   // the level-1 boundary bin is split (the later levels run)
-  uint32_t need1 = 0u;
+  uint32_t b1 = 0u, need1 = 0u;   // the boundary bin and the count still needed there
   for (int w = tid; w < kFusedRmax / 32; w += 64 * kFW) s.sel[w] = s.cand[w] = s.csel[w] = 0u;
   __syncthreads();
   if (all) {
@@ -623,7 +643,7 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
     copy_dev_words(hist, &Z[kFZH1], kHistBins);
     __syncthreads();
     find_threshold_wave<kHistBins>(hist, (uint32_t)tn, &s.sh_bin, &s.sh_need);
-    const uint32_t b1 = (uint32_t)s.sh_bin;
+    b1 = (uint32_t)s.sh_bin;
     need1 = s.sh_need;
     lvl2 = hist[b1] != need1;
     // above b1 selected, in b1 candidates (all selected when b1 is taken
@@ -650,32 +670,163 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
   }
   __syncthreads();
 
-  // ---- C: V once (kFVW wavefronts) beside the selection's later levels and
-  // the selected tokens (kFSW) ---------------------------------------------
-  // the V stream takes every token that is neither selected nor a candidate
-  // at level 1; the two lists (selected, candidates) go to the special
-  // wavefronts in batches of kFTPW
+  // ---- B': the later levels, when level 1 leaves its boundary bin split ---
+  // Every work-group adds its candidates to the head's level-2 histogram (the
+  // next 12 key bits) and writes their keys and token indices to its slot of
+  // the head's list, with its count.  After one wait, when every range
+  // fitted its slot (the head has at most kFListRanges ranges), each
+  // work-group reads the whole list (4 entries a thread, into registers) and
+  // takes the exact need1-th largest key by a radix select (digits of 8, 8
+  // and 4 bits below the level-1 bin's 12, counted in LDS): keys above it
+  // are selected, and of the keys equal to it the lowest token indices fill
+  // what is still needed.  Otherwise the histograms settle it, one more wait
+  // per level (select_by_histograms, by wavefront 0).
+  if (tid == 0) s.used3 = 0u;
+  if (lvl2) {
+    const bool listed = nwg <= (uint32_t)kFListRanges;
+    const uint32_t slot = listed ? (uint32_t)(kFListMax / nwg) & ~63u : 0u;   // a multiple of 64
+    uint32_t* keys = Z + kFZL;
+    uint32_t* toks = keys + kFListMax;
+    uint32_t* counts = toks + kFListMax;
+    {
+      const uint32_t cw = tid < nw ? s.cand[tid] : 0u;
+      uint32_t total;
+      uint32_t pos = block_exclusive_scan<64 * kFW>((uint32_t)__popc(cw), s.scan, total);
+      for (uint32_t bits = cw; bits; bits &= bits - 1u, ++pos) {
+        const int t = 32 * tid + __ffs(bits) - 1;
+        const uint32_t key = token_key<G>(s.lg, t);
+        atomicAdd(&Z[kFZH2 + ((key >> 8) & 0xFFFu)], 1u);
+        if (pos < slot) {
+          st_dev(&keys[(uint32_t)wi * slot + pos], key);
+          st_dev(&toks[(uint32_t)wi * slot + pos], (uint32_t)(lo + t));
+        }
+      }
+      if (listed && tid == 0) st_dev(&counts[wi], total);
+    }
+    if (!group_wait(s, &Z[kFZC + 1], nwg, p.fstatus)) return;
+    // the counts and the list's keys in one round of loads; entry e = tid +
+    // 1024 i is position e % slot of range e / slot
+    constexpr int KPT = kFListMax / (64 * kFW);
+    uint32_t kk[KPT];
+    if (listed) {
+      const rsrc_t rk = make_rsrc(keys, (uint32_t)kFListMax * 4u);
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) kk[i] = __builtin_bit_cast(uint32_t, ld_devf(rk, 4u * (uint32_t)(tid + 64 * kFW * i)));
+      if (tid < (int)nwg) s.lcnt[tid] = ld_dev(&counts[tid]);
+    }
+    if (tid == 0) s.sh_flag = listed ? 1u : 0u;
+    __syncthreads();
+    if (tid < (int)nwg && listed && s.lcnt[tid] > slot) s.sh_flag = 0u;
+    __syncthreads();
+    if (s.sh_flag) {
+      // key 0 marks an empty entry: no candidate has it (the level-1 bin's
+      // 12 bits are those of a real score)
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const uint32_t e = (uint32_t)(tid + 64 * kFW * i), rg2 = e / slot;
+        if (rg2 >= nwg || e % slot >= s.lcnt[rg2]) kk[i] = 0u;
+      }
+      // after each digit: keys above the boundary digit are selected; when
+      // its bin is taken whole the keys from hval up are (no ties), else
+      // the next digit splits it
+      uint32_t hval = b1 << (32 - kHistBits), hmask = ~0u << (32 - kHistBits), need = need1, cnt = 0u;
+      bool whole = false;
+#pragma unroll
+      for (int pass = 0; pass < 3; ++pass) {
+        if (whole) break;
+        const int shift = pass == 0 ? 12 : pass == 1 ? 4 : 0;
+        const uint32_t dmask = pass == 2 ? 0xFu : 0xFFu;
+        if (tid < 256) s.shist[tid] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < KPT; ++i)
+          if (kk[i] != 0u && (kk[i] & hmask) == hval) atomicAdd(&s.shist[(kk[i] >> shift) & dmask], 1u);
+        __syncthreads();
+        if (wid == 0) {
+          int d;
+          uint32_t above, c;
+          if (pass == 2)
+            wave_boundary<16>(s.shist, need, d, above, c);
+          else
+            wave_boundary<256>(s.shist, need, d, above, c);
+          if (lane == 0) {
+            s.sh_bin = d;
+            s.sh_need = need - above;
+            s.sh_cnt = c;
+          }
+        }
+        __syncthreads();
+        need = s.sh_need;
+        cnt = s.sh_cnt;
+        hval |= (uint32_t)s.sh_bin << shift;
+        hmask |= dmask << shift;
+        whole = need == cnt;
+      }
+      // whole: every key >= hval selected (hval's lower bits are zero); else
+      // keys above hval selected, `need` of the `cnt` keys equal to it taken
+      const uint32_t thr = hval, take = need;
+      uint32_t selw = 0u, tw = 0u;
+      if (tid < nw)
+        for (uint32_t bits = s.cand[tid]; bits; bits &= bits - 1u) {
+          const int bit = __ffs(bits) - 1;
+          const uint32_t key = token_key<G>(s.lg, 32 * tid + bit);
+          if (whole ? key >= thr : key > thr)
+            selw |= 1u << bit;
+          else if (key == thr)
+            tw |= 1u << bit;
+        }
+      if (!whole) {
+        // equal keys: the head's tied tokens before this range, then this
+        // range's ties in token order
+        const rsrc_t rt = make_rsrc(toks, (uint32_t)kFListMax * 4u);
+        uint32_t bf = 0u;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i)
+          if (kk[i] == thr)
+            bf += __builtin_bit_cast(uint32_t, ld_devf(rt, 4u * (uint32_t)(tid + 64 * kFW * i))) < (uint32_t)lo ? 1u : 0u;
+        uint32_t before, ntie;
+        (void)block_exclusive_scan<64 * kFW>(bf, s.scan, before);
+        uint32_t rank = block_exclusive_scan<64 * kFW>((uint32_t)__popc(tw), s.scan, ntie) + before;
+        for (uint32_t bits = tw; bits; bits &= bits - 1u, ++rank)
+          if (rank < take) selw |= 1u << (__ffs(bits) - 1);
+      }
+      if (tid < nw) s.sel[tid] |= selw;
+    } else {
+      if (wid == 0) {
+        uint32_t cw[2], selw[2] = {0u, 0u};
+#pragma unroll
+        for (int k = 0; k < 2; ++k) cw[k] = 64 * k + lane < nw ? s.cand[64 * k + lane] : 0u;
+        select_by_histograms<G>(p, s, Z, cw, selw, nwg, need1, sk, wi);
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+          if (64 * k + lane < nw) s.csel[64 * k + lane] = selw[k];
+      }
+      __syncthreads();
+      if (tid < nw) s.sel[tid] |= s.csel[tid];
+    }
+    __syncthreads();
+  }
+  if (select && p.fsel && tid < nw) st_dev(&p.bitmap[sk * p.bm_words + (lo >> 5) + tid], s.sel[tid]);
+
+  // ---- C: V once (kFVW wavefronts), the selected tokens beside it (kFSW) ----
+  // the streaming wavefronts take every token that is not selected; the
+  // selected tokens go to the refining wavefronts in batches of kFTPW,
+  // round-robin (fixed, so that the sums do not depend on timing), each
+  // fetching its first batch's rows before the stream starts (they lead the
+  // memory queue), at top issue priority (they are few and latency-bound)
   const bool masked = select && p.use_refine != 0;
   if (masked) {
-    const uint32_t v = tid < nw ? (uint32_t)__popc(s.sel[tid]) | ((uint32_t)__popc(s.cand[tid]) << 16) : 0u;
     uint32_t total;
-    const uint32_t pos = block_exclusive_scan<64 * kFW>(v, s.scan, total);   // two 16-bit counts (<= 4096 each)
-    if (tid < nw) {
-      s.pre1[tid] = (uint16_t)(pos & 0xFFFFu);
-      s.pre2[tid] = (uint16_t)(pos >> 16);
-    }
+    const uint32_t pos = block_exclusive_scan<64 * kFW>(tid < nw ? (uint32_t)__popc(s.sel[tid]) : 0u, s.scan, total);
+    if (tid < nw) s.pre1[tid] = (uint16_t)pos;
     if (tid == 0) {
-      s.pre1[nw] = (uint16_t)(total & 0xFFFFu);
-      s.pre2[nw] = (uint16_t)(total >> 16);
-      s.n1 = total & 0xFFFFu;
-      s.n2 = total >> 16;
+      s.pre1[nw] = (uint16_t)total;
+      s.n1 = total;
     }
+    for (int i = tid; i < G * kHeadDim; i += 64 * kFW)
+      s.qs[i / kHeadDim][i % kHeadDim] = p.q[((int64_t)seq * p.hq + kvh * G) * kHeadDim + i];
   } else if (tid == 0) {
-    s.n1 = s.n2 = 0u;
-  }
-  if (tid == 0) {
-    s.sel_done = lvl2 ? 0u : 1u;
-    s.used3 = 0u;
+    s.n1 = 0u;
   }
   if (wid < kFVW)
     for (int i = lane; i < 2 * G * 32; i += 64) (&s.wt[wid][0][0])[i] = (_Float16)0.f;
@@ -684,7 +835,7 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
   const int t = lane & 15, hl = lane >> 4;        // logit layout: token t (and 16 + t), head hl
   const int n = lane & 15, rg = lane >> 4;        // P.V layout: column n, k-group rg
   // each wave's partial, kept in registers until the ring is free: a
-  // streaming wave's P.V (lanes n in [G, 2G)), maximum and sum; a special
+  // streaming wave's P.V (lanes n in [G, 2G)), maximum and sum; a refining
   // wave's running softmax
   float out[8][4];
   float mx = -INFINITY, ls = 0.f;
@@ -702,12 +853,12 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
       bdma16(rV, oV, c * 1024u, st.c);
       bdma4(rVS, oS, c * 256u, st.s);
     };
-#pragma unroll
+  #pragma unroll
     for (int k = 0; k < kFRingV - 1; ++k)
       if (k < nv) issueV(k, ring[k]);
     // the tokens the special wavefronts take: lane L holds words L and 64 + L
-    const uint32_t sw0 = masked && lane < nw ? s.sel[lane] | s.cand[lane] : 0u;
-    const uint32_t sw1 = masked && 64 + lane < nw ? s.sel[64 + lane] | s.cand[64 + lane] : 0u;
+    const uint32_t sw0 = masked && lane < nw ? s.sel[lane] : 0u;
+    const uint32_t sw1 = masked && 64 + lane < nw ? s.sel[64 + lane] : 0u;
     const int hlc = hl < G ? hl : 0;
     const uint32_t hsel = 2u * (uint32_t)(n & 1);
     const uint32_t psel = hsel | ((hsel + 1u) << 8) | ((hsel + 4u) << 16) | ((hsel + 5u) << 24);
@@ -718,7 +869,7 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
     const uint32_t lgA = lds_addr(&s.lg[0]) + 4u * (uint32_t)(t * G + hlc);
     const uint32_t aS = ring0 + (uint32_t)(offsetof(FStage, s) + 8 * t);
     uint32_t aV[4];
-#pragma unroll
+  #pragma unroll
     for (int v = 0; v < 4; ++v) aV[v] = ring0 + (uint32_t)(offsetof(FStage, c) + (4 * rg + (v ^ rg)) * 32 + 4 * vdw);
     const uint64_t rows = G >= 4 ? ~0ull : (1ull << (16 * (G & 3))) - 1ull;
     const float ninf = -INFINITY;
@@ -728,7 +879,7 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
     int sexp = 127;
     float wsc = 1.0f;
     v4f acc[8];
-#pragma unroll
+  #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
     auto body = [&](auto kc, int i) {
       constexpr int k = decltype(kc)::value;
@@ -748,7 +899,7 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
       read_vstage<k * (int)sizeof(FStage)>(aL0, aL1, aS, aV, lgr, vsr, vw);
       float lgx[2];
       float2 vsc[2];
-#pragma unroll
+  #pragma unroll
       for (int j = 0; j < 2; ++j) {
         lgx[j] = lane_select(mk[j], lgr[j], ninf);
         vsc[j] = __builtin_bit_cast(float2, vsr[j]);
@@ -772,7 +923,7 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
         t1 *= alpha;
         const int hc = n < 2 * G ? n % G : 0;
         float f = lane_value(alpha, 0);
-#pragma unroll
+  #pragma unroll
         for (int h = 1; h < G; ++h) {
           // read with every lane active (a lane read inside the selection
           // could run where lane 16 h is off)
@@ -784,12 +935,12 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
           sexp = need;
           wsc = __builtin_ldexpf(1.0f, sexp);
         }
-#pragma unroll
+  #pragma unroll
         for (int j = 0; j < 8; ++j) acc[j] *= f;
         m = mnew;
       }
       float wv[2];
-#pragma unroll
+  #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const float pk = __builtin_amdgcn_exp2f(lgx[j] - m);
         lsum += pk;
@@ -804,13 +955,13 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
       }
       const v8h bw = lds_read_v8h(wtR);
       uint32_t P[4];
-#pragma unroll
+  #pragma unroll
       for (int v = 0; v < 4; ++v) P[v] = __builtin_amdgcn_perm(vw[2 * v + 1], vw[2 * v], psel);
-#pragma unroll
+  #pragma unroll
       for (int tt = 0; tt < 8; ++tt) {
         const uint32_t msk = 0x00030003u << code_bit(tt);
         v4u av;
-#pragma unroll
+  #pragma unroll
         for (int v = 0; v < 4; ++v) av[v] = (tt < 2 ? P[v] << 4 : tt < 5 ? P[v] : P[v] >> 6) & msk;
         acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, av), bw, acc[tt], 0, 0, 0);
       }
@@ -827,16 +978,16 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
     lsum = row16_sum(lsum);
     t1 = row16_sum(t1);
     float t1h = 0.f;
-#pragma unroll
+  #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float th = lane_value(t1, 16 * h);   // every lane active (see the rescale above)
       t1h = n - G == h ? th : t1h;
     }
     const int se = sexp == 127 ? 0 : sexp;
-#pragma unroll
+  #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
       const float f = __builtin_ldexpf(1.0f, 24 - code_bit(tt) - se);
-#pragma unroll
+  #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float x = acc[tt][j] * f;
         const float hi_part =
@@ -854,42 +1005,21 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
       lsn[h] = 0.f;
       accs[h][0] = accs[h][1] = 0.f;
     }
-    if (sw == 0) {
-      // the selector: the candidates settled, the range's selection words to
-      // device memory when asked, then the candidates' list opened
-      if (lvl2) select_candidates<G>(p, s, Z, nw, nwg, need1, sk, wi);
-      if (select && p.fsel)
-        for (int w = lane; w < nw; w += 64) st_dev(&p.bitmap[sk * p.bm_words + (lo >> 5) + w], s.sel[w] | s.csel[w]);
-      if (lvl2) __hip_atomic_store(&s.sel_done, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
-    if (masked) {
-      // every special wavefront writes the whole query (the same values): it
-      // then reads only what it wrote itself
+    const uint32_t nsel = s.n1;
+    if ((uint32_t)(kFTPW * sw) < nsel) {
+      __builtin_amdgcn_s_setprio(3);
+      SelRows rw;
+      sel_fetch<G>(p, s, (uint32_t)(kFTPW * sw), (int)min((uint32_t)kFTPW, nsel - kFTPW * sw), kvh, t0, nw, rw);
       float qsum[G];
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float* qh = p.q + ((int64_t)seq * p.hq + kvh * G + h) * kHeadDim;
-        const float q0 = qh[lane], q1 = qh[64 + lane];
-        s.u.st.h.sp.qs[h][lane] = q0;
-        s.u.st.h.sp.qs[h][64 + lane] = q1;
-        qsum[h] = wave_sum_dpp(q0 + q1);
+      for (int h = 0; h < G; ++h) qsum[h] = wave_sum_dpp(s.qs[h][lane] + s.qs[h][64 + lane]);
+      sel_compute<G>(p, s, sw, rw, (int)min((uint32_t)kFTPW, nsel - kFTPW * sw), qsum, msn, lsn, accs);
+      for (uint32_t j0 = (uint32_t)(kFTPW * (sw + kFSW)); j0 < nsel; j0 += (uint32_t)(kFTPW * kFSW)) {
+        const int cnt = (int)min((uint32_t)kFTPW, nsel - j0);
+        sel_fetch<G>(p, s, j0, cnt, kvh, t0, nw, rw);
+        sel_compute<G>(p, s, sw, rw, cnt, qsum, msn, lsn, accs);
       }
-      wave_barrier();
-      // batches round-robin, fixed for the head (so that the sums do not
-      // depend on timing): the selected list over the wavefronts other than
-      // the selector while the later levels run, the candidates over all
-      for (int lst = 0; lst < 2; ++lst) {
-        if (lst == 1)
-          while (__hip_atomic_load(&s.sel_done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0u)
-            __builtin_amdgcn_s_sleep(2);
-        const uint32_t len = lst ? s.n2 : s.n1;
-        const int nwk = lst == 0 && lvl2 ? kFSW - 1 : kFSW;
-        const int me = lst == 0 && lvl2 ? sw - 1 : sw;
-        if (me < 0) continue;
-        for (uint32_t j0 = (uint32_t)(kFTPW * me); j0 < len; j0 += (uint32_t)(kFTPW * nwk))
-          special_batch<G>(p, s, sw, lst, j0, (int)min((uint32_t)kFTPW, len - j0), kvh, t0, nw, qsum, msn, lsn,
-                           accs);
-      }
+      __builtin_amdgcn_s_setprio(0);
     }
   }
   __syncthreads();   // every wave is done with the ring and the staging

@@ -116,6 +116,53 @@ def test_flat_rows_and_all_equal_scores():
     assert np.array_equal(run.sel[0, 0], np.arange(w.top_t))
 
 
+def _near_equal_keys(k, v):
+    # every key close to one row: more than 2,048 tokens share the level-1
+    # boundary bin, so the single launch settles them by its histogram levels
+    k[:] = k[5] + 1e-3 * k
+
+
+def _pivot_ties(k, v):
+    # 40 exact copies of one row spread over the context
+    rng = np.random.default_rng(7)
+    dst = rng.choice(np.arange(1, k.shape[0]), size=40, replace=False)
+    W.duplicate_rows(k, v, [0] * 40, dst)
+
+
+def _all_equal(k, v):
+    k[:] = k[5]
+
+
+SELECT_CASES = {
+    "random": (dict(ctx=20000, top_t=500), None),
+    "pivot_ties": (dict(ctx=9000, top_t=300), _pivot_ties),
+    "near_equal": (dict(ctx=6000, top_t=300), _near_equal_keys),
+    "all_equal": (dict(ctx=5000, top_t=100), _all_equal),
+}
+
+
+@pytest.mark.parametrize("case", list(SELECT_CASES))
+def test_single_launch_selects_as_the_five_kernel_form(case):
+    """Both forms take the exact top-T of the same fp32 keys, ties to the
+    lower index, so their selections are identical (the single launch through
+    its candidate list, or through its histogram levels when the level-1
+    boundary bin holds more than 2,048 tokens)."""
+    over, dup = SELECT_CASES[case]
+    w = W.small(cfg_id=304, **over)
+    off = W.seq_offsets(w.seq_lengths())
+    k, v = W.layer_kv(w, 0)
+    if dup is not None:
+        dup(k, v)
+    q = W.query(w, 0)
+    print(f"case {case}: {over}", flush=True)
+    a = P.run_gpu(w, k, v, q, off, w.top_t)
+    b = P.run_gpu(w, k, v, q, off, w.top_t, multi_pass=True)
+    assert np.array_equal(a.scores.view(np.uint32), b.scores.view(np.uint32))
+    assert np.array_equal(a.sel, b.sel)
+    assert float(np.abs(a.out - b.out).max()) < 1e-4
+    P.compare_layer(w, k, v, q, off, w.top_t, a)
+
+
 def test_deterministic_repeat():
     w = W.small(cfg_id=302, ctx=5000, n_q_heads=8, n_kv_heads=2, top_t=128)
     lens = w.seq_lengths()
