@@ -9,10 +9,13 @@ Inputs are seeded synthetic K/V/q of the named head geometry, resident in HBM
 before timing starts.
 
 Prints ONE JSON line: steps/s (whole job), the step's algorithmic HBM GB/s,
-a roofline record of the dominant kernel (score or attention pass) timed live
-with HIP events, the CPU oracle timed on a bounded sample on the host, and
-secondary measurements (32K context; host-pinned refinement store with an
-AR(1) query process: hit rate and bytes fetched per step).
+a roofline record of the dominant kernel (the single-launch decode kernel, or
+the score or attention pass of the five-kernel form) timed live with HIP
+events, the CPU oracle timed on a bounded sample on the host, and secondary
+measurements (the five-kernel form beside the single launch; 32K context; the
+16-sequence batch over distinct layers; host-pinned refinement store over 64
+AR(1) steps: cold and warm step time, hit rate and bytes fetched; the
+multi-step reuse run).
 """
 import argparse
 import json
@@ -43,6 +46,12 @@ def algorithmic_bytes(w, lens):
     return tot
 
 
+def fused_bytes(w, lens):
+    """The single-launch form moves every algorithmic byte of the layer in its
+    one kernel."""
+    return {"fused": algorithmic_bytes(w, lens)}
+
+
 def kernel_bytes(w, lens):
     """The layer's algorithmic bytes, each credited to the one pass that moves
     it.  score: base K codes and (lo, delta) of every token, and the query.
@@ -61,7 +70,7 @@ def kernel_bytes(w, lens):
 class Model:
     """The workload's layers resident on the GPU."""
 
-    def __init__(self, w, tier, layers=None):
+    def __init__(self, w, tier, layers=None, multi_pass=False):
         import torch
         from selective_kv_cache_amd import binding as B
         from selective_kv_cache_amd import workloads as W
@@ -70,27 +79,41 @@ class Model:
         self.lens = w.seq_lengths()
         self.off = W.seq_offsets(self.lens)
         self.L = w.layers if layers is None else layers
+        self.multi_pass = multi_pass
         g = B.geom(w.head_dim, w.n_q_heads, w.n_kv_heads, w.base_bits, w.refine_bits)
         ntot = int(self.off[-1])
-        self.caches, self.qs = [], []
+        self.caches = []
+        # one query buffer for all layers ([L][B][Hq][D]); a step reads it in
+        # place, so new queries are copied in between steps
+        self.qbuf = torch.empty((self.L, w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
         for l in range(self.L):
             c = LayerCache(g, ntot, tier=tier, max_seqs=w.batch, cache_slots=w.cache_slots())
             k, v = W.layer_kv(w, l, device="cuda")
             c.append(k, v, 0)
             del k, v
             self.caches.append(c)
-            self.qs.append(torch.as_tensor(W.query(w, l), device="cuda"))
+            self.qbuf[l].copy_(torch.as_tensor(W.query(w, l)))
+        self.qs = [self.qbuf[l] for l in range(self.L)]
         torch.cuda.synchronize()
         self.dec = Decoder(g, self.off, w.top_t)
         self.outs = [torch.empty((w.batch, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
                      for _ in range(self.L)]
+
+    def ar1_queries(self, n_steps, rho=0.9):
+        """[n_steps][L][B][Hq][D] queries following the AR(1) process per layer
+        (selections then change from step to step but overlap)."""
+        import torch
+        from selective_kv_cache_amd import workloads as W
+        wq = W.Workload(**{**self.w.__dict__, "rho": rho})
+        per = np.stack([W.queries(wq, l, n_steps) for l in range(self.L)], axis=1)
+        return torch.as_tensor(per, device="cuda")
 
     def step(self, qs=None, events=None, stats=False):
         acc = {"selected": 0, "hits": 0, "misses": 0, "h2d_bytes": 0}
         for l in range(self.L):
             ev = events[l] if events is not None else None
             res = self.dec.step(self.caches[l], (qs or self.qs)[l], out=self.outs[l], events=ev,
-                                want_stats=stats)
+                                want_stats=stats, multi_pass=self.multi_pass)
             if stats:
                 for k2 in acc:
                     acc[k2] += res[1][k2]
@@ -130,17 +153,23 @@ def capture_step(model):
     return graph
 
 
-def time_graph(graph, steps, warmup):
+def time_graph(graph, steps, warmup, model=None, qseq=None):
     """Exactly `steps` back-to-back graph replays, synchronized on both sides,
     with a HIP event between consecutive ones: (mean ms per step over the
-    whole timed region, per-step ms)."""
+    whole timed region, per-step ms).  With ``qseq`` ([warmup + steps][L]...)
+    each replay is preceded by the copy of that step's queries into the
+    model's query buffer (inside the timed region)."""
     import torch
-    for _ in range(warmup):
+    for i in range(warmup):
+        if qseq is not None:
+            model.qbuf.copy_(qseq[i])
         graph.replay()
     torch.cuda.synchronize()
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     evs[0].record()
     for i in range(steps):
+        if qseq is not None:
+            model.qbuf.copy_(qseq[warmup + i])
         graph.replay()
         evs[i + 1].record()
     torch.cuda.synchronize()
@@ -148,23 +177,28 @@ def time_graph(graph, steps, warmup):
     return evs[0].elapsed_time(evs[-1]) / steps, per
 
 
-def achievable_read_gbps():
-    """Streaming read bandwidth of the box from a plain reduction over 4 GiB
-    (torch's kernel; context for the peak, not a measurement of this path)."""
+def achievable_read_gbps(nbytes=4 << 30):
+    """Streaming read bandwidth of the box: the library's plain read kernel
+    (sf_stream_read) over a 4 GiB buffer, the best of a few launch widths;
+    context for the peak, not a measurement of the decode path."""
     import torch
-    x = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
-    for _ in range(2):
-        x.sum()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(5):
-        x.sum()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / 5
+    from selective_kv_cache_amd import binding as B
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    best = {}
+    for blocks in (1024, 2048, 4096, 8192):
+        for _ in range(2):
+            B.sf_stream_read(x, nbytes, 0xDEADBEEF, sink, blocks)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            B.sf_stream_read(x, nbytes, 0xDEADBEEF, sink, blocks)
+        e1.record()
+        torch.cuda.synchronize()
+        best[blocks] = x_bytes_per_ms(nbytes, e0.elapsed_time(e1) / 5)
     del x
-    return x_bytes_per_ms(4 << 30, ms)
+    return max(best.values()), best
 
 
 def source_hash():
@@ -202,7 +236,7 @@ def x_bytes_per_ms(nbytes, ms):
 KERNELS = ("score", "scan", "resolve", "attend", "combine")
 
 
-def time_kernels(model, steps):
+def time_kernels(model, steps, names=KERNELS):
     """Average duration of each kernel of the step, from a pair of HIP events
     around every launch: the start event is recorded just before the kernel's
     dispatch, the stop event completes with it (both created without the
@@ -210,7 +244,7 @@ def time_kernels(model, steps):
     elapsed(start, stop) is the kernel's time as it ran inside the step."""
     import torch
     from selective_kv_cache_amd.binding import TimingEvent
-    evs = [[tuple((TimingEvent(), TimingEvent()) for _ in KERNELS) for _ in range(model.L)]
+    evs = [[tuple((TimingEvent(), TimingEvent()) for _ in names) for _ in range(model.L)]
            for _ in range(steps)]
     torch.cuda.synchronize()
     # hold the stream with a spin kernel while the host queues every timed
@@ -220,37 +254,36 @@ def time_kernels(model, steps):
     for s in range(steps):
         model.step(events=evs[s])
     torch.cuda.synchronize()
-    dur = {k: [] for k in KERNELS}
+    dur = {k: [] for k in names}
     for row in evs:
         for quint in row:
-            for k, (e0, e1) in zip(KERNELS, quint):
+            for k, (e0, e1) in zip(names, quint):
                 dur[k].append(e0.elapsed_ms(e1))
+            for e0, e1 in quint:
                 e0.close()
                 e1.close()
     out = {}
-    for k in KERNELS:
+    for k in names:
         out[k] = float(np.mean(dur[k]))
         out[k + "_median"] = float(np.median(dur[k]))
     return out
 
 
-def cpu_baseline(w, min_s=10.0, max_s=30.0, n_layers=3):
-    """The oracle timed on the host on a bounded sample: the decode of the
-    first n_layers layers (all KV heads of every sequence), layer after layer
-    and again until at least min_s of timed work (stopping at max_s), scaled
-    to whole-model steps/s."""
-    import torch
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_rate(w, layers, heads, off, min_s, max_s):
+    """Seconds per whole layer of the oracle, timed over the given layers'
+    (sequence, KV head) units in turn until at least min_s (at most max_s)."""
     import oracle.kv_oracle as O
-    from selective_kv_cache_amd import workloads as W
-    lens = w.seq_lengths()
-    off = W.seq_offsets(lens)
-    layers = []
-    for l in range(min(n_layers, w.layers)):
-        k, v = W.layer_kv(w, l, device="cuda")
-        k, v = k.cpu().numpy(), v.cpu().numpy()
-        layers.append((W.query(w, l), O.quantize_cache(k, v, w.base_bits, w.refine_bits)))   # setup, not timed
-        del k, v
-    heads = [(s, h) for s in range(w.batch) for h in range(w.n_kv_heads)]
     dt, done, full = 0.0, 0, 0
     while dt < min_s:
         for q, cache in layers:
@@ -268,52 +301,89 @@ def cpu_baseline(w, min_s=10.0, max_s=30.0, n_layers=3):
                 break
         if dt > max_s:
             break
-    layer_s = dt * len(heads) / done
+    return dt * len(heads) / done, dt, done, full
+
+
+def cpu_baseline(w, min_s=8.0, max_s=15.0, n_layers=3):
+    """The oracle timed on the host on a bounded sample: the decode of the
+    first n_layers layers (all KV heads of every sequence), layer after layer
+    and again until at least min_s of timed work (stopping at max_s), scaled
+    to whole-model steps/s; once with the BLAS thread pool at one thread and
+    once with every core the process may use."""
+    import oracle.kv_oracle as O
+    from selective_kv_cache_amd import workloads as W
+    lens = w.seq_lengths()
+    off = W.seq_offsets(lens)
+    layers = []
+    for l in range(min(n_layers, w.layers)):
+        k, v = W.layer_kv(w, l, device="cuda")
+        k, v = k.cpu().numpy(), v.cpu().numpy()
+        layers.append((W.query(w, l), O.quantize_cache(k, v, w.base_bits, w.refine_bits)))   # setup, not timed
+        del k, v
+    heads = [(s, h) for s in range(w.batch) for h in range(w.n_kv_heads)]
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_limits
     except Exception:
-        threads = 1
-    return {"value": 1.0 / (layer_s * w.layers), "unit": "steps/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"layers 0-{len(layers) - 1} of {w.name}, in turn: {done} (sequence, KV head) units "
-                      f"({full} whole layers) timed, {dt:.1f} s, scaled to {w.layers} layers; numpy fp64 "
-                      f"oracle, quantization excluded"}
+        threadpool_limits = None
+    res = {}
+    for label, nthreads in (("all_cores", cores), ("one_core", 1)):
+        if threadpool_limits is not None:
+            with threadpool_limits(limits=nthreads):
+                layer_s, dt, done, full = _oracle_rate(w, layers, heads, off, min_s, max_s)
+        else:
+            layer_s, dt, done, full = _oracle_rate(w, layers, heads, off, min_s, max_s)
+        res[label] = {"steps_per_s": 1.0 / (layer_s * w.layers), "threads": nthreads, "timed_s": dt,
+                      "units": done, "whole_layers": full}
+    return {"value": res["all_cores"]["steps_per_s"], "unit": "steps/s", "cores": cores, "kind": "oracle",
+            "cpu_model": _cpu_model(), "one_core_value": res["one_core"]["steps_per_s"], "runs": res,
+            "sample": f"layers 0-{len(layers) - 1} of {w.name}, in turn: the (sequence, KV head) units of each "
+                      f"layer timed until {min_s:.0f} s (at most {max_s:.0f} s) of work, scaled to {w.layers} "
+                      f"layers; numpy fp64 oracle (BLAS threads: all {cores} cores the process may use, then 1), "
+                      f"quantization excluded"}
 
 
-def host_tier_run(w, steps, warmup):
-    """Host-pinned refinement store + device cache; queries follow an AR(1)
-    process (rho = 0.9) so selections overlap across steps."""
+def host_tier_run(w, steps=64):
+    """Host-pinned refinement store + device cache over `steps` steps of an
+    AR(1) query process (rho = 0.9, selections overlap from step to step),
+    from empty caches: every step timed on its own (eager launches, no
+    statistics, so nothing waits on the host), then the same queries again
+    from empty caches with statistics for the hit rate and link bytes of each
+    step.  Cold = the first step, warm = the second half."""
     import torch
     from selective_kv_cache_amd import binding as B
-    from selective_kv_cache_amd import workloads as W
-    wq = W.Workload(**{**w.__dict__, "rho": 0.9})
     m = Model(w, B.SF_TIER_HOST_PINNED)
     try:
-        n = warmup + steps
-        per_layer = [W.queries(wq, l, n) for l in range(m.L)]
-        qsteps = [[torch.as_tensor(per_layer[l][t], device="cuda") for l in range(m.L)] for t in range(n)]
-        # timed without statistics (asking for them makes every call wait)
-        for t in range(warmup):
-            m.step(qsteps[t])
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for t in range(warmup, n):
-            m.step(qsteps[t])
-        torch.cuda.synchronize()
-        dt = (time.perf_counter() - t0) / steps
-        # the same query sequence again from empty caches, with statistics
+        qseq = m.ar1_queries(steps)
         for c in m.caches:
             c.clear_cache()
-        tot = {"selected": 0, "hits": 0, "misses": 0, "h2d_bytes": 0}
-        for t in range(n):
-            st = m.step(qsteps[t], stats=True)
-            if t >= warmup:
-                for k2 in tot:
-                    tot[k2] += st[k2]
-        return {"workload": w.name, "store": "host_pinned", "query_process": "AR(1) rho=0.9",
-                "steps": steps, "warmup": warmup, "ms_per_step": dt * 1e3, "steps_per_s": 1.0 / dt,
-                "hit_rate": tot["hits"] / max(tot["selected"], 1),
-                "h2d_bytes_per_step": tot["h2d_bytes"] / steps}
+        torch.cuda.synchronize()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        for t in range(steps):
+            m.qbuf.copy_(qseq[t])
+            evs[t].record()
+            m.step()
+        evs[steps].record()
+        torch.cuda.synchronize()
+        per = [evs[t].elapsed_time(evs[t + 1]) for t in range(steps)]
+        for c in m.caches:
+            c.clear_cache()
+        st = []
+        for t in range(steps):
+            m.qbuf.copy_(qseq[t])
+            st.append(m.step(stats=True))
+        half = steps // 2
+        warm = st[half:]
+        sel_w = sum(x["selected"] for x in warm)
+        return {"workload": w.name, "store": "host_pinned", "query_process": "AR(1) rho=0.9", "steps": steps,
+                "launch": "eager", "from": "empty caches",
+                "cold_ms_per_step": per[0], "warm_ms_per_step": float(np.mean(per[half:])),
+                "warm_steps_per_s": 1e3 / float(np.mean(per[half:])), "all_steps_ms_mean": float(np.mean(per)),
+                "cold_hit_rate": st[0]["hits"] / max(st[0]["selected"], 1),
+                "warm_hit_rate": sum(x["hits"] for x in warm) / max(sel_w, 1),
+                "cold_h2d_bytes": st[0]["h2d_bytes"],
+                "warm_h2d_bytes_per_step": float(np.mean([x["h2d_bytes"] for x in warm])),
+                "warm": f"steps {half}-{steps - 1}"}
     finally:
         m.close()
 
@@ -394,6 +464,37 @@ def reuse_record(w):
                              "compared": f"every layer's output at every 16th step ({len(o_skip)} outputs)"}}
 
 
+def headline(w, tier, steps, warmup, multi_pass=False):
+    """steps/s of the workload: eager launches with fixed queries, then the
+    step captured as a HIP graph and replayed under AR(1) queries (copied into
+    the query buffer before each replay, inside the timed region), then each
+    kernel timed with event pairs.  Returns (record, per-kernel times, form)."""
+    import torch
+    from selective_kv_cache_amd import binding as B
+    model = Model(w, tier, multi_pass=multi_pass)
+    try:
+        form = model.dec.form(model.caches[0], multi_pass=multi_pass)
+        ms_eager = time_steps(model, steps, warmup)
+        rec = {"eager_ms_per_step": ms_eager, "kernels_per_layer": form}
+        if tier == B.SF_TIER_DEVICE:
+            qseq = model.ar1_queries(warmup + steps)
+            graph = capture_step(model)
+            ms, per = time_graph(graph, steps, warmup, model, qseq)
+            del graph
+            rec.update(ms_per_step=ms, launch="hip_graph", query_process="AR(1) rho=0.9, new queries every step",
+                       ms_per_step_p50=float(np.percentile(per, 50)),
+                       ms_per_step_p10=float(np.percentile(per, 10)),
+                       ms_per_step_p90=float(np.percentile(per, 90)))
+        else:
+            rec.update(ms_per_step=ms_eager, launch="eager", query_process="fixed per layer")
+        names = ("fused",) if form == 1 else KERNELS
+        kt = time_kernels(model, max(2, steps // 4), names)
+        assert model.dec.check() == B.SF_OK, "a bounded wait expired"
+        return rec, kt, form
+    finally:
+        model.close()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -401,6 +502,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="llama8b_128k")
     ap.add_argument("--tier", choices=["device", "host"], default="device")
+    ap.add_argument("--multi-pass", action="store_true", help="the five-kernel form for the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -427,26 +529,15 @@ def main():
     w = W.WORKLOADS[args.workload]
     tier = B.SF_TIER_DEVICE if args.tier == "device" else B.SF_TIER_HOST_PINNED
     log(f"setup {w.name}: {w.layers} layers, ctx {w.seq_lengths()[:4]}, tier {args.tier}")
-    model = Model(w, tier)
-    log("timing steps (eager launches)")
-    ms_eager = time_steps(model, args.steps, args.warmup)
-    launch = "eager"
-    ms, p50, p10, p90 = ms_eager, None, None, None
-    if tier == B.SF_TIER_DEVICE:
-        log(f"{ms_eager:.3f} ms/step eager; capturing the step as a HIP graph")
-        graph = capture_step(model)
-        ms, per = time_graph(graph, args.steps, args.warmup)
-        p50, p10, p90 = (float(np.percentile(per, q)) for q in (50, 10, 90))
-        launch = "hip_graph"
-        del graph
-    log(f"{ms:.3f} ms/step ({launch}); timing each kernel with HIP events")
-    kt = time_kernels(model, max(2, args.steps // 4))
-    model.close()
-    del model
-    step_bytes = algorithmic_bytes(w, w.seq_lengths()) * w.layers
-    kb = kernel_bytes(w, w.seq_lengths())
+    hl, kt, form = headline(w, tier, args.steps, args.warmup, args.multi_pass)
+    ms = hl["ms_per_step"]
+    log(f"{ms:.3f} ms/step ({hl['launch']}, {form} kernel(s) per layer); kernels {kt}")
+    lens = w.seq_lengths()
+    step_bytes = algorithmic_bytes(w, lens) * w.layers
+    kb = fused_bytes(w, lens) if form == 1 else kernel_bytes(w, lens)
     dom = max(kb, key=lambda k: kt[k])
     gbps = {k: kb[k] / (kt[k] * 1e-3) / 1e9 for k in kb}
+    traffic = measured_traffic(w.name).get(dom + "_decode" if form == 1 else dom + "_mfma")
     rec = {
         "metric": METRIC, "value": 1e3 / ms, "unit": "steps/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
@@ -454,60 +545,59 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "ctx": w.ctx or list(w.ctx_range),
                    "layers": w.layers, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "base_bits": w.base_bits, "refine_bits": w.refine_bits,
-                   "top_t": w.top_t, "refinement_store": args.tier, "launch": launch},
-        "ms_per_step_p50": p50, "ms_per_step_p10": p10, "ms_per_step_p90": p90, "eager_ms_per_step": ms_eager,
+                   "top_t": w.top_t, "refinement_store": args.tier, "launch": hl["launch"],
+                   "query_process": hl["query_process"], "kernels_per_layer": form},
+        "ms_per_step_p50": hl.get("ms_per_step_p50"), "ms_per_step_p10": hl.get("ms_per_step_p10"),
+        "ms_per_step_p90": hl.get("ms_per_step_p90"), "eager_ms_per_step": hl["eager_ms_per_step"],
         "step_algorithmic_bytes": step_bytes,
         "step_hbm_gbps": step_bytes / (ms * 1e-3) / 1e9,
         "step_frac_of_peak": step_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "roofline": {"bound": "hbm", "achieved": gbps[dom], "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": gbps[dom] / PEAK_HBM_GBPS,
-                     "traffic": measured_traffic(w.name).get(dom + "_mfma"), "kernel": dom,
+                     "frac": gbps[dom] / PEAK_HBM_GBPS, "traffic": traffic, "kernel": dom,
                      "bytes_per_launch": kb[dom], "avg_launch_ms": kt[dom],
                      "kernels": {k: {"bytes_per_launch": kb[k], "avg_launch_ms": kt[k],
                                      "median_launch_ms": kt[k + "_median"], "achieved_gbps": gbps[k]}
                                  for k in kb},
-                     "other_kernels_avg_ms": {k: kt[k] for k in KERNELS if k not in kb},
+                     "other_kernels_avg_ms": {k: kt[k] for k in kt if k not in kb and not k.endswith("_median")},
                      "event_timing": "start/stop HIP event pair around each launch, in this run"},
     }
     if not args.no_secondary:
         sec = {}
+        if form == 1:
+            log(f"secondary: {w.name}, the five-kernel form")
+            hm, ktm, _ = headline(w, tier, args.steps, args.warmup, multi_pass=True)
+            sec["multi_pass"] = {"ms_per_step": hm["ms_per_step"], "steps_per_s": 1e3 / hm["ms_per_step"],
+                                 "launch": hm["launch"], "kernels_avg_ms": {k: ktm[k] for k in KERNELS}}
         w2 = W.WORKLOADS["llama8b_32k"]
         log("secondary: llama8b_32k")
-        m2 = Model(w2, B.SF_TIER_DEVICE)
-        g2 = capture_step(m2)
-        ms2 = time_graph(g2, args.steps, args.warmup)[0]
-        del g2
-        m2.close()
-        del m2
+        h2, kt2, f2 = headline(w2, B.SF_TIER_DEVICE, args.steps, args.warmup)
         b2 = algorithmic_bytes(w2, w2.seq_lengths()) * w2.layers
-        sec["llama8b_32k"] = {"steps_per_s": 1e3 / ms2, "ms_per_step": ms2, "launch": "hip_graph",
-                              "step_hbm_gbps": b2 / (ms2 * 1e-3) / 1e9,
-                              "step_frac_of_peak": b2 / (ms2 * 1e-3) / 1e9 / PEAK_HBM_GBPS}
-        w4 = W.WORKLOADS["qwen8b_b16"]
-        log("secondary: qwen8b_b16")
-        m4 = Model(w4, B.SF_TIER_DEVICE)
-        # one layer per step: a graph replay's own fixed cost is then a large
-        # share, so the eager rate (the host queues ahead) is timed as well
-        ms4e = time_steps(m4, 8 * args.steps, args.warmup)
-        g4 = capture_step(m4)
-        ms4g = time_graph(g4, 8 * args.steps, args.warmup)[0]
-        del g4
-        m4.close()
-        del m4
-        ms4, launch4 = (ms4g, "hip_graph") if ms4g <= ms4e else (ms4e, "eager")
-        b4 = algorithmic_bytes(w4, w4.seq_lengths()) * w4.layers
-        sec["qwen8b_b16"] = {"layer_steps_per_s": 1e3 / ms4, "ms_per_layer_step": ms4, "launch": launch4,
-                             "ms_per_layer_step_graph": ms4g, "ms_per_layer_step_eager": ms4e,
-                             "batch": w4.batch, "tokens": int(sum(w4.seq_lengths())),
+        sec["llama8b_32k"] = {"steps_per_s": 1e3 / h2["ms_per_step"], "ms_per_step": h2["ms_per_step"],
+                              "launch": h2["launch"], "kernels_per_layer": f2,
+                              "kernels_avg_ms": {k: v for k, v in kt2.items() if not k.endswith("_median")},
+                              "step_hbm_gbps": b2 / (h2["ms_per_step"] * 1e-3) / 1e9,
+                              "step_frac_of_peak": b2 / (h2["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+        w4 = W.Workload(**{**W.WORKLOADS["qwen8b_b16"].__dict__, "layers": 4})
+        log("secondary: qwen8b_b16 over 4 distinct layers")
+        h4, kt4, f4 = headline(w4, B.SF_TIER_DEVICE, args.steps, args.warmup)
+        ms4 = min(h4["ms_per_step"], h4["eager_ms_per_step"]) / w4.layers
+        b4 = algorithmic_bytes(w4, w4.seq_lengths())
+        sec["qwen8b_b16"] = {"layer_steps_per_s": 1e3 / ms4, "ms_per_layer_step": ms4,
+                             "layers_timed": w4.layers, "working_set_bytes": b4 * w4.layers,
+                             "launch": "hip_graph" if h4["ms_per_step"] <= h4["eager_ms_per_step"] else "eager",
+                             "kernels_per_layer": f4, "batch": w4.batch, "tokens": int(sum(w4.seq_lengths())),
+                             "kernels_avg_ms": {k: v for k, v in kt4.items() if not k.endswith("_median")},
                              "step_hbm_gbps": b4 / (ms4 * 1e-3) / 1e9,
                              "step_frac_of_peak": b4 / (ms4 * 1e-3) / 1e9 / PEAK_HBM_GBPS}
         if w.host_store:
-            log("secondary: host-pinned store")
-            sec["host_store"] = host_tier_run(w, max(4, args.steps // 2), 2)
+            log("secondary: host-pinned store, 64 AR(1) steps from empty caches")
+            sec["host_store"] = host_tier_run(w, 64)
         log("secondary: multi-step reuse run (llama8b_reuse)")
         sec["reuse"] = reuse_record(W.WORKLOADS["llama8b_reuse"])
         rec["secondary"] = sec
-    rec["achievable_read_gbps"] = achievable_read_gbps()
+    rd, rd_all = achievable_read_gbps()
+    rec["achievable_read_gbps"] = rd
+    rec["achievable_read"] = {"kernel": "sf_stream_read", "bytes": 4 << 30, "gbps_by_blocks": rd_all}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on a bounded sample)")
         rec["cpu_baseline"] = cpu_baseline(w)
