@@ -98,6 +98,21 @@ sf_status sf_kv_quantize(const sf_geom* geom, const float* x, int64_t n_tok,
                          int64_t tok_begin, int64_t cap, uint8_t* codes,
                          float* scales, uint8_t* refine_rows, void* stream);
 
+/* sf_kv_quantize_ex flags: fp16 scale storage (the pages fix no scale
+ * format; 4 bytes per row instead of 8).  lo is the row minimum rounded down
+ * to IEEE fp16 and delta = (max - lo) * 2^-b rounded up to fp16, so that lo +
+ * 2^b delta still reaches the maximum; the codes are measured against those
+ * values (one fp32 subtraction, one fp32 division by delta * 2^-r, clamped
+ * to the top code).  The scales land in the same [Hkv][cap][2] fp32 slots,
+ * holding fp16 values, so the decode step reads them unchanged.  Rows must
+ * lie within the fp16 range. */
+#define SF_QUANT_FP16_SCALES 1
+
+/* sf_kv_quantize with flags (0 or SF_QUANT_FP16_SCALES); same arguments and
+ * errors otherwise. */
+sf_status sf_kv_quantize_ex(const sf_geom* geom, const float* x, int64_t n_tok, int64_t tok_begin, int64_t cap,
+                            uint8_t* codes, float* scales, uint8_t* refine_rows, int32_t flags, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Refinement store and device refinement cache.
  *
@@ -203,6 +218,31 @@ typedef struct sf_step_stats {
  * multi-pass form (different summation order). */
 #define SF_DECODE_MULTI_PASS 4
 
+/* sf_decode_args.flags, the comparison variants of page "StrataFlux --
+ * Selective precision streaming -- What does it mean?" (paragraph "What
+ * travels over the link ..." and the comparison table); each runs the step
+ * as its five kernels.
+ *
+ * SF_DECODE_DROP_UNSELECTED: the unselected tokens are left out of the
+ * attention (table row "Sparse attention"): the softmax runs over the
+ * selected tokens alone.  Needs top_t > 0 and refinement (r > 0 and a
+ * store) or SF_DECODE_ROWS16.
+ *
+ * SF_DECODE_ROWS16: the selected tokens take their complete 16-bit K and V
+ * rows (table row "SpeCache (16-bit fetching)"): args.rows16 holds, in
+ * device memory, [2][Hkv][cap][D] IEEE fp16 rows, K then V; the store and
+ * the refinement codes are not read.  Needs top_t > 0.
+ *
+ * SF_DECODE_SCORE_SOFTMAX: a token's score is the attention it receives
+ * (paragraph "Which tiles count ..."): the sum over its KV head's group of
+ * the softmax probability, over the sequence's tokens, of q_h . Khat_i /
+ * sqrt(D) (the logits from the base keys), instead of the maximum logit.
+ * Supported for 2-bit base codes with groups of 1, 2 or 4 query heads
+ * (else SF_ERR_UNSUPPORTED). */
+#define SF_DECODE_DROP_UNSELECTED 8
+#define SF_DECODE_ROWS16 16
+#define SF_DECODE_SCORE_SOFTMAX 32
+
 typedef struct sf_decode_args {
   int32_t batch;                 /* B >= 1 sequences                                    */
   const int64_t* seq_off_host;   /* host [B+1], nondecreasing, every sequence non-empty,
@@ -228,7 +268,8 @@ typedef struct sf_decode_args {
   void* workspace;               /* device scratch of sf_decode_workspace_size() bytes  */
   size_t workspace_bytes;
   int32_t flags;                 /* 0 or SF_DECODE_HIST_CLEAN | SF_DECODE_SKIP_MISSES |
-                                    SF_DECODE_MULTI_PASS                                */
+                                    SF_DECODE_MULTI_PASS | SF_DECODE_DROP_UNSELECTED |
+                                    SF_DECODE_ROWS16 | SF_DECODE_SCORE_SOFTMAX          */
   void* start_events[5];         /* optional hipEvent_t pairs (NULL = none) that time the */
   void* events[5];               /* step's kernels: start_events[k] is recorded just
                                     before kernel k is dispatched, events[k] completes
@@ -238,6 +279,8 @@ typedef struct sf_decode_args {
                                     step records pair [0] only, around its one kernel.
                                     elapsed(start, stop) is the kernel's time (create
                                     both without the system-scope fence).               */
+  const void* rows16;            /* device [2][Hkv][cap][D] fp16 K and V rows for
+                                    SF_DECODE_ROWS16, else NULL                         */
 } sf_decode_args;
 
 /* Scratch needed by sf_decode_step for this batch shape.

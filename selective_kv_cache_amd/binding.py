@@ -23,10 +23,14 @@ SF_K, SF_V = 0, 1
 SF_DECODE_HIST_CLEAN = 1
 SF_DECODE_SKIP_MISSES = 2
 SF_DECODE_MULTI_PASS = 4
+SF_DECODE_DROP_UNSELECTED = 8
+SF_DECODE_ROWS16 = 16
+SF_DECODE_SCORE_SOFTMAX = 32
+SF_QUANT_FP16_SCALES = 1
 
 c_i32, c_i64, c_vp, c_size = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
 
-EXPORTS = ("sf_status_string", "sf_last_error_string", "sf_kv_quantize", "sf_store_create",
+EXPORTS = ("sf_status_string", "sf_last_error_string", "sf_kv_quantize", "sf_kv_quantize_ex", "sf_store_create",
            "sf_store_destroy", "sf_refine_store", "sf_store_clear_cache", "sf_store_check",
            "sf_decode_workspace_size", "sf_decode_step", "sf_decode_step_noalloc",
            "sf_decode_noalloc_max_bytes", "sf_decode_check", "sf_stream_read", "sf_decode_form")
@@ -50,7 +54,7 @@ class sf_decode_args(ctypes.Structure):
                 ("v_scales", c_vp), ("cap", c_i64), ("store", c_vp), ("top_t", c_i32), ("out", c_vp),
                 ("sel_out", c_vp), ("scores_out", c_vp), ("stats", ctypes.POINTER(sf_step_stats)),
                 ("workspace", c_vp), ("workspace_bytes", c_size), ("flags", c_i32),
-                ("start_events", c_vp * 5), ("events", c_vp * 5)]
+                ("start_events", c_vp * 5), ("events", c_vp * 5), ("rows16", c_vp)]
 
 
 class SfError(RuntimeError):
@@ -81,6 +85,7 @@ def load() -> ctypes.CDLL:
     lib.sf_last_error_string.argtypes = []
     G = ctypes.POINTER(sf_geom)
     lib.sf_kv_quantize.argtypes = [G, c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp]
+    lib.sf_kv_quantize_ex.argtypes = [G, c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_i32, c_vp]
     lib.sf_store_create.argtypes = [G, c_i64, c_i32, c_i32, c_i32, ctypes.POINTER(c_vp)]
     lib.sf_store_destroy.argtypes = [c_vp]
     lib.sf_refine_store.argtypes = [c_vp, c_i32, c_vp, c_i64, c_i64, c_vp]
@@ -167,8 +172,13 @@ def geom(head_dim: int, n_q_heads: int, n_kv_heads: int, base_bits: int, refine_
 
 
 def sf_kv_quantize(g: sf_geom, x, n_tok: int, tok_begin: int, cap: int, codes, scales, refine_rows=None,
-                   stream=None) -> None:
+                   stream=None, flags: int = 0) -> None:
+    """sf_kv_quantize, or sf_kv_quantize_ex when ``flags`` is nonzero."""
     lib = load()
+    if flags:
+        _check(lib.sf_kv_quantize_ex(ctypes.byref(g), _ptr(x), n_tok, tok_begin, cap, _ptr(codes), _ptr(scales),
+                                     _ptr(refine_rows), flags, _stream(stream)), "sf_kv_quantize_ex")
+        return
     _check(lib.sf_kv_quantize(ctypes.byref(g), _ptr(x), n_tok, tok_begin, cap, _ptr(codes), _ptr(scales),
                               _ptr(refine_rows), _stream(stream)), "sf_kv_quantize")
 
@@ -235,10 +245,11 @@ def sf_decode_noalloc_max_bytes() -> int:
 def sf_decode_step(g: sf_geom, *, seq_off_host: Sequence[int], seq_off_dev, q, k_codes, k_scales, v_codes,
                    v_scales, cap: int, store: Optional[int], top_t: int, out, workspace, sel_out=None,
                    scores_out=None, want_stats: bool = False, events=None, stream=None, flags: int = 0,
-                   noalloc: bool = False):
+                   noalloc: bool = False, rows16=None):
     """One decode step; returns the step statistics as a dict when asked.
     ``noalloc``: sf_decode_step_noalloc (the library's scratch; ``workspace``
-    may then be None)."""
+    may then be None).  ``rows16``: the [2][Hkv][cap][D] fp16 rows for
+    SF_DECODE_ROWS16."""
     off = np.ascontiguousarray(np.asarray(seq_off_host, dtype=np.int64))
     a = sf_decode_args()
     a.batch = len(off) - 1
@@ -253,6 +264,7 @@ def sf_decode_step(g: sf_geom, *, seq_off_host: Sequence[int], seq_off_dev, q, k
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     a.flags = flags
+    a.rows16 = _ptr(rows16)
     if events is not None:
         # (start, stop) pairs of score, scan, resolve, attention, combine; a
         # stop alone, or None, allowed

@@ -182,7 +182,7 @@ __global__ void __launch_bounds__(256) combine(DecodeParams p) {
     const int lane = tid & 63;
     const bool in = lane < s;
     const int64_t n = in ? p.seq_off[lane + 1] - p.seq_off[lane] : 0;
-    const uint32_t nb = in ? (uint32_t)((n + p.split - 1) / p.split) : 0u;
+    const uint32_t nb = in && !p.drop ? (uint32_t)((n + p.split - 1) / p.split) : 0u;
     const uint32_t ns = in && p.use_refine ? (uint32_t)(((n < p.top_t ? n : p.top_t) + p.sel_blk_tok - 1) / p.sel_blk_tok)
                                           : 0u;
     bb = (int)__builtin_amdgcn_readlane(wave_inclusive_scan(nb), 63);
@@ -190,12 +190,12 @@ __global__ void __launch_bounds__(256) combine(DecodeParams p) {
   } else {
     for (int i = 0; i < s; ++i) {
       const int64_t n = seq_at(p, i + 1) - seq_at(p, i);
-      bb += (int)((n + p.split - 1) / p.split);
+      if (!p.drop) bb += (int)((n + p.split - 1) / p.split);
       if (p.use_refine) sb += (int)(((n < p.top_t ? n : p.top_t) + p.sel_blk_tok - 1) / p.sel_blk_tok);
     }
   }
   const int64_t n = seq_at(p, s + 1) - seq_at(p, s);
-  const int nb = (int)((n + p.split - 1) / p.split);
+  const int nb = p.drop ? 0 : (int)((n + p.split - 1) / p.split);   // left out: no base partials
   const int ns = p.use_refine ? (int)(((n < p.top_t ? n : p.top_t) + p.sel_blk_tok - 1) / p.sel_blk_tok) : 0;
   const int64_t stride = (int64_t)p.grp * kPartStride;
   const float* base = p.part + (int64_t)kvh * (p.n_sel_blk + p.n_split) * stride + hg * kPartStride;

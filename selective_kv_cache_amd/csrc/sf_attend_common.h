@@ -380,10 +380,97 @@ __device__ inline void selected_block(const DecodeParams& p, int blk, int kvh, u
   write_partial_shared<G, NW>(part, s.mall, s.lw, s.accw);
 }
 
+// Selected tokens of one (sequence, KV head) with their complete 16-bit K
+// and V rows (the comparison variant of page "StrataFlux -- Selective
+// precision streaming -- What does it mean?", table row "SpeCache (16-bit
+// fetching)"): the work-group takes p.sel_blk_tok tokens of the selection,
+// wavefront w the tokens w, w + NW, ...; lane l holds elements 2l and 2l + 1.
+// The same partial as selected_block (natural-log maximum shared by the
+// work-group).
+template <int G, int NW>
+struct Sel16Lds {
+  float lg[kSelBlkTok][G];
+  float mred[NW][G], mall[NW][G], lw[NW][G];
+  float accw[NW][G][kHeadDim];
+};
+
+template <int G, int NW, bool Batched = false>
+__device__ inline void selected16_block(const DecodeParams& p, int blk, int kvh, uint8_t* smem) {
+  using Lds = Sel16Lds<G, NW>;
+  Lds& s = *reinterpret_cast<Lds*>(smem);
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  int64_t lo, hi;
+  int first;
+  const int seq = locate_unit<Batched>(p, p.sel_blk_tok, blk, true, lo, hi, first);
+  const int64_t a = seq_at(p, seq);
+  const int64_t sk = (int64_t)seq * p.hkv + kvh;
+  const int n = (int)(hi - lo);                     // <= p.sel_blk_tok <= kSelBlkTok
+  const float* qg = p.q + ((int64_t)seq * p.hq + kvh * G) * kHeadDim;
+  float q0[G], q1[G], mloc[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    q0[h] = qg[h * kHeadDim + 2 * lane];
+    q1[h] = qg[h * kHeadDim + 2 * lane + 1];
+    mloc[h] = -INFINITY;
+  }
+  auto token = [&](int j) {
+    const int32_t e = p.sel[sk * p.top_t + lo + j];
+    return a + (e >= 0 ? e : ~e);
+  };
+  for (int j = wid; j < n; j += NW) {
+    const _Float16* kr = p.rows16 + ((int64_t)kvh * p.cap + token(j)) * kHeadDim;
+    const float k0 = (float)kr[2 * lane], k1 = (float)kr[2 * lane + 1];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float l = wave_sum_dpp(fmaf(q0[h], k0, q1[h] * k1)) * kRsqrtD;
+      if (lane == 0) s.lg[j][h] = l;
+      mloc[h] = fmaxf(mloc[h], l);
+    }
+  }
+  if (lane == 0)
+#pragma unroll
+    for (int h = 0; h < G; ++h) s.mred[wid][h] = mloc[h];
+  __syncthreads();
+  float M[G], l[G], acc[G][2];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    M[h] = s.mred[0][h];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M[h] = fmaxf(M[h], s.mred[w][h]);
+    l[h] = acc[h][0] = acc[h][1] = 0.f;
+  }
+  for (int j = wid; j < n; j += NW) {
+    const _Float16* vr = p.rows16 + (((int64_t)p.hkv + kvh) * p.cap + token(j)) * kHeadDim;
+    const float v0 = (float)vr[2 * lane], v1 = (float)vr[2 * lane + 1];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float w = expf(s.lg[j][h] - M[h]);
+      l[h] += w;
+      acc[h][0] = fmaf(w, v0, acc[h][0]);
+      acc[h][1] = fmaf(w, v1, acc[h][1]);
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    s.accw[wid][h][2 * lane] = acc[h][0];
+    s.accw[wid][h][2 * lane + 1] = acc[h][1];
+    if (lane == 0) {
+      s.lw[wid][h] = l[h];
+      s.mall[wid][h] = M[h];
+    }
+  }
+  __syncthreads();
+  float* part = p.part + ((int64_t)kvh * (p.n_sel_blk + p.n_split) + blk) * G * kPartStride;
+  write_partial_shared<G, NW>(part, s.mall, s.lw, s.accw);
+}
+
 // The selected block's shape chosen on the host: p.sel_blk_tok = NW TPW.
 template <int BB, int G, int NW, bool LG, bool Batched = false>
 __device__ inline void selected_block_any(const DecodeParams& p, int blk, int kvh, uint8_t* smem) {
-  if (p.sel_blk_tok == NW * 4)
+  static_assert(sizeof(Sel16Lds<G, NW>) <= sizeof(SelLds<BB, G, NW, 4>), "fits the selected blocks' LDS");
+  if (p.rows16)
+    selected16_block<G, NW, Batched>(p, blk, kvh, smem);
+  else if (p.sel_blk_tok == NW * 4)
     selected_block<BB, G, NW, LG, 4, Batched>(p, blk, kvh, smem);
   else
     selected_block<BB, G, NW, LG, 16, Batched>(p, blk, kvh, smem);

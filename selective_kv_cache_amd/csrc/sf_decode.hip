@@ -104,6 +104,9 @@ Carve carve(const sf_geom& g, int32_t batch, int64_t total_tokens, int64_t max_s
   c.bitmap = at; at += align256((size_t)batch * hkv * bm_words * 4);
   c.sel = at; at += align256((size_t)batch * hkv * t * 4);
   c.part = at; at += align256((size_t)hkv * n_part_bound * grp * kPartStride * 4);
+  // the summed-probability score's (maximum, sum) per score unit (units of
+  // at least 256 tokens)
+  c.sstat = at; at += align256((size_t)hkv * (total_tokens / 256 + batch) * grp * 8);
   c.total = at;
   return c;
 }
@@ -138,7 +141,8 @@ using namespace sfk;
 static int32_t fused_plan(const sf_geom& g, const sf_decode_args& a, bool refine, int32_t* n_units) {
   const int32_t grp = g.n_q_heads / g.n_kv_heads;
   *n_units = 0;
-  if ((a.flags & (SF_DECODE_MULTI_PASS | SF_DECODE_SKIP_MISSES)) || g.base_bits != 2 ||
+  if ((a.flags & (SF_DECODE_MULTI_PASS | SF_DECODE_SKIP_MISSES | SF_DECODE_DROP_UNSELECTED | SF_DECODE_ROWS16 |
+                  SF_DECODE_SCORE_SOFTMAX)) || g.base_bits != 2 ||
       !(grp == 1 || grp == 2 || grp == 4) || (refine && a.store->tier == SF_TIER_HOST_PINNED))
     return 0;
   const int cap = fused_capacity(grp, a.batch > 1);
@@ -199,8 +203,14 @@ sf_status sf_decode_step_ws(const sf_geom* geom, const sf_decode_args* a, void* 
   if (s != SF_OK) return s;
   if (!a || a->batch <= 0 || !a->seq_off_host || !a->seq_off_dev || !a->q || !a->k_codes ||
       !a->k_scales || !a->v_codes || !a->v_scales || !a->out || !workspace || a->cap <= 0 ||
-      a->top_t < 0 || (a->flags & ~(SF_DECODE_HIST_CLEAN | SF_DECODE_SKIP_MISSES | SF_DECODE_MULTI_PASS)) != 0)
+      a->top_t < 0 ||
+      (a->flags & ~(SF_DECODE_HIST_CLEAN | SF_DECODE_SKIP_MISSES | SF_DECODE_MULTI_PASS | SF_DECODE_DROP_UNSELECTED |
+                    SF_DECODE_ROWS16 | SF_DECODE_SCORE_SOFTMAX)) != 0)
     return SF_ERR_INVALID_ARG;
+  const bool rows16 = (a->flags & SF_DECODE_ROWS16) != 0;
+  const bool drop = (a->flags & SF_DECODE_DROP_UNSELECTED) != 0;
+  const bool smax = (a->flags & SF_DECODE_SCORE_SOFTMAX) != 0;
+  if (rows16 != (a->rows16 != nullptr) || (rows16 && a->top_t <= 0)) return SF_ERR_INVALID_ARG;
   const int32_t B = a->batch;
   const int64_t* off = a->seq_off_host;
   if (off[0] < 0) return SF_ERR_INVALID_ARG;
@@ -213,7 +223,11 @@ sf_status sf_decode_step_ws(const sf_geom* geom, const sf_decode_args* a, void* 
   if (off[B] > a->cap) return SF_ERR_INVALID_ARG;
   if (max_seq > (int64_t)kMaxSelChunks * kSelChunk) return SF_ERR_UNSUPPORTED;
   const int64_t total = off[B] - off[0];
-  const bool refine = a->top_t > 0 && geom->refine_bits > 0;
+  // refinement codes read for the selection (not with 16-bit rows); the
+  // selected tokens' work-groups run with either
+  const bool refine = a->top_t > 0 && geom->refine_bits > 0 && !rows16;
+  const bool sel_work = refine || rows16;
+  if (drop && !sel_work) return SF_ERR_INVALID_ARG;   // the selection must take part
   if (refine) {
     if (!a->store) return SF_ERR_INVALID_ARG;
     const sf_store_s* st = a->store;
@@ -230,6 +244,7 @@ sf_status sf_decode_step_ws(const sf_geom* geom, const sf_decode_args* a, void* 
   // the other 4: about 4096 wavefronts either way
   const int32_t grp = geom->n_q_heads / geom->n_kv_heads;
   const bool score_mfma = geom->base_bits == 2 && (grp == 1 || grp == 2 || grp == 4);
+  if (smax && !score_mfma) return SF_ERR_UNSUPPORTED;   // needs the score pass's per-head logits
   const int32_t score_split = choose_score_split(total, geom->n_kv_heads, score_mfma ? 4096 / kScoreWaves : 1024);
   const Carve c = carve(*geom, B, total, max_seq, a->top_t, part_bound(total, B, split, a->top_t));
   if (workspace_bytes < c.total) return SF_ERR_INVALID_ARG;
@@ -241,7 +256,7 @@ sf_status sf_decode_step_ws(const sf_geom* geom, const sf_decode_args* a, void* 
     n_split += (int32_t)((n + split - 1) / split);
     n_score += (int32_t)((n + score_split - 1) / score_split);
     n_sel += (int32_t)((n + kSelChunk - 1) / kSelChunk);
-    if (refine) n_small += (int32_t)((std::min<int64_t>(n, a->top_t) + kSelBlkTokMin - 1) / kSelBlkTokMin);
+    if (sel_work) n_small += (int32_t)((std::min<int64_t>(n, a->top_t) + kSelBlkTokMin - 1) / kSelBlkTokMin);
   }
   static_assert(kAttendWaves == 4 && kSelBlkTokMin == 4 * 4 && kSelBlkTok == 4 * 16,
                 "selected blocks: 4 wavefronts of 4 or 16 tokens");
@@ -251,7 +266,7 @@ sf_status sf_decode_step_ws(const sf_geom* geom, const sf_decode_args* a, void* 
   const int32_t sel_blk_tok =
       (int64_t)(n_small + n_split) * geom->n_kv_heads <= 3 * (int64_t)cus ? kSelBlkTokMin : kSelBlkTok;
   int32_t n_sel_blk = 0;
-  for (int i = 0; i < B && refine; ++i)
+  for (int i = 0; i < B && sel_work; ++i)
     n_sel_blk += (int32_t)((std::min<int64_t>(off[i + 1] - off[i], a->top_t) + sel_blk_tok - 1) / sel_blk_tok);
   if (max_seq / split + 1 + (a->top_t + sel_blk_tok - 1) / sel_blk_tok > kCombineMax) return SF_ERR_UNSUPPORTED;
 
@@ -270,7 +285,11 @@ sf_status sf_decode_step_ws(const sf_geom* geom, const sf_decode_args* a, void* 
   p.n_score_split = n_score;
   p.n_split = n_split;
   p.bm_words = (int32_t)(((max_seq + kSelThreads - 1) / kSelThreads) * (kSelThreads / 32));
-  p.use_refine = refine ? 1 : 0;
+  p.use_refine = sel_work ? 1 : 0;
+  p.drop = drop ? 1 : 0;
+  p.score_mode = smax ? 1 : 0;
+  p.rows16 = static_cast<const _Float16*>(a->rows16);
+  p.sstat = reinterpret_cast<float2*>(ws + c.sstat);
   p.n_sel_blk = n_sel_blk;
   p.sel_blk_tok = sel_blk_tok;
   p.cnt_stride = (int32_t)((max_seq + kSelChunk - 1) / kSelChunk) + 2;   // + level-1 boundary
@@ -339,6 +358,10 @@ sf_status sf_decode_step_ws(const sf_geom* geom, const sf_decode_args* a, void* 
   if (!launch_score(p, dim3(n_score, p.hkv), hs, stop(0)))
     return SF_ERR_UNSUPPORTED;
   SF_LAUNCH_CHECK("score");
+  if (smax) {
+    if (!launch_softmax_scores(p, dim3(n_score, p.hkv), hs)) return SF_ERR_UNSUPPORTED;
+    SF_LAUNCH_CHECK("softmax_scores");
+  }
   if (a->top_t > 0) {
     launch_select(p, dim3(n_sel, p.hkv), hs, stop(1), stop(2));
     SF_LAUNCH_CHECK("select_top_t");
@@ -354,7 +377,7 @@ sf_status sf_decode_step_ws(const sf_geom* geom, const sf_decode_args* a, void* 
     if (s != SF_OK) return s;
     if (a->stats) a->stats->hits = a->stats->selected - a->stats->misses;
   }
-  if (!launch_attend(p, dim3(n_sel_blk + n_split, p.hkv), hs, stop(3)))
+  if (!launch_attend(p, dim3(n_sel_blk + (drop ? 0 : n_split), p.hkv), hs, stop(3)))
     return SF_ERR_UNSUPPORTED;
   SF_LAUNCH_CHECK("attend");
   launch_combine(p, hs, stop(4));

@@ -40,6 +40,11 @@ struct DecodeParams {
   int32_t* store_err;         // host tier: the store's error word (inconsistent cache tables)
   int32_t slots, rb;
   float* out;          // [batch][hq][D]
+  // comparison variants (five-kernel form only)
+  int32_t drop;               // the unselected tokens take no part (no base splits)
+  int32_t score_mode;         // 0: maximum logit over the group; 1: summed softmax probability
+  const _Float16* rows16;     // [2][hkv][cap][D] fp16 K and V rows of the selected tokens, or NULL
+  float2* sstat;              // [hkv][n_score_split][grp] (maximum, sum) of 2^logit per score unit
   // single-launch (fused) path
   int32_t fr;          // tokens per work-group
   int32_t fscores;     // write the scores to `scores` (the caller asked for them)
@@ -328,6 +333,7 @@ constexpr int kFusedRmax = 4096;        // tokens per work-group at most
 constexpr int kFusedMinR = 256;         // and at least (a multiple of it)
 constexpr int kFusedMaxRanges = 512;    // work-groups per (sequence, KV head) at most
 bool launch_fused(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev);
+bool launch_softmax_scores(const DecodeParams& p, dim3 grid, hipStream_t st);   // the score variant's two kernels
 int fused_capacity(int grp, bool batched);   // co-resident work-groups on the device
 
 }  // namespace sfk

@@ -27,7 +27,7 @@ __host__ __device__ inline uint32_t score_key(float s) {
 
 // Workspace carve-out (byte offsets from the workspace base).
 struct Carve {
-  size_t status, hist, zero_end, ftie, scores, logits, counters, cand, bitmap, sel, part, total;
+  size_t status, hist, zero_end, ftie, scores, logits, counters, cand, bitmap, sel, part, sstat, total;
 };
 
 int32_t choose_split(int64_t total_tokens, int32_t n_kv_heads, int32_t groups);

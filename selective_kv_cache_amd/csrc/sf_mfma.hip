@@ -78,7 +78,8 @@ __global__ void __launch_bounds__(64 * NW) score_mfma(DecodeParams p) {
     bdma16(rK, oK, c * 1024u, st.k);
     bdma4(rS, oS, c * 256u, st.ks);
   };
-  const bool hist = p.top_t > 0;   // no selection, no histogram
+  // no selection, no histogram; the summed-probability score builds its own
+  const bool hist = p.top_t > 0 && p.score_mode == 0;
   for (int i = tid; i < kHistBins; i += 64 * NW) lhist[i] = 0u;
 #pragma unroll
   for (int k = 0; k < kSRing - 1; ++k)
@@ -154,6 +155,137 @@ __global__ void __launch_bounds__(64 * NW) score_mfma(DecodeParams p) {
     const uint32_t c = lhist[i];
     if (c) atomicAdd(&gh[i], c);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Score variant: the attention a token receives (page "StrataFlux --
+// Selective precision streaming -- What does it mean?", paragraph "Which
+// tiles count ..."), the sum over the group of each query head's softmax
+// probability over the sequence's tokens, from the logits (log2 units) the
+// score pass left.  softmax_stats: per score unit, each head's maximum and
+// sum of 2^(logit - maximum); softmax_scores: the sequence's normalisers
+// from its units' pairs, then the unit's scores and the level-1 histogram.
+// One work-group of 256 threads per (score unit, KV head), as the score pass.
+// ---------------------------------------------------------------------------
+
+template <int N>
+__device__ inline void block_max_sum(float (&m)[N], float* red, bool take_max) {
+  // every thread ends with the block's maximum (take_max) or sum of each value
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float v = take_max ? wave_max_dpp(m[i]) : wave_sum_dpp(m[i]);
+    if (lane == 0) red[wid * N + i] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    float v = red[i];
+    for (int w = 1; w < (int)(blockDim.x >> 6); ++w) v = take_max ? fmaxf(v, red[w * N + i]) : v + red[w * N + i];
+    m[i] = v;
+  }
+  __syncthreads();
+}
+
+template <int G, bool Batched>
+__global__ void __launch_bounds__(256) softmax_stats(DecodeParams p) {
+  __shared__ float red[4 * G];
+  const int kvh = blockIdx.y;
+  int64_t lo, hi;
+  int first;
+  const int seq = locate_unit<Batched>(p, p.score_split, blockIdx.x, false, lo, hi, first);
+  const int64_t a = seq_at(p, seq);
+  const float* lg = p.logits + ((int64_t)kvh * p.ntot + (a - p.off0) + lo) * G;
+  const int n = (int)(hi - lo);
+  float m[G], z[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) m[h] = -INFINITY;
+  for (int i = threadIdx.x; i < n; i += blockDim.x)
+#pragma unroll
+    for (int h = 0; h < G; ++h) m[h] = fmaxf(m[h], lg[i * G + h]);
+  block_max_sum<G>(m, red, true);
+#pragma unroll
+  for (int h = 0; h < G; ++h) z[h] = 0.f;
+  for (int i = threadIdx.x; i < n; i += blockDim.x)
+#pragma unroll
+    for (int h = 0; h < G; ++h) z[h] += __builtin_amdgcn_exp2f(lg[i * G + h] - m[h]);
+  block_max_sum<G>(z, red, false);
+  if (threadIdx.x == 0)
+#pragma unroll
+    for (int h = 0; h < G; ++h) p.sstat[((int64_t)kvh * p.n_score_split + blockIdx.x) * G + h] = make_float2(m[h], z[h]);
+}
+
+template <int G, bool Batched>
+__global__ void __launch_bounds__(256) softmax_scores(DecodeParams p) {
+  __shared__ float red[4 * G];
+  __shared__ uint32_t lhist[kHistBins];
+  const int kvh = blockIdx.y;
+  int64_t lo, hi;
+  int first;
+  const int seq = locate_unit<Batched>(p, p.score_split, blockIdx.x, false, lo, hi, first);
+  const int64_t a = seq_at(p, seq);
+  const int64_t n_s = seq_at(p, seq + 1) - a;
+  const int nu = (int)((n_s + p.score_split - 1) / p.score_split);   // the sequence's units
+  const float2* st = p.sstat + ((int64_t)kvh * p.n_score_split + first) * G;
+  for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) lhist[i] = 0u;
+  // the normalisers: M = max of the units' maxima, Z = sum of z_u 2^(m_u - M)
+  float M[G], Z[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) M[h] = -INFINITY;
+  for (int u = threadIdx.x; u < nu; u += blockDim.x)
+#pragma unroll
+    for (int h = 0; h < G; ++h) M[h] = fmaxf(M[h], st[u * G + h].x);
+  block_max_sum<G>(M, red, true);
+#pragma unroll
+  for (int h = 0; h < G; ++h) Z[h] = 0.f;
+  for (int u = threadIdx.x; u < nu; u += blockDim.x)
+#pragma unroll
+    for (int h = 0; h < G; ++h) Z[h] += st[u * G + h].y * __builtin_amdgcn_exp2f(st[u * G + h].x - M[h]);
+  block_max_sum<G>(Z, red, false);
+  float rz[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) rz[h] = 1.0f / Z[h];
+  const float* lg = p.logits + ((int64_t)kvh * p.ntot + (a - p.off0) + lo) * G;
+  float* scores = p.scores + (int64_t)kvh * p.ntot + (a - p.off0) + lo;
+  const int n = (int)(hi - lo);
+  const bool hist = p.top_t > 0;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    float sc = 0.f;
+#pragma unroll
+    for (int h = 0; h < G; ++h) sc = fmaf(__builtin_amdgcn_exp2f(lg[i * G + h] - M[h]), rz[h], sc);
+    scores[i] = sc;
+    if (hist) atomicAdd(&lhist[score_key(sc) >> (32 - kHistBits)], 1u);
+  }
+  if (!hist) return;
+  __syncthreads();
+  uint32_t* gh = p.hist + ((int64_t)seq * p.hkv + kvh) * kHistBins;   // level-1 histogram
+  for (int i = threadIdx.x; i < kHistBins; i += blockDim.x) {
+    const uint32_t c = lhist[i];
+    if (c) atomicAdd(&gh[i], c);
+  }
+}
+
+template <bool Batched>
+static bool launch_softmax_scores_b(const DecodeParams& p, dim3 grid, hipStream_t st) {
+  switch (p.grp) {
+    case 1:
+      hipLaunchKernelGGL((softmax_stats<1, Batched>), grid, dim3(256), 0, st, p);
+      hipLaunchKernelGGL((softmax_scores<1, Batched>), grid, dim3(256), 0, st, p);
+      return true;
+    case 2:
+      hipLaunchKernelGGL((softmax_stats<2, Batched>), grid, dim3(256), 0, st, p);
+      hipLaunchKernelGGL((softmax_scores<2, Batched>), grid, dim3(256), 0, st, p);
+      return true;
+    case 4:
+      hipLaunchKernelGGL((softmax_stats<4, Batched>), grid, dim3(256), 0, st, p);
+      hipLaunchKernelGGL((softmax_scores<4, Batched>), grid, dim3(256), 0, st, p);
+      return true;
+  }
+  return false;
+}
+
+bool launch_softmax_scores(const DecodeParams& p, dim3 grid, hipStream_t st) {
+  return p.batch > 1 ? launch_softmax_scores_b<true>(p, grid, st) : launch_softmax_scores_b<false>(p, grid, st);
 }
 
 // The base pass streams its split through a per-wavefront ring of LDS stages

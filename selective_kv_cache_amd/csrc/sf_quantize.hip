@@ -39,10 +39,28 @@ __device__ inline void or_bits(uint32_t* words, int pos, uint32_t val, int nbits
 
 constexpr int kRowsPerBlock = 4;
 
+// The largest fp16 value <= x and the smallest >= x (x finite, within the
+// fp16 range), as fp32: the nearest fp16, moved one step when it lies on the
+// wrong side (one step down from +0 is the negative smallest subnormal).
+__device__ inline float fp16_down(float x) {
+  const _Float16 h = (_Float16)x;
+  if ((float)h <= x) return (float)h;
+  uint16_t u = __builtin_bit_cast(uint16_t, h);
+  u = (u & 0x8000u) ? (uint16_t)(u + 1u) : (u == 0u ? (uint16_t)0x8001u : (uint16_t)(u - 1u));
+  return (float)__builtin_bit_cast(_Float16, u);
+}
+__device__ inline float fp16_up(float x) {
+  const _Float16 h = (_Float16)x;
+  if ((float)h >= x) return (float)h;
+  uint16_t u = __builtin_bit_cast(uint16_t, h);
+  u = (u & 0x8000u) ? (u == 0x8000u ? (uint16_t)1u : (uint16_t)(u - 1u)) : (uint16_t)(u + 1u);
+  return (float)__builtin_bit_cast(_Float16, u);
+}
+
 __global__ void __launch_bounds__(256)
 quantize_rows_kernel(const float* __restrict__ x, int64_t n_rows, int hkv, int64_t n_tok,
                      int64_t tok_begin, int64_t cap, int b, int r, uint8_t* __restrict__ codes,
-                     float* __restrict__ scales, uint8_t* __restrict__ refine_rows) {
+                     float* __restrict__ scales, uint8_t* __restrict__ refine_rows, int fp16_scales) {
   __shared__ uint32_t words[kRowsPerBlock][16 + 33];   // 4b <= 16 base words, 4r <= 32 refine words
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
@@ -59,14 +77,19 @@ quantize_rows_kernel(const float* __restrict__ x, int64_t n_rows, int hkv, int64
     mx = fmaxf(mx, __shfl_xor(mx, o));
   }
   const int f = b + r;
-  const float range = __fsub_rn(mx, mn);
-  const float delta = __fmul_rn(range, __builtin_ldexpf(1.0f, -b));   // exact power-of-two scaling
-  const float delta_f = __fmul_rn(range, __builtin_ldexpf(1.0f, -f));
+  // fp16 scales: lo rounded down, delta from the stored lo rounded up (the
+  // stored range reaches the maximum); else the fp32 row minimum and range
+  const float lo = fp16_scales ? fp16_down(mn) : mn;
+  const float range = __fsub_rn(mx, lo);
+  const float delta = fp16_scales ? fp16_up(__fmul_rn(range, __builtin_ldexpf(1.0f, -b)))
+                                  : __fmul_rn(range, __builtin_ldexpf(1.0f, -b));   // exact power-of-two scaling
+  const float delta_f = fp16_scales ? __fmul_rn(delta, __builtin_ldexpf(1.0f, -r))
+                                    : __fmul_rn(range, __builtin_ldexpf(1.0f, -f));
   const uint32_t qmax = (1u << f) - 1u;
   uint32_t q0 = 0, q1 = 0;
   if (delta_f != 0.0f) {
-    const float u0 = __fdiv_rn(__fsub_rn(v.x, mn), delta_f);
-    const float u1 = __fdiv_rn(__fsub_rn(v.y, mn), delta_f);
+    const float u0 = __fdiv_rn(__fsub_rn(v.x, lo), delta_f);   // >= 0: lo <= every element
+    const float u1 = __fdiv_rn(__fsub_rn(v.y, lo), delta_f);
     q0 = min((uint32_t)floorf(u0), qmax);
     q1 = min((uint32_t)floorf(u1), qmax);
   }
@@ -91,7 +114,7 @@ quantize_rows_kernel(const float* __restrict__ x, int64_t n_rows, int hkv, int64
   }
   if (lane == 0) {
     float2* s = reinterpret_cast<float2*>(scales) + ((int64_t)h * cap + tok_begin + t);
-    *s = make_float2(mn, delta);
+    *s = make_float2(lo, delta);
   }
 }
 
@@ -129,10 +152,11 @@ sf_status sf_check_geom(const sf_geom* g) {
   return SF_OK;
 }
 
-extern "C" sf_status sf_kv_quantize(const sf_geom* geom, const float* x, int64_t n_tok,
-                                    int64_t tok_begin, int64_t cap, uint8_t* codes, float* scales,
-                                    uint8_t* refine_rows, void* stream) {
+extern "C" sf_status sf_kv_quantize_ex(const sf_geom* geom, const float* x, int64_t n_tok, int64_t tok_begin,
+                                       int64_t cap, uint8_t* codes, float* scales, uint8_t* refine_rows,
+                                       int32_t flags, void* stream) {
   clear_error();
+  if (flags & ~SF_QUANT_FP16_SCALES) return SF_ERR_INVALID_ARG;
   sf_status st = sf_check_geom(geom);
   if (st != SF_OK) return st;
   if (n_tok < 0 || tok_begin < 0 || cap <= 0 || tok_begin + n_tok > cap) return SF_ERR_INVALID_ARG;
@@ -147,7 +171,13 @@ extern "C" sf_status sf_kv_quantize(const sf_geom* geom, const float* x, int64_t
   if (blocks > 0x7fffffffLL) return SF_ERR_UNSUPPORTED;
   hipLaunchKernelGGL(quantize_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
                      x, n_rows, geom->n_kv_heads, n_tok, tok_begin, cap, geom->base_bits,
-                     geom->refine_bits, codes, scales, refine_rows);
+                     geom->refine_bits, codes, scales, refine_rows, (flags & SF_QUANT_FP16_SCALES) ? 1 : 0);
   SF_LAUNCH_CHECK("quantize_rows_kernel");
   return SF_OK;
+}
+
+extern "C" sf_status sf_kv_quantize(const sf_geom* geom, const float* x, int64_t n_tok,
+                                    int64_t tok_begin, int64_t cap, uint8_t* codes, float* scales,
+                                    uint8_t* refine_rows, void* stream) {
+  return sf_kv_quantize_ex(geom, x, n_tok, tok_begin, cap, codes, scales, refine_rows, 0, stream);
 }

@@ -18,8 +18,12 @@ class LayerCache:
     refinement store.  ``tier`` is binding.SF_TIER_DEVICE or SF_TIER_HOST_PINNED."""
 
     def __init__(self, g: B.sf_geom, cap: int, device="cuda", tier: int = B.SF_TIER_DEVICE,
-                 max_seqs: int = 1, cache_slots: int = 0):
+                 max_seqs: int = 1, cache_slots: int = 0, fp16_scales: bool = False, rows16: bool = False):
+        """``fp16_scales``: scales quantized as fp16 values (SF_QUANT_FP16_SCALES);
+        ``rows16``: also keep the appended K and V rows as fp16 ([2][Hkv][cap][D],
+        the complete 16-bit entries the SF_DECODE_ROWS16 comparison fetches)."""
         self.g, self.cap, self.device, self.tier = g, cap, torch.device(device), tier
+        self.quant_flags = B.SF_QUANT_FP16_SCALES if fp16_scales else 0
         hkv, d, b, r = g.n_kv_heads, g.head_dim, g.base_bits, g.refine_bits
         mk = lambda shape, dt: torch.empty(shape, dtype=dt, device=self.device)
         self.k_codes = mk((hkv, cap, d * b // 8), torch.uint8)
@@ -27,6 +31,7 @@ class LayerCache:
         self.k_scales = mk((hkv, cap, 2), torch.float32)
         self.v_scales = mk((hkv, cap, 2), torch.float32)
         self.store = B.sf_store_create(g, cap, max_seqs, tier, cache_slots) if r > 0 else None
+        self.rows16 = mk((2, hkv, cap, d), torch.float16) if rows16 else None
 
     def append(self, k: torch.Tensor, v: torch.Tensor, tok_begin: int, keep_refine: bool = False):
         """Quantize token-major [n][Hkv][D] fp32 K and V into tokens
@@ -40,9 +45,11 @@ class LayerCache:
                                         (v, self.v_codes, self.v_scales, B.SF_V)):
             x = x.contiguous()
             rr = torch.empty((hkv, n, d * r // 8), dtype=torch.uint8, device=self.device) if r else None
-            B.sf_kv_quantize(self.g, x, n, tok_begin, self.cap, codes, scales, rr)
+            B.sf_kv_quantize(self.g, x, n, tok_begin, self.cap, codes, scales, rr, flags=self.quant_flags)
             if r:
                 B.sf_refine_store(self.store, which, rr, tok_begin, n)
+            if self.rows16 is not None:
+                self.rows16[which, :, tok_begin:tok_begin + n] = x.transpose(0, 1).to(torch.float16)
             out.append(rr)
         return tuple(out) if keep_refine else None
 
@@ -111,10 +118,12 @@ class Decoder:
     def step(self, cache: LayerCache, q: torch.Tensor, out: Optional[torch.Tensor] = None,
              sel_out: Optional[torch.Tensor] = None, scores_out: Optional[torch.Tensor] = None,
              want_stats: bool = False, events=None, stream=None, skip_misses: bool = False,
-             multi_pass: bool = False):
+             multi_pass: bool = False, variant: int = 0):
         """One decode step of one layer.  ``skip_misses``: policy "skip" on
         a refinement-cache miss (SF_DECODE_SKIP_MISSES); ``multi_pass``: the
-        five-kernel form even where the single launch applies."""
+        five-kernel form even where the single launch applies; ``variant``:
+        SF_DECODE_DROP_UNSELECTED | SF_DECODE_ROWS16 | SF_DECODE_SCORE_SOFTMAX
+        (the 16-bit rows are the cache's)."""
         if out is None:
             out = torch.empty((self.batch, self.g.n_q_heads, self.g.head_dim), dtype=torch.float32,
                               device=self.device)
@@ -123,12 +132,14 @@ class Decoder:
             flags |= B.SF_DECODE_SKIP_MISSES
         if multi_pass:
             flags |= B.SF_DECODE_MULTI_PASS
+        flags |= variant
         self._hist_clean = False
         st = B.sf_decode_step(self.g, seq_off_host=self.seq_off, seq_off_dev=self.seq_off_dev, q=q,
                               k_codes=cache.k_codes, k_scales=cache.k_scales, v_codes=cache.v_codes,
                               v_scales=cache.v_scales, cap=cache.cap, store=cache.store,
                               top_t=self.top_t, out=out, workspace=self.workspace, sel_out=sel_out,
                               scores_out=scores_out, want_stats=want_stats, events=events,
-                              stream=stream, flags=flags)
+                              stream=stream, flags=flags,
+                              rows16=cache.rows16 if variant & B.SF_DECODE_ROWS16 else None)
         self._hist_clean = True
         return (out, st) if want_stats else out
