@@ -241,3 +241,15 @@ MUTATIONS = [
 def test_pins_catch_planted_mistakes(monkeypatch, name, fn):
     monkeypatch.setattr(V, name, fn)
     assert _fails_some_pin(), f"no pin failed with {fn.__name__} planted in {name}"
+
+
+def test_accuracy_study_runs_small():
+    # the study script at a small size: every KL is finite and >= 0, and
+    # refining T tokens improves on the base-only cache
+    import dataclasses
+    import accuracy_study as S
+    from selective_kv_cache_amd import workloads as W
+    w = dataclasses.replace(W.WORKLOADS["llama8b_32k"], top_t=64)
+    res = S.study(w, 4, layers=(0,), heads=(0, 1), n_tok=4096)
+    assert all(np.isfinite(v) and v >= 0 for v in res.values())
+    assert res["nested"] < res["base_only"]
