@@ -114,6 +114,65 @@ sf_status sf_kv_quantize_ex(const sf_geom* geom, const float* x, int64_t n_tok, 
                             uint8_t* codes, float* scales, uint8_t* refine_rows, int32_t flags, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Weight-side refinement GEMV (page "StrataFlux -- Selective precision
+ * streaming -- What does it mean?", paragraph "Which tiles count ...": the
+ * input channels of a projection are split into chunks of 1,024 and the k
+ * channels with the largest activation magnitude in each chunk are refined at
+ * this step; paragraph "What travels over the link ...": the refinement bits
+ * subdivide the bin of the resident code; the worked example: k = 32, 4-bit
+ * refinements of 3-bit weights).
+ *
+ * y = W x with W [m][k]: along each output row, groups of 128 input channels
+ * are quantized with the nested quantizer of sf_kv_quantize (b-bit base code,
+ * r refinement bits, fp32 (lo, delta) per group).  The step selects, per chunk
+ * of `chunk` input channels, the top_k channels of largest |x| (ties to the
+ * lower index) and uses their refined weights; the other channels use the
+ * base weights (bin centres).
+ * ------------------------------------------------------------------------- */
+typedef struct sf_wgeom {
+  int32_t m;            /* output rows, a multiple of 32                         */
+  int32_t k;            /* input channels, a multiple of 128, at most 15,360
+                           (x is staged in LDS; SF_ERR_UNSUPPORTED above)        */
+  int32_t base_bits;    /* b: 2, 3 or 4                                          */
+  int32_t refine_bits;  /* r: 1 .. 8                                             */
+  int32_t top_k;        /* channels refined per chunk, 0 <= top_k <= chunk       */
+  int32_t chunk;        /* input channels per selection chunk, 1 .. 4096 (1,024
+                           on the page); the last chunk may be shorter           */
+} sf_wgeom;
+
+/* Quantize W (device [m][k] fp32, row-major) into
+ *   codes        device [m][k*b/8]: per row, per group of 128 channels an
+ *                LSB-first bitstream of the b-bit base codes
+ *   scales       device [m][k/128][2] fp32 {lo, delta}
+ *   refine_cols  device [k][m*r/8]: per input channel, the r-bit refinement
+ *                codes of every output row (LSB-first bitstream over rows):
+ *                a selected channel's column is what crosses the link
+ *   scratch      device, m*k*r/8 bytes (the codes row-major before the
+ *                transpose)
+ * All pointers 16-byte aligned.  SF_ERR_INVALID_ARG for a bad shape. */
+sf_status sf_w_quantize(const sf_wgeom* g, const float* w, uint8_t* codes, float* scales, uint8_t* refine_cols,
+                        uint8_t* scratch, void* stream);
+
+/* Words of the workspace sf_w_gemv takes: 2 ceil(k / chunk) min(top_k, chunk)
+ * + 2. */
+sf_status sf_w_gemv_workspace_words(const sf_wgeom* g, int32_t* words);
+
+/* y = W x as above: x device [k] fp32, y device [m] fp32, sel device int32
+ * [ceil(k/chunk) * min(top_k, chunk)]: the selected channels, ascending within
+ * each chunk (written by the call; a shorter last chunk pads with -1).
+ * workspace: device uint32 [sf_w_gemv_workspace_words], zero-filled before
+ * its first use and then left to the calls: the selection tagged with the
+ * call's epoch (a per-process counter) and a status word.  One kernel on
+ * `stream`: its first work-groups select the channels, the others compute the
+ * rows and take the selection once it carries the call's epoch (a bounded
+ * wait, about 0.2 s) to add the refined channels.  A wait that expires sets
+ * the status word (the last workspace word) nonzero and leaves NaN in the
+ * rows concerned.  Calls that share a workspace must not overlap.  x, scales,
+ * codes and workspace 16-byte aligned, else SF_ERR_INVALID_ARG. */
+sf_status sf_w_gemv(const sf_wgeom* g, const uint8_t* codes, const float* scales, const uint8_t* refine_cols,
+                    const float* x, float* y, int32_t* sel, uint32_t* workspace, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Refinement store and device refinement cache.
  *
  * The store holds the refinement codes of every cached row (paragraph "Think

@@ -33,12 +33,18 @@ c_i32, c_i64, c_vp, c_size = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ct
 EXPORTS = ("sf_status_string", "sf_last_error_string", "sf_kv_quantize", "sf_kv_quantize_ex", "sf_store_create",
            "sf_store_destroy", "sf_refine_store", "sf_store_clear_cache", "sf_store_check",
            "sf_decode_workspace_size", "sf_decode_step", "sf_decode_step_noalloc",
-           "sf_decode_noalloc_max_bytes", "sf_decode_check", "sf_stream_read", "sf_decode_form")
+           "sf_decode_noalloc_max_bytes", "sf_decode_check", "sf_stream_read", "sf_decode_form",
+           "sf_w_quantize", "sf_w_gemv_workspace_words", "sf_w_gemv")
 
 
 class sf_geom(ctypes.Structure):
     _fields_ = [("head_dim", c_i32), ("n_q_heads", c_i32), ("n_kv_heads", c_i32),
                 ("base_bits", c_i32), ("refine_bits", c_i32)]
+
+
+class sf_wgeom(ctypes.Structure):
+    _fields_ = [("m", c_i32), ("k", c_i32), ("base_bits", c_i32), ("refine_bits", c_i32), ("top_k", c_i32),
+                ("chunk", c_i32)]
 
 
 class sf_step_stats(ctypes.Structure):
@@ -98,6 +104,10 @@ def load() -> ctypes.CDLL:
     lib.sf_decode_check.argtypes = [c_vp, c_vp]
     lib.sf_stream_read.argtypes = [c_vp, c_size, ctypes.c_uint32, c_vp, c_i32, c_vp]
     lib.sf_decode_form.argtypes = [G, ctypes.POINTER(sf_decode_args), ctypes.POINTER(c_i32)]
+    WG = ctypes.POINTER(sf_wgeom)
+    lib.sf_w_quantize.argtypes = [WG, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]
+    lib.sf_w_gemv_workspace_words.argtypes = [WG, ctypes.POINTER(c_i32)]
+    lib.sf_w_gemv.argtypes = [WG, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]
     for name in EXPORTS:
         if name not in ("sf_status_string", "sf_last_error_string", "sf_decode_noalloc_max_bytes"):
             getattr(lib, name).restype = c_i32
@@ -279,3 +289,23 @@ def sf_decode_step(g: sf_geom, *, seq_off_host: Sequence[int], seq_off_dev, q, k
     _check(fn(ctypes.byref(g), ctypes.byref(a), _stream(stream)),
            "sf_decode_step_noalloc" if noalloc else "sf_decode_step")
     return st.as_dict() if want_stats else None
+
+
+def wgeom(m: int, k: int, base_bits: int, refine_bits: int, top_k: int, chunk: int = 1024) -> sf_wgeom:
+    return sf_wgeom(m, k, base_bits, refine_bits, top_k, chunk)
+
+
+def sf_w_quantize(g: sf_wgeom, w, codes, scales, refine_cols, scratch, stream=None) -> None:
+    _check(load().sf_w_quantize(ctypes.byref(g), _ptr(w), _ptr(codes), _ptr(scales), _ptr(refine_cols),
+                                _ptr(scratch), _stream(stream)), "sf_w_quantize")
+
+
+def sf_w_gemv_workspace_words(g: sf_wgeom) -> int:
+    n = c_i32()
+    _check(load().sf_w_gemv_workspace_words(ctypes.byref(g), ctypes.byref(n)), "sf_w_gemv_workspace_words")
+    return n.value
+
+
+def sf_w_gemv(g: sf_wgeom, codes, scales, refine_cols, x, y, sel, workspace, stream=None) -> None:
+    _check(load().sf_w_gemv(ctypes.byref(g), _ptr(codes), _ptr(scales), _ptr(refine_cols), _ptr(x), _ptr(y),
+                            _ptr(sel), _ptr(workspace), _stream(stream)), "sf_w_gemv")

@@ -15,7 +15,8 @@ used: none is available.
 
 Seeds: every draw comes from ``numpy.random.default_rng(SeedSequence([cfg_id,
 layer, stream, step]))`` with stream 0 = K, 1 = V, 2 = outlier channels,
-3 = query, 4 = appended tokens, 5 = sequence lengths.  A torch variant draws
+3 = query, 4 = appended tokens, 5 = sequence lengths, 6 = projection
+weights, 7 = projection activations.  A torch variant draws
 the large per-layer K/V tensors directly on a GPU (``torch.Generator`` seeded
 from the same tuple); its numbers differ from numpy's, so any comparison must
 feed one draw to both sides.
@@ -28,7 +29,7 @@ from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
-STREAM_K, STREAM_V, STREAM_OUTLIER, STREAM_Q, STREAM_APPEND, STREAM_LEN = range(6)
+STREAM_K, STREAM_V, STREAM_OUTLIER, STREAM_Q, STREAM_APPEND, STREAM_LEN, STREAM_W, STREAM_X = range(8)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -200,3 +201,35 @@ def duplicate_rows(k: np.ndarray, v: np.ndarray, src: Sequence[int], dst: Sequen
     """Copy token rows ``src`` onto ``dst`` in place: exact score ties."""
     k[list(dst)] = k[list(src)]
     v[list(dst)] = v[list(src)]
+
+
+# Projection shapes of Llama-3.1-8B (hidden 4,096, MLP 14,336): (output rows,
+# input channels) of the gate/up projection and of the down projection.
+PROJECTIONS: Dict[str, Tuple[int, int]] = {
+    "llama8b_up": (14336, 4096),
+    "llama8b_down": (4096, 14336),
+}
+
+
+def projection_weights(cfg_id: int, m: int, k: int) -> np.ndarray:
+    """[m][k] fp32 weights, normal with standard deviation 1/sqrt(k)."""
+    rng = _rng(cfg_id, 0, STREAM_W, 0)
+    return (rng.standard_normal((m, k), dtype=np.float32) / np.float32(np.sqrt(k))).astype(np.float32)
+
+
+def projection_input(cfg_id: int, k: int, step: int = 0, n_outlier: int = 0, outlier_scale: float = 8.0,
+                     ties: int = 0) -> np.ndarray:
+    """[k] fp32 activations: standard normal, ``n_outlier`` channels scaled by
+    ``outlier_scale`` (heavy activation channels), and ``ties`` channels made
+    to share one magnitude (with random signs) so that selections must break
+    ties by index."""
+    rng = _rng(cfg_id, 0, STREAM_X, step)
+    x = rng.standard_normal(k, dtype=np.float32)
+    if n_outlier:
+        x[rng.choice(k, size=min(n_outlier, k), replace=False)] *= np.float32(outlier_scale)
+    if ties:
+        idx = rng.choice(k, size=min(ties, k), replace=False)
+        mag = np.float32(np.quantile(np.abs(x), 0.97))
+        x[idx] = np.where(rng.random(idx.size) < 0.5, -mag, mag).astype(np.float32)
+    return x
+

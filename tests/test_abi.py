@@ -173,3 +173,39 @@ def test_decoder_follows_a_growing_context():
     assert dec.workspace.numel() == need + need // 4 and dec._hist_clean
     dec.set_offsets(np.array([0, 100, 300]))                 # another batch size: not clean
     assert dec.batch == 2 and not dec._hist_clean and dec.seq_off_dev.tolist() == [0, 100, 300]
+
+
+@pytest.mark.parametrize("geom,status", [
+    ((33, 256, 2, 2, 4, 128), B.SF_ERR_INVALID_ARG),       # rows not a multiple of 32
+    ((32, 200, 2, 2, 4, 128), B.SF_ERR_INVALID_ARG),       # channels not a multiple of 128
+    ((32, 256, 1, 2, 4, 128), B.SF_ERR_INVALID_ARG),
+    ((32, 256, 5, 2, 4, 128), B.SF_ERR_INVALID_ARG),
+    ((32, 256, 2, 0, 4, 128), B.SF_ERR_INVALID_ARG),
+    ((32, 256, 2, 9, 4, 128), B.SF_ERR_INVALID_ARG),
+    ((32, 256, 2, 2, 129, 128), B.SF_ERR_INVALID_ARG),     # more channels than the chunk holds
+    ((32, 256, 2, 2, 4, 0), B.SF_ERR_INVALID_ARG),
+    ((32, 256, 2, 2, 4, 4097), B.SF_ERR_INVALID_ARG),
+    ((32, 15488, 2, 2, 4, 128), B.SF_ERR_UNSUPPORTED),     # x no longer fits the work-group's LDS
+])
+def test_weight_gemv_rejects_before_launch(geom, status):
+    lib = _lib()
+    g = B.wgeom(*geom)
+    fake = 1 << 20
+    assert lib.sf_w_gemv(ctypes.byref(g), fake, fake, fake, fake, fake, fake, fake, None) == status
+    n = ctypes.c_int32()
+    assert lib.sf_w_gemv_workspace_words(ctypes.byref(g), ctypes.byref(n)) == status
+    assert lib.sf_w_quantize(ctypes.byref(g), fake, fake, fake, fake, fake, None) == status
+
+
+def test_weight_gemv_rejects_null_buffers():
+    lib = _lib()
+    g = B.wgeom(64, 1024, 3, 4, 32, 1024)
+    fake = 1 << 20
+    assert lib.sf_w_gemv(ctypes.byref(g), fake, fake, fake, fake, fake, None, fake, None) == B.SF_ERR_INVALID_ARG
+    assert lib.sf_w_gemv(ctypes.byref(g), fake, fake, fake, fake, fake, fake, None, None) == B.SF_ERR_INVALID_ARG
+    assert lib.sf_w_gemv(ctypes.byref(g), fake, fake, fake, fake + 4, fake, fake, fake, None) == B.SF_ERR_INVALID_ARG
+    n = ctypes.c_int32()
+    assert lib.sf_w_gemv_workspace_words(ctypes.byref(g), ctypes.byref(n)) == B.SF_OK and n.value == 2 * 32 + 2
+    g2 = B.wgeom(64, 2688, 3, 4, 32, 1000)
+    assert lib.sf_w_gemv_workspace_words(ctypes.byref(g2), ctypes.byref(n)) == B.SF_OK and n.value == 2 * 3 * 32 + 2
+    assert lib.sf_w_quantize(ctypes.byref(g), fake, fake, fake, None, fake, None) == B.SF_ERR_INVALID_ARG
