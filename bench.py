@@ -15,7 +15,8 @@ events, the CPU oracle timed on a bounded sample on the host, and secondary
 measurements (the five-kernel form beside the single launch; 32K context; the
 16-sequence batch over distinct layers; host-pinned refinement store over 64
 AR(1) steps: cold and warm step time, hit rate and bytes fetched; the
-multi-step reuse run).
+multi-step reuse run; the weight-side refinement GEMV at the Llama-3.1-8B
+projection shapes).
 """
 import argparse
 import json
@@ -175,6 +176,63 @@ def time_graph(graph, steps, warmup, model=None, qseq=None):
     torch.cuda.synchronize()
     per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
     return evs[0].elapsed_time(evs[-1]) / steps, per
+
+
+def gemv_record(calls=32, reps=10):
+    """Weight-side refinement GEMV (sf_w_gemv) at the Llama-3.1-8B projection
+    shapes: 3-bit resident weights, 4-bit refinements, k = 32 of every 1,024
+    input channels.  `calls` calls, each on its own activation vector (so
+    each selects anew), captured back to back in one HIP graph; the time per
+    call is the replay time over `calls`.  Algorithmic bytes per call: base
+    codes, (lo, delta) scales, the selected channels' refinement columns, x,
+    y and the selection."""
+    import torch
+    from selective_kv_cache_amd import binding as B
+    from selective_kv_cache_amd import workloads as W
+    out = {}
+    b, r, top_k, chunk = 3, 4, 32, 1024
+    for name, (m, k) in sorted(W.PROJECTIONS.items()):
+        g = B.wgeom(m, k, b, r, top_k, chunk)
+        w = torch.as_tensor(W.projection_weights(800, m, k), device="cuda")
+        codes = torch.empty((m, k // 128, 16 * b), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((m, k // 128, 2), dtype=torch.float32, device="cuda")
+        cols = torch.empty((k, m * r // 8), dtype=torch.uint8, device="cuda")
+        scratch = torch.empty(m * k * r // 8, dtype=torch.uint8, device="cuda")
+        B.sf_w_quantize(g, w, codes, scales, cols, scratch)
+        torch.cuda.synchronize()
+        del w, scratch
+        nchunks = (k + chunk - 1) // chunk
+        n_sel = nchunks * top_k
+        xs = [torch.as_tensor(W.projection_input(800, k, step=i, n_outlier=12), device="cuda") for i in range(calls)]
+        ys = [torch.empty(m, device="cuda") for _ in range(calls)]
+        sels = [torch.empty(n_sel, dtype=torch.int32, device="cuda") for _ in range(calls)]
+        ws = torch.zeros(B.sf_w_gemv_workspace_words(g), dtype=torch.int32, device="cuda")
+        for i in range(calls):
+            B.sf_w_gemv(g, codes, scales, cols, xs[i], ys[i], sels[i], ws)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(calls):
+                B.sf_w_gemv(g, codes, scales, cols, xs[i], ys[i], sels[i], ws)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        assert int(ws[-1].item()) == 0, "a GEMV wait expired"
+        us = e0.elapsed_time(e1) * 1e3 / (reps * calls)
+        nbytes = m * k * b // 8 + m * (k // 128) * 8 + n_sel * m * r // 8 + k * 4 + m * 4 + n_sel * 4
+        out[name] = {"m": m, "k": k, "base_bits": b, "refine_bits": r, "top_k": top_k, "chunk": chunk,
+                     "us_per_call": us, "algorithmic_bytes": nbytes, "gbps": nbytes / (us * 1e-6) / 1e9,
+                     "frac_of_peak": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+                     "timing": f"{calls} calls on distinct activations in one HIP graph, {reps} replays"}
+        del graph, xs, ys, sels, codes, scales, cols
+        torch.cuda.empty_cache()
+    return out
 
 
 def achievable_read_gbps(nbytes=4 << 30):
@@ -594,6 +652,8 @@ def main():
             sec["host_store"] = host_tier_run(w, 64)
         log("secondary: multi-step reuse run (llama8b_reuse)")
         sec["reuse"] = reuse_record(W.WORKLOADS["llama8b_reuse"])
+        log("secondary: weight-side refinement GEMV")
+        sec["weight_gemv"] = gemv_record()
         rec["secondary"] = sec
     rd, rd_all = achievable_read_gbps()
     rec["achievable_read_gbps"] = rd

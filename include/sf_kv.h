@@ -153,22 +153,25 @@ typedef struct sf_wgeom {
 sf_status sf_w_quantize(const sf_wgeom* g, const float* w, uint8_t* codes, float* scales, uint8_t* refine_cols,
                         uint8_t* scratch, void* stream);
 
-/* Words of the workspace sf_w_gemv takes: 2 ceil(k / chunk) min(top_k, chunk)
- * + 2. */
+/* Words of the workspace sf_w_gemv takes: 514 + 2 ceil(k / chunk)
+ * min(top_k, chunk). */
 sf_status sf_w_gemv_workspace_words(const sf_wgeom* g, int32_t* words);
 
 /* y = W x as above: x device [k] fp32, y device [m] fp32, sel device int32
  * [ceil(k/chunk) * min(top_k, chunk)]: the selected channels, ascending within
  * each chunk (written by the call; a shorter last chunk pads with -1).
  * workspace: device uint32 [sf_w_gemv_workspace_words], zero-filled before
- * its first use and then left to the calls: the selection tagged with the
- * call's epoch (a per-process counter) and a status word.  One kernel on
- * `stream`: its first work-groups select the channels, the others compute the
- * rows and take the selection once it carries the call's epoch (a bounded
- * wait, about 0.2 s) to add the refined channels.  A wait that expires sets
- * the status word (the last workspace word) nonzero and leaves NaN in the
- * rows concerned.  Calls that share a workspace must not overlap.  x, scales,
- * codes and workspace 16-byte aligned, else SF_ERR_INVALID_ARG. */
+ * its first use and then left to the calls: counters that every call's
+ * wavefronts advance (they give the call its epoch on the device, so that
+ * captured graphs replay correctly), the selection tagged with the epoch,
+ * and a status word.  A workspace serves one geometry: calls with another
+ * geometry need a workspace of their own (zero-filled).  One kernel on
+ * `stream`: its first work-groups select the channels, the others compute
+ * the rows and take the selection once it carries the call's epoch (a
+ * bounded wait, about 0.2 s) to add the refined channels.  A wait that
+ * expires sets the status word (the last workspace word) nonzero and leaves
+ * NaN in the rows concerned.  Calls that share a workspace must not overlap.
+ * x, scales, codes and workspace 16-byte aligned, else SF_ERR_INVALID_ARG. */
 sf_status sf_w_gemv(const sf_wgeom* g, const uint8_t* codes, const float* scales, const uint8_t* refine_cols,
                     const float* x, float* y, int32_t* sel, uint32_t* workspace, void* stream);
 

@@ -14,27 +14,27 @@
 // row, LSB-first over rows).
 //
 // One launch, two kinds of work-group:
-// * the first ceil(k / chunk) work-groups select one chunk each: a radix
-//   select (11, 10 and 10 bits of |x|) finds the k-th largest magnitude,
-//   ties at it go to the lower indices, and the chosen channels are written
-//   in ascending order with device-scope stores; then the chunk's flag in the
-//   workspace is set to the call's epoch;
+// * the first work-groups select, one chunk per wavefront (the top-k of the
+//   chunk's |x|, ties to the lower index; see select_chunk_wave), and write
+//   the chosen channels in ascending order, each tagged with the call's
+//   epoch (device-scope stores; the epoch comes from counters in the
+//   workspace that every wavefront advances when it starts);
 // * the others compute 8 P output rows over all of k.  The input channels
 //   are cut into slices of 2,048 (64 lanes x 32 channels); wavefront (slice
-//   s, row group g) holds its 32 channels of x in registers and, for each of
-//   its 8 rows, decodes the lane's 32 base codes: with c the codes, the
+//   s, row group g) reads its 32 channels of x from LDS and, for each of its
+//   8 rows, decodes the lane's 32 base codes: with c the codes, the
 //   segment's sum of (lo + (c + 1/2) delta) x is lo S0 + delta (sum c x +
 //   S0 / 2), S0 the segment's sum of x.  The 8 row sums are reduced across
 //   the lanes at once (halving exchanges), the slices summed in LDS in a
-//   fixed order.  Only then does the work-group wait for the selection flags
-//   (the selecting work-groups come first in the dispatch order and wait for
-//   nothing), and add, per (row, selected channel), delta ((s + 1/2) 2^-r -
-//   1/2) x_c with s the channel's refinement code for the row.
+//   fixed order.  The selection, loaded early, is taken once every entry
+//   carries the call's epoch (the selecting work-groups come first in the
+//   dispatch order and wait for nothing; a bounded wait otherwise), and per
+//   (row, selected channel) delta ((s + 1/2) 2^-r - 1/2) x_c is added, s the
+//   channel's refinement code for the row.
 // Every result is summed in a fixed order: the call is deterministic.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <atomic>
 
 #include "sf_decode_kernels.h"
 #include "sf_internal.h"
@@ -49,6 +49,8 @@ constexpr int kWMaxK = 15360;         // at most 8 slices: 8 wavefronts per work
 constexpr int kWMaxThreads = 512;
 constexpr int kWSpinLimit = 1 << 18;  // bounded wait: about 0.2 s
 constexpr int kWTile = 1024;          // selected channels staged in LDS at a time
+constexpr int kWCalls = 16;           // counters of started wavefronts (the call's epoch)
+constexpr int kWCallStride = 32;      // words between them (separate cache lines)
 
 __device__ inline uint32_t wld(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -118,6 +120,46 @@ __device__ inline uint32_t wave_incl_scan(uint32_t v) {
 // from moving them.
 __device__ inline void wave_lds_order() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
 
+struct WArgs {
+  const uint8_t* codes;
+  const float2* scales;
+  const uint8_t* refine_cols;
+  const float* x;
+  float* y;
+  int32_t* sel;
+  uint64_t* tags;       // [nchunks kout] selected channels tagged with the call's epoch
+  uint32_t* calls;      // [kWCalls] 64-bit counters of started wavefronts, kWCallStride words apart
+  uint32_t* status;     // set nonzero when a wait expired
+  int32_t m, k, r, top_k, chunk, kout, nchunks, nsel_wg, ns, p;
+};
+
+// The call's epoch, without host state (so that a captured graph replays
+// correctly): every wavefront of the launch adds 1 to counter gw mod kWCalls
+// (gw its index in the launch; counters on separate cache lines) when it
+// starts.  With a fixed launch shape counter j gains the same n_j every
+// call, so v / n_j (v the value it returned) is the number of earlier calls,
+// the same for every wavefront of the call.  The counter's value is read
+// where the epoch is needed, late, so the atomic's latency is hidden.
+__device__ inline uint64_t start_count(const WArgs& a) {
+  const uint32_t gw = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  unsigned long long v = 0ull;
+  if ((threadIdx.x & 63) == 0)
+    v = atomicAdd(reinterpret_cast<unsigned long long*>(a.calls + (gw % kWCalls) * kWCallStride), 1ull);
+  return v;
+}
+
+// The call's epoch from a wavefront's start count v (see start_count): the
+// number of earlier calls plus 1.
+__device__ inline uint32_t epoch_of(uint64_t v) {
+  const uint32_t wpg = blockDim.x >> 6;
+  const uint32_t gw = blockIdx.x * wpg + (threadIdx.x >> 6);
+  const uint32_t total = gridDim.x * wpg, j = gw % kWCalls;
+  const uint32_t n_j = (total - j + kWCalls - 1) / kWCalls;
+  const uint64_t v0 = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 0) << 32) |
+                      (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 0);
+  return (uint32_t)(v0 / n_j) + 1u;
+}
+
 // Number of lanes below this one whose bit is set in `mask`.
 __device__ inline uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
@@ -141,10 +183,10 @@ __device__ inline uint32_t lanes_below(uint64_t mask) {
 //   it are ranked with ballots (the lanes below in the round plus the
 //   earlier rounds) and written ascending to out[0, kk) and to tags[] with
 //   the epoch in the upper half (device-scope stores); out[kk, kout) = -1.
-__device__ __attribute__((always_inline)) inline void select_chunk_wave(uint32_t* hist, uint32_t* xl,
+__device__ __attribute__((always_inline)) inline void select_chunk_wave(const WArgs& a, uint32_t* hist, uint32_t* xl,
                                                                        const float* __restrict__ x, int c0, int n,
                                                                        int k, int kout, int32_t* __restrict__ out,
-                                                                       uint64_t* __restrict__ tags, uint32_t epoch) {
+                                                                       uint64_t* __restrict__ tags) {
   const int lane = threadIdx.x & 63;
   const int kk = min(k, n);
   const int rounds = (n + 63) / 64;
@@ -163,6 +205,9 @@ __device__ __attribute__((always_inline)) inline void select_chunk_wave(uint32_t
     }
     wave_lds_order();
   }
+  // counted after the staging loads, so that waiting for them does not wait
+  // for the atomic
+  const uint64_t started = start_count(a);
   // the block's values: u[j] of element (r0 + j) 64 + lane, 0 past the chunk
   auto load_block = [&](int r0, uint32_t (&u)[kR]) {
 #pragma unroll
@@ -172,7 +217,6 @@ __device__ __attribute__((always_inline)) inline void select_chunk_wave(uint32_t
       u[j] = e < n ? t : 0u;
     }
   };
-  const uint64_t tag = (uint64_t)epoch << 32;
   uint32_t floor_u = 0u;
   if (kk < n && kk <= 64) {
     // the kk-th largest of the lanes' maxima, ranked against all 64 in LDS
@@ -228,6 +272,7 @@ __device__ __attribute__((always_inline)) inline void select_chunk_wave(uint32_t
       }
       const bool chosen = mine && rank < (uint32_t)kk;
       const uint32_t p = lanes_below(__builtin_amdgcn_ballot_w64(chosen));
+      const uint64_t tag = (uint64_t)epoch_of(started) << 32;
       if (chosen && p < (uint32_t)kout) {
         out[p] = c0 + (int)me;
         wst64(tags + p, tag | (uint32_t)(c0 + (int)me));
@@ -292,6 +337,7 @@ __device__ __attribute__((always_inline)) inline void select_chunk_wave(uint32_t
     prefix = 0u;     // every channel is chosen: all are above or equal to 0
     need = (uint32_t)n;
   }
+  const uint64_t tag = (uint64_t)epoch_of(started) << 32;
   uint32_t eq_seen = 0u, pos = 0u;
   for (int r0 = 0; r0 < rounds; r0 += kR) {
     uint32_t u[kR];
@@ -348,18 +394,7 @@ __device__ inline float reduce8_rows(const float (&p)[8]) {
   return v;
 }
 
-struct WArgs {
-  const uint8_t* codes;
-  const float2* scales;
-  const uint8_t* refine_cols;
-  const float* x;
-  float* y;
-  int32_t* sel;
-  uint64_t* tags;       // [nchunks kout] selected channels tagged with the call's epoch
-  uint32_t* status;     // set nonzero when a wait expired
-  int32_t m, k, r, top_k, chunk, kout, nchunks, nsel_wg, ns, p;
-  uint32_t epoch;
-};
+
 
 template <int B>
 __global__ void __launch_bounds__(kWMaxThreads) w_gemv(WArgs a) {
@@ -373,8 +408,10 @@ __global__ void __launch_bounds__(kWMaxThreads) w_gemv(WArgs a) {
       const int c0 = q * a.chunk;
       // the chunks of one work-group are disjoint ranges of k: each
       // wavefront stages its chunk at the chunk's own place in the x area
-      select_chunk_wave(s.hist[wv], reinterpret_cast<uint32_t*>(xs4) + c0, a.x, c0, min(a.chunk, a.k - c0), a.top_k,
-                        a.kout, a.sel + (int64_t)q * a.kout, a.tags + (int64_t)q * a.kout, a.epoch);
+      select_chunk_wave(a, s.hist[wv], reinterpret_cast<uint32_t*>(xs4) + c0, a.x, c0, min(a.chunk, a.k - c0),
+                        a.top_k, a.kout, a.sel + (int64_t)q * a.kout, a.tags + (int64_t)q * a.kout);
+    } else {
+      start_count(a);                                  // every wavefront counts itself
     }
     return;
   }
@@ -407,6 +444,9 @@ __global__ void __launch_bounds__(kWMaxThreads) w_gemv(WArgs a) {
       sc[i] = make_float2(__uint_as_float(v[0]), __uint_as_float(v[1]));
     }
   }
+  // counted after the code loads (waiting for them then does not wait for
+  // the atomic)
+  const uint64_t started = start_count(a);
   // the first tile of the selection, speculatively: an entry is valid once
   // it carries this call's epoch
   constexpr int kSpec = kWTile / 256;
@@ -449,6 +489,7 @@ __global__ void __launch_bounds__(kWMaxThreads) w_gemv(WArgs a) {
   const float2* srow = a.scales + (int64_t)row * ngrp;
   float corr = 0.f;
   bool ok = true;
+  const uint32_t epoch = n_sel > 0 ? epoch_of(started) : 0u;
   for (int t0 = 0; t0 < n_sel && ok; t0 += kWTile) {
     const int nt = min(kWTile, n_sel - t0);
     bool mine = true;                                  // this thread's entries of the tile are valid
@@ -457,7 +498,7 @@ __global__ void __launch_bounds__(kWMaxThreads) w_gemv(WArgs a) {
       for (int u = 0; u < kSpec; ++u) {
         const int j = tid + u * (int)blockDim.x;
         if (j < nt) {
-          mine = mine && (uint32_t)(spec[u] >> 32) == a.epoch;
+          mine = mine && (uint32_t)(spec[u] >> 32) == epoch;
           s.tile[j] = (int32_t)(uint32_t)spec[u];
         }
       }
@@ -470,7 +511,7 @@ __global__ void __launch_bounds__(kWMaxThreads) w_gemv(WArgs a) {
       mine = true;
       for (int j = tid; j < nt; j += blockDim.x) {
         const uint64_t e = wld64(a.tags + t0 + j);
-        mine = mine && (uint32_t)(e >> 32) == a.epoch;
+        mine = mine && (uint32_t)(e >> 32) == epoch;
         s.tile[j] = (int32_t)(uint32_t)e;
       }
       if (++spins > kWSpinLimit) {
@@ -579,7 +620,7 @@ extern "C" sf_status sf_w_gemv_workspace_words(const sf_wgeom* g, int32_t* words
   if (s != SF_OK) return s;
   if (!words) return SF_ERR_INVALID_ARG;
   const int32_t nchunks = (g->k + g->chunk - 1) / g->chunk;
-  *words = 2 * nchunks * std::min(g->top_k, g->chunk) + 2;
+  *words = kWCallStride * kWCalls + 2 * nchunks * std::min(g->top_k, g->chunk) + 2;
   return SF_OK;
 }
 
@@ -593,9 +634,6 @@ extern "C" sf_status sf_w_gemv(const sf_wgeom* g, const uint8_t* codes, const fl
   if ((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(scales) | reinterpret_cast<uintptr_t>(codes) |
        reinterpret_cast<uintptr_t>(workspace)) & 15)
     return SF_ERR_INVALID_ARG;
-  static std::atomic<uint32_t> epoch_counter{0};
-  uint32_t epoch = ++epoch_counter;
-  if (epoch == 0u) epoch = ++epoch_counter;
   WArgs a{};
   a.codes = codes;
   a.scales = reinterpret_cast<const float2*>(scales);
@@ -614,9 +652,10 @@ extern "C" sf_status sf_w_gemv(const sf_wgeom* g, const uint8_t* codes, const fl
   a.p = a.ns == 1 ? 4 : (a.ns <= 3 ? 2 : 1);        // at least 4 wavefronts; 8 P rows per work-group
   const int threads = 64 * a.ns * a.p;
   a.nsel_wg = a.kout > 0 ? (a.nchunks + threads / 64 - 1) / (threads / 64) : 0;   // one chunk per wavefront
-  a.tags = reinterpret_cast<uint64_t*>(workspace);
-  a.status = workspace + 2 * (int64_t)a.nchunks * a.kout + 1;   // the last word
-  a.epoch = epoch;
+  // workspace: counters, then the tagged selection, then the status word
+  a.calls = workspace;
+  a.tags = reinterpret_cast<uint64_t*>(workspace + kWCallStride * kWCalls);
+  a.status = workspace + kWCallStride * kWCalls + 2 * (int64_t)a.nchunks * a.kout + 1;   // the last word
   const dim3 grid((unsigned)(a.nsel_wg + g->m / (8 * a.p)));
   const size_t lds = (size_t)g->k * sizeof(float);
   hipStream_t st = (hipStream_t)stream;

@@ -205,7 +205,7 @@ def test_weight_gemv_rejects_null_buffers():
     assert lib.sf_w_gemv(ctypes.byref(g), fake, fake, fake, fake, fake, fake, None, None) == B.SF_ERR_INVALID_ARG
     assert lib.sf_w_gemv(ctypes.byref(g), fake, fake, fake, fake + 4, fake, fake, fake, None) == B.SF_ERR_INVALID_ARG
     n = ctypes.c_int32()
-    assert lib.sf_w_gemv_workspace_words(ctypes.byref(g), ctypes.byref(n)) == B.SF_OK and n.value == 2 * 32 + 2
+    assert lib.sf_w_gemv_workspace_words(ctypes.byref(g), ctypes.byref(n)) == B.SF_OK and n.value == 512 + 2 * 32 + 2
     g2 = B.wgeom(64, 2688, 3, 4, 32, 1000)
-    assert lib.sf_w_gemv_workspace_words(ctypes.byref(g2), ctypes.byref(n)) == B.SF_OK and n.value == 2 * 3 * 32 + 2
+    assert lib.sf_w_gemv_workspace_words(ctypes.byref(g2), ctypes.byref(n)) == B.SF_OK and n.value == 512 + 2 * 3 * 32 + 2
     assert lib.sf_w_quantize(ctypes.byref(g), fake, fake, fake, None, fake, None) == B.SF_ERR_INVALID_ARG

@@ -202,3 +202,39 @@ def test_gemv_argument_checks():
         B.sf_w_gemv(B.wgeom(32, 15488, 2, 2, 4, 128), t["codes"], t["scales"], t["cols"], x, y, sel, ws)
     with pytest.raises(B.SfError):        # x not 16-byte aligned
         B.sf_w_gemv(g, t["codes"], t["scales"], t["cols"], x[1:], y, sel, ws)
+
+
+def test_gemv_graph_replays_follow_new_inputs():
+    # the call's epoch lives on the device: a captured call replayed with new
+    # activations (copied into the captured buffer between replays, with
+    # eager work and synchronization in between) selects and sums anew
+    import torch
+    from selective_kv_cache_amd import binding as B
+    m, k, b, r, top_k, chunk = 192, 3072, 3, 4, 32, 1024
+    w = W.projection_weights(950, m, k)
+    qw = G.quantize_weights(w, b, r)
+    g, t = _gpu_quantize(w, b, r, top_k, chunk)
+    ws = _workspace(g)
+    x = torch.zeros(k, device="cuda")
+    y = torch.empty(m, device="cuda")
+    sel = torch.empty(3 * top_k, dtype=torch.int32, device="cuda")
+    x.copy_(torch.as_tensor(W.projection_input(950, k, step=99), device="cuda"))
+    B.sf_w_gemv(g, t["codes"], t["scales"], t["cols"], x, y, sel, ws)     # eager warm-up
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            B.sf_w_gemv(g, t["codes"], t["scales"], t["cols"], x, y, sel, ws, stream=s)
+    torch.cuda.synchronize()
+    for step in range(4):
+        xn = W.projection_input(950, k, step=step, n_outlier=3)
+        x.copy_(torch.as_tensor(xn, device="cuda"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert int(ws[-1]) == 0
+        _check_gemv(y.cpu().numpy(), sel.cpu().numpy(), qw, xn, b, top_k, chunk)
+        # an eager call between replays shares the workspace
+        y2, sel2 = _gpu_gemv(g, t, xn, ws)
+        assert np.array_equal(sel2, sel.cpu().numpy()) and np.array_equal(y2, y.cpu().numpy())
