@@ -160,6 +160,19 @@ __device__ inline uint32_t epoch_of(uint64_t v) {
   return (uint32_t)(v0 / n_j) + 1u;
 }
 
+// The need-th largest (1 <= need <= count) of the lanes' 31-bit values v
+// where `active`, by bisection from the top bit: the largest T with at
+// least `need` active values >= T.  Ballots and scalar counts only.
+__device__ inline uint32_t wave_kth_largest(uint32_t v, bool active, uint32_t need) {
+  uint32_t t = 0u;
+#pragma unroll
+  for (int b = 30; b >= 0; --b) {
+    const uint32_t c = t | (1u << b);
+    if ((uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(active && v >= c)) >= need) t = c;
+  }
+  return t;
+}
+
 // Number of lanes below this one whose bit is set in `mask`.
 __device__ inline uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
@@ -174,9 +187,11 @@ __device__ inline uint32_t lanes_below(uint64_t mask) {
 // * A lower bound of the kk-th largest magnitude (kk = min(k, n)): when kk
 //   <= 64, the kk-th largest of the 64 lanes' maxima (kk lanes hold an
 //   element at least that large); else 0.  Only the candidates at or above
-//   it can be chosen.  When at most 64 are, they are listed in index order,
-//   each ranked against all (larger magnitude first, then lower index), and
-//   those ranked below kk written in list order: done.
+//   it can be chosen.  For chunks of at most 1,024 (lane l holding 16
+//   consecutive elements) with at most 64 candidates, they are listed in
+//   index order one per lane (a prefix sum of the lanes' counts), the kk-th
+//   largest of them found by bisection, and those above it and the first of
+//   those equal to it written in list order: done.
 // * Else a radix select over the candidates' 31 bits of |x| (digits of 8,
 //   8, 8 and 7 bits, a 256-bin histogram in `hist`) finds the kk-th largest.
 // * Round by round, the channels above it and the first of those equal to
@@ -218,59 +233,49 @@ __device__ __attribute__((always_inline)) inline void select_chunk_wave(const WA
     }
   };
   uint32_t floor_u = 0u;
-  if (kk < n && kk <= 64) {
-    // the kk-th largest of the lanes' maxima, ranked against all 64 in LDS
-    uint32_t lm = 0u;
-    for (int r0 = 0; r0 < rounds; r0 += kR) {
-      uint32_t u[kR];
-      load_block(r0, u);
+  if (kk < n && kk <= 64 && n <= 64 * kR) {
+    // lane l holds elements l E .. l E + E - 1 (E = rounds <= kR), so that
+    // lane order then element order is index order
+    const int E = rounds;
+    uint32_t u[kR];
+    uint32_t valid = 0u, lm = 0u;
 #pragma unroll
-      for (int j = 0; j < kR; ++j) lm = max(lm, u[j]);
+    for (int j = 0; j < kR; ++j) {
+      const int e = lane * E + j;
+      const bool ok = j < E && e < n;
+      u[j] = ok ? xl[min(e, n - 1)] : 0u;
+      valid |= ok ? 1u << j : 0u;
+      lm = max(lm, u[j]);
     }
-    hist[lane] = lm;
-    wave_lds_order();
-    uint32_t gt = 0u, ge = 0u;
+    // the kk-th largest of the lanes' maxima bounds the kk-th largest below
+    floor_u = wave_kth_largest(lm, true, (uint32_t)kk);
+    uint32_t cm = 0u;
 #pragma unroll
-    for (int j = 0; j < 64; j += 4) {
-      const uint4 v = *reinterpret_cast<const uint4*>(hist + j);
-      gt += (v.x > lm ? 1u : 0u) + (v.y > lm ? 1u : 0u) + (v.z > lm ? 1u : 0u) + (v.w > lm ? 1u : 0u);
-      ge += (v.x >= lm ? 1u : 0u) + (v.y >= lm ? 1u : 0u) + (v.z >= lm ? 1u : 0u) + (v.w >= lm ? 1u : 0u);
-    }
-    const uint64_t at = __builtin_amdgcn_ballot_w64(gt < (uint32_t)kk && ge >= (uint32_t)kk);
-    floor_u = (uint32_t)__builtin_amdgcn_readlane((int)lm, at ? (int)__builtin_ctzll(at) : 0);
-    // the candidates (|x| >= floor) in index order into a list of at most 64
-    uint32_t* cu = hist + 64;     // magnitudes
-    uint32_t* ce = hist + 128;    // element indices
-    uint32_t cnt = 0u;
-    for (int r0 = 0; r0 < rounds; r0 += kR) {
-      uint32_t u[kR];
-      load_block(r0, u);
-#pragma unroll
-      for (int j = 0; j < kR; ++j) {
-        const int e = (r0 + j) * 64 + lane;
-        const bool cand = e < n && u[j] >= floor_u;
-        const uint64_t b = __builtin_amdgcn_ballot_w64(cand);
-        const uint32_t p = cnt + lanes_below(b);
-        if (cand && p < 64u) {
-          cu[p] = u[j];
-          ce[p] = (uint32_t)e;
-        }
-        cnt += (uint32_t)__builtin_popcountll(b);
-      }
-    }
-    wave_lds_order();
+    for (int j = 0; j < kR; ++j) cm |= ((valid >> j) & 1u) && u[j] >= floor_u ? 1u << j : 0u;
+    const uint32_t c = (uint32_t)__builtin_popcount(cm);
+    const uint32_t inc = wave_incl_scan(c);
+    const uint32_t cnt = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
     if (cnt <= 64u) {
-      // exact ranks among the candidates: larger magnitude first, then lower index
+      // the candidates in index order, one per lane, through LDS
+      uint32_t* cu = hist;          // magnitudes
+      uint32_t* ce = hist + 64;     // element indices
+      uint32_t pos = inc - c;
+#pragma unroll
+      for (int j = 0; j < kR; ++j)
+        if ((cm >> j) & 1u) {
+          cu[pos] = u[j];
+          ce[pos] = (uint32_t)(lane * E + j);
+          ++pos;
+        }
+      wave_lds_order();
+      // the kk-th largest magnitude among them; those above it, and the
+      // first of those equal to it, are chosen
       const bool mine = (uint32_t)lane < cnt;
       const uint32_t mu = mine ? cu[lane] : 0u, me = mine ? ce[lane] : 0u;
-      uint32_t rank = 0u;
-#pragma unroll 8
-      for (int j = 0; j < 64; ++j) {
-        const uint32_t vu = cu[j], ve = ce[j];
-        const bool before = (uint32_t)j < cnt && (vu > mu || (vu == mu && ve < me));
-        rank += before ? 1u : 0u;
-      }
-      const bool chosen = mine && rank < (uint32_t)kk;
+      const uint32_t thr = wave_kth_largest(mu, mine, (uint32_t)kk);
+      const uint32_t n_above = (uint32_t)__builtin_popcountll(__builtin_amdgcn_ballot_w64(mine && mu > thr));
+      const uint64_t beq = __builtin_amdgcn_ballot_w64(mine && mu == thr);
+      const bool chosen = mine && (mu > thr || (mu == thr && lanes_below(beq) < (uint32_t)kk - n_above));
       const uint32_t p = lanes_below(__builtin_amdgcn_ballot_w64(chosen));
       const uint64_t tag = (uint64_t)epoch_of(started) << 32;
       if (chosen && p < (uint32_t)kout) {
@@ -284,6 +289,16 @@ __device__ __attribute__((always_inline)) inline void select_chunk_wave(const WA
       return;
     }
     wave_lds_order();
+  } else if (kk < n && kk <= 64) {
+    // longer chunks: the same bound, the candidates left to the radix select
+    uint32_t lm = 0u;
+    for (int r0 = 0; r0 < rounds; r0 += kR) {
+      uint32_t u[kR];
+      load_block(r0, u);
+#pragma unroll
+      for (int j = 0; j < kR; ++j) lm = max(lm, u[j]);
+    }
+    floor_u = wave_kth_largest(lm, true, (uint32_t)kk);
   }
   // the general case: a radix select over the candidates
   uint32_t prefix = 0u, pmask = 0u, need = (uint32_t)kk;
@@ -402,6 +417,9 @@ __global__ void __launch_bounds__(kWMaxThreads) w_gemv(WArgs a) {
   extern __shared__ float4 xs4[];                      // x, k / 4 units, rotated (xswz)
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   if ((int)blockIdx.x < a.nsel_wg) {
+    // the selection is a chain of dependent steps that the row work-groups
+    // wait for at their end: it takes the issue slots first
+    __builtin_amdgcn_s_setprio(3);
     // wavefront wv of selecting work-group b: chunk b (blockDim / 64) + wv
     const int q = blockIdx.x * (int)(blockDim.x >> 6) + wv;
     if (q < a.nchunks) {
@@ -520,14 +538,15 @@ __global__ void __launch_bounds__(kWMaxThreads) w_gemv(WArgs a) {
       }
     }
     if (!ok) break;
-    for (int j = j0; j < nt; j += 4 * tpr) {
-      int c[4];
-      uint32_t lo8[4], hi8[4];
-      float dl[4], xc[4];
+    constexpr int kU = 8;                            // entries a thread loads at once
+    for (int j = j0; j < nt; j += kU * tpr) {
+      int c[kU];
+      uint32_t lo8[kU], hi8[kU];
+      float dl[kU], xc[kU];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) c[u] = j + u * tpr < nt ? s.tile[j + u * tpr] : -1;
+      for (int u = 0; u < kU; ++u) c[u] = j + u * tpr < nt ? s.tile[j + u * tpr] : -1;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kU; ++u) {
         const int cc = c[u] < 0 ? 0 : c[u];
         const uint8_t* col = a.refine_cols + (int64_t)cc * col_bytes + (bit >> 3);
         lo8[u] = col[0];
@@ -537,7 +556,7 @@ __global__ void __launch_bounds__(kWMaxThreads) w_gemv(WArgs a) {
         xc[u] = (cc & 2) ? ((cc & 1) ? xq.w : xq.z) : ((cc & 1) ? xq.y : xq.x);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kU; ++u) {
         const uint32_t code = ((lo8[u] | (hi8[u] << 8)) >> (bit & 7)) & mask;
         const float t = dl[u] * fmaf((float)code + 0.5f, sub, -0.5f) * xc[u];
         corr += c[u] < 0 ? 0.f : t;
