@@ -563,6 +563,8 @@ def main():
     ap.add_argument("--multi-pass", action="store_true", help="the five-kernel form for the headline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--gemv", action="store_true",
+                    help="only the weight-side GEMV record (one JSON line), for profiling it alone")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only copy BYTES between two device buffers 3 times (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -583,6 +585,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"copied {args.calibrate_copy} bytes 3 times")
+        return
+    if args.gemv:
+        print(json.dumps({"weight_gemv": gemv_record()}), flush=True)
         return
     w = W.WORKLOADS[args.workload]
     tier = B.SF_TIER_DEVICE if args.tier == "device" else B.SF_TIER_HOST_PINNED
