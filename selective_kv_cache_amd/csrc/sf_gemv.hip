@@ -434,7 +434,17 @@ __global__ void __launch_bounds__(kWMaxThreads) w_gemv(WArgs a) {
     return;
   }
   const int rb = 8 * a.p;                              // rows of the work-group
-  const int row0 = (blockIdx.x - a.nsel_wg) * rb;
+  // XCD-aware rows: work-groups are dealt to the 8 XCDs in turn, so base
+  // work-group b runs on XCD (b + nsel_wg) mod 8; the blocks that share an
+  // XCD take contiguous rows, and a selected channel's refinement line
+  // (whose rows span several blocks) is fetched into that XCD's L2 once
+  // instead of by every XCD
+  int row0;
+  {
+    const int nb = a.m / rb, b = blockIdx.x - a.nsel_wg;
+    const int q8 = nb >> 3, r8 = nb & 7, x8 = b & 7;
+    row0 = (x8 * q8 + min(x8, r8) + (b >> 3)) * rb;
+  }
   const int ngrp = a.k / kWGroup, nseg = a.k / kWSeg;
   const uint32_t row_bytes = (uint32_t)a.k * B / 8;
   const int n_sel = a.kout > 0 ? a.nchunks * a.kout : 0;
