@@ -35,6 +35,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 #include "sf_decode_kernels.h"
 #include "sf_internal.h"
@@ -131,6 +134,7 @@ struct WArgs {
   uint32_t* calls;      // [kWCalls] 64-bit counters of started wavefronts, kWCallStride words apart
   uint32_t* status;     // set nonzero when a wait expired
   int32_t m, k, r, top_k, chunk, kout, nchunks, nsel_wg, ns, p;
+  int32_t merged;       // the selecting work-groups go on to their own rows
 };
 
 // The call's epoch, without host state (so that a captured graph replays
@@ -201,7 +205,7 @@ __device__ inline uint32_t lanes_below(uint64_t mask) {
 __device__ __attribute__((always_inline)) inline void select_chunk_wave(const WArgs& a, uint32_t* hist, uint32_t* xl,
                                                                        const float* __restrict__ x, int c0, int n,
                                                                        int k, int kout, int32_t* __restrict__ out,
-                                                                       uint64_t* __restrict__ tags) {
+                                                                       uint64_t* __restrict__ tags, uint64_t& started) {
   const int lane = threadIdx.x & 63;
   const int kk = min(k, n);
   const int rounds = (n + 63) / 64;
@@ -222,7 +226,7 @@ __device__ __attribute__((always_inline)) inline void select_chunk_wave(const WA
   }
   // counted after the staging loads, so that waiting for them does not wait
   // for the atomic
-  const uint64_t started = start_count(a);
+  started = start_count(a);
   // the block's values: u[j] of element (r0 + j) 64 + lane, 0 past the chunk
   auto load_block = [&](int r0, uint32_t (&u)[kR]) {
 #pragma unroll
@@ -416,7 +420,9 @@ __global__ void __launch_bounds__(kWMaxThreads) w_gemv(WArgs a) {
   __shared__ WLds s;
   extern __shared__ float4 xs4[];                      // x, k / 4 units, rotated (xswz)
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  if ((int)blockIdx.x < a.nsel_wg) {
+  uint64_t started = 0ull;                             // the call's epoch: epoch_of(started)
+  const bool selecting = (int)blockIdx.x < a.nsel_wg;
+  if (selecting) {
     // the selection is a chain of dependent steps that the row work-groups
     // wait for at their end: it takes the issue slots first
     __builtin_amdgcn_s_setprio(3);
@@ -427,11 +433,15 @@ __global__ void __launch_bounds__(kWMaxThreads) w_gemv(WArgs a) {
       // the chunks of one work-group are disjoint ranges of k: each
       // wavefront stages its chunk at the chunk's own place in the x area
       select_chunk_wave(a, s.hist[wv], reinterpret_cast<uint32_t*>(xs4) + c0, a.x, c0, min(a.chunk, a.k - c0),
-                        a.top_k, a.kout, a.sel + (int64_t)q * a.kout, a.tags + (int64_t)q * a.kout);
+                        a.top_k, a.kout, a.sel + (int64_t)q * a.kout, a.tags + (int64_t)q * a.kout, started);
     } else {
-      start_count(a);                                  // every wavefront counts itself
+      started = start_count(a);                        // every wavefront counts itself, once
     }
-    return;
+    if (!a.merged) return;
+    // merged: this work-group goes on to its own rows once every wavefront
+    // is done with the selection's staging area
+    __builtin_amdgcn_s_setprio(0);
+    __syncthreads();
   }
   const int rb = 8 * a.p;                              // rows of the work-group
   // XCD-aware rows: work-groups are dealt to the 8 XCDs in turn, so base
@@ -441,7 +451,7 @@ __global__ void __launch_bounds__(kWMaxThreads) w_gemv(WArgs a) {
   // instead of by every XCD
   int row0;
   {
-    const int nb = a.m / rb, b = blockIdx.x - a.nsel_wg;
+    const int nb = a.m / rb, b = a.merged ? (int)blockIdx.x : (int)blockIdx.x - a.nsel_wg;
     const int q8 = nb >> 3, r8 = nb & 7, x8 = b & 7;
     row0 = (x8 * q8 + min(x8, r8) + (b >> 3)) * rb;
   }
@@ -473,8 +483,8 @@ __global__ void __launch_bounds__(kWMaxThreads) w_gemv(WArgs a) {
     }
   }
   // counted after the code loads (waiting for them then does not wait for
-  // the atomic)
-  const uint64_t started = start_count(a);
+  // the atomic); a wavefront that selected has counted already
+  if (!selecting) started = start_count(a);
   // the first tile of the selection, speculatively: an entry is valid once
   // it carries this call's epoch
   constexpr int kSpec = kWTile / 256;
@@ -643,6 +653,33 @@ extern "C" sf_status sf_w_quantize(const sf_wgeom* g, const float* w, uint8_t* c
   return SF_OK;
 }
 
+// Work-groups of w_gemv<b> (threads, dynamic LDS) resident at once on the
+// current device; cached per shape.
+static int resident_wgs(int b, int threads, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, int, int, size_t>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1 << 30;
+  const auto key = std::make_tuple(dev, b, threads, lds);
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    const auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  int per_cu = 0, cus = 0;
+  hipError_t e = b == 2   ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, w_gemv<2>, threads, lds)
+                 : b == 3 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, w_gemv<3>, threads, lds)
+                          : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, w_gemv<4>, threads, lds);
+  if (e != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 1 << 30;      // unknown: the extra selecting work-groups
+  }
+  const int n = per_cu * cus;
+  std::lock_guard<std::mutex> lk(mu);
+  cache[key] = n;
+  return n;
+}
+
 extern "C" sf_status sf_w_gemv_workspace_words(const sf_wgeom* g, int32_t* words) {
   clear_error();
   sf_status s = check_wgeom(g);
@@ -685,8 +722,14 @@ extern "C" sf_status sf_w_gemv(const sf_wgeom* g, const uint8_t* codes, const fl
   a.calls = workspace;
   a.tags = reinterpret_cast<uint64_t*>(workspace + kWCallStride * kWCalls);
   a.status = workspace + kWCallStride * kWCalls + 2 * (int64_t)a.nchunks * a.kout + 1;   // the last word
-  const dim3 grid((unsigned)(a.nsel_wg + g->m / (8 * a.p)));
+  // the selecting work-groups are extra ones, dispatched first, while the
+  // whole launch fits the device's resident work-groups; when it would not,
+  // the first row work-groups select before taking their rows (one resident
+  // wave: no work-group waits for another to leave)
+  const int nb = g->m / (8 * a.p);
   const size_t lds = (size_t)g->k * sizeof(float);
+  a.merged = (a.nsel_wg > 0 && a.nsel_wg <= nb && a.nsel_wg + nb > resident_wgs(g->base_bits, threads, lds)) ? 1 : 0;
+  const dim3 grid((unsigned)(a.merged ? nb : a.nsel_wg + nb));
   hipStream_t st = (hipStream_t)stream;
   switch (g->base_bits) {
     case 2: hipLaunchKernelGGL(w_gemv<2>, grid, dim3(threads), lds, st, a); break;
