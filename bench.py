@@ -226,9 +226,11 @@ def gemv_record(calls=32, reps=10):
         assert int(ws[-1].item()) == 0, "a GEMV wait expired"
         us = e0.elapsed_time(e1) * 1e3 / (reps * calls)
         nbytes = m * k * b // 8 + m * (k // 128) * 8 + n_sel * m * r // 8 + k * 4 + m * 4 + n_sel * 4
+        traffic = measured_traffic(None, os.path.join(ROOT, "profiles", "weight_gemv_llama8b_projections.md"))
         out[name] = {"m": m, "k": k, "base_bits": b, "refine_bits": r, "top_k": top_k, "chunk": chunk,
                      "us_per_call": us, "algorithmic_bytes": nbytes, "gbps": nbytes / (us * 1e-6) / 1e9,
                      "frac_of_peak": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS,
+                     "traffic": traffic.get(name),
                      "timing": f"{calls} calls on distinct activations in one HIP graph, {reps} replays"}
         del graph, xs, ys, sels, codes, scales, cols
         torch.cuda.empty_cache()
@@ -269,11 +271,11 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, path=None):
     """HBM bytes per launch of each kernel from the committed counter summary
     (rocprofv3 FETCH_SIZE / WRITE_SIZE, scaled by a copy of known size), or {}
     when there is none or it was taken on other library sources."""
-    path = os.path.join(ROOT, "profiles", f"decode_step_{workload}_hbm_traffic.md")
+    path = path or os.path.join(ROOT, "profiles", f"decode_step_{workload}_hbm_traffic.md")
     if not os.path.exists(path):
         return {}
     vals, sha = {}, None
