@@ -13,6 +13,7 @@ a roofline record of the dominant kernel (the single-launch decode kernel, or
 the score or attention pass of the five-kernel form) timed live with HIP
 events, the CPU oracle timed on a bounded sample on the host, and secondary
 measurements (the five-kernel form beside the single launch; 32K context; the
+multi-step run's shape (3-bit codes, 8,192 tokens) on the device tier; the
 16-sequence batch over distinct layers; host-pinned refinement store over 64
 AR(1) steps: cold and warm step time, hit rate and bytes fetched; the
 multi-step reuse run; the weight-side refinement GEMV at the Llama-3.1-8B
@@ -642,6 +643,20 @@ def main():
                               "kernels_avg_ms": {k: v for k, v in kt2.items() if not k.endswith("_median")},
                               "step_hbm_gbps": b2 / (h2["ms_per_step"] * 1e-3) / 1e9,
                               "step_frac_of_peak": b2 / (h2["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+        w5 = W.WORKLOADS["llama8b_reuse"]
+        log("secondary: llama8b_reuse shape on the device tier (3-bit base codes)")
+        h5, kt5, f5 = headline(w5, B.SF_TIER_DEVICE, args.steps, args.warmup)
+        l5 = w5.seq_lengths()
+        b5 = algorithmic_bytes(w5, l5) * w5.layers
+        kb5 = kernel_bytes(w5, l5)
+        sec["llama8b_reuse_device"] = {
+            "steps_per_s": 1e3 / h5["ms_per_step"], "ms_per_step": h5["ms_per_step"],
+            "us_per_layer": 1e3 * h5["ms_per_step"] / w5.layers, "launch": h5["launch"],
+            "kernels_per_layer": f5, "ctx": int(l5[0]), "base_bits": w5.base_bits, "refine_bits": w5.refine_bits,
+            "top_t": w5.top_t, "kernels_avg_ms": {k: v for k, v in kt5.items() if not k.endswith("_median")},
+            "kernels_gbps": {k: x_bytes_per_ms(kb5[k], kt5[k]) for k in kb5},
+            "step_hbm_gbps": b5 / (h5["ms_per_step"] * 1e-3) / 1e9,
+            "step_frac_of_peak": b5 / (h5["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBPS}
         w4 = W.Workload(**{**W.WORKLOADS["qwen8b_b16"].__dict__, "layers": 4})
         log("secondary: qwen8b_b16 over 4 distinct layers")
         h4, kt4, f4 = headline(w4, B.SF_TIER_DEVICE, args.steps, args.warmup)

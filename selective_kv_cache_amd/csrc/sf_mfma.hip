@@ -1,5 +1,5 @@
 // Matrix-core (CDNA4 MFMA) forms of the score pass and of the base attention
-// pass, for 2-bit base codes and GQA groups of up to 4 query heads.
+// pass, for 2- and 3-bit base codes and GQA groups of up to 4 query heads.
 //
 // Logits (page "StrataFlux -- Selective precision streaming -- What does it
 // mean?", paragraph "Which tiles count ...": scores from the resident low-bit
@@ -25,6 +25,15 @@
 // gave errors near 1e-4 of the result, bit 2 near 2e-5, bits 4-8 the fp32
 // level, 1e-6).  The codes of 8 tokens at one element are gathered with one
 // v_perm_b32 per token pair, so the packed rows are read as they are stored.
+//
+// 3-bit codes straddle dword boundaries.  Row n of a P.V tile stands for
+// elements 8n + tt (tile tt), so the lane of row n needs the 24-bit group of
+// codes 8n .. 8n + 7 of each of its tokens: bits 24n .. 24n + 23 of the row,
+// taken from two dwords with one funnel shift (v_alignbit_b32).  Two byte
+// permutes pair the groups of two tokens (codes 0-3 and 4-7 of each in the
+// two halves), and a shift and a mask per code put it at mantissa bit 4-7.
+// The logit product takes a lane's 32 codes (96 bits) as four such groups,
+// each half spread to one code per byte (decode_b3).
 #include <math.h>
 #include <stddef.h>
 
@@ -42,19 +51,23 @@ namespace sfk {
 // maximum over the group to the scores and the level-1 histogram.
 // ---------------------------------------------------------------------------
 constexpr int kSRing = 4;                      // stages per wavefront
-constexpr int kSRingLoads = 2;                 // direct loads per stage
 
+template <int BB>
 struct SStage {
-  uint8_t k[32 * 32];
+  uint8_t k[32 * 16 * BB];                     // one 32-token chunk's K rows, as stored
   float2 ks[32];
 };
 
-template <int G, int NW, bool Batched>
+template <int G, int NW, bool Batched, int BB = 2>
 __global__ void __launch_bounds__(64 * NW) score_mfma(DecodeParams p) {
   static_assert(NW >= 4, "waves 0-3 prepare the query digits");
+  static_assert(BB == 2 || BB == 3, "2- or 3-bit codes");
+  constexpr int RB = 16 * BB;                    // bytes of a packed row
+  constexpr int kSRingLoads = BB == 2 ? 2 : 3;   // direct loads per stage
+  using SSt = SStage<BB>;
   __shared__ QPrep qp;
   __shared__ uint32_t lhist[kHistBins];
-  __shared__ SStage ring[NW][kSRing];
+  __shared__ SSt ring[NW][kSRing];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kvh = blockIdx.y;
@@ -67,15 +80,17 @@ __global__ void __launch_bounds__(64 * NW) score_mfma(DecodeParams p) {
   const int nsp = (int)(hi - lo);
   const int nchunks = (nsp + 31) / 32;
   const int nmine = nchunks > wid ? (nchunks - wid + NW - 1) / NW : 0;
-  // stage i <- chunk wid + NW i of the wave's own chunks: lane L loads half
-  // L&1 of K row L/2 and scale word L; the resources end at the split's end
-  // (tokens past it read as zeros)
-  const rsrc_t rK = make_rsrc(p.kc + t0 * 32, (uint32_t)nsp * 32u);
+  // stage i <- chunk wid + NW i of the wave's own chunks: lane L loads bytes
+  // 16L .. 16L + 15 of the chunk's K rows (2-bit: half L&1 of row L/2; 3-bit:
+  // lanes L < 32 also bytes 1024 + 16L ..) and scale word L; the resources
+  // end at the split's end (tokens past it read as zeros)
+  const rsrc_t rK = make_rsrc(p.kc + t0 * RB, (uint32_t)nsp * (uint32_t)RB);
   const rsrc_t rS = make_rsrc(p.ks + t0 * 2, (uint32_t)nsp * 8u);
   const uint32_t oK = 16u * (uint32_t)lane, oS = 4u * (uint32_t)lane;
-  auto issue = [&](int i, SStage& st) {
+  auto issue = [&](int i, SSt& st) {
     const uint32_t c = (uint32_t)(wid + NW * i);
-    bdma16(rK, oK, c * 1024u, st.k);
+    bdma16(rK, oK, c * (32u * RB), st.k);
+    if (BB == 3 && lane < 32) bdma16(rK, oK + 1024u, c * (32u * RB), st.k + 1024);
     bdma4(rS, oS, c * 256u, st.ks);
   };
   // no selection, no histogram; the summed-probability score builds its own
@@ -85,7 +100,7 @@ __global__ void __launch_bounds__(64 * NW) score_mfma(DecodeParams p) {
   for (int k = 0; k < kSRing - 1; ++k)
     if (k < nmine) issue(k, ring[wid][k]);
   v4i a0, a1;
-  prep_query<G>(qx, qp, a0, a1);
+  prep_query<G, BB>(qx, qp, a0, a1);
   // logits in log2 units (1/sqrt(D) and log2(e) folded into the per-head
   // constants): the attention pass's softmax takes them as they are
   constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
@@ -95,35 +110,63 @@ __global__ void __launch_bounds__(64 * NW) score_mfma(DecodeParams p) {
   float* scores = p.scores + (int64_t)kvh * p.ntot + (a - p.off0) + lo;
   float* lgo = p.logits + ((int64_t)kvh * p.ntot + (a - p.off0) + lo) * G;
   const uint32_t ring0 = lds_addr(&ring[wid][0]);
-  const uint32_t aK = ring0 + (uint32_t)(t * 32 + 8 * hl);
-  const uint32_t aS = ring0 + (uint32_t)(offsetof(SStage, ks) + 8 * t);
+  // the lane's 32 codes of token t: bytes 8 hl .. (2-bit) or 12 hl .. (3-bit)
+  const uint32_t aK = ring0 + (uint32_t)(t * RB + 4 * BB * hl);
+  const uint32_t aS = ring0 + (uint32_t)(offsetof(SSt, ks) + 8 * t);
   const int hx = hl >> 1;                         // the tile a lane writes the score of
   const uint32_t hist0 = lds_addr(&lhist[0]);
   auto body = [&](auto kc, int i) {
     constexpr int k = decltype(kc)::value;        // stage of chunk i
-    constexpr int OFF = k * (int)sizeof(SStage);
+    constexpr int OFF = k * (int)sizeof(SSt);
     if (i + kSRing - 1 < nmine) issue(i + kSRing - 1, ring[wid][(k + kSRing - 1) % kSRing]);
     // this wave's loads complete in order: stage i is in once no more than
     // the stages issued after it are outstanding (stores only add to the count)
     wait_stages<kSRingLoads, kSRing - 1>(min(kSRing - 1, nmine - 1 - i));
     const int c = wid + NW * i;
-    uint64_t kw[2], ks[2];
-    asm volatile(
-        "ds_read_b64 %0, %4 offset:%6\n\t"
-        "ds_read_b64 %1, %4 offset:%7\n\t"
-        "ds_read_b64 %2, %5 offset:%6\n\t"
-        "ds_read_b64 %3, %5 offset:%8\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(kw[0]), "=&v"(kw[1]), "=&v"(ks[0]), "=&v"(ks[1])
-        : "v"(aK), "v"(aS), "n"(OFF), "n"(OFF + 512), "n"(OFF + 128)
-        : "memory");
+    uint32_t kw[2][3];
+    uint64_t ks[2];
+    if constexpr (BB == 2) {
+      uint64_t k0, k1;
+      asm volatile(
+          "ds_read_b64 %0, %4 offset:%6\n\t"
+          "ds_read_b64 %1, %4 offset:%7\n\t"
+          "ds_read_b64 %2, %5 offset:%6\n\t"
+          "ds_read_b64 %3, %5 offset:%8\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(k0), "=&v"(k1), "=&v"(ks[0]), "=&v"(ks[1])
+          : "v"(aK), "v"(aS), "n"(OFF), "n"(OFF + 16 * RB), "n"(OFF + 128)
+          : "memory");
+      kw[0][0] = (uint32_t)k0;
+      kw[0][1] = (uint32_t)(k0 >> 32);
+      kw[1][0] = (uint32_t)k1;
+      kw[1][1] = (uint32_t)(k1 >> 32);
+      kw[0][2] = kw[1][2] = 0u;
+    } else {
+      asm volatile(
+          "ds_read_b32 %0, %8 offset:%10\n\t"
+          "ds_read_b32 %1, %8 offset:%11\n\t"
+          "ds_read_b32 %2, %8 offset:%12\n\t"
+          "ds_read_b32 %3, %8 offset:%13\n\t"
+          "ds_read_b32 %4, %8 offset:%14\n\t"
+          "ds_read_b32 %5, %8 offset:%15\n\t"
+          "ds_read_b64 %6, %9 offset:%10\n\t"
+          "ds_read_b64 %7, %9 offset:%16\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(kw[0][0]), "=&v"(kw[0][1]), "=&v"(kw[0][2]), "=&v"(kw[1][0]), "=&v"(kw[1][1]), "=&v"(kw[1][2]),
+            "=&v"(ks[0]), "=&v"(ks[1])
+          : "v"(aK), "v"(aS), "n"(OFF), "n"(OFF + 4), "n"(OFF + 8), "n"(OFF + 16 * RB), "n"(OFF + 16 * RB + 4),
+            "n"(OFF + 16 * RB + 8), "n"(OFF + 128)
+          : "memory");
+    }
     const bool full = 32 * c + 32 <= nsp;         // every token of the chunk inside the split
     float lg[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const uint2 w = __builtin_bit_cast(uint2, kw[j]);
       v4i b0, b1;
-      decode_b2(w.x, w.y, b0, b1);
+      if constexpr (BB == 2)
+        decode_b2(kw[j][0], kw[j][1], b0, b1);
+      else
+        decode_b3(kw[j][0], kw[j][1], kw[j][2], b0, b1);
       v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, v4i{0, 0, 0, 0}, 0, 0, 0);
       D = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, D, 0, 0, 0);
       const float x = logit_scaled(D, __builtin_bit_cast(float2, ks[j]), scale, sumq);
@@ -295,22 +338,21 @@ bool launch_softmax_scores(const DecodeParams& p, dim3 grid, hipStream_t st) {
 // pass left, V codes (1 KiB, as stored) and V scales (256 B).  K is not read
 // again.
 constexpr int kRing = 4;                       // stages per wavefront; kRing - 1 chunks in flight
-constexpr int kRingLoads = 3;                  // direct loads per stage
 
-template <int G>
+template <int G, int BB = 2>
 struct Stage {
   float lg[32 * G];
-  uint8_t v[32 * 32];
+  uint8_t v[32 * 16 * BB];
   float2 vs[32];
 };
 
-template <int G, int NW>
+template <int G, int NW, int BB = 2>
 struct MfmaLds {
   alignas(16) _Float16 wt[NW][2 * G][32];   // per wave: P.V weights [column][kappa]: hi parts, then lo parts
   alignas(16) _Float16 wzero[8];            // weight columns >= 2G read zeros
   float mw[NW][G], lw[NW][G];
   union {
-    Stage<G> ring[NW][kRing];
+    Stage<G, BB> ring[NW][kRing];
     float accw[NW][2 * G][kHeadDim + 1];    // after the stream: per-wave P.V, hi and lo columns
                                             // (rows padded by a word: the 16 columns one write spans hit different banks)
   } u;
@@ -350,10 +392,59 @@ __device__ inline void read_stage(uint32_t aL, uint32_t aS, const uint32_t (&aV)
       : "memory");
 }
 
-template <int G, int NW, bool Batched>
+// The 3-bit form: the two dwords holding row n's 24-bit group of each of
+// the lane's 8 tokens (4rg + v: vw[4v], vw[4v + 1]; 16 + 4rg + v: vw[4v + 2],
+// vw[4v + 3]).  aV points at the first dword of token 4rg's group.
+struct StageRegs3 {
+  float lg[2];
+  uint64_t vsc[2];
+  uint32_t vw[16];
+};
+
+template <int G, int OFF>
+__device__ inline void read_stage3(uint32_t aL, uint32_t aS, uint32_t aV, StageRegs3& r) {
+  constexpr int RB = 48, T16 = 16 * RB;
+  asm volatile(
+      "ds_read_b32 %0, %20 offset:%23\n\t"
+      "ds_read_b32 %1, %20 offset:%24\n\t"
+      "ds_read_b64 %2, %21 offset:%23\n\t"
+      "ds_read_b64 %3, %21 offset:%25\n\t"
+      "ds_read_b32 %4, %22 offset:%23\n\t"
+      "ds_read_b32 %5, %22 offset:%26\n\t"
+      "ds_read_b32 %6, %22 offset:%27\n\t"
+      "ds_read_b32 %7, %22 offset:%28\n\t"
+      "ds_read_b32 %8, %22 offset:%29\n\t"
+      "ds_read_b32 %9, %22 offset:%30\n\t"
+      "ds_read_b32 %10, %22 offset:%31\n\t"
+      "ds_read_b32 %11, %22 offset:%32\n\t"
+      "ds_read_b32 %12, %22 offset:%33\n\t"
+      "ds_read_b32 %13, %22 offset:%34\n\t"
+      "ds_read_b32 %14, %22 offset:%35\n\t"
+      "ds_read_b32 %15, %22 offset:%36\n\t"
+      "ds_read_b32 %16, %22 offset:%37\n\t"
+      "ds_read_b32 %17, %22 offset:%38\n\t"
+      "ds_read_b32 %18, %22 offset:%39\n\t"
+      "ds_read_b32 %19, %22 offset:%40\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r.lg[0]), "=&v"(r.lg[1]), "=&v"(r.vsc[0]), "=&v"(r.vsc[1]), "=&v"(r.vw[0]), "=&v"(r.vw[1]),
+        "=&v"(r.vw[2]), "=&v"(r.vw[3]), "=&v"(r.vw[4]), "=&v"(r.vw[5]), "=&v"(r.vw[6]), "=&v"(r.vw[7]),
+        "=&v"(r.vw[8]), "=&v"(r.vw[9]), "=&v"(r.vw[10]), "=&v"(r.vw[11]), "=&v"(r.vw[12]), "=&v"(r.vw[13]),
+        "=&v"(r.vw[14]), "=&v"(r.vw[15])
+      : "v"(aL), "v"(aS), "v"(aV), "n"(OFF), "n"(OFF + 16 * G * 4), "n"(OFF + 128), "n"(OFF + 4),
+        "n"(OFF + T16), "n"(OFF + T16 + 4), "n"(OFF + RB), "n"(OFF + RB + 4), "n"(OFF + T16 + RB),
+        "n"(OFF + T16 + RB + 4), "n"(OFF + 2 * RB), "n"(OFF + 2 * RB + 4), "n"(OFF + T16 + 2 * RB),
+        "n"(OFF + T16 + 2 * RB + 4), "n"(OFF + 3 * RB), "n"(OFF + 3 * RB + 4), "n"(OFF + T16 + 3 * RB),
+        "n"(OFF + T16 + 3 * RB + 4)
+      : "memory");
+}
+
+template <int G, int NW, bool Batched, int BB = 2>
 __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh, uint8_t* smem) {
-  using Lds = MfmaLds<G, NW>;
-  using St = Stage<G>;
+  static_assert(BB == 2 || BB == 3, "2- or 3-bit codes");
+  constexpr int RB = 16 * BB;                      // bytes of a packed row
+  constexpr int kRingLoads = BB == 2 ? 3 : 4;      // direct loads per stage
+  using Lds = MfmaLds<G, NW, BB>;
+  using St = Stage<G, BB>;
   Lds& s = *reinterpret_cast<Lds*>(smem);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -370,19 +461,24 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
 
   // Stage i of this wave <- chunk wid + NW*i.  Lane L loads the scale word L
   // of the chunk (token L/2), lanes L < 8G the logits' bytes [16L, 16L+16),
-  // and half L&1 of V row (L/2) ^ ((L/8) & 3): row r of the chunk sits at
-  // stage row r ^ ((r/4) & 3), so that the four rows one P.V read takes
-  // (4rg + v, rg = 0..3) fall in different LDS banks.  The resources end at
-  // the split's end: tokens past it read as zeros.
-  const rsrc_t rV = make_rsrc(p.vc + t0 * 32, (uint32_t)nsp * 32u);
+  // and 2-bit codes: half L&1 of V row (L/2) ^ ((L/8) & 3): row r of the
+  // chunk sits at stage row r ^ ((r/4) & 3), so that the four rows one P.V
+  // read takes (4rg + v, rg = 0..3) fall in different LDS banks; 3-bit codes:
+  // bytes 16L .. 16L + 15 of the chunk's rows as stored (and lanes L < 32
+  // bytes 1024 + 16L ..; rows 48 bytes apart already spread the four rows
+  // over the banks).  The resources end at the split's end: tokens past it
+  // read as zeros.
+  const rsrc_t rV = make_rsrc(p.vc + t0 * RB, (uint32_t)nsp * (uint32_t)RB);
   const rsrc_t rS = make_rsrc(p.vs + t0 * 2, (uint32_t)nsp * 8u);
   const rsrc_t rL = make_rsrc(p.logits + ((int64_t)kvh * p.ntot + (a - p.off0) + lo) * G, (uint32_t)nsp * G * 4u);
-  const uint32_t oV = (uint32_t)(((lane >> 1) ^ ((lane >> 3) & 3)) * 32 + 16 * (lane & 1));
+  const uint32_t oV =
+      BB == 2 ? (uint32_t)(((lane >> 1) ^ ((lane >> 3) & 3)) * 32 + 16 * (lane & 1)) : 16u * (uint32_t)lane;
   const uint32_t oS = 4u * (uint32_t)lane, oL = 16u * (uint32_t)lane;
   auto issue = [&](int i, St& st) {
     const uint32_t c = (uint32_t)(wid + NW * i);
     if (lane < 8 * G) bdma16(rL, oL, c * (32u * G * 4u), st.lg);
-    bdma16(rV, oV, c * 1024u, st.v);
+    bdma16(rV, oV, c * (32u * RB), st.v);
+    if (BB == 3 && lane < 32) bdma16(rV, oV + 1024u, c * (32u * RB), st.v + 1024);
     bdma4(rS, oS, c * 256u, st.vs);
   };
 #pragma unroll
@@ -418,9 +514,12 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   const uint32_t wtHi = lds_addr(&s.wt[wid][hlc][2 * t]), wtLo = lds_addr(&s.wt[wid][G + hlc][2 * t]);
   const uint32_t aL = ring0 + (uint32_t)(offsetof(St, lg) + 4 * (t * G + hlc));
   const uint32_t aS = ring0 + (uint32_t)(offsetof(St, vs) + 8 * t);
-  uint32_t aV[4];                                 // token 4rg + v at stage row 4rg + (v ^ rg)
+  uint32_t aV[4];                                 // 2-bit: token 4rg + v at stage row 4rg + (v ^ rg)
 #pragma unroll
   for (int v = 0; v < 4; ++v) aV[v] = ring0 + (uint32_t)(offsetof(St, v) + (4 * rg + (v ^ rg)) * 32 + 4 * vdw);
+  // 3-bit: row n's group (bits 24n ..) starts in dword 3n/4 at bit 24n % 32
+  const uint32_t aV3 = ring0 + (uint32_t)(offsetof(St, v) + 4 * rg * RB + 4 * ((3 * n) >> 2));
+  const uint32_t gsh = (uint32_t)((24 * n) & 31);
   // rows hl < G hold heads; the others take no part
   const uint64_t rows = G >= 4 ? ~0ull : (1ull << (16 * (G & 3))) - 1ull;
   const float ninf = -INFINITY;
@@ -451,7 +550,16 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
     const uint32_t y0 = (vm & 0xFFFFu) | (vm << 16), y1 = (vm >> 16) | (vm & 0xFFFF0000u);
     const uint64_t mk[2] = {((uint64_t)y0 | ((uint64_t)y0 << 32)) & rows, ((uint64_t)y1 | ((uint64_t)y1 << 32)) & rows};
     StageRegs R;
-    read_stage<G, k * (int)sizeof(St)>(aL, aS, aV, R);
+    [[maybe_unused]] StageRegs3 R3;
+    if constexpr (BB == 2) {
+      read_stage<G, k * (int)sizeof(St)>(aL, aS, aV, R);
+    } else {
+      read_stage3<G, k * (int)sizeof(St)>(aL, aS, aV3, R3);
+      R.lg[0] = R3.lg[0];
+      R.lg[1] = R3.lg[1];
+      R.vsc[0] = R3.vsc[0];
+      R.vsc[1] = R3.vsc[1];
+    }
     // logits (log2 units, as the score pass kept them); -inf where the token
     // takes no part
     float lg[2];
@@ -516,21 +624,52 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
       lds_write_u32(wtLo, __builtin_bit_cast(uint32_t, wlo));
     }
     const v8h bw = lds_read_v8h(wtR);
-    const uint32_t* vw = R.vw;
-    // each 16-bit half of P holds the 8 codes (2 bits each, code tt at bit
-    // 2tt) of one token; code tt goes in at mantissa bit code_bit(tt) >= 4:
-    // codes 0-1 from P << 4, 2-4 from P, 5-7 from P >> 6 (the masks keep
-    // each half's own bits)
-    uint32_t P[4];
+    if constexpr (BB == 2) {
+      const uint32_t* vw = R.vw;
+      // each 16-bit half of P holds the 8 codes (2 bits each, code tt at bit
+      // 2tt) of one token; code tt goes in at mantissa bit code_bit(tt) >= 4:
+      // codes 0-1 from P << 4, 2-4 from P, 5-7 from P >> 6 (the masks keep
+      // each half's own bits)
+      uint32_t P[4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) P[v] = __builtin_amdgcn_perm(vw[2 * v + 1], vw[2 * v], psel);
+      for (int v = 0; v < 4; ++v) P[v] = __builtin_amdgcn_perm(vw[2 * v + 1], vw[2 * v], psel);
 #pragma unroll
-    for (int tt = 0; tt < 8; ++tt) {
-      const uint32_t msk = 0x00030003u << code_bit(tt);
-      v4u av;
+      for (int tt = 0; tt < 8; ++tt) {
+        const uint32_t msk = 0x00030003u << code_bit(tt);
+        v4u av;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) av[v] = (tt < 2 ? P[v] << 4 : tt < 5 ? P[v] : P[v] >> 6) & msk;
-      acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, av), bw, acc[tt], 0, 0, 0);
+        for (int v = 0; v < 4; ++v) av[v] = (tt < 2 ? P[v] << 4 : tt < 5 ? P[v] : P[v] >> 6) & msk;
+        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, av), bw, acc[tt], 0, 0, 0);
+      }
+    } else {
+      // the 24-bit groups of the token pair (4rg + v, 16 + 4rg + v); P03
+      // holds bits 0-15 of each in its two halves (codes 0-4), P47 bits
+      // 8-23 (codes 4-7 at bits 4, 7, 10, 13); code tt goes in at mantissa
+      // bit code_bit3(tt): 0 and 1 from P03 << 4, 2 from P03, 3 from
+      // P03 >> 2, 4 and 5 from P47, 6 and 7 from P47 >> 6
+      uint32_t P03[4], P47[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const uint32_t ga = __builtin_amdgcn_alignbit(R3.vw[4 * v + 1], R3.vw[4 * v], gsh);
+        const uint32_t gb = __builtin_amdgcn_alignbit(R3.vw[4 * v + 3], R3.vw[4 * v + 2], gsh);
+        P03[v] = __builtin_amdgcn_perm(gb, ga, 0x05040100u);
+        P47[v] = __builtin_amdgcn_perm(gb, ga, 0x06050201u);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        const uint32_t msk = 0x00070007u << code_bit3(tt);
+        v4u av;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint32_t x = tt < 2    ? P03[v] << 4
+                             : tt == 2 ? P03[v]
+                             : tt == 3 ? P03[v] >> 2
+                             : tt < 6  ? P47[v]
+                                       : P47[v] >> 6;
+          av[v] = x & msk;
+        }
+        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, av), bw, acc[tt], 0, 0, 0);
+      }
     }
   };
   for (int i = 0; i < nmine; i += kRing) {
@@ -562,7 +701,7 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   if (n < 2 * G) {
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
-      const float f = __builtin_ldexpf(1.0f, 24 - code_bit(tt) - se);
+      const float f = __builtin_ldexpf(1.0f, 24 - (BB == 2 ? code_bit(tt) : code_bit3(tt)) - se);
 #pragma unroll
       for (int j = 0; j < 4; ++j) s.u.accw[wid][n][32 * rg + 8 * j + tt] = fmaf(acc[tt][j], f, t1n);
     }
@@ -592,31 +731,31 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   }
 }
 
-template <int G, int NW, bool Batched>
+template <int G, int NW, bool Batched, int BB = 2>
 __global__ void __launch_bounds__(64 * NW) attend_mfma(DecodeParams p) {
-  __shared__ __align__(16) uint8_t smem[cmax(sizeof(SelLds<2, G, NW, 16>), sizeof(MfmaLds<G, NW>))];
+  __shared__ __align__(16) uint8_t smem[cmax(sizeof(SelLds<BB, G, NW, 16>), sizeof(MfmaLds<G, NW, BB>))];
   if ((int)blockIdx.x < p.n_sel_blk)
-    selected_block_any<2, G, NW, true, Batched>(p, blockIdx.x, blockIdx.y, smem);
+    selected_block_any<BB, G, NW, true, Batched>(p, blockIdx.x, blockIdx.y, smem);
   else
-    base_split_mfma<G, NW, Batched>(p, blockIdx.x - p.n_sel_blk, blockIdx.y, smem);
+    base_split_mfma<G, NW, Batched, BB>(p, blockIdx.x - p.n_sel_blk, blockIdx.y, smem);
 }
 
-template <bool Batched>
+template <bool Batched, int BB>
 static bool launch_score_mfma_b(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev) {
   switch (p.grp) {
-    case 1: sf_launch(score_mfma<1, kScoreWaves, Batched>, grid, dim3(64 * kScoreWaves), st, ev, p); return true;
-    case 2: sf_launch(score_mfma<2, kScoreWaves, Batched>, grid, dim3(64 * kScoreWaves), st, ev, p); return true;
-    case 4: sf_launch(score_mfma<4, kScoreWaves, Batched>, grid, dim3(64 * kScoreWaves), st, ev, p); return true;
+    case 1: sf_launch(score_mfma<1, kScoreWaves, Batched, BB>, grid, dim3(64 * kScoreWaves), st, ev, p); return true;
+    case 2: sf_launch(score_mfma<2, kScoreWaves, Batched, BB>, grid, dim3(64 * kScoreWaves), st, ev, p); return true;
+    case 4: sf_launch(score_mfma<4, kScoreWaves, Batched, BB>, grid, dim3(64 * kScoreWaves), st, ev, p); return true;
   }
   return false;
 }
 
-template <bool Batched>
+template <bool Batched, int BB>
 static bool launch_attend_mfma_b(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev) {
   switch (p.grp) {
-    case 1: sf_launch(attend_mfma<1, kAttendWaves, Batched>, grid, dim3(64 * kAttendWaves), st, ev, p); return true;
-    case 2: sf_launch(attend_mfma<2, kAttendWaves, Batched>, grid, dim3(64 * kAttendWaves), st, ev, p); return true;
-    case 4: sf_launch(attend_mfma<4, kAttendWaves, Batched>, grid, dim3(64 * kAttendWaves), st, ev, p); return true;
+    case 1: sf_launch(attend_mfma<1, kAttendWaves, Batched, BB>, grid, dim3(64 * kAttendWaves), st, ev, p); return true;
+    case 2: sf_launch(attend_mfma<2, kAttendWaves, Batched, BB>, grid, dim3(64 * kAttendWaves), st, ev, p); return true;
+    case 4: sf_launch(attend_mfma<4, kAttendWaves, Batched, BB>, grid, dim3(64 * kAttendWaves), st, ev, p); return true;
   }
   return false;
 }
@@ -624,13 +763,19 @@ static bool launch_attend_mfma_b(const DecodeParams& p, dim3 grid, hipStream_t s
 // Single-sequence steps take the instantiations without the batched
 // sequence search, so that their kernels' start stays as short as it can be.
 bool launch_score_mfma(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev) {
-  if (p.b != 2) return false;
-  return p.batch > 1 ? launch_score_mfma_b<true>(p, grid, st, ev) : launch_score_mfma_b<false>(p, grid, st, ev);
+  if (p.b == 2)
+    return p.batch > 1 ? launch_score_mfma_b<true, 2>(p, grid, st, ev) : launch_score_mfma_b<false, 2>(p, grid, st, ev);
+  if (p.b == 3)
+    return p.batch > 1 ? launch_score_mfma_b<true, 3>(p, grid, st, ev) : launch_score_mfma_b<false, 3>(p, grid, st, ev);
+  return false;
 }
 
 bool launch_attend_mfma(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev) {
-  if (p.b != 2) return false;
-  return p.batch > 1 ? launch_attend_mfma_b<true>(p, grid, st, ev) : launch_attend_mfma_b<false>(p, grid, st, ev);
+  if (p.b == 2)
+    return p.batch > 1 ? launch_attend_mfma_b<true, 2>(p, grid, st, ev) : launch_attend_mfma_b<false, 2>(p, grid, st, ev);
+  if (p.b == 3)
+    return p.batch > 1 ? launch_attend_mfma_b<true, 3>(p, grid, st, ev) : launch_attend_mfma_b<false, 3>(p, grid, st, ev);
+  return false;
 }
 
 }  // namespace sfk

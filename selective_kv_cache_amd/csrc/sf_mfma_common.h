@@ -31,10 +31,32 @@ __device__ inline void decode_b2(uint32_t w0, uint32_t w1, v4i& b0, v4i& b1) {
            (int)((w1 >> 6) & 0x03030303u)};
 }
 
+// Four 3-bit codes (bits 3j, j = 0..3, of w; higher bits ignored) spread to
+// the four bytes of a dword: the pair (c0, c1) stays at bits 0-5 and (c2, c3)
+// moves to bits 16-21 (one bit-field insert), then c1 and c3 move up by 5 to
+// bits 8 and 24 while c0 and c2 stay at 0 and 16.
+__device__ inline uint32_t spread3x4(uint32_t w) {
+  const uint32_t t = (w & 0x3Fu) | ((w << 10) & ~0x3Fu);
+  return ((t << 5) & 0x07000700u) | (t & 0x00070007u);
+}
+
+// 3-bit codes to the int8 B operands of the two logit MFMAs.  A lane's 32
+// codes are 96 consecutive bits of the packed row (w0, w1, w2): four groups
+// of 8 codes (24 bits each), each group's halves spread by spread3x4, so
+// byte b of dword v of operand i carries element 16i + 4v + b of the lane
+// group's 32 (the codes in their own order).
+__device__ inline void decode_b3(uint32_t w0, uint32_t w1, uint32_t w2, v4i& b0, v4i& b1) {
+  const uint32_t g0 = w0, g1 = __builtin_amdgcn_alignbit(w1, w0, 24), g2 = __builtin_amdgcn_alignbit(w2, w1, 16),
+                 g3 = w2 >> 8;
+  b0 = v4i{(int)spread3x4(g0), (int)spread3x4(g0 >> 12), (int)spread3x4(g1), (int)spread3x4(g1 >> 12)};
+  b1 = v4i{(int)spread3x4(g2), (int)spread3x4(g2 >> 12), (int)spread3x4(g3), (int)spread3x4(g3 >> 12)};
+}
+
 // Query digits and per-head constants of the score pass.  The digits are
 // stored in A-operand order: op[h][k][g] holds the 32 bytes lane group g of
 // row (h, k) feeds its two MFMAs (operand i, dword v, byte b = element
-// 32g + 16i + v + 4b, matching decode_b2's element order).
+// 32g + 16i + v + 4b for 2-bit codes, matching decode_b2's element order,
+// and 32g + 16i + 4v + b for 3-bit codes, decode_b3's).
 struct QPrep {
   alignas(16) int8_t op[4][4][4][32];   // [head][digit][lane group][byte]
   float scale[4];                        // s_h
@@ -55,8 +77,9 @@ __device__ inline float2 load_query(const float* q) {
 // digits, q = s * (d0 + d1/254 + d2/254^2 + d3/254^3), s = max|q|/127.  Then
 // each lane reads its two A operands (row = 4*head + digit, 16 bytes each of
 // lane group l/16) with two 16-byte LDS reads.
-template <int G>
+template <int G, int BB = 2>
 __device__ inline void prep_query(float2 x, QPrep& qp, v4i& a0, v4i& a1) {
+  static_assert(BB == 2 || BB == 3, "2- or 3-bit codes");
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   if (wid < 4) {
     const float amax = wave_max(fmaxf(fabsf(x.x), fabsf(x.y)));
@@ -66,7 +89,7 @@ __device__ inline void prep_query(float2 x, QPrep& qp, v4i& a0, v4i& a1) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int d = 2 * lane + e, g = d >> 5, r = d & 31;
-      const int pos = 16 * (r >> 4) + 4 * (r & 3) + ((r & 15) >> 2);
+      const int pos = BB == 3 ? r : 16 * (r >> 4) + 4 * (r & 3) + ((r & 15) >> 2);
       float rr = xs[e];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -267,8 +290,11 @@ __device__ inline float row16_max_dpp(float x) {
 }
 
 // Mantissa bit at which the P.V product takes code tt (0-7) of a token's
-// 8-element group.
+// 8-element group: 2-bit codes at bits 4, 6, 4, 6, 8, 4, 6, 8; 3-bit codes at
+// bits 4, 7, 6, 7, 4, 7, 4, 7 (every code inside the 10 mantissa bits, its
+// lowest bit at 4 or above).
 constexpr int code_bit(int tt) { return tt < 2 ? 2 * tt + 4 : tt < 5 ? 2 * tt : 2 * tt - 6; }
+constexpr int code_bit3(int tt) { return tt == 0 || tt == 4 || tt == 6 ? 4 : tt == 2 ? 6 : 7; }
 
 // Maximum over the four rows of two tiles at once: x0, x1 are a lane's
 // values of tiles 0 and 1; the result holds tile 0's maximum over lanes

@@ -52,6 +52,10 @@ SMALL = [
     dict(ctx=20_000, n_q_heads=32, n_kv_heads=8, base_bits=3, refine_bits=2, top_t=2048),  # 64-token selected blocks
     dict(ctx=300_000, n_q_heads=2, n_kv_heads=1, top_t=1000),                 # > 64 selection chunks
     dict(ctx=600_000, n_q_heads=2, n_kv_heads=1, top_t=3000),                 # bitmap beyond LDS
+    dict(ctx=777, n_q_heads=2, n_kv_heads=2, base_bits=3, refine_bits=2, top_t=50),   # 3-bit, G = 1
+    dict(ctx=1500, n_q_heads=4, n_kv_heads=2, base_bits=3, refine_bits=4, top_t=64),  # 3-bit, G = 2
+    dict(ctx=1300, n_q_heads=8, n_kv_heads=1, base_bits=3, refine_bits=2, top_t=64),  # 3-bit, G = 8
+    dict(ctx=33, n_q_heads=8, n_kv_heads=2, base_bits=3, refine_bits=8, top_t=7),     # 3-bit, one chunk + 1
 ]
 
 
@@ -61,6 +65,14 @@ def test_base_pass_precision():
     2-bit codes enter that product at fp16 mantissa bits >= 4; with codes at
     bit 0 its error on this case was 2.5e-4 (measured 1.8e-5 after)."""
     _, st = _case(W.small(cfg_id=228, ctx=1000, top_t=0))
+    assert st["max_out_err"] <= 1e-4, st
+
+
+def test_base_pass_precision_3bit():
+    """The same with 3-bit base codes: every token through the matrix-core
+    P.V with the codes cut from two dwords by a funnel shift and placed at
+    fp16 mantissa bits 4-9."""
+    _, st = _case(W.small(cfg_id=229, ctx=1000, base_bits=3, refine_bits=2, top_t=0))
     assert st["max_out_err"] <= 1e-4, st
 
 
