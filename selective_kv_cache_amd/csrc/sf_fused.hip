@@ -354,8 +354,9 @@ __device__ inline void select_by_histograms(const DecodeParams& p, FusedLds<G>& 
 // q . s over quarter qd of head_dim for each of the G heads, from the lane's
 // R-bit refinement codes in registers: four codes at a time, each taken by
 // every head (few registers live).
-template <int R, int G>
-__device__ inline void quarter_qs(const uint32_t (&kr)[8], const float* qs, int qd, float (&ds)[G]) {
+template <int R, int G, int N>
+__device__ inline void quarter_qs(const uint32_t (&kr)[N], const float* qs, int qd, float (&ds)[G]) {
+  static_assert(R <= N, "the codes fit the words");
 #pragma unroll
   for (int h = 0; h < G; ++h) ds[h] = 0.f;
 #pragma unroll
@@ -376,8 +377,9 @@ __device__ inline void quarter_qs(const uint32_t (&kr)[8], const float* qs, int 
 // Rows of a batch of selected tokens held in registers between their fetch
 // and their use: lane (tl, qd) holds quarter qd (elements 32 qd .. 32 qd +
 // 31) of token tl.
+template <int NWD = 8>
 struct SelRows {
-  uint32_t vb[2], kr[8], vr[8];   // V base codes, K and V refinement codes (r words each)
+  uint32_t vb[2], kr[NWD], vr[NWD];   // V base codes, K and V refinement codes (r <= NWD words each)
   float2 vsc;                     // V (lo, delta)
   float kd;                       // K delta
   int off;                        // the token within the range
@@ -385,14 +387,14 @@ struct SelRows {
 
 // Fetch the rows of the range's selected tokens j0 .. j0 + cnt - 1 (cnt <=
 // kFTPW, in token order).
-template <int G>
+template <int G, int NWD>
 __device__ inline void sel_fetch(const DecodeParams& p, const FusedLds<G>& s, uint32_t j0, int cnt, int kvh,
-                                 int64_t row0, int nw, SelRows& rw) {
+                                 int64_t row0, int nw, SelRows<NWD>& rw) {
   const int lane = threadIdx.x & 63, tl = lane >> 2, qd = lane & 3;
   const int r = p.r;
   rw.vb[0] = rw.vb[1] = 0u;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) rw.kr[i] = rw.vr[i] = 0u;
+  for (int i = 0; i < NWD; ++i) rw.kr[i] = rw.vr[i] = 0u;
   rw.vsc = make_float2(0.f, 0.f);
   rw.kd = 0.f;
   rw.off = 0;
@@ -418,7 +420,7 @@ __device__ inline void sel_fetch(const DecodeParams& p, const FusedLds<G>& s, ui
   const uint32_t* rv =
       reinterpret_cast<const uint32_t*>(p.ref_rows + (((int64_t)p.hkv + kvh) * p.cap + tok) * p.rb) + qd * r;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < NWD; ++i) {
     rw.kr[i] = i < r ? rk[i] : 0u;
     rw.vr[i] = i < r ? rv[i] : 0u;
   }
@@ -430,8 +432,8 @@ __device__ inline void sel_fetch(const DecodeParams& p, const FusedLds<G>& s, ui
 // base logit in LDS plus the refinement's change, the quarter dots summed
 // over the token's four lanes; the V rows through the wave's staging to the
 // P.V, where the lane holds output elements 2 lane and 2 lane + 1.
-template <int G>
-__device__ inline void sel_compute(const DecodeParams& p, FusedLds<G>& s, int w, const SelRows& rw, int cnt,
+template <int G, int NWD>
+__device__ inline void sel_compute(const DecodeParams& p, FusedLds<G>& s, int w, const SelRows<NWD>& rw, int cnt,
                                    const float (&qsum)[G], float (&m_run)[G], float (&l_run)[G],
                                    float (&acc)[G][2]) {
   static_assert(kFTPW * 4 == 64, "four lanes a token");
@@ -444,7 +446,7 @@ __device__ inline void sel_compute(const DecodeParams& p, FusedLds<G>& s, int w,
   sp.vt[w][tl][2 * qd] = rw.vb[0];
   sp.vt[w][tl][2 * qd + 1] = rw.vb[1];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < NWD; ++i)
     if (i < r) sp.vr[w][tl][qd * r + i] = rw.vr[i];
   const bool lead = qd == 0;
   if (lead) {
@@ -461,10 +463,16 @@ __device__ inline void sel_compute(const DecodeParams& p, FusedLds<G>& s, int w,
     case 2: quarter_qs<2, G>(rw.kr, &s.qs[0][0], qd, ds); break;
     case 3: quarter_qs<3, G>(rw.kr, &s.qs[0][0], qd, ds); break;
     case 4: quarter_qs<4, G>(rw.kr, &s.qs[0][0], qd, ds); break;
-    case 5: quarter_qs<5, G>(rw.kr, &s.qs[0][0], qd, ds); break;
-    case 6: quarter_qs<6, G>(rw.kr, &s.qs[0][0], qd, ds); break;
-    case 7: quarter_qs<7, G>(rw.kr, &s.qs[0][0], qd, ds); break;
-    default: quarter_qs<8, G>(rw.kr, &s.qs[0][0], qd, ds); break;
+    default:
+      if constexpr (NWD == 8) {
+        switch (r) {
+          case 5: quarter_qs<5, G>(rw.kr, &s.qs[0][0], qd, ds); break;
+          case 6: quarter_qs<6, G>(rw.kr, &s.qs[0][0], qd, ds); break;
+          case 7: quarter_qs<7, G>(rw.kr, &s.qs[0][0], qd, ds); break;
+          default: quarter_qs<8, G>(rw.kr, &s.qs[0][0], qd, ds); break;
+        }
+      }
+      break;
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
@@ -1008,16 +1016,36 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
     const uint32_t nsel = s.n1;
     if ((uint32_t)(kFTPW * sw) < nsel) {
       __builtin_amdgcn_s_setprio(3);
-      SelRows rw;
-      sel_fetch<G>(p, s, (uint32_t)(kFTPW * sw), (int)min((uint32_t)kFTPW, nsel - kFTPW * sw), kvh, t0, nw, rw);
+      constexpr uint32_t st = (uint32_t)(kFTPW * kFSW);
+      auto cnt = [&](uint32_t j0) { return (int)min((uint32_t)kFTPW, nsel - j0); };
       float qsum[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) qsum[h] = wave_sum_dpp(s.qs[h][lane] + s.qs[h][64 + lane]);
-      sel_compute<G>(p, s, sw, rw, (int)min((uint32_t)kFTPW, nsel - kFTPW * sw), qsum, msn, lsn, accs);
-      for (uint32_t j0 = (uint32_t)(kFTPW * (sw + kFSW)); j0 < nsel; j0 += (uint32_t)(kFTPW * kFSW)) {
-        const int cnt = (int)min((uint32_t)kFTPW, nsel - j0);
-        sel_fetch<G>(p, s, j0, cnt, kvh, t0, nw, rw);
-        sel_compute<G>(p, s, sw, rw, cnt, qsum, msn, lsn, accs);
+      uint32_t j = (uint32_t)(kFTPW * sw);
+      if (p.r <= 4) {
+        // the wave's batches j, j + st, ... in turn, the rows of the next
+        // batch fetched before the current one is computed (two sets of rows
+        // in registers, r <= 4 words each), so that a wave with two batches
+        // waits for one round of memory latency, not two
+        SelRows<4> ra, rb;
+        sel_fetch<G>(p, s, j, cnt(j), kvh, t0, nw, ra);
+        if (j + st < nsel) sel_fetch<G>(p, s, j + st, cnt(j + st), kvh, t0, nw, rb);
+        for (;;) {
+          sel_compute<G>(p, s, sw, ra, cnt(j), qsum, msn, lsn, accs);
+          if (j + 2 * st < nsel) sel_fetch<G>(p, s, j + 2 * st, cnt(j + 2 * st), kvh, t0, nw, ra);
+          j += st;
+          if (j >= nsel) break;
+          sel_compute<G>(p, s, sw, rb, cnt(j), qsum, msn, lsn, accs);
+          if (j + 2 * st < nsel) sel_fetch<G>(p, s, j + 2 * st, cnt(j + 2 * st), kvh, t0, nw, rb);
+          j += st;
+          if (j >= nsel) break;
+        }
+      } else {
+        SelRows<8> rw;
+        for (; j < nsel; j += st) {
+          sel_fetch<G>(p, s, j, cnt(j), kvh, t0, nw, rw);
+          sel_compute<G>(p, s, sw, rw, cnt(j), qsum, msn, lsn, accs);
+        }
       }
       __builtin_amdgcn_s_setprio(0);
     }
