@@ -1,5 +1,8 @@
 // Matrix-core (CDNA4 MFMA) forms of the score pass and of the base attention
-// pass, for 2- and 3-bit base codes and GQA groups of up to 4 query heads.
+// pass, for 2- and 3-bit base codes and GQA groups of 1, 2, 4 or 8 query
+// heads (a group of 8 takes two tiles of 4 heads in the logit product and
+// two heads per lane in the softmax; its 16 weight columns, hi and lo parts,
+// fill the P.V product's 16).
 //
 // Logits (page "StrataFlux -- Selective precision streaming -- What does it
 // mean?", paragraph "Which tiles count ...": scores from the resident low-bit
@@ -65,7 +68,9 @@ __global__ void __launch_bounds__(64 * NW) score_mfma(DecodeParams p) {
   constexpr int RB = 16 * BB;                    // bytes of a packed row
   constexpr int kSRingLoads = BB == 2 ? 2 : 3;   // direct loads per stage
   using SSt = SStage<BB>;
-  __shared__ QPrep qp;
+  constexpr int NT = G > 4 ? 2 : 1;              // tiles of 4 query heads
+  static_assert(G <= 4 || G == 8, "groups of 1, 2, 4 or 8 query heads");
+  __shared__ QPrepN<4 * NT> qp;
   __shared__ uint32_t lhist[kHistBins];
   __shared__ SSt ring[NW][kSRing];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -99,14 +104,22 @@ __global__ void __launch_bounds__(64 * NW) score_mfma(DecodeParams p) {
 #pragma unroll
   for (int k = 0; k < kSRing - 1; ++k)
     if (k < nmine) issue(k, ring[wid][k]);
-  v4i a0, a1;
-  prep_query<G, BB>(qx, qp, a0, a1);
+  v4i aq[2 * NT];                                 // A operands: tile tl's k-halves in aq[2 tl], aq[2 tl + 1]
+  if constexpr (NT == 2)
+    prep_query8<BB>(qx, qp, aq);
+  else
+    prep_query<G, BB>(qx, qp, aq[0], aq[1]);
   // logits in log2 units (1/sqrt(D) and log2(e) folded into the per-head
-  // constants): the attention pass's softmax takes them as they are
+  // constants): the attention pass's softmax takes them as they are; lane
+  // (t, hl) holds head hl of each tile (hl and 4 + hl)
   constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
   const int t = lane & 15, hl = lane >> 4;
-  const float scale = qp.scale[hl < G ? hl : 0] * (kRsqrtD * kLog2e);
-  const float sumq = qp.sumq[hl < G ? hl : 0] * (kRsqrtD * kLog2e);
+  float scale[NT], sumq[NT];
+#pragma unroll
+  for (int tl = 0; tl < NT; ++tl) {
+    scale[tl] = qp.scale[4 * tl + (hl < G ? hl : 0)] * (kRsqrtD * kLog2e);
+    sumq[tl] = qp.sumq[4 * tl + (hl < G ? hl : 0)] * (kRsqrtD * kLog2e);
+  }
   float* scores = p.scores + (int64_t)kvh * p.ntot + (a - p.off0) + lo;
   float* lgo = p.logits + ((int64_t)kvh * p.ntot + (a - p.off0) + lo) * G;
   const uint32_t ring0 = lds_addr(&ring[wid][0]);
@@ -167,12 +180,17 @@ __global__ void __launch_bounds__(64 * NW) score_mfma(DecodeParams p) {
         decode_b2(kw[j][0], kw[j][1], b0, b1);
       else
         decode_b3(kw[j][0], kw[j][1], kw[j][2], b0, b1);
-      v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(a0, b0, v4i{0, 0, 0, 0}, 0, 0, 0);
-      D = __builtin_amdgcn_mfma_i32_16x16x64_i8(a1, b1, D, 0, 0, 0);
-      const float x = logit_scaled(D, __builtin_bit_cast(float2, ks[j]), scale, sumq);
-      lg[j] = hl < G ? x : -INFINITY;
       const int rel = 32 * c + 16 * j + t;
-      if (hl < G && (full || rel < nsp)) store_through(&lgo[rel * G + hl], x);   // kept for the attention pass
+      float xm = -INFINITY;
+#pragma unroll
+      for (int tl = 0; tl < NT; ++tl) {
+        v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[2 * tl], b0, v4i{0, 0, 0, 0}, 0, 0, 0);
+        D = __builtin_amdgcn_mfma_i32_16x16x64_i8(aq[2 * tl + 1], b1, D, 0, 0, 0);
+        const float x = logit_scaled(D, __builtin_bit_cast(float2, ks[j]), scale[tl], sumq[tl]);
+        xm = fmaxf(xm, hl < G ? x : -INFINITY);
+        if (hl < G && (full || rel < nsp)) store_through(&lgo[rel * G + 4 * tl + hl], x);   // kept for the attention pass
+      }
+      lg[j] = xm;
     }
     // maximum over the heads, two tiles at once: lane (t, hl) keeps tile
     // hl/2 (token 16 (hl/2) + t)
@@ -441,6 +459,8 @@ __device__ inline void read_stage3(uint32_t aL, uint32_t aS, uint32_t aV, StageR
 template <int G, int NW, bool Batched, int BB = 2>
 __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh, uint8_t* smem) {
   static_assert(BB == 2 || BB == 3, "2- or 3-bit codes");
+  static_assert(G <= 4 || G == 8, "groups of 1, 2, 4 or 8 query heads");
+  constexpr int NS = G > 4 ? 2 : 1;                // query heads per logit lane: hl (and 4 + hl)
   constexpr int RB = 16 * BB;                      // bytes of a packed row
   constexpr int kRingLoads = BB == 2 ? 3 : 4;      // direct loads per stage
   using Lds = MfmaLds<G, NW, BB>;
@@ -511,7 +531,12 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   // product per tile takes both.
   const uint32_t ring0 = lds_addr(&s.u.ring[wid][0]);
   const uint32_t wtR = n < 2 * G ? lds_addr(&s.wt[wid][n][8 * rg]) : lds_addr(&s.wzero[0]);
-  const uint32_t wtHi = lds_addr(&s.wt[wid][hlc][2 * t]), wtLo = lds_addr(&s.wt[wid][G + hlc][2 * t]);
+  uint32_t wtHi[NS], wtLo[NS];
+#pragma unroll
+  for (int q = 0; q < NS; ++q) {
+    wtHi[q] = lds_addr(&s.wt[wid][4 * q + hlc][2 * t]);
+    wtLo[q] = lds_addr(&s.wt[wid][G + 4 * q + hlc][2 * t]);
+  }
   const uint32_t aL = ring0 + (uint32_t)(offsetof(St, lg) + 4 * (t * G + hlc));
   const uint32_t aS = ring0 + (uint32_t)(offsetof(St, vs) + 8 * t);
   uint32_t aV[4];                                 // 2-bit: token 4rg + v at stage row 4rg + (v ^ rg)
@@ -528,7 +553,12 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   // part, so exp2(logit - m) is 0 (not NaN) for the -inf of tokens left out
   constexpr float kFloor = -1e30f;
   constexpr int kSlack = 6;                       // weights up to 2^kSlack (log2 units of the reference)
-  float m = kFloor, lsum = 0.f, t1 = 0.f;
+  float m[NS], lsum[NS], t1[NS];
+#pragma unroll
+  for (int q = 0; q < NS; ++q) {
+    m[q] = kFloor;
+    lsum[q] = t1[q] = 0.f;
+  }
   int sexp = 127;                                 // weight scale 2^sexp; 127 = not set yet
   float wsc = 1.0f;                               // 2^sexp once set
   v4f acc[8];
@@ -560,21 +590,40 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
       R.vsc[0] = R3.vsc[0];
       R.vsc[1] = R3.vsc[1];
     }
+    // head 4 + hl's logits (groups of 8)
+    float lgB[2] = {0.f, 0.f};
+    if constexpr (NS == 2) {
+      constexpr int OFF = k * (int)sizeof(St);
+      asm volatile(
+          "ds_read_b32 %0, %2 offset:%3\n\t"
+          "ds_read_b32 %1, %2 offset:%4\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(lgB[0]), "=&v"(lgB[1])
+          : "v"(aL), "n"(OFF + 16), "n"(OFF + 16 * G * 4 + 16)
+          : "memory");
+    }
     // logits (log2 units, as the score pass kept them); -inf where the token
     // takes no part
-    float lg[2];
+    float lg[NS][2];
     float2 vsc[2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      lg[j] = lane_select(mk[j], R.lg[j], ninf);
-      vsc[j] = __builtin_bit_cast(float2, R.vsc[j]);
+    for (int jj = 0; jj < 2; ++jj) {
+      lg[0][jj] = lane_select(mk[jj], R.lg[jj], ninf);
+      if constexpr (NS == 2) lg[NS - 1][jj] = lane_select(mk[jj], lgB[jj], ninf);
+      vsc[jj] = __builtin_bit_cast(float2, R.vsc[jj]);
     }
     // online softmax with a lazy reference: m moves (and the sums are
     // rescaled) only when a logit exceeds it by more than kSlack, so the
     // weights stay below 2^kSlack and most chunks need no row maximum
-    const float xm = fmaxf(lg[0], lg[1]);
-    const bool grow = __ballot(xm > m + kSlack) != 0ull;
-    const float mnew = grow ? fmaxf(m, row16_max_dpp(xm)) : m;
+    float xm[NS], mnew[NS];
+    bool grow = false;
+#pragma unroll
+    for (int q = 0; q < NS; ++q) {
+      xm[q] = fmaxf(lg[q][0], lg[q][1]);
+      grow = grow || __ballot(xm[q] > m[q] + kSlack) != 0ull;
+    }
+#pragma unroll
+    for (int q = 0; q < NS; ++q) mnew[q] = grow ? fmaxf(m[q], row16_max_dpp(xm[q])) : m[q];
     // weight scale: keep delta * 2^sexp below 2^(14 - kSlack) over the
     // chunk; the chunk's largest delta is needed only when one reaches it
     float dmax = fmaxf(lane_select(mk[0], vsc[0].y, 0.f), lane_select(mk[1], vsc[1].y, 0.f));
@@ -586,16 +635,21 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
       need = 14 - kSlack - e2;   // wave-uniform, and so is sexp
     }
     if (grow || need < sexp) {
-      const float alpha = mnew > m ? __builtin_amdgcn_exp2f(m - mnew) : 1.f;   // 0 from the floor
-      lsum *= alpha;
-      t1 *= alpha;
+      float alpha[NS];
+#pragma unroll
+      for (int q = 0; q < NS; ++q) {
+        alpha[q] = mnew[q] > m[q] ? __builtin_amdgcn_exp2f(m[q] - mnew[q]) : 1.f;   // 0 from the floor
+        lsum[q] *= alpha[q];
+        t1[q] *= alpha[q];
+      }
+      // column n < 2G: head n % G (lane group (n % G) % 4, slot (n % G) / 4)
       const int hc = n < 2 * G ? n % G : 0;
-      float f = lane_value(alpha, 0);
+      float f = lane_value(alpha[0], 0);
 #pragma unroll
       for (int h = 1; h < G; ++h) {
         // read with every lane active (a lane read inside the selection
         // could run where lane 16 h is off)
-        const float ah = lane_value(alpha, 16 * h);
+        const float ah = lane_value(alpha[h / 4], 16 * (h % 4));
         f = hc == h ? ah : f;
       }
       if (need < sexp) {
@@ -604,24 +658,28 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
         wsc = __builtin_ldexpf(1.0f, sexp);
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[j] *= f;
-      m = mnew;
-    }
-    float wv[2];
+      for (int jj = 0; jj < 8; ++jj) acc[jj] *= f;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const float pk = __builtin_amdgcn_exp2f(lg[j] - m);   // exp2(-inf) = 0: tokens left out
-      lsum += pk;
-      t1 = fmaf(pk, fmaf(0.5f, vsc[j].y, vsc[j].x), t1);
-      wv[j] = pk * (vsc[j].y * wsc);
+      for (int q = 0; q < NS; ++q) m[q] = mnew[q];
     }
     // weights as fp16 hi + lo (truncated hi, exact remainder): 22 bits, the
     // two parts in separate columns of one product
-    const auto whi = __builtin_amdgcn_cvt_pkrtz(wv[0], wv[1]);
-    const auto wlo = __builtin_amdgcn_cvt_pkrtz(wv[0] - (float)whi[0], wv[1] - (float)whi[1]);
-    if (hl < G) {
-      lds_write_u32(wtHi, __builtin_bit_cast(uint32_t, whi));
-      lds_write_u32(wtLo, __builtin_bit_cast(uint32_t, wlo));
+#pragma unroll
+    for (int q = 0; q < NS; ++q) {
+      float wv[2];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const float pk = __builtin_amdgcn_exp2f(lg[q][jj] - m[q]);   // exp2(-inf) = 0: tokens left out
+        lsum[q] += pk;
+        t1[q] = fmaf(pk, fmaf(0.5f, vsc[jj].y, vsc[jj].x), t1[q]);
+        wv[jj] = pk * (vsc[jj].y * wsc);
+      }
+      const auto whi = __builtin_amdgcn_cvt_pkrtz(wv[0], wv[1]);
+      const auto wlo = __builtin_amdgcn_cvt_pkrtz(wv[0] - (float)whi[0], wv[1] - (float)whi[1]);
+      if (4 * q + hl < G) {
+        lds_write_u32(wtHi[q], __builtin_bit_cast(uint32_t, whi));
+        lds_write_u32(wtLo[q], __builtin_bit_cast(uint32_t, wlo));
+      }
     }
     const v8h bw = lds_read_v8h(wtR);
     if constexpr (BB == 2) {
@@ -685,16 +743,23 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   // wave totals: l and the scalar term per head (row sums), P.V per column
   // (column n < G: head n's hi part, G + h: its lo part); maxima stay in
   // log2 units until the partial is written
-  lsum = row16_sum(lsum);
-  t1 = row16_sum(t1);
-  if (hl < G && t == 0) {
-    s.mw[wid][hl] = m == kFloor ? -INFINITY : m;   // -inf: no token took part
-    s.lw[wid][hl] = lsum;
+#pragma unroll
+  for (int q = 0; q < NS; ++q) {
+    lsum[q] = row16_sum(lsum[q]);
+    t1[q] = row16_sum(t1[q]);
+  }
+  if (t == 0) {
+#pragma unroll
+    for (int q = 0; q < NS; ++q)
+      if (4 * q + hl < G) {
+        s.mw[wid][4 * q + hl] = m[q] == kFloor ? -INFINITY : m[q];   // -inf: no token took part
+        s.lw[wid][4 * q + hl] = lsum[q];
+      }
   }
   float t1n = 0.f;                                // the scalar term goes with the hi column
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    const float th = lane_value(t1, 16 * h);   // every lane active (see the rescale above)
+    const float th = lane_value(t1[h / 4], 16 * (h % 4));   // every lane active (see the rescale above)
     t1n = n == h ? th : t1n;
   }
   const int se = sexp == 127 ? 0 : sexp;
@@ -746,6 +811,7 @@ static bool launch_score_mfma_b(const DecodeParams& p, dim3 grid, hipStream_t st
     case 1: sf_launch(score_mfma<1, kScoreWaves, Batched, BB>, grid, dim3(64 * kScoreWaves), st, ev, p); return true;
     case 2: sf_launch(score_mfma<2, kScoreWaves, Batched, BB>, grid, dim3(64 * kScoreWaves), st, ev, p); return true;
     case 4: sf_launch(score_mfma<4, kScoreWaves, Batched, BB>, grid, dim3(64 * kScoreWaves), st, ev, p); return true;
+    case 8: sf_launch(score_mfma<8, kScoreWaves, Batched, BB>, grid, dim3(64 * kScoreWaves), st, ev, p); return true;
   }
   return false;
 }
@@ -756,6 +822,7 @@ static bool launch_attend_mfma_b(const DecodeParams& p, dim3 grid, hipStream_t s
     case 1: sf_launch(attend_mfma<1, kAttendWaves, Batched, BB>, grid, dim3(64 * kAttendWaves), st, ev, p); return true;
     case 2: sf_launch(attend_mfma<2, kAttendWaves, Batched, BB>, grid, dim3(64 * kAttendWaves), st, ev, p); return true;
     case 4: sf_launch(attend_mfma<4, kAttendWaves, Batched, BB>, grid, dim3(64 * kAttendWaves), st, ev, p); return true;
+    case 8: sf_launch(attend_mfma<8, kAttendWaves, Batched, BB>, grid, dim3(64 * kAttendWaves), st, ev, p); return true;
   }
   return false;
 }

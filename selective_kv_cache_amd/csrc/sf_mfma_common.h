@@ -57,11 +57,13 @@ __device__ inline void decode_b3(uint32_t w0, uint32_t w1, uint32_t w2, v4i& b0,
 // row (h, k) feeds its two MFMAs (operand i, dword v, byte b = element
 // 32g + 16i + v + 4b for 2-bit codes, matching decode_b2's element order,
 // and 32g + 16i + 4v + b for 3-bit codes, decode_b3's).
-struct QPrep {
-  alignas(16) int8_t op[4][4][4][32];   // [head][digit][lane group][byte]
-  float scale[4];                        // s_h
-  float sumq[4];                         // sum(q_h)
+template <int NH>
+struct QPrepN {
+  alignas(16) int8_t op[NH][4][4][32];  // [head][digit][lane group][byte]
+  float scale[NH];                       // s_h
+  float sumq[NH];                        // sum(q_h)
 };
+using QPrep = QPrepN<4>;
 
 // The query elements wave h < G turns into digits: elements 2*lane, 2*lane+1
 // of head h.  Loaded before anything else of the work-group so that their
@@ -74,14 +76,15 @@ __device__ inline float2 load_query(const float* q) {
 }
 
 // Work-group prologue: wave h < G turns query head h into 4 base-254 int8
-// digits, q = s * (d0 + d1/254 + d2/254^2 + d3/254^3), s = max|q|/127.  Then
-// each lane reads its two A operands (row = 4*head + digit, 16 bytes each of
-// lane group l/16) with two 16-byte LDS reads.
-template <int G, int BB = 2>
-__device__ inline void prep_query(float2 x, QPrep& qp, v4i& a0, v4i& a1) {
+// digits, q = s * (d0 + d1/254 + d2/254^2 + d3/254^3), s = max|q|/127 (waves
+// G .. NH - 1 write zero digits).  Then each lane reads its A operands (row
+// = 4*head + digit of a tile of 4 heads, 16 bytes each of lane group l/16)
+// with 16-byte LDS reads: two per tile.
+template <int G, int BB, int NH>
+__device__ inline void prep_digits(float2 x, QPrepN<NH>& qp) {
   static_assert(BB == 2 || BB == 3, "2- or 3-bit codes");
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  if (wid < 4) {
+  if (wid < NH) {
     const float amax = wave_max(fmaxf(fabsf(x.x), fabsf(x.y)));
     const float sum = wave_sum(x.x + x.y);
     const float sc = amax > 0.f ? amax / 127.0f : 1.0f;
@@ -104,10 +107,31 @@ __device__ inline void prep_query(float2 x, QPrep& qp, v4i& a0, v4i& a1) {
     }
   }
   __syncthreads();
-  const int m = lane & 15, g = lane >> 4;
+}
+
+// Groups of up to 4 query heads: one tile of 4 heads x 4 digits.
+template <int G, int BB = 2>
+__device__ inline void prep_query(float2 x, QPrep& qp, v4i& a0, v4i& a1) {
+  static_assert(G <= 4, "one tile of heads");
+  prep_digits<G, BB, 4>(x, qp);
+  const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
   const v4i* src = reinterpret_cast<const v4i*>(&qp.op[m >> 2][m & 3][g][0]);
   a0 = src[0];
   a1 = src[1];
+}
+
+// Groups of 8 query heads: tile 0 holds heads 0-3 (a[0], a[1]), tile 1 heads
+// 4-7 (a[2], a[3]).
+template <int BB = 2>
+__device__ inline void prep_query8(float2 x, QPrepN<8>& qp, v4i (&a)[4]) {
+  prep_digits<8, BB, 8>(x, qp);
+  const int lane = threadIdx.x & 63, m = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int tl = 0; tl < 2; ++tl) {
+    const v4i* src = reinterpret_cast<const v4i*>(&qp.op[4 * tl + (m >> 2)][m & 3][g][0]);
+    a[2 * tl] = src[0];
+    a[2 * tl + 1] = src[1];
+  }
 }
 
 // Logit of (head l/16, token l%16) from the digit sums; -inf for heads >= G.

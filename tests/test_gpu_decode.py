@@ -56,6 +56,7 @@ SMALL = [
     dict(ctx=1500, n_q_heads=4, n_kv_heads=2, base_bits=3, refine_bits=4, top_t=64),  # 3-bit, G = 2
     dict(ctx=1300, n_q_heads=8, n_kv_heads=1, base_bits=3, refine_bits=2, top_t=64),  # 3-bit, G = 8
     dict(ctx=33, n_q_heads=8, n_kv_heads=2, base_bits=3, refine_bits=8, top_t=7),     # 3-bit, one chunk + 1
+    dict(ctx=9000, n_q_heads=16, n_kv_heads=2, refine_bits=4, top_t=300),             # G = 8, several splits
 ]
 
 
@@ -73,6 +74,14 @@ def test_base_pass_precision_3bit():
     P.V with the codes cut from two dwords by a funnel shift and placed at
     fp16 mantissa bits 4-9."""
     _, st = _case(W.small(cfg_id=229, ctx=1000, base_bits=3, refine_bits=2, top_t=0))
+    assert st["max_out_err"] <= 1e-4, st
+
+
+def test_base_pass_precision_group8():
+    """The same for groups of 8 query heads: two heads per softmax lane and
+    the 16 weight columns (hi and lo parts of 8 heads) filling the P.V
+    product."""
+    _, st = _case(W.small(cfg_id=230, ctx=1000, n_q_heads=16, n_kv_heads=2, top_t=0))
     assert st["max_out_err"] <= 1e-4, st
 
 
