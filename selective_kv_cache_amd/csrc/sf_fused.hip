@@ -99,7 +99,7 @@ struct FusedLds {
   uint16_t pre1[kFusedRmax / 32 + 1];        // selected tokens before each word
   uint32_t lcnt[kFListRanges];               // candidates of each range of the head
   float mw[kFW][G], lw[kFW][G];              // per-wave partials: maxima (log2 units), sums
-  float mstar[G];
+  float mstar[G];                            // E: each head's denominator
   uint32_t scan[kFW];
   int sh_bin;
   uint32_t sh_need, sh_flag;
@@ -1130,15 +1130,24 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
   for (int j = 0; j < 32; ++j)
     xa[j] = summer && w0 + j < w1 ? ld_devf(rP, (uint32_t)(((w0 + j) * G + ho) * kPartStride + dout) * 4u) : 0.f;
   __syncthreads();
-  if (tid < G) {
+  // wavefront h < G: head h's maximum over the ranges, each range's weight
+  // 2^(m_w - m*) (in place of its maximum) and the denominator
+  // sum_w weight_w l_w, as wavefront reductions
+  if (wid < G) {
+    float* mh = mwg + wid * nwg;
+    const float* lh = lwg + wid * nwg;
     float M = -INFINITY;
-    for (uint32_t w = 0; w < nwg; ++w) M = fmaxf(M, mwg[tid * nwg + w]);
-    s.mstar[tid] = M;
-  }
-  __syncthreads();
-  for (int i = tid; i < G * (int)nwg; i += 64 * kFW) {
-    const float mv = mwg[i];
-    mwg[i] = mv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv - s.mstar[i / nwg]);
+    for (uint32_t w = (uint32_t)lane; w < nwg; w += 64) M = fmaxf(M, mh[w]);
+    M = wave_max_dpp(M);
+    float den = 0.f;
+    for (uint32_t w = (uint32_t)lane; w < nwg; w += 64) {
+      const float mv = mh[w];
+      const float e = mv == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv - M);
+      mh[w] = e;
+      den = fmaf(e, lh[w], den);
+    }
+    den = wave_sum_dpp(den);
+    if (lane == 0) s.mstar[wid] = den;
   }
   __syncthreads();
   float num = 0.f;
@@ -1151,11 +1160,7 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
     if (hlf) half[io] = num;
   }
   __syncthreads();
-  if (tid < G * kHeadDim) {
-    float den = 0.f;
-    for (uint32_t w = 0; w < nwg; ++w) den = fmaf(mwg[ho * nwg + w], lwg[ho * nwg + w], den);
-    p.out[((int64_t)seq * p.hq + kvh * G + ho) * kHeadDim + dout] = (num + half[io]) / den;
-  }
+  if (tid < G * kHeadDim) p.out[((int64_t)seq * p.hq + kvh * G + ho) * kHeadDim + dout] = (num + half[io]) / s.mstar[ho];
   if (select && p.fsel) {
     // the selection, ascending, from the ranges' words
     const uint32_t* bm = p.bitmap + sk * p.bm_words;
