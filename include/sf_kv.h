@@ -414,7 +414,7 @@ sf_status sf_decode_check(void* workspace, void* stream);
  */
 sf_status sf_decode_step_noalloc(const sf_geom* geom, const sf_decode_args* args, void* stream);
 
-/* Size of the device buffer of sf_decode_step_noalloc (64 MiB). */
+/* Size of the device buffer of sf_decode_step_noalloc (96 MiB). */
 size_t sf_decode_noalloc_max_bytes(void);
 
 

@@ -17,7 +17,7 @@
 
 namespace sfk {
 
-constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr size_t kScratchBytes = (size_t)96 << 20;
 constexpr int kMaxDevices = 64;
 
 static __device__ __align__(256) uint8_t scratch[kScratchBytes];

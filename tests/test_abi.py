@@ -209,3 +209,17 @@ def test_weight_gemv_rejects_null_buffers():
     g2 = B.wgeom(64, 2688, 3, 4, 32, 1000)
     assert lib.sf_w_gemv_workspace_words(ctypes.byref(g2), ctypes.byref(n)) == B.SF_OK and n.value == 512 + 2 * 3 * 32 + 2
     assert lib.sf_w_quantize(ctypes.byref(g), fake, fake, fake, None, fake, None) == B.SF_ERR_INVALID_ARG
+
+
+def test_noalloc_scratch_holds_every_workload_step():
+    """sf_decode_step_noalloc's fixed device buffer holds the workspace of a
+    step of every workload the benchmark and the tests run at full size (the
+    16-sequence batch is the largest)."""
+    from selective_kv_cache_amd import workloads as W
+    cap = B.sf_decode_noalloc_max_bytes()
+    for name, w in W.WORKLOADS.items():
+        lens = w.seq_lengths()
+        off = W.seq_offsets(lens)
+        g = B.geom(w.head_dim, w.n_q_heads, w.n_kv_heads, w.base_bits, w.refine_bits)
+        need = B.sf_decode_workspace_size(g, w.batch, int(off[-1]), int(max(lens)), w.top_t)
+        assert need <= cap, (name, need, cap)
