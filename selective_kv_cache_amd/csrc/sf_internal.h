@@ -60,7 +60,8 @@ struct sf_store_s {
                            // 2 = the check found the slot <-> token tables inconsistent
   int32_t* slot_tok;       // [max_seqs][Hkv][slots] token in the slot, -1 if free
   int32_t* stamp;          // [max_seqs][Hkv][slots] last step the token was selected
-  int32_t step;
+  int32_t* dstep;          // device word: lookups so far (this step's LRU stamp); the fetch kernel
+                           // advances it, so a step's launches can be captured in a graph and replayed
   // staging for fetched rows and the miss lists
   uint8_t* host_rows_dev;   // host_rows as the device addresses it
   int32_t* h_miss;         // pinned: the miss lists, copied back only for statistics

@@ -93,8 +93,9 @@ constexpr int kMaxSlots = 4096;   // keeps the lookup's keys and lists in LDS (<
 // keys (uint64) and selected-resident flags, the misses' ranks and the victim
 // list (top_t each).
 __global__ void __launch_bounds__(kLookupThreads)
-cache_lookup(DecodeParams p, int32_t* slot_tok, int32_t* stamp, int32_t* tok_slot, int32_t step, int32_t* miss,
-             int32_t mark_misses) {
+cache_lookup(DecodeParams p, int32_t* slot_tok, int32_t* stamp, int32_t* tok_slot, const int32_t* dstep,
+             int32_t* miss, int32_t mark_misses) {
+  const int32_t step = *dstep;                                    // this step's stamp
   extern __shared__ uint64_t keys[];                              // [slots]: victim keys
   uint32_t* flag = reinterpret_cast<uint32_t*>(keys + p.slots);   // [slots]: 1 = selected resident
   int32_t* mrank = reinterpret_cast<int32_t*>(flag + p.slots);    // [top_t]: rank among misses, -1 = hit
@@ -267,7 +268,9 @@ constexpr int kFetchWGs = 16;
 constexpr int kFetchUnroll = 4;
 __global__ void __launch_bounds__(256)
 cache_fetch(const int32_t* miss, int32_t top_t, int32_t hkv, int64_t cap, int32_t slots, int32_t rb,
-            const uint8_t* host_rows, uint8_t* cache_data) {
+            const uint8_t* host_rows, uint8_t* cache_data, int32_t* dstep) {
+  // the step's lookup is done (stream order): the next step stamps with the next value
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *dstep += 1;
   const int64_t sk = blockIdx.x;
   const int kvh = (int)(sk % hkv);
   const int32_t* m = miss + sk * 2 * (int64_t)(top_t + 1);
@@ -310,6 +313,7 @@ static void free_store(sf_store_s* s) {
   if (s->h_miss) (void)hipHostFree(s->h_miss);
   if (s->err) (void)hipFree(s->err);
   if (s->miss) (void)hipFree(s->miss);
+  if (s->dstep) (void)hipFree(s->dstep);
   if (s->looked_up) (void)hipEventDestroy(s->looked_up);
   if (s->fetched) (void)hipEventDestroy(s->fetched);
   if (s->side) (void)hipStreamDestroy(s->side);
@@ -367,6 +371,8 @@ extern "C" sf_status sf_store_create(const sf_geom* geom, int64_t cap_tokens, in
     SF_ALLOC(hipHostMalloc((void**)&s->h_miss, (size_t)max_seqs * hkv * (2 * (s->slots + 1) + 1) * 4,
                            hipHostMallocDefault));
     SF_ALLOC(hipMalloc((void**)&s->miss, (size_t)max_seqs * hkv * (2 * (s->slots + 1) + 1) * 4));
+    SF_ALLOC(hipMalloc((void**)&s->dstep, 4));
+    SF_ALLOC(hipMemset(s->dstep, 0, 4));
     SF_ALLOC(hipStreamCreateWithFlags(&s->side, hipStreamNonBlocking));
     SF_ALLOC(hipEventCreateWithFlags(&s->looked_up, hipEventDisableTiming));
     SF_ALLOC(hipEventCreateWithFlags(&s->fetched, hipEventDisableTiming));
@@ -470,13 +476,12 @@ sf_status sf_store_fetch(sf_store s, const DecodeParams& p, hipStream_t st, bool
   const int32_t B = p.batch, hkv = p.hkv;
   const int64_t groups = (int64_t)B * hkv;
   const size_t lds = (size_t)s->slots * 12 + (size_t)p.top_t * 8;
-  const int32_t step = s->step++;
   int32_t* miss_dev = s->miss;
   // the previous skip step's fetch reads the miss lists and fills slots
   const sf_status ws = wait_side_fetch(s, st);
   if (ws != SF_OK) return ws;
   hipLaunchKernelGGL(cache_lookup, dim3((unsigned)groups), dim3(kLookupThreads), lds, st, p, s->slot_tok,
-                     s->stamp, s->tok_slot, step, miss_dev, skip ? 1 : 0);
+                     s->stamp, s->tok_slot, s->dstep, miss_dev, skip ? 1 : 0);
   SF_LAUNCH_CHECK("cache_lookup");
   hipStream_t fs = st;
   if (skip) {
@@ -485,7 +490,7 @@ sf_status sf_store_fetch(sf_store s, const DecodeParams& p, hipStream_t st, bool
     fs = s->side;
   }
   hipLaunchKernelGGL(cache_fetch, dim3((unsigned)groups, kFetchWGs), dim3(256), 0, fs, miss_dev, p.top_t, hkv,
-                     s->cap, s->slots, (int32_t)s->row_bytes, s->host_rows_dev, s->cache_data);
+                     s->cap, s->slots, (int32_t)s->row_bytes, s->host_rows_dev, s->cache_data, s->dstep);
   SF_LAUNCH_CHECK("cache_fetch");
   if (skip) {
     SF_HIP_CHECK(hipEventRecord(s->fetched, s->side));

@@ -303,6 +303,59 @@ def test_host_tier_matches_device_tier_and_cache_simulation():
         host.close()
 
 
+def test_host_tier_graph_replays_match_eager():
+    """The host-tier step (cache lookup, fetch of the misses over the link,
+    the five kernels) captured as a HIP graph and replayed under an AR(1)
+    query process: every replay's output bit-identical to the same step
+    launched eagerly on an identical store, and the caches left in the same
+    state (the LRU stamp advances on the device, so replays age the cache as
+    eager steps do)."""
+    import torch
+    from selective_kv_cache_amd import binding as B
+    from selective_kv_cache_amd.kvcache import Decoder, LayerCache
+    w = W.small("hostgraph", cfg_id=310, ctx=3000, n_q_heads=8, n_kv_heads=2, refine_bits=4, top_t=128, rho=0.9)
+    g = P.geom_of(w)
+    off = W.seq_offsets([3000])
+    k, v = W.layer_kv(w, 0)
+    qs = W.queries(w, 0, 10)
+    stores = [LayerCache(g, 3000, tier=B.SF_TIER_HOST_PINNED, max_seqs=1, cache_slots=w.top_t + 64)
+              for _ in range(2)]
+    try:
+        kd, vd = torch.as_tensor(k, device="cuda"), torch.as_tensor(v, device="cuda")
+        decs = []
+        for c in stores:
+            c.append(kd, vd, 0)
+            decs.append(Decoder(g, off, w.top_t))
+        qbuf = torch.as_tensor(qs[0], device="cuda").clone()
+        obuf = torch.empty((1, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+        for c, d in zip(stores, decs):            # the same warm-up step on both
+            d.step(c, qbuf)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            decs[1].step(stores[1], qbuf, out=obuf)
+        torch.cuda.synchronize()
+        for c in stores:
+            c.clear_cache()
+        torch.cuda.synchronize()
+        for t in range(qs.shape[0] - 1):
+            qd = torch.as_tensor(qs[t], device="cuda")
+            o_eager = decs[0].step(stores[0], qd).cpu().numpy()
+            qbuf.copy_(qd)
+            graph.replay()
+            torch.cuda.synchronize()
+            o_graph = obuf.cpu().numpy()
+            assert np.array_equal(o_eager.view(np.uint32), o_graph.view(np.uint32)), t
+        qd = torch.as_tensor(qs[-1], device="cuda")
+        st = [d.step(c, qd, want_stats=True)[1] for c, d in zip(stores, decs)]
+        assert st[0]["hits"] == st[1]["hits"] and st[0]["misses"] == st[1]["misses"], st
+        assert 0 < st[0]["hits"] < st[0]["selected"], st
+        del graph
+    finally:
+        for c in stores:
+            c.close()
+
+
 def test_append_steps_host_tier():
     """Multi-step reuse run, reduced: each step appends one token (quantized on
     the GPU, its refinement rows put in the pinned store) and decodes over the
