@@ -58,15 +58,15 @@ int32_t choose_split(int64_t total_tokens, int32_t n_kv_heads, int32_t groups) {
   return s;
 }
 
-// The attention pass's shape: the matrix-core form (2- or 3-bit base codes,
-// GQA groups of 1, 2, 4 or 8) runs kAttendWaves wavefronts per work-group, the
+// The attention pass's shape: the matrix-core form (2-, 3- or 4-bit base
+// codes, GQA groups of 1, 2, 4 or 8) runs kAttendWaves wavefronts per work-group, the
 // VALU form 4; about 2048 wavefronts of base tokens either way.
 struct AttendShape {
   int32_t split;
 };
 static AttendShape attend_shape(const sf_geom& g, int64_t total_tokens) {
   const int32_t grp = g.n_q_heads / g.n_kv_heads;
-  const bool mfma = (g.base_bits == 2 || g.base_bits == 3) && (grp == 1 || grp == 2 || grp == 4 || grp == 8);
+  const bool mfma = g.base_bits >= 2 && g.base_bits <= 4 && (grp == 1 || grp == 2 || grp == 4 || grp == 8);
   const int waves = mfma ? kAttendWaves : 4;
   return AttendShape{choose_split(total_tokens, g.n_kv_heads, 2048 / waves)};
 }
@@ -244,8 +244,7 @@ sf_status sf_decode_step_ws(const sf_geom* geom, const sf_decode_args* a, void* 
   // the matrix-core score pass runs kScoreWaves wavefronts per work-group,
   // the other 4: about 4096 wavefronts either way
   const int32_t grp = geom->n_q_heads / geom->n_kv_heads;
-  const bool score_mfma =
-      (geom->base_bits == 2 || geom->base_bits == 3) && (grp == 1 || grp == 2 || grp == 4 || grp == 8);
+  const bool score_mfma = geom->base_bits >= 2 && geom->base_bits <= 4 && (grp == 1 || grp == 2 || grp == 4 || grp == 8);
   // the summed-probability score needs the score pass's per-head logits (its
   // kernels take groups of up to 4)
   if (smax && (!score_mfma || grp > 4)) return SF_ERR_UNSUPPORTED;

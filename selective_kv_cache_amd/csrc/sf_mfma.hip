@@ -1,5 +1,5 @@
 // Matrix-core (CDNA4 MFMA) forms of the score pass and of the base attention
-// pass, for 2- and 3-bit base codes and GQA groups of 1, 2, 4 or 8 query
+// pass, for 2-, 3- and 4-bit base codes and GQA groups of 1, 2, 4 or 8 query
 // heads (a group of 8 takes two tiles of 4 heads in the logit product and
 // two heads per lane in the softmax; its 16 weight columns, hi and lo parts,
 // fill the P.V product's 16).
@@ -64,15 +64,16 @@ struct SStage {
 template <int G, int NW, bool Batched, int BB = 2>
 __global__ void __launch_bounds__(64 * NW) score_mfma(DecodeParams p) {
   static_assert(NW >= 4, "waves 0-3 prepare the query digits");
-  static_assert(BB == 2 || BB == 3, "2- or 3-bit codes");
+  static_assert(BB >= 2 && BB <= 4, "2-, 3- or 4-bit codes");
   constexpr int RB = 16 * BB;                    // bytes of a packed row
   constexpr int kSRingLoads = BB == 2 ? 2 : 3;   // direct loads per stage
+  constexpr int SR = BB == 4 ? 3 : kSRing;       // stages per wavefront (4-bit: 3, so the ring fits the LDS)
   using SSt = SStage<BB>;
   constexpr int NT = G > 4 ? 2 : 1;              // tiles of 4 query heads
   static_assert(G <= 4 || G == 8, "groups of 1, 2, 4 or 8 query heads");
   __shared__ QPrepN<4 * NT> qp;
   __shared__ uint32_t lhist[kHistBins];
-  __shared__ SSt ring[NW][kSRing];
+  __shared__ SSt ring[NW][SR];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kvh = blockIdx.y;
@@ -95,14 +96,14 @@ __global__ void __launch_bounds__(64 * NW) score_mfma(DecodeParams p) {
   auto issue = [&](int i, SSt& st) {
     const uint32_t c = (uint32_t)(wid + NW * i);
     bdma16(rK, oK, c * (32u * RB), st.k);
-    if (BB == 3 && lane < 32) bdma16(rK, oK + 1024u, c * (32u * RB), st.k + 1024);
+    if (BB == 4 || (BB == 3 && lane < 32)) bdma16(rK, oK + 1024u, c * (32u * RB), st.k + 1024);
     bdma4(rS, oS, c * 256u, st.ks);
   };
   // no selection, no histogram; the summed-probability score builds its own
   const bool hist = p.top_t > 0 && p.score_mode == 0;
   for (int i = tid; i < kHistBins; i += 64 * NW) lhist[i] = 0u;
 #pragma unroll
-  for (int k = 0; k < kSRing - 1; ++k)
+  for (int k = 0; k < SR - 1; ++k)
     if (k < nmine) issue(k, ring[wid][k]);
   v4i aq[2 * NT];                                 // A operands: tile tl's k-halves in aq[2 tl], aq[2 tl + 1]
   if constexpr (NT == 2)
@@ -131,12 +132,12 @@ __global__ void __launch_bounds__(64 * NW) score_mfma(DecodeParams p) {
   auto body = [&](auto kc, int i) {
     constexpr int k = decltype(kc)::value;        // stage of chunk i
     constexpr int OFF = k * (int)sizeof(SSt);
-    if (i + kSRing - 1 < nmine) issue(i + kSRing - 1, ring[wid][(k + kSRing - 1) % kSRing]);
+    if (i + SR - 1 < nmine) issue(i + SR - 1, ring[wid][(k + SR - 1) % SR]);
     // this wave's loads complete in order: stage i is in once no more than
     // the stages issued after it are outstanding (stores only add to the count)
-    wait_stages<kSRingLoads, kSRing - 1>(min(kSRing - 1, nmine - 1 - i));
+    wait_stages<kSRingLoads, SR - 1>(min(SR - 1, nmine - 1 - i));
     const int c = wid + NW * i;
-    uint32_t kw[2][3];
+    uint32_t kw[2][4];
     uint64_t ks[2];
     if constexpr (BB == 2) {
       uint64_t k0, k1;
@@ -153,7 +154,23 @@ __global__ void __launch_bounds__(64 * NW) score_mfma(DecodeParams p) {
       kw[0][1] = (uint32_t)(k0 >> 32);
       kw[1][0] = (uint32_t)k1;
       kw[1][1] = (uint32_t)(k1 >> 32);
-      kw[0][2] = kw[1][2] = 0u;
+      kw[0][2] = kw[1][2] = kw[0][3] = kw[1][3] = 0u;
+    } else if constexpr (BB == 4) {
+      v4u k0, k1;
+      asm volatile(
+          "ds_read_b128 %0, %4 offset:%6\n\t"
+          "ds_read_b128 %1, %4 offset:%7\n\t"
+          "ds_read_b64 %2, %5 offset:%6\n\t"
+          "ds_read_b64 %3, %5 offset:%8\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(k0), "=&v"(k1), "=&v"(ks[0]), "=&v"(ks[1])
+          : "v"(aK), "v"(aS), "n"(OFF), "n"(OFF + 16 * RB), "n"(OFF + 128)
+          : "memory");
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        kw[0][x] = k0[x];
+        kw[1][x] = k1[x];
+      }
     } else {
       asm volatile(
           "ds_read_b32 %0, %8 offset:%10\n\t"
@@ -170,6 +187,7 @@ __global__ void __launch_bounds__(64 * NW) score_mfma(DecodeParams p) {
           : "v"(aK), "v"(aS), "n"(OFF), "n"(OFF + 4), "n"(OFF + 8), "n"(OFF + 16 * RB), "n"(OFF + 16 * RB + 4),
             "n"(OFF + 16 * RB + 8), "n"(OFF + 128)
           : "memory");
+      kw[0][3] = kw[1][3] = 0u;
     }
     const bool full = 32 * c + 32 <= nsp;         // every token of the chunk inside the split
     float lg[2];
@@ -178,8 +196,10 @@ __global__ void __launch_bounds__(64 * NW) score_mfma(DecodeParams p) {
       v4i b0, b1;
       if constexpr (BB == 2)
         decode_b2(kw[j][0], kw[j][1], b0, b1);
-      else
+      else if constexpr (BB == 3)
         decode_b3(kw[j][0], kw[j][1], kw[j][2], b0, b1);
+      else
+        decode_b4(kw[j][0], kw[j][1], kw[j][2], kw[j][3], b0, b1);
       const int rel = 32 * c + 16 * j + t;
       float xm = -INFINITY;
 #pragma unroll
@@ -202,9 +222,9 @@ __global__ void __launch_bounds__(64 * NW) score_mfma(DecodeParams p) {
       if (hist) lds_add_u32(hist0 + 4u * (score_key(sc) >> (32 - kHistBits)), 1u);
     }
   };
-  for (int i = 0; i < nmine; i += kSRing) {
+  for (int i = 0; i < nmine; i += SR) {
     progress_priority(nmine - i, nmine);
-    ring_round<kSRing>(body, i, nmine);
+    ring_round<SR>(body, i, nmine);
   }
   __builtin_amdgcn_s_setprio(0);
   // the histogram adds (asm, not waited for) complete before the barrier
@@ -412,7 +432,10 @@ __device__ inline void read_stage(uint32_t aL, uint32_t aS, const uint32_t (&aV)
 
 // The 3-bit form: the two dwords holding row n's 24-bit group of each of
 // the lane's 8 tokens (4rg + v: vw[4v], vw[4v + 1]; 16 + 4rg + v: vw[4v + 2],
-// vw[4v + 3]).  aV points at the first dword of token 4rg's group.
+// vw[4v + 3]).  aV points at the first dword of token 4rg's group.  Row 15's
+// group lies in the row's last dword alone; its second read (the next row's
+// first dword, or for token 31 the stage's first scale word) stays inside
+// the stage and its value is shifted out.
 struct StageRegs3 {
   float lg[2];
   uint64_t vsc[2];
@@ -456,13 +479,36 @@ __device__ inline void read_stage3(uint32_t aL, uint32_t aS, uint32_t aV, StageR
       : "memory");
 }
 
+// The 4-bit form: dword n of each of the lane's 8 tokens' rows (row n's 8
+// codes; 4rg + v: vw[2v], 16 + 4rg + v: vw[2v + 1]).  aV points at dword n of
+// token 4rg's row.
+template <int OFF>
+__device__ inline void read_vrows4(uint32_t aV, uint32_t (&vw)[8]) {
+  constexpr int RB = 64, T16 = 16 * RB;
+  asm volatile(
+      "ds_read_b32 %0, %8 offset:%9\n\t"
+      "ds_read_b32 %1, %8 offset:%10\n\t"
+      "ds_read_b32 %2, %8 offset:%11\n\t"
+      "ds_read_b32 %3, %8 offset:%12\n\t"
+      "ds_read_b32 %4, %8 offset:%13\n\t"
+      "ds_read_b32 %5, %8 offset:%14\n\t"
+      "ds_read_b32 %6, %8 offset:%15\n\t"
+      "ds_read_b32 %7, %8 offset:%16\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(vw[0]), "=&v"(vw[1]), "=&v"(vw[2]), "=&v"(vw[3]), "=&v"(vw[4]), "=&v"(vw[5]), "=&v"(vw[6]),
+        "=&v"(vw[7])
+      : "v"(aV), "n"(OFF), "n"(OFF + T16), "n"(OFF + RB), "n"(OFF + T16 + RB), "n"(OFF + 2 * RB),
+        "n"(OFF + T16 + 2 * RB), "n"(OFF + 3 * RB), "n"(OFF + T16 + 3 * RB)
+      : "memory");
+}
+
 template <int G, int NW, bool Batched, int BB = 2>
 __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh, uint8_t* smem) {
-  static_assert(BB == 2 || BB == 3, "2- or 3-bit codes");
+  static_assert(BB >= 2 && BB <= 4, "2-, 3- or 4-bit codes");
   static_assert(G <= 4 || G == 8, "groups of 1, 2, 4 or 8 query heads");
   constexpr int NS = G > 4 ? 2 : 1;                // query heads per logit lane: hl (and 4 + hl)
   constexpr int RB = 16 * BB;                      // bytes of a packed row
-  constexpr int kRingLoads = BB == 2 ? 3 : 4;      // direct loads per stage
+  constexpr int kRingLoads = BB == 2 ? 3 : 4;      // direct loads per stage (3- and 4-bit rows: two V loads)
   using Lds = MfmaLds<G, NW, BB>;
   using St = Stage<G, BB>;
   Lds& s = *reinterpret_cast<Lds*>(smem);
@@ -498,7 +544,7 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
     const uint32_t c = (uint32_t)(wid + NW * i);
     if (lane < 8 * G) bdma16(rL, oL, c * (32u * G * 4u), st.lg);
     bdma16(rV, oV, c * (32u * RB), st.v);
-    if (BB == 3 && lane < 32) bdma16(rV, oV + 1024u, c * (32u * RB), st.v + 1024);
+    if (BB == 4 || (BB == 3 && lane < 32)) bdma16(rV, oV + 1024u, c * (32u * RB), st.v + 1024);
     bdma4(rS, oS, c * 256u, st.vs);
   };
 #pragma unroll
@@ -544,6 +590,8 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   for (int v = 0; v < 4; ++v) aV[v] = ring0 + (uint32_t)(offsetof(St, v) + (4 * rg + (v ^ rg)) * 32 + 4 * vdw);
   // 3-bit: row n's group (bits 24n ..) starts in dword 3n/4 at bit 24n % 32
   const uint32_t aV3 = ring0 + (uint32_t)(offsetof(St, v) + 4 * rg * RB + 4 * ((3 * n) >> 2));
+  // 4-bit: row n's group is dword n of the row
+  const uint32_t aV4 = ring0 + (uint32_t)(offsetof(St, v) + 4 * rg * RB + 4 * n);
   const uint32_t gsh = (uint32_t)((24 * n) & 31);
   // rows hl < G hold heads; the others take no part
   const uint64_t rows = G >= 4 ? ~0ull : (1ull << (16 * (G & 3))) - 1ull;
@@ -583,6 +631,11 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
     [[maybe_unused]] StageRegs3 R3;
     if constexpr (BB == 2) {
       read_stage<G, k * (int)sizeof(St)>(aL, aS, aV, R);
+    } else if constexpr (BB == 4) {
+      // the logits and scales as in the 2-bit read (its V reads go to the
+      // first row, unused), then the rows' dwords n
+      read_stage<G, k * (int)sizeof(St)>(aL, aS, aV, R);
+      read_vrows4<k * (int)sizeof(St)>(aV4, R.vw);
     } else {
       read_stage3<G, k * (int)sizeof(St)>(aL, aS, aV3, R3);
       R.lg[0] = R3.lg[0];
@@ -699,6 +752,28 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
         for (int v = 0; v < 4; ++v) av[v] = (tt < 2 ? P[v] << 4 : tt < 5 ? P[v] : P[v] >> 6) & msk;
         acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, av), bw, acc[tt], 0, 0, 0);
       }
+    } else if constexpr (BB == 4) {
+      // row n's 8 codes are dword n of each row: P03 pairs the two tokens'
+      // low halves (codes 0-3 at bits 0, 4, 8, 12 of each half), P47 their
+      // high halves (codes 4-7); code tt goes in at mantissa bit 4
+      uint32_t P03[4], P47[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        P03[v] = __builtin_amdgcn_perm(R.vw[2 * v + 1], R.vw[2 * v], 0x05040100u);
+        P47[v] = __builtin_amdgcn_perm(R.vw[2 * v + 1], R.vw[2 * v], 0x07060302u);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 8; ++tt) {
+        v4u av;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const uint32_t y = tt < 4 ? P03[v] : P47[v];
+          const int q = tt & 3;
+          const uint32_t x = q == 0 ? y << 4 : q == 1 ? y : q == 2 ? y >> 4 : y >> 8;
+          av[v] = x & 0x00F000F0u;
+        }
+        acc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, av), bw, acc[tt], 0, 0, 0);
+      }
     } else {
       // the 24-bit groups of the token pair (4rg + v, 16 + 4rg + v); P03
       // holds bits 0-15 of each in its two halves (codes 0-4), P47 bits
@@ -766,7 +841,7 @@ __device__ inline void base_split_mfma(const DecodeParams& p, int split, int kvh
   if (n < 2 * G) {
 #pragma unroll
     for (int tt = 0; tt < 8; ++tt) {
-      const float f = __builtin_ldexpf(1.0f, 24 - (BB == 2 ? code_bit(tt) : code_bit3(tt)) - se);
+      const float f = __builtin_ldexpf(1.0f, 24 - code_bit_of<BB>(tt) - se);
 #pragma unroll
       for (int j = 0; j < 4; ++j) s.u.accw[wid][n][32 * rg + 8 * j + tt] = fmaf(acc[tt][j], f, t1n);
     }
@@ -834,6 +909,8 @@ bool launch_score_mfma(const DecodeParams& p, dim3 grid, hipStream_t st, KernelE
     return p.batch > 1 ? launch_score_mfma_b<true, 2>(p, grid, st, ev) : launch_score_mfma_b<false, 2>(p, grid, st, ev);
   if (p.b == 3)
     return p.batch > 1 ? launch_score_mfma_b<true, 3>(p, grid, st, ev) : launch_score_mfma_b<false, 3>(p, grid, st, ev);
+  if (p.b == 4)
+    return p.batch > 1 ? launch_score_mfma_b<true, 4>(p, grid, st, ev) : launch_score_mfma_b<false, 4>(p, grid, st, ev);
   return false;
 }
 
@@ -842,6 +919,8 @@ bool launch_attend_mfma(const DecodeParams& p, dim3 grid, hipStream_t st, Kernel
     return p.batch > 1 ? launch_attend_mfma_b<true, 2>(p, grid, st, ev) : launch_attend_mfma_b<false, 2>(p, grid, st, ev);
   if (p.b == 3)
     return p.batch > 1 ? launch_attend_mfma_b<true, 3>(p, grid, st, ev) : launch_attend_mfma_b<false, 3>(p, grid, st, ev);
+  if (p.b == 4)
+    return p.batch > 1 ? launch_attend_mfma_b<true, 4>(p, grid, st, ev) : launch_attend_mfma_b<false, 4>(p, grid, st, ev);
   return false;
 }
 

@@ -52,11 +52,23 @@ __device__ inline void decode_b3(uint32_t w0, uint32_t w1, uint32_t w2, v4i& b0,
   b1 = v4i{(int)spread3x4(g2), (int)spread3x4(g2 >> 12), (int)spread3x4(g3), (int)spread3x4(g3 >> 12)};
 }
 
+// 4-bit codes to the int8 B operands: operand i takes the lane's dwords
+// w[2i], w[2i + 1] (codes 16i .. 16i + 15); (w >> 4s) & 0x0F0F0F0F keeps
+// the even (s = 0) or odd (s = 1) nibbles, so byte b of dword v of operand i
+// carries element 16i + 8 (v >> 1) + 2b + (v & 1) of the lane group's 32.
+__device__ inline void decode_b4(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, v4i& b0, v4i& b1) {
+  b0 = v4i{(int)(w0 & 0x0F0F0F0Fu), (int)((w0 >> 4) & 0x0F0F0F0Fu), (int)(w1 & 0x0F0F0F0Fu),
+           (int)((w1 >> 4) & 0x0F0F0F0Fu)};
+  b1 = v4i{(int)(w2 & 0x0F0F0F0Fu), (int)((w2 >> 4) & 0x0F0F0F0Fu), (int)(w3 & 0x0F0F0F0Fu),
+           (int)((w3 >> 4) & 0x0F0F0F0Fu)};
+}
+
 // Query digits and per-head constants of the score pass.  The digits are
 // stored in A-operand order: op[h][k][g] holds the 32 bytes lane group g of
 // row (h, k) feeds its two MFMAs (operand i, dword v, byte b = element
 // 32g + 16i + v + 4b for 2-bit codes, matching decode_b2's element order,
-// and 32g + 16i + 4v + b for 3-bit codes, decode_b3's).
+// 32g + 16i + 4v + b for 3-bit codes, decode_b3's, and
+// 32g + 16i + 8 (v >> 1) + 2b + (v & 1) for 4-bit codes, decode_b4's).
 template <int NH>
 struct QPrepN {
   alignas(16) int8_t op[NH][4][4][32];  // [head][digit][lane group][byte]
@@ -82,7 +94,7 @@ __device__ inline float2 load_query(const float* q) {
 // with 16-byte LDS reads: two per tile.
 template <int G, int BB, int NH>
 __device__ inline void prep_digits(float2 x, QPrepN<NH>& qp) {
-  static_assert(BB == 2 || BB == 3, "2- or 3-bit codes");
+  static_assert(BB >= 2 && BB <= 4, "2-, 3- or 4-bit codes");
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   if (wid < NH) {
     const float amax = wave_max(fmaxf(fabsf(x.x), fabsf(x.y)));
@@ -92,7 +104,10 @@ __device__ inline void prep_digits(float2 x, QPrepN<NH>& qp) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int d = 2 * lane + e, g = d >> 5, r = d & 31;
-      const int pos = BB == 3 ? r : 16 * (r >> 4) + 4 * (r & 3) + ((r & 15) >> 2);
+      const int r16 = r & 15;
+      const int pos = BB == 3   ? r
+                      : BB == 4 ? 16 * (r >> 4) + 4 * (((r16 >> 3) << 1) | (r16 & 1)) + ((r16 & 7) >> 1)
+                                : 16 * (r >> 4) + 4 * (r & 3) + (r16 >> 2);
       float rr = xs[e];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -315,10 +330,12 @@ __device__ inline float row16_max_dpp(float x) {
 
 // Mantissa bit at which the P.V product takes code tt (0-7) of a token's
 // 8-element group: 2-bit codes at bits 4, 6, 4, 6, 8, 4, 6, 8; 3-bit codes at
-// bits 4, 7, 6, 7, 4, 7, 4, 7 (every code inside the 10 mantissa bits, its
-// lowest bit at 4 or above).
+// bits 4, 7, 6, 7, 4, 7, 4, 7; 4-bit codes at bit 4 (every code inside the 10
+// mantissa bits, its lowest bit at 4 or above).
 constexpr int code_bit(int tt) { return tt < 2 ? 2 * tt + 4 : tt < 5 ? 2 * tt : 2 * tt - 6; }
 constexpr int code_bit3(int tt) { return tt == 0 || tt == 4 || tt == 6 ? 4 : tt == 2 ? 6 : 7; }
+template <int BB>
+constexpr int code_bit_of(int tt) { return BB == 2 ? code_bit(tt) : BB == 3 ? code_bit3(tt) : 4; }
 
 // Maximum over the four rows of two tiles at once: x0, x1 are a lane's
 // values of tiles 0 and 1; the result holds tile 0's maximum over lanes

@@ -57,6 +57,8 @@ SMALL = [
     dict(ctx=1300, n_q_heads=8, n_kv_heads=1, base_bits=3, refine_bits=2, top_t=64),  # 3-bit, G = 8
     dict(ctx=33, n_q_heads=8, n_kv_heads=2, base_bits=3, refine_bits=8, top_t=7),     # 3-bit, one chunk + 1
     dict(ctx=9000, n_q_heads=16, n_kv_heads=2, refine_bits=4, top_t=300),             # G = 8, several splits
+    dict(ctx=1111, n_q_heads=2, n_kv_heads=2, base_bits=4, refine_bits=2, top_t=90),  # 4-bit, G = 1
+    dict(ctx=5000, n_q_heads=16, n_kv_heads=2, base_bits=4, refine_bits=4, top_t=256), # 4-bit, G = 8
 ]
 
 
@@ -74,6 +76,13 @@ def test_base_pass_precision_3bit():
     P.V with the codes cut from two dwords by a funnel shift and placed at
     fp16 mantissa bits 4-9."""
     _, st = _case(W.small(cfg_id=229, ctx=1000, base_bits=3, refine_bits=2, top_t=0))
+    assert st["max_out_err"] <= 1e-4, st
+
+
+def test_base_pass_precision_4bit():
+    """The same with 4-bit base codes (dword n of a row holds row n's 8 codes,
+    placed at fp16 mantissa bits 4-7)."""
+    _, st = _case(W.small(cfg_id=231, ctx=1000, base_bits=4, refine_bits=4, top_t=0))
     assert st["max_out_err"] <= 1e-4, st
 
 
