@@ -904,7 +904,7 @@ static bool launch_attend_mfma_b(const DecodeParams& p, dim3 grid, hipStream_t s
 
 // Single-sequence steps take the instantiations without the batched
 // sequence search, so that their kernels' start stays as short as it can be.
-bool launch_score_mfma(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev) {
+bool launch_score(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev) {
   if (p.b == 2)
     return p.batch > 1 ? launch_score_mfma_b<true, 2>(p, grid, st, ev) : launch_score_mfma_b<false, 2>(p, grid, st, ev);
   if (p.b == 3)
@@ -914,7 +914,7 @@ bool launch_score_mfma(const DecodeParams& p, dim3 grid, hipStream_t st, KernelE
   return false;
 }
 
-bool launch_attend_mfma(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev) {
+bool launch_attend(const DecodeParams& p, dim3 grid, hipStream_t st, KernelEvents ev) {
   if (p.b == 2)
     return p.batch > 1 ? launch_attend_mfma_b<true, 2>(p, grid, st, ev) : launch_attend_mfma_b<false, 2>(p, grid, st, ev);
   if (p.b == 3)
