@@ -573,6 +573,10 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
     if (k < nmine) issueK(k, s.u.st.ring[wid * kFRing + k]);
   v4i a0, a1;
   prep_query<G>(qx, s.qp, a0, a1);
+  // the query in fp32 for the refining wavefronts of C (wave h < G holds
+  // head h's elements 2 lane, 2 lane + 1), staged now rather than loaded
+  // again between the selection and the V stream
+  if (wid < G) *reinterpret_cast<float2*>(&s.qs[wid][2 * lane]) = qx;
   {
     const int t = lane & 15, hl = lane >> 4;
     const float scale = s.qp.scale[hl < G ? hl : 0] * (kRsqrtD * kLog2e);
@@ -831,8 +835,6 @@ __global__ void __launch_bounds__(64 * kFW) fused_decode(DecodeParams p) {
       s.pre1[nw] = (uint16_t)total;
       s.n1 = total;
     }
-    for (int i = tid; i < G * kHeadDim; i += 64 * kFW)
-      s.qs[i / kHeadDim][i % kHeadDim] = p.q[((int64_t)seq * p.hq + kvh * G) * kHeadDim + i];
   } else if (tid == 0) {
     s.n1 = 0u;
   }

@@ -303,10 +303,14 @@ __device__ inline void store_through(float* p, float v) {
 }
 
 // v_cndmask with a wave-uniform 64-bit lane mask (SGPR pair): lane l takes
-// yes where bit l of mask is set, else no.
+// yes where bit l of mask is set, else no.  The mask's halves go through
+// readfirstlane, which costs nothing for a value already in SGPRs and keeps
+// the operand scalar when the compiler cannot prove the value uniform.
 __device__ inline float lane_select(uint64_t mask, float yes, float no) {
+  const uint64_t m = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(mask >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)mask);
   float r;
-  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(no), "v"(yes), "s"(mask));
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(no), "v"(yes), "s"(m));
   return r;
 }
 
