@@ -299,8 +299,8 @@ typedef struct sf_step_stats {
  * (paragraph "Which tiles count ..."): the sum over its KV head's group of
  * the softmax probability, over the sequence's tokens, of q_h . Khat_i /
  * sqrt(D) (the logits from the base keys), instead of the maximum logit.
- * Supported for 2-bit base codes with groups of 1, 2 or 4 query heads
- * (else SF_ERR_UNSUPPORTED). */
+ * Supported for groups of 1, 2 or 4 query heads (a group of 8:
+ * SF_ERR_UNSUPPORTED). */
 #define SF_DECODE_DROP_UNSELECTED 8
 #define SF_DECODE_ROWS16 16
 #define SF_DECODE_SCORE_SOFTMAX 32

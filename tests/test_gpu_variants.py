@@ -88,6 +88,8 @@ CASES = [
     dict(ctx=3000, n_q_heads=8, n_kv_heads=2, top_t=100),                 # G = 4, ragged tail
     dict(ctx=1100, n_q_heads=2, n_kv_heads=2, top_t=37, refine_bits=4),   # G = 1
     dict(batch=3, ctx=0, ctx_range=(300, 900), n_q_heads=4, n_kv_heads=2, top_t=50),   # varlen batch, G = 2
+    dict(ctx=2500, n_q_heads=8, n_kv_heads=2, top_t=80, base_bits=3, refine_bits=2),   # 3-bit base codes
+    dict(ctx=1700, n_q_heads=4, n_kv_heads=2, top_t=60, base_bits=4, refine_bits=4),   # 4-bit base codes
 ]
 
 
