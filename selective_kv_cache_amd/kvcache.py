@@ -107,7 +107,13 @@ class Decoder:
             self.batch = batch
             self._hist_clean = False
         if self.seq_off_dev.numel() == self.seq_off.size:
-            self.seq_off_dev.copy_(torch.as_tensor(self.seq_off))
+            src = torch.as_tensor(self.seq_off)
+            if self.device.type == "cuda":
+                # from pinned memory, stream-ordered: a copy from pageable
+                # memory would wait for every launch queued before it
+                self.seq_off_dev.copy_(src.pin_memory(), non_blocking=True)
+            else:
+                self.seq_off_dev.copy_(src)
         else:
             self.seq_off_dev = torch.as_tensor(self.seq_off, device=self.device)
         nbytes = B.sf_decode_workspace_size(self.g, self.batch, self.total, self.max_seq, self.top_t)
