@@ -54,12 +54,14 @@
 namespace sfk {
 
 constexpr int kFW = 16;          // wavefronts per work-group
-constexpr int kFVW = 12;         // of them streaming V in phase C,
-constexpr int kFSW = kFW - kFVW; // and refining the selected tokens beside them
+constexpr int kFVW = 11;         // of them streaming V in phase C,
+constexpr int kFSW = kFW - kFVW; // and refining the selected tokens beside them (5 x 16 tokens
+                                 // a round: a 4,096-token range's share of a 2,048-token
+                                 // selection of 128K, 64 +- 8, in one round)
 constexpr int kFRing = 3;        // phase A: ring stages per wavefront (2 chunks in flight)
-constexpr int kFRingV = kFW * kFRing / kFVW;   // phase C: 4 stages per streaming wavefront
+constexpr int kFRingV = kFW * kFRing / kFVW;   // phase C: 4 stages per streaming wavefront (44 of the 48)
 constexpr int kFTPW = 16;        // selected tokens per batch of a refining wavefront (4 lanes each)
-static_assert(kFRingV * kFVW == kFW * kFRing, "phase C's ring is phase A's");
+static_assert(kFRingV * kFVW <= kFW * kFRing, "phase C's ring lies in phase A's");
 constexpr int kFSpinLimit = 1 << 18;   // bounded waits: about 0.2 s
 static_assert(2 * kFusedMaxRanges + kHeadDim <= kFW * kHeadDim, "merge arrays fit in the wave partials");
 
