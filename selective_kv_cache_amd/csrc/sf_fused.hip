@@ -27,10 +27,10 @@
 //      select in LDS, ties to the lower token index (when a range overflows
 //      its slot, the next 12 and the last 8 key bits settle them through
 //      histograms in device memory, one wait per level);
-//   C  12 wavefronts stream the range's V codes once: every token that is
+//   C  11 wavefronts stream the range's V codes once: every token that is
 //      not selected enters the online softmax at base precision (logits
 //      from LDS, P.V on the matrix cores as in the two-pass form); beside
-//      them 4 wavefronts take the selected tokens in batches of 16 (refined
+//      them 5 wavefronts take the selected tokens in batches of 16 (refined
 //      logit and value from their refinement rows, on the vector units);
 //   D  the wavefronts' partials merge into the range's partial (m, l,
 //      acc[D]) per query head, written to device memory;
