@@ -163,28 +163,36 @@ cache_lookup(DecodeParams p, int32_t* slot_tok, int32_t* stamp, int32_t* tok_slo
     if (mrank[j] == 0) mrank[j] = (int32_t)(rk++);
   // Victims: free slots first, then the residents not selected now, oldest
   // stamp first (lower token first): the nmiss smallest of the keys
-  //   free slot i: i;   resident: 2^62 | (stamp + 1) << 31 | token;
-  // hits and selected slots take no part (~0).  Every key differs, so the
-  // nmiss-th smallest, found by an 8-bit radix select, splits them exactly;
-  // the victims are then listed in slot order (which miss takes which
-  // victim does not change what stays cached).
+  //   free slot i: i;   resident: (stamp + 1) << tb | token,
+  // tb the token index's width, at least 12 bits (so that every resident's
+  // key lies above every free slot's: slots <= 4096); hits and selected
+  // slots take no part (~0).  Every key differs, so the nmiss-th smallest,
+  // found by an 8-bit radix select, splits them exactly; the victims are
+  // then listed in slot order (which miss takes which victim does not change
+  // what stays cached).  A resident's stamp is at most this step, so no key
+  // has a bit above hb = tb + bitlen(step + 1) - 1 and the select starts at
+  // the byte holding hb.
+  const int tb = max(12, p.cap > 1 ? 64 - __clzll((unsigned long long)(p.cap - 1)) : 0);
+  const uint64_t tmask = (1ull << tb) - 1ull;
   for (int i = tid; i < p.slots; i += kLookupThreads) {
     uint64_t k = ~0ull;
     const int32_t tok = st_tok[i];
     if (tok < 0)
       k = (uint64_t)i;
     else if (!flag[i])
-      k = (1ull << 62) | ((uint64_t)(uint32_t)(st_stamp[i] + 1) << 31) | (uint64_t)(uint32_t)tok;
+      k = ((uint64_t)(uint32_t)(st_stamp[i] + 1) << tb) | (uint64_t)(uint32_t)tok;
     keys[i] = k;
   }
+  const int hb = tb + (32 - __clz((uint32_t)step + 1u)) - 1;
+  const int start = (hb >> 3) << 3;
   if (tid == 0) {
     sh_prefix = 0ull;
-    sh_mask = 0ull;
+    sh_mask = start + 8 < 64 ? ~0ull << (start + 8) : 0ull;
     sh_left = nmiss;
     sh_whole = nmiss == 0 ? 1u : 0u;
   }
   __syncthreads();
-  for (int shift = 56; shift >= 0 && !sh_whole; shift -= 8) {
+  for (int shift = start; shift >= 0 && !sh_whole; shift -= 8) {
     for (int i = tid; i < 256; i += kLookupThreads) rh[i] = 0u;
     __syncthreads();
     const uint64_t pre = sh_prefix, msk = sh_mask;
@@ -247,8 +255,8 @@ cache_lookup(DecodeParams p, int32_t* slot_tok, int32_t* stamp, int32_t* tok_slo
     if (k < 0 || k >= (int32_t)vtot) continue;   // fewer victims than misses: cannot happen with slots >= T
     const int32_t slot = vlist[k];
     const uint64_t key = keys[slot];
-    if (key >= (1ull << 62))   // the resident leaves (its token's entry, if it still names this slot)
-      atomicCAS(&ts[(int32_t)(key & 0x7FFFFFFFull)], gbase + slot, -1);
+    if (key > tmask)   // the resident leaves (its token's entry, if it still names this slot)
+      atomicCAS(&ts[(int32_t)(key & tmask)], gbase + slot, -1);
     const int32_t g = (int32_t)(a + sel[j]);
     st_tok[slot] = g;
     st_stamp[slot] = step;
